@@ -1,0 +1,373 @@
+"""CPU oracle of the KronQ per-sublayer quantization path (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module:
+only the tests, the smoke check of the package entry point and the benchmark's
+CPU-baseline leg use it.  It shares no code with the GPU library.
+
+Sources (cited by page and section; the pages are web renderings of the KronQ
+paper, arXiv 2607.07964, "KronQ: LLM Quantization via Kronecker-Factored
+Hessian", Lee, Li, Yin, Panda, COLM 2026):
+  [summary]  hyper.ai paper summary, section "Method".
+  [review]   Pith review page (pith.science, S4FLMGRF): referee summary, and the
+             appendix fragments it reproduces -- proof of Proposition 1 (A.1),
+             proof of Theorem 1 (A.2), Table 9, Algorithms 1 and 2.
+  [readme]   GitHub README of the KronQ repository, "Reproduce from scratch"
+             (flags --w_asym, --w_groupsize, --act_order, --alpha).
+Where the pages leave a step open the plainest reading is taken; every such
+reading is listed in the design notes of the repository and flagged below with
+"Reading:".
+
+Notation: W is m x n (rows = output channels, columns = input channels);
+X is N x n activations, G is N x m output gradients; all float64 here.
+Every function is pinned by a CPU test against closed forms, brute force or
+hand-worked values (tests/test_oracle_pins.py); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Step 1: Kronecker factors.  [summary] Method: the per-sample gradient of a
+# linear layer is g x^T, and under the K-FAC independence assumption the
+# empirical-Fisher Hessian factorizes as H ~ H_X (x) H_G with H_X = E[x x^T],
+# H_G = E[g g^T].  Reading: the expectation is the mean over the N token rows.
+# --------------------------------------------------------------------------
+
+
+def gram(A: np.ndarray) -> np.ndarray:
+    """H = A^T A / N for A of shape (N, d): the second moment of the rows."""
+    A = np.asarray(A, dtype=np.float64)
+    return (A.T @ A) / A.shape[0]
+
+
+def proxy_loss(dW: np.ndarray, HX: np.ndarray, HG: np.ndarray) -> float:
+    """Kronecker-factored layer objective tr(H_G dW H_X dW^T).
+
+    [summary] Method (the K-FAC quantization objective, equation not rendered);
+    [review] proof of Theorem 1 writes the first term in exactly this trace form.
+    """
+    dW = np.asarray(dW, dtype=np.float64)
+    return float(np.trace(HG @ dW @ HX @ dW.T))
+
+
+def proxy_loss_kron(dW: np.ndarray, HX: np.ndarray, HG: np.ndarray) -> float:
+    """The same objective written with the explicit Kronecker Hessian:
+    vec(dW)^T (H_X (x) H_G) vec(dW), vec stacking columns.  Tiny inputs only."""
+    v = np.asarray(dW, dtype=np.float64).reshape(-1, order="F")
+    return float(v @ np.kron(HX, HG) @ v)
+
+
+# --------------------------------------------------------------------------
+# Step 2: bidirectional incoherence processing (BiIP).  [summary] Method and
+# [review] Eq. 11-12 / proof of Theorem 1: an output-side diagonal rescale S_G
+# (novel) next to the input-side one, then orthogonal transforms
+# W' = U W V^T, H_G' = U H_G U^T, H_X' = V H_X V^T with U, V randomized
+# Hadamard transforms (machinery after QuIP#, [readme]).
+# Readings: S_G = diag(H_G)^alpha applied as W <- S_G W, H_G <- S_G^-1 H_G S_G^-1
+# (the direction that leaves the objective unchanged); S_X = I; a randomized
+# Hadamard transform on a dimension d = b*k is (I_b (x) H_k) D / sqrt(k) with
+# H_k the Sylvester matrix and D = diag(signs); the signs are inputs.
+# --------------------------------------------------------------------------
+
+
+def hadamard_matrix(k: int) -> np.ndarray:
+    """Sylvester Hadamard matrix, H[a, b] = (-1)^popcount(a & b)."""
+    if k < 1 or (k & (k - 1)):
+        raise ValueError("Hadamard order must be a power of two")
+    a = np.arange(k)
+    bits = np.bitwise_and.outer(a, a)
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits >>= 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    """Unnormalized Walsh-Hadamard transform along the last axis (textbook
+    in-place butterflies: for each h = 1, 2, 4, ..., pairs (i, i + h) become
+    (a + b, a - b)).  Equals x @ hadamard_matrix(k)."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    k = y.shape[-1]
+    if k & (k - 1):
+        raise ValueError("length must be a power of two")
+    h = 1
+    while h < k:
+        y = y.reshape(y.shape[:-1] + (k // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        y = y.reshape(y.shape[:-3] + (k,))
+        h *= 2
+    return y
+
+
+def rotate_rows(M: np.ndarray, block: int, signs: np.ndarray) -> np.ndarray:
+    """M T^T where T = (I (x) H_block) diag(signs) / sqrt(block) acts on the
+    column index of M (each row r becomes T M[r, :])."""
+    M = np.asarray(M, dtype=np.float64)
+    rows, d = M.shape
+    if d % block:
+        raise ValueError("block must divide the dimension")
+    Y = (M * np.asarray(signs, dtype=np.float64)[None, :]).reshape(rows, d // block, block)
+    return fwht(Y).reshape(rows, d) / np.sqrt(block)
+
+
+def rotate_cols(M: np.ndarray, block: int, signs: np.ndarray) -> np.ndarray:
+    """T M with T as in rotate_rows acting on the row index of M."""
+    return rotate_rows(np.asarray(M, dtype=np.float64).T, block, signs).T
+
+
+def rotation_matrix(d: int, block: int, signs: np.ndarray) -> np.ndarray:
+    """Explicit T = (I (x) H_block) diag(signs) / sqrt(block); small d only."""
+    T = np.kron(np.eye(d // block), hadamard_matrix(block)) / np.sqrt(block)
+    return T * np.asarray(signs, dtype=np.float64)[None, :]
+
+
+def output_rescale(HG: np.ndarray, alpha: float) -> np.ndarray:
+    """s_g = diag(H_G)^alpha; a non-positive diagonal entry gives 1."""
+    d = np.diag(np.asarray(HG, dtype=np.float64)).copy()
+    s = np.ones_like(d)
+    pos = d > 0
+    s[pos] = d[pos] ** alpha
+    return s
+
+
+def biip(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha):
+    """Returns (W', H_X', H_G', s_g):
+       W'   = U S_G W V^T
+       H_X' = V H_X V^T
+       H_G' = U S_G^-1 H_G S_G^-1 U^T
+    with U = (I (x) H_out_block) D_out / sqrt(out_block) and V likewise on the
+    input side.  HX or HG may be None (then returned as None)."""
+    W = np.asarray(W, dtype=np.float64)
+    s = output_rescale(HG, alpha) if HG is not None else np.ones(W.shape[0])
+    Ws = W * s[:, None]
+    Wp = rotate_cols(rotate_rows(Ws, in_block, in_signs), out_block, out_signs)
+    HXp = None
+    if HX is not None:
+        HXp = rotate_cols(rotate_rows(HX, in_block, in_signs), in_block, in_signs)
+    HGp = None
+    if HG is not None:
+        HGs = np.asarray(HG, dtype=np.float64) / s[:, None] / s[None, :]
+        HGp = rotate_cols(rotate_rows(HGs, out_block, out_signs), out_block, out_signs)
+    return Wp, HXp, HGp, s
+
+
+# --------------------------------------------------------------------------
+# Step 3: act-order, damping and the Cholesky factor of the inverse.
+# [review] Algorithm 2 (its damping step, then its inverse-Cholesky step): the
+# damped H_X is H_X + lambda mean(diag(H_X)) I, and the loop takes the inverse
+# Cholesky factor of it.  [readme] --act_order.
+# Readings: the act-order key is diag(H_X') (post-BiIP, undamped), sorted in
+# descending order, ties to the lower index; "InverseCholesky" is the upper
+# triangular R with positive diagonal and R^T R = H^-1 (the factor the
+# column loop's compensation uses).
+# --------------------------------------------------------------------------
+
+
+def act_order_perm(HX: np.ndarray) -> np.ndarray:
+    """perm[j] = original column processed j-th: stable descending sort of diag."""
+    d = np.diag(np.asarray(HX, dtype=np.float64))
+    return np.argsort(-d, kind="stable").astype(np.int64)
+
+
+def damp(H: np.ndarray, lam: float) -> np.ndarray:
+    """H + lam * mean(diag(H)) * I."""
+    H = np.asarray(H, dtype=np.float64)
+    return H + lam * np.mean(np.diag(H)) * np.eye(H.shape[0])
+
+
+def chol_inv_upper(H: np.ndarray):
+    """Returns (R, info): R upper triangular with positive diagonal and
+    R^T R = H^-1; info = -1 on success, else the first index whose pivot of the
+    Cholesky factorization of H is not positive (R is then None)."""
+    H = np.asarray(H, dtype=np.float64)
+    try:
+        np.linalg.cholesky(H)
+    except np.linalg.LinAlgError:
+        # locate the first non-positive pivot by the textbook column loop
+        n = H.shape[0]
+        L = np.zeros_like(H)
+        for j in range(n):
+            piv = H[j, j] - L[j, :j] @ L[j, :j]
+            if not piv > 0:
+                return None, j
+            L[j, j] = np.sqrt(piv)
+            L[j + 1:, j] = (H[j + 1:, j] - L[j + 1:, :j] @ L[j, :j]) / L[j, j]
+        return None, n - 1
+    Hinv = np.linalg.inv(H)
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    R = np.linalg.cholesky(Hinv).T
+    return R, -1
+
+
+def prepare_hessian(HXp: np.ndarray, lam: float, act_order: bool):
+    """Act-order permutation (or identity) and the damped, permuted H."""
+    n = HXp.shape[0]
+    perm = act_order_perm(HXp) if act_order else np.arange(n, dtype=np.int64)
+    Hp = np.asarray(HXp, dtype=np.float64)[np.ix_(perm, perm)]
+    return perm, damp(Hp, lam)
+
+
+# --------------------------------------------------------------------------
+# Step 4: column-wise OBS quantize-and-compensate using H_X alone.
+# [summary] Method and [review] Proposition 1: after quantizing column p the
+# compensation is the scaled quantization error times rows of the inverse
+# Cholesky factor; H_G cancels, so the solver is GPTQ/GPTAQ's.  [review]
+# Algorithm 2: lazy batches of B columns (an exact reordering of the same
+# updates, so this oracle runs the plain column-sequential loop).  GPTAQ's
+# asymmetric term is zero here because no drifted input stream exists.
+# Quantizer ([readme] --w_asym, --w_groupsize; [review] "plain uniform
+# per-channel grid"): asymmetric uniform min/max grid.  Readings: the range
+# includes 0; a degenerate range becomes [-1, 1]; scale = (max-min)/(2^b-1);
+# zero = round(-min/scale); codes round half to even and clamp to [0, 2^b-1];
+# per-channel parameters come from the whole initial row, group parameters from
+# the current compensated values of the group when its first column is reached;
+# groups follow processing order.
+# --------------------------------------------------------------------------
+
+
+def quant_params(V: np.ndarray, bits: int):
+    """Per-row (scale, zero) of the asymmetric grid for the rows of V (m x c)."""
+    V = np.asarray(V, dtype=np.float64)
+    maxq = 2 ** bits - 1
+    xmin = np.minimum(V.min(axis=1), 0.0)
+    xmax = np.maximum(V.max(axis=1), 0.0)
+    deg = xmin == xmax
+    xmin = np.where(deg, -1.0, xmin)
+    xmax = np.where(deg, 1.0, xmax)
+    scale = (xmax - xmin) / maxq
+    zero = np.rint(-xmin / scale)
+    return scale, zero
+
+
+def zero_pre_round(V: np.ndarray, bits: int):
+    """-min/scale of quant_params before rounding (for tie checks)."""
+    V = np.asarray(V, dtype=np.float64)
+    maxq = 2 ** bits - 1
+    xmin = np.minimum(V.min(axis=1), 0.0)
+    xmax = np.maximum(V.max(axis=1), 0.0)
+    deg = xmin == xmax
+    xmin = np.where(deg, -1.0, xmin)
+    xmax = np.where(deg, 1.0, xmax)
+    return -xmin / ((xmax - xmin) / maxq)
+
+
+def rtn(V: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int):
+    """Round-to-nearest on the grid: returns (codes, dequantized, pre-round t)."""
+    t = np.asarray(V, dtype=np.float64) / scale[:, None] + zero[:, None]
+    q = np.clip(np.rint(t), 0, 2 ** bits - 1)
+    return q, scale[:, None] * (q - zero[:, None]), t
+
+
+def gptq(W: np.ndarray, R: np.ndarray, perm, bits: int, group: int, decide_codes=None,
+         decide_params=None):
+    """Column-sequential OBS loop.
+
+    W      : m x n weights in natural column order (BiIP domain).
+    R      : n x n upper factor in processing order (R^T R = H^-1 of the
+             damped, permuted H).
+    perm   : processing order (perm[j] = natural column of step j).
+    group  : <= 0 per-channel; else group size in processing order.
+    decide_codes  : optional hook (j, t, q) -> q; the tests use it to compare a
+                    second implementation whose rounding ties may differ (it
+                    receives step j's pre-round values t and this oracle's q).
+    decide_params : optional hook (g, scale, zero, zt) -> (scale, zero) for the
+                    parameters of group g (zt = -min/scale before rounding).
+    Returns dict(codes (m x n natural, int), scales, zeros (m x ngroups), What
+    (m x n natural), pre (m x n natural), E (m x n processing order)).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    m, n = W.shape
+    perm = np.asarray(perm, dtype=np.int64)
+    maxq = 2 ** bits - 1
+    Wt = W[:, perm].copy()
+    ng = 1 if group <= 0 else (n + group - 1) // group
+    scales = np.zeros((m, ng))
+    zeros = np.zeros((m, ng))
+    codes = np.zeros((m, n))
+    What = np.zeros((m, n))
+    pre = np.zeros((m, n))
+    E = np.zeros((m, n))
+    if group <= 0:
+        scale, zero = quant_params(Wt, bits)
+        if decide_params is not None:
+            scale, zero = decide_params(0, scale, zero, zero_pre_round(Wt, bits))
+        scales[:, 0], zeros[:, 0] = scale, zero
+    for j in range(n):
+        if group > 0 and j % group == 0:
+            scale, zero = quant_params(Wt[:, j:j + group], bits)
+            if decide_params is not None:
+                scale, zero = decide_params(j // group, scale, zero,
+                                            zero_pre_round(Wt[:, j:j + group], bits))
+            scales[:, j // group], zeros[:, j // group] = scale, zero
+        t = Wt[:, j] / scale + zero
+        q = np.clip(np.rint(t), 0, maxq)
+        if decide_codes is not None:
+            q = decide_codes(j, t, q)
+        wq = scale * (q - zero)
+        e = (Wt[:, j] - wq) / R[j, j]
+        Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:])
+        codes[:, j], What[:, j], pre[:, j], E[:, j] = q, wq, t, e
+    inv = np.empty(n, dtype=np.int64)
+    inv[perm] = np.arange(n)
+    return dict(codes=codes[:, inv], scales=scales, zeros=zeros, What=What[:, inv],
+                pre=pre[:, inv], E=E)
+
+
+# --------------------------------------------------------------------------
+# Step 5: sensitivity and bit allocation.  [summary] Method: the expected loss
+# of a sublayer scales with eps^2 tr(H); with H ~ H_X (x) H_G the score is
+# s = tr(H_G) tr(H_X), computed after BiIP; higher bit-widths go to larger s.
+# [readme] --inter_layer_mp: upgrade the top sensitive sublayer types by +1 bit.
+# Readings: traces of the post-BiIP, undamped factors; allocation is greedy
+# from bmin, visiting sublayers in descending score (ties to the lower index),
+# raising each by one bit at a time while it is below bmax and the parameter-
+# weighted bit total stays within the budget.
+# --------------------------------------------------------------------------
+
+
+def sensitivity(HXp: np.ndarray, HGp: np.ndarray):
+    trx = float(np.sum(np.diag(np.asarray(HXp, dtype=np.float64))))
+    trg = float(np.sum(np.diag(np.asarray(HGp, dtype=np.float64))))
+    return trx, trg, trx * trg
+
+
+def allocate_bits(scores, n_params, bmin: int, bmax: int, budget_bits: int):
+    """Greedy allocation; returns the list of bits (raises ValueError when the
+    budget cannot hold every sublayer at bmin)."""
+    L = len(scores)
+    n_params = [int(x) for x in n_params]
+    used = bmin * sum(n_params)
+    if budget_bits < used or bmin > bmax:
+        raise ValueError("budget below the minimum allocation")
+    bits = [bmin] * L
+    order = sorted(range(L), key=lambda i: (-float(scores[i]), i))
+    for i in order:
+        while bits[i] < bmax and used + n_params[i] <= budget_bits:
+            bits[i] += 1
+            used += n_params[i]
+    return bits
+
+
+# --------------------------------------------------------------------------
+# Whole sublayer, end to end (float64 throughout).
+# --------------------------------------------------------------------------
+
+
+def quantize_sublayer(W, X, G, in_signs, in_block, out_signs, out_block, alpha, lam, bits,
+                      group, act_order):
+    HX = gram(X)
+    HG = gram(G)
+    Wp, HXp, HGp, s = biip(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha)
+    trs = sensitivity(HXp, HGp)
+    perm, H = prepare_hessian(HXp, lam, act_order)
+    R, info = chol_inv_upper(H)
+    if R is None:
+        raise np.linalg.LinAlgError("damped H not positive definite at pivot %d" % info)
+    out = gptq(Wp, R, perm, bits, group)
+    out.update(HX=HX, HG=HG, Wp=Wp, HXp=HXp, HGp=HGp, sg=s, traces=trs, perm=perm, R=R, H=H)
+    return out

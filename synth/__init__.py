@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs shared by the GPU library's tests and the CPU oracle.
+
+The generator itself is C (``synth.c``, built into ``libsynth.so`` next to this
+file); this wrapper only marshals numpy arrays.  It contains no arithmetic of
+the quantizer.  See ``synth.c`` for the exact definition of every stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libsynth.so")
+_SRC = os.path.join(_HERE, "synth.c")
+
+NORMAL, ACT_NORMAL, ACT_T4, GRAD_LOGNORMAL, INT = 0, 1, 2, 3, 4
+_DT = {"f64": (0, np.float64), "f32": (1, np.float32), "bf16": (2, np.uint16)}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile libsynth.so with gcc (OpenMP); returns its path."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        i64, u64, vp, dbl = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_double
+        lib.synth_matrix.argtypes = [ctypes.c_int, u64, i64, i64, i64, i64, i64, i64, dbl, vp, i64,
+                                     dbl, ctypes.c_int, vp, i64]
+        lib.synth_matrix.restype = ctypes.c_int
+        lib.synth_outlier_channels.argtypes = [u64, i64, i64, vp]
+        lib.synth_outlier_channels.restype = ctypes.c_int
+        lib.synth_signs.argtypes = [u64, i64, vp]
+        lib.synth_signs.restype = ctypes.c_int
+        lib.synth_mix64.argtypes = [u64]
+        lib.synth_mix64.restype = u64
+        _lib = lib
+    return _lib
+
+
+def mix64(z: int) -> int:
+    return int(_load().synth_mix64(z & 0xFFFFFFFFFFFFFFFF))
+
+
+def outlier_channels(seed: int, n: int, k: int) -> np.ndarray:
+    out = np.zeros(max(k, 1), dtype=np.int64)
+    rc = _load().synth_outlier_channels(seed, n, k, out.ctypes.data)
+    if rc:
+        raise ValueError("synth_outlier_channels failed (%d)" % rc)
+    return out[:k].copy()
+
+
+def signs(seed: int, n: int) -> np.ndarray:
+    """+-1.0 float32 vector (stream 5 of `seed`)."""
+    out = np.zeros(max(n, 1), dtype=np.float32)
+    rc = _load().synth_signs(seed, n, out.ctypes.data)
+    if rc:
+        raise ValueError("synth_signs failed (%d)" % rc)
+    return out[:n].copy()
+
+
+def matrix(kind: int, seed: int, rows: int, cols: int, *, r0: int = 0, nr: int | None = None,
+           c0: int = 0, nc: int | None = None, p1: float = 1.0, outliers=None,
+           out_factor: float = 1.0, dtype: str = "f64", out: np.ndarray | None = None) -> np.ndarray:
+    """Block [r0:r0+nr, c0:c0+nc] of the logical rows x cols matrix of `kind`.
+
+    dtype "bf16" returns the raw bf16 bit patterns as uint16.
+    """
+    nr = rows - r0 if nr is None else nr
+    nc = cols - c0 if nc is None else nc
+    code, npdt = _DT[dtype]
+    if out is None:
+        out = np.empty((nr, nc), dtype=npdt)
+    assert out.dtype == npdt and out.shape == (nr, nc) and out.flags["C_CONTIGUOUS"]
+    if outliers is None or len(outliers) == 0:
+        optr, nout = None, 0
+    else:
+        outliers = np.ascontiguousarray(outliers, dtype=np.int64)
+        optr, nout = outliers.ctypes.data, len(outliers)
+    rc = _load().synth_matrix(kind, seed, rows, cols, r0, nr, c0, nc, float(p1), optr, nout,
+                              float(out_factor), code, out.ctypes.data if out.size else None,
+                              max(nc, 1))
+    if rc:
+        raise ValueError("synth_matrix failed (%d)" % rc)
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of raw bf16 bit patterns (uint16) to float64."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)

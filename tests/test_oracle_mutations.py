@@ -1,0 +1,62 @@
+"""The oracle's pins must fail on plausible mistakes.
+
+Each case plants one mistake (a dropped term, a wrong sign, index, operand or
+rounding rule) in a temporary copy of the oracle and runs the pin tests against
+that copy; every mutant must be caught.  The oracle file itself is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kronq_oracle.py")
+
+MUTANTS = [
+    ("gram normalization", "return (A.T @ A) / A.shape[0]", "return (A.T @ A) / (A.shape[0] - 1)"),
+    ("butterfly sign", "y[..., 1, :] = a - b", "y[..., 1, :] = b - a"),
+    ("rotation normalization", "return fwht(Y).reshape(rows, d) / np.sqrt(block)",
+     "return fwht(Y).reshape(rows, d) / block"),
+    ("rescale exponent", "s[pos] = d[pos] ** alpha", "s[pos] = d[pos] ** (2 * alpha)"),
+    ("H_G rescale direction", "HGs = np.asarray(HG, dtype=np.float64) / s[:, None] / s[None, :]",
+     "HGs = np.asarray(HG, dtype=np.float64) * s[:, None] * s[None, :]"),
+    ("W rescale direction", "Ws = W * s[:, None]", "Ws = W / s[:, None]"),
+    ("act-order tie order", 'return np.argsort(-d, kind="stable").astype(np.int64)',
+     'return np.argsort(d, kind="stable")[::-1].astype(np.int64)'),
+    ("damping scale", "return H + lam * np.mean(np.diag(H)) * np.eye(H.shape[0])",
+     "return H + lam * np.eye(H.shape[0])"),
+    ("factor of H instead of H^-1", "R = np.linalg.cholesky(Hinv).T", "R = np.linalg.cholesky(H).T"),
+    ("range without zero", "xmin = np.minimum(V.min(axis=1), 0.0)\n    xmax = np.maximum(V.max(axis=1), 0.0)\n    deg = xmin == xmax\n    xmin = np.where(deg, -1.0, xmin)\n    xmax = np.where(deg, 1.0, xmax)\n    scale",
+     "xmin = V.min(axis=1)\n    xmax = V.max(axis=1)\n    deg = xmin == xmax\n    xmin = np.where(deg, -1.0, xmin)\n    xmax = np.where(deg, 1.0, xmax)\n    scale"),
+    ("zero point floor", "zero = np.rint(-xmin / scale)\n    return scale, zero",
+     "zero = np.floor(-xmin / scale)\n    return scale, zero"),
+    ("error scaling", "e = (Wt[:, j] - wq) / R[j, j]", "e = (Wt[:, j] - wq) * R[j, j]"),
+    ("update sign", "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:])", "Wt[:, j + 1:] += np.outer(e, R[j, j + 1:])"),
+    ("transposed factor", "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:])", "Wt[:, j + 1:] -= np.outer(e, R[j + 1:, j])"),
+    ("group params from uncompensated W", "scale, zero = quant_params(Wt[:, j:j + group], bits)",
+     "scale, zero = quant_params(W[:, perm][:, j:j + group], bits)"),
+    ("round half up", "q = np.clip(np.rint(t), 0, maxq)\n        if decide_codes",
+     "q = np.clip(np.floor(t + 0.5), 0, maxq)\n        if decide_codes"),
+    ("dropped trace term", "trg = float(np.sum(np.diag(np.asarray(HGp, dtype=np.float64))))",
+     "trg = float(np.sum(np.diag(np.asarray(HGp, dtype=np.float64))[1:]))"),
+    ("ascending allocation", "order = sorted(range(L), key=lambda i: (-float(scores[i]), i))",
+     "order = sorted(range(L), key=lambda i: (float(scores[i]), i))"),
+    ("budget boundary", "while bits[i] < bmax and used + n_params[i] <= budget_bits:",
+     "while bits[i] < bmax and used + n_params[i] < budget_bits:"),
+    ("wrong un-permutation", "codes=codes[:, inv]", "codes=codes[:, perm]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, "mutation anchor not found: " + name
+    (tmp_path / "mutant_oracle.py").write_text(text.replace(old, new, 1))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = str(tmp_path) + os.pathsep + env.get("PYTHONPATH", "")
+    env["KRONQ_ORACLE_UNDER_TEST"] = "mutant_oracle"
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "pins did not catch the planted mistake: " + name

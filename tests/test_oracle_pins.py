@@ -1,0 +1,449 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test ties one oracle function to something other than itself: a closed
+form, an identity stated on the pages (Kronecker objective, Proposition 1's
+H_G cancellation, Theorem 1's rotation invariance, the trace of a Kronecker
+product), brute force on tiny inputs, or a hand-worked value stored under
+tests/golden/ with its derivation.
+"""
+import importlib
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+# the mutation test points this at a planted-mistake copy of the oracle
+O = importlib.import_module(os.environ.get("KRONQ_ORACLE_UNDER_TEST", "oracle.kronq_oracle"))
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def rand_spd(rng, d, cond=10.0):
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    ev = np.geomspace(1.0, cond, d)
+    return (Q * ev) @ Q.T
+
+
+# ---------------------------------------------------------------- Gram
+
+
+def test_gram_brute_force_integer():
+    rng = np.random.default_rng(0)
+    A = rng.integers(-3, 4, size=(7, 3)).astype(float)
+    H = O.gram(A)
+    for i in range(3):
+        for j in range(3):
+            s = 0.0
+            for t in range(7):
+                s += A[t][i] * A[t][j]
+            assert H[i, j] == s / 7
+
+
+def test_gram_closed_form_hadamard_rows():
+    # rows of a Hadamard matrix are orthogonal: X^T X = N I exactly
+    X = O.hadamard_matrix(16)
+    np.testing.assert_array_equal(O.gram(X), np.eye(16))
+
+
+def test_gram_symmetric_psd():
+    rng = np.random.default_rng(1)
+    H = O.gram(rng.standard_normal((50, 9)))
+    np.testing.assert_array_equal(H, H.T)
+    assert np.linalg.eigvalsh(H).min() > -1e-12
+
+
+# ------------------------------------------------- Kronecker objective
+
+
+def test_kronecker_identity():
+    # vec(dW)^T (H_X (x) H_G) vec(dW) = tr(H_G dW H_X dW^T)
+    rng = np.random.default_rng(2)
+    for m, n in [(2, 3), (3, 5), (4, 4)]:
+        dW = rng.standard_normal((m, n))
+        HX, HG = rand_spd(rng, n), rand_spd(rng, m)
+        a = O.proxy_loss(dW, HX, HG)
+        b = O.proxy_loss_kron(dW, HX, HG)
+        assert abs(a - b) <= 1e-12 * abs(b)
+
+
+def test_objective_identity_factors_is_frobenius():
+    rng = np.random.default_rng(3)
+    dW = rng.standard_normal((3, 4))
+    assert O.proxy_loss(dW, np.eye(4), np.eye(3)) == pytest.approx(np.sum(dW * dW), rel=1e-14)
+
+
+# ------------------------------------------------------------ Hadamard
+
+
+def test_hadamard_printed_and_sylvester():
+    np.testing.assert_array_equal(O.hadamard_matrix(4), np.array(gold("hadamard_sylvester_4.json")["H4"]))
+    np.testing.assert_array_equal(O.hadamard_matrix(1), [[1.0]])
+    for k in [2, 4, 8, 32]:
+        H = O.hadamard_matrix(k)
+        h = O.hadamard_matrix(k // 2)
+        np.testing.assert_array_equal(H, np.block([[h, h], [h, -h]]))
+        np.testing.assert_array_equal(H @ H.T, k * np.eye(k))
+
+
+def test_fwht_matches_matrix_and_special_vectors():
+    rng = np.random.default_rng(4)
+    for k in [1, 2, 8, 64, 256]:
+        x = rng.standard_normal((3, k))
+        np.testing.assert_allclose(O.fwht(x), x @ O.hadamard_matrix(k), rtol=0, atol=1e-12 * k)
+        # delta -> first row of H (all ones); constant -> k * delta
+        d = np.zeros(k); d[0] = 1.0
+        np.testing.assert_array_equal(O.fwht(d), np.ones(k))
+        c = np.ones(k)
+        e = np.zeros(k); e[0] = k
+        np.testing.assert_array_equal(O.fwht(c), e)
+        # round trip: H H = k I
+        np.testing.assert_allclose(O.fwht(O.fwht(x)) / k, x, rtol=0, atol=1e-12 * k)
+
+
+def test_rotation_orthogonal_and_matches_explicit():
+    rng = np.random.default_rng(5)
+    for d, b in [(16, 16), (12, 4), (24, 8), (43 * 4, 4)]:
+        s = rng.choice([-1.0, 1.0], size=d)
+        T = O.rotation_matrix(d, b, s)
+        np.testing.assert_allclose(T @ T.T, np.eye(d), atol=1e-13)
+        M = rng.standard_normal((5, d))
+        np.testing.assert_allclose(O.rotate_rows(M, b, s), M @ T.T, atol=1e-12)
+        np.testing.assert_allclose(O.rotate_cols(M.T, b, s), T @ M.T, atol=1e-12)
+        # block-diagonal: mixing stays inside each block
+        assert np.all(T[:b, b:] == 0)
+
+
+def test_rotation_spreads_a_spike():
+    # W = c e_i e_j^T: every entry of U W V^T inside the (i-block, j-block)
+    # has magnitude c / sqrt(k_out k_in): maximal incoherence of a spike
+    m, n, ko, ki = 8, 16, 8, 4
+    W = np.zeros((m, n)); W[3, 5] = 2.0
+    rng = np.random.default_rng(6)
+    so, si = rng.choice([-1.0, 1.0], m), rng.choice([-1.0, 1.0], n)
+    Wp, _, _, _ = O.biip(W, None, np.eye(m), si, ki, so, ko, 0.0)
+    blk = np.abs(Wp[:, 4:8])
+    np.testing.assert_allclose(blk, np.full_like(blk, 2.0 / np.sqrt(ko * ki)), atol=1e-14)
+    assert np.count_nonzero(np.abs(Wp) > 1e-15) == ko * ki
+
+
+# ---------------------------------------------------------------- BiIP
+
+
+def _biip_case(seed, m=8, n=12, ki=4, ko=8, alpha=0.25):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((m, n))
+    HX = rand_spd(rng, n, 50.0)
+    HG = rand_spd(rng, m, 1e3)
+    si, so = rng.choice([-1.0, 1.0], n), rng.choice([-1.0, 1.0], m)
+    return W, HX, HG, si, ki, so, ko, alpha
+
+
+def test_biip_explicit_matrices():
+    W, HX, HG, si, ki, so, ko, a = _biip_case(7)
+    Wp, HXp, HGp, s = O.biip(W, HX, HG, si, ki, so, ko, a)
+    U = O.rotation_matrix(W.shape[0], ko, so)
+    V = O.rotation_matrix(W.shape[1], ki, si)
+    S = np.diag(np.diag(HG) ** a)
+    np.testing.assert_allclose(Wp, U @ S @ W @ V.T, atol=1e-12)
+    np.testing.assert_allclose(HXp, V @ HX @ V.T, atol=1e-10)
+    Si = np.linalg.inv(S)
+    np.testing.assert_allclose(HGp, U @ Si @ HG @ Si @ U.T, atol=1e-10)
+
+
+def test_biip_objective_invariance_theorem1():
+    # Theorem 1 (rotation invariance), extended to the S_G rescale: the
+    # objective of any perturbation is the same before and after BiIP
+    W, HX, HG, si, ki, so, ko, a = _biip_case(8)
+    rng = np.random.default_rng(9)
+    dW = rng.standard_normal(W.shape)
+    dWp, HXp, HGp, _ = O.biip(dW, HX, HG, si, ki, so, ko, a)
+    assert O.proxy_loss(dWp, HXp, HGp) == pytest.approx(O.proxy_loss(dW, HX, HG), rel=1e-11)
+
+
+def test_biip_trace_closed_forms():
+    W, HX, HG, si, ki, so, ko, a = _biip_case(10)
+    _, HXp, HGp, s = O.biip(W, HX, HG, si, ki, so, ko, a)
+    assert np.trace(HXp) == pytest.approx(np.trace(HX), rel=1e-13)
+    assert np.trace(HGp) == pytest.approx(np.sum(np.diag(HG) ** (1 - 2 * a)), rel=1e-13)
+    np.testing.assert_allclose(s, np.diag(HG) ** a, rtol=1e-15)
+    # alpha = 0: no rescale, H_G trace preserved
+    _, _, HGp0, s0 = O.biip(W, HX, HG, si, ki, so, ko, 0.0)
+    np.testing.assert_array_equal(s0, np.ones_like(s0))
+    assert np.trace(HGp0) == pytest.approx(np.trace(HG), rel=1e-13)
+
+
+def test_biip_zero_diagonal_rescale_is_one():
+    HG = np.diag([4.0, 0.0, 9.0])
+    np.testing.assert_allclose(O.output_rescale(HG, 0.5), [2.0, 1.0, 3.0])
+
+
+# ---------------------------------------------- act-order, damping, R
+
+
+def test_act_order_ties_stable():
+    H = np.diag([1.0, 3.0, 3.0, 2.0])
+    np.testing.assert_array_equal(O.act_order_perm(H), [1, 2, 3, 0])
+
+
+def test_damping_hand_value():
+    H = np.array([[2.0, 1.0], [1.0, 4.0]])
+    np.testing.assert_array_equal(O.damp(H, 0.5), [[3.5, 1.0], [1.0, 5.5]])
+
+
+def test_chol_inv_worked_example():
+    g = gold("chol_inv_2x2.json")
+    R, info = O.chol_inv_upper(np.array(g["H"]))
+    assert info == -1
+    np.testing.assert_allclose(R, g["R"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(R, [[np.sqrt(3 / 8), -1 / np.sqrt(6)], [0, 1 / np.sqrt(3)]], rtol=1e-14)
+    np.testing.assert_allclose(1.0 / np.diag(R) ** 2, g["schur_D"], rtol=1e-14)
+
+
+def test_chol_inv_schur_diagonal_and_inverse():
+    # 1/R_jj^2 is the Schur complement of the trailing block at j (the D of
+    # H = U D U^T, U unit upper): the tr(D_X) terms of Table 9
+    rng = np.random.default_rng(11)
+    H = rand_spd(rng, 6, 100.0)
+    R, info = O.chol_inv_upper(H)
+    assert info == -1
+    assert np.allclose(np.tril(R, -1), 0) and np.all(np.diag(R) > 0)
+    np.testing.assert_allclose(R.T @ R @ H, np.eye(6), atol=1e-10)
+    for j in range(6):
+        a = H[j, j]
+        if j + 1 < 6:
+            b = H[j, j + 1:]
+            C = H[j + 1:, j + 1:]
+            a = a - b @ np.linalg.solve(C, b)
+        assert 1.0 / R[j, j] ** 2 == pytest.approx(a, rel=1e-10)
+
+
+def test_chol_inv_not_pd_reports_pivot():
+    assert O.chol_inv_upper(np.array([[1.0, 2.0], [2.0, 1.0]]))[1] == 1
+    assert O.chol_inv_upper(np.array([[-1.0, 0.0], [0.0, 1.0]]))[1] == 0
+    assert O.chol_inv_upper(np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 1.0], [0.0, 1.0, 1.0]]))[1] == 2
+
+
+# ----------------------------------------------------------- quantizer
+
+
+def test_quant_params_hand_values():
+    s, z = O.quant_params(np.array([[-1.0, 0.0, 2.0]]), 2)
+    assert (s[0], z[0]) == (1.0, 1.0)
+    q, d, t = O.rtn(np.array([[-1.0, 0.0, 2.0]]), s, z, 2)
+    np.testing.assert_array_equal(q, [[0, 1, 3]])
+    np.testing.assert_array_equal(d, [[-1, 0, 2]])
+    # all-positive group: the range is widened to include 0
+    s, z = O.quant_params(np.array([[1.0, 2.0, 3.0]]), 2)
+    assert (s[0], z[0]) == (1.0, 0.0)
+    # degenerate range -> [-1, 1]; zero = round-half-even(1.5) = 2
+    s, z = O.quant_params(np.array([[0.0, 0.0]]), 2)
+    assert s[0] == pytest.approx(2 / 3) and z[0] == 2.0
+    # round half to even on codes: t = 0.5 -> 0, 2.5 -> 2
+    q, _, _ = O.rtn(np.array([[0.5, 2.5]]), np.array([1.0]), np.array([0.0]), 2)
+    np.testing.assert_array_equal(q, [[0, 2]])
+    # clamp to [0, 2^b - 1]
+    q, _, _ = O.rtn(np.array([[-3.0, 9.0]]), np.array([1.0]), np.array([0.0]), 2)
+    np.testing.assert_array_equal(q, [[0, 3]])
+
+
+# --------------------------------------------------------- GPTQ loop
+
+
+def test_gptq_hand_worked_obs():
+    g = gold("obs_1x2.json")
+    R, _ = O.chol_inv_upper(np.array(g["H"]))
+    out = O.gptq(np.array(g["W"]), R, [0, 1], g["bits"], -1)
+    np.testing.assert_array_equal(out["codes"], g["codes"])
+    np.testing.assert_allclose(out["What"], g["What"], atol=1e-15)
+    np.testing.assert_allclose(out["pre"], g["pre_round"], rtol=1e-14)
+
+
+@pytest.mark.parametrize("group", [-1, 4])
+def test_gptq_identity_hessian_is_rtn(group):
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((6, 8))
+    out = O.gptq(W, np.eye(8), np.arange(8), 3, group)
+    if group <= 0:
+        s, z = O.quant_params(W, 3)
+        q, d, _ = O.rtn(W, s, z, 3)
+    else:
+        qs, ds = [], []
+        for c in range(0, 8, group):
+            s, z = O.quant_params(W[:, c:c + group], 3)
+            q_, d_, _ = O.rtn(W[:, c:c + group], s, z, 3)
+            qs.append(q_); ds.append(d_)
+        q, d = np.hstack(qs), np.hstack(ds)
+    np.testing.assert_array_equal(out["codes"], q)
+    np.testing.assert_allclose(out["What"], d, atol=1e-15)
+
+
+def test_gptq_ties_round_half_even_and_natural_order_outputs():
+    # R = I: no compensation, so the loop is RTN.  t = 2.5 must round to 2
+    # (half to even); with a processing order that is not an involution the
+    # returned codes must still be in natural column order
+    W = np.array([[-1.0, 2.0, 1.5, 0.25], [0.3, -0.6, 0.9, 0.0]])
+    perm = np.array([2, 0, 3, 1])
+    out = O.gptq(W, np.eye(4), perm, 2, -1)
+    s, z = O.quant_params(W, 2)
+    q, d, t = O.rtn(W, s, z, 2)
+    assert t[0, 2] == 2.5 and q[0, 2] == 2
+    np.testing.assert_array_equal(out["codes"], q)
+    np.testing.assert_allclose(out["What"], d, atol=1e-15)
+    np.testing.assert_allclose(out["pre"], t, atol=1e-15)
+
+
+def _obs_full_kronecker(W, HX, HG, bits):
+    """Sequential OBS with the explicit (mn x mn) Hessian H_X (x) H_G: each step
+    fixes the m entries of one column jointly and moves the still-free
+    coordinates by -Hinv[:, S] Hinv[S, S]^-1 (w_S - q_S); the inverse over the
+    free set is refreshed by a Schur complement.  Per-channel grid."""
+    m, n = W.shape
+    maxq = 2 ** bits - 1
+    scale, zero = O.quant_params(W, bits)
+    w = W.reshape(-1, order="F").copy()          # vec, column stacking
+    Hinv = np.linalg.inv(np.kron(HX, HG))
+    free = list(range(m * n))
+    codes = np.zeros((m, n))
+    for j in range(n):
+        S = [j * m + i for i in range(m)]
+        q = np.clip(np.rint(w[S] / scale + zero), 0, maxq)
+        codes[:, j] = q
+        wq = scale * (q - zero)
+        pos = [free.index(s) for s in S]
+        A = Hinv[:, pos]
+        delta = -A @ np.linalg.solve(Hinv[np.ix_(pos, pos)], w[S] - wq)
+        w[free] += delta
+        w[S] = wq
+        keep = [p for p in range(len(free)) if p not in pos]
+        Hinv = Hinv[np.ix_(keep, keep)] - Hinv[np.ix_(keep, pos)] @ np.linalg.solve(
+            Hinv[np.ix_(pos, pos)], Hinv[np.ix_(pos, keep)])
+        free = [free[p] for p in keep]
+    return codes, w.reshape((m, n), order="F")
+
+
+@pytest.mark.parametrize("seed", [13, 14, 15])
+def test_hg_cancels_proposition1_brute_force(seed):
+    # Proposition 1: with the full Kronecker Hessian the column update does not
+    # depend on H_G, so the H_X-only loop gives the same codes and weights
+    rng = np.random.default_rng(seed)
+    m, n, bits = 3, 5, 2
+    W = rng.standard_normal((m, n))
+    HX = rand_spd(rng, n, 30.0)
+    HG = rand_spd(rng, m, 1e3)
+    codes_k, w_k = _obs_full_kronecker(W, HX, HG, bits)
+    R, _ = O.chol_inv_upper(HX)
+    out = O.gptq(W, R, np.arange(n), bits, -1)
+    np.testing.assert_array_equal(out["codes"], codes_k)
+    np.testing.assert_allclose(out["What"], w_k, atol=1e-12)
+
+
+def test_gptq_ldl_identity_and_bound():
+    # Delta W = E R (processing order), hence for any H_G:
+    # tr(H_G dW H dW^T) = sum_j e_j^T H_G e_j  (H = (R^T R)^-1); with no clamp
+    # the H_G = I loss is at most 1/4 sum_j sum_r scale_r^2 / R_jj^2 (Table 9's
+    # GPTQ-LDLQ form with tr(D))
+    rng = np.random.default_rng(16)
+    m, n, bits = 5, 16, 4
+    W = rng.standard_normal((m, n)) * 0.1
+    H = O.damp(O.gram(rng.standard_normal((64, n)) * rng.uniform(0.2, 3.0, n)), 0.01)
+    perm = O.act_order_perm(H)
+    Hp = H[np.ix_(perm, perm)]
+    R, _ = O.chol_inv_upper(Hp)
+    out = O.gptq(W, R, perm, bits, -1)
+    dW = (W - out["What"])[:, perm]
+    np.testing.assert_allclose(dW, out["E"] @ R, atol=1e-12)
+    HG = rand_spd(rng, m, 100.0)
+    lhs = O.proxy_loss(dW, Hp, HG)
+    rhs = float(np.sum(out["E"] * (HG @ out["E"])))
+    assert lhs == pytest.approx(rhs, rel=1e-9)
+    pre = out["pre"]
+    if np.all((pre >= -0.5) & (pre <= 2 ** bits - 0.5)):
+        bound = 0.25 * np.sum(out["scales"][:, 0] ** 2) * np.sum(1.0 / np.diag(R) ** 2)
+        assert O.proxy_loss(dW, Hp, np.eye(m)) <= bound * (1 + 1e-12)
+
+
+def test_gptq_exhaustive_2x4_two_bits():
+    # exhaustive search over all 4^8 grid codes bounds the compensated loss
+    rng = np.random.default_rng(17)
+    m, n, bits = 2, 4, 2
+    W = rng.standard_normal((m, n))
+    HX = O.damp(rand_spd(rng, n, 20.0), 0.01)
+    HG = rand_spd(rng, m, 10.0)
+    R, _ = O.chol_inv_upper(HX)
+    out = O.gptq(W, R, np.arange(n), bits, -1)
+    scale, zero = O.quant_params(W, bits)
+    best = np.inf
+    for cs in itertools.product(range(4), repeat=m * n):
+        q = np.array(cs, dtype=float).reshape(m, n)
+        best = min(best, O.proxy_loss(W - scale[:, None] * (q - zero[:, None]), HX, HG))
+    loss_gptq = O.proxy_loss(W - out["What"], HX, HG)
+    _, d_rtn, _ = O.rtn(W, scale, zero, bits)
+    assert best <= loss_gptq + 1e-12
+    assert best <= O.proxy_loss(W - d_rtn, HX, HG) + 1e-12
+    # the codes GPTQ returns are on the grid
+    np.testing.assert_allclose(out["What"], scale[:, None] * (out["codes"] - zero[:, None]), atol=1e-15)
+
+
+def test_gptq_group_params_from_compensated_values():
+    # Group parameters are taken when the group's first column is reached, from
+    # the values as compensated so far.  One row, 1 bit, group 2, R = I except
+    # R[0, 2] = 0.5; by hand: group 0 [0.3, 1.0] -> scale 1, zero 0; column 0
+    # rounds to 0 with error e = 0.3, moving w2 by -0.15 to 0.25; group 1 is then
+    # [0.25, 0.2] -> scale 0.25 (the uncompensated values would give 0.4);
+    # column 3: t = 0.8 -> code 1.
+    W = np.array([[0.3, 1.0, 0.4, 0.2]])
+    R = np.eye(4)
+    R[0, 2] = 0.5
+    out = O.gptq(W, R, np.arange(4), 1, 2)
+    np.testing.assert_array_equal(out["codes"], [[0, 1, 1, 1]])
+    np.testing.assert_allclose(out["scales"], [[1.0, 0.25]], rtol=1e-15)
+    np.testing.assert_allclose(out["zeros"], [[0.0, 0.0]])
+    np.testing.assert_allclose(out["What"], [[0.0, 1.0, 0.25, 0.25]], rtol=1e-15)
+    np.testing.assert_allclose(out["pre"][0, 3], 0.8, rtol=1e-14)
+
+
+# -------------------------------------------------- sensitivity, bits
+
+
+def test_sensitivity_trace_of_kronecker():
+    rng = np.random.default_rng(18)
+    HX, HG = rand_spd(rng, 5), rand_spd(rng, 3)
+    trx, trg, s = O.sensitivity(HX, HG)
+    assert s == pytest.approx(np.trace(np.kron(HX, HG)), rel=1e-13)
+    assert trx == pytest.approx(np.trace(HX), rel=1e-15)
+
+
+def test_allocation_worked_example():
+    g = gold("allocation_llama3_8b_block.json")
+    bits = O.allocate_bits(g["scores"], g["n_params"], g["bmin"], g["bmax"], g["budget_bits"])
+    assert bits == g["bits"]
+    n = np.array(g["n_params"])
+    assert int(np.sum(n * np.array(bits))) == g["budget_bits"]
+
+
+def test_allocation_invariants():
+    rng = np.random.default_rng(19)
+    for _ in range(50):
+        L = int(rng.integers(1, 9))
+        n = rng.integers(1, 1000, size=L)
+        sc = rng.random(L)
+        budget = int(rng.integers(2 * n.sum(), 4 * n.sum() + 1))
+        b = np.array(O.allocate_bits(sc, n, 2, 4, budget))
+        assert np.all((b >= 2) & (b <= 4))
+        assert int(np.sum(b * n)) <= budget
+        # maximality: no single +1 still fits
+        used = int(np.sum(b * n))
+        for i in range(L):
+            assert b[i] == 4 or used + n[i] > budget
+        # the most sensitive sublayer is raised as far as the budget allows
+        top = int(np.argmax(sc))
+        assert b[top] == min(4, 2 + (budget - 2 * int(n.sum())) // int(n[top]))
+    with pytest.raises(ValueError):
+        O.allocate_bits([1.0, 2.0], [10, 10], 2, 4, 39)
