@@ -1,0 +1,264 @@
+"""Benchmark of the KronQ per-sublayer quantization path on one MI355X.
+
+One step = the whole hot path for one sublayer, inputs resident in HBM:
+  H_X = X^T X / N, H_G = G^T G / N            (kronq_gram x 2, bf16 matrix cores)
+  BiIP: S_G rescale + Hadamard both sides      (kronq_biip_rotate)
+  sensitivity tr(H_X') tr(H_G')                (kronq_sensitivity)
+  damping + inverse Cholesky factor            (kronq_chol_inv, synchronizes)
+  column-wise OBS quantize-and-compensate      (kronq_gptq_quantize)
+  bit allocation                               (kronq_allocate_bits, host)
+Workload: Llama-2-7B q_proj shape -- W 4096 x 4096, X and G 262144 x 4096 bf16
+(128 sequences x 2048 tokens), 2-bit asymmetric groups of 128, Hadamard 4096 on
+both sides, alpha 0.25, damping 1% of the mean diagonal.  Synthetic inputs
+(heavy-tailed activations with outlier channels, log-normal gradient channel
+scales) stand in for the calibration set.
+
+Prints one JSON line.  `value` is the wall time of one sublayer quantization
+(seconds, lower is better).  Per-stage times come from HIP events recorded on
+the stream the kernels run on; `roofline` is for the Gram kernel call.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_TFLOPS = 157.3
+PEAK_FP64_TFLOPS = 78.6
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="approximate CPU seconds for the oracle baseline sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gram_bf16_llama2_7b_q_proj_traffic.json"))
+    return ap.parse_args()
+
+
+def cpu_baseline(w, X, G, W, budget_s):
+    """The oracle (numpy float64, as it stands) on a bounded sample of the same
+    workload, extrapolated to one sublayer:
+      Gram: a token prefix of X and of G (the Gram is linear in N),
+      BiIP: full W, H_X, H_G rotations (sample-free),
+      damping + inverse Cholesky: full,
+      column loop: a row sample (rows are independent), all columns."""
+    import synth
+    from oracle import kronq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    s = w.sub("q_proj")
+    N = w.N
+    t0 = time.perf_counter()
+    Np = 4096
+    xs = synth.bf16_to_f64(X[:Np])
+    gs = synth.bf16_to_f64(G[:Np])
+    t_g0 = time.perf_counter()
+    HXs = O.gram(xs)
+    HGs = O.gram(gs)
+    t_gram = (time.perf_counter() - t_g0) * (N / Np)
+    # BiIP: the three 4096 x 4096 rotations cost the same; W's is timed, x3
+    t_b0 = time.perf_counter()
+    Wp, _, _, sg = O.biip(synth.bf16_to_f64(W), None, HGs, w.in_signs("x"), s.in_block,
+                          w.out_signs("q_proj"), s.out_block, w.alpha)
+    t_biip = 3.0 * (time.perf_counter() - t_b0)
+    t_s0 = time.perf_counter()
+    O.sensitivity(HXs, HGs)
+    t_sens = time.perf_counter() - t_s0
+    t_c0 = time.perf_counter()
+    perm, H = O.prepare_hessian(HXs, w.lam, s.act_order)
+    R, _ = O.chol_inv_upper(H)
+    t_chol = time.perf_counter() - t_c0
+    rows = 16
+    t_q0 = time.perf_counter()
+    O.gptq(Wp[:rows], R, perm, s.bits, s.group)
+    t_gptq = (time.perf_counter() - t_q0) * (s.m / rows)
+    total = t_gram + t_biip + t_sens + t_chol + t_gptq
+    wall = time.perf_counter() - t0
+    return {
+        "value": total, "unit": "s", "cores": int(cores), "kind": "oracle",
+        "sample": ("Gram on the first %d of %d tokens of X and G, scaled x%d; BiIP rotation of W "
+                   "timed and scaled x3 (H_X, H_G cost the same); sensitivity and damped inverse "
+                   "Cholesky in full; column loop on %d of %d rows, scaled x%d; float64 numpy; "
+                   "%.1f s of host time") % (Np, N, N // Np, rows, s.m, s.m // rows, wall),
+        "stages_s": {"gram_x_g": t_gram, "biip": t_biip, "sensitivity": t_sens, "chol_inv": t_chol,
+                     "gptq": t_gptq},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import post_quantization_02_amd as kq
+    import synth
+    from synth import workloads as WL
+
+    w = WL.C2
+    s = w.sub("q_proj")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs", w.name)
+    t0 = time.perf_counter()
+    X = w.gen_x("x")
+    G = w.gen_g("q_proj")
+    W = w.gen_w("q_proj")
+    t_gen = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
+    Gd = torch.from_numpy(G.view(np.int16)).view(torch.bfloat16).to(dev)
+    W0 = torch.from_numpy(synth.bf16_to_f32(W)).to(dev)
+    si = torch.from_numpy(w.in_signs("x")).to(dev)
+    so = torch.from_numpy(w.out_signs("q_proj")).to(dev)
+    torch.cuda.synchronize()
+    t_h2d = time.perf_counter() - t0
+    m, n, N = s.m, s.n, w.N
+
+    HX = torch.empty((n, n), dtype=torch.float32, device=dev)
+    HG = torch.empty((m, m), dtype=torch.float32, device=dev)
+    Wk = torch.empty_like(W0)
+    sg = torch.empty(m, dtype=torch.float32, device=dev)
+    tr = torch.empty(3, dtype=torch.float64, device=dev)
+    R = torch.empty((n, n), dtype=torch.float32, device=dev)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    What = torch.empty((m, n), dtype=torch.float32, device=dev)
+    codes = torch.empty((m, n), dtype=torch.uint8, device=dev)
+    ng = n // s.group
+    scales = torch.empty((m, ng), dtype=torch.float32, device=dev)
+    zeros = torch.empty((m, ng), dtype=torch.float32, device=dev)
+    lib = kq.load()
+    ws_g = torch.empty(max(1, lib.kronq_gram_ws(N, n, kq.KRONQ_BF16)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, lib.kronq_biip_ws(m, n)), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, lib.kronq_chol_inv_ws(n)), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(max(1, lib.kronq_gptq_ws(m, n)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["gram_x", "gram_g", "biip", "sensitivity", "chol_inv", "gptq", "allocate"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kq.kronq_gram(Xd, HX, ws=ws_g)
+        if ev is not None:
+            ev[1].record(stream)
+        kq.kronq_gram(Gd, HG, ws=ws_g)
+        if ev is not None:
+            ev[2].record(stream)
+        Wk.copy_(W0)
+        kq.kronq_biip_rotate(Wk, HX, HG, si, s.in_block, so, s.out_block, w.alpha, sg, ws=ws_b)
+        if ev is not None:
+            ev[3].record(stream)
+        kq.kronq_sensitivity(HX, HG, out=tr)
+        if ev is not None:
+            ev[4].record(stream)
+        kq.kronq_chol_inv(HX, w.lam, s.act_order, perm=perm, R=R, ws=ws_c)
+        if ev is not None:
+            ev[5].record(stream)
+        kq.kronq_gptq_quantize(Wk, R, perm, s.bits, s.group, What=What, ws=ws_q, codes=codes,
+                               scales=scales, zeros=zeros)
+        if ev is not None:
+            ev[6].record(stream)
+        score = float(tr[2].item())
+        bits = kq.kronq_allocate_bits([score], [m * n], s.bits, s.bits, s.bits * m * n)
+        if ev is not None:
+            ev[7].record(stream)
+        return bits
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    log("timing", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+        log("  step", k + 1, "done")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                for i, nm in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+
+    gram_flops = float(N) * n * (n + 1)        # one factor, unique triangle
+    gram_ms = 0.5 * (stage_ms["gram_x"] + stage_ms["gram_g"])
+    gram_tflops = gram_flops / (gram_ms * 1e-3) / 1e12
+    fwht_bytes = 16.0 * (m * n + n * n + m * m)   # two one-sided passes, 8 B per element each
+    fwht_gbs = fwht_bytes / (stage_ms["biip"] * 1e-3) / 1e9
+    chol_flops = 2.0 * n ** 3 / 3
+    gptq_flops = float(m) * n * n
+    gptq_bytes = 9.0 * m * n + 2.0 * n * n
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f)
+            traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "sublayer quantize wall time (s) + Gram TFLOP/s & FWHT GB/s vs MI355X peak",
+        "value": ms_step / 1e3,
+        "unit": "s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": N, "m": m, "n": n, "x_dtype": "bf16", "bits": s.bits,
+                   "group": s.group, "hadamard_in": s.in_block, "hadamard_out": s.out_block,
+                   "alpha": w.alpha, "damp": w.lam, "act_order": s.act_order},
+        "stage_ms": stage_ms,
+        "stage_dtypes": {"gram": "bf16 products, fp32 accumulate", "biip": "fp32",
+                         "chol_inv": "fp32 (diagonal blocks fp64)", "gptq": "fp64",
+                         "sensitivity": "fp64 sums"},
+        "gram_tflops": gram_tflops,
+        "gram_frac_bf16_peak": gram_tflops / PEAK_BF16_TFLOPS,
+        "fwht_gbs": fwht_gbs,
+        "fwht_frac_hbm_peak": fwht_gbs / PEAK_HBM_GBS,
+        "chol_tflops_fp32": chol_flops / (stage_ms["chol_inv"] * 1e-3) / 1e12,
+        "gptq_tflops_fp64": gptq_flops / (stage_ms["gptq"] * 1e-3) / 1e12,
+        "gptq_min_bytes_gbs": gptq_bytes / (stage_ms["gptq"] * 1e-3) / 1e9,
+        "roofline": {"kernel": "kronq_gram call (gram_bf16_kernel + gram_finalize_kernel)",
+                     "bound": "mfma", "achieved": gram_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gram_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic},
+        "input_gen_s": t_gen,
+        "h2d_s": t_h2d,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        out["cpu_baseline"] = cpu_baseline(w, X, G, W, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * kronq.h -- C ABI of the KronQ per-sublayer quantization path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (KronQ, arXiv 2607.07964, "KronQ: LLM Quantization via
+ * Kronecker-Factored Hessian"; pages cited below by name and section):
+ *   1. Kronecker factors H_X = X^T X / N and H_G = G^T G / N of the K-FAC
+ *      Hessian H ~ H_X (x) H_G            (hyper.ai summary, Method)
+ *   2. bidirectional incoherence processing: output rescale S_G and randomized
+ *      Hadamard transforms on both sides  (hyper.ai summary, Method; Pith
+ *      review, Eq. 11-12 and the proof of Theorem 1)
+ *   3. damping and the inverse Cholesky factor of H_X (Pith review, Algorithm 2)
+ *   4. the column-wise OBS quantize-and-compensate loop with H_X alone, since
+ *      H_G cancels                       (Pith review, Proposition 1)
+ *   5. the sensitivity tr(H_X) tr(H_G) and the bit allocation it drives
+ *                                         (hyper.ai summary, Method, Eq. 14)
+ *
+ * Conventions for every call:
+ *   - All matrices are row-major; leading dimensions are in elements.
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     never allocates, frees or retains caller memory.  Calls that need scratch
+ *     memory take a caller-provided device workspace `ws` of at least the size
+ *     returned by the matching *_ws() query (KRONQ_EWORKSPACE otherwise).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls are
+ *     asynchronous on `stream` except kronq_chol_inv, which synchronizes it.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid argument returns KRONQ_EINVAL and launches nothing.  HIP runtime
+ *     failures return KRONQ_EHIP.  kronq_last_error() gives a readable detail
+ *     of the last failure on the calling thread.
+ *   - The library keeps no state between calls: calls on different streams may
+ *     run concurrently as long as their buffers do not overlap.
+ */
+#ifndef KRONQ_H
+#define KRONQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kronq_status;
+#define KRONQ_OK 0
+#define KRONQ_EINVAL 1         /* invalid argument (nothing launched) */
+#define KRONQ_ENOTPD 2         /* damped H not positive definite */
+#define KRONQ_EHIP 3           /* HIP runtime error */
+#define KRONQ_EWORKSPACE 4     /* workspace smaller than the *_ws() size */
+#define KRONQ_EUNSUPPORTED 5   /* valid request this build does not implement */
+
+#define KRONQ_F32 0            /* element type codes for kronq_gram */
+#define KRONQ_BF16 1
+
+/* One side of a randomized (block) Hadamard transform T = (I_b (x) H_block)
+ * diag(signs) / sqrt(block) on a dimension dim = b * block; block is a power of
+ * two (Sylvester order) between 1 and 32768; signs is a device array of dim
+ * floats, each +1.0f or -1.0f (the random draw is the caller's input). */
+typedef struct {
+  int64_t dim;
+  int64_t block;
+  const float* signs;
+} kronq_had;
+
+/* Quantizer of the column loop: asymmetric uniform grid with 2^bits levels
+ * (bits in 1..8); group <= 0 means one grid per output row (per-channel),
+ * otherwise one grid per `group` consecutive columns in processing order
+ * (group must divide n). */
+typedef struct {
+  int32_t bits;
+  int32_t group;
+} kronq_qcfg;
+
+const char* kronq_status_string(kronq_status s);
+const char* kronq_last_error(void);
+int32_t kronq_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Kronecker factor (hyper.ai summary, Method: H_X = E[x x^T], H_G = E[g g^T]
+ * under the K-FAC factorization).
+ *   H <- scale * A^T A + beta * H
+ * A     : N x d device matrix, row-major with leading dimension lda >= d, of
+ *         element type dtype (KRONQ_BF16 or KRONQ_F32); one token per row.
+ * H     : d x d device fp32, leading dimension ldh >= d; both triangles are
+ *         written (full symmetric storage).  With beta == 0, H is not read.
+ * scale : typically 1/N; beta = 1 accumulates token chunks.
+ * bf16 products are exact in fp32 and accumulate in fp32 on the bf16 matrix
+ * cores; fp32 input uses the fp32 matrix cores.
+ * ws    : device workspace of kronq_gram_ws(N, d, dtype) bytes (may be 0).
+ * Requires N >= 1, d >= 1, A and H 16-byte aligned, lda a multiple of 8
+ * (bf16) or 4 (f32).
+ * ------------------------------------------------------------------------- */
+size_t kronq_gram_ws(int64_t N, int64_t d, int32_t dtype);
+kronq_status kronq_gram(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda, float* H,
+                        int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Bidirectional incoherence processing (hyper.ai summary, Method: rescale on
+ * the output side by S_G, then orthogonal transforms; Pith review, proof of
+ * Theorem 1: W' = U W V^T, H_G' = U H_G U^T, H_X' = V H_X V^T).
+ *   sg[i] = HG[i][i]^alpha  (1 where HG[i][i] <= 0; all 1 when alpha == 0)
+ *   W  (m x n) <- U diag(sg) W V^T
+ *   HX (n x n) <- V HX V^T
+ *   HG (m x m) <- U diag(sg)^-1 HG diag(sg)^-1 U^T
+ * with U from out_side (dim m) and V from in_side (dim n), in place, fp32.
+ * HX may be NULL (skipped, e.g. when sublayers share an already rotated H_X);
+ * HG may be NULL only when alpha == 0 (then sg is all ones).  sg (device,
+ * m floats) may be NULL.  W and HX/HG must not overlap.
+ * ws : kronq_biip_ws(m, n) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_biip_ws(int64_t m, int64_t n);
+kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
+                               int64_t ldhx, float* HG, int64_t ldhg, const kronq_had* in_side,
+                               const kronq_had* out_side, float alpha, float* sg, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Act-order, damping and inverse Cholesky factor (Pith review, Algorithm 2:
+ * the damped H_X is H_X + lambda mean(diag H_X) I and the loop uses its
+ * inverse Cholesky factor; GitHub README, flag --act_order).
+ *   perm  : if act_order, the stable descending order of diag(H) (ties to the
+ *           lower index); else the identity.  perm[j] = original column
+ *           processed at step j.  Device int32[n].
+ *   Hd    = P (H + lambda * mean(diag H) * I) P^T
+ *   R     : upper triangular, positive diagonal, R^T R = Hd^-1 (fp32, lower
+ *           triangle written as zeros).  Device, leading dimension ldr.
+ * H is read only (n x n fp32 device, symmetric).  Computed in fp32 on the
+ * matrix cores (blocked factorization of the reversed matrix, then a blocked
+ * triangular inverse).
+ * info  : host pointer; -1 on success, else the index (in processing order) of
+ *         the first non-positive pivot, with KRONQ_ENOTPD returned.
+ * Synchronizes `stream` before returning.
+ * ws    : kronq_chol_inv_ws(n) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_chol_inv_ws(int64_t n);
+kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda,
+                            int32_t act_order, int32_t* perm, float* R, int64_t ldr,
+                            int64_t* info, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Column-wise OBS quantize-and-compensate with H_X alone (Pith review,
+ * Proposition 1: H_G cancels from the column update; Algorithm 2: lazy
+ * batches of columns).  For every row independently and for j = 0..n-1 in
+ * processing order (column c = perm[j]):
+ *   t = w[c] / scale + zero;  q = clamp(round-half-even(t), 0, 2^bits - 1)
+ *   wq = scale * (q - zero);  e = (w[c] - wq) / R[j][j]
+ *   w[perm[k]] -= e * R[j][k]   for k > j
+ * Grid parameters: xmin = min(0, min v), xmax = max(0, max v) (a degenerate
+ * range becomes [-1, 1]), scale = (xmax - xmin) / (2^bits - 1),
+ * zero = round-half-even(-xmin / scale), with v the whole initial row
+ * (per-channel) or the current compensated values of the group when its first
+ * column is reached.  The loop runs in fp64 (inputs fp32).
+ * W        : m x n fp32 device, natural column order (read only).
+ * R        : n x n fp32 device upper factor in processing order.
+ * perm     : device int32[n] or NULL (identity).
+ * codes    : m x n uint8 device, natural column order, leading dimension n.
+ * scales, zeros : m x ngroups fp32 device (ngroups = 1 per-channel, else
+ *            n / group), groups in processing order, leading dimension ngroups.
+ * What     : m x n fp32 device dequantized weights, natural order, leading
+ *            dimension n; may be NULL.  May alias W when ldw == n.
+ * pre_round: m x n fp32 device t values (natural order) or NULL.
+ * ws       : kronq_gptq_ws(m, n) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_gptq_ws(int64_t m, int64_t n);
+kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t ldw,
+                                 const float* R, int64_t ldr, const int32_t* perm,
+                                 const kronq_qcfg* q, uint8_t* codes, float* scales,
+                                 float* zeros, float* What, float* pre_round, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sensitivity (hyper.ai summary, Method, Eq. 14: s = tr(H_G) tr(H_X) computed
+ * after BiIP).  out3 (device, 3 doubles) = { tr(HX), tr(HG), tr(HX) * tr(HG) },
+ * diagonals summed in fp64.  HX is n x n, HG is m x m (fp32 device).
+ * ------------------------------------------------------------------------- */
+kronq_status kronq_sensitivity(const float* HX, int64_t n, int64_t ldhx, const float* HG,
+                               int64_t m, int64_t ldhg, double* out3, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Bit allocation (hyper.ai summary, Method: higher bit-widths for larger
+ * s; GitHub README, --inter_layer_mp: upgrade the most sensitive sublayers by
+ * +1 bit).  Host only, pure, deterministic.  Every sublayer starts at bmin;
+ * sublayers are visited by descending score (ties: lower index first) and each
+ * is raised one bit at a time while it is below bmax and
+ * sum(bits * n_params) stays <= budget_bits.  scores (L doubles), n_params
+ * (L int64 > 0) and bits_out (L int32) are host arrays.
+ * KRONQ_EINVAL if L < 1, bmin < 1, bmax < bmin, a score is NaN or
+ * budget_bits < bmin * sum(n_params).
+ * ------------------------------------------------------------------------- */
+kronq_status kronq_allocate_bits(int32_t L, const double* scores, const int64_t* n_params,
+                                 int32_t bmin, int32_t bmax, int64_t budget_bits,
+                                 int32_t* bits_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KRONQ_H */

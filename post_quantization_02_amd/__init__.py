@@ -1,0 +1,249 @@
+"""KronQ per-sublayer quantization path on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libkronq.so (the C ABI declared in include/kronq.h):
+argument marshalling only -- every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory (tensors, workspaces) and the
+current HIP stream.  The library must be built first
+(``python -m post_quantization_02_amd.build``); importing this module without
+it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkronq.so")
+
+KRONQ_OK, KRONQ_EINVAL, KRONQ_ENOTPD, KRONQ_EHIP, KRONQ_EWORKSPACE, KRONQ_EUNSUPPORTED = range(6)
+KRONQ_F32, KRONQ_BF16 = 0, 1
+
+# every entry point declared in include/kronq.h
+EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gram_ws",
+           "kronq_gram", "kronq_biip_ws", "kronq_biip_rotate", "kronq_chol_inv_ws",
+           "kronq_chol_inv", "kronq_gptq_ws", "kronq_gptq_quantize", "kronq_sensitivity",
+           "kronq_allocate_bits")
+
+
+class KronqError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__("%s: status %d (%s)" % (where, status, detail))
+        self.status = status
+
+
+class Had(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int64), ("block", ctypes.c_int64), ("signs", ctypes.c_void_p)]
+
+
+class QCfg(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libkronq.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError("libkronq.so not built: run `python -m post_quantization_02_amd.build` (%s)" % path)
+    lib = ctypes.CDLL(path)
+    i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    lib.kronq_status_string.argtypes = [i32]
+    lib.kronq_status_string.restype = ctypes.c_char_p
+    lib.kronq_last_error.argtypes = []
+    lib.kronq_last_error.restype = ctypes.c_char_p
+    lib.kronq_version.restype = i32
+    lib.kronq_gram_ws.argtypes = [i64, i64, i32]
+    lib.kronq_gram_ws.restype = sz
+    lib.kronq_gram.argtypes = [vp, i32, i64, i64, i64, vp, i64, f32, f32, vp, sz, vp]
+    lib.kronq_gram.restype = i32
+    lib.kronq_biip_ws.argtypes = [i64, i64]
+    lib.kronq_biip_ws.restype = sz
+    lib.kronq_biip_rotate.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, ctypes.POINTER(Had),
+                                      ctypes.POINTER(Had), f32, vp, vp, sz, vp]
+    lib.kronq_biip_rotate.restype = i32
+    lib.kronq_chol_inv_ws.argtypes = [i64]
+    lib.kronq_chol_inv_ws.restype = sz
+    lib.kronq_chol_inv.argtypes = [vp, i64, i64, f32, i32, vp, vp, i64, ctypes.POINTER(i64), vp, sz, vp]
+    lib.kronq_chol_inv.restype = i32
+    lib.kronq_gptq_ws.argtypes = [i64, i64]
+    lib.kronq_gptq_ws.restype = sz
+    lib.kronq_gptq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.POINTER(QCfg), vp, vp,
+                                        vp, vp, vp, vp, sz, vp]
+    lib.kronq_gptq_quantize.restype = i32
+    lib.kronq_sensitivity.argtypes = [vp, i64, i64, vp, i64, i64, vp, vp]
+    lib.kronq_sensitivity.restype = i32
+    lib.kronq_allocate_bits.argtypes = [i32, vp, vp, i32, i32, i64, vp]
+    lib.kronq_allocate_bits.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(st: int, where: str):
+    if st != KRONQ_OK:
+        lib = load()
+        raise KronqError(st, where, lib.kronq_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ws(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s" % (name, dtype))
+    if t.dim() == 2 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major (unit column stride)" % name)
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+# ---------------------------------------------------------------- calls
+
+def kronq_gram(A: torch.Tensor, H: torch.Tensor | None = None, scale: float | None = None,
+               beta: float = 0.0, stream=None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """H <- scale * A^T A + beta * H (A: N x d bf16 or fp32; H: d x d fp32)."""
+    lib = load()
+    _dev(A, "A")
+    if A.dtype == torch.bfloat16:
+        dt = KRONQ_BF16
+    elif A.dtype == torch.float32:
+        dt = KRONQ_F32
+    else:
+        raise ValueError("A must be bfloat16 or float32")
+    N, d = A.shape
+    if H is None:
+        H = torch.empty((d, d), dtype=torch.float32, device=A.device)
+    _dev(H, "H", torch.float32)
+    scale = 1.0 / N if scale is None else scale
+    need = lib.kronq_gram_ws(N, d, dt)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, A.device)
+    _check(lib.kronq_gram(_ptr(A), dt, N, d, _ld(A), _ptr(H), _ld(H), scale, beta, _ptr(ws),
+                          need, _stream(stream)), "kronq_gram")
+    return H
+
+
+def kronq_biip_rotate(W: torch.Tensor, HX: torch.Tensor | None, HG: torch.Tensor | None,
+                      in_signs: torch.Tensor, in_block: int, out_signs: torch.Tensor,
+                      out_block: int, alpha: float, sg: torch.Tensor | None = None,
+                      stream=None, ws: torch.Tensor | None = None) -> torch.Tensor | None:
+    """In place: W <- U S_G W V^T, HX <- V HX V^T, HG <- U S_G^-1 HG S_G^-1 U^T."""
+    lib = load()
+    _dev(W, "W", torch.float32)
+    m, n = W.shape
+    for t, nm in ((HX, "HX"), (HG, "HG"), (sg, "sg"), (in_signs, "in_signs"), (out_signs, "out_signs")):
+        if t is not None:
+            _dev(t, nm, torch.float32)
+    hin = Had(n, in_block, _ptr(in_signs))
+    hout = Had(m, out_block, _ptr(out_signs))
+    need = lib.kronq_biip_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, W.device)
+    _check(lib.kronq_biip_rotate(_ptr(W), m, n, _ld(W), _ptr(HX), _ld(HX) if HX is not None else n,
+                                 _ptr(HG), _ld(HG) if HG is not None else m, ctypes.byref(hin),
+                                 ctypes.byref(hout), alpha, _ptr(sg), _ptr(ws), need,
+                                 _stream(stream)), "kronq_biip_rotate")
+    return sg
+
+
+def kronq_chol_inv(H: torch.Tensor, lam: float, act_order: bool = False,
+                   perm: torch.Tensor | None = None, R: torch.Tensor | None = None, stream=None,
+                   ws: torch.Tensor | None = None):
+    """Returns (R, perm, info): R upper with R^T R = (P(H + lam mean(diag) I)P^T)^-1.
+    Raises KronqError (status KRONQ_ENOTPD, .info set) when not positive definite."""
+    lib = load()
+    _dev(H, "H", torch.float32)
+    n = H.shape[0]
+    if perm is None:
+        perm = torch.empty(n, dtype=torch.int32, device=H.device)
+    if R is None:
+        R = torch.empty((n, n), dtype=torch.float32, device=H.device)
+    need = lib.kronq_chol_inv_ws(n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, H.device)
+    info = ctypes.c_int64(-1)
+    st = lib.kronq_chol_inv(_ptr(H), n, _ld(H), lam, 1 if act_order else 0, _ptr(perm), _ptr(R),
+                            _ld(R), ctypes.byref(info), _ptr(ws), need, _stream(stream))
+    if st != KRONQ_OK:
+        err = KronqError(st, "kronq_chol_inv", lib.kronq_last_error().decode(errors="replace"))
+        err.info = info.value
+        raise err
+    return R, perm, info.value
+
+
+def kronq_gptq_quantize(W: torch.Tensor, R: torch.Tensor, perm: torch.Tensor | None, bits: int,
+                        group: int, What: torch.Tensor | None = None, want_pre: bool = False,
+                        stream=None, ws: torch.Tensor | None = None, codes=None, scales=None,
+                        zeros=None):
+    """Column-wise OBS loop.  Returns dict(codes, scales, zeros, What, pre)."""
+    lib = load()
+    _dev(W, "W", torch.float32)
+    _dev(R, "R", torch.float32)
+    m, n = W.shape
+    ng = 1 if group <= 0 else n // group
+    dev = W.device
+    if codes is None:
+        codes = torch.empty((m, n), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((m, ng), dtype=torch.float32, device=dev)
+    if zeros is None:
+        zeros = torch.empty((m, ng), dtype=torch.float32, device=dev)
+    if What is None:
+        What = torch.empty((m, n), dtype=torch.float32, device=dev)
+    pre = torch.empty((m, n), dtype=torch.float32, device=dev) if want_pre else None
+    q = QCfg(bits, group)
+    need = lib.kronq_gptq_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(lib.kronq_gptq_quantize(_ptr(W), m, n, _ld(W), _ptr(R), _ld(R), _ptr(perm),
+                                   ctypes.byref(q), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                   _ptr(What), _ptr(pre), _ptr(ws), need, _stream(stream)),
+           "kronq_gptq_quantize")
+    return dict(codes=codes, scales=scales, zeros=zeros, What=What, pre=pre)
+
+
+def kronq_sensitivity(HX: torch.Tensor, HG: torch.Tensor, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Device tensor of 3 doubles: tr(HX), tr(HG), product."""
+    lib = load()
+    _dev(HX, "HX", torch.float32)
+    _dev(HG, "HG", torch.float32)
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=HX.device)
+    _check(lib.kronq_sensitivity(_ptr(HX), HX.shape[0], _ld(HX), _ptr(HG), HG.shape[0], _ld(HG),
+                                 _ptr(out), _stream(stream)), "kronq_sensitivity")
+    return out
+
+
+def kronq_allocate_bits(scores, n_params, bmin: int, bmax: int, budget_bits: int) -> list:
+    """Host-only greedy allocation (see include/kronq.h)."""
+    import numpy as np
+    lib = load()
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    npar = np.ascontiguousarray(n_params, dtype=np.int64)
+    out = np.zeros(len(sc), dtype=np.int32)
+    _check(lib.kronq_allocate_bits(len(sc), sc.ctypes.data, npar.ctypes.data, bmin, bmax,
+                                   int(budget_bits), out.ctypes.data), "kronq_allocate_bits")
+    return [int(x) for x in out]

@@ -1,0 +1,212 @@
+// Host half of libkronq: argument validation, workspace checks, dispatch to the
+// kernel launchers, and the host-only bit allocator.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+
+#include "kronq_internal.h"
+
+namespace kronq {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+kronq_status fail(kronq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kronq_status hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return KRONQ_EHIP;
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static kronq_status check_had(const kronq_had* h, int64_t dim, const char* side) {
+  if (!h) return fail(KRONQ_EINVAL, "%s Hadamard spec is NULL", side);
+  if (h->dim != dim)
+    return fail(KRONQ_EINVAL, "%s Hadamard dim %lld != matrix dimension %lld", side,
+                (long long)h->dim, (long long)dim);
+  if (!pow2(h->block) || h->block > 32768 || dim % h->block)
+    return fail(KRONQ_EINVAL, "%s Hadamard block %lld must be a power of two <= 32768 dividing %lld",
+                side, (long long)h->block, (long long)dim);
+  if (!h->signs) return fail(KRONQ_EINVAL, "%s Hadamard signs are NULL", side);
+  return KRONQ_OK;
+}
+
+}  // namespace kronq
+
+using namespace kronq;
+
+extern "C" {
+
+const char* kronq_status_string(kronq_status s) {
+  switch (s) {
+    case KRONQ_OK: return "ok";
+    case KRONQ_EINVAL: return "invalid argument";
+    case KRONQ_ENOTPD: return "matrix not positive definite";
+    case KRONQ_EHIP: return "HIP runtime error";
+    case KRONQ_EWORKSPACE: return "workspace too small";
+    case KRONQ_EUNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+const char* kronq_last_error(void) { return g_err; }
+
+int32_t kronq_version(void) { return 1; }
+
+size_t kronq_gram_ws(int64_t N, int64_t d, int32_t dtype) {
+  if (N < 1 || d < 1 || (dtype != KRONQ_F32 && dtype != KRONQ_BF16)) return 0;
+  return gram_ws_bytes(N, d, dtype);
+}
+
+kronq_status kronq_gram(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda, float* H,
+                        int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!A || !H) return fail(KRONQ_EINVAL, "kronq_gram: NULL pointer");
+  if (dtype != KRONQ_F32 && dtype != KRONQ_BF16)
+    return fail(KRONQ_EINVAL, "kronq_gram: dtype %d", (int)dtype);
+  if (N < 1 || d < 1) return fail(KRONQ_EINVAL, "kronq_gram: N=%lld d=%lld", (long long)N, (long long)d);
+  if (lda < d || ldh < d) return fail(KRONQ_EINVAL, "kronq_gram: leading dimension below d");
+  if (!aligned(A, 16) || !aligned(H, 16))
+    return fail(KRONQ_EINVAL, "kronq_gram: A and H must be 16-byte aligned");
+  if ((dtype == KRONQ_BF16 && lda % 8) || (dtype == KRONQ_F32 && lda % 4))
+    return fail(KRONQ_EINVAL, "kronq_gram: lda must be a multiple of 16 bytes");
+  if (!std::isfinite(scale) || !std::isfinite(beta))
+    return fail(KRONQ_EINVAL, "kronq_gram: scale/beta not finite");
+  size_t need = gram_ws_bytes(N, d, dtype);
+  if (ws_bytes < need || (need && !ws))
+    return fail(KRONQ_EWORKSPACE, "kronq_gram: workspace %zu < %zu bytes", ws_bytes, need);
+  return gram_launch(A, dtype, N, d, lda, H, ldh, scale, beta, ws, ws_bytes, (hipStream_t)stream);
+}
+
+size_t kronq_biip_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return biip_ws_bytes(m, n);
+}
+
+kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
+                               int64_t ldhx, float* HG, int64_t ldhg, const kronq_had* in_side,
+                               const kronq_had* out_side, float alpha, float* sg, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!W) return fail(KRONQ_EINVAL, "kronq_biip_rotate: W is NULL");
+  if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "kronq_biip_rotate: bad W shape");
+  if (HX && ldhx < n) return fail(KRONQ_EINVAL, "kronq_biip_rotate: ldhx < n");
+  if (HG && ldhg < m) return fail(KRONQ_EINVAL, "kronq_biip_rotate: ldhg < m");
+  if (!std::isfinite(alpha)) return fail(KRONQ_EINVAL, "kronq_biip_rotate: alpha not finite");
+  if (alpha != 0.0f && !HG)
+    return fail(KRONQ_EINVAL, "kronq_biip_rotate: the output rescale needs HG");
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  st = check_had(out_side, m, "output-side");
+  if (st) return st;
+  size_t need = biip_ws_bytes(m, n);
+  if (ws_bytes < need || (need && !ws))
+    return fail(KRONQ_EWORKSPACE, "kronq_biip_rotate: workspace %zu < %zu bytes", ws_bytes, need);
+  return biip_launch(W, m, n, ldw, HX, ldhx, HG, ldhg, *in_side, *out_side, alpha, sg, ws, ws_bytes,
+                     (hipStream_t)stream);
+}
+
+size_t kronq_chol_inv_ws(int64_t n) {
+  if (n < 1) return 0;
+  return chol_ws_bytes(n);
+}
+
+kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda,
+                            int32_t act_order, int32_t* perm, float* R, int64_t ldr,
+                            int64_t* info, void* ws, size_t ws_bytes, void* stream) {
+  if (info) *info = -1;
+  if (!H || !R || !perm || !info) return fail(KRONQ_EINVAL, "kronq_chol_inv: NULL pointer");
+  if (n < 1 || ldh < n || ldr < n) return fail(KRONQ_EINVAL, "kronq_chol_inv: bad shape");
+  if (!(lambda >= 0.0f) || !std::isfinite(lambda))
+    return fail(KRONQ_EINVAL, "kronq_chol_inv: lambda must be finite and >= 0");
+  size_t need = chol_ws_bytes(n);
+  if (ws_bytes < need || (need && !ws))
+    return fail(KRONQ_EWORKSPACE, "kronq_chol_inv: workspace %zu < %zu bytes", ws_bytes, need);
+  return chol_launch(H, n, ldh, lambda, act_order ? 1 : 0, perm, R, ldr, info, ws, ws_bytes,
+                     (hipStream_t)stream);
+}
+
+size_t kronq_gptq_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return gptq_ws_bytes(m, n);
+}
+
+kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t ldw,
+                                 const float* R, int64_t ldr, const int32_t* perm,
+                                 const kronq_qcfg* q, uint8_t* codes, float* scales,
+                                 float* zeros, float* What, float* pre_round, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!W || !R || !q || !codes || !scales || !zeros)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: NULL pointer");
+  if (m < 1 || n < 1 || ldw < n || ldr < n)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bad shape");
+  if (q->bits < 1 || q->bits > 8)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bits %d outside 1..8", (int)q->bits);
+  if (q->group > 0 && n % q->group)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: group %d does not divide n", (int)q->group);
+  if (What == W && ldw != n)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: What may alias W only when ldw == n");
+  size_t need = gptq_ws_bytes(m, n);
+  if (ws_bytes < need || (need && !ws))
+    return fail(KRONQ_EWORKSPACE, "kronq_gptq_quantize: workspace %zu < %zu bytes", ws_bytes, need);
+  return gptq_launch(W, m, n, ldw, R, ldr, perm, q->bits, q->group > 0 ? q->group : 0, codes,
+                     scales, zeros, What, pre_round, ws, ws_bytes, (hipStream_t)stream);
+}
+
+kronq_status kronq_sensitivity(const float* HX, int64_t n, int64_t ldhx, const float* HG,
+                               int64_t m, int64_t ldhg, double* out3, void* stream) {
+  if (!HX || !HG || !out3) return fail(KRONQ_EINVAL, "kronq_sensitivity: NULL pointer");
+  if (n < 1 || m < 1 || ldhx < n || ldhg < m)
+    return fail(KRONQ_EINVAL, "kronq_sensitivity: bad shape");
+  return trace_launch(HX, n, ldhx, HG, m, ldhg, out3, (hipStream_t)stream);
+}
+
+kronq_status kronq_allocate_bits(int32_t L, const double* scores, const int64_t* n_params,
+                                 int32_t bmin, int32_t bmax, int64_t budget_bits,
+                                 int32_t* bits_out) {
+  if (L < 1 || !scores || !n_params || !bits_out)
+    return fail(KRONQ_EINVAL, "kronq_allocate_bits: bad arguments");
+  if (bmin < 1 || bmax < bmin || bmax > 64)
+    return fail(KRONQ_EINVAL, "kronq_allocate_bits: bad bit range [%d, %d]", (int)bmin, (int)bmax);
+  // exact integer budget arithmetic (__int128 guards the products)
+  __int128 total = 0;
+  for (int32_t i = 0; i < L; ++i) {
+    if (n_params[i] < 1) return fail(KRONQ_EINVAL, "kronq_allocate_bits: n_params[%d] < 1", (int)i);
+    if (std::isnan(scores[i])) return fail(KRONQ_EINVAL, "kronq_allocate_bits: score %d is NaN", (int)i);
+    total += (__int128)n_params[i];
+  }
+  __int128 used = total * bmin;
+  if ((__int128)budget_bits < used)
+    return fail(KRONQ_EINVAL, "kronq_allocate_bits: budget below bmin for every sublayer");
+  std::vector<int32_t> order((size_t)L);
+  for (int32_t i = 0; i < L; ++i) order[(size_t)i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return scores[a] > scores[b]; });
+  for (int32_t i = 0; i < L; ++i) bits_out[i] = bmin;
+  for (int32_t i : order) {
+    while (bits_out[i] < bmax && used + (__int128)n_params[i] <= (__int128)budget_bits) {
+      bits_out[i] += 1;
+      used += n_params[i];
+    }
+  }
+  return KRONQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+// Bidirectional incoherence processing: S_G rescale and randomized block
+// Hadamard transforms on both sides of W, H_X and H_G (hyper.ai summary of the
+// KronQ paper, Method; Pith review, proof of Theorem 1: W' = U W V^T,
+// H_G' = U H_G U^T, H_X' = V H_X V^T).
+//
+// Every transform here has the form  M <- (I (x) H_kr) Dr M Dc (I (x) H_kc) / sqrt(kr kc)
+// for an R x C matrix M: Dr, Dc diagonal (signs, times the S_G rescale where
+// it applies), H_k Sylvester Hadamard matrices of order k mixing contiguous
+// blocks of rows (kr) and of columns (kc).  Because H_kr = H_{kr/R1} (x) H_R1 in
+// Sylvester order, the mixing splits into factors that act on separate bits
+// of the (row, column) index and commute, so the whole 2-D transform runs in
+// two read-modify-write passes over HBM:
+//   pass 1: a tile of R1 consecutive rows x one column block (kc columns);
+//           applies Dr, Dc, the full column-side transform and the low R1 part
+//           of the row-side transform (R1 * kc <= tile size);
+//   pass 2: a tile of kr/R1 rows at stride R1 x a strip of CW columns; applies
+//           the remaining kr/R1 part of the row-side transform (skipped when
+//           R1 == kr).
+// Each pass stages its tile (up to 2^15 floats = 128 KiB) in LDS and runs the
+// butterflies radix-16: a thread gathers 16 elements differing in 4 index bits,
+// does 4 butterfly stages in registers and scatters them back.  HBM traffic is
+// float4 and coalesced (rows of a column block are contiguous; pass-2 strips
+// are >= 64 B wide).  LDS rows are padded by 4 floats per 32 so that
+// float4-aligned accesses stay 16-byte aligned and the low-bit rounds are
+// bank-conflict free.
+#include "kronq_internal.h"
+
+namespace kronq {
+namespace {
+
+constexpr int LOG_TILE = 15;
+constexpr int TILE = 1 << LOG_TILE;
+constexpr int NT = 512;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int pad(int i) { return i + ((i >> 5) << 2); }
+constexpr int padded(int n) { return n + ((n >> 5) << 2); }
+
+// In-register Walsh-Hadamard over K bits (2^K values, natural order).
+template <int K>
+__device__ __forceinline__ void wht_regs(float (&v)[1 << K]) {
+#pragma unroll
+  for (int h = 1; h < (1 << K); h <<= 1)
+#pragma unroll
+    for (int i = 0; i < (1 << K); ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+}
+
+template <int K>
+__device__ __forceinline__ void lds_round(float* s, int p, int b) {
+  const int ngroups = 1 << (p - K);
+  const int lowmask = (1 << b) - 1;
+  for (int g = threadIdx.x; g < ngroups; g += NT) {
+    const int base = ((g >> b) << (b + K)) | (g & lowmask);
+    float v[1 << K];
+#pragma unroll
+    for (int c = 0; c < (1 << K); ++c) v[c] = s[pad(base | (c << b))];
+    wht_regs<K>(v);
+#pragma unroll
+    for (int c = 0; c < (1 << K); ++c) s[pad(base | (c << b))] = v[c];
+  }
+}
+
+// Unnormalized WHT over index bits [blo, bhi) of the 2^p-element LDS tile.
+__device__ void lds_wht_bits(float* s, int p, int blo, int bhi) {
+  for (int b = blo; b < bhi; b += 4) {
+    const int k = min(4, bhi - b);
+    switch (k) {
+      case 4: lds_round<4>(s, p, b); break;
+      case 3: lds_round<3>(s, p, b); break;
+      case 2: lds_round<2>(s, p, b); break;
+      default: lds_round<1>(s, p, b); break;
+    }
+    __syncthreads();
+  }
+}
+
+struct Side {
+  int64_t block;
+  const float* fac;   // per-index factor (signs [* rescale]); never NULL
+};
+
+struct TParams {
+  float* M;
+  int64_t R, C, ld;
+  Side row, col;
+  int64_t R1;          // low row-block factor handled by pass 1
+  int lg_kc, lg_r1;    // log2 of kc and R1
+  int lg_rows2;        // log2(kr / R1)
+  int lg_cw;           // pass-2 strip width (log2)
+  int64_t strips;      // pass-2 strips per row of blocks
+  float norm1, norm2;
+  int64_t tiles1, tiles2;
+  int per_xcd1, per_xcd2;
+};
+
+__device__ __forceinline__ bool xcd_tile(int64_t ntiles, int per_xcd, int64_t& t) {
+  const int b = blockIdx.x;
+  t = (int64_t)(b % kXcds) * per_xcd + b / kXcds;
+  return (b / kXcds) < per_xcd && t < ntiles;
+}
+
+// pass 1: tile = R1 rows x kc columns, index e = rr * kc + cc
+template <bool kVec>
+__global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
+  extern __shared__ __align__(16) float s[];
+  int64_t t;
+  if (!xcd_tile(p.tiles1, p.per_xcd1, t)) return;
+  const int64_t kc = p.col.block;
+  const int64_t nb = p.C / kc;
+  const int64_t r0 = (t / nb) * p.R1, c0 = (t % nb) * kc;
+  const int lg = p.lg_kc + p.lg_r1;
+  const int E = 1 << lg;
+  if (kVec) {
+    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
+      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const int64_t r = r0 + rr, c = c0 + cc;
+      const float4 x = *reinterpret_cast<const float4*>(p.M + r * p.ld + c);
+      const float4 f = *reinterpret_cast<const float4*>(p.col.fac + c);
+      const float g = p.row.fac[r];
+      *reinterpret_cast<float4*>(s + pad(e)) =
+          make_float4(x.x * f.x * g, x.y * f.y * g, x.z * f.z * g, x.w * f.w * g);
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const int64_t r = r0 + rr, c = c0 + cc;
+      s[pad(e)] = p.M[r * p.ld + c] * p.col.fac[c] * p.row.fac[r];
+    }
+  }
+  __syncthreads();
+  lds_wht_bits(s, lg, 0, lg);
+  const float nrm = p.norm1;
+  if (kVec) {
+    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
+      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
+      *reinterpret_cast<float4*>(p.M + (r0 + rr) * p.ld + c0 + cc) =
+          make_float4(y.x * nrm, y.y * nrm, y.z * nrm, y.w * nrm);
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      p.M[(r0 + rr) * p.ld + c0 + cc] = s[pad(e)] * nrm;
+    }
+  }
+}
+
+// pass 2: tile = (kr / R1) rows at stride R1 x CW columns, index e = j * CW + c
+template <bool kVec>
+__global__ void __launch_bounds__(NT) biip_pass2(TParams p) {
+  extern __shared__ __align__(16) float s[];
+  int64_t t;
+  if (!xcd_tile(p.tiles2, p.per_xcd2, t)) return;
+  const int64_t kr = p.row.block;
+  const int64_t strip = t % p.strips;
+  const int64_t rest = t / p.strips;
+  const int64_t res = rest % p.R1, rb = rest / p.R1;
+  const int64_t rbase = rb * kr + res;
+  const int64_t cbase = strip << p.lg_cw;
+  const int lg = p.lg_rows2 + p.lg_cw;
+  const int E = 1 << lg;
+  const int64_t cmask = (1 << p.lg_cw) - 1;
+  if (kVec) {
+    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
+      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < p.C) x = *reinterpret_cast<const float4*>(p.M + (rbase + j * p.R1) * p.ld + c);
+      *reinterpret_cast<float4*>(s + pad(e)) = x;
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
+      s[pad(e)] = (c < p.C) ? p.M[(rbase + j * p.R1) * p.ld + c] : 0.f;
+    }
+  }
+  __syncthreads();
+  lds_wht_bits(s, lg, p.lg_cw, lg);
+  const float nrm = p.norm2;
+  if (kVec) {
+    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
+      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
+      if (c < p.C) {
+        const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
+        *reinterpret_cast<float4*>(p.M + (rbase + j * p.R1) * p.ld + c) =
+            make_float4(y.x * nrm, y.y * nrm, y.z * nrm, y.w * nrm);
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
+      if (c < p.C) p.M[(rbase + j * p.R1) * p.ld + c] = s[pad(e)] * nrm;
+    }
+  }
+}
+
+// sg[i] = HG[i][i]^alpha (1 when not positive or alpha == 0);
+// rfW[i] = so[i] * sg[i];  rfG[i] = so[i] / sg[i]
+__global__ void biip_prep(const float* HG, int64_t ldhg, int64_t m, float alpha, const float* so,
+                          float* sg_ws, float* rfW, float* rfG, float* sg_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= m) return;
+  float g = 1.0f;
+  if (alpha != 0.0f) {
+    const float dgi = HG[i * ldhg + i];
+    if (dgi > 0.0f) g = powf(dgi, alpha);
+  }
+  sg_ws[i] = g;
+  rfW[i] = so[i] * g;
+  rfG[i] = so[i] / g;
+  if (sg_out) sg_out[i] = g;
+}
+
+int ilog2(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+
+int64_t pow2_floor(int64_t x) {
+  int64_t p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr, const float* rfac,
+                         int64_t kc, const float* cfac, hipStream_t st) {
+  TParams p{};
+  p.M = M;
+  p.R = R;
+  p.C = C;
+  p.ld = ld;
+  p.row = Side{kr, rfac};
+  p.col = Side{kc, cfac};
+  p.R1 = std::min<int64_t>(kr, TILE / kc);
+  p.lg_kc = ilog2(kc);
+  p.lg_r1 = ilog2(p.R1);
+  const int64_t rows2 = kr / p.R1;
+  p.lg_rows2 = ilog2(rows2);
+  p.norm1 = (float)(1.0 / std::sqrt((double)(p.R1 * kc)));
+  p.norm2 = (float)(1.0 / std::sqrt((double)rows2));
+  const int64_t cw = std::min<int64_t>(pow2_floor(C), TILE / rows2);
+  p.lg_cw = ilog2(cw);
+  p.strips = (C + cw - 1) / cw;
+  p.tiles1 = (R / p.R1) * (C / kc);
+  p.tiles2 = (rows2 > 1) ? (R / kr) * p.R1 * p.strips : 0;
+  p.per_xcd1 = (int)((p.tiles1 + kXcds - 1) / kXcds);
+  p.per_xcd2 = (int)((p.tiles2 + kXcds - 1) / kXcds);
+  const bool vec1 = (kc % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0) &&
+                    ((uintptr_t)cfac % 16 == 0);
+  const bool vec2 = (cw % 4 == 0) && (C % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0);
+  const size_t lds1 = padded(1 << (p.lg_kc + p.lg_r1)) * sizeof(float);
+  const size_t lds2 = padded(1 << (p.lg_rows2 + p.lg_cw)) * sizeof(float);
+  const size_t ldsmax = padded(TILE) * sizeof(float);
+  {
+    auto k1 = vec1 ? biip_pass1<true> : biip_pass1<false>;
+    KQ_HIP(hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
+    hipLaunchKernelGGL(k1, dim3(p.per_xcd1 * kXcds), dim3(NT), lds1, st, p);
+    KQ_LAUNCHED("biip_pass1");
+  }
+  if (p.tiles2) {
+    auto k2 = vec2 ? biip_pass2<true> : biip_pass2<false>;
+    KQ_HIP(hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
+    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(NT), lds2, st, p);
+    KQ_LAUNCHED("biip_pass2");
+  }
+  return KRONQ_OK;
+}
+
+}  // namespace
+
+size_t biip_ws_bytes(int64_t m, int64_t n) {
+  (void)n;
+  return 3 * align_up((size_t)m * sizeof(float), 256);
+}
+
+kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX, int64_t ldhx,
+                         float* HG, int64_t ldhg, const kronq_had& in, const kronq_had& out,
+                         float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws_bytes;
+  const size_t seg = align_up((size_t)m * sizeof(float), 256);
+  float* sg_ws = static_cast<float*>(ws);
+  float* rfW = reinterpret_cast<float*>(static_cast<char*>(ws) + seg);
+  float* rfG = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * seg);
+  hipLaunchKernelGGL(biip_prep, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s,
+                     (const float*)HG, ldhg, m, alpha, out.signs, sg_ws, rfW, rfG, sg);
+  KQ_LAUNCHED("biip_prep");
+  kronq_status st = transform2d(W, m, n, ldw, out.block, rfW, in.block, in.signs, s);
+  if (st) return st;
+  if (HX) {
+    st = transform2d(HX, n, n, ldhx, in.block, in.signs, in.block, in.signs, s);
+    if (st) return st;
+  }
+  if (HG) {
+    st = transform2d(HG, m, m, ldhg, out.block, rfG, out.block, rfG, s);
+    if (st) return st;
+  }
+  return KRONQ_OK;
+}
+
+}  // namespace kronq

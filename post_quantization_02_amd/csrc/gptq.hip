@@ -1,0 +1,307 @@
+// Column-wise OBS quantize-and-compensate with H_X alone (Pith review of the
+// KronQ paper, Proposition 1: with H = H_X (x) H_G the column update does not
+// depend on H_G, so every output row is an independent GPTQ/GPTAQ problem;
+// Algorithm 2: lazy batches of B = 128 columns).
+//
+// One workgroup owns RT = 16 rows and walks all n columns (processing order)
+// in blocks of 128, left-looking, in a single launch:
+//   1. acc = W[:, block] - E[:, 0:jb] R[0:jb, block]   (all earlier errors at
+//      once; fp64 v_mfma_f64_16x16x4f64, K split over the four waves and
+//      reduced in LDS; E is the fp64 error matrix of this workgroup's rows)
+//   2. the 128 columns of the block sequentially: each of the four waves owns
+//      four rows with 16 lanes per row and 8 columns per lane; the owner lane
+//      of column c rounds it onto the grid, forms e = (w - wq) / R[c][c], the
+//      error is broadcast across the row's lanes and every later column of the
+//      block is compensated with the row of R staged in LDS.
+// The loop runs in fp64 from fp32 inputs, so rounding decisions match a
+// float64 reference up to summation order.  Grid parameters: per-channel from
+// the whole initial row (a separate pass), or per group of g | 128 columns from
+// the current compensated values when the group's first column is reached.
+#include "kronq_internal.h"
+
+namespace kronq {
+namespace {
+
+typedef double f64x4_t __attribute__((__vector_size__(4 * sizeof(double))));
+
+constexpr int RT = 16;         // rows per workgroup
+constexpr int BLK = 128;       // columns per block
+constexpr int GT = 256;        // threads
+constexpr int RLD = BLK + 4;   // LDS stride of the R block (floats)
+
+struct GptqParams {
+  const float* W;
+  int64_t m, n, ldw;
+  const float* R;
+  int64_t ldr;
+  const int32_t* perm;     // may be NULL
+  int bits, group;         // group 0: per-channel
+  int ngroups;
+  uint8_t* codes;
+  float* scales;
+  float* zeros;
+  float* What;             // may be NULL
+  float* pre;              // may be NULL
+  double* E;               // m x ldE, processing order
+  int64_t ldE;             // n rounded up to 16 (128-byte rows)
+  const double* pc;        // per-channel (scale, zero) pairs, m x 2
+};
+
+__device__ __forceinline__ int64_t colmap(const GptqParams& p, int64_t j) {
+  return p.perm ? (int64_t)p.perm[j] : j;
+}
+
+// grid parameters of an asymmetric uniform grid from (min, max)
+__device__ __forceinline__ void grid_params(double lo, double hi, int bits, double& scale,
+                                            double& zero) {
+  lo = fmin(lo, 0.0);
+  hi = fmax(hi, 0.0);
+  if (lo == hi) {
+    lo = -1.0;
+    hi = 1.0;
+  }
+  scale = (hi - lo) / (double)((1 << bits) - 1);
+  zero = rint(-lo / scale);
+}
+
+// per-channel parameters from the whole initial row (natural order)
+__global__ void __launch_bounds__(256) gptq_row_params(GptqParams p, double* pc) {
+  const int64_t r = blockIdx.x;
+  __shared__ double smin[4], smax[4];
+  double lo = INFINITY, hi = -INFINITY;
+  for (int64_t c = threadIdx.x; c < p.n; c += 256) {
+    const double v = (double)p.W[r * p.ldw + c];
+    lo = fmin(lo, v);
+    hi = fmax(hi, v);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = fmin(lo, __shfl_xor(lo, off, 64));
+    hi = fmax(hi, __shfl_xor(hi, off, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    smin[threadIdx.x >> 6] = lo;
+    smax[threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    lo = fmin(fmin(smin[0], smin[1]), fmin(smin[2], smin[3]));
+    hi = fmax(fmax(smax[0], smax[1]), fmax(smax[2], smax[3]));
+    double scale, zero;
+    grid_params(lo, hi, p.bits, scale, zero);
+    pc[2 * r] = scale;
+    pc[2 * r + 1] = zero;
+    p.scales[r] = (float)scale;
+    p.zeros[r] = (float)zero;
+  }
+}
+
+__global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
+  extern __shared__ __align__(16) double gl[];
+  double* part = gl;                                       // 4 x RT x BLK doubles
+  float* Rb = reinterpret_cast<float*>(gl + 4 * RT * BLK);  // BLK x RLD floats
+  double* invd = reinterpret_cast<double*>(Rb + BLK * RLD); // BLK doubles
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t row0 = (int64_t)blockIdx.x * RT;
+  // in-block mapping
+  const int lrow = 4 * wave + (lane >> 4);  // 0..15
+  const int part_id = lane & 15;            // 8 columns each
+  const int64_t grow = row0 + lrow;
+  const bool row_ok = grow < p.m;
+  const int maxq = (1 << p.bits) - 1;
+
+  double scale = 1.0, zero = 0.0;
+  if (p.group == 0 && row_ok) {
+    scale = p.pc[2 * grow];
+    zero = p.pc[2 * grow + 1];
+  }
+
+  const int nblocks = (int)((p.n + BLK - 1) / BLK);
+  for (int b = 0; b < nblocks; ++b) {
+    const int64_t jb = (int64_t)b * BLK;
+    const int ncols = (int)min<int64_t>(BLK, p.n - jb);
+
+    // ---- 1. left-looking update on the matrix cores ----
+    {
+      f64x4_t acc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+      const int64_t kq = jb / 4;
+      const int64_t k_lo = kq * wave, k_hi = kq * (wave + 1);
+      const int64_t arow = row0 + (lane & 15);
+      const bool arow_ok = arow < p.m;
+      const double* Erow = p.E + (arow_ok ? arow : 0) * p.ldE;
+      for (int64_t k0 = k_lo; k0 < k_hi; k0 += 4) {
+        const int64_t k = k0 + (lane >> 4);
+        const double a = arow_ok ? Erow[k] : 0.0;
+        const float* Rk = p.R + k * p.ldr + jb + (lane & 15);
+        double bv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int64_t c = jb + 16 * t + (lane & 15);
+          bv[t] = (c < p.n) ? (double)Rk[16 * t] : 0.0;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv[t], acc[t], 0, 0, 0);
+      }
+      // partial of this wave -> LDS; f64 16x16 accumulator layout: lane holds
+      // column lane % 16, register v holds row 4 * v + lane / 16
+      double* pw = part + wave * RT * BLK;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pw[(4 * v + (lane >> 4)) * BLK + 16 * t + (lane & 15)] = acc[t][v];
+    }
+    // stage the diagonal block of R
+    for (int e = tid; e < BLK * BLK; e += GT) {
+      const int i = e / BLK, j = e % BLK;
+      Rb[i * RLD + j] = (i < ncols && j < ncols) ? p.R[(jb + i) * p.ldr + jb + j] : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < BLK; i += GT) invd[i] = (i < ncols) ? 1.0 / (double)Rb[i * RLD + i] : 0.0;
+    // reduce the four partials and add W (natural column perm[jb + c])
+    for (int e = tid; e < RT * BLK; e += GT) {
+      const int r = e / BLK, c = e % BLK;
+      const int64_t gr = row0 + r;
+      double w = 0.0;
+      if (gr < p.m && c < ncols) w = (double)p.W[gr * p.ldw + colmap(p, jb + c)];
+      part[e] = w - (part[e] + part[RT * BLK + e] + part[2 * RT * BLK + e] + part[3 * RT * BLK + e]);
+    }
+    __syncthreads();
+
+    // ---- 2. sequential columns of the block ----
+    double v[8], ev[8], wq[8], tv[8];
+    int qv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      v[s] = part[lrow * BLK + 8 * part_id + s];
+      ev[s] = 0.0;
+      wq[s] = 0.0;
+      tv[s] = 0.0;
+      qv[s] = 0;
+    }
+    for (int o = 0; o < 16; ++o) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 8 * o + s;
+        if (c >= ncols) break;
+        if (p.group > 0 && (c % p.group) == 0) {
+          // parameters of the group [c, c + group) from the current values
+          double lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int cc = 8 * part_id + q;
+            if (cc >= c && cc < c + p.group && cc < ncols) {
+              lo = fmin(lo, v[q]);
+              hi = fmax(hi, v[q]);
+            }
+          }
+#pragma unroll
+          for (int off = 8; off > 0; off >>= 1) {
+            lo = fmin(lo, __shfl_xor(lo, off, 16));
+            hi = fmax(hi, __shfl_xor(hi, off, 16));
+          }
+          grid_params(lo, hi, p.bits, scale, zero);
+          if (part_id == o && row_ok) {
+            const int64_t g = (jb + c) / p.group;
+            p.scales[grow * p.ngroups + g] = (float)scale;
+            p.zeros[grow * p.ngroups + g] = (float)zero;
+          }
+        }
+        // owner lane: round column c
+        const double t = v[s] / scale + zero;
+        const double q = fmin(fmax(rint(t), 0.0), (double)maxq);
+        const double w_q = scale * (q - zero);
+        const double e = (v[s] - w_q) * invd[c];
+        if (part_id == o) {
+          ev[s] = e;
+          wq[s] = w_q;
+          tv[s] = t;
+          qv[s] = (int)q;
+        }
+        const double eb = __shfl(e, (lane & 48) | o, 64);
+        // compensate the later columns of the block held by this lane
+        const float* Rrow = Rb + c * RLD + 8 * part_id;
+        const float4 r0v = *reinterpret_cast<const float4*>(Rrow);
+        const float4 r1v = *reinterpret_cast<const float4*>(Rrow + 4);
+        const float rr[8] = {r0v.x, r0v.y, r0v.z, r0v.w, r1v.x, r1v.y, r1v.z, r1v.w};
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2)
+          if (8 * part_id + q2 > c) v[q2] -= eb * (double)rr[q2];
+      }
+    }
+    // ---- 3. write errors and outputs of this block ----
+    if (row_ok) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 8 * part_id + s;
+        if (c < ncols) {
+          const int64_t j = jb + c;
+          p.E[grow * p.ldE + j] = ev[s];
+          const int64_t nc = colmap(p, j);
+          p.codes[grow * p.n + nc] = (uint8_t)qv[s];
+          if (p.What) p.What[grow * p.n + nc] = (float)wq[s];
+          if (p.pre) p.pre[grow * p.n + nc] = (float)tv[s];
+        }
+      }
+    }
+    // E of this block must be visible to every wave before the next block's
+    // left-looking product (global memory, same workgroup)
+    __threadfence();
+    __syncthreads();
+    __threadfence();
+  }
+}
+
+int64_t lde(int64_t n) { return (n + 15) / 16 * 16; }
+
+}  // namespace
+
+size_t gptq_ws_bytes(int64_t m, int64_t n) {
+  return align_up((size_t)m * lde(n) * sizeof(double), 256) +
+         align_up((size_t)m * 2 * sizeof(double), 256);
+}
+
+kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
+                         int64_t ldr, const int32_t* perm, int bits, int group, uint8_t* codes,
+                         float* scales, float* zeros, float* What, float* pre_round, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  (void)ws_bytes;
+  if (group > 0 && (BLK % group != 0 || group % 8 != 0))
+    return fail(KRONQ_EUNSUPPORTED, "kronq_gptq_quantize: group %d must be a multiple of 8 dividing %d",
+                group, BLK);
+  GptqParams p{};
+  p.W = W;
+  p.m = m;
+  p.n = n;
+  p.ldw = ldw;
+  p.R = R;
+  p.ldr = ldr;
+  p.perm = perm;
+  p.bits = bits;
+  p.group = group;
+  p.ngroups = group > 0 ? (int)(n / group) : 1;
+  p.codes = codes;
+  p.scales = scales;
+  p.zeros = zeros;
+  p.What = What;
+  p.pre = pre_round;
+  p.E = static_cast<double*>(ws);
+  p.ldE = lde(n);
+  double* pc = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                         align_up((size_t)m * p.ldE * sizeof(double), 256));
+  p.pc = pc;
+  if (group == 0) {
+    hipLaunchKernelGGL(gptq_row_params, dim3((unsigned)m), dim3(256), 0, s, p, pc);
+    KQ_LAUNCHED("gptq_row_params");
+  }
+  const size_t lds = 4 * RT * BLK * sizeof(double) + BLK * RLD * sizeof(float) + BLK * sizeof(double);
+  KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds));
+  hipLaunchKernelGGL(gptq_kernel, dim3((unsigned)((m + RT - 1) / RT)), dim3(GT), lds, s, p);
+  KQ_LAUNCHED("gptq_kernel");
+  return KRONQ_OK;
+}
+
+}  // namespace kronq

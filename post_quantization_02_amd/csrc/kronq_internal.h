@@ -1,0 +1,63 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kronq.h"
+
+namespace kronq {
+
+// Thread-local error detail behind kronq_last_error().
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+kronq_status fail(kronq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kronq_status hip_fail(hipError_t e, const char* what);
+
+#define KQ_HIP(call)                                              \
+  do {                                                            \
+    hipError_t _e = (call);                                       \
+    if (_e != hipSuccess) return ::kronq::hip_fail(_e, #call);    \
+  } while (0)
+
+#define KQ_LAUNCHED(name)                                         \
+  do {                                                            \
+    hipError_t _e = hipGetLastError();                            \
+    if (_e != hipSuccess) return ::kronq::hip_fail(_e, name);     \
+  } while (0)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- launchers (one translation unit per kernel family) ----
+
+// gram.hip
+size_t gram_ws_bytes(int64_t N, int64_t d, int32_t dtype);
+kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda, float* H,
+                         int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
+                         hipStream_t s);
+
+// fwht.hip
+size_t biip_ws_bytes(int64_t m, int64_t n);
+kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX, int64_t ldhx,
+                         float* HG, int64_t ldhg, const kronq_had& in, const kronq_had& out,
+                         float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s);
+
+// chol.hip
+size_t chol_ws_bytes(int64_t n);
+kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, int act_order,
+                         int32_t* perm, float* R, int64_t ldr, int64_t* info, void* ws,
+                         size_t ws_bytes, hipStream_t s);
+
+// gptq.hip
+size_t gptq_ws_bytes(int64_t m, int64_t n);
+kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
+                         int64_t ldr, const int32_t* perm, int bits, int group, uint8_t* codes,
+                         float* scales, float* zeros, float* What, float* pre_round, void* ws,
+                         size_t ws_bytes, hipStream_t s);
+
+// trace.hip
+kronq_status trace_launch(const float* HX, int64_t n, int64_t ldhx, const float* HG, int64_t m,
+                          int64_t ldhg, double* out3, hipStream_t s);
+
+}  // namespace kronq

@@ -1,0 +1,93 @@
+"""Parity of kronq_chol_inv (act-order, damping, inverse Cholesky factor)."""
+import numpy as np
+import pytest
+import torch
+
+import post_quantization_02_amd as kq
+from oracle import kronq_oracle as O
+from gpu_helpers import DEV, host, rel_fro, say, spd_from_gram, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _backward_error(R, Hd):
+    # || R^-1 R^-T - Hd ||_F / ||Hd||_F  with R^-1 from a triangular solve
+    Ri = np.linalg.solve(R.astype(np.float64), np.eye(R.shape[0]))
+    return rel_fro(Ri @ Ri.T, Hd)
+
+
+@pytest.mark.parametrize("n,act", [(300, True), (300, False), (512, False), (130, True), (1, False),
+                                   (1024, True)])
+def test_chol_inv_small(n, act):
+    say("chol", n, act)
+    H = spd_from_gram(61, n).astype(np.float32)
+    R, perm, info = kq.kronq_chol_inv(to_dev_f32(H), 0.01, act)
+    R, perm = host(R), host(perm)
+    assert info == -1
+    operm, Hd = O.prepare_hessian(H.astype(np.float64), 0.01, act)
+    np.testing.assert_array_equal(perm, operm)
+    Ro, _ = O.chol_inv_upper(Hd)
+    assert np.all(np.tril(R, -1) == 0) and np.all(np.diag(R) > 0)
+    be, fe = _backward_error(R, Hd), rel_fro(R, Ro)
+    say("  backward %.2e forward %.2e" % (be, fe))
+    assert be <= 1e-5
+    assert fe <= 1e-3
+
+
+def test_chol_act_order_ties():
+    say("chol act-order ties")
+    d = np.array([3.0, 1.0, 3.0, 2.0, 1.0, 3.0], dtype=np.float32)
+    H = np.diag(d)
+    _, perm, _ = kq.kronq_chol_inv(to_dev_f32(H), 0.0, True)
+    np.testing.assert_array_equal(host(perm), [0, 2, 5, 3, 1, 4])
+
+
+def _largest_non_pd_trailing(Hd):
+    n = Hd.shape[0]
+    for k in range(n - 1, -1, -1):
+        if np.linalg.eigvalsh(Hd[k:, k:]).min() <= 0:
+            return k
+    return -1
+
+
+def test_chol_not_positive_definite():
+    say("chol ENOTPD")
+    n = 200
+    H = np.eye(n, dtype=np.float32)
+    H[150, 150] = -5.0
+    with pytest.raises(kq.KronqError) as e:
+        kq.kronq_chol_inv(to_dev_f32(H), 0.01, False)
+    assert e.value.status == kq.KRONQ_ENOTPD
+    _, Hd = O.prepare_hessian(H.astype(np.float64), 0.01, False)
+    assert e.value.info == _largest_non_pd_trailing(Hd) == 150
+    # the library stays usable after a failure
+    R, _, info = kq.kronq_chol_inv(to_dev_f32(np.eye(8, dtype=np.float32)), 0.0, False)
+    assert info == -1
+    np.testing.assert_allclose(host(R), np.eye(8), atol=1e-7)
+
+
+def test_chol_worked_example():
+    # H = [[4, 2], [2, 3]] -> R = [[sqrt(3/8), -1/sqrt(6)], [0, 1/sqrt(3)]]
+    say("chol 2x2 worked example")
+    R, _, _ = kq.kronq_chol_inv(to_dev_f32(np.array([[4, 2], [2, 3]], dtype=np.float32)), 0.0, False)
+    np.testing.assert_allclose(host(R), [[np.sqrt(3 / 8), -1 / np.sqrt(6)], [0, 1 / np.sqrt(3)]],
+                               rtol=1e-6)
+
+
+def test_chol_full_size_llama2_7b_q_proj():
+    n = 4096
+    say("chol full size", n)
+    H = spd_from_gram(62, n, N=16384).astype(np.float32)
+    R, perm, info = kq.kronq_chol_inv(to_dev_f32(H), 0.01, False)
+    R = host(R)
+    _, Hd = O.prepare_hessian(H.astype(np.float64), 0.01, False)
+    # backward error through probes: || Hd R^T R v - v || / ||v||
+    rng = np.random.default_rng(0)
+    V = rng.standard_normal((n, 4))
+    Rd = R.astype(np.float64)
+    resid = np.linalg.norm(Hd @ (Rd.T @ (Rd @ V)) - V) / np.linalg.norm(V)
+    Ro, _ = O.chol_inv_upper(Hd)
+    fe = rel_fro(R, Ro)
+    say("  probe residual %.2e forward %.2e" % (resid, fe))
+    assert resid <= 1e-3
+    assert fe <= 1e-3
