@@ -11,18 +11,19 @@
 //
 // Blocked right-looking sweep over panels of NB = 128 columns of A (padded
 // with an identity block to a multiple of NB; the padding is block diagonal
-// with A so it changes nothing):
-//   diag kernel   (1 workgroup): factor A_pp in fp64 in LDS, invert it by
-//                 recursive doubling, store Linv_pp (fp32); report pivots <= 0
-//   panel kernel  : L_ip = A_ip Linv_pp^T (stored over A_ip) and
-//                   M_ip = L_ip Linv_pp, for every row tile i > p
-//   update kernel : A_ij -= L_ip L_jp^T        (i >= j > p; Cholesky SYRK)
-//                   B_i[:, c] -= M_ip B_p[:, c] (i > p, c <= p; forward
-//                   substitution of L Y = I with B initialised to I)
-// and finally Y_p = Linv_pp B_p and R = J Y J.  All tile products run on the
-// fp32 matrix cores (v_mfma_f32_32x32x2f32), 128 x 128 output tiles with four
-// waves of 64 x 64.  A device flag set by a failed pivot makes every later
-// kernel return at once; the host reads the flag after the last launch.
+// with A so it changes nothing), solving L Y = I alongside (B starts as I):
+//   diag kernel   (1 workgroup, 512 threads): Cholesky of A_pp and, in the
+//                 same elimination sweep, Linv_pp (augmented [A_pp | I]); fp64
+//                 in registers, 8 x 8 elements per thread, 2 barriers per
+//                 column; pivots <= 0 are reported
+//   panel kernel  : Lp_i = A_ip Linv_pp^T (i > p) and Yp_c = Linv_pp B_pc
+//                   (c <= p), each as four 128 x 32 quarter tiles
+//   update kernel : A_ij -= Lp_i Lp_j^T (i >= j > p; Cholesky SYRK),
+//                   B_ic -= Lp_i Yp_c   (i > p, c <= p; forward substitution),
+//                   B_pc  = Yp_c        (row block p of Y = L^-1 is final)
+// and finally R = J Y J.  Tile products run on the fp32 matrix cores
+// (v_mfma_f32_32x32x2f32).  A device flag set by a failed pivot makes every
+// later kernel return at once; the host reads the flag after the last launch.
 #include "kronq_internal.h"
 
 namespace kronq {
@@ -37,8 +38,9 @@ constexpr int LDT = NB + 1;   // odd LDS stride: conflict-free transposed stores
 struct CholWs {
   float* A;       // npad x npad (reversed, permuted, damped)
   float* B;       // npad x npad (forward substitution; ends as Y = L^-1)
-  float* M;       // npad x NB   (M_ip for the current panel)
-  float* Linv;    // P x NB x NB (inverse diagonal blocks)
+  float* Lp;      // npad x NB   (panel L_ip of the current step)
+  float* Yp;      // NB x npad   (row block Y_p of the current step)
+  float* Linv;    // NB x NB     (inverse of the current diagonal block)
   double* damp;   // lambda * mean(diag H)
   int* flag;      // nonzero after a failed pivot
   long long* info;
@@ -47,17 +49,19 @@ struct CholWs {
 size_t ws_layout(int64_t n, CholWs* w, void* base) {
   const int64_t npad = (n + NB - 1) / NB * NB;
   const size_t sA = align_up((size_t)npad * npad * sizeof(float), 256);
-  const size_t sM = align_up((size_t)npad * NB * sizeof(float), 256);
+  const size_t sP = align_up((size_t)npad * NB * sizeof(float), 256);
   size_t off = 0;
   char* b = static_cast<char*>(base);
   if (w) w->A = reinterpret_cast<float*>(b + off);
   off += sA;
   if (w) w->B = reinterpret_cast<float*>(b + off);
   off += sA;
-  if (w) w->M = reinterpret_cast<float*>(b + off);
-  off += sM;
+  if (w) w->Lp = reinterpret_cast<float*>(b + off);
+  off += sP;
+  if (w) w->Yp = reinterpret_cast<float*>(b + off);
+  off += sP;
   if (w) w->Linv = reinterpret_cast<float*>(b + off);
-  off += sM;
+  off += align_up((size_t)NB * NB * sizeof(float), 256);
   if (w) w->damp = reinterpret_cast<double*>(b + off);
   off += 256;
   if (w) w->flag = reinterpret_cast<int*>(b + off);
@@ -140,47 +144,105 @@ __global__ void __launch_bounds__(256) chol_gather(const float* H, int64_t n, in
 
 // ------------------------------------------------------- diagonal block
 
-// Factor the NB x NB block A_pp (lower, fp64) and invert it; Linv_pp stored in
-// fp32 (full block, zeros above the diagonal).
-__global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p, CholWs w) {
+// Row-block of the 8 x 8 element block held by a thread: the four waves of a
+// role take row blocks {w, 7-w, 8+w, 15-w} so that the lower-triangle work is
+// even across waves.
+__device__ __forceinline__ int diag_rowblock(int w, int r) {
+  return r == 0 ? w : r == 1 ? 7 - w : r == 2 ? 8 + w : 15 - w;
+}
+
+// Factor A_pp = L L^T and invert L in one elimination sweep over [A_pp | I]:
+// for each column j, l_jj = sqrt(a_jj), l_ij = a_ij / l_jj (i > j), row j of
+// the right-hand side becomes x_j = b_j / l_jj, then a_ik -= l_ij l_kj and
+// b_ic -= l_ij x_jc for i > j.  Threads 0..255 hold 8 x 8 blocks of A, threads
+// 256..511 the blocks of B (= L^-1 at the end), fp64 in registers.
+__global__ void __launch_bounds__(512) chol_diag(int64_t npad, int64_t n, int p, CholWs w) {
   if (*w.flag) return;
-  extern __shared__ __align__(16) double sd[];
-  double* a = sd;              // NB x NB
-  double* col = sd + NB * NB;  // NB
+  __shared__ double col[NB];
+  __shared__ double xrow[NB];
+  __shared__ double piv;
   __shared__ int bad;
   const int tid = threadIdx.x;
+  const bool isA = tid < 256;
+  const int t = tid & 255;
+  const int wv = t >> 6, ln = t & 63;
+  const int bi = diag_rowblock(wv, ln >> 4);  // row block
+  const int bk = ln & 15;                     // column block
+  const bool act = bk <= bi;                  // lower-triangle block
+  double r[8][8];
   const float* Ap = w.A + (int64_t)p * NB * npad + (int64_t)p * NB;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    a[e] = (k <= i) ? (double)Ap[(int64_t)i * npad + k] : 0.0;
+  if (isA) {
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        r[ii][kk] = act ? (double)Ap[(int64_t)(8 * bi + ii) * npad + 8 * bk + kk] : 0.0;
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) r[ii][kk] = (bi == bk && ii == kk) ? 1.0 : 0.0;
   }
-  if (tid == 0) bad = -1;
-  __syncthreads();
-  for (int j = 0; j < NB; ++j) {
-    if (tid < NB && tid >= j) col[tid] = a[tid * NB + j];
-    __syncthreads();
-    const double d = col[j];
-    if (!(d > 0.0)) {
-      if (tid == 0) bad = j;
-      break;
-    }
-    const double lj = sqrt(d);
-    __syncthreads();
-    if (tid < NB && tid > j) {
-      const double v = col[tid] / lj;
-      col[tid] = v;
-      a[tid * NB + j] = v;
-    }
-    if (tid == 0) a[j * NB + j] = lj;
-    __syncthreads();
-    const int cnt = NB - 1 - j;
-    for (int e = tid; e < cnt * cnt; e += 256) {
-      const int i = j + 1 + e / cnt, k = j + 1 + e % cnt;
-      if (k <= i) a[i * NB + k] -= col[i] * col[k];
-    }
-    __syncthreads();
+  if (tid == 0) {
+    piv = r[0][0];
+    bad = -1;
   }
   __syncthreads();
+  // The broadcast column (l_ij, zero for i <= j) and row (x_jc, zero for
+  // c > j) make every update below uniform: each thread updates its whole
+  // 8 x 8 block; entries outside the trailing region receive zero, and the
+  // upper blocks that take part are never read.
+  for (int jb = 0; jb < NB / 8; ++jb) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = 8 * jb + jj;
+      // ---- column j of L and row j of L^-1
+      const double d = piv;
+      if (isA && bk == jb) {
+        const double sd = sqrt(d), inv = 1.0 / sd;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = 8 * bi + ii;
+          const double l = (i > j) ? r[ii][jj] * inv : 0.0;
+          if (i > j) r[ii][jj] = l;
+          if (i == j) r[ii][jj] = sd;
+          col[i] = l;
+        }
+        if (bi == jb && !(d > 0.0)) bad = j;
+      } else if (!isA && bi == jb) {
+        const double inv = 1.0 / sqrt(d);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const double x = (bk <= jb) ? r[jj][cc] * inv : 0.0;
+          if (bk <= jb) r[jj][cc] = x;
+          xrow[8 * bk + cc] = x;
+        }
+      }
+      __syncthreads();
+      if (bad >= 0) break;
+      // ---- trailing updates: a_ik -= l_ij l_kj ; b_ic -= l_ij x_jc
+      double ci[8], ck[8];
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) ci[ii] = col[8 * bi + ii];
+      const double* src = isA ? col : xrow;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) ck[kk] = src[8 * bk + kk];
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) r[ii][kk] = fma(-ci[ii], ck[kk], r[ii][kk]);
+      // next pivot (its owner updated it just above)
+      if (isA && j + 1 < NB) {
+        if (jj < 7) {
+          if (bi == jb && bk == jb) piv = r[jj + 1][jj + 1];
+        } else {
+          if (bi == jb + 1 && bk == jb + 1) piv = r[0][0];
+        }
+      }
+      __syncthreads();
+    }
+    if (bad >= 0) break;
+  }
   if (bad >= 0) {
     if (tid == 0) {
       // reversed position p*NB + bad is processing index n - 1 - that
@@ -190,56 +252,30 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
     }
     return;
   }
-  // invert the lower triangle in place by recursive doubling:
-  // diag 1 / l_ii, then for block size s = 2, 4, ..., NB:
-  //   X21 = -X22 (L21 X11), with the product L21 X11 staged in the (unused)
-  //   strictly upper block of the same diagonal block.
-  for (int i = tid; i < NB; i += 256) a[i * NB + i] = 1.0 / a[i * NB + i];
-  __syncthreads();
-  for (int s = 2; s <= NB; s <<= 1) {
-    const int h = s / 2;
-    const int nblk = NB / s;
-    // T = L21 X11 : (h x h) per block, stored at [o + r][o + h + c]
-    for (int e = tid; e < nblk * h * h; e += 256) {
-      const int blk = e / (h * h), r = (e / h) % h, c = e % h;
-      const int o = blk * s;
-      double t = 0.0;
-      for (int k = c; k < h; ++k) t += a[(o + h + r) * NB + o + k] * a[(o + k) * NB + o + c];
-      a[(o + r) * NB + o + h + c] = t;
-    }
-    __syncthreads();
-    // X21 = -X22 T
-    for (int e = tid; e < nblk * h * h; e += 256) {
-      const int blk = e / (h * h), r = (e / h) % h, c = e % h;
-      const int o = blk * s;
-      double t = 0.0;
-      for (int k = 0; k <= r; ++k) t += a[(o + h + r) * NB + o + h + k] * a[(o + k) * NB + o + h + c];
-      a[(o + h + r) * NB + o + c] = -t;
-    }
-    __syncthreads();
-  }
-  float* L = w.Linv + (int64_t)p * NB * NB;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    L[e] = (k <= i) ? (float)a[e] : 0.f;
+  if (!isA) {
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        w.Linv[(8 * bi + ii) * NB + 8 * bk + kk] =
+            (act && (bi > bk || kk <= ii)) ? (float)r[ii][kk] : 0.f;
   }
 }
 
 // ------------------------------------------------------- tile products
 
-// Layout of a global operand tile: element (x, k) of a 128 x K operand.
+// Layout of a global operand tile: element (x, k) of an X x K operand.
 //   XK: stored row-major as [x][k] (leading dimension ld)
 //   KX: stored row-major as [k][x]
 enum { XK = 0, KX = 1 };
 
-template <int LAY>
+// Stage KS values of k for X consecutive x into LDS as sT[k][x] (stride LDT).
+template <int LAY, int X>
 __device__ inline void stage_load(float* sT, const float* G, int64_t ld, int k0) {
-  // sT[k][x], k in [0, KS), x in [0, NB)
   const int tid = threadIdx.x;
   if (LAY == XK) {
-    // 128 rows x 32 k: thread reads float4 along k
 #pragma unroll
-    for (int q = 0; q < (NB * KS / 4) / 256; ++q) {
+    for (int q = 0; q < (X * KS / 4) / 256; ++q) {
       const int idx = tid + 256 * q;
       const int x = idx >> 3, k4 = (idx & 7) * 4;
       const float4 v = *reinterpret_cast<const float4*>(G + (int64_t)x * ld + k0 + k4);
@@ -250,9 +286,9 @@ __device__ inline void stage_load(float* sT, const float* G, int64_t ld, int k0)
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < (NB * KS / 4) / 256; ++q) {
+    for (int q = 0; q < (X * KS / 4) / 256; ++q) {
       const int idx = tid + 256 * q;
-      const int k = idx >> 5, x4 = (idx & 31) * 4;
+      const int k = idx / (X / 4), x4 = (idx % (X / 4)) * 4;
       const float4 v = *reinterpret_cast<const float4*>(G + (int64_t)(k0 + k) * ld + x4);
       sT[k * LDT + x4 + 0] = v.x;
       sT[k * LDT + x4 + 1] = v.y;
@@ -262,131 +298,134 @@ __device__ inline void stage_load(float* sT, const float* G, int64_t ld, int k0)
   }
 }
 
-// acc (per wave 64 x 64 of the 128 x 128 result) = sum_k A(x=i, k) B(x=j, k)
-template <int LA, int LB>
-__device__ inline void tile_mma(f32x16_t (&acc)[2][2], const float* Ag, int64_t lda, const float* Bg,
-                                int64_t ldb, int K, float* sA, float* sB) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lk = lane >> 5;
-  for (int k0 = 0; k0 < K; k0 += KS) {
-    __syncthreads();
-    stage_load<LA>(sA, Ag, lda, k0);
-    stage_load<LB>(sB, Bg, ldb, k0);
-    __syncthreads();
+// Workgroup tile product: out(x=i, y=j) = sum_k A(i, k) B(j, k) for an
+// MR x MC output (MR = WR * TR * 32 rows, MC = WC * TC * 32 columns; four
+// waves as WR x WC, each TR x TC accumulators of 32 x 32), K = NB.
+template <int WR, int WC, int TR, int TC>
+struct TileMma {
+  static constexpr int MR = WR * TR * 32, MC = WC * TC * 32;
+  f32x16_t acc[TR][TC];
+
+  __device__ void zero() {
 #pragma unroll
-    for (int kk = 0; kk < KS; kk += 2) {
-      float af[2], bf[2];
+    for (int a = 0; a < TR; ++a)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = sA[(kk + lk) * LDT + wm * 64 + 32 * a + lr];
+      for (int b = 0; b < TC; ++b)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bf[b] = sB[(kk + lk) * LDT + wn * 64 + 32 * b + lr];
+        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+  }
+
+  template <int LA, int LB>
+  __device__ void run(const float* Ag, int64_t lda, const float* Bg, int64_t ldb, float* sA,
+                      float* sB) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WC, wn = wave % WC;
+    const int lr = lane & 31, lk = lane >> 5;
+    for (int k0 = 0; k0 < NB; k0 += KS) {
+      __syncthreads();
+      stage_load<LA, MR>(sA, Ag, lda, k0);
+      stage_load<LB, MC>(sB, Bg, ldb, k0);
+      __syncthreads();
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int kk = 0; kk < KS; kk += 2) {
+        float af[TR], bf[TC];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
+        for (int a = 0; a < TR; ++a) af[a] = sA[(kk + lk) * LDT + (wm * TR + a) * 32 + lr];
+#pragma unroll
+        for (int b = 0; b < TC; ++b) bf[b] = sB[(kk + lk) * LDT + (wn * TC + b) * 32 + lr];
+#pragma unroll
+        for (int a = 0; a < TR; ++a)
+#pragma unroll
+          for (int b = 0; b < TC; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
+      }
     }
   }
-}
 
-__device__ inline void zero_acc(f32x16_t (&acc)[2][2]) {
+  // MODE 0: C = acc; MODE 1: C -= acc.  32x32 accumulator layout: lane holds
+  // column lane % 32; register v holds row 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+  template <int MODE>
+  __device__ void store(float* C, int64_t ldc) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WC, wn = wave % WC;
+    const int lr = lane & 31, lk = lane >> 5;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < TR; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < TC; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-}
+        for (int v = 0; v < 16; ++v) {
+          const int r = (wm * TR + a) * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+          const int c = (wn * TC + b) * 32 + lr;
+          float* dst = C + (int64_t)r * ldc + c;
+          if (MODE == 0) *dst = acc[a][b][v];
+          else *dst -= acc[a][b][v];
+        }
+  }
+};
 
-// mode 0: C = acc; mode 1: C -= acc
-template <int MODE>
-__device__ inline void tile_store(float* C, int64_t ldc, const f32x16_t (&acc)[2][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + 32 * a + 8 * (v >> 2) + 4 * lk + (v & 3);
-        const int c = wn * 64 + 32 * b + lr;
-        float* dst = C + (int64_t)r * ldc + c;
-        if (MODE == 0) *dst = acc[a][b][v];
-        else *dst -= acc[a][b][v];
-      }
-}
-
-// L_ip = A_ip Linv^T -> A_ip ; M_ip = L_ip Linv -> M[i]
-__global__ void __launch_bounds__(256) chol_panel(int64_t npad, int p, CholWs w) {
+// Quarter tiles (128 x 32) of Lp_i = A_ip Linv^T (i > p) and
+// Yp_c = Linv B_pc (c <= p).
+__global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
   float* sA = sm;
   float* sB = sm + KS * LDT;
-  const int i = p + 1 + blockIdx.x;
-  float* Aip = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
-  const float* Lv = w.Linv + (int64_t)p * NB * NB;
-  f32x16_t acc[2][2];
-  zero_acc(acc);
-  tile_mma<XK, XK>(acc, Aip, npad, Lv, NB, NB, sA, sB);  // B(j, k) = Linv[j][k]
-  __syncthreads();
-  tile_store<0>(Aip, npad, acc);
-  // the tile is read back below by other waves of this workgroup
-  __threadfence();
-  __syncthreads();
-  __threadfence();
-  zero_acc(acc);
-  tile_mma<XK, KX>(acc, Aip, npad, Lv, NB, NB, sA, sB);  // B(j, k) = Linv[k][j]
-  tile_store<0>(w.M + (int64_t)i * NB * NB, NB, acc);
+  const int q = P - p - 1;
+  const int t = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  TileMma<4, 1, 1, 1> mm;
+  mm.zero();
+  if (t < q) {
+    const int i = p + 1 + t;
+    const float* Aip = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
+    // B(j, k) = Linv[32 quarter + j][k]
+    mm.run<XK, XK>(Aip, npad, w.Linv + (int64_t)32 * quarter * NB, NB, sA, sB);
+    mm.store<0>(w.Lp + (int64_t)i * NB * NB + 32 * quarter, NB);
+  } else {
+    const int c = t - q;
+    // A(i, k) = Linv[i][k]; B(j, k) = B[p NB + k][c NB + 32 quarter + j]
+    const float* Bpc = w.B + (int64_t)p * NB * npad + (int64_t)c * NB + 32 * quarter;
+    mm.run<XK, KX>(w.Linv, NB, Bpc, npad, sA, sB);
+    mm.store<0>(w.Yp + (int64_t)c * NB + 32 * quarter, npad);
+  }
 }
 
-// SYRK tiles (i >= j > p) then B-update tiles (i > p, c <= p)
+// SYRK tiles (i >= j > p), then forward-substitution tiles (i > p, c <= p),
+// then the copy of Y_p into row block p of B.
 __global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
   float* sA = sm;
   float* sB = sm + KS * LDT;
-  const int q = P - p - 1;             // row tiles below the panel
+  const int q = P - p - 1;
   const int nsyrk = q * (q + 1) / 2;
+  const int nfwd = q * (p + 1);
   int t = blockIdx.x;
-  f32x16_t acc[2][2];
-  zero_acc(acc);
-  if (t < nsyrk) {
-    int a = 0;
-    while (t >= a + 1) { t -= a + 1; ++a; }
-    const int i = p + 1 + a, j = p + 1 + t;   // j <= i
-    const float* Li = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
-    const float* Lj = w.A + (int64_t)j * NB * npad + (int64_t)p * NB;
-    tile_mma<XK, XK>(acc, Li, npad, Lj, npad, NB, sA, sB);
-    tile_store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB, npad, acc);
+  if (t < nsyrk + nfwd) {
+    TileMma<2, 2, 2, 2> mm;
+    mm.zero();
+    if (t < nsyrk) {
+      int a = 0;
+      while (t >= a + 1) { t -= a + 1; ++a; }
+      const int i = p + 1 + a, j = p + 1 + t;   // j <= i
+      mm.run<XK, XK>(w.Lp + (int64_t)i * NB * NB, NB, w.Lp + (int64_t)j * NB * NB, NB, sA, sB);
+      mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB, npad);
+    } else {
+      t -= nsyrk;
+      const int i = p + 1 + t / (p + 1), c = t % (p + 1);
+      mm.run<XK, KX>(w.Lp + (int64_t)i * NB * NB, NB, w.Yp + (int64_t)c * NB, npad, sA, sB);
+      mm.store<1>(w.B + (int64_t)i * NB * npad + (int64_t)c * NB, npad);
+    }
   } else {
-    t -= nsyrk;
-    const int i = p + 1 + t / (p + 1), c = t % (p + 1);
-    const float* Mi = w.M + (int64_t)i * NB * NB;
-    const float* Bp = w.B + (int64_t)p * NB * npad + (int64_t)c * NB;
-    tile_mma<XK, KX>(acc, Mi, NB, Bp, npad, NB, sA, sB);
-    tile_store<1>(w.B + (int64_t)i * NB * npad + (int64_t)c * NB, npad, acc);
+    const int c = t - nsyrk - nfwd;   // copy tile c of Y_p
+    const float* src = w.Yp + (int64_t)c * NB;
+    float* dst = w.B + (int64_t)p * NB * npad + (int64_t)c * NB;
+    for (int e = threadIdx.x; e < NB * NB / 4; e += 256) {
+      const int r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
+      *reinterpret_cast<float4*>(dst + (int64_t)r * npad + c4) =
+          *reinterpret_cast<const float4*>(src + (int64_t)r * npad + c4);
+    }
   }
-}
-
-// Y_p[:, c] = Linv_pp B_p[:, c] in place, for all p and c <= p.
-__global__ void __launch_bounds__(256) chol_finish_y(int64_t npad, CholWs w) {
-  if (*w.flag) return;
-  extern __shared__ __align__(16) float sm[];
-  float* sA = sm;
-  float* sB = sm + KS * LDT;
-  int t = blockIdx.x, p = 0;
-  while (t >= p + 1) { t -= p + 1; ++p; }
-  const int c = t;
-  float* Bt = w.B + (int64_t)p * NB * npad + (int64_t)c * NB;
-  const float* Lv = w.Linv + (int64_t)p * NB * NB;
-  f32x16_t acc[2][2];
-  zero_acc(acc);
-  tile_mma<XK, KX>(acc, Lv, NB, Bt, npad, NB, sA, sB);
-  __syncthreads();
-  tile_store<0>(Bt, npad, acc);
 }
 
 // R[a][b] = Y[n-1-a][n-1-b] for b >= a, 0 below the diagonal.
@@ -425,23 +464,17 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
                        (const int32_t*)perm, npad, w);
     KQ_LAUNCHED("chol_gather");
   }
-  const size_t lds_diag = (size_t)(NB * NB + NB) * sizeof(double);
   const size_t lds_tile = 2 * (size_t)KS * LDT * sizeof(float);
-  KQ_HIP(hipFuncSetAttribute((const void*)chol_diag, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)lds_diag));
   for (int p = 0; p < P; ++p) {
-    hipLaunchKernelGGL(chol_diag, dim3(1), dim3(256), lds_diag, s, npad, n, p, w);
+    hipLaunchKernelGGL(chol_diag, dim3(1), dim3(512), 0, s, npad, n, p, w);
     KQ_LAUNCHED("chol_diag");
     const int q = P - p - 1;
-    if (q == 0) break;
-    hipLaunchKernelGGL(chol_panel, dim3(q), dim3(256), lds_tile, s, npad, p, w);
+    hipLaunchKernelGGL(chol_panel, dim3(4 * (q + p + 1)), dim3(256), lds_tile, s, npad, P, p, w);
     KQ_LAUNCHED("chol_panel");
-    const int tiles = q * (q + 1) / 2 + q * (p + 1);
+    const int tiles = q * (q + 1) / 2 + q * (p + 1) + (p + 1);
     hipLaunchKernelGGL(chol_update, dim3(tiles), dim3(256), lds_tile, s, npad, P, p, w);
     KQ_LAUNCHED("chol_update");
   }
-  hipLaunchKernelGGL(chol_finish_y, dim3(P * (P + 1) / 2), dim3(256), lds_tile, s, npad, w);
-  KQ_LAUNCHED("chol_finish_y");
   {
     const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 64);
     hipLaunchKernelGGL(chol_flip, dim3(gx, (unsigned)n), dim3(256), 0, s, n, npad, R, ldr, w);

@@ -47,6 +47,23 @@ struct GptqParams {
   const double* pc;        // per-channel (scale, zero) pairs, m x 2
 };
 
+// value of `x` held by lane 16 * (lane / 16) + o, for every lane: four
+// uniform-index lane reads (no LDS round trip) and a select by row group
+__device__ __forceinline__ double bcast_row(double x, int o, int lane) {
+  const long long b = __double_as_longlong(x);
+  const int lo = (int)(b & 0xffffffffLL), hi = (int)(b >> 32);
+  long long r[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const unsigned l = (unsigned)__builtin_amdgcn_readlane(lo, 16 * g + o);
+    const unsigned h = (unsigned)__builtin_amdgcn_readlane(hi, 16 * g + o);
+    r[g] = (long long)(((unsigned long long)h << 32) | l);
+  }
+  const int g = lane >> 4;
+  const long long y = g == 0 ? r[0] : g == 1 ? r[1] : g == 2 ? r[2] : r[3];
+  return __longlong_as_double(y);
+}
+
 __device__ __forceinline__ int64_t colmap(const GptqParams& p, int64_t j) {
   return p.perm ? (int64_t)p.perm[j] : j;
 }
@@ -116,6 +133,7 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
     scale = p.pc[2 * grow];
     zero = p.pc[2 * grow + 1];
   }
+  double inv_scale = 1.0 / scale;
 
   const int nblocks = (int)((p.n + BLK - 1) / BLK);
   for (int b = 0; b < nblocks; ++b) {
@@ -127,23 +145,42 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
       f64x4_t acc[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-      const int64_t kq = jb / 4;
+      const int64_t kq = jb / 4;  // multiple of 32
       const int64_t k_lo = kq * wave, k_hi = kq * (wave + 1);
       const int64_t arow = row0 + (lane & 15);
       const bool arow_ok = arow < p.m;
       const double* Erow = p.E + (arow_ok ? arow : 0) * p.ldE;
-      for (int64_t k0 = k_lo; k0 < k_hi; k0 += 4) {
-        const int64_t k = k0 + (lane >> 4);
-        const double a = arow_ok ? Erow[k] : 0.0;
-        const float* Rk = p.R + k * p.ldr + jb + (lane & 15);
-        double bv[8];
+      const int cl = lane & 15, kl = lane >> 4;
+      bool cok[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int64_t c = jb + 16 * t + (lane & 15);
-          bv[t] = (c < p.n) ? (double)Rk[16 * t] : 0.0;
+      for (int t = 0; t < 8; ++t) cok[t] = (jb + 16 * t + cl) < p.n;
+      // batches of 16 k (4 MFMA k-steps), double-buffered in registers
+      double ea[2][4];
+      float rb[2][4][8];
+      auto load = [&](int buf, int64_t kb) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int64_t k = kb + 4 * s4 + kl;
+          ea[buf][s4] = arow_ok ? Erow[k] : 0.0;
+          const float* Rk = p.R + k * p.ldr + jb + cl;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) rb[buf][s4][t] = cok[t] ? Rk[16 * t] : 0.f;
         }
+      };
+      auto mma = [&](int buf) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv[t], acc[t], 0, 0, 0);
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(ea[buf][s4], (double)rb[buf][s4][t], acc[t],
+                                                          0, 0, 0);
+      };
+      if (k_lo < k_hi) load(0, k_lo);
+      for (int64_t kb = k_lo; kb < k_hi; kb += 32) {
+        load(1, kb + 16);
+        mma(0);
+        if (kb + 32 < k_hi) load(0, kb + 32);
+        mma(1);
       }
       // partial of this wave -> LDS; f64 16x16 accumulator layout: lane holds
       // column lane % 16, register v holds row 4 * v + lane / 16
@@ -153,13 +190,16 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) pw[(4 * v + (lane >> 4)) * BLK + 16 * t + (lane & 15)] = acc[t][v];
     }
-    // stage the diagonal block of R
+    // stage the diagonal block of R: strictly upper part (zeros on and below
+    // the diagonal, so compensating with a row needs no column test) and the
+    // reciprocal diagonal
     for (int e = tid; e < BLK * BLK; e += GT) {
       const int i = e / BLK, j = e % BLK;
-      Rb[i * RLD + j] = (i < ncols && j < ncols) ? p.R[(jb + i) * p.ldr + jb + j] : 0.f;
+      Rb[i * RLD + j] = (i < ncols && j < ncols && j > i) ? p.R[(jb + i) * p.ldr + jb + j] : 0.f;
     }
+    for (int i = tid; i < BLK; i += GT)
+      invd[i] = (i < ncols) ? 1.0 / (double)p.R[(jb + i) * p.ldr + jb + i] : 0.0;
     __syncthreads();
-    for (int i = tid; i < BLK; i += GT) invd[i] = (i < ncols) ? 1.0 / (double)Rb[i * RLD + i] : 0.0;
     // reduce the four partials and add W (natural column perm[jb + c])
     for (int e = tid; e < RT * BLK; e += GT) {
       const int r = e / BLK, c = e % BLK;
@@ -203,6 +243,7 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
             hi = fmax(hi, __shfl_xor(hi, off, 16));
           }
           grid_params(lo, hi, p.bits, scale, zero);
+          inv_scale = 1.0 / scale;
           if (part_id == o && row_ok) {
             const int64_t g = (jb + c) / p.group;
             p.scales[grow * p.ngroups + g] = (float)scale;
@@ -210,7 +251,7 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
           }
         }
         // owner lane: round column c
-        const double t = v[s] / scale + zero;
+        const double t = fma(v[s], inv_scale, zero);
         const double q = fmin(fmax(rint(t), 0.0), (double)maxq);
         const double w_q = scale * (q - zero);
         const double e = (v[s] - w_q) * invd[c];
@@ -220,15 +261,15 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
           tv[s] = t;
           qv[s] = (int)q;
         }
-        const double eb = __shfl(e, (lane & 48) | o, 64);
-        // compensate the later columns of the block held by this lane
+        const double eb = bcast_row(e, o, lane);
+        // compensate the later columns of the block held by this lane (the
+        // staged row is zero at and before column c)
         const float* Rrow = Rb + c * RLD + 8 * part_id;
         const float4 r0v = *reinterpret_cast<const float4*>(Rrow);
         const float4 r1v = *reinterpret_cast<const float4*>(Rrow + 4);
         const float rr[8] = {r0v.x, r0v.y, r0v.z, r0v.w, r1v.x, r1v.y, r1v.z, r1v.w};
 #pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2)
-          if (8 * part_id + q2 > c) v[q2] -= eb * (double)rr[q2];
+        for (int q2 = 0; q2 < 8; ++q2) v[q2] = fma(-eb, (double)rr[q2], v[q2]);
       }
     }
     // ---- 3. write errors and outputs of this block ----

@@ -275,6 +275,283 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_kernel(GramParams p) {
 }
 
 // =====================================================================
+// bf16 kernel, direct-to-LDS pipeline (d a multiple of 256)
+// =====================================================================
+//
+// Stage = 32 tokens of the I and J panels (256 features each), fetched with
+// global_load_lds (16 bytes per lane, no register staging) into a ring of D
+// LDS stages, so D - 1 stages of loads are in flight while one is consumed.
+// A panel stage is stored token-major (512-byte rows, as in memory) with its
+// 16-byte chunks XOR-swizzled by the token (chunk ^ SWZ[token % 4]); the MFMA
+// operands (8 consecutive tokens of one feature per lane) are read with the
+// transposing ds_read_b64_tr_b16: within each 16 lanes, lane j addresses token
+// t0 + j / 4, features f0 + 4 (j % 4) .. + 3, and lane i receives tokens
+// t0 .. t0 + 3 of feature f0 + i.  The swizzle keeps these reads free of bank
+// conflicts for 32 or 64 LDS banks.
+
+constexpr int V2K = 32;                    // tokens per stage
+constexpr int V2D = 4;                     // stages in the ring
+constexpr int V2ROW = BT * 2;              // bytes per token row of a panel
+constexpr int V2PANEL = V2K * V2ROW;       // bytes per panel stage (16 KiB)
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// chunk swizzle {0, 6, 12, 10}[token % 4]: within any 4 consecutive tokens the
+// swizzled chunk pairs are distinct mod 8 and the chunk quads distinct mod 16
+__device__ __forceinline__ int v2_swz(int token) { return (0xAC60 >> (4 * (token & 3))) & 15; }
+
+// Ring slots: panel I and panel J of each of the four stages are distinct LDS
+// objects so that the compiler's LDS-DMA tracking sees that refilling one
+// does not alias reads of another (otherwise every operand read would wait
+// for all loads in flight).  Diagonal tiles load their panel into both.
+struct V2Panel {
+  unsigned char b[V2PANEL];
+};
+
+template <int SLOT, int PN>
+__device__ __forceinline__ unsigned char* v2_panel() {
+  __shared__ __align__(16) V2Panel i0, i1, i2, i3, j0, j1, j2, j3;
+  if constexpr (PN == 0) {
+    if constexpr (SLOT == 0) return i0.b;
+    else if constexpr (SLOT == 1) return i1.b;
+    else if constexpr (SLOT == 2) return i2.b;
+    else return i3.b;
+  } else {
+    if constexpr (SLOT == 0) return j0.b;
+    else if constexpr (SLOT == 1) return j1.b;
+    else if constexpr (SLOT == 2) return j2.b;
+    else return j3.b;
+  }
+}
+
+// Per-lane state of the pipelined kernel.  Everything that depends on the
+// lane is computed once: the operand read offsets (the swizzle of a lane's
+// tokens is fixed because stage and half offsets are multiples of 4 tokens)
+// and the byte offsets of the lane's direct loads within a stage.
+struct V2Ctx {
+  const GramParams* p;
+  const unsigned char* gI;   // byte address of X[0][I0]
+  const unsigned char* gJ;   // byte address of X[0][J0]
+  int64_t row_bytes;         // lda * 2
+  int rdI[4], rdJ[4];        // LDS byte offsets of the operand reads (token 0 of the half)
+  int ldoff[4];              // byte offset of load q within a stage (token row * row_bytes + chunk)
+  int wave, lane;
+};
+
+// An empty register-only asm hides the value of `x` from the optimizer, so the
+// panel-base additions below are redone at each use instead of being hoisted
+// out of the loop into one live register per (slot, panel, operand).
+__device__ __forceinline__ int v2_opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Stages here are always whole (the host hands a token tail shorter than a
+// stage to the generic kernel), so a load is a uniform base plus the lane's
+// fixed 32-bit offset.
+template <int SLOT, int PN>
+__device__ __forceinline__ void v2_issue_panel(const V2Ctx& c, int64_t tok0) {
+  unsigned char* lbase = v2_panel<SLOT, PN>() + c.wave * 4 * 2 * V2ROW;
+  const unsigned char* gbase = (PN ? c.gJ : c.gI) + tok0 * c.row_bytes;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_global_load_lds((const void*)(gbase + v2_opaque(c.ldoff[q])),
+                                     (lds_void_t*)(lbase + q * 2 * V2ROW), 16, 0, 0);
+}
+
+template <int SLOT>
+__device__ __forceinline__ void v2_issue(const V2Ctx& c, int64_t st) {
+  v2_issue_panel<SLOT, 0>(c, st * V2K);
+  v2_issue_panel<SLOT, 1>(c, st * V2K);
+}
+
+// tokens 0..3 and 4..7 of one feature -> the 8-value MFMA operand
+__device__ __forceinline__ bf16x8_t v2_cat(i16x4_t lo, i16x4_t hi) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ i16x4_t v2_ld(const unsigned char* ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)ptr);
+}
+
+// operands of one 16-token half (HALF = 0, 1) of the stage in slot SLOT
+struct V2Half {
+  bf16x8_t a[4], b[4];
+};
+
+template <int SLOT, int HALF>
+__device__ __forceinline__ void v2_read(const V2Ctx& c, V2Half& f) {
+  const unsigned char* PI = v2_panel<SLOT, 0>() + HALF * 16 * V2ROW;
+  const unsigned char* PJ = v2_panel<SLOT, 1>() + HALF * 16 * V2ROW;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const unsigned char* q = PI + v2_opaque(c.rdI[a]);
+    f.a[a] = v2_cat(v2_ld(q), v2_ld(q + 4 * V2ROW));
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const unsigned char* q = PJ + v2_opaque(c.rdJ[b]);
+    f.b[b] = v2_cat(v2_ld(q), v2_ld(q + 4 * V2ROW));
+  }
+}
+
+__device__ __forceinline__ void v2_mma(const V2Half& f, f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[a], f.b[b], acc[a][b], 0, 0, 0);
+}
+
+// interleave 16 MFMAs with the 16 operand reads issued just before them
+__device__ __forceinline__ void v2_interleave() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+}
+
+// wait until at most `ahead` later stages of this wave's loads (8 per stage)
+// are in flight
+__device__ __forceinline__ void v2_wait(int64_t ahead) {
+  if (ahead >= 3) __builtin_amdgcn_s_waitcnt((24 & 15) | (7 << 4) | (15 << 8) | ((24 >> 4) << 14));
+  else if (ahead == 2) __builtin_amdgcn_s_waitcnt((16 & 15) | (7 << 4) | (15 << 8) | ((16 >> 4) << 14));
+  else if (ahead == 1) __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+  else __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
+}
+
+// Step `it` with slot K = it % 4.  On entry H0 holds the first half of stage
+// it.  First half: multiply H0 while reading the second half into H1.  Then
+// wait for stage it + 1 and synchronize (every wave has finished reading slot
+// K), refill slot K with stage it + 4, and multiply H1 while reading the first
+// half of stage it + 1 into H0.  The multiply path is unconditional (after the
+// last stage the read of "stage it + 1" only fetches stale LDS data that is
+// never used), so the accumulators never meet at a control-flow join.
+template <int K>
+__device__ __forceinline__ void v2_step(const V2Ctx& c, int64_t it, int64_t st0, int64_t nstages,
+                                        V2Half& H0, V2Half& H1, f32x16_t (&acc)[4][4]) {
+  v2_read<K, 1>(c, H1);
+  v2_mma(H0, acc);
+  v2_interleave();
+  v2_wait(max<int64_t>(0, min<int64_t>(V2D - 2, nstages - 2 - it)));
+  __builtin_amdgcn_s_barrier();
+  if (it + V2D < nstages) v2_issue<K>(c, st0 + it + V2D);
+  v2_read<(K + 1) % V2D, 0>(c, H0);
+  v2_mma(H1, acc);
+  v2_interleave();
+}
+
+__global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p) {
+  int item;
+  if (!my_item(p, item)) return;
+  const int s = item / p.ntiles;
+  const int t = item % p.ntiles;
+  int ti, tj;
+  tile_coords(t, p.T, ti, tj);
+  const int64_t I0 = (int64_t)ti * BT, J0 = (int64_t)tj * BT;
+  const bool diag = ti == tj;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  V2Ctx c;
+  c.p = &p;
+  c.wave = wave;
+  c.lane = lane;
+  c.row_bytes = p.lda * 2;
+  c.gI = static_cast<const unsigned char*>(p.A) + I0 * 2;
+  c.gJ = static_cast<const unsigned char*>(p.A) + J0 * 2;
+  {
+    // operand reads: group g = lane / 16, j = lane % 16 addresses token
+    // 8 (g / 2) + j / 4 (+ 4 for the second read) and features
+    // base + 16 (g % 2) + 4 (j % 4) .. + 3
+    const int g = lane >> 4, j = lane & 15;
+    const int tok = 8 * (g >> 1) + (j >> 2);
+    const int sw = v2_swz(tok);
+    const int fo = 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int fi = wm * 128 + 32 * a + fo, fj = wn * 128 + 32 * a + fo;
+      c.rdI[a] = tok * V2ROW + (((fi >> 3) ^ sw) << 4) + (fi & 7) * 2;
+      c.rdJ[a] = tok * V2ROW + (((fj >> 3) ^ sw) << 4) + (fj & 7) * 2;
+    }
+    // loads: row pair 4 * wave + q; lane covers token row 2 * pair + lane / 32
+    // and LDS chunk lane % 32, holding logical chunk (lane % 32) ^ swz(row)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 2 * (4 * wave + q) + (lane >> 5);
+      const int lchunk = (lane & 31) ^ v2_swz(row);
+      c.ldoff[q] = (int)(row * c.row_bytes) + lchunk * 16;
+    }
+  }
+  (void)diag;
+  // token range of this split: whole units of V2D stages (N is a multiple of
+  // V2D * V2K tokens and the unit count is at least S)
+  const int64_t nunits = p.N / (V2D * V2K);
+  const int64_t u0 = nunits * s / p.S, u1 = nunits * (s + 1) / p.S;
+  const int64_t st0 = V2D * u0, nstages = V2D * (u1 - u0);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  V2Half H0, H1;
+  v2_issue<0>(c, st0);
+  v2_issue<1>(c, st0 + 1);
+  v2_issue<2>(c, st0 + 2);
+  v2_issue<3>(c, st0 + 3);
+  v2_wait(V2D - 1);
+  __builtin_amdgcn_s_barrier();
+  v2_read<0, 0>(c, H0);
+  for (int64_t it = 0; it < nstages; it += V2D) {
+    v2_step<0>(c, it, st0, nstages, H0, H1, acc);
+    v2_step<1>(c, it + 1, st0, nstages, H0, H1, acc);
+    v2_step<2>(c, it + 2, st0, nstages, H0, H1, acc);
+    v2_step<3>(c, it + 3, st0, nstages, H0, H1, acc);
+  }
+
+  const int lr = lane & 31, lk = lane >> 5;
+  if (p.S == 1) {
+    const int64_t ib = I0 + wm * 128 + 4 * lk, jb = J0 + wn * 128 + lr;
+    const bool beta0 = (p.beta == 0.0f);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t i = ib + 32 * a + 8 * (v >> 2) + (v & 3);
+          const int64_t jj = jb + 32 * b;
+          const float x = p.scale * acc[a][b][v];
+          float* h = p.H + i * p.ldh + jj;
+          *h = beta0 ? x : fmaf(p.beta, *h, x);
+          if (!diag) {
+            float* gg = p.H + jj * p.ldh + i;
+            *gg = beta0 ? x : fmaf(p.beta, *gg, x);
+          }
+        }
+  } else {
+    float* out = p.part + (int64_t)item * BT * BT + (wm * 128 + 4 * lk) * BT + wn * 128 + lr;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          __builtin_nontemporal_store(acc[a][b][v],
+                                      out + (32 * a + 8 * (v >> 2) + (v & 3)) * BT + 32 * b);
+  }
+}
+
+// =====================================================================
 // fp32 kernel
 // =====================================================================
 
@@ -435,14 +712,55 @@ void plan(int64_t N, int64_t d, int32_t dtype, int& T, int& ntiles, int& S, int6
 
 }  // namespace
 
+// workspace: the split-K partial tiles (S > 1)
 size_t gram_ws_bytes(int64_t N, int64_t d, int32_t dtype) {
   int T, ntiles, S;
   int64_t nstages;
   plan(N, d, dtype, T, ntiles, S, nstages);
-  if (S == 1) return 0;
   const int ts = (dtype == KRONQ_BF16) ? BT : FT;
-  return (size_t)ntiles * (size_t)S * (size_t)ts * (size_t)ts * sizeof(float);
+  return (S == 1) ? 0 : (size_t)ntiles * (size_t)S * (size_t)ts * (size_t)ts * sizeof(float);
 }
+
+namespace {
+
+// One launch of the split-K scheme for rows [0, p.N) of p.A with the split
+// count already planned; `kind` 0 = direct-to-LDS bf16 pipeline (N a multiple
+// of V2K, d a multiple of 256), 1 = generic bf16, 2 = fp32.
+kronq_status launch_gram(GramParams p, int kind, hipStream_t s) {
+  p.nitems = p.ntiles * p.S;
+  p.per_xcd = (p.nitems + kXcds - 1) / kXcds;
+  const int grid = p.per_xcd * kXcds;
+  if (kind == 0) {
+    hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(grid), dim3(BTHREADS), 0, s, p);
+    KQ_LAUNCHED("gram_bf16_lds_kernel");
+  } else if (kind == 1) {
+    const size_t lds = 4 * PANEL * sizeof(uint16_t);
+    if (p.d % 8 == 0) {
+      KQ_HIP(hipFuncSetAttribute((const void*)gram_bf16_kernel<false>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      hipLaunchKernelGGL(gram_bf16_kernel<false>, dim3(grid), dim3(BTHREADS), lds, s, p);
+    } else {
+      KQ_HIP(hipFuncSetAttribute((const void*)gram_bf16_kernel<true>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      hipLaunchKernelGGL(gram_bf16_kernel<true>, dim3(grid), dim3(BTHREADS), lds, s, p);
+    }
+    KQ_LAUNCHED("gram_bf16_kernel");
+  } else {
+    const size_t lds = 4 * FPANEL * sizeof(float);
+    hipLaunchKernelGGL(gram_f32_kernel, dim3(grid), dim3(256), lds, s, p);
+    KQ_LAUNCHED("gram_f32_kernel");
+  }
+  if (p.S > 1) {
+    if (kind == 2)
+      hipLaunchKernelGGL(gram_finalize_kernel<FT>, dim3(p.ntiles * (FT / (1024 / FT))), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(gram_finalize_kernel<BT>, dim3(p.ntiles * (BT / (1024 / BT))), dim3(256), 0, s, p);
+    KQ_LAUNCHED("gram_finalize_kernel");
+  }
+  return KRONQ_OK;
+}
+
+}  // namespace
 
 kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda, float* H,
                          int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
@@ -459,33 +777,28 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
   p.scale = scale;
   p.beta = beta;
   plan(N, d, dtype, p.T, p.ntiles, p.S, p.nstages);
-  p.nitems = p.ntiles * p.S;
-  p.per_xcd = (p.nitems + kXcds - 1) / kXcds;
-  const int grid = p.per_xcd * kXcds;
-  if (dtype == KRONQ_BF16) {
-    const size_t lds = 4 * PANEL * sizeof(uint16_t);
-    if (d % 8 == 0) {
-      KQ_HIP(hipFuncSetAttribute((const void*)gram_bf16_kernel<false>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      hipLaunchKernelGGL(gram_bf16_kernel<false>, dim3(grid), dim3(BTHREADS), lds, s, p);
-    } else {
-      KQ_HIP(hipFuncSetAttribute((const void*)gram_bf16_kernel<true>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      hipLaunchKernelGGL(gram_bf16_kernel<true>, dim3(grid), dim3(BTHREADS), lds, s, p);
-    }
-    KQ_LAUNCHED("gram_bf16_kernel");
-    if (p.S > 1) {
-      hipLaunchKernelGGL(gram_finalize_kernel<BT>, dim3(p.ntiles * (BT / (1024 / BT))), dim3(256), 0, s, p);
-      KQ_LAUNCHED("gram_finalize_kernel");
-    }
-  } else {
-    const size_t lds = 4 * FPANEL * sizeof(float);
-    hipLaunchKernelGGL(gram_f32_kernel, dim3(grid), dim3(256), lds, s, p);
-    KQ_LAUNCHED("gram_f32_kernel");
-    if (p.S > 1) {
-      hipLaunchKernelGGL(gram_finalize_kernel<FT>, dim3(p.ntiles * (FT / (1024 / FT))), dim3(256), 0, s, p);
-      KQ_LAUNCHED("gram_finalize_kernel");
-    }
+  if (dtype != KRONQ_BF16) return launch_gram(p, 2, s);
+  if (d % BT != 0) return launch_gram(p, 1, s);
+  // whole units of V2D stages (128 tokens) through the direct-to-LDS
+  // pipeline, then the remaining < 128 tokens accumulated by the generic
+  // kernel (beta = 1)
+  const int64_t unit = (int64_t)V2D * V2K;
+  const int64_t Nmain = N / unit * unit;
+  if (Nmain > 0) {
+    GramParams q = p;
+    q.N = Nmain;
+    q.S = (int)std::min<int64_t>(p.S, Nmain / unit);
+    kronq_status st = launch_gram(q, 0, s);
+    if (st) return st;
+  }
+  if (N > Nmain) {
+    GramParams q = p;
+    q.A = static_cast<const uint16_t*>(A) + Nmain * lda;
+    q.N = N - Nmain;
+    q.S = 1;
+    q.nstages = 1;
+    if (Nmain > 0) q.beta = 1.0f;
+    return launch_gram(q, 1, s);
   }
   return KRONQ_OK;
 }
