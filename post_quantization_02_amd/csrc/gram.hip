@@ -290,7 +290,10 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_kernel(GramParams p) {
 // conflicts for 32 or 64 LDS banks.
 
 constexpr int V2K = 32;                    // tokens per stage
-constexpr int V2D = 4;                     // stages in the ring
+#ifndef KRONQ_GRAM_RING
+#define KRONQ_GRAM_RING 4
+#endif
+constexpr int V2D = KRONQ_GRAM_RING;       // stages in the ring
 constexpr int V2ROW = BT * 2;              // bytes per token row of a panel
 constexpr int V2PANEL = V2K * V2ROW;       // bytes per panel stage (16 KiB)
 
@@ -303,28 +306,26 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // swizzled chunk pairs are distinct mod 8 and the chunk quads distinct mod 16
 __device__ __forceinline__ int v2_swz(int token) { return (0xAC60 >> (4 * (token & 3))) & 15; }
 
-// Ring slots: panel I and panel J of each of the four stages are distinct LDS
-// objects so that the compiler's LDS-DMA tracking sees that refilling one
-// does not alias reads of another (otherwise every operand read would wait
-// for all loads in flight).  Diagonal tiles load their panel into both.
-struct V2Panel {
-  unsigned char b[V2PANEL];
+// Ring slots: each stage slot (panels I and J) is a distinct LDS object, so
+// that the compiler's LDS-DMA tracking (which follows at most eight objects)
+// sees that refilling one slot does not alias reads of another; otherwise
+// every operand read would wait for all loads in flight.  Diagonal tiles load
+// their panel into both halves.
+// (Namespace-scope objects: a static local of the template below would be a
+// separate object in every instantiation.)
+struct V2Slot {
+  unsigned char b[2][V2PANEL];
 };
+__shared__ __align__(16) V2Slot v2_s0, v2_s1, v2_s2, v2_s3, v2_s4;
 
 template <int SLOT, int PN>
 __device__ __forceinline__ unsigned char* v2_panel() {
-  __shared__ __align__(16) V2Panel i0, i1, i2, i3, j0, j1, j2, j3;
-  if constexpr (PN == 0) {
-    if constexpr (SLOT == 0) return i0.b;
-    else if constexpr (SLOT == 1) return i1.b;
-    else if constexpr (SLOT == 2) return i2.b;
-    else return i3.b;
-  } else {
-    if constexpr (SLOT == 0) return j0.b;
-    else if constexpr (SLOT == 1) return j1.b;
-    else if constexpr (SLOT == 2) return j2.b;
-    else return j3.b;
-  }
+  static_assert(SLOT < V2D && V2D <= 5, "ring slot");
+  if constexpr (SLOT == 0) return v2_s0.b[PN];
+  else if constexpr (SLOT == 1) return v2_s1.b[PN];
+  else if constexpr (SLOT == 2) return v2_s2.b[PN];
+  else if constexpr (SLOT == 3) return v2_s3.b[PN];
+  else return v2_s4.b[PN];
 }
 
 // Per-lane state of the pipelined kernel.  Everything that depends on the
@@ -415,39 +416,66 @@ __device__ __forceinline__ void v2_interleave() {
   }
 }
 
-// wait until at most `ahead` later stages of this wave's loads (8 per stage)
-// are in flight
-__device__ __forceinline__ void v2_wait(int64_t ahead) {
-  if (ahead >= 3) __builtin_amdgcn_s_waitcnt((24 & 15) | (7 << 4) | (15 << 8) | ((24 >> 4) << 14));
-  else if (ahead == 2) __builtin_amdgcn_s_waitcnt((16 & 15) | (7 << 4) | (15 << 8) | ((16 >> 4) << 14));
-  else if (ahead == 1) __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
-  else __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
-}
+// s_waitcnt immediate: at most `vm` loads in flight (vmcnt, 6 bits split over
+// [3:0] and [15:14]), expcnt unconstrained, at most `lgkm` LDS operations
+constexpr int v2_cnt(int vm, int lgkm) { return (vm & 15) | (7 << 4) | (lgkm << 8) | ((vm >> 4) << 14); }
 
-// Step `it` with slot K = it % 4.  On entry H0 holds the first half of stage
-// it.  First half: multiply H0 while reading the second half into H1.  Then
-// wait for stage it + 1 and synchronize (every wave has finished reading slot
-// K), refill slot K with stage it + 4, and multiply H1 while reading the first
-// half of stage it + 1 into H0.  The multiply path is unconditional (after the
-// last stage the read of "stage it + 1" only fetches stale LDS data that is
-// never used), so the accumulators never meet at a control-flow join.
+// Wait until stage it + 1 of this wave's loads has landed (8 loads per stage;
+// stages it + 2 .. it + D - 1 stay in flight) and every LDS read of this wave has
+// returned, so that the barrier which follows orders all reads of slot K
+// before its refill.  Every step issues exactly one stage, so the count is
+// the same at every step.
+__device__ __forceinline__ void v2_wait_next() { __builtin_amdgcn_s_waitcnt(v2_cnt(8 * (V2D - 2), 0)); }
+
+// Step `it` with slot K = it mod D.  On entry H0 holds the first half of
+// stage it.  First half: multiply H0 while reading the second half into H1.
+// Then wait for stage it + 1 and synchronize (every wave has finished reading
+// slot K), refill slot K with stage it + D, and multiply H1 while reading the
+// first half of stage it + 1 into H0.
+//
+// The step has no branch.  Past the end of the split the refill loads the
+// split's last stage again (in bounds, never consumed), and after the last
+// stage the read of "stage it + 1" fetches LDS data that is never used.  A
+// conditional refill would leave a control-flow join after which the
+// compiler can no longer tell which ring slot a load writes, and it would then
+// make every operand read wait for all loads in flight; conditional multiplies
+// would merge the accumulators at a join.
 template <int K>
-__device__ __forceinline__ void v2_step(const V2Ctx& c, int64_t it, int64_t st0, int64_t nstages,
+__device__ __forceinline__ void v2_step(const V2Ctx& c, int64_t it, int64_t st0, int64_t st_last,
                                         V2Half& H0, V2Half& H1, f32x16_t (&acc)[4][4]) {
   v2_read<K, 1>(c, H1);
   v2_mma(H0, acc);
   v2_interleave();
-  v2_wait(max<int64_t>(0, min<int64_t>(V2D - 2, nstages - 2 - it)));
+  v2_wait_next();
   __builtin_amdgcn_s_barrier();
-  if (it + V2D < nstages) v2_issue<K>(c, st0 + it + V2D);
+  v2_issue<K>(c, min<int64_t>(st0 + it + V2D, st_last));
   v2_read<(K + 1) % V2D, 0>(c, H0);
   v2_mma(H1, acc);
   v2_interleave();
 }
 
+// Item of a pipelined-kernel workgroup.  XCD x (workgroup b runs on XCD b % 8)
+// owns the contiguous range of ceil(ntiles / 8) tiles starting at tile
+// x * ceil(ntiles / 8), compact in the super-tile order, and walks it once per
+// token split, split by split.  The tiles that run together on one XCD then
+// share most of their panels in its L2, and all XCDs stream the same token
+// range at about the same time, so the memory-side cache serves the panels
+// that several XCDs read.
+__device__ inline bool my_item_region(const GramParams& p, int& item) {
+  const int b = blockIdx.x;
+  const int x = b % kXcds, li = b / kXcds;
+  const int R = (p.ntiles + kXcds - 1) / kXcds;
+  const int r0 = x * R, rn = min(R, p.ntiles - r0);
+  if (rn <= 0) return false;
+  const int s = li / rn, t = r0 + li % rn;
+  if (s >= p.S) return false;
+  item = s * p.ntiles + t;
+  return true;
+}
+
 __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p) {
   int item;
-  if (!my_item(p, item)) return;
+  if (!my_item_region(p, item)) return;
   const int s = item / p.ntiles;
   const int t = item % p.ntiles;
   int ti, tj;
@@ -455,7 +483,9 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p
   const int64_t I0 = (int64_t)ti * BT, J0 = (int64_t)tj * BT;
   const bool diag = ti == tj;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave index as a uniform value, so LDS bases of the direct loads (M0) are
+  // scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
   V2Ctx c;
@@ -494,6 +524,7 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p
   const int64_t nunits = p.N / (V2D * V2K);
   const int64_t u0 = nunits * s / p.S, u1 = nunits * (s + 1) / p.S;
   const int64_t st0 = V2D * u0, nstages = V2D * (u1 - u0);
+  const int64_t st_last = st0 + nstages - 1;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -508,15 +539,20 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p
   v2_issue<1>(c, st0 + 1);
   v2_issue<2>(c, st0 + 2);
   v2_issue<3>(c, st0 + 3);
-  v2_wait(V2D - 1);
+  if constexpr (V2D > 4) v2_issue<V2D - 1>(c, st0 + V2D - 1);
+  __builtin_amdgcn_s_waitcnt(v2_cnt(8 * (V2D - 1), 0));  // stage 0 landed
   __builtin_amdgcn_s_barrier();
   v2_read<0, 0>(c, H0);
   for (int64_t it = 0; it < nstages; it += V2D) {
-    v2_step<0>(c, it, st0, nstages, H0, H1, acc);
-    v2_step<1>(c, it + 1, st0, nstages, H0, H1, acc);
-    v2_step<2>(c, it + 2, st0, nstages, H0, H1, acc);
-    v2_step<3>(c, it + 3, st0, nstages, H0, H1, acc);
+    v2_step<0>(c, it, st0, st_last, H0, H1, acc);
+    v2_step<1>(c, it + 1, st0, st_last, H0, H1, acc);
+    v2_step<2>(c, it + 2, st0, st_last, H0, H1, acc);
+    v2_step<3>(c, it + 3, st0, st_last, H0, H1, acc);
+    if constexpr (V2D > 4) v2_step<V2D - 1>(c, it + V2D - 1, st0, st_last, H0, H1, acc);
   }
+  // the refills past the end are still landing in LDS: drain them before the
+  // workgroup can exit
+  __builtin_amdgcn_s_waitcnt(v2_cnt(0, 0));
 
   const int lr = lane & 31, lk = lane >> 5;
   if (p.S == 1) {
@@ -685,17 +721,20 @@ __global__ void __launch_bounds__(256) gram_finalize_kernel(GramParams p) {
   for (int q = 0; q < 4; ++q) put(p, i, (int64_t)tj * TS + c + q, sum[q], !diag);
 }
 
-int choose_splits(int ntiles, int64_t nstages) {
-  // smallest S whose item count fills at least 90% of whole CU rounds; else the
-  // best fill; never more splits than stages
+int choose_splits(int ntiles, int64_t nstages, bool region) {
+  // smallest S whose item count fills at least 95% of whole CU rounds; else the
+  // best fill; never more splits than stages.  With the per-XCD tile regions
+  // of the pipelined kernel the rounds are counted per XCD.
   int best = 1;
   double best_eff = 0.0;
   const int smax = (int)std::min<int64_t>(64, nstages);
+  const int per_xcd_cus = kCUs / kXcds, R = (ntiles + kXcds - 1) / kXcds;
   for (int S = 1; S <= smax; ++S) {
     const int64_t items = (int64_t)ntiles * S;
-    const int64_t rounds = (items + kCUs - 1) / kCUs;
+    const int64_t rounds = region ? ((int64_t)R * S + per_xcd_cus - 1) / per_xcd_cus
+                                  : (items + kCUs - 1) / kCUs;
     const double eff = (double)items / (double)(rounds * kCUs);
-    if (eff >= 0.9) return S;
+    if (eff >= 0.95) return S;
     if (eff > best_eff + 1e-9) { best_eff = eff; best = S; }
   }
   return best;
@@ -707,7 +746,7 @@ void plan(int64_t N, int64_t d, int32_t dtype, int& T, int& ntiles, int& S, int6
   T = (int)((d + ts - 1) / ts);
   ntiles = T * (T + 1) / 2;
   nstages = (N + kst - 1) / kst;
-  S = choose_splits(ntiles, nstages);
+  S = choose_splits(ntiles, nstages, dtype == KRONQ_BF16 && d % BT == 0);
 }
 
 }  // namespace
@@ -731,7 +770,8 @@ kronq_status launch_gram(GramParams p, int kind, hipStream_t s) {
   p.per_xcd = (p.nitems + kXcds - 1) / kXcds;
   const int grid = p.per_xcd * kXcds;
   if (kind == 0) {
-    hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(grid), dim3(BTHREADS), 0, s, p);
+    const int rgrid = kXcds * ((p.ntiles + kXcds - 1) / kXcds) * p.S;
+    hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(rgrid), dim3(BTHREADS), 0, s, p);
     KQ_LAUNCHED("gram_bf16_lds_kernel");
   } else if (kind == 1) {
     const size_t lds = 4 * PANEL * sizeof(uint16_t);
