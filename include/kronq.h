@@ -127,8 +127,11 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
  * H is read only (n x n fp32 device, symmetric).  Computed in fp32 on the
  * matrix cores (blocked factorization of the reversed matrix, then a blocked
  * triangular inverse).
- * info  : host pointer; -1 on success, else the index (in processing order) of
- *         the first non-positive pivot, with KRONQ_ENOTPD returned.
+ * info  : host pointer; -1 on success.  When Hd is not positive definite,
+ *         KRONQ_ENOTPD is returned and info is the largest k (processing
+ *         order) whose trailing block Hd[k:, k:] is not positive definite
+ *         (the factorization runs on the reversed matrix, so this is where its
+ *         first non-positive pivot falls).
  * Synchronizes `stream` before returning.
  * ws    : kronq_chol_inv_ws(n) bytes.
  * ------------------------------------------------------------------------- */
@@ -151,7 +154,8 @@ kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda
  * (per-channel) or the current compensated values of the group when its first
  * column is reached.  The loop runs in fp64 (inputs fp32).
  * W        : m x n fp32 device, natural column order (read only).
- * R        : n x n fp32 device upper factor in processing order.
+ * R        : n x n fp32 device upper factor in processing order, 16-byte
+ *            aligned with ldr a multiple of 4 (else KRONQ_EINVAL).
  * perm     : device int32[n] or NULL (identity).
  * codes    : m x n uint8 device, natural column order, leading dimension n.
  * scales, zeros : m x ngroups fp32 device (ngroups = 1 per-channel, else

@@ -157,6 +157,8 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
     return fail(KRONQ_EINVAL, "kronq_gptq_quantize: NULL pointer");
   if (m < 1 || n < 1 || ldw < n || ldr < n)
     return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bad shape");
+  if (!aligned(R, 16) || ldr % 4 != 0)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: R must be 16-byte aligned with ldr a multiple of 4");
   if (q->bits < 1 || q->bits > 8)
     return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bits %d outside 1..8", (int)q->bits);
   if (q->group > 0 && n % q->group)

@@ -23,6 +23,8 @@ namespace kronq {
 namespace {
 
 typedef double f64x4_t __attribute__((__vector_size__(4 * sizeof(double))));
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int RT = 16;         // rows per workgroup
 constexpr int BLK = 128;       // columns per block
@@ -113,6 +115,45 @@ __global__ void __launch_bounds__(256) gptq_row_params(GptqParams p, double* pc)
   }
 }
 
+// Left-looking product of one block: the four waves split K = jb into
+// quarters (each a multiple of KB = 32) and walk theirs in batches of 32 k.
+// In MFMA step s of a batch, lane (r = lane % 16, g = lane / 16) supplies
+// E[row0 + r][kb + 8 g + s] and, for accumulator tile t, R[kb + 8 g + s][jb +
+// 8 r + t]: each lane loads 8 contiguous doubles of E and 8 rows of 8
+// contiguous floats of R per batch (16-byte loads), and tile t, column r holds
+// block column 8 r + t.
+constexpr int KB = 32;
+
+struct GqBatch {
+  f64x2_t e[4];       // E[arow][kb + 8 g .. + 7]
+  f32x4_t r[8][2];    // R[kb + 8 g + s][jb + 8 r .. + 7]
+};
+
+__device__ __forceinline__ void gq_load(GqBatch& B, const double* Eb, const float* Rb, int64_t ldr,
+                                        int64_t kb) {
+  const double* e = Eb + kb;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) B.e[q] = *reinterpret_cast<const f64x2_t*>(e + 2 * q);
+  const float* r = Rb + kb * ldr;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    B.r[s][0] = *reinterpret_cast<const f32x4_t*>(r + s * ldr);
+    B.r[s][1] = *reinterpret_cast<const f32x4_t*>(r + s * ldr + 4);
+  }
+}
+
+// acc[t] += E R over the batch; `live` false turns the batch into a no-op
+// (its E operand is zeroed) without a branch around the accumulators
+__device__ __forceinline__ void gq_mma(const GqBatch& B, bool live, f64x4_t (&acc)[8]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const double a = live ? B.e[s >> 1][s & 1] : 0.0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t >> 2][t & 3], acc[t], 0, 0, 0);
+  }
+}
+
 __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
   extern __shared__ __align__(16) double gl[];
   double* part = gl;                                       // 4 x RT x BLK doubles
@@ -145,68 +186,77 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
       f64x4_t acc[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-      const int64_t kq = jb / 4;  // multiple of 32
-      const int64_t k_lo = kq * wave, k_hi = kq * (wave + 1);
-      const int64_t arow = row0 + (lane & 15);
-      const bool arow_ok = arow < p.m;
-      const double* Erow = p.E + (arow_ok ? arow : 0) * p.ldE;
-      const int cl = lane & 15, kl = lane >> 4;
-      bool cok[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) cok[t] = (jb + 16 * t + cl) < p.n;
-      // batches of 16 k (4 MFMA k-steps), double-buffered in registers
-      double ea[2][4];
-      float rb[2][4][8];
-      auto load = [&](int buf, int64_t kb) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int64_t k = kb + 4 * s4 + kl;
-          ea[buf][s4] = arow_ok ? Erow[k] : 0.0;
-          const float* Rk = p.R + k * p.ldr + jb + cl;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) rb[buf][s4][t] = cok[t] ? Rk[16 * t] : 0.f;
+      const int64_t kq = jb / 4;  // multiple of KB
+      const int64_t k_lo = kq * wave;
+      const int nb = (int)(kq / KB);
+      if (nb > 0) {
+        const int r = lane & 15, g = lane >> 4;
+        // rows past m read row m - 1 (results discarded); columns past n in
+        // the last block read the next row of R or its padding (rows k < jb
+        // <= n - 2, so the reads stay inside R; results discarded)
+        const int64_t arow = min<int64_t>(row0 + r, p.m - 1);
+        const double* Eb = p.E + arow * p.ldE + 8 * g;
+        const float* Rg = p.R + (int64_t)(8 * g) * p.ldr + jb + 8 * r;
+        // two register buffers, each refilled a whole batch of MFMAs before
+        // it is consumed; the scheduling barriers keep the compiler from
+        // sinking the loads next to their use
+        GqBatch A, B;
+        gq_load(A, Eb, Rg, p.ldr, k_lo);
+        for (int i = 0; i < nb; i += 2) {
+          gq_load(B, Eb, Rg, p.ldr, k_lo + (int64_t)KB * min(i + 1, nb - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          gq_mma(A, true, acc);
+          __builtin_amdgcn_sched_barrier(0);
+          gq_load(A, Eb, Rg, p.ldr, k_lo + (int64_t)KB * min(i + 2, nb - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          gq_mma(B, i + 1 < nb, acc);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      auto mma = [&](int buf) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(ea[buf][s4], (double)rb[buf][s4][t], acc[t],
-                                                          0, 0, 0);
-      };
-      if (k_lo < k_hi) load(0, k_lo);
-      for (int64_t kb = k_lo; kb < k_hi; kb += 32) {
-        load(1, kb + 16);
-        mma(0);
-        if (kb + 32 < k_hi) load(0, kb + 32);
-        mma(1);
       }
-      // partial of this wave -> LDS; f64 16x16 accumulator layout: lane holds
-      // column lane % 16, register v holds row 4 * v + lane / 16
+      // partial of this wave -> LDS; f64 16x16 accumulator layout: register v
+      // holds row 4 v + lane / 16; tile t, lane column r is block column 8 r + t
       double* pw = part + wave * RT * BLK;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) pw[(4 * v + (lane >> 4)) * BLK + 16 * t + (lane & 15)] = acc[t][v];
+        for (int v = 0; v < 4; ++v) pw[(4 * v + (lane >> 4)) * BLK + 8 * (lane & 15) + t] = acc[t][v];
     }
     // stage the diagonal block of R: strictly upper part (zeros on and below
     // the diagonal, so compensating with a row needs no column test) and the
     // reciprocal diagonal
-    for (int e = tid; e < BLK * BLK; e += GT) {
-      const int i = e / BLK, j = e % BLK;
-      Rb[i * RLD + j] = (i < ncols && j < ncols && j > i) ? p.R[(jb + i) * p.ldr + jb + j] : 0.f;
+    if (ncols == BLK) {
+#pragma unroll
+      for (int q = 0; q < BLK * BLK / 4 / GT; ++q) {
+        const int e4 = tid + GT * q;
+        const int i = e4 / (BLK / 4), j = (e4 % (BLK / 4)) * 4;
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.R + (jb + i) * p.ldr + jb + j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (j + u > i) ? v[u] : 0.f;
+        *reinterpret_cast<f32x4_t*>(Rb + i * RLD + j) = v;
+      }
+    } else {
+      for (int e = tid; e < BLK * BLK; e += GT) {
+        const int i = e / BLK, j = e % BLK;
+        Rb[i * RLD + j] = (i < ncols && j < ncols && j > i) ? p.R[(jb + i) * p.ldr + jb + j] : 0.f;
+      }
     }
-    for (int i = tid; i < BLK; i += GT)
-      invd[i] = (i < ncols) ? 1.0 / (double)p.R[(jb + i) * p.ldr + jb + i] : 0.0;
+    for (int i = tid; i < BLK; i += GT) {
+      const int64_t ii = min<int64_t>(jb + i, p.n - 1);
+      const double rd = (double)p.R[ii * p.ldr + ii];
+      invd[i] = (i < ncols) ? 1.0 / rd : 0.0;
+    }
     __syncthreads();
-    // reduce the four partials and add W (natural column perm[jb + c])
+    // reduce the four partials and add W (natural column perm[jb + c]);
+    // rows past m and columns past n read clamped addresses and get zero
     for (int e = tid; e < RT * BLK; e += GT) {
       const int r = e / BLK, c = e % BLK;
       const int64_t gr = row0 + r;
-      double w = 0.0;
-      if (gr < p.m && c < ncols) w = (double)p.W[gr * p.ldw + colmap(p, jb + c)];
-      part[e] = w - (part[e] + part[RT * BLK + e] + part[2 * RT * BLK + e] + part[3 * RT * BLK + e]);
+      const bool ok = gr < p.m && c < ncols;
+      const int64_t wr = min<int64_t>(gr, p.m - 1);
+      const int64_t wc = colmap(p, min<int64_t>(jb + c, p.n - 1));
+      const double w = (double)p.W[wr * p.ldw + wc];
+      const double s4 = part[e] + part[RT * BLK + e] + part[2 * RT * BLK + e] + part[3 * RT * BLK + e];
+      part[e] = ok ? w - s4 : 0.0;
     }
     __syncthreads();
 
@@ -221,11 +271,13 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
       tv[s] = 0.0;
       qv[s] = 0;
     }
+    // Every column of the block is walked (past ncols the values, invd and
+    // staged rows are zero and nothing is stored), so the loop has no exit
+    // inside and the reads of R and invd do not wait on the chain.
     for (int o = 0; o < 16; ++o) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int c = 8 * o + s;
-        if (c >= ncols) break;
         if (p.group > 0 && (c % p.group) == 0) {
           // parameters of the group [c, c + group) from the current values
           double lo = INFINITY, hi = -INFINITY;
@@ -244,17 +296,21 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
           }
           grid_params(lo, hi, p.bits, scale, zero);
           inv_scale = 1.0 / scale;
-          if (part_id == o && row_ok) {
+          if (part_id == o && row_ok && c < ncols) {
             const int64_t g = (jb + c) / p.group;
             p.scales[grow * p.ngroups + g] = (float)scale;
             p.zeros[grow * p.ngroups + g] = (float)zero;
           }
         }
+        const float* Rrow = Rb + c * RLD + 8 * part_id;
+        const f32x4_t r0v = *reinterpret_cast<const f32x4_t*>(Rrow);
+        const f32x4_t r1v = *reinterpret_cast<const f32x4_t*>(Rrow + 4);
+        const double id = invd[c];
         // owner lane: round column c
         const double t = fma(v[s], inv_scale, zero);
         const double q = fmin(fmax(rint(t), 0.0), (double)maxq);
         const double w_q = scale * (q - zero);
-        const double e = (v[s] - w_q) * invd[c];
+        const double e = (v[s] - w_q) * id;
         if (part_id == o) {
           ev[s] = e;
           wq[s] = w_q;
@@ -264,12 +320,11 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
         const double eb = bcast_row(e, o, lane);
         // compensate the later columns of the block held by this lane (the
         // staged row is zero at and before column c)
-        const float* Rrow = Rb + c * RLD + 8 * part_id;
-        const float4 r0v = *reinterpret_cast<const float4*>(Rrow);
-        const float4 r1v = *reinterpret_cast<const float4*>(Rrow + 4);
-        const float rr[8] = {r0v.x, r0v.y, r0v.z, r0v.w, r1v.x, r1v.y, r1v.z, r1v.w};
 #pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) v[q2] = fma(-eb, (double)rr[q2], v[q2]);
+        for (int q2 = 0; q2 < 4; ++q2) {
+          v[q2] = fma(-eb, (double)r0v[q2], v[q2]);
+          v[4 + q2] = fma(-eb, (double)r1v[q2], v[4 + q2]);
+        }
       }
     }
     // ---- 3. write errors and outputs of this block ----
@@ -287,11 +342,11 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
         }
       }
     }
-    // E of this block must be visible to every wave before the next block's
-    // left-looking product (global memory, same workgroup)
-    __threadfence();
+    // E of this block is read by the other waves of this workgroup in the
+    // next block's product: the barrier's workgroup-scope release/acquire
+    // orders those global stores before the loads (the lines of the new
+    // columns were never cached by this CU)
     __syncthreads();
-    __threadfence();
   }
 }
 

@@ -118,6 +118,15 @@ def test_invalid_arguments_rejected_before_launch(lib):
     st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake, 8, None, ctypes.byref(q), fake, fake, fake,
                                  None, None, fake, 1 << 30, None)
     assert st == kq.KRONQ_EINVAL
+    # R not 16-byte aligned, ldr not a multiple of 4 (the product reads R rows
+    # with 16-byte loads)
+    q = kq.QCfg(2, 4)
+    st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake + 4, 8, None,
+                                 ctypes.byref(q), fake, fake, fake, None, None, fake, 1 << 30, None)
+    assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
+    st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake, 10, None, ctypes.byref(q), fake, fake, fake,
+                                 None, None, fake, 1 << 30, None)
+    assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
     # negative damping
     info = i64(0)
     st = lib.kronq_chol_inv(fake, 8, 8, -1.0, 0, fake, fake, 8, ctypes.byref(info), fake, 1 << 30, None)
