@@ -12,10 +12,10 @@
 // Blocked right-looking sweep over panels of NB = 128 columns of A (padded
 // with an identity block to a multiple of NB; the padding is block diagonal
 // with A so it changes nothing), solving L Y = I alongside (B starts as I):
-//   diag kernel   (1 workgroup, 512 threads): Cholesky of A_pp and, in the
-//                 same elimination sweep, Linv_pp (augmented [A_pp | I]); fp64
-//                 in registers, 8 x 8 elements per thread, 2 barriers per
-//                 column; pivots <= 0 are reported
+//   diag kernel   (1 workgroup): Cholesky of A_pp and Linv_pp in fp64, blocked
+//                 by 32 columns (one wave factors and inverts each 32 x 32
+//                 diagonal sub-block in registers; the sub-block products run
+//                 on the fp64 matrix cores); pivots <= 0 are reported
 //   panel kernel  : Lp_i = A_ip Linv_pp^T (i > p) and Yp_c = Linv_pp B_pc
 //                   (c <= p), each as four 128 x 32 quarter tiles
 //   update kernel : A_ij -= Lp_i Lp_j^T (i >= j > p; Cholesky SYRK),
@@ -143,122 +143,246 @@ __global__ void __launch_bounds__(256) chol_gather(const float* H, int64_t n, in
 }
 
 // ------------------------------------------------------- diagonal block
+//
+// Factor the diagonal block S = A_pp = L L^T and invert L (fp64, one
+// workgroup of four waves), blocked by SB = 32 columns:
+//   for kb = 0..3:
+//     B1 (wave 0): S_kk = L_kk L_kk^T and M_kk = L_kk^-1 column by column in
+//        registers: lanes 0..31 hold the rows of S_kk, lanes 32..63 the
+//        columns of the identity that becomes M_kk.  At step j both halves
+//        apply v[k] -= (v[j] / d) c[k] for k > j, with c = column j of S_kk
+//        (passed through LDS) and d = c[j]; the M half then scales v[j] by
+//        1 / sqrt(d).  No barrier inside.
+//     B2: L_ik = S_ik M_kk^T           (kb < i, one wave per block)
+//     B3: S_ij -= L_ik L_jk^T           (kb < j <= i)
+//   C: the blocked triangular inverse, one row block at a time:
+//      X_ii = M_ii,  X_ij = -M_ii sum_{k=j}^{i-1} L_ik X_kj   (j < i)
+// Only the lower triangle of S is read.  Block products are 32 x 32 x 32 on
+// v_mfma_f64_16x16x4f64, one wave each.
 
-// Row-block of the 8 x 8 element block held by a thread: the four waves of a
-// role take row blocks {w, 7-w, 8+w, 15-w} so that the lower-triangle work is
-// even across waves.
-__device__ __forceinline__ int diag_rowblock(int w, int r) {
-  return r == 0 ? w : r == 1 ? 7 - w : r == 2 ? 8 + w : 15 - w;
+constexpr int SB = 32;
+constexpr int NSB = NB / SB;       // sub-blocks per side
+constexpr int LDB = SB + 1;        // LDS row stride of a stored sub-block (doubles)
+constexpr int BLKD = SB * LDB;     // doubles per stored sub-block
+
+typedef double f64x4_t __attribute__((__vector_size__(4 * sizeof(double))));
+
+// lower sub-block (i >= j) -> slot
+__device__ __forceinline__ int lslot(int i, int j) { return i * (i + 1) / 2 + j; }
+
+// acc (2 x 2 tiles of 16 x 16) += sign * A B over 32 k, A(r, t) = pa[r * sar + t * sat],
+// B(t, c) = pb[t * sbt + c * sbc] (LDS).  Lane l supplies A(16 ti + l % 16, k0 + l / 16)
+// and B(k0 + l / 16, 16 tj + l % 16); register v of tile (ti, tj) holds element
+// (16 ti + 4 v + l / 16, 16 tj + l % 16).
+__device__ __forceinline__ void bmma(f64x4_t (&acc)[2][2], const double* pa, int sar, int sat,
+                                     const double* pb, int sbt, int sbc, double sign) {
+  const int l = threadIdx.x & 63, r = l & 15, kk = l >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < SB; k0 += 4) {
+    double av[2], bv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      av[t] = sign * pa[(16 * t + r) * sar + (k0 + kk) * sat];
+      bv[t] = pb[(k0 + kk) * sbt + (16 * t + r) * sbc];
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+        acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ti], bv[tj], acc[ti][tj], 0, 0, 0);
+  }
 }
 
-// Factor A_pp = L L^T and invert L in one elimination sweep over [A_pp | I]:
-// for each column j, l_jj = sqrt(a_jj), l_ij = a_ij / l_jj (i > j), row j of
-// the right-hand side becomes x_j = b_j / l_jj, then a_ik -= l_ij l_kj and
-// b_ic -= l_ij x_jc for i > j.  Threads 0..255 hold 8 x 8 blocks of A, threads
-// 256..511 the blocks of B (= L^-1 at the end), fp64 in registers.
-__global__ void __launch_bounds__(512) chol_diag(int64_t npad, int64_t n, int p, CholWs w) {
-  if (*w.flag) return;
-  __shared__ double col[NB];
-  __shared__ double xrow[NB];
-  __shared__ double piv;
-  __shared__ int bad;
-  const int tid = threadIdx.x;
-  const bool isA = tid < 256;
-  const int t = tid & 255;
-  const int wv = t >> 6, ln = t & 63;
-  const int bi = diag_rowblock(wv, ln >> 4);  // row block
-  const int bk = ln & 15;                     // column block
-  const bool act = bk <= bi;                  // lower-triangle block
-  double r[8][8];
-  const float* Ap = w.A + (int64_t)p * NB * npad + (int64_t)p * NB;
-  if (isA) {
+__device__ __forceinline__ void bzero(f64x4_t (&acc)[2][2]) {
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii)
+  for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        r[ii][kk] = act ? (double)Ap[(int64_t)(8 * bi + ii) * npad + 8 * bk + kk] : 0.0;
-  } else {
+    for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+}
+
+__device__ __forceinline__ void bload(f64x4_t (&acc)[2][2], const double* blk) {
+  const int l = threadIdx.x & 63;
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii)
+  for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) r[ii][kk] = (bi == bk && ii == kk) ? 1.0 : 0.0;
-  }
-  if (tid == 0) {
-    piv = r[0][0];
-    bad = -1;
-  }
-  __syncthreads();
-  // The broadcast column (l_ij, zero for i <= j) and row (x_jc, zero for
-  // c > j) make every update below uniform: each thread updates its whole
-  // 8 x 8 block; entries outside the trailing region receive zero, and the
-  // upper blocks that take part are never read.
-  for (int jb = 0; jb < NB / 8; ++jb) {
+    for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = 8 * jb + jj;
-      // ---- column j of L and row j of L^-1
-      const double d = piv;
-      if (isA && bk == jb) {
-        const double sd = sqrt(d), inv = 1.0 / sd;
+      for (int v = 0; v < 4; ++v) acc[ti][tj][v] = blk[(16 * ti + 4 * v + (l >> 4)) * LDB + 16 * tj + (l & 15)];
+}
+
+__device__ __forceinline__ void bstore(const f64x4_t (&acc)[2][2], double* blk) {
+  const int l = threadIdx.x & 63;
 #pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int i = 8 * bi + ii;
-          const double l = (i > j) ? r[ii][jj] * inv : 0.0;
-          if (i > j) r[ii][jj] = l;
-          if (i == j) r[ii][jj] = sd;
-          col[i] = l;
-        }
-        if (bi == jb && !(d > 0.0)) bad = j;
-      } else if (!isA && bi == jb) {
-        const double inv = 1.0 / sqrt(d);
+  for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const double x = (bk <= jb) ? r[jj][cc] * inv : 0.0;
-          if (bk <= jb) r[jj][cc] = x;
-          xrow[8 * bk + cc] = x;
-        }
-      }
-      __syncthreads();
-      if (bad >= 0) break;
-      // ---- trailing updates: a_ik -= l_ij l_kj ; b_ic -= l_ij x_jc
-      double ci[8], ck[8];
+    for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) ci[ii] = col[8 * bi + ii];
-      const double* src = isA ? col : xrow;
+      for (int v = 0; v < 4; ++v) blk[(16 * ti + 4 * v + (l >> 4)) * LDB + 16 * tj + (l & 15)] = acc[ti][tj][v];
+}
+
+// B1 on one wave: factor the stored block Sk (lower triangle read) and write
+// M = L^-1 (lower triangular) to Mk.  Returns the first column whose pivot is
+// not positive (or NaN), else -1; past a failed pivot the sweep continues with
+// d = 1 and its results are discarded.
+__device__ __noinline__ int diag_factor32(const double* Sk, double* Mk, double* col) {
+  const int l = threadIdx.x & 63, r = l & 31;
+  const bool isS = l < 32;
+  double v[SB], c[SB];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) ck[kk] = src[8 * bk + kk];
+  for (int k = 0; k < SB; ++k) v[k] = isS ? Sk[max(r, k) * LDB + min(r, k)] : (k == r ? 1.0 : 0.0);
+  if (isS) col[r] = v[0];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii)
+  for (int k = 0; k < SB; ++k) c[k] = col[k];
+  int bad = -1;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) r[ii][kk] = fma(-ci[ii], ck[kk], r[ii][kk]);
-      // next pivot (its owner updated it just above)
-      if (isA && j + 1 < NB) {
-        if (jj < 7) {
-          if (bi == jb && bk == jb) piv = r[jj + 1][jj + 1];
-        } else {
-          if (bi == jb + 1 && bk == jb + 1) piv = r[0][0];
-        }
-      }
-      __syncthreads();
+  for (int j = 0; j < SB; ++j) {
+    double d = c[j];
+    if (!(d > 0.0)) {
+      if (bad < 0) bad = j;
+      d = 1.0;
     }
-    if (bad >= 0) break;
+    // y = 1 / sqrt(d): hardware estimate refined by two Newton-Raphson steps
+    // y <- y (3 - d y^2) / 2
+    double y = __builtin_amdgcn_rsq(d);
+    y = y * fma(-0.5 * d, y * y, 1.5);
+    y = y * fma(-0.5 * d, y * y, 1.5);
+    const double coef = v[j] * (y * y);
+    double cn[SB];
+    if (j + 1 < SB) {
+      // next column first, so that its broadcast overlaps the rest of the update
+      v[j + 1] = fma(-coef, c[j + 1], v[j + 1]);
+      if (isS) col[r] = v[j + 1];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int k = 0; k < SB; ++k) cn[k] = col[k];
+    }
+#pragma unroll
+    for (int k = j + 2; k < SB; ++k) v[k] = fma(-coef, c[k], v[k]);
+    if (!isS) v[j] *= y;
+    if (j + 1 < SB) {
+#pragma unroll
+      for (int k = 0; k < SB; ++k) c[k] = cn[k];
+    }
   }
-  if (bad >= 0) {
+  if (!isS) {
+#pragma unroll
+    for (int i = 0; i < SB; ++i) Mk[i * LDB + r] = v[i];
+  }
+  return bad;
+}
+
+__global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p, CholWs w) {
+  if (*w.flag) return;
+  __shared__ double Ls[NSB * (NSB + 1) / 2 * BLKD];  // lower sub-blocks of S, then L, then X
+  __shared__ double Ms[NSB * BLKD];                  // M_kk = L_kk^-1
+  __shared__ double Ts[(NSB - 1) * BLKD];            // per-wave scratch of the inverse
+  __shared__ __align__(16) double col[SB];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x, wave = tid >> 6;
+
+  // ---- A: load the lower sub-blocks of A_pp (fp32 -> fp64)
+  {
+    const float* Ap = w.A + (int64_t)p * NB * npad + (int64_t)p * NB;
+    constexpr int NQ = NSB * (NSB + 1) / 2 * SB * (SB / 4);  // float4 count
+    for (int e = tid; e < NQ; e += 256) {
+      const int blk = e / (SB * SB / 4), rem = e % (SB * SB / 4);
+      const int r = rem / (SB / 4), c4 = (rem % (SB / 4)) * 4;
+      int bi = 0;
+      while (lslot(bi + 1, 0) <= blk) ++bi;
+      const int bj = blk - lslot(bi, 0);
+      const float4 v = *reinterpret_cast<const float4*>(Ap + (int64_t)(SB * bi + r) * npad + SB * bj + c4);
+      double* dst = Ls + blk * BLKD + r * LDB + c4;
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
+    }
+  }
+  if (tid == 0) s_bad = -1;
+  __syncthreads();
+
+  // ---- B: blocked factorization
+  for (int kb = 0; kb < NSB; ++kb) {
+    if (wave == 0) {
+      const int bad = diag_factor32(Ls + lslot(kb, kb) * BLKD, Ms + kb * BLKD, col);
+      if (tid == 0 && bad >= 0) s_bad = SB * kb + bad;
+    }
+    __syncthreads();
+    if (s_bad >= 0) break;
+    // B2: L_ik = S_ik M_kk^T
+    {
+      const int i = kb + 1 + wave;
+      if (i < NSB) {
+        f64x4_t acc[2][2];
+        bzero(acc);
+        double* Sik = Ls + lslot(i, kb) * BLKD;
+        bmma(acc, Sik, LDB, 1, Ms + kb * BLKD, 1, LDB, 1.0);
+        bstore(acc, Sik);
+      }
+    }
+    __syncthreads();
+    // B3: S_ij -= L_ik L_jk^T for kb < j <= i
+    {
+      const int q = NSB - 1 - kb;  // trailing sub-blocks per side
+      for (int t = wave; t < q * (q + 1) / 2; t += 4) {
+        int a = 0, u = t;
+        while (u > a) { u -= a + 1; ++a; }
+        const int i = kb + 1 + a, j = kb + 1 + u;
+        f64x4_t acc[2][2];
+        double* Sij = Ls + lslot(i, j) * BLKD;
+        bload(acc, Sij);
+        bmma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Ls + lslot(j, kb) * BLKD, 1, LDB, -1.0);
+        bstore(acc, Sij);
+      }
+    }
+    __syncthreads();
+  }
+  if (s_bad >= 0) {
     if (tid == 0) {
       // reversed position p*NB + bad is processing index n - 1 - that
-      const int64_t pos = (int64_t)p * NB + bad;
+      const int64_t pos = (int64_t)p * NB + s_bad;
       *w.info = (pos < n) ? (long long)(n - 1 - pos) : (long long)-2;
       *w.flag = 1;
     }
     return;
   }
-  if (!isA) {
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii)
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        w.Linv[(8 * bi + ii) * NB + 8 * bk + kk] =
-            (act && (bi > bk || kk <= ii)) ? (float)r[ii][kk] : 0.f;
+
+  // ---- C: X = L^-1, row block by row block (X_ij overwrites L_ij)
+  for (int i = 1; i < NSB; ++i) {
+    f64x4_t x[2][2];
+    if (wave < i) {
+      const int j = wave;
+      f64x4_t acc[2][2];
+      bzero(acc);
+      for (int k = j; k < i; ++k) {
+        const double* Xkj = (k == j) ? Ms + j * BLKD : Ls + lslot(k, j) * BLKD;
+        bmma(acc, Ls + lslot(i, k) * BLKD, LDB, 1, Xkj, LDB, 1, 1.0);
+      }
+      bstore(acc, Ts + j * BLKD);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      bzero(x);
+      bmma(x, Ms + i * BLKD, LDB, 1, Ts + j * BLKD, LDB, 1, -1.0);
+    }
+    __syncthreads();
+    if (wave < i) bstore(x, Ls + lslot(i, wave) * BLKD);
+    __syncthreads();
+  }
+
+  // ---- D: Linv (fp32, NB x NB, zeros above the diagonal)
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    const int bi = r / SB, bj = c / SB, rr = r % SB, cc = c % SB;
+    float v = 0.f;
+    if (bi > bj) v = (float)Ls[lslot(bi, bj) * BLKD + rr * LDB + cc];
+    else if (bi == bj) v = (float)Ms[bi * BLKD + rr * LDB + cc];
+    w.Linv[e] = v;
   }
 }
 
@@ -466,7 +590,7 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
   }
   const size_t lds_tile = 2 * (size_t)KS * LDT * sizeof(float);
   for (int p = 0; p < P; ++p) {
-    hipLaunchKernelGGL(chol_diag, dim3(1), dim3(512), 0, s, npad, n, p, w);
+    hipLaunchKernelGGL(chol_diag, dim3(1), dim3(256), 0, s, npad, n, p, w);
     KQ_LAUNCHED("chol_diag");
     const int q = P - p - 1;
     hipLaunchKernelGGL(chol_panel, dim3(4 * (q + p + 1)), dim3(256), lds_tile, s, npad, P, p, w);
