@@ -16,14 +16,26 @@
 //                 by 32 columns (one wave factors and inverts each 32 x 32
 //                 diagonal sub-block in registers; the sub-block products run
 //                 on the fp64 matrix cores); pivots <= 0 are reported
-//   panel kernel  : Lp_i = A_ip Linv_pp^T (i > p) and Yp_c = Linv_pp B_pc
-//                   (c <= p), each as four 128 x 32 quarter tiles
-//   update kernel : A_ij -= Lp_i Lp_j^T (i >= j > p; Cholesky SYRK),
-//                   B_ic -= Lp_i Yp_c   (i > p, c <= p; forward substitution),
-//                   B_pc  = Yp_c        (row block p of Y = L^-1 is final)
+//   panel kernels : PL: Lp_i = A_ip Linv_pp^T (i > p) and PY: Yp_c = Linv_pp
+//                   B_pc (c <= p), each as four 128 x 32 quarter tiles
+//   update kernels: U1: A_i,p+1 -= Lp_i Lp_p+1^T (i > p; the next column),
+//                   U2: A_ij -= Lp_i Lp_j^T (i >= j > p + 1; Cholesky SYRK),
+//                       B_ic -= Lp_i Yp_c   (i > p, c <= p; forward
+//                       substitution), B_pc = Yp_c (row block p of Y = L^-1)
 // and finally R = J Y J.  Tile products run on the fp32 matrix cores
-// (v_mfma_f32_32x32x2f32).  A device flag set by a failed pivot makes every
+// (v_mfma_f32_32x32x2f32).
+//
+// Look-ahead over two streams: the caller's stream carries the critical path
+// diag(p) -> PL(p) -> U1(p) -> diag(p + 1), and a second stream carries PY(p)
+// and U2(p), which overlap the next diagonal block.  Linv, Lp and Yp are
+// double-buffered by the parity of p.  Ordering: PY(p) waits for diag(p),
+// U2(p) for U1(p) (hence PL(p); the small critical-path update then does not
+// queue behind the large one), and U1(p) for U2(p - 1) (both write column
+// p + 1); the next use of a buffer of parity p % 2 (diag, PL at p + 2) comes
+// after U1(p + 1), hence after U2(p).  A device flag set by a failed pivot makes every
 // later kernel return at once; the host reads the flag after the last launch.
+#include <mutex>
+
 #include "kronq_internal.h"
 
 namespace kronq {
@@ -38,13 +50,19 @@ constexpr int LDT = NB + 1;   // odd LDS stride: conflict-free transposed stores
 struct CholWs {
   float* A;       // npad x npad (reversed, permuted, damped)
   float* B;       // npad x npad (forward substitution; ends as Y = L^-1)
-  float* Lp;      // npad x NB   (panel L_ip of the current step)
-  float* Yp;      // NB x npad   (row block Y_p of the current step)
-  float* Linv;    // NB x NB     (inverse of the current diagonal block)
+  float* Lp;      // npad x NB   (panel L_ip of step p; two buffers by p % 2)
+  float* Yp;      // NB x npad   (row block Y_p of step p; two buffers)
+  float* Linv;    // NB x NB     (inverse of diagonal block p; two buffers)
   double* damp;   // lambda * mean(diag H)
   int* flag;      // nonzero after a failed pivot
   long long* info;
+  int64_t sP;     // floats between the two Lp (and the two Yp) buffers
 };
+
+// buffer of parity `par` of a double-buffered array
+__device__ __forceinline__ float* lp_buf(const CholWs& w, int par) { return w.Lp + par * w.sP; }
+__device__ __forceinline__ float* yp_buf(const CholWs& w, int par) { return w.Yp + par * w.sP; }
+__device__ __forceinline__ float* linv_buf(const CholWs& w, int par) { return w.Linv + par * NB * NB; }
 
 size_t ws_layout(int64_t n, CholWs* w, void* base) {
   const int64_t npad = (n + NB - 1) / NB * NB;
@@ -57,11 +75,12 @@ size_t ws_layout(int64_t n, CholWs* w, void* base) {
   if (w) w->B = reinterpret_cast<float*>(b + off);
   off += sA;
   if (w) w->Lp = reinterpret_cast<float*>(b + off);
-  off += sP;
+  off += 2 * sP;
   if (w) w->Yp = reinterpret_cast<float*>(b + off);
-  off += sP;
+  off += 2 * sP;
   if (w) w->Linv = reinterpret_cast<float*>(b + off);
-  off += align_up((size_t)NB * NB * sizeof(float), 256);
+  off += 2 * align_up((size_t)NB * NB * sizeof(float), 256);
+  if (w) w->sP = (int64_t)(sP / sizeof(float));
   if (w) w->damp = reinterpret_cast<double*>(b + off);
   off += 256;
   if (w) w->flag = reinterpret_cast<int*>(b + off);
@@ -145,20 +164,19 @@ __global__ void __launch_bounds__(256) chol_gather(const float* H, int64_t n, in
 // ------------------------------------------------------- diagonal block
 //
 // Factor the diagonal block S = A_pp = L L^T and invert L (fp64, one
-// workgroup of four waves), blocked by SB = 32 columns:
+// workgroup of four waves), blocked by SB = 32 columns.  With M_kk = L_kk^-1,
+// X = L^-1 and the right-hand-side accumulators Bacc_ic = -sum_{k<i} L_ik X_kc:
 //   for kb = 0..3:
-//     B1 (wave 0): S_kk = L_kk L_kk^T and M_kk = L_kk^-1 column by column in
-//        registers: lanes 0..31 hold the rows of S_kk, lanes 32..63 the
-//        columns of the identity that becomes M_kk.  At step j both halves
-//        apply v[k] -= (v[j] / d) c[k] for k > j, with c = column j of S_kk
-//        (passed through LDS) and d = c[j]; the M half then scales v[j] by
-//        1 / sqrt(d).  No barrier inside.
-//     B2: L_ik = S_ik M_kk^T           (kb < i, one wave per block)
-//     B3: S_ij -= L_ik L_jk^T           (kb < j <= i)
-//   C: the blocked triangular inverse, one row block at a time:
-//      X_ii = M_ii,  X_ij = -M_ii sum_{k=j}^{i-1} L_ik X_kj   (j < i)
-// Only the lower triangle of S is read.  Block products are 32 x 32 x 32 on
-// v_mfma_f64_16x16x4f64, one wave each.
+//     B1 (wave 0): S_kk = L_kk L_kk^T and M_kk, two columns per step in
+//        registers (lanes 0..31 hold the rows of S_kk, lanes 32..63 the
+//        columns of the identity that becomes M_kk); the two current columns
+//        of S_kk reach every lane through LDS.  No barrier inside.
+//     P1: L_ik = S_ik M_kk^T (i > kb)   and   X_kb,c = M_kk Bacc_kb,c (c < kb)
+//     P2: S_ij -= L_ik L_jk^T (kb < j <= i)   and
+//         Bacc_ic -= L_ik X_kb,c (i > kb, c <= kb; X_kb,kb = M_kk)
+// At the end row block i of L^-1 is X_i0 .. X_i,i-1, M_ii.  Only the lower
+// triangle of S is read.  P1 and P2 are split into 16 x 16 output tiles
+// (K = 32 on v_mfma_f64_16x16x4f64) dealt round-robin to the four waves.
 
 constexpr int SB = 32;
 constexpr int NSB = NB / SB;       // sub-blocks per side
@@ -166,134 +184,154 @@ constexpr int LDB = SB + 1;        // LDS row stride of a stored sub-block (doub
 constexpr int BLKD = SB * LDB;     // doubles per stored sub-block
 
 typedef double f64x4_t __attribute__((__vector_size__(4 * sizeof(double))));
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
 
-// lower sub-block (i >= j) -> slot
+// lower sub-block (i >= j) -> slot; strictly lower (i > c) -> accumulator slot
 __device__ __forceinline__ int lslot(int i, int j) { return i * (i + 1) / 2 + j; }
+__device__ __forceinline__ int bslot(int i, int c) { return i * (i - 1) / 2 + c; }
 
-// acc (2 x 2 tiles of 16 x 16) += sign * A B over 32 k, A(r, t) = pa[r * sar + t * sat],
-// B(t, c) = pb[t * sbt + c * sbc] (LDS).  Lane l supplies A(16 ti + l % 16, k0 + l / 16)
-// and B(k0 + l / 16, 16 tj + l % 16); register v of tile (ti, tj) holds element
+// Tile (ti, tj) of acc + sign * A B over K = 32, A(r, t) = pa[r * sar + t * sat],
+// B(t, c) = pb[t * sbt + c * sbc] (LDS).  Lane l supplies A(16 ti + l % 16,
+// k0 + l / 16) and B(k0 + l / 16, 16 tj + l % 16); register v holds element
 // (16 ti + 4 v + l / 16, 16 tj + l % 16).
-__device__ __forceinline__ void bmma(f64x4_t (&acc)[2][2], const double* pa, int sar, int sat,
-                                     const double* pb, int sbt, int sbc, double sign) {
+__device__ __forceinline__ f64x4_t tile_mma(f64x4_t acc, const double* pa, int sar, int sat,
+                                            const double* pb, int sbt, int sbc, double sign, int ti,
+                                            int tj) {
   const int l = threadIdx.x & 63, r = l & 15, kk = l >> 4;
 #pragma unroll
   for (int k0 = 0; k0 < SB; k0 += 4) {
-    double av[2], bv[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      av[t] = sign * pa[(16 * t + r) * sar + (k0 + kk) * sat];
-      bv[t] = pb[(k0 + kk) * sbt + (16 * t + r) * sbc];
-    }
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-      for (int tj = 0; tj < 2; ++tj)
-        acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ti], bv[tj], acc[ti][tj], 0, 0, 0);
+    const double av = sign * pa[(16 * ti + r) * sar + (k0 + kk) * sat];
+    const double bv = pb[(k0 + kk) * sbt + (16 * tj + r) * sbc];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
   }
+  return acc;
 }
 
-__device__ __forceinline__ void bzero(f64x4_t (&acc)[2][2]) {
+__device__ __forceinline__ f64x4_t tile_load(const double* blk, int ti, int tj) {
+  const int l = threadIdx.x & 63;
+  f64x4_t t;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-    for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int v = 0; v < 4; ++v) t[v] = blk[(16 * ti + 4 * v + (l >> 4)) * LDB + 16 * tj + (l & 15)];
+  return t;
 }
 
-__device__ __forceinline__ void bload(f64x4_t (&acc)[2][2], const double* blk) {
+__device__ __forceinline__ void tile_store(const f64x4_t& t, double* blk, int ti, int tj) {
   const int l = threadIdx.x & 63;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-    for (int tj = 0; tj < 2; ++tj)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[ti][tj][v] = blk[(16 * ti + 4 * v + (l >> 4)) * LDB + 16 * tj + (l & 15)];
+  for (int v = 0; v < 4; ++v) blk[(16 * ti + 4 * v + (l >> 4)) * LDB + 16 * tj + (l & 15)] = t[v];
 }
 
-__device__ __forceinline__ void bstore(const f64x4_t (&acc)[2][2], double* blk) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-    for (int tj = 0; tj < 2; ++tj)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) blk[(16 * ti + 4 * v + (l >> 4)) * LDB + 16 * tj + (l & 15)] = acc[ti][tj][v];
+// 1 / sqrt(x): hardware estimate refined by two Newton-Raphson steps
+// y <- y (3 - x y^2) / 2 (each step doubles the correct bits)
+__device__ __forceinline__ double rsqrt_nr(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  return y;
 }
 
-// B1 on one wave: factor the stored block Sk (lower triangle read) and write
-// M = L^-1 (lower triangular) to Mk.  Returns the first column whose pivot is
-// not positive (or NaN), else -1; past a failed pivot the sweep continues with
-// d = 1 and its results are discarded.
-__device__ __noinline__ int diag_factor32(const double* Sk, double* Mk, double* col) {
-  const int l = threadIdx.x & 63, r = l & 31;
-  const bool isS = l < 32;
-  double v[SB], c[SB];
-#pragma unroll
-  for (int k = 0; k < SB; ++k) v[k] = isS ? Sk[max(r, k) * LDB + min(r, k)] : (k == r ? 1.0 : 0.0);
-  if (isS) col[r] = v[0];
+__device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// B1 on one wave: factor the stored block Sk (lower triangle read) and
+// overwrite it with M = L^-1 (lower triangular, zeros above).  Columns j and
+// j + 1 are eliminated together: with d0 = S_jj, a = S_j+1,j, e = S_j+1,j+1 d0
+// - a^2 (= d0 times the second pivot), y0 = 1/sqrt(d0), y1 = d0 y0 / sqrt(e),
+// g = a / d0, every lane applies v[k] -= alpha c0[k] + beta c1[k] (k > j + 1)
+// with beta = (v[j+1] - g v[j]) y1^2 and alpha = v[j] y0^2 - g beta, which is
+// the rank-2 Cholesky update on the S rows and the forward substitution on the
+// M columns; the M half then sets v[j] = v[j] y0, v[j+1] = (v[j+1] - g v[j]) y1.
+// Lane r of the S half loads all of row r; its entries right of the diagonal
+// (finite values of the stored block) only ever update other such entries of
+// the same lane, so they never reach the factor.  Returns the first column
+// whose pivot is not positive (or NaN), else -1; past a failed pivot the
+// sweep continues with harmless values and its results are discarded.  (Kept
+// out of line: inlined into the kernel it spills heavily.)
+__device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
+  const int l = threadIdx.x & 63, r = l & 31;
+  const bool isS = l < 32;
+  double v[SB], c0[SB], c1[SB];
 #pragma unroll
-  for (int k = 0; k < SB; ++k) c[k] = col[k];
+  for (int k = 0; k < SB; ++k) v[k] = isS ? Sk[r * LDB + k] : (k == r ? 1.0 : 0.0);
+  if (isS) *reinterpret_cast<f64x2_t*>(col2 + 2 * r) = f64x2_t{v[0], v[1]};
+  wave_sync_lds();
+#pragma unroll
+  for (int k = 0; k < SB; ++k) {
+    const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
+    c0[k] = t[0];
+    c1[k] = t[1];
+  }
   int bad = -1;
 #pragma unroll
-  for (int j = 0; j < SB; ++j) {
-    double d = c[j];
-    if (!(d > 0.0)) {
+  for (int j = 0; j < SB; j += 2) {
+    double d0 = c0[j];
+    const double a = c0[j + 1];
+    if (!(d0 > 0.0)) {
       if (bad < 0) bad = j;
-      d = 1.0;
+      d0 = 1.0;
     }
-    // y = 1 / sqrt(d): hardware estimate refined by two Newton-Raphson steps
-    // y <- y (3 - d y^2) / 2
-    double y = __builtin_amdgcn_rsq(d);
-    y = y * fma(-0.5 * d, y * y, 1.5);
-    y = y * fma(-0.5 * d, y * y, 1.5);
-    const double coef = v[j] * (y * y);
-    double cn[SB];
-    if (j + 1 < SB) {
-      // next column first, so that its broadcast overlaps the rest of the update
-      v[j + 1] = fma(-coef, c[j + 1], v[j + 1]);
-      if (isS) col[r] = v[j + 1];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int k = 0; k < SB; ++k) cn[k] = col[k];
+    double e = fma(c1[j + 1], d0, -a * a);
+    if (!(e > 0.0)) {
+      if (bad < 0) bad = j + 1;
+      e = d0;
+    }
+    const double y0 = rsqrt_nr(d0), ye = rsqrt_nr(e);
+    const double y0s = y0 * y0;
+    const double g = a * y0s;
+    const double y1 = ye * (d0 * y0);
+    const double beta = fma(-g, v[j], v[j + 1]) * (y1 * y1);
+    const double alpha = fma(v[j], y0s, -g * beta);
+    if (j + 2 < SB) {
+      // the next two columns first, so that their store overlaps the rest of
+      // the update (their read-back comes after it: holding both column pairs
+      // at once would not fit in registers)
+      v[j + 2] = fma(-alpha, c0[j + 2], fma(-beta, c1[j + 2], v[j + 2]));
+      v[j + 3] = fma(-alpha, c0[j + 3], fma(-beta, c1[j + 3], v[j + 3]));
+      if (isS) *reinterpret_cast<f64x2_t*>(col2 + 2 * r) = f64x2_t{v[j + 2], v[j + 3]};
     }
 #pragma unroll
-    for (int k = j + 2; k < SB; ++k) v[k] = fma(-coef, c[k], v[k]);
-    if (!isS) v[j] *= y;
-    if (j + 1 < SB) {
+    for (int k = j + 4; k < SB; ++k) v[k] = fma(-alpha, c0[k], fma(-beta, c1[k], v[k]));
+    if (!isS) {
+      const double xj = v[j] * y0;
+      v[j + 1] = fma(-g, v[j], v[j + 1]) * y1;
+      v[j] = xj;
+    }
+    if (j + 2 < SB) {
+      wave_sync_lds();
 #pragma unroll
-      for (int k = 0; k < SB; ++k) c[k] = cn[k];
+      for (int k = j + 2; k < SB; ++k) {
+        const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
+        c0[k] = t[0];
+        c1[k] = t[1];
+      }
     }
   }
   if (!isS) {
 #pragma unroll
-    for (int i = 0; i < SB; ++i) Mk[i * LDB + r] = v[i];
+    for (int i = 0; i < SB; ++i) Sk[i * LDB + r] = v[i];
   }
   return bad;
 }
 
 __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p, CholWs w) {
   if (*w.flag) return;
-  __shared__ double Ls[NSB * (NSB + 1) / 2 * BLKD];  // lower sub-blocks of S, then L, then X
-  __shared__ double Ms[NSB * BLKD];                  // M_kk = L_kk^-1
-  __shared__ double Ts[(NSB - 1) * BLKD];            // per-wave scratch of the inverse
-  __shared__ __align__(16) double col[SB];
+  __shared__ double Ls[NSB * (NSB + 1) / 2 * BLKD];  // S, then L (below) / M (diagonal) / X
+  __shared__ double Bs[NSB * (NSB - 1) / 2 * BLKD];  // Bacc_ic, i > c
+  __shared__ __align__(16) double col2[2 * SB];
   __shared__ int s_bad;
   const int tid = threadIdx.x, wave = tid >> 6;
 
-  // ---- A: load the lower sub-blocks of A_pp (fp32 -> fp64)
+  // ---- load the lower sub-blocks of A_pp (fp32 -> fp64)
   {
     const float* Ap = w.A + (int64_t)p * NB * npad + (int64_t)p * NB;
-    constexpr int NQ = NSB * (NSB + 1) / 2 * SB * (SB / 4);  // float4 count
-    for (int e = tid; e < NQ; e += 256) {
-      const int blk = e / (SB * SB / 4), rem = e % (SB * SB / 4);
+    constexpr int PER = SB * SB / 4;                         // float4 per sub-block
+    for (int e = tid; e < NSB * (NSB + 1) / 2 * PER; e += 256) {
+      const int blk = e / PER, rem = e % PER;
       const int r = rem / (SB / 4), c4 = (rem % (SB / 4)) * 4;
-      int bi = 0;
-      while (lslot(bi + 1, 0) <= blk) ++bi;
+      const int bi = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
       const int bj = blk - lslot(bi, 0);
       const float4 v = *reinterpret_cast<const float4*>(Ap + (int64_t)(SB * bi + r) * npad + SB * bj + c4);
       double* dst = Ls + blk * BLKD + r * LDB + c4;
@@ -306,38 +344,66 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
   if (tid == 0) s_bad = -1;
   __syncthreads();
 
-  // ---- B: blocked factorization
   for (int kb = 0; kb < NSB; ++kb) {
+    // ---- B1
     if (wave == 0) {
-      const int bad = diag_factor32(Ls + lslot(kb, kb) * BLKD, Ms + kb * BLKD, col);
+      const int bad = diag_factor32(Ls + lslot(kb, kb) * BLKD, col2);
       if (tid == 0 && bad >= 0) s_bad = SB * kb + bad;
     }
     __syncthreads();
     if (s_bad >= 0) break;
-    // B2: L_ik = S_ik M_kk^T
+    const double* Mk = Ls + lslot(kb, kb) * BLKD;
+    // ---- P1: 3 products x 4 tiles; results held until every wave has read
+    // the blocks they overwrite
     {
-      const int i = kb + 1 + wave;
-      if (i < NSB) {
-        f64x4_t acc[2][2];
-        bzero(acc);
-        double* Sik = Ls + lslot(i, kb) * BLKD;
-        bmma(acc, Sik, LDB, 1, Ms + kb * BLKD, 1, LDB, 1.0);
-        bstore(acc, Sik);
+      f64x4_t res[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int job = wave + 4 * u, prod = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+        f64x4_t acc = f64x4_t{0.0, 0.0, 0.0, 0.0};
+        if (prod < NSB - 1 - kb) {
+          const int i = kb + 1 + prod;   // L_ik = S_ik M_kk^T
+          acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Mk, 1, LDB, 1.0, ti, tj);
+        } else {
+          const int c = prod - (NSB - 1 - kb);   // X_kb,c = M_kk Bacc_kb,c
+          acc = tile_mma(acc, Mk, LDB, 1, Bs + bslot(kb, c) * BLKD, LDB, 1, 1.0, ti, tj);
+        }
+        res[u] = acc;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int job = wave + 4 * u, prod = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+        double* out = (prod < NSB - 1 - kb) ? Ls + lslot(kb + 1 + prod, kb) * BLKD
+                                            : Ls + lslot(kb, prod - (NSB - 1 - kb)) * BLKD;
+        tile_store(res[u], out, ti, tj);
       }
     }
     __syncthreads();
-    // B3: S_ij -= L_ik L_jk^T for kb < j <= i
+    // ---- P2: trailing update of S and of the accumulators, in place
     {
-      const int q = NSB - 1 - kb;  // trailing sub-blocks per side
-      for (int t = wave; t < q * (q + 1) / 2; t += 4) {
-        int a = 0, u = t;
-        while (u > a) { u -= a + 1; ++a; }
-        const int i = kb + 1 + a, j = kb + 1 + u;
-        f64x4_t acc[2][2];
-        double* Sij = Ls + lslot(i, j) * BLKD;
-        bload(acc, Sij);
-        bmma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Ls + lslot(j, kb) * BLKD, 1, LDB, -1.0);
-        bstore(acc, Sij);
+      const int q = NSB - 1 - kb;
+      const int nS = q * (q + 1) / 2, nB = q * (kb + 1);
+      for (int job = wave; job < 4 * (nS + nB); job += 4) {
+        const int prod = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+        if (prod < nS) {
+          int a = 0, u = prod;
+          while (u > a) { u -= a + 1; ++a; }
+          const int i = kb + 1 + a, j = kb + 1 + u;   // S_ij -= L_ik L_jk^T
+          double* Sij = Ls + lslot(i, j) * BLKD;
+          f64x4_t acc = tile_load(Sij, ti, tj);
+          acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Ls + lslot(j, kb) * BLKD, 1, LDB, -1.0,
+                         ti, tj);
+          tile_store(acc, Sij, ti, tj);
+        } else {
+          const int pb = prod - nS;
+          const int i = kb + 1 + pb / (kb + 1), c = pb % (kb + 1);   // Bacc_ic -= L_ik X_kb,c
+          double* Bic = Bs + bslot(i, c) * BLKD;
+          f64x4_t acc = (c == kb) ? f64x4_t{0.0, 0.0, 0.0, 0.0} : tile_load(Bic, ti, tj);
+          const double* X = (c == kb) ? Mk : Ls + lslot(kb, c) * BLKD;
+          acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, X, LDB, 1, -1.0, ti, tj);
+          tile_store(acc, Bic, ti, tj);
+        }
       }
     }
     __syncthreads();
@@ -352,37 +418,16 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
     return;
   }
 
-  // ---- C: X = L^-1, row block by row block (X_ij overwrites L_ij)
-  for (int i = 1; i < NSB; ++i) {
-    f64x4_t x[2][2];
-    if (wave < i) {
-      const int j = wave;
-      f64x4_t acc[2][2];
-      bzero(acc);
-      for (int k = j; k < i; ++k) {
-        const double* Xkj = (k == j) ? Ms + j * BLKD : Ls + lslot(k, j) * BLKD;
-        bmma(acc, Ls + lslot(i, k) * BLKD, LDB, 1, Xkj, LDB, 1, 1.0);
-      }
-      bstore(acc, Ts + j * BLKD);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      bzero(x);
-      bmma(x, Ms + i * BLKD, LDB, 1, Ts + j * BLKD, LDB, 1, -1.0);
-    }
-    __syncthreads();
-    if (wave < i) bstore(x, Ls + lslot(i, wave) * BLKD);
-    __syncthreads();
-  }
-
-  // ---- D: Linv (fp32, NB x NB, zeros above the diagonal)
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
+  // ---- Linv (fp32, NB x NB, zeros above the diagonal), 4 columns per store
+  for (int e = tid; e < NB * NB / 4; e += 256) {
+    const int r = e / (NB / 4), c = (e % (NB / 4)) * 4;
     const int bi = r / SB, bj = c / SB, rr = r % SB, cc = c % SB;
-    float v = 0.f;
-    if (bi > bj) v = (float)Ls[lslot(bi, bj) * BLKD + rr * LDB + cc];
-    else if (bi == bj) v = (float)Ms[bi * BLKD + rr * LDB + cc];
-    w.Linv[e] = v;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (bi >= bj) {
+      const double* src = Ls + lslot(bi, bj) * BLKD + rr * LDB + cc;
+      v = make_float4((float)src[0], (float)src[1], (float)src[2], (float)src[3]);
+    }
+    *reinterpret_cast<float4*>(linv_buf(w, p & 1) + (int64_t)r * NB + c) = v;
   }
 }
 
@@ -488,61 +533,79 @@ struct TileMma {
   }
 };
 
-// Quarter tiles (128 x 32) of Lp_i = A_ip Linv^T (i > p) and
-// Yp_c = Linv B_pc (c <= p).
-__global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, CholWs w) {
+// Quarter tiles (128 x 32): PL (mode 0) Lp_i = A_ip Linv^T for i > p; PY
+// (mode 1) Yp_c = Linv B_pc for c <= p.  Buffers of parity p % 2.
+__global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, int mode, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
   float* sA = sm;
   float* sB = sm + KS * LDT;
-  const int q = P - p - 1;
   const int t = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const float* Linv = linv_buf(w, p & 1);
   TileMma<4, 1, 1, 1> mm;
   mm.zero();
-  if (t < q) {
+  if (mode == 0) {
     const int i = p + 1 + t;
     const float* Aip = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
     // B(j, k) = Linv[32 quarter + j][k]
-    mm.run<XK, XK>(Aip, npad, w.Linv + (int64_t)32 * quarter * NB, NB, sA, sB);
-    mm.store<0>(w.Lp + (int64_t)i * NB * NB + 32 * quarter, NB);
+    mm.run<XK, XK>(Aip, npad, Linv + (int64_t)32 * quarter * NB, NB, sA, sB);
+    mm.store<0>(lp_buf(w, p & 1) + (int64_t)i * NB * NB + 32 * quarter, NB);
   } else {
-    const int c = t - q;
+    const int c = t;
     // A(i, k) = Linv[i][k]; B(j, k) = B[p NB + k][c NB + 32 quarter + j]
     const float* Bpc = w.B + (int64_t)p * NB * npad + (int64_t)c * NB + 32 * quarter;
-    mm.run<XK, KX>(w.Linv, NB, Bpc, npad, sA, sB);
-    mm.store<0>(w.Yp + (int64_t)c * NB + 32 * quarter, npad);
+    mm.run<XK, KX>(Linv, NB, Bpc, npad, sA, sB);
+    mm.store<0>(yp_buf(w, p & 1) + (int64_t)c * NB + 32 * quarter, npad);
   }
 }
 
-// SYRK tiles (i >= j > p), then forward-substitution tiles (i > p, c <= p),
-// then the copy of Y_p into row block p of B.
-__global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, CholWs w) {
+// U1 (mode 0): the SYRK tiles of column p + 1, A_i,p+1 for i > p, as quarter
+// tiles.
+// U2 (mode 1): the other SYRK tiles (i >= j > p + 1), then the forward-
+// substitution tiles (i > p, c <= p), then the copy of Y_p into row block p
+// of B.
+__global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, int mode, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
   float* sA = sm;
   float* sB = sm + KS * LDT;
+  const float* Lp = lp_buf(w, p & 1);
+  const float* Yp = yp_buf(w, p & 1);
   const int q = P - p - 1;
-  const int nsyrk = q * (q + 1) / 2;
-  const int nfwd = q * (p + 1);
   int t = blockIdx.x;
+  if (mode == 0) {
+    // quarter tiles (128 x 32): four times the workgroups, a quarter of the
+    // latency, for the kernel on the critical path
+    TileMma<4, 1, 1, 1> mm;
+    mm.zero();
+    const int quarter = t & 3;
+    const int i = p + 1 + (t >> 2), j = p + 1;
+    mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB + 32 * quarter * NB, NB,
+                   sA, sB);
+    mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB + 32 * quarter, npad);
+    return;
+  }
+  const int q2 = q - 1;   // trailing columns after p + 1
+  const int nsyrk = q2 > 0 ? q2 * (q2 + 1) / 2 : 0;
+  const int nfwd = q * (p + 1);
   if (t < nsyrk + nfwd) {
     TileMma<2, 2, 2, 2> mm;
     mm.zero();
     if (t < nsyrk) {
       int a = 0;
       while (t >= a + 1) { t -= a + 1; ++a; }
-      const int i = p + 1 + a, j = p + 1 + t;   // j <= i
-      mm.run<XK, XK>(w.Lp + (int64_t)i * NB * NB, NB, w.Lp + (int64_t)j * NB * NB, NB, sA, sB);
+      const int i = p + 2 + a, j = p + 2 + t;   // j <= i
+      mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB, NB, sA, sB);
       mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB, npad);
     } else {
       t -= nsyrk;
       const int i = p + 1 + t / (p + 1), c = t % (p + 1);
-      mm.run<XK, KX>(w.Lp + (int64_t)i * NB * NB, NB, w.Yp + (int64_t)c * NB, npad, sA, sB);
+      mm.run<XK, KX>(Lp + (int64_t)i * NB * NB, NB, Yp + (int64_t)c * NB, npad, sA, sB);
       mm.store<1>(w.B + (int64_t)i * NB * npad + (int64_t)c * NB, npad);
     }
   } else {
     const int c = t - nsyrk - nfwd;   // copy tile c of Y_p
-    const float* src = w.Yp + (int64_t)c * NB;
+    const float* src = Yp + (int64_t)c * NB;
     float* dst = w.B + (int64_t)p * NB * npad + (int64_t)c * NB;
     for (int e = threadIdx.x; e < NB * NB / 4; e += 256) {
       const int r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
@@ -564,6 +627,48 @@ __global__ void __launch_bounds__(256) chol_flip(int64_t n, int64_t npad, float*
 }  // namespace
 
 size_t chol_ws_bytes(int64_t n) { return ws_layout(n, nullptr, nullptr); }
+
+namespace {
+
+// Second stream of the look-ahead and its events, one set per device, created
+// on first use and kept until the process ends.  The mutex serializes the
+// enqueueing of concurrent calls on one device (the work itself still runs
+// asynchronously on the caller's stream and this one).
+struct SideStream {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, diag_done = nullptr, u1_done = nullptr, u2_done[2] = {nullptr, nullptr};
+};
+
+#define KQ_CHECKED(call)                   \
+  do {                                     \
+    kronq_status _s = (call);              \
+    if (_s != KRONQ_OK) return _s;         \
+  } while (0)
+
+kronq_status side_stream(SideStream** out) {
+  constexpr int kMaxDev = 64;
+  static SideStream sets[kMaxDev];
+  static std::mutex init_mu;
+  int dev = 0;
+  KQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDev) return fail(KRONQ_EHIP, "kronq_chol_inv: device %d out of range", dev);
+  SideStream& ss = sets[dev];
+  std::lock_guard<std::mutex> g(init_mu);
+  if (!ss.stream) {
+    const unsigned ef = hipEventDisableTiming;
+    KQ_HIP(hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking));
+    KQ_HIP(hipEventCreateWithFlags(&ss.fork, ef));
+    KQ_HIP(hipEventCreateWithFlags(&ss.diag_done, ef));
+    KQ_HIP(hipEventCreateWithFlags(&ss.u1_done, ef));
+    KQ_HIP(hipEventCreateWithFlags(&ss.u2_done[0], ef));
+    KQ_HIP(hipEventCreateWithFlags(&ss.u2_done[1], ef));
+  }
+  *out = &ss;
+  return KRONQ_OK;
+}
+
+}  // namespace
 
 kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, int act_order,
                          int32_t* perm, float* R, int64_t ldr, int64_t* info, void* ws,
@@ -589,15 +694,42 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
     KQ_LAUNCHED("chol_gather");
   }
   const size_t lds_tile = 2 * (size_t)KS * LDT * sizeof(float);
-  for (int p = 0; p < P; ++p) {
-    hipLaunchKernelGGL(chol_diag, dim3(1), dim3(256), 0, s, npad, n, p, w);
-    KQ_LAUNCHED("chol_diag");
-    const int q = P - p - 1;
-    hipLaunchKernelGGL(chol_panel, dim3(4 * (q + p + 1)), dim3(256), lds_tile, s, npad, P, p, w);
-    KQ_LAUNCHED("chol_panel");
-    const int tiles = q * (q + 1) / 2 + q * (p + 1) + (p + 1);
-    hipLaunchKernelGGL(chol_update, dim3(tiles), dim3(256), lds_tile, s, npad, P, p, w);
-    KQ_LAUNCHED("chol_update");
+  SideStream* ss = nullptr;
+  KQ_CHECKED(side_stream(&ss));
+  {
+    std::lock_guard<std::mutex> guard(ss->mu);
+    hipStream_t s2 = ss->stream;
+    // the second stream starts after the gather
+    KQ_HIP(hipEventRecord(ss->fork, s));
+    KQ_HIP(hipStreamWaitEvent(s2, ss->fork, 0));
+    for (int p = 0; p < P; ++p) {
+      const int q = P - p - 1;
+      hipLaunchKernelGGL(chol_diag, dim3(1), dim3(256), 0, s, npad, n, p, w);
+      KQ_LAUNCHED("chol_diag");
+      KQ_HIP(hipEventRecord(ss->diag_done, s));
+      if (q > 0) {
+        hipLaunchKernelGGL(chol_panel, dim3(4 * q), dim3(256), lds_tile, s, npad, P, p, 0, w);
+        KQ_LAUNCHED("chol_panel");
+        // critical path: U1(p) after U2(p - 1) (both write column p + 1)
+        if (p > 0) KQ_HIP(hipStreamWaitEvent(s, ss->u2_done[(p - 1) & 1], 0));
+        hipLaunchKernelGGL(chol_update, dim3(4 * q), dim3(256), lds_tile, s, npad, P, p, 0, w);
+        KQ_LAUNCHED("chol_update");
+      }
+      KQ_HIP(hipEventRecord(ss->u1_done, s));
+      // second stream: PY(p), then U2(p) once U1(p) is done, so that the
+      // small critical-path update does not queue behind the large one
+      KQ_HIP(hipStreamWaitEvent(s2, ss->diag_done, 0));
+      hipLaunchKernelGGL(chol_panel, dim3(4 * (p + 1)), dim3(256), lds_tile, s2, npad, P, p, 1, w);
+      KQ_LAUNCHED("chol_panel");
+      KQ_HIP(hipStreamWaitEvent(s2, ss->u1_done, 0));
+      const int q2 = q - 1;
+      const int u2 = (q2 > 0 ? q2 * (q2 + 1) / 2 : 0) + q * (p + 1) + (p + 1);
+      hipLaunchKernelGGL(chol_update, dim3(u2), dim3(256), lds_tile, s2, npad, P, p, 1, w);
+      KQ_LAUNCHED("chol_update");
+      KQ_HIP(hipEventRecord(ss->u2_done[p & 1], s2));
+    }
+    // join: the flip reads all of B
+    KQ_HIP(hipStreamWaitEvent(s, ss->u2_done[(P - 1) & 1], 0));
   }
   {
     const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 64);

@@ -407,13 +407,16 @@ __device__ __forceinline__ void v2_mma(const V2Half& f, f32x16_t (&acc)[4][4]) {
       acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[a], f.b[b], acc[a][b], 0, 0, 0);
 }
 
-// interleave 16 MFMAs with the 16 operand reads issued just before them
+// interleave the 16 MFMAs of a half-stage with the 16 operand reads of the
+// next half: two reads after each of the first eight MFMAs, so that the last
+// read has landed well before the next half's first MFMA waits for it
 __device__ __forceinline__ void v2_interleave() {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // eight MFMAs
 }
 
 // s_waitcnt immediate: at most `vm` loads in flight (vmcnt, 6 bits split over
