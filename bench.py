@@ -49,7 +49,81 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gram_bf16_llama2_7b_q_proj_traffic.json"))
+    ap.add_argument("--copy-probe", type=int, metavar="BYTES", default=0,
+                    help="only run a plain device copy of BYTES five times (calibrates the HBM byte "
+                         "counters) and exit")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                             "COPY_WRITE_CSV"),
+                    help="only turn four rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and "
+                         "WRITE_SIZE of this benchmark, then of --copy-probe) into the traffic file "
+                         "(--traffic-json) and exit")
+    ap.add_argument("--copy-bytes", type=int, default=256 * 1024 * 1024,
+                    help="BYTES the copy-probe runs used (for --summarize-traffic)")
     return ap.parse_args()
+
+
+GRAM_SRC = os.path.join(ROOT, "post_quantization_02_amd", "csrc", "gram.hip")
+GRAM_KERNELS = ("gram_bf16_lds_kernel", "gram_finalize_kernel", "gram_bf16_kernel")
+
+
+def gram_source_hash():
+    import hashlib
+    with open(GRAM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def copy_probe(nbytes):
+    """Plain device-to-device copy of a known size, five times."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "copies": 5}), flush=True)
+
+
+def _pmc_mean(path, kernel_pred, counter):
+    import csv
+    per_dispatch = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and kernel_pred(r["Kernel_Name"]):
+                key = r["Dispatch_Id"]
+                per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    vals = list(per_dispatch.values())
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_traffic(args):
+    """HBM bytes per kronq_gram call (the Gram kernel and its split-K finalize)
+    from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled so that the
+    same counter over a plain copy of known size reads that size."""
+    f_csv, w_csv, cf_csv, cw_csv = args.summarize_traffic
+    copy = lambda k: "copyBuffer" in k
+    cf, _ = _pmc_mean(cf_csv, copy, "FETCH_SIZE")
+    cw, _ = _pmc_mean(cw_csv, copy, "WRITE_SIZE")
+    kib = args.copy_bytes / 1024.0
+    f_scale, w_scale = kib / cf, kib / cw
+    out = {"counters": {}, "copy_probe": {"bytes": args.copy_bytes, "fetch_kib": cf, "write_kib": cw,
+                                          "fetch_scale": f_scale, "write_scale": w_scale}}
+    total = 0.0
+    for k in GRAM_KERNELS:
+        pred = lambda name, k=k: k in name
+        fk, nf = _pmc_mean(f_csv, pred, "FETCH_SIZE")
+        wk, nw = _pmc_mean(w_csv, pred, "WRITE_SIZE")
+        if fk is None or wk is None:
+            continue
+        b = (fk * f_scale + wk * w_scale) * 1024.0
+        out["counters"][k] = {"fetch_kib": fk, "write_kib": wk, "dispatches": nf,
+                              "hbm_bytes_per_dispatch": b}
+        total += b
+    out["bytes_per_launch"] = total
+    out["unit"] = "bytes per kronq_gram call (sum over its kernels, scaled counters)"
+    out["gram_source_sha256"] = gram_source_hash()
+    with open(args.traffic_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, X, G, W, budget_s):
@@ -107,6 +181,12 @@ def cpu_baseline(w, X, G, W, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -211,12 +291,15 @@ def main():
     gptq_flops = float(m) * n * n
     gptq_bytes = 9.0 * m * n + 2.0 * n * n
 
+    # HBM traffic per Gram call from the committed counter summary, null when the
+    # Gram source has changed since the counters were taken
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f)
-            traffic = tj.get("bytes_per_launch")
+            if tj.get("gram_source_sha256") == gram_source_hash():
+                traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
 
