@@ -148,11 +148,14 @@ def kronq_gram(A: torch.Tensor, H: torch.Tensor | None = None, scale: float | No
 def kronq_biip_rotate(W: torch.Tensor, HX: torch.Tensor | None, HG: torch.Tensor | None,
                       in_signs: torch.Tensor, in_block: int, out_signs: torch.Tensor,
                       out_block: int, alpha: float, sg: torch.Tensor | None = None,
-                      stream=None, ws: torch.Tensor | None = None) -> torch.Tensor | None:
-    """In place: W <- U S_G W V^T, HX <- V HX V^T, HG <- U S_G^-1 HG S_G^-1 U^T."""
+                      stream=None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """In place: W <- U S_G W V^T, HX <- V HX V^T, HG <- U S_G^-1 HG S_G^-1 U^T.
+    Returns s_g = diag(H_G)^alpha (allocated when `sg` is None)."""
     lib = load()
     _dev(W, "W", torch.float32)
     m, n = W.shape
+    if sg is None:
+        sg = torch.empty(m, dtype=torch.float32, device=W.device)
     for t, nm in ((HX, "HX"), (HG, "HG"), (sg, "sg"), (in_signs, "in_signs"), (out_signs, "out_signs")):
         if t is not None:
             _dev(t, nm, torch.float32)

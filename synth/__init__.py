@@ -15,6 +15,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libsynth.so")
 _SRC = os.path.join(_HERE, "synth.c")
+_SO_DEV = os.path.join(_HERE, "libsynth_gpu.so")
+_SRC_DEV = os.path.join(_HERE, "synth_gpu.hip")
 
 NORMAL, ACT_NORMAL, ACT_T4, GRAD_LOGNORMAL, INT = 0, 1, 2, 3, 4
 _DT = {"f64": (0, np.float64), "f32": (1, np.float32), "bf16": (2, np.uint16)}
@@ -22,12 +24,23 @@ _DT = {"f64": (0, np.float64), "f32": (1, np.float32), "bf16": (2, np.uint16)}
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile libsynth.so with gcc (OpenMP); returns its path."""
+def build(force: bool = False, device: bool = True) -> str:
+    """Compile libsynth.so with gcc (OpenMP) and, with `device`, its device
+    copy libsynth_gpu.so with hipcc for gfx950; returns the host library path."""
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _SO)
+    if device and (force or not os.path.exists(_SO_DEV)
+                   or os.path.getmtime(_SO_DEV) < os.path.getmtime(_SRC_DEV)):
+        tmp = _SO_DEV + ".tmp%d" % os.getpid()
+        hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+        r = subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-ffp-contract=off",
+                            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", _SRC_DEV, "-o", tmp],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("building %s failed:\n%s" % (_SRC_DEV, r.stderr))
+        os.replace(tmp, _SO_DEV)
     return _SO
 
 
@@ -47,8 +60,26 @@ def _load():
         lib.synth_signs.restype = ctypes.c_int
         lib.synth_mix64.argtypes = [u64]
         lib.synth_mix64.restype = u64
+        lib.synth_col_factors.argtypes = [ctypes.c_int, u64, i64, i64, dbl, vp, i64, dbl, vp]
+        lib.synth_col_factors.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+_lib_dev = None
+
+
+def _load_dev():
+    global _lib_dev
+    if _lib_dev is None:
+        if not os.path.exists(_SO_DEV):
+            raise OSError("libsynth_gpu.so not built: run synth.build()")
+        lib = ctypes.CDLL(_SO_DEV)
+        i64, u64, vp, dbl = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_double
+        lib.synth_matrix_dev.argtypes = [ctypes.c_int, u64, i64, i64, dbl, vp, ctypes.c_int, vp, i64, vp]
+        lib.synth_matrix_dev.restype = ctypes.c_int
+        _lib_dev = lib
+    return _lib_dev
 
 
 def mix64(z: int) -> int:
@@ -95,6 +126,40 @@ def matrix(kind: int, seed: int, rows: int, cols: int, *, r0: int = 0, nr: int |
                               max(nc, 1))
     if rc:
         raise ValueError("synth_matrix failed (%d)" % rc)
+    return out
+
+
+def col_factors(kind: int, seed: int, cols: int, *, p1: float = 1.0, outliers=None,
+                out_factor: float = 1.0) -> np.ndarray:
+    """The per-column factors `matrix` applies (float64[cols])."""
+    colf = np.empty(max(cols, 1), dtype=np.float64)
+    if outliers is None or len(outliers) == 0:
+        optr, nout = None, 0
+    else:
+        outliers = np.ascontiguousarray(outliers, dtype=np.int64)
+        optr, nout = outliers.ctypes.data, len(outliers)
+    rc = _load().synth_col_factors(kind, seed, 0, cols, float(p1), optr, nout, float(out_factor),
+                                   colf.ctypes.data)
+    if rc:
+        raise ValueError("synth_col_factors failed (%d)" % rc)
+    return colf[:cols]
+
+
+def matrix_dev(kind: int, seed: int, rows: int, cols: int, *, p1: float = 1.0, outliers=None,
+               out_factor: float = 1.0, dtype: str = "bf16", device="cuda:0", stream=None):
+    """The whole rows x cols matrix of `kind` generated in device memory by the
+    device copy of the generator; returns a torch tensor (bf16 for "bf16")."""
+    import torch
+    colf = torch.from_numpy(col_factors(kind, seed, cols, p1=p1, outliers=outliers,
+                                        out_factor=out_factor)).to(device)
+    tdt = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    out = torch.empty((rows, cols), dtype=tdt, device=device)
+    st = torch.cuda.current_stream(device) if stream is None else stream
+    rc = _load_dev().synth_matrix_dev(kind, seed, rows, cols, float(p1), colf.data_ptr(), _DT[dtype][0],
+                                      out.data_ptr(), cols, st.cuda_stream)
+    if rc:
+        raise ValueError("synth_matrix_dev failed (%d)" % rc)
+    torch.cuda.current_stream(device).synchronize()
     return out
 
 

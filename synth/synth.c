@@ -90,6 +90,27 @@ int synth_signs(uint64_t seed, int64_t n, float* out) {
 }
 
 /*
+ * Column factors of columns [c0, c0+nc): out_factor on the listed outlier
+ * columns of the activation kinds, exp(p1 * normal(stream 4, column)) for the
+ * gradient kind, 1 otherwise.
+ */
+int synth_col_factors(int kind, uint64_t seed, int64_t c0, int64_t nc, double p1,
+                      const int64_t* outliers, int64_t n_out, double out_factor, double* colf) {
+  if (c0 < 0 || nc < 0 || (nc > 0 && !colf)) return 1;
+  for (int64_t c = 0; c < nc; ++c) colf[c] = 1.0;
+  if (kind == SYN_ACT_NORMAL || kind == SYN_ACT_T4) {
+    for (int64_t o = 0; o < n_out; ++o) {
+      int64_t ch = outliers[o];
+      if (ch >= c0 && ch < c0 + nc) colf[ch - c0] = out_factor;
+    }
+  } else if (kind == SYN_GRAD_LOGNORMAL) {
+    uint64_t k4 = stream_key(seed, 4);
+    for (int64_t c = 0; c < nc; ++c) colf[c] = exp(p1 * normal_at(k4, (uint64_t)(c0 + c)));
+  }
+  return 0;
+}
+
+/*
  * Fill block [r0, r0+nr) x [c0, c0+nc) of a logical rows x cols matrix.
  *   kind SYN_NORMAL         : p1 * normal(stream 0)
  *   kind SYN_ACT_NORMAL     : normal(stream 1) * channel factor
@@ -108,16 +129,7 @@ int synth_matrix(int kind, uint64_t seed, int64_t rows, int64_t cols, int64_t r0
   if (kind < SYN_NORMAL || kind > SYN_INT) return 1;
   double* colf = (double*)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
   if (!colf) return 2;
-  for (int64_t c = 0; c < nc; ++c) colf[c] = 1.0;
-  if (kind == SYN_ACT_NORMAL || kind == SYN_ACT_T4) {
-    for (int64_t o = 0; o < n_out; ++o) {
-      int64_t ch = outliers[o];
-      if (ch >= c0 && ch < c0 + nc) colf[ch - c0] = out_factor;
-    }
-  } else if (kind == SYN_GRAD_LOGNORMAL) {
-    uint64_t k4 = stream_key(seed, 4);
-    for (int64_t c = 0; c < nc; ++c) colf[c] = exp(p1 * normal_at(k4, (uint64_t)(c0 + c)));
-  }
+  synth_col_factors(kind, seed, c0, nc, p1, outliers, n_out, out_factor, colf);
   uint64_t k0 = stream_key(seed, 0), k1 = stream_key(seed, 1), k3 = stream_key(seed, 3),
            k6 = stream_key(seed, 6);
   int64_t ip1 = (int64_t)p1;

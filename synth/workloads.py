@@ -91,6 +91,18 @@ class Workload:
         return synth.matrix(synth.GRAD_LOGNORMAL, self.g_seed(sname), self.N, s.m, r0=r0, nr=nr,
                             c0=c0, nc=nc, p1=self.grad_sigma, dtype=dtype or self.dtype, out=out)
 
+    # ---- generation in device memory (large inputs; torch tensors) ----
+    def gen_x_dev(self, xname, device="cuda:0"):
+        spec = self.input(xname)
+        return synth.matrix_dev(spec.kind, self.x_seed(xname), self.N, spec.n,
+                                outliers=self.outliers(xname), out_factor=spec.factor,
+                                dtype=self.dtype, device=device)
+
+    def gen_g_dev(self, sname, device="cuda:0"):
+        s = self.sub(sname)
+        return synth.matrix_dev(synth.GRAD_LOGNORMAL, self.g_seed(sname), self.N, s.m,
+                                p1=self.grad_sigma, dtype=self.dtype, device=device)
+
     def gen_w(self, sname, dtype=None):
         s = self.sub(sname)
         return synth.matrix(synth.NORMAL, self.w_seed(sname), s.m, s.n, p1=self.w_std,
