@@ -17,6 +17,8 @@
 // float64 reference up to summation order.  Grid parameters: per-channel from
 // the whole initial row (a separate pass), or per group of g | 128 columns from
 // the current compensated values when the group's first column is reached.
+#include <utility>
+
 #include "kronq_internal.h"
 
 namespace kronq {
@@ -49,21 +51,15 @@ struct GptqParams {
   const double* pc;        // per-channel (scale, zero) pairs, m x 2
 };
 
-// value of `x` held by lane 16 * (lane / 16) + o, for every lane: four
-// uniform-index lane reads (no LDS round trip) and a select by row group
-__device__ __forceinline__ double bcast_row(double x, int o, int lane) {
+// value of `x` held by lane 16 * (lane / 16) + O, for every lane: DPP
+// row_newbcast (lane O of each 16-lane row to the whole row), a 64-bit value
+// moved as two halves
+template <int O>
+__device__ __forceinline__ double bcast_row(double x) {
   const long long b = __double_as_longlong(x);
-  const int lo = (int)(b & 0xffffffffLL), hi = (int)(b >> 32);
-  long long r[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const unsigned l = (unsigned)__builtin_amdgcn_readlane(lo, 16 * g + o);
-    const unsigned h = (unsigned)__builtin_amdgcn_readlane(hi, 16 * g + o);
-    r[g] = (long long)(((unsigned long long)h << 32) | l);
-  }
-  const int g = lane >> 4;
-  const long long y = g == 0 ? r[0] : g == 1 ? r[1] : g == 2 ? r[2] : r[3];
-  return __longlong_as_double(y);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, 0x150 + O, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), 0x150 + O, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
 __device__ __forceinline__ int64_t colmap(const GptqParams& p, int64_t j) {
@@ -152,6 +148,102 @@ __device__ __forceinline__ void gq_mma(const GqBatch& B, bool live, f64x4_t (&ac
     for (int t = 0; t < 8; ++t)
       acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t >> 2][t & 3], acc[t], 0, 0, 0);
   }
+}
+
+// An empty register-only asm hides the value from the optimizer, so that an
+// address built from it is recomputed at each use instead of being hoisted
+// out of the block loop (one live register per column otherwise).
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// State of one lane in the block's column loop: the lane's 8 columns of its
+// row (v), the outputs of the columns it owns, and the grid parameters.
+struct InBlock {
+  double (&v)[8], (&ev)[8], (&wq)[8], (&tv)[8];
+  int (&qv)[8];
+  double scale, zero, inv_scale;
+  f32x4_t r0, r1;   // staged R row of the next column (this lane's 8 entries)
+  double id;        // 1 / R_cc of the next column
+};
+
+// Columns 8 O .. 8 O + 7 of the block (owned by lane O of each 16-lane row).
+template <int O>
+__device__ __forceinline__ void in_block_octet(InBlock& st, const GptqParams& p, const float* Rb,
+                                               const double* invd, int part_id, bool row_ok,
+                                               int64_t grow, int64_t jb, int ncols, int maxq) {
+  if (p.group > 0 && ((8 * O) % p.group) == 0) {
+    // parameters of the group [8 O, 8 O + group) from the current values
+    const int c = 8 * O;
+    double lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int cc = 8 * part_id + q;
+      const bool in = cc >= c && cc < c + p.group && cc < ncols;
+      lo = in ? fmin(lo, st.v[q]) : lo;
+      hi = in ? fmax(hi, st.v[q]) : hi;
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      lo = fmin(lo, __shfl_xor(lo, off, 16));
+      hi = fmax(hi, __shfl_xor(hi, off, 16));
+    }
+    grid_params(lo, hi, p.bits, st.scale, st.zero);
+    st.inv_scale = 1.0 / st.scale;
+    if (part_id == O && row_ok && c < ncols) {
+      const int64_t g = (jb + c) / p.group;
+      p.scales[grow * p.ngroups + g] = (float)st.scale;
+      p.zeros[grow * p.ngroups + g] = (float)st.zero;
+    }
+  }
+  const bool own = part_id == O;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int c = 8 * O + s;
+    // this column's staged R row and 1 / R_cc were read one column ahead;
+    // read the next column's now
+    const f32x4_t r0v = st.r0, r1v = st.r1;
+    const double id = st.id;
+    if (c + 1 < BLK) {
+      const float* Rn = Rb + (c + 1) * RLD + opaque_int(8 * part_id);
+      st.r0 = *reinterpret_cast<const f32x4_t*>(Rn);
+      st.r1 = *reinterpret_cast<const f32x4_t*>(Rn + 4);
+      st.id = invd[opaque_int(c + 1)];
+    }
+    // owner lane: round column c
+    const double t = fma(st.v[s], st.inv_scale, st.zero);
+    const double q = fmin(fmax(rint(t), 0.0), (double)maxq);
+    const double w_q = st.scale * (q - st.zero);
+    const double e = (st.v[s] - w_q) * id;
+    // select now (an empty asm pins each result here): left to itself the
+    // compiler keeps every octet's candidates live and selects at the end
+    st.ev[s] = own ? e : st.ev[s];
+    st.wq[s] = own ? w_q : st.wq[s];
+    st.tv[s] = own ? t : st.tv[s];
+    st.qv[s] = own ? (int)q : st.qv[s];
+    asm volatile("" : "+v"(st.ev[s]), "+v"(st.wq[s]), "+v"(st.tv[s]), "+v"(st.qv[s]));
+    const double eb = bcast_row<O>(e);
+    // compensate the later columns of the block held by this lane (the
+    // staged row is zero at and before column c); the next column first
+    if (s + 1 < 8) st.v[s + 1] = fma(-eb, (double)(s + 1 < 4 ? r0v[(s + 1) & 3] : r1v[(s + 1) & 3]), st.v[s + 1]);
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2) {
+      if (q2 == s + 1) continue;
+      st.v[q2] = fma(-eb, (double)(q2 < 4 ? r0v[q2 & 3] : r1v[q2 & 3]), st.v[q2]);
+    }
+    // keep the scheduler from hoisting later columns' reads (one straight
+    // line of 128 columns would otherwise be scheduled as a whole)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int... O>
+__device__ __forceinline__ void in_block_octets(InBlock& st, const GptqParams& p, const float* Rb,
+                                                const double* invd, int part_id, bool row_ok,
+                                                int64_t grow, int64_t jb, int ncols, int maxq,
+                                                std::integer_sequence<int, O...>) {
+  (in_block_octet<O>(st, p, Rb, invd, part_id, row_ok, grow, jb, ncols, maxq), ...);
 }
 
 __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
@@ -273,60 +365,17 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
     }
     // Every column of the block is walked (past ncols the values, invd and
     // staged rows are zero and nothing is stored), so the loop has no exit
-    // inside and the reads of R and invd do not wait on the chain.
-    for (int o = 0; o < 16; ++o) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int c = 8 * o + s;
-        if (p.group > 0 && (c % p.group) == 0) {
-          // parameters of the group [c, c + group) from the current values
-          double lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int cc = 8 * part_id + q;
-            if (cc >= c && cc < c + p.group && cc < ncols) {
-              lo = fmin(lo, v[q]);
-              hi = fmax(hi, v[q]);
-            }
-          }
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) {
-            lo = fmin(lo, __shfl_xor(lo, off, 16));
-            hi = fmax(hi, __shfl_xor(hi, off, 16));
-          }
-          grid_params(lo, hi, p.bits, scale, zero);
-          inv_scale = 1.0 / scale;
-          if (part_id == o && row_ok && c < ncols) {
-            const int64_t g = (jb + c) / p.group;
-            p.scales[grow * p.ngroups + g] = (float)scale;
-            p.zeros[grow * p.ngroups + g] = (float)zero;
-          }
-        }
-        const float* Rrow = Rb + c * RLD + 8 * part_id;
-        const f32x4_t r0v = *reinterpret_cast<const f32x4_t*>(Rrow);
-        const f32x4_t r1v = *reinterpret_cast<const f32x4_t*>(Rrow + 4);
-        const double id = invd[c];
-        // owner lane: round column c
-        const double t = fma(v[s], inv_scale, zero);
-        const double q = fmin(fmax(rint(t), 0.0), (double)maxq);
-        const double w_q = scale * (q - zero);
-        const double e = (v[s] - w_q) * id;
-        if (part_id == o) {
-          ev[s] = e;
-          wq[s] = w_q;
-          tv[s] = t;
-          qv[s] = (int)q;
-        }
-        const double eb = bcast_row(e, o, lane);
-        // compensate the later columns of the block held by this lane (the
-        // staged row is zero at and before column c)
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          v[q2] = fma(-eb, (double)r0v[q2], v[q2]);
-          v[4 + q2] = fma(-eb, (double)r1v[q2], v[4 + q2]);
-        }
-      }
-    }
+    // inside and the reads of R and invd do not wait on the chain.  The 16
+    // octets of columns are a compile-time sequence, so the owner lane of a
+    // column (broadcast by DPP) and the register holding it are constants.
+    InBlock st{v, ev, wq, tv, qv, scale, zero, inv_scale,
+               *reinterpret_cast<const f32x4_t*>(Rb + 8 * part_id),
+               *reinterpret_cast<const f32x4_t*>(Rb + 8 * part_id + 4), invd[0]};
+    in_block_octets(st, p, Rb, invd, part_id, row_ok, grow, jb, ncols, maxq,
+                    std::make_integer_sequence<int, 16>{});
+    scale = st.scale;
+    zero = st.zero;
+    inv_scale = st.inv_scale;
     // ---- 3. write errors and outputs of this block ----
     if (row_ok) {
 #pragma unroll
