@@ -16,7 +16,9 @@
 //   pass 2: a tile of kr/R1 rows at stride R1 x a strip of CW columns; applies
 //           the remaining kr/R1 part of the row-side transform (skipped when
 //           R1 == kr).
-// Each pass stages its tile (up to 2^15 floats = 128 KiB) in LDS and runs the
+// Each pass stages its tile (up to 2^14 floats = 64 KiB, so that two
+// workgroups share a CU and overlap each other's HBM and LDS phases) in LDS
+// and runs the
 // butterflies radix-16: a thread gathers 16 elements differing in 4 index bits,
 // does 4 butterfly stages in registers and scatters them back.  HBM traffic is
 // float4 and coalesced (rows of a column block are contiguous; pass-2 strips
@@ -28,7 +30,7 @@
 namespace kronq {
 namespace {
 
-constexpr int LOG_TILE = 15;
+constexpr int LOG_TILE = 14;   // 64 KiB tiles: two workgroups per CU overlap HBM and LDS phases
 constexpr int TILE = 1 << LOG_TILE;
 constexpr int NT = 512;
 constexpr int kXcds = 8;
