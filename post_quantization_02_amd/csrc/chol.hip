@@ -284,13 +284,25 @@ __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
     const double y1 = ye * (d0 * y0);
     const double beta = fma(-g, v[j], v[j + 1]) * (y1 * y1);
     const double alpha = fma(v[j], y0s, -g * beta);
+    // The next two columns first, so that their broadcast overlaps the rest
+    // of the update.  From column 18 on both column pairs fit in registers
+    // and the read-back is issued before the remaining FMAs; earlier it
+    // follows them.
+    constexpr int kEarlyRead = 18;
+    double n0[SB], n1[SB];
     if (j + 2 < SB) {
-      // the next two columns first, so that their store overlaps the rest of
-      // the update (their read-back comes after it: holding both column pairs
-      // at once would not fit in registers)
       v[j + 2] = fma(-alpha, c0[j + 2], fma(-beta, c1[j + 2], v[j + 2]));
       v[j + 3] = fma(-alpha, c0[j + 3], fma(-beta, c1[j + 3], v[j + 3]));
       if (isS) *reinterpret_cast<f64x2_t*>(col2 + 2 * r) = f64x2_t{v[j + 2], v[j + 3]};
+      if (j >= kEarlyRead) {
+        wave_sync_lds();
+#pragma unroll
+        for (int k = j + 2; k < SB; ++k) {
+          const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
+          n0[k] = t[0];
+          n1[k] = t[1];
+        }
+      }
     }
 #pragma unroll
     for (int k = j + 4; k < SB; ++k) v[k] = fma(-alpha, c0[k], fma(-beta, c1[k], v[k]));
@@ -300,12 +312,19 @@ __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
       v[j] = xj;
     }
     if (j + 2 < SB) {
-      wave_sync_lds();
+      if (j < kEarlyRead) {
+        wave_sync_lds();
+#pragma unroll
+        for (int k = j + 2; k < SB; ++k) {
+          const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
+          n0[k] = t[0];
+          n1[k] = t[1];
+        }
+      }
 #pragma unroll
       for (int k = j + 2; k < SB; ++k) {
-        const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
-        c0[k] = t[0];
-        c1[k] = t[1];
+        c0[k] = n0[k];
+        c1[k] = n1[k];
       }
     }
   }
@@ -438,34 +457,52 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
 //   KX: stored row-major as [k][x]
 enum { XK = 0, KX = 1 };
 
-// Stage KS values of k for X consecutive x into LDS as sT[k][x] (stride LDT).
+// A stage is KS values of k for X consecutive x, held in LDS as sT[k][x]
+// (stride LDT).  gload fetches a thread's share of it (16-byte loads) into
+// registers; lstore writes those registers to LDS.
+template <int X>
+constexpr int stage_vecs() { return (X * KS / 4) / 256; }
+
 template <int LAY, int X>
-__device__ inline void stage_load(float* sT, const float* G, int64_t ld, int k0) {
+__device__ inline void gload(float4 (&r)[stage_vecs<X>()], const float* G, int64_t ld, int k0) {
   const int tid = threadIdx.x;
-  if (LAY == XK) {
 #pragma unroll
-    for (int q = 0; q < (X * KS / 4) / 256; ++q) {
-      const int idx = tid + 256 * q;
+  for (int q = 0; q < stage_vecs<X>(); ++q) {
+    const int idx = tid + 256 * q;
+    if (LAY == XK) {
       const int x = idx >> 3, k4 = (idx & 7) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(G + (int64_t)x * ld + k0 + k4);
-      sT[(k4 + 0) * LDT + x] = v.x;
-      sT[(k4 + 1) * LDT + x] = v.y;
-      sT[(k4 + 2) * LDT + x] = v.z;
-      sT[(k4 + 3) * LDT + x] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < (X * KS / 4) / 256; ++q) {
-      const int idx = tid + 256 * q;
+      r[q] = *reinterpret_cast<const float4*>(G + (int64_t)x * ld + k0 + k4);
+    } else {
       const int k = idx / (X / 4), x4 = (idx % (X / 4)) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(G + (int64_t)(k0 + k) * ld + x4);
-      sT[k * LDT + x4 + 0] = v.x;
-      sT[k * LDT + x4 + 1] = v.y;
-      sT[k * LDT + x4 + 2] = v.z;
-      sT[k * LDT + x4 + 3] = v.w;
+      r[q] = *reinterpret_cast<const float4*>(G + (int64_t)(k0 + k) * ld + x4);
     }
   }
 }
+
+template <int LAY, int X>
+__device__ inline void lstore(float* sT, const float4 (&r)[stage_vecs<X>()]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < stage_vecs<X>(); ++q) {
+    const int idx = tid + 256 * q;
+    if (LAY == XK) {
+      const int x = idx >> 3, k4 = (idx & 7) * 4;
+      sT[(k4 + 0) * LDT + x] = r[q].x;
+      sT[(k4 + 1) * LDT + x] = r[q].y;
+      sT[(k4 + 2) * LDT + x] = r[q].z;
+      sT[(k4 + 3) * LDT + x] = r[q].w;
+    } else {
+      const int k = idx / (X / 4), x4 = (idx % (X / 4)) * 4;
+      sT[k * LDT + x4 + 0] = r[q].x;
+      sT[k * LDT + x4 + 1] = r[q].y;
+      sT[k * LDT + x4 + 2] = r[q].z;
+      sT[k * LDT + x4 + 3] = r[q].w;
+    }
+  }
+}
+
+// LDS of a tile product: two buffers each of the A and B stages
+constexpr size_t kTileLds = 4 * (size_t)KS * LDT * sizeof(float);
 
 // Workgroup tile product: out(x=i, y=j) = sum_k A(i, k) B(j, k) for an
 // MR x MC output (MR = WR * TR * 32 rows, MC = WC * TC * 32 columns; four
@@ -484,30 +521,49 @@ struct TileMma {
         for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
   }
 
+  // K in NB / KS stages, double-buffered: stage s + 1 is fetched into
+  // registers while stage s is multiplied, then written to the other LDS
+  // buffer (whose last readers passed the barrier that ended stage s - 1).
   template <int LA, int LB>
-  __device__ void run(const float* Ag, int64_t lda, const float* Bg, int64_t ldb, float* sA,
-                      float* sB) {
+  __device__ void run(const float* Ag, int64_t lda, const float* Bg, int64_t ldb, float* sm) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WC, wn = wave % WC;
     const int lr = lane & 31, lk = lane >> 5;
-    for (int k0 = 0; k0 < NB; k0 += KS) {
-      __syncthreads();
-      stage_load<LA, MR>(sA, Ag, lda, k0);
-      stage_load<LB, MC>(sB, Bg, ldb, k0);
-      __syncthreads();
+    float* sA[2] = {sm, sm + KS * LDT};
+    float* sB[2] = {sm + 2 * KS * LDT, sm + 3 * KS * LDT};
+    float4 ra[stage_vecs<MR>()], rb[stage_vecs<MC>()];
+    gload<LA, MR>(ra, Ag, lda, 0);
+    gload<LB, MC>(rb, Bg, ldb, 0);
+    lstore<LA, MR>(sA[0], ra);
+    lstore<LB, MC>(sB[0], rb);
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < NB / KS; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < NB / KS) {
+        gload<LA, MR>(ra, Ag, lda, (st + 1) * KS);
+        gload<LB, MC>(rb, Bg, ldb, (st + 1) * KS);
+      }
+      const float* cA = sA[cur];
+      const float* cB = sB[cur];
 #pragma unroll
       for (int kk = 0; kk < KS; kk += 2) {
         float af[TR], bf[TC];
 #pragma unroll
-        for (int a = 0; a < TR; ++a) af[a] = sA[(kk + lk) * LDT + (wm * TR + a) * 32 + lr];
+        for (int a = 0; a < TR; ++a) af[a] = cA[(kk + lk) * LDT + (wm * TR + a) * 32 + lr];
 #pragma unroll
-        for (int b = 0; b < TC; ++b) bf[b] = sB[(kk + lk) * LDT + (wn * TC + b) * 32 + lr];
+        for (int b = 0; b < TC; ++b) bf[b] = cB[(kk + lk) * LDT + (wn * TC + b) * 32 + lr];
 #pragma unroll
         for (int a = 0; a < TR; ++a)
 #pragma unroll
           for (int b = 0; b < TC; ++b)
             acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
       }
+      if (st + 1 < NB / KS) {
+        lstore<LA, MR>(sA[cur ^ 1], ra);
+        lstore<LB, MC>(sB[cur ^ 1], rb);
+      }
+      __syncthreads();
     }
   }
 
@@ -538,8 +594,6 @@ struct TileMma {
 __global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, int mode, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
-  float* sA = sm;
-  float* sB = sm + KS * LDT;
   const int t = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   const float* Linv = linv_buf(w, p & 1);
   TileMma<4, 1, 1, 1> mm;
@@ -548,13 +602,13 @@ __global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, in
     const int i = p + 1 + t;
     const float* Aip = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
     // B(j, k) = Linv[32 quarter + j][k]
-    mm.run<XK, XK>(Aip, npad, Linv + (int64_t)32 * quarter * NB, NB, sA, sB);
+    mm.run<XK, XK>(Aip, npad, Linv + (int64_t)32 * quarter * NB, NB, sm);
     mm.store<0>(lp_buf(w, p & 1) + (int64_t)i * NB * NB + 32 * quarter, NB);
   } else {
     const int c = t;
     // A(i, k) = Linv[i][k]; B(j, k) = B[p NB + k][c NB + 32 quarter + j]
     const float* Bpc = w.B + (int64_t)p * NB * npad + (int64_t)c * NB + 32 * quarter;
-    mm.run<XK, KX>(Linv, NB, Bpc, npad, sA, sB);
+    mm.run<XK, KX>(Linv, NB, Bpc, npad, sm);
     mm.store<0>(yp_buf(w, p & 1) + (int64_t)c * NB + 32 * quarter, npad);
   }
 }
@@ -567,8 +621,6 @@ __global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, in
 __global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, int mode, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
-  float* sA = sm;
-  float* sB = sm + KS * LDT;
   const float* Lp = lp_buf(w, p & 1);
   const float* Yp = yp_buf(w, p & 1);
   const int q = P - p - 1;
@@ -581,7 +633,7 @@ __global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, i
     const int quarter = t & 3;
     const int i = p + 1 + (t >> 2), j = p + 1;
     mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB + 32 * quarter * NB, NB,
-                   sA, sB);
+                   sm);
     mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB + 32 * quarter, npad);
     return;
   }
@@ -595,12 +647,12 @@ __global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, i
       int a = 0;
       while (t >= a + 1) { t -= a + 1; ++a; }
       const int i = p + 2 + a, j = p + 2 + t;   // j <= i
-      mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB, NB, sA, sB);
+      mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB, NB, sm);
       mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB, npad);
     } else {
       t -= nsyrk;
       const int i = p + 1 + t / (p + 1), c = t % (p + 1);
-      mm.run<XK, KX>(Lp + (int64_t)i * NB * NB, NB, Yp + (int64_t)c * NB, npad, sA, sB);
+      mm.run<XK, KX>(Lp + (int64_t)i * NB * NB, NB, Yp + (int64_t)c * NB, npad, sm);
       mm.store<1>(w.B + (int64_t)i * NB * npad + (int64_t)c * NB, npad);
     }
   } else {
@@ -693,7 +745,7 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
                        (const int32_t*)perm, npad, w);
     KQ_LAUNCHED("chol_gather");
   }
-  const size_t lds_tile = 2 * (size_t)KS * LDT * sizeof(float);
+  const size_t lds_tile = kTileLds;
   SideStream* ss = nullptr;
   KQ_CHECKED(side_stream(&ss));
   {
