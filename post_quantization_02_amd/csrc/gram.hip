@@ -457,28 +457,25 @@ __device__ __forceinline__ void v2_step(const V2Ctx& c, int64_t it, int64_t st0,
   v2_interleave();
 }
 
-// Item of a pipelined-kernel workgroup.  XCD x (workgroup b runs on XCD b % 8)
-// owns the contiguous range of ceil(ntiles / 8) tiles starting at tile
-// x * ceil(ntiles / 8), compact in the super-tile order, and walks it once per
-// token split, split by split.  The tiles that run together on one XCD then
-// share most of their panels in its L2, and all XCDs stream the same token
-// range at about the same time, so the memory-side cache serves the panels
-// that several XCDs read.
-__device__ inline bool my_item_region(const GramParams& p, int& item) {
+// Item of a pipelined-kernel workgroup.  The split-major item list (item =
+// s * ntiles + t, tiles in super-tile order) is cut into groups of 32
+// consecutive items, and group k runs on XCD k % 8 (workgroup b runs on XCD
+// b % 8): the 32 workgroups of an XCD stream one token range over a compact
+// range of tiles that share most of their panels in its L2, and the XCDs
+// stream at most a few token ranges at a time, so the memory-side cache
+// serves the panels that several XCDs read.
+__device__ inline bool my_item_group(const GramParams& p, int& item) {
   const int b = blockIdx.x;
-  const int x = b % kXcds, li = b / kXcds;
-  const int R = (p.ntiles + kXcds - 1) / kXcds;
-  const int r0 = x * R, rn = min(R, p.ntiles - r0);
-  if (rn <= 0) return false;
-  const int s = li / rn, t = r0 + li % rn;
-  if (s >= p.S) return false;
-  item = s * p.ntiles + t;
+  const int x = b % kXcds, j = b / kXcds;
+  const int it = 32 * (kXcds * (j / 32) + x) + j % 32;
+  if (it >= p.nitems) return false;
+  item = it;
   return true;
 }
 
 __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p) {
   int item;
-  if (!my_item_region(p, item)) return;
+  if (!my_item_group(p, item)) return;
   const int s = item / p.ntiles;
   const int t = item % p.ntiles;
   int ti, tj;
@@ -724,20 +721,19 @@ __global__ void __launch_bounds__(256) gram_finalize_kernel(GramParams p) {
   for (int q = 0; q < 4; ++q) put(p, i, (int64_t)tj * TS + c + q, sum[q], !diag);
 }
 
-int choose_splits(int ntiles, int64_t nstages, bool region) {
-  // smallest S whose item count fills at least 95% of whole CU rounds; else the
-  // best fill; never more splits than stages.  With the per-XCD tile regions
-  // of the pipelined kernel the rounds are counted per XCD.
+int choose_splits(int ntiles, int64_t nstages) {
+  // smallest S whose item count fills at least 98% of whole CU rounds, else
+  // the best fill; at most 16 rounds of items (so the partial tiles stay a
+  // small multiple of H) and never more splits than stages
   int best = 1;
   double best_eff = 0.0;
-  const int smax = (int)std::min<int64_t>(64, nstages);
-  const int per_xcd_cus = kCUs / kXcds, R = (ntiles + kXcds - 1) / kXcds;
+  const int smax = (int)std::max<int64_t>(
+      1, std::min<int64_t>(std::min<int64_t>(64, nstages), 16 * kCUs / ntiles));
   for (int S = 1; S <= smax; ++S) {
     const int64_t items = (int64_t)ntiles * S;
-    const int64_t rounds = region ? ((int64_t)R * S + per_xcd_cus - 1) / per_xcd_cus
-                                  : (items + kCUs - 1) / kCUs;
+    const int64_t rounds = (items + kCUs - 1) / kCUs;
     const double eff = (double)items / (double)(rounds * kCUs);
-    if (eff >= 0.95) return S;
+    if (eff >= 0.98) return S;
     if (eff > best_eff + 1e-9) { best_eff = eff; best = S; }
   }
   return best;
@@ -749,7 +745,7 @@ void plan(int64_t N, int64_t d, int32_t dtype, int& T, int& ntiles, int& S, int6
   T = (int)((d + ts - 1) / ts);
   ntiles = T * (T + 1) / 2;
   nstages = (N + kst - 1) / kst;
-  S = choose_splits(ntiles, nstages, dtype == KRONQ_BF16 && d % BT == 0);
+  S = choose_splits(ntiles, nstages);
 }
 
 }  // namespace
@@ -773,7 +769,8 @@ kronq_status launch_gram(GramParams p, int kind, hipStream_t s) {
   p.per_xcd = (p.nitems + kXcds - 1) / kXcds;
   const int grid = p.per_xcd * kXcds;
   if (kind == 0) {
-    const int rgrid = kXcds * ((p.ntiles + kXcds - 1) / kXcds) * p.S;
+    const int ngroups = (p.nitems + 31) / 32;
+    const int rgrid = 32 * kXcds * ((ngroups + kXcds - 1) / kXcds);
     hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(rgrid), dim3(BTHREADS), 0, s, p);
     KQ_LAUNCHED("gram_bf16_lds_kernel");
   } else if (kind == 1) {
