@@ -30,8 +30,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int RT = 16;         // rows per workgroup
 constexpr int BLK = 128;       // columns per block
-constexpr int GT = 256;        // threads
-constexpr int RLD = BLK + 4;   // LDS stride of the R block (floats)
+constexpr int CT = 256;        // chain threads (waves 0..3)
+constexpr int GT = 512;        // threads: chain waves, then four product waves
 
 struct GptqParams {
   const float* W;
@@ -49,6 +49,7 @@ struct GptqParams {
   double* E;               // m x ldE, processing order
   int64_t ldE;             // n rounded up to 16 (128-byte rows)
   const double* pc;        // per-channel (scale, zero) pairs, m x 2
+  bool vec_out;            // natural order, n % 8 == 0, outputs 16-byte aligned
 };
 
 // value of `x` held by lane 16 * (lane / 16) + O, for every lane: DPP
@@ -57,8 +58,8 @@ struct GptqParams {
 template <int O>
 __device__ __forceinline__ double bcast_row(double x) {
   const long long b = __double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, 0x150 + O, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), 0x150 + O, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)b, 0x150 + O, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), 0x150 + O, 0xf, 0xf, false);
   return __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
@@ -111,70 +112,73 @@ __global__ void __launch_bounds__(256) gptq_row_params(GptqParams p, double* pc)
   }
 }
 
-// Left-looking product of one block: the four waves split K = jb into
-// quarters (each a multiple of KB = 32) and walk theirs in batches of 32 k.
-// In MFMA step s of a batch, lane (r = lane % 16, g = lane / 16) supplies
-// E[row0 + r][kb + 8 g + s] and, for accumulator tile t, R[kb + 8 g + s][jb +
-// 8 r + t]: each lane loads 8 contiguous doubles of E and 8 rows of 8
-// contiguous floats of R per batch (16-byte loads), and tile t, column r holds
-// block column 8 r + t.
-constexpr int KB = 32;
-
-struct GqBatch {
-  f64x2_t e[4];       // E[arow][kb + 8 g .. + 7]
-  f32x4_t r[8][2];    // R[kb + 8 g + s][jb + 8 r .. + 7]
-};
-
-__device__ __forceinline__ void gq_load(GqBatch& B, const double* Eb, const float* Rb, int64_t ldr,
-                                        int64_t kb) {
-  const double* e = Eb + kb;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) B.e[q] = *reinterpret_cast<const f64x2_t*>(e + 2 * q);
-  const float* r = Rb + kb * ldr;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    B.r[s][0] = *reinterpret_cast<const f32x4_t*>(r + s * ldr);
-    B.r[s][1] = *reinterpret_cast<const f32x4_t*>(r + s * ldr + 4);
-  }
-}
-
-// acc[t] += E R over the batch; `live` false turns the batch into a no-op
-// (its E operand is zeroed) without a branch around the accumulators
-__device__ __forceinline__ void gq_mma(const GqBatch& B, bool live, f64x4_t (&acc)[8]) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const double a = live ? B.e[s >> 1][s & 1] : 0.0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t >> 2][t & 3], acc[t], 0, 0, 0);
-  }
-}
-
 // An empty register-only asm hides the value from the optimizer, so that an
-// address built from it is recomputed at each use instead of being hoisted
-// out of the block loop (one live register per column otherwise).
+// address built from it is recomputed where it is used instead of being
+// hoisted out of the block loop (one live register per octet otherwise).
 __device__ __forceinline__ int opaque_int(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
 
-// State of one lane in the block's column loop: the lane's 8 columns of its
-// row (v), the outputs of the columns it owns, and the grid parameters.
-struct InBlock {
-  double (&v)[8], (&ev)[8], (&wq)[8], (&tv)[8];
-  int (&qv)[8];
-  double scale, zero, inv_scale;
-  f32x4_t r0, r1;   // staged R row of the next column (this lane's 8 entries)
-  double id;        // 1 / R_cc of the next column
+constexpr int KB = 32;   // k per batch of the product
+
+// ---------------------------------------------------------------------------
+// Main kernel.  One workgroup owns RT = 16 rows; its eight waves have two
+// roles that run side by side, one of each on every SIMD:
+//   chain waves 0..3   walk the 128 columns of block b one after another
+//                      (rows 4 w .. 4 w + 3, 16 lanes per row, 8 columns per
+//                      lane), then write the block's outputs and errors;
+//   product waves 4..7 meanwhile form block b + 1's start values from the
+//                      errors of blocks 0 .. b - 1 (E R on the fp64 matrix
+//                      cores) and, once block b's errors are out, add block
+//                      b's share.
+// LDS (exactly 160 KiB):
+//   Rsq  128 x 128 doubles: the diagonal block of R, strictly upper part
+//        (zeros on and below the diagonal, so compensating with a row needs no
+//        column test); row 127 has no entries above the diagonal and holds
+//        1 / R_cc instead
+//   P0   16 x 128 doubles: W minus the first half of the K range's product
+//   P1   16 x 128 doubles: the second half's product
+// The start value of (row, column) is P0 - P1.
+constexpr int SQ = BLK * BLK;   // doubles in Rsq
+constexpr size_t kGptqLds = (size_t)(SQ + 2 * RT * BLK) * sizeof(double);
+static_assert(kGptqLds == 160 * 1024, "LDS layout");
+
+// Quantize one value onto the grid: grid coordinate t, code q, and the scaled
+// error e = (v - w_q) / R_cc with w_q = scale (q - zero).  The column loop and
+// the output pass call this same function, so their e agree bit for bit.
+struct Quant {
+  double t, q, e;
 };
+__device__ __forceinline__ Quant quant(double v, double scale, double zero, double inv_scale,
+                                       double maxq, double id) {
+#pragma clang fp contract(off)
+  Quant r;
+  r.t = fma(v, inv_scale, zero);
+  r.q = fmin(fmax(rint(r.t), 0.0), maxq);
+  r.e = fma(-scale, r.q - zero, v) * id;
+  return r;
+}
+
+// ---- chain role ----
+
+struct Chain {
+  double v[8];               // this lane's 8 columns of its row
+  f64x2_t rc[4];             // staged R row of the current column (this lane's 8 entries)
+  double idc;                // 1 / R_cc of the current column
+  double scale, zero, inv_scale;     // grid of the current group
+  double oscale, ozero, oinv;        // grid of the group holding this lane's columns
+};
+
+__device__ __forceinline__ double rc_at(const Chain& st, int q) { return st.rc[q >> 1][q & 1]; }
 
 // Columns 8 O .. 8 O + 7 of the block (owned by lane O of each 16-lane row).
 template <int O>
-__device__ __forceinline__ void in_block_octet(InBlock& st, const GptqParams& p, const float* Rb,
-                                               const double* invd, int part_id, bool row_ok,
-                                               int64_t grow, int64_t jb, int ncols, int maxq) {
+__device__ __forceinline__ void chain_octet(Chain& st, const GptqParams& p, const double* Rsq,
+                                            int part_id, bool row_ok, int64_t grow, int64_t jb,
+                                            int ncols, double maxq) {
   if (p.group > 0 && ((8 * O) % p.group) == 0) {
-    // parameters of the group [8 O, 8 O + group) from the current values
+    // grid of the group [8 O, 8 O + group) from the current values
     const int c = 8 * O;
     double lo = INFINITY, hi = -INFINITY;
 #pragma unroll
@@ -196,42 +200,45 @@ __device__ __forceinline__ void in_block_octet(InBlock& st, const GptqParams& p,
       p.scales[grow * p.ngroups + g] = (float)st.scale;
       p.zeros[grow * p.ngroups + g] = (float)st.zero;
     }
+    const bool mine = 8 * part_id >= c && 8 * part_id < c + p.group;
+    st.oscale = mine ? st.scale : st.oscale;
+    st.ozero = mine ? st.zero : st.ozero;
+    st.oinv = mine ? st.inv_scale : st.oinv;
   }
-  const bool own = part_id == O;
+  // this lane's entries of row 8 O, and the reciprocal diagonal from column
+  // 8 O on: one address per octet (kept out of the block loop by the empty
+  // asm), the columns' offsets are immediates
+  const double* rb = Rsq + 8 * O * BLK + opaque_int(8 * part_id);
+  const double* ib = Rsq + (BLK - 1) * BLK + opaque_int(8 * O);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int c = 8 * O + s;
-    // this column's staged R row and 1 / R_cc were read one column ahead;
-    // read the next column's now
-    const f32x4_t r0v = st.r0, r1v = st.r1;
-    const double id = st.id;
-    if (c + 1 < BLK) {
-      const float* Rn = Rb + (c + 1) * RLD + opaque_int(8 * part_id);
-      st.r0 = *reinterpret_cast<const f32x4_t*>(Rn);
-      st.r1 = *reinterpret_cast<const f32x4_t*>(Rn + 4);
-      st.id = invd[opaque_int(c + 1)];
-    }
-    // owner lane: round column c
-    const double t = fma(st.v[s], st.inv_scale, st.zero);
-    const double q = fmin(fmax(rint(t), 0.0), (double)maxq);
-    const double w_q = st.scale * (q - st.zero);
-    const double e = (st.v[s] - w_q) * id;
-    // select now (an empty asm pins each result here): left to itself the
-    // compiler keeps every octet's candidates live and selects at the end
-    st.ev[s] = own ? e : st.ev[s];
-    st.wq[s] = own ? w_q : st.wq[s];
-    st.tv[s] = own ? t : st.tv[s];
-    st.qv[s] = own ? (int)q : st.qv[s];
-    asm volatile("" : "+v"(st.ev[s]), "+v"(st.wq[s]), "+v"(st.tv[s]), "+v"(st.qv[s]));
-    const double eb = bcast_row<O>(e);
-    // compensate the later columns of the block held by this lane (the
-    // staged row is zero at and before column c); the next column first
-    if (s + 1 < 8) st.v[s + 1] = fma(-eb, (double)(s + 1 < 4 ? r0v[(s + 1) & 3] : r1v[(s + 1) & 3]), st.v[s + 1]);
+    // the next column's staged row and 1 / R_cc (row 127 holds no R entries:
+    // column 127 compensates nothing)
+    f64x2_t rn[4];
+    double idn = 0.0;
+    if (c + 1 < BLK - 1) {
 #pragma unroll
-    for (int q2 = 0; q2 < 8; ++q2) {
-      if (q2 == s + 1) continue;
-      st.v[q2] = fma(-eb, (double)(q2 < 4 ? r0v[q2 & 3] : r1v[q2 & 3]), st.v[q2]);
+      for (int q = 0; q < 4; ++q) rn[q] = *reinterpret_cast<const f64x2_t*>(rb + (s + 1) * BLK + 2 * q);
     }
+    if (c + 1 < BLK) idn = ib[s + 1];
+    // the owner lane quantizes column c; its error goes to the whole row
+    const Quant z = quant(st.v[s], st.scale, st.zero, st.inv_scale, maxq, st.idc);
+    const double eb = bcast_row<O>(z.e);
+    if (c + 1 < BLK) {
+      // compensate the later columns held by this lane (the staged row is zero
+      // at and before column c); the next column first
+      const int nx = (s + 1) & 7;
+      st.v[nx] = fma(-eb, rc_at(st, nx), st.v[nx]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q != nx) st.v[q] = fma(-eb, rc_at(st, q), st.v[q]);
+    }
+    if (c + 1 < BLK - 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st.rc[q] = rn[q];
+    }
+    st.idc = idn;
     // keep the scheduler from hoisting later columns' reads (one straight
     // line of 128 columns would otherwise be scheduled as a whole)
     __builtin_amdgcn_sched_barrier(0);
@@ -239,167 +246,306 @@ __device__ __forceinline__ void in_block_octet(InBlock& st, const GptqParams& p,
 }
 
 template <int... O>
-__device__ __forceinline__ void in_block_octets(InBlock& st, const GptqParams& p, const float* Rb,
-                                                const double* invd, int part_id, bool row_ok,
-                                                int64_t grow, int64_t jb, int ncols, int maxq,
-                                                std::integer_sequence<int, O...>) {
-  (in_block_octet<O>(st, p, Rb, invd, part_id, row_ok, grow, jb, ncols, maxq), ...);
+__device__ __forceinline__ void chain_octets(Chain& st, const GptqParams& p, const double* Rsq,
+                                             int part_id, bool row_ok, int64_t grow, int64_t jb,
+                                             int ncols, double maxq, std::integer_sequence<int, O...>) {
+  (chain_octet<O>(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq), ...);
 }
 
-__global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
-  extern __shared__ __align__(16) double gl[];
-  double* part = gl;                                       // 4 x RT x BLK doubles
-  float* Rb = reinterpret_cast<float*>(gl + 4 * RT * BLK);  // BLK x RLD floats
-  double* invd = reinterpret_cast<double*>(Rb + BLK * RLD); // BLK doubles
+// Stage the diagonal block at column jb into Rsq.  Threads t = 0 .. CT - 1.
+__device__ __forceinline__ void stage_rsq(const GptqParams& p, double* Rsq, int64_t jb, int ncols,
+                                          int t) {
+  if (ncols == BLK) {
+#pragma unroll
+    for (int q = 0; q < SQ / 4 / CT; ++q) {
+      const int e4 = t + CT * q;
+      const int i = e4 / (BLK / 4), j = (e4 % (BLK / 4)) * 4;
+      if (i == BLK - 1) continue;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.R + (jb + i) * p.ldr + jb + j);
+      f64x2_t lo, hi;
+      lo[0] = (j > i) ? (double)v[0] : 0.0;
+      lo[1] = (j + 1 > i) ? (double)v[1] : 0.0;
+      hi[0] = (j + 2 > i) ? (double)v[2] : 0.0;
+      hi[1] = (j + 3 > i) ? (double)v[3] : 0.0;
+      *reinterpret_cast<f64x2_t*>(Rsq + i * BLK + j) = lo;
+      *reinterpret_cast<f64x2_t*>(Rsq + i * BLK + j + 2) = hi;
+    }
+  } else {
+    for (int e = t; e < SQ - BLK; e += CT) {
+      const int i = e / BLK, j = e % BLK;
+      Rsq[e] = (i < ncols && j < ncols && j > i) ? (double)p.R[(jb + i) * p.ldr + jb + j] : 0.0;
+    }
+  }
+  for (int j = t; j < BLK; j += CT) {
+    const int64_t jj = min<int64_t>(jb + j, p.n - 1);
+    const double rd = (double)p.R[jj * p.ldr + jj];
+    Rsq[(BLK - 1) * BLK + j] = (j < ncols) ? 1.0 / rd : 0.0;
+  }
+}
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int tid) {
+  double* Rsq = gl;
+  const double* P0 = gl + SQ;
+  const double* P1 = P0 + RT * BLK;
+  const int wave = tid >> 6, lane = tid & 63;
   const int64_t row0 = (int64_t)blockIdx.x * RT;
-  // in-block mapping
   const int lrow = 4 * wave + (lane >> 4);  // 0..15
   const int part_id = lane & 15;            // 8 columns each
   const int64_t grow = row0 + lrow;
   const bool row_ok = grow < p.m;
-  const int maxq = (1 << p.bits) - 1;
+  const double maxq = (double)((1 << p.bits) - 1);
 
-  double scale = 1.0, zero = 0.0;
+  Chain st;
+  st.scale = 1.0;
+  st.zero = 0.0;
   if (p.group == 0 && row_ok) {
-    scale = p.pc[2 * grow];
-    zero = p.pc[2 * grow + 1];
+    st.scale = p.pc[2 * grow];
+    st.zero = p.pc[2 * grow + 1];
   }
-  double inv_scale = 1.0 / scale;
+  st.inv_scale = 1.0 / st.scale;
+  st.oscale = st.scale;
+  st.ozero = st.zero;
+  st.oinv = st.inv_scale;
 
   const int nblocks = (int)((p.n + BLK - 1) / BLK);
+  stage_rsq(p, Rsq, 0, (int)min<int64_t>(BLK, p.n), tid);
+  __syncthreads();
   for (int b = 0; b < nblocks; ++b) {
     const int64_t jb = (int64_t)b * BLK;
     const int ncols = (int)min<int64_t>(BLK, p.n - jb);
-
-    // ---- 1. left-looking update on the matrix cores ----
+    // ---- the columns of block b ----
     {
-      f64x4_t acc[8];
+      const double* p0 = P0 + lrow * BLK + 8 * part_id;
+      const double* p1 = P1 + lrow * BLK + 8 * part_id;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-      const int64_t kq = jb / 4;  // multiple of KB
-      const int64_t k_lo = kq * wave;
-      const int nb = (int)(kq / KB);
-      if (nb > 0) {
-        const int r = lane & 15, g = lane >> 4;
-        // rows past m read row m - 1 (results discarded); columns past n in
-        // the last block read the next row of R or its padding (rows k < jb
-        // <= n - 2, so the reads stay inside R; results discarded)
-        const int64_t arow = min<int64_t>(row0 + r, p.m - 1);
-        const double* Eb = p.E + arow * p.ldE + 8 * g;
-        const float* Rg = p.R + (int64_t)(8 * g) * p.ldr + jb + 8 * r;
-        // two register buffers, each refilled a whole batch of MFMAs before
-        // it is consumed; the scheduling barriers keep the compiler from
-        // sinking the loads next to their use
-        GqBatch A, B;
-        gq_load(A, Eb, Rg, p.ldr, k_lo);
-        for (int i = 0; i < nb; i += 2) {
-          gq_load(B, Eb, Rg, p.ldr, k_lo + (int64_t)KB * min(i + 1, nb - 1));
-          __builtin_amdgcn_sched_barrier(0);
-          gq_mma(A, true, acc);
-          __builtin_amdgcn_sched_barrier(0);
-          gq_load(A, Eb, Rg, p.ldr, k_lo + (int64_t)KB * min(i + 2, nb - 1));
-          __builtin_amdgcn_sched_barrier(0);
-          gq_mma(B, i + 1 < nb, acc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const f64x2_t a = *reinterpret_cast<const f64x2_t*>(p0 + 2 * q);
+        const f64x2_t c = *reinterpret_cast<const f64x2_t*>(p1 + 2 * q);
+        st.v[2 * q] = a[0] - c[0];
+        st.v[2 * q + 1] = a[1] - c[1];
+        st.rc[q] = *reinterpret_cast<const f64x2_t*>(Rsq + 8 * part_id + 2 * q);
       }
-      // partial of this wave -> LDS; f64 16x16 accumulator layout: register v
-      // holds row 4 v + lane / 16; tile t, lane column r is block column 8 r + t
-      double* pw = part + wave * RT * BLK;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) pw[(4 * v + (lane >> 4)) * BLK + 8 * (lane & 15) + t] = acc[t][v];
+      st.idc = Rsq[(BLK - 1) * BLK];
     }
-    // stage the diagonal block of R: strictly upper part (zeros on and below
-    // the diagonal, so compensating with a row needs no column test) and the
-    // reciprocal diagonal
-    if (ncols == BLK) {
-#pragma unroll
-      for (int q = 0; q < BLK * BLK / 4 / GT; ++q) {
-        const int e4 = tid + GT * q;
-        const int i = e4 / (BLK / 4), j = (e4 % (BLK / 4)) * 4;
-        f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.R + (jb + i) * p.ldr + jb + j);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = (j + u > i) ? v[u] : 0.f;
-        *reinterpret_cast<f32x4_t*>(Rb + i * RLD + j) = v;
-      }
-    } else {
-      for (int e = tid; e < BLK * BLK; e += GT) {
-        const int i = e / BLK, j = e % BLK;
-        Rb[i * RLD + j] = (i < ncols && j < ncols && j > i) ? p.R[(jb + i) * p.ldr + jb + j] : 0.f;
-      }
-    }
-    for (int i = tid; i < BLK; i += GT) {
-      const int64_t ii = min<int64_t>(jb + i, p.n - 1);
-      const double rd = (double)p.R[ii * p.ldr + ii];
-      invd[i] = (i < ncols) ? 1.0 / rd : 0.0;
-    }
-    __syncthreads();
-    // reduce the four partials and add W (natural column perm[jb + c]);
-    // rows past m and columns past n read clamped addresses and get zero
-    for (int e = tid; e < RT * BLK; e += GT) {
-      const int r = e / BLK, c = e % BLK;
-      const int64_t gr = row0 + r;
-      const bool ok = gr < p.m && c < ncols;
-      const int64_t wr = min<int64_t>(gr, p.m - 1);
-      const int64_t wc = colmap(p, min<int64_t>(jb + c, p.n - 1));
-      const double w = (double)p.W[wr * p.ldw + wc];
-      const double s4 = part[e] + part[RT * BLK + e] + part[2 * RT * BLK + e] + part[3 * RT * BLK + e];
-      part[e] = ok ? w - s4 : 0.0;
-    }
-    __syncthreads();
-
-    // ---- 2. sequential columns of the block ----
-    double v[8], ev[8], wq[8], tv[8];
-    int qv[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      v[s] = part[lrow * BLK + 8 * part_id + s];
-      ev[s] = 0.0;
-      wq[s] = 0.0;
-      tv[s] = 0.0;
-      qv[s] = 0;
-    }
-    // Every column of the block is walked (past ncols the values, invd and
-    // staged rows are zero and nothing is stored), so the loop has no exit
-    // inside and the reads of R and invd do not wait on the chain.  The 16
+    // Every column of the block is walked (past ncols the values, staged rows
+    // and reciprocals are zero and nothing is stored), so the loop has no exit
+    // inside and the reads of the staged rows do not wait on the chain.  The 16
     // octets of columns are a compile-time sequence, so the owner lane of a
     // column (broadcast by DPP) and the register holding it are constants.
-    InBlock st{v, ev, wq, tv, qv, scale, zero, inv_scale,
-               *reinterpret_cast<const f32x4_t*>(Rb + 8 * part_id),
-               *reinterpret_cast<const f32x4_t*>(Rb + 8 * part_id + 4), invd[0]};
-    in_block_octets(st, p, Rb, invd, part_id, row_ok, grow, jb, ncols, maxq,
-                    std::make_integer_sequence<int, 16>{});
-    scale = st.scale;
-    zero = st.zero;
-    inv_scale = st.inv_scale;
-    // ---- 3. write errors and outputs of this block ----
+    chain_octets(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq,
+                 std::make_integer_sequence<int, 16>{});
+    // ---- outputs of this lane's columns ----
+    // A column's value is final once its own step is done (later steps
+    // compensate later columns only), so the owner recomputes its outputs
+    // from it with the same arithmetic as in the loop.
     if (row_ok) {
+      const double* idr = Rsq + (BLK - 1) * BLK + 8 * part_id;
+      double ev[8], wq[8], tv[8];
+      int qv[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int c = 8 * part_id + s;
-        if (c < ncols) {
-          const int64_t j = jb + c;
-          p.E[grow * p.ldE + j] = ev[s];
-          const int64_t nc = colmap(p, j);
-          p.codes[grow * p.n + nc] = (uint8_t)qv[s];
-          if (p.What) p.What[grow * p.n + nc] = (float)wq[s];
-          if (p.pre) p.pre[grow * p.n + nc] = (float)tv[s];
+        const Quant z = quant(st.v[s], st.oscale, st.ozero, st.oinv, maxq, idr[s]);
+        ev[s] = z.e;
+        tv[s] = z.t;
+        qv[s] = (int)z.q;
+        wq[s] = st.oscale * (z.q - st.ozero);
+      }
+      const int c0 = 8 * part_id;
+      const int64_t j0 = jb + c0;
+      if (c0 + 8 <= ncols) {
+#pragma unroll
+        for (int s = 0; s < 8; s += 2)
+          *reinterpret_cast<f64x2_t*>(p.E + grow * p.ldE + j0 + s) = f64x2_t{ev[s], ev[s + 1]};
+      } else {
+        for (int s = 0; s < 8; ++s)
+          if (c0 + s < ncols) p.E[grow * p.ldE + j0 + s] = ev[s];
+      }
+      if (p.vec_out && c0 + 8 <= ncols) {
+        // natural order, 8 consecutive columns, aligned
+        const int64_t o = grow * p.n + j0;
+        uint32_t c4[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c4[h] = (uint32_t)qv[4 * h] | ((uint32_t)qv[4 * h + 1] << 8) | ((uint32_t)qv[4 * h + 2] << 16) |
+                  ((uint32_t)qv[4 * h + 3] << 24);
+        *reinterpret_cast<uint2*>(p.codes + o) = make_uint2(c4[0], c4[1]);
+        if (p.What) {
+          *reinterpret_cast<f32x4_t*>(p.What + o) = f32x4_t{(float)wq[0], (float)wq[1], (float)wq[2], (float)wq[3]};
+          *reinterpret_cast<f32x4_t*>(p.What + o + 4) = f32x4_t{(float)wq[4], (float)wq[5], (float)wq[6], (float)wq[7]};
+        }
+        if (p.pre) {
+          *reinterpret_cast<f32x4_t*>(p.pre + o) = f32x4_t{(float)tv[0], (float)tv[1], (float)tv[2], (float)tv[3]};
+          *reinterpret_cast<f32x4_t*>(p.pre + o + 4) = f32x4_t{(float)tv[4], (float)tv[5], (float)tv[6], (float)tv[7]};
+        }
+      } else {
+        for (int s = 0; s < 8; ++s) {
+          if (c0 + s < ncols) {
+            const int64_t nc = colmap(p, j0 + s);
+            p.codes[grow * p.n + nc] = (uint8_t)qv[s];
+            if (p.What) p.What[grow * p.n + nc] = (float)wq[s];
+            if (p.pre) p.pre[grow * p.n + nc] = (float)tv[s];
+          }
         }
       }
     }
-    // E of this block is read by the other waves of this workgroup in the
-    // next block's product: the barrier's workgroup-scope release/acquire
-    // orders those global stores before the loads (the lines of the new
-    // columns were never cached by this CU)
+    // The E stores reach the product waves' loads through this barrier's
+    // workgroup-scope release/acquire (the lines of a block's columns are
+    // never read before they are written, so no stale copy sits in this CU's
+    // cache).
+    __syncthreads();
+    if (b + 1 < nblocks) stage_rsq(p, Rsq, jb + BLK, (int)min<int64_t>(BLK, p.n - jb - BLK), tid);
     __syncthreads();
   }
 }
 
+// ---- product role ----
+//
+// Product wave pw = 0..3 covers columns 64 ch .. 64 ch + 63 of the next block
+// (ch = pw & 1; four 16 x 16 tiles) over half kh = pw >> 1 of the K range, in
+// batches of 32 k.  In MFMA step s of a batch, lane (r = lane % 16, g = lane /
+// 16) supplies E[row r][kb + 8 g + s] and, for tile t, R[kb + 8 g + s][64 ch +
+// 4 r + t]: each lane loads 8 contiguous doubles of E and 8 rows of 4
+// contiguous floats of R per batch (16-byte loads).  Tile t's lane column r is
+// block column 64 ch + 4 r + t; accumulator register v holds row 4 v + g.
+struct PBatch {
+  f64x2_t e[4];   // E[arow][kb + 8 g .. + 7]
+  f32x4_t r[8];   // R[kb + 8 g + s][64 ch + 4 r .. + 3]
+};
+
+__device__ __forceinline__ void pb_load(PBatch& B, const double* Eg, const float* Rg, int64_t ldr,
+                                        int64_t kb) {
+  const double* e = Eg + kb;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) B.e[q] = *reinterpret_cast<const f64x2_t*>(e + 2 * q);
+  const float* r = Rg + kb * ldr;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) B.r[s] = *reinterpret_cast<const f32x4_t*>(r + s * ldr);
+}
+
+__device__ __forceinline__ void pb_mma(const PBatch& B, f64x4_t (&acc)[4]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const double a = B.e[s >> 1][s & 1];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t], acc[t], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void product_role(const GptqParams& p, double* gl, int tid) {
+  double* P0 = gl + SQ;
+  double* P1 = P0 + RT * BLK;
+  const int pw = (tid >> 6) - CT / 64, lane = tid & 63;
+  const int kh = pw >> 1, ch = pw & 1;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * RT;
+  // rows past m read row m - 1 (results discarded); columns past n in the
+  // last block read the next row of R or its padding (rows k < jn <= n - 2
+  // when the next block is not empty, so the reads stay inside R; results
+  // discarded)
+  const int64_t arow = min<int64_t>(row0 + r, p.m - 1);
+  const double* Eg = p.E + arow * p.ldE + 8 * g;
+  const int nblocks = (int)((p.n + BLK - 1) / BLK);
+  double* P = kh == 0 ? P0 : P1;
+
+  // W of the block at column jn for this lane's outputs (first K half only)
+  auto load_w = [&](int64_t jn, float (&w)[4][4]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t wr = min<int64_t>(row0 + 4 * v + g, p.m - 1);
+        const int64_t wc = colmap(p, min<int64_t>(jn + 64 * ch + 4 * r + t, p.n - 1));
+        w[v][t] = p.W[wr * p.ldw + wc];
+      }
+  };
+  // start values of the block at column jn: W - acc (first half), acc (second)
+  auto store = [&](int64_t jn, const f64x4_t (&acc)[4], const float (&w)[4][4]) {
+    const int ncn = (int)min<int64_t>(BLK, p.n - jn);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 4 * v + g;
+      const bool rok = row0 + row < p.m;
+      double o[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int col = 64 * ch + 4 * r + t;
+        const double x = kh == 0 ? (double)w[v][t] - acc[t][v] : acc[t][v];
+        o[t] = (rok && col < ncn) ? x : 0.0;
+      }
+      double* d = P + row * BLK + 64 * ch + 4 * r;
+      *reinterpret_cast<f64x2_t*>(d) = f64x2_t{o[0], o[1]};
+      *reinterpret_cast<f64x2_t*>(d + 2) = f64x2_t{o[2], o[3]};
+    }
+  };
+
+  {
+    // block 0: no product yet
+    float w[4][4];
+    if (kh == 0) load_w(0, w);
+    f64x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    store(0, acc, w);
+  }
+  __syncthreads();
+  for (int b = 0; b < nblocks; ++b) {
+    const int64_t jb = (int64_t)b * BLK, jn = jb + BLK;
+    const bool more = b + 1 < nblocks;
+    const float* Rg = p.R + (int64_t)(8 * g) * p.ldr + jn + 64 * ch + 4 * r;
+    f64x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    float w[4][4];
+    if (more && kh == 0) load_w(jn, w);
+    // errors of blocks 0 .. b - 1: this half of [0, jb) is 2 b batches
+    const int nbat = more ? 2 * b : 0;
+    if (nbat > 0) {
+      const int64_t k0 = (int64_t)kh * (jb / 2);
+      // two register buffers, each refilled a whole batch of MFMAs before it
+      // is consumed; the scheduling barriers keep the compiler from sinking
+      // the loads next to their use
+      PBatch A, B;
+      pb_load(A, Eg, Rg, p.ldr, k0);
+      for (int i = 0; i < nbat; i += 2) {
+        pb_load(B, Eg, Rg, p.ldr, k0 + (int64_t)KB * (i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        pb_mma(A, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        pb_load(A, Eg, Rg, p.ldr, k0 + (int64_t)KB * min(i + 2, nbat - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        pb_mma(B, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    if (more) {
+      // block b's errors: this half of [jb, jb + 128)
+      PBatch A, B;
+      pb_load(A, Eg, Rg, p.ldr, jb + BLK / 2 * kh);
+      pb_load(B, Eg, Rg, p.ldr, jb + BLK / 2 * kh + KB);
+      pb_mma(A, acc);
+      pb_mma(B, acc);
+      store(jn, acc, w);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
+  extern __shared__ __align__(16) double gl[];
+  const int tid = threadIdx.x;
+  // the role is uniform per wave: a scalar branch; both roles pass the same
+  // sequence of barriers
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) < CT / 64)
+    chain_role(p, gl, tid);
+  else
+    product_role(p, gl, tid);
+}
+
 int64_t lde(int64_t n) { return (n + 15) / 16 * 16; }
+
+bool aligned(const void* q, size_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; }
 
 }  // namespace
 
@@ -437,11 +583,13 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
   double* pc = reinterpret_cast<double*>(static_cast<char*>(ws) +
                                          align_up((size_t)m * p.ldE * sizeof(double), 256));
   p.pc = pc;
+  p.vec_out = perm == nullptr && n % 8 == 0 && aligned(codes, 8) && (What == nullptr || aligned(What, 16)) &&
+              (pre_round == nullptr || aligned(pre_round, 16));
   if (group == 0) {
     hipLaunchKernelGGL(gptq_row_params, dim3((unsigned)m), dim3(256), 0, s, p, pc);
     KQ_LAUNCHED("gptq_row_params");
   }
-  const size_t lds = 4 * RT * BLK * sizeof(double) + BLK * RLD * sizeof(float) + BLK * sizeof(double);
+  const size_t lds = kGptqLds;
   KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)lds));
   hipLaunchKernelGGL(gptq_kernel, dim3((unsigned)((m + RT - 1) / RT)), dim3(GT), lds, s, p);
