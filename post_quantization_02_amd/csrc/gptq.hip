@@ -49,6 +49,9 @@ struct GptqParams {
   double* E;               // m x ldE, processing order
   int64_t ldE;             // n rounded up to 16 (128-byte rows)
   const double* pc;        // per-channel (scale, zero) pairs, m x 2
+  double* R64;             // fp64 copy of R right of the diagonal blocks, n x ldr64
+  int64_t ldr64;
+  double* D64;             // staged images of the diagonal blocks, nblocks x 128 x 128
   bool vec_out;            // natural order, n % 8 == 0, outputs 16-byte aligned
 };
 
@@ -252,34 +255,18 @@ __device__ __forceinline__ void chain_octets(Chain& st, const GptqParams& p, con
   (chain_octet<O>(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq), ...);
 }
 
-// Stage the diagonal block at column jb into Rsq.  Threads t = 0 .. CT - 1.
-__device__ __forceinline__ void stage_rsq(const GptqParams& p, double* Rsq, int64_t jb, int ncols,
-                                          int t) {
-  if (ncols == BLK) {
+// Stage diagonal block b (its fp64 image, made once per call) into Rsq.
+// Threads t = 0 .. CT - 1; a plain copy of 128 KiB.
+__device__ __forceinline__ void stage_rsq(const GptqParams& p, double* Rsq, int b, int t) {
+  const f64x2_t* src = reinterpret_cast<const f64x2_t*>(p.D64 + (int64_t)b * SQ);
+  f64x2_t* dst = reinterpret_cast<f64x2_t*>(Rsq);
 #pragma unroll
-    for (int q = 0; q < SQ / 4 / CT; ++q) {
-      const int e4 = t + CT * q;
-      const int i = e4 / (BLK / 4), j = (e4 % (BLK / 4)) * 4;
-      if (i == BLK - 1) continue;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.R + (jb + i) * p.ldr + jb + j);
-      f64x2_t lo, hi;
-      lo[0] = (j > i) ? (double)v[0] : 0.0;
-      lo[1] = (j + 1 > i) ? (double)v[1] : 0.0;
-      hi[0] = (j + 2 > i) ? (double)v[2] : 0.0;
-      hi[1] = (j + 3 > i) ? (double)v[3] : 0.0;
-      *reinterpret_cast<f64x2_t*>(Rsq + i * BLK + j) = lo;
-      *reinterpret_cast<f64x2_t*>(Rsq + i * BLK + j + 2) = hi;
-    }
-  } else {
-    for (int e = t; e < SQ - BLK; e += CT) {
-      const int i = e / BLK, j = e % BLK;
-      Rsq[e] = (i < ncols && j < ncols && j > i) ? (double)p.R[(jb + i) * p.ldr + jb + j] : 0.0;
-    }
-  }
-  for (int j = t; j < BLK; j += CT) {
-    const int64_t jj = min<int64_t>(jb + j, p.n - 1);
-    const double rd = (double)p.R[jj * p.ldr + jj];
-    Rsq[(BLK - 1) * BLK + j] = (j < ncols) ? 1.0 / rd : 0.0;
+  for (int h = 0; h < 2; ++h) {
+    f64x2_t x[SQ / 2 / CT / 2];
+#pragma unroll
+    for (int q = 0; q < SQ / 2 / CT / 2; ++q) x[q] = src[t + CT * (q + h * SQ / 2 / CT / 2)];
+#pragma unroll
+    for (int q = 0; q < SQ / 2 / CT / 2; ++q) dst[t + CT * (q + h * SQ / 2 / CT / 2)] = x[q];
   }
 }
 
@@ -287,7 +274,7 @@ __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int 
   double* Rsq = gl;
   const double* P0 = gl + SQ;
   const double* P1 = P0 + RT * BLK;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t row0 = (int64_t)blockIdx.x * RT;
   const int lrow = 4 * wave + (lane >> 4);  // 0..15
   const int part_id = lane & 15;            // 8 columns each
@@ -308,7 +295,7 @@ __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int 
   st.oinv = st.inv_scale;
 
   const int nblocks = (int)((p.n + BLK - 1) / BLK);
-  stage_rsq(p, Rsq, 0, (int)min<int64_t>(BLK, p.n), tid);
+  stage_rsq(p, Rsq, 0, tid);
   __syncthreads();
   for (int b = 0; b < nblocks; ++b) {
     const int64_t jb = (int64_t)b * BLK;
@@ -393,7 +380,7 @@ __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int 
     // never read before they are written, so no stale copy sits in this CU's
     // cache).
     __syncthreads();
-    if (b + 1 < nblocks) stage_rsq(p, Rsq, jb + BLK, (int)min<int64_t>(BLK, p.n - jb - BLK), tid);
+    if (b + 1 < nblocks) stage_rsq(p, Rsq, b + 1, tid);
     __syncthreads();
   }
 }
@@ -405,21 +392,26 @@ __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int 
 // batches of 32 k.  In MFMA step s of a batch, lane (r = lane % 16, g = lane /
 // 16) supplies E[row r][kb + 8 g + s] and, for tile t, R[kb + 8 g + s][64 ch +
 // 4 r + t]: each lane loads 8 contiguous doubles of E and 8 rows of 4
-// contiguous floats of R per batch (16-byte loads).  Tile t's lane column r is
-// block column 64 ch + 4 r + t; accumulator register v holds row 4 v + g.
+// contiguous doubles of R per batch (16-byte loads).  Tile t's lane column r
+// is block column 64 ch + 4 r + t; accumulator register v holds row 4 v + g.
+// R is read from its fp64 copy: a conversion in this loop would take issue
+// cycles from the fp64 matrix operations.
 struct PBatch {
-  f64x2_t e[4];   // E[arow][kb + 8 g .. + 7]
-  f32x4_t r[8];   // R[kb + 8 g + s][64 ch + 4 r .. + 3]
+  f64x2_t e[4];      // E[arow][kb + 8 g .. + 7]
+  f64x2_t r[8][2];   // R[kb + 8 g + s][64 ch + 4 r .. + 3]
 };
 
-__device__ __forceinline__ void pb_load(PBatch& B, const double* Eg, const float* Rg, int64_t ldr,
+__device__ __forceinline__ void pb_load(PBatch& B, const double* Eg, const double* Rg, int64_t ldr,
                                         int64_t kb) {
   const double* e = Eg + kb;
 #pragma unroll
   for (int q = 0; q < 4; ++q) B.e[q] = *reinterpret_cast<const f64x2_t*>(e + 2 * q);
-  const float* r = Rg + kb * ldr;
+  const double* r = Rg + kb * ldr;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) B.r[s] = *reinterpret_cast<const f32x4_t*>(r + s * ldr);
+  for (int s = 0; s < 8; ++s) {
+    B.r[s][0] = *reinterpret_cast<const f64x2_t*>(r + s * ldr);
+    B.r[s][1] = *reinterpret_cast<const f64x2_t*>(r + s * ldr + 2);
+  }
 }
 
 __device__ __forceinline__ void pb_mma(const PBatch& B, f64x4_t (&acc)[4]) {
@@ -428,21 +420,53 @@ __device__ __forceinline__ void pb_mma(const PBatch& B, f64x4_t (&acc)[4]) {
     const double a = B.e[s >> 1][s & 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, B.r[s][t >> 1][t & 1], acc[t], 0, 0, 0);
   }
+}
+
+// fp64 images of R, made once per call.  Row k of R64: the blocks right of
+// k's diagonal block (the only part the product reads).  D64: each diagonal
+// block as staged for the column loop, its strictly upper part with zeros on
+// and below the diagonal and past n, and in row 127 the reciprocal diagonal.
+// One workgroup per row of the padded block grid.
+__global__ void __launch_bounds__(256) gptq_r64(GptqParams p) {
+  const int64_t k = blockIdx.x;
+  const int i = (int)(k % BLK);
+  const int64_t jb = k - i;
+  const int ncols = (int)min<int64_t>(BLK, p.n - jb);
+  double* drow = p.D64 + (jb / BLK) * SQ + (int64_t)i * BLK;
+  if (i == BLK - 1) {
+    for (int j = threadIdx.x; j < BLK; j += 256)
+      drow[j] = j < ncols ? 1.0 / (double)p.R[(jb + j) * p.ldr + jb + j] : 0.0;
+  } else {
+    for (int j = threadIdx.x; j < BLK; j += 256)
+      drow[j] = (j > i && j < ncols) ? (double)p.R[k * p.ldr + jb + j] : 0.0;
+  }
+  if (k >= p.n) return;
+  const int64_t j0 = jb + BLK;
+  const float* src = p.R + k * p.ldr;
+  double* dst = p.R64 + k * p.ldr64;
+  const int64_t n4 = j0 + max<int64_t>(p.n - j0, 0) / 4 * 4;
+  for (int64_t j = j0 + 4 * threadIdx.x; j < n4; j += 4 * 256) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + j);
+    *reinterpret_cast<f64x2_t*>(dst + j) = f64x2_t{(double)v[0], (double)v[1]};
+    *reinterpret_cast<f64x2_t*>(dst + j + 2) = f64x2_t{(double)v[2], (double)v[3]};
+  }
+  for (int64_t j = n4 + threadIdx.x; j < p.n; j += 256) dst[j] = (double)src[j];
 }
 
 __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, int tid) {
   double* P0 = gl + SQ;
   double* P1 = P0 + RT * BLK;
-  const int pw = (tid >> 6) - CT / 64, lane = tid & 63;
+  // wave-uniform: the K and column offsets below are scalar arithmetic
+  const int pw = __builtin_amdgcn_readfirstlane(tid >> 6) - CT / 64, lane = tid & 63;
   const int kh = pw >> 1, ch = pw & 1;
   const int r = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * RT;
   // rows past m read row m - 1 (results discarded); columns past n in the
-  // last block read the next row of R or its padding (rows k < jn <= n - 2
-  // when the next block is not empty, so the reads stay inside R; results
-  // discarded)
+  // last block read the start of the next row of the fp64 copy (rows k < jn
+  // <= n - 1 when the next block is not empty, so the reads stay inside it;
+  // the values are not written there and the results are discarded)
   const int64_t arow = min<int64_t>(row0 + r, p.m - 1);
   const double* Eg = p.E + arow * p.ldE + 8 * g;
   const int nblocks = (int)((p.n + BLK - 1) / BLK);
@@ -492,7 +516,7 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
   for (int b = 0; b < nblocks; ++b) {
     const int64_t jb = (int64_t)b * BLK, jn = jb + BLK;
     const bool more = b + 1 < nblocks;
-    const float* Rg = p.R + (int64_t)(8 * g) * p.ldr + jn + 64 * ch + 4 * r;
+    const double* Rg = p.R64 + (int64_t)(8 * g) * p.ldr64 + jn + 64 * ch + 4 * r;
     f64x4_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
@@ -506,13 +530,13 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
       // is consumed; the scheduling barriers keep the compiler from sinking
       // the loads next to their use
       PBatch A, B;
-      pb_load(A, Eg, Rg, p.ldr, k0);
+      pb_load(A, Eg, Rg, p.ldr64, k0);
       for (int i = 0; i < nbat; i += 2) {
-        pb_load(B, Eg, Rg, p.ldr, k0 + (int64_t)KB * (i + 1));
+        pb_load(B, Eg, Rg, p.ldr64, k0 + (int64_t)KB * (i + 1));
         __builtin_amdgcn_sched_barrier(0);
         pb_mma(A, acc);
         __builtin_amdgcn_sched_barrier(0);
-        pb_load(A, Eg, Rg, p.ldr, k0 + (int64_t)KB * min(i + 2, nbat - 1));
+        pb_load(A, Eg, Rg, p.ldr64, k0 + (int64_t)KB * min(i + 2, nbat - 1));
         __builtin_amdgcn_sched_barrier(0);
         pb_mma(B, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -522,8 +546,8 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
     if (more) {
       // block b's errors: this half of [jb, jb + 128)
       PBatch A, B;
-      pb_load(A, Eg, Rg, p.ldr, jb + BLK / 2 * kh);
-      pb_load(B, Eg, Rg, p.ldr, jb + BLK / 2 * kh + KB);
+      pb_load(A, Eg, Rg, p.ldr64, jb + BLK / 2 * kh);
+      pb_load(B, Eg, Rg, p.ldr64, jb + BLK / 2 * kh + KB);
       pb_mma(A, acc);
       pb_mma(B, acc);
       store(jn, acc, w);
@@ -551,7 +575,9 @@ bool aligned(const void* q, size_t a) { return (reinterpret_cast<uintptr_t>(q) %
 
 size_t gptq_ws_bytes(int64_t m, int64_t n) {
   return align_up((size_t)m * lde(n) * sizeof(double), 256) +
-         align_up((size_t)m * 2 * sizeof(double), 256);
+         align_up((size_t)m * 2 * sizeof(double), 256) +
+         align_up((size_t)n * lde(n) * sizeof(double), 256) +
+         (size_t)((n + BLK - 1) / BLK) * SQ * sizeof(double);
 }
 
 kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
@@ -583,12 +609,17 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
   double* pc = reinterpret_cast<double*>(static_cast<char*>(ws) +
                                          align_up((size_t)m * p.ldE * sizeof(double), 256));
   p.pc = pc;
+  p.ldr64 = lde(n);
+  p.R64 = reinterpret_cast<double*>(reinterpret_cast<char*>(pc) + align_up((size_t)m * 2 * sizeof(double), 256));
   p.vec_out = perm == nullptr && n % 8 == 0 && aligned(codes, 8) && (What == nullptr || aligned(What, 16)) &&
               (pre_round == nullptr || aligned(pre_round, 16));
   if (group == 0) {
     hipLaunchKernelGGL(gptq_row_params, dim3((unsigned)m), dim3(256), 0, s, p, pc);
     KQ_LAUNCHED("gptq_row_params");
   }
+  p.D64 = p.R64 + align_up((size_t)n * lde(n) * sizeof(double), 256) / sizeof(double);
+  hipLaunchKernelGGL(gptq_r64, dim3((unsigned)((n + BLK - 1) / BLK * BLK)), dim3(256), 0, s, p);
+  KQ_LAUNCHED("gptq_r64");
   const size_t lds = kGptqLds;
   KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)lds));
