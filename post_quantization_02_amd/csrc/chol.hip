@@ -25,16 +25,17 @@
 // and finally R = J Y J.  Tile products run on the fp32 matrix cores
 // (v_mfma_f32_32x32x2f32).
 //
-// Look-ahead over two streams: the caller's stream carries the critical path
-// diag(p) -> PL(p) -> U1(p) -> diag(p + 1), and a second stream carries PY(p)
-// and U2(p), which overlap the next diagonal block.  Linv, Lp and Yp are
-// double-buffered by the parity of p.  Ordering: PY(p) waits for diag(p),
-// U2(p) for U1(p) (hence PL(p); the small critical-path update then does not
-// queue behind the large one), and U1(p) for U2(p - 1) (both write column
-// p + 1); the next use of a buffer of parity p % 2 (diag, PL at p + 2) comes
-// after U1(p + 1), hence after U2(p).  A device flag set by a failed pivot makes every
-// later kernel return at once; the host reads the flag after the last launch.
-#include <mutex>
+// Look-ahead in one stream: U2(p - 1) runs in the same launch as diag(p)
+// (workgroup 0 takes the diagonal block, the others the U2 tiles), then PL(p)
+// and PY(p) share a launch, then U1(p).  The critical path diag(p) -> PL(p) ->
+// U1(p) -> diag(p + 1) so never waits on the large update, and no event
+// crosses streams.  U2(p - 1) writes columns past p and row blocks of B past
+// p - 1, so it is independent of diag(p); U1(p) writes column p + 1 after
+// U2(p - 1), which also writes it, has finished.  Linv, Lp and Yp are
+// double-buffered by the parity of p (diag(p) writes Linv of parity p while
+// U2(p - 1) reads Lp and Yp of the other).  A device flag set by a failed
+// pivot makes every later kernel return at once; the host reads the flag
+// after the last launch.
 
 #include "kronq_internal.h"
 
@@ -45,7 +46,6 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int NB = 128;
 constexpr int KS = 32;        // K rows per LDS stage
-constexpr int LDT = NB + 1;   // odd LDS stride: conflict-free transposed stores
 
 struct CholWs {
   float* A;       // npad x npad (reversed, permuted, damped)
@@ -335,12 +335,44 @@ __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
   return bad;
 }
 
-__global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p, CholWs w) {
-  if (*w.flag) return;
-  __shared__ double Ls[NSB * (NSB + 1) / 2 * BLKD];  // S, then L (below) / M (diagonal) / X
-  __shared__ double Bs[NSB * (NSB - 1) / 2 * BLKD];  // Bacc_ic, i > c
-  __shared__ __align__(16) double col2[2 * SB];
-  __shared__ int s_bad;
+// Step kb's trailing update except the diagonal block kb + 1: S_ij -= L_ik
+// L_jk^T (kb < j <= i, (i, j) != (kb + 1, kb + 1)) and Bacc_ic -= L_ik X_kb,c
+// (i > kb, c <= kb; X_kb,kb = M_kk), as 16 x 16 tiles dealt round-robin to
+// `nw` waves (this one is number `w0`).
+__device__ __forceinline__ void p2_rest(int kb, int w0, int nw, double* Ls, double* Bs) {
+  const double* Mk = Ls + lslot(kb, kb) * BLKD;
+  const int q = NSB - 1 - kb;
+  const int nS = q * (q + 1) / 2, nB = q * (kb + 1);
+  for (int job = w0; job < 4 * (nS + nB); job += nw) {
+    const int prod = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+    if (prod < nS) {
+      int a = 0, u = prod;
+      while (u > a) { u -= a + 1; ++a; }
+      const int i = kb + 1 + a, j = kb + 1 + u;   // S_ij -= L_ik L_jk^T
+      if (i == kb + 1 && j == kb + 1) continue;   // done before B1 of step kb + 1
+      double* Sij = Ls + lslot(i, j) * BLKD;
+      f64x4_t acc = tile_load(Sij, ti, tj);
+      acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Ls + lslot(j, kb) * BLKD, 1, LDB, -1.0,
+                     ti, tj);
+      tile_store(acc, Sij, ti, tj);
+    } else {
+      const int pb = prod - nS;
+      const int i = kb + 1 + pb / (kb + 1), c = pb % (kb + 1);   // Bacc_ic -= L_ik X_kb,c
+      double* Bic = Bs + bslot(i, c) * BLKD;
+      f64x4_t acc = (c == kb) ? f64x4_t{0.0, 0.0, 0.0, 0.0} : tile_load(Bic, ti, tj);
+      const double* X = (c == kb) ? Mk : Ls + lslot(kb, c) * BLKD;
+      acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, X, LDB, 1, -1.0, ti, tj);
+      tile_store(acc, Bic, ti, tj);
+    }
+  }
+}
+
+// LDS of the diagonal step
+constexpr int kLsD = NSB * (NSB + 1) / 2 * BLKD;   // S, then L (below) / M (diagonal) / X
+constexpr int kBsD = NSB * (NSB - 1) / 2 * BLKD;   // Bacc_ic, i > c
+
+__device__ __forceinline__ void diag_step(int64_t npad, int64_t n, int p, const CholWs& w, double* Ls,
+                                          double* Bs, double* col2, int& s_bad) {
   const int tid = threadIdx.x, wave = tid >> 6;
 
   // ---- load the lower sub-blocks of A_pp (fp32 -> fp64)
@@ -364,10 +396,13 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
   __syncthreads();
 
   for (int kb = 0; kb < NSB; ++kb) {
-    // ---- B1
+    // ---- B1 on wave 0; meanwhile waves 1..3 finish the trailing update of
+    // step kb - 1 (all but the diagonal block kb, which B1 reads)
     if (wave == 0) {
       const int bad = diag_factor32(Ls + lslot(kb, kb) * BLKD, col2);
       if (tid == 0 && bad >= 0) s_bad = SB * kb + bad;
+    } else if (kb > 0) {
+      p2_rest(kb - 1, wave - 1, 3, Ls, Bs);
     }
     __syncthreads();
     if (s_bad >= 0) break;
@@ -399,33 +434,16 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
       }
     }
     __syncthreads();
-    // ---- P2: trailing update of S and of the accumulators, in place
-    {
-      const int q = NSB - 1 - kb;
-      const int nS = q * (q + 1) / 2, nB = q * (kb + 1);
-      for (int job = wave; job < 4 * (nS + nB); job += 4) {
-        const int prod = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
-        if (prod < nS) {
-          int a = 0, u = prod;
-          while (u > a) { u -= a + 1; ++a; }
-          const int i = kb + 1 + a, j = kb + 1 + u;   // S_ij -= L_ik L_jk^T
-          double* Sij = Ls + lslot(i, j) * BLKD;
-          f64x4_t acc = tile_load(Sij, ti, tj);
-          acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Ls + lslot(j, kb) * BLKD, 1, LDB, -1.0,
-                         ti, tj);
-          tile_store(acc, Sij, ti, tj);
-        } else {
-          const int pb = prod - nS;
-          const int i = kb + 1 + pb / (kb + 1), c = pb % (kb + 1);   // Bacc_ic -= L_ik X_kb,c
-          double* Bic = Bs + bslot(i, c) * BLKD;
-          f64x4_t acc = (c == kb) ? f64x4_t{0.0, 0.0, 0.0, 0.0} : tile_load(Bic, ti, tj);
-          const double* X = (c == kb) ? Mk : Ls + lslot(kb, c) * BLKD;
-          acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, X, LDB, 1, -1.0, ti, tj);
-          tile_store(acc, Bic, ti, tj);
-        }
-      }
+    // ---- the next diagonal block's share of the trailing update, S_k+1,k+1
+    // -= L_k+1,k L_k+1,k^T (one tile per wave), so that B1 can start on it
+    if (kb + 1 < NSB) {
+      const int ti = wave >> 1, tj = wave & 1, i = kb + 1;
+      double* Sii = Ls + lslot(i, i) * BLKD;
+      f64x4_t acc = tile_load(Sii, ti, tj);
+      acc = tile_mma(acc, Ls + lslot(i, kb) * BLKD, LDB, 1, Ls + lslot(i, kb) * BLKD, 1, LDB, -1.0, ti, tj);
+      tile_store(acc, Sii, ti, tj);
+      __syncthreads();
     }
-    __syncthreads();
   }
   if (s_bad >= 0) {
     if (tid == 0) {
@@ -458,8 +476,9 @@ __global__ void __launch_bounds__(256) chol_diag(int64_t npad, int64_t n, int p,
 enum { XK = 0, KX = 1 };
 
 // A stage is KS values of k for X consecutive x, held in LDS as sT[k][x]
-// (stride LDT).  gload fetches a thread's share of it (16-byte loads) into
-// registers; lstore writes those registers to LDS.
+// (stride ST = X + 1, odd: conflict-free transposed stores).  gload fetches a
+// thread's share of it (16-byte loads) into registers; lstore writes those
+// registers to LDS.
 template <int X>
 constexpr int stage_vecs() { return (X * KS / 4) / 256; }
 
@@ -479,7 +498,7 @@ __device__ inline void gload(float4 (&r)[stage_vecs<X>()], const float* G, int64
   }
 }
 
-template <int LAY, int X>
+template <int LAY, int X, int ST = X + 1>
 __device__ inline void lstore(float* sT, const float4 (&r)[stage_vecs<X>()]) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -487,22 +506,24 @@ __device__ inline void lstore(float* sT, const float4 (&r)[stage_vecs<X>()]) {
     const int idx = tid + 256 * q;
     if (LAY == XK) {
       const int x = idx >> 3, k4 = (idx & 7) * 4;
-      sT[(k4 + 0) * LDT + x] = r[q].x;
-      sT[(k4 + 1) * LDT + x] = r[q].y;
-      sT[(k4 + 2) * LDT + x] = r[q].z;
-      sT[(k4 + 3) * LDT + x] = r[q].w;
+      sT[(k4 + 0) * ST + x] = r[q].x;
+      sT[(k4 + 1) * ST + x] = r[q].y;
+      sT[(k4 + 2) * ST + x] = r[q].z;
+      sT[(k4 + 3) * ST + x] = r[q].w;
     } else {
       const int k = idx / (X / 4), x4 = (idx % (X / 4)) * 4;
-      sT[k * LDT + x4 + 0] = r[q].x;
-      sT[k * LDT + x4 + 1] = r[q].y;
-      sT[k * LDT + x4 + 2] = r[q].z;
-      sT[k * LDT + x4 + 3] = r[q].w;
+      sT[k * ST + x4 + 0] = r[q].x;
+      sT[k * ST + x4 + 1] = r[q].y;
+      sT[k * ST + x4 + 2] = r[q].z;
+      sT[k * ST + x4 + 3] = r[q].w;
     }
   }
 }
 
-// LDS of a tile product: two buffers each of the A and B stages
-constexpr size_t kTileLds = 4 * (size_t)KS * LDT * sizeof(float);
+// LDS of a tile product with MR x MC output: all of K for both operands
+constexpr size_t tile_lds(int MR, int MC) { return (size_t)NB * (MR + 1 + MC + 1) * sizeof(float); }
+constexpr size_t kTileLdsFull = tile_lds(128, 128);   // U2 tiles
+constexpr size_t kTileLdsQuarter = tile_lds(128, 32);  // PL, PY, U1 quarter tiles
 
 // Workgroup tile product: out(x=i, y=j) = sum_k A(i, k) B(j, k) for an
 // MR x MC output (MR = WR * TR * 32 rows, MC = WC * TC * 32 columns; four
@@ -521,59 +542,70 @@ struct TileMma {
         for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
   }
 
-  // K in NB / KS stages, double-buffered: stage s + 1 is fetched into
-  // registers while stage s is multiplied, then written to the other LDS
-  // buffer (whose last readers passed the barrier that ended stage s - 1).
+  // All of K at once: every thread issues its loads of all NB / KS stages
+  // before the first is written to LDS, so the global latency is paid once;
+  // one barrier, then the MFMAs run with no further waits on memory.
   template <int LA, int LB>
   __device__ void run(const float* Ag, int64_t lda, const float* Bg, int64_t ldb, float* sm) {
+    constexpr int NS = NB / KS, SA = MR + 1, SBT = MC + 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WC, wn = wave % WC;
     const int lr = lane & 31, lk = lane >> 5;
-    float* sA[2] = {sm, sm + KS * LDT};
-    float* sB[2] = {sm + 2 * KS * LDT, sm + 3 * KS * LDT};
-    float4 ra[stage_vecs<MR>()], rb[stage_vecs<MC>()];
-    gload<LA, MR>(ra, Ag, lda, 0);
-    gload<LB, MC>(rb, Bg, ldb, 0);
-    lstore<LA, MR>(sA[0], ra);
-    lstore<LB, MC>(sB[0], rb);
+    float* sA = sm;              // NB x SA: sA[k][x]
+    float* sB = sm + NB * SA;    // NB x SBT
+    {
+      float4 ra[NS][stage_vecs<MR>()], rb[NS][stage_vecs<MC>()];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        gload<LA, MR>(ra[st], Ag, lda, st * KS);
+        gload<LB, MC>(rb[st], Bg, ldb, st * KS);
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        lstore<LA, MR, SA>(sA + st * KS * SA, ra[st]);
+        lstore<LB, MC, SBT>(sB + st * KS * SBT, rb[st]);
+      }
+    }
     __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < NB; kk += 2) {
+      float af[TR], bf[TC];
 #pragma unroll
-    for (int st = 0; st < NB / KS; ++st) {
-      const int cur = st & 1;
-      if (st + 1 < NB / KS) {
-        gload<LA, MR>(ra, Ag, lda, (st + 1) * KS);
-        gload<LB, MC>(rb, Bg, ldb, (st + 1) * KS);
-      }
-      const float* cA = sA[cur];
-      const float* cB = sB[cur];
+      for (int a = 0; a < TR; ++a) af[a] = sA[(kk + lk) * SA + (wm * TR + a) * 32 + lr];
 #pragma unroll
-      for (int kk = 0; kk < KS; kk += 2) {
-        float af[TR], bf[TC];
+      for (int b = 0; b < TC; ++b) bf[b] = sB[(kk + lk) * SBT + (wn * TC + b) * 32 + lr];
 #pragma unroll
-        for (int a = 0; a < TR; ++a) af[a] = cA[(kk + lk) * LDT + (wm * TR + a) * 32 + lr];
+      for (int a = 0; a < TR; ++a)
 #pragma unroll
-        for (int b = 0; b < TC; ++b) bf[b] = cB[(kk + lk) * LDT + (wn * TC + b) * 32 + lr];
-#pragma unroll
-        for (int a = 0; a < TR; ++a)
-#pragma unroll
-          for (int b = 0; b < TC; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
-      }
-      if (st + 1 < NB / KS) {
-        lstore<LA, MR>(sA[cur ^ 1], ra);
-        lstore<LB, MC>(sB[cur ^ 1], rb);
-      }
-      __syncthreads();
+        for (int b = 0; b < TC; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
   }
 
   // MODE 0: C = acc; MODE 1: C -= acc.  32x32 accumulator layout: lane holds
   // column lane % 32; register v holds row 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+  // In MODE 1 every old value is loaded before the first store (written as
+  // one load per element followed by its store, the compiler would keep them
+  // in order, one memory round trip per element, as it cannot rule out that
+  // two elements alias).
   template <int MODE>
   __device__ void store(float* C, int64_t ldc) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WC, wn = wave % WC;
     const int lr = lane & 31, lk = lane >> 5;
+    float old[TR][TC][16];
+    if (MODE == 1) {
+#pragma unroll
+      for (int a = 0; a < TR; ++a)
+#pragma unroll
+        for (int b = 0; b < TC; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = (wm * TR + a) * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+            const int c = (wn * TC + b) * 32 + lr;
+            old[a][b][v] = C[(int64_t)r * ldc + c];
+          }
+    }
 #pragma unroll
     for (int a = 0; a < TR; ++a)
 #pragma unroll
@@ -582,23 +614,25 @@ struct TileMma {
         for (int v = 0; v < 16; ++v) {
           const int r = (wm * TR + a) * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
           const int c = (wn * TC + b) * 32 + lr;
-          float* dst = C + (int64_t)r * ldc + c;
-          if (MODE == 0) *dst = acc[a][b][v];
-          else *dst -= acc[a][b][v];
+          C[(int64_t)r * ldc + c] = MODE == 0 ? acc[a][b][v] : old[a][b][v] - acc[a][b][v];
         }
   }
 };
 
-// Quarter tiles (128 x 32): PL (mode 0) Lp_i = A_ip Linv^T for i > p; PY
-// (mode 1) Yp_c = Linv B_pc for c <= p.  Buffers of parity p % 2.
-__global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, int mode, CholWs w) {
+// Step p's panels, as quarter tiles (128 x 32): PL, Lp_i = A_ip Linv^T for i
+// > p (the first 4 (P - p - 1) workgroups), and PY, Yp_c = Linv B_pc for c <=
+// p (the next 4 (p + 1)).  Buffers of parity p % 2.
+__global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
-  const int t = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int npl = 4 * (P - p - 1);
+  const bool pl = (int)blockIdx.x < npl;
+  const int u = pl ? blockIdx.x : blockIdx.x - npl;
+  const int t = u >> 2, quarter = u & 3;
   const float* Linv = linv_buf(w, p & 1);
   TileMma<4, 1, 1, 1> mm;
   mm.zero();
-  if (mode == 0) {
+  if (pl) {
     const int i = p + 1 + t;
     const float* Aip = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
     // B(j, k) = Linv[32 quarter + j][k]
@@ -613,30 +647,19 @@ __global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, in
   }
 }
 
-// U1 (mode 0): the SYRK tiles of column p + 1, A_i,p+1 for i > p, as quarter
-// tiles.
-// U2 (mode 1): the other SYRK tiles (i >= j > p + 1), then the forward-
-// substitution tiles (i > p, c <= p), then the copy of Y_p into row block p
-// of B.
-__global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, int mode, CholWs w) {
-  if (*w.flag) return;
-  extern __shared__ __align__(16) float sm[];
+// Number of U2 tiles of step p (see u2_tile).
+__host__ __device__ inline int u2_tiles(int P, int p) {
+  const int q = P - p - 1, q2 = q - 1;
+  return (q2 > 0 ? q2 * (q2 + 1) / 2 : 0) + q * (p + 1) + (p + 1);
+}
+
+// U2 of step p, tile t: the SYRK tiles A_ij -= Lp_i Lp_j^T (i >= j > p + 1),
+// then the forward-substitution tiles B_ic -= Lp_i Yp_c (i > p, c <= p), then
+// the copy of Y_p into row block p of B.  `sm` holds kTileLdsFull bytes.
+__device__ __forceinline__ void u2_tile(int64_t npad, int P, int p, int t, const CholWs& w, float* sm) {
   const float* Lp = lp_buf(w, p & 1);
   const float* Yp = yp_buf(w, p & 1);
   const int q = P - p - 1;
-  int t = blockIdx.x;
-  if (mode == 0) {
-    // quarter tiles (128 x 32): four times the workgroups, a quarter of the
-    // latency, for the kernel on the critical path
-    TileMma<4, 1, 1, 1> mm;
-    mm.zero();
-    const int quarter = t & 3;
-    const int i = p + 1 + (t >> 2), j = p + 1;
-    mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB + 32 * quarter * NB, NB,
-                   sm);
-    mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB + 32 * quarter, npad);
-    return;
-  }
   const int q2 = q - 1;   // trailing columns after p + 1
   const int nsyrk = q2 > 0 ? q2 * (q2 + 1) / 2 : 0;
   const int nfwd = q * (p + 1);
@@ -667,6 +690,38 @@ __global__ void __launch_bounds__(256) chol_update(int64_t npad, int P, int p, i
   }
 }
 
+// Step p of the sweep, one launch: workgroup 0 factors and inverts diagonal
+// block p (if p < P); the others run U2 of step p - 1, which writes only
+// columns past p and row blocks past p - 1 of B, so it overlaps the diagonal
+// block.  The U2 tiles reuse the diagonal step's LDS for their stages.
+__global__ void __launch_bounds__(256) chol_step(int64_t npad, int64_t n, int P, int p, CholWs w) {
+  if (*w.flag) return;
+  __shared__ __align__(16) double lds[kLsD + kBsD + 2 * SB];
+  __shared__ int s_bad;
+  static_assert(sizeof(lds) >= kTileLdsFull, "a U2 tile fits the diagonal step's LDS");
+  if (blockIdx.x > 0) {
+    u2_tile(npad, P, p - 1, (int)blockIdx.x - 1, w, reinterpret_cast<float*>(lds));
+    return;
+  }
+  if (p < P) diag_step(npad, n, p, w, lds, lds + kLsD, lds + kLsD + kBsD, s_bad);
+}
+
+// U1 of step p: the SYRK tiles of column p + 1, A_i,p+1 -= Lp_i Lp_p+1^T for
+// i > p, as 128 x 32 quarter tiles (four times the workgroups, a quarter of
+// the latency, for the kernel on the critical path).
+__global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
+  if (*w.flag) return;
+  extern __shared__ __align__(16) float sm[];
+  const float* Lp = lp_buf(w, p & 1);
+  const int t = blockIdx.x;
+  TileMma<4, 1, 1, 1> mm;
+  mm.zero();
+  const int quarter = t & 3;
+  const int i = p + 1 + (t >> 2), j = p + 1;
+  mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB + 32 * quarter * NB, NB, sm);
+  mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB + 32 * quarter, npad);
+}
+
 // R[a][b] = Y[n-1-a][n-1-b] for b >= a, 0 below the diagonal.
 __global__ void __launch_bounds__(256) chol_flip(int64_t n, int64_t npad, float* R, int64_t ldr,
                                                  CholWs w) {
@@ -679,48 +734,6 @@ __global__ void __launch_bounds__(256) chol_flip(int64_t n, int64_t npad, float*
 }  // namespace
 
 size_t chol_ws_bytes(int64_t n) { return ws_layout(n, nullptr, nullptr); }
-
-namespace {
-
-// Second stream of the look-ahead and its events, one set per device, created
-// on first use and kept until the process ends.  The mutex serializes the
-// enqueueing of concurrent calls on one device (the work itself still runs
-// asynchronously on the caller's stream and this one).
-struct SideStream {
-  std::mutex mu;
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, diag_done = nullptr, u1_done = nullptr, u2_done[2] = {nullptr, nullptr};
-};
-
-#define KQ_CHECKED(call)                   \
-  do {                                     \
-    kronq_status _s = (call);              \
-    if (_s != KRONQ_OK) return _s;         \
-  } while (0)
-
-kronq_status side_stream(SideStream** out) {
-  constexpr int kMaxDev = 64;
-  static SideStream sets[kMaxDev];
-  static std::mutex init_mu;
-  int dev = 0;
-  KQ_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDev) return fail(KRONQ_EHIP, "kronq_chol_inv: device %d out of range", dev);
-  SideStream& ss = sets[dev];
-  std::lock_guard<std::mutex> g(init_mu);
-  if (!ss.stream) {
-    const unsigned ef = hipEventDisableTiming;
-    KQ_HIP(hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking));
-    KQ_HIP(hipEventCreateWithFlags(&ss.fork, ef));
-    KQ_HIP(hipEventCreateWithFlags(&ss.diag_done, ef));
-    KQ_HIP(hipEventCreateWithFlags(&ss.u1_done, ef));
-    KQ_HIP(hipEventCreateWithFlags(&ss.u2_done[0], ef));
-    KQ_HIP(hipEventCreateWithFlags(&ss.u2_done[1], ef));
-  }
-  *out = &ss;
-  return KRONQ_OK;
-}
-
-}  // namespace
 
 kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, int act_order,
                          int32_t* perm, float* R, int64_t ldr, int64_t* info, void* ws,
@@ -745,43 +758,21 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
                        (const int32_t*)perm, npad, w);
     KQ_LAUNCHED("chol_gather");
   }
-  const size_t lds_tile = kTileLds;
-  SideStream* ss = nullptr;
-  KQ_CHECKED(side_stream(&ss));
-  {
-    std::lock_guard<std::mutex> guard(ss->mu);
-    hipStream_t s2 = ss->stream;
-    // the second stream starts after the gather
-    KQ_HIP(hipEventRecord(ss->fork, s));
-    KQ_HIP(hipStreamWaitEvent(s2, ss->fork, 0));
-    for (int p = 0; p < P; ++p) {
-      const int q = P - p - 1;
-      hipLaunchKernelGGL(chol_diag, dim3(1), dim3(256), 0, s, npad, n, p, w);
-      KQ_LAUNCHED("chol_diag");
-      KQ_HIP(hipEventRecord(ss->diag_done, s));
-      if (q > 0) {
-        hipLaunchKernelGGL(chol_panel, dim3(4 * q), dim3(256), lds_tile, s, npad, P, p, 0, w);
-        KQ_LAUNCHED("chol_panel");
-        // critical path: U1(p) after U2(p - 1) (both write column p + 1)
-        if (p > 0) KQ_HIP(hipStreamWaitEvent(s, ss->u2_done[(p - 1) & 1], 0));
-        hipLaunchKernelGGL(chol_update, dim3(4 * q), dim3(256), lds_tile, s, npad, P, p, 0, w);
-        KQ_LAUNCHED("chol_update");
-      }
-      KQ_HIP(hipEventRecord(ss->u1_done, s));
-      // second stream: PY(p), then U2(p) once U1(p) is done, so that the
-      // small critical-path update does not queue behind the large one
-      KQ_HIP(hipStreamWaitEvent(s2, ss->diag_done, 0));
-      hipLaunchKernelGGL(chol_panel, dim3(4 * (p + 1)), dim3(256), lds_tile, s2, npad, P, p, 1, w);
-      KQ_LAUNCHED("chol_panel");
-      KQ_HIP(hipStreamWaitEvent(s2, ss->u1_done, 0));
-      const int q2 = q - 1;
-      const int u2 = (q2 > 0 ? q2 * (q2 + 1) / 2 : 0) + q * (p + 1) + (p + 1);
-      hipLaunchKernelGGL(chol_update, dim3(u2), dim3(256), lds_tile, s2, npad, P, p, 1, w);
-      KQ_LAUNCHED("chol_update");
-      KQ_HIP(hipEventRecord(ss->u2_done[p & 1], s2));
+  // one stream: step p (diagonal block p with U2 of step p - 1), the panels
+  // of step p, U1 of step p; a last step launch runs U2 of step P - 1
+  const size_t lds_tile = kTileLdsQuarter;
+  for (int p = 0; p <= P; ++p) {
+    const int nu2 = p > 0 ? u2_tiles(P, p - 1) : 0;
+    hipLaunchKernelGGL(chol_step, dim3((unsigned)(1 + nu2)), dim3(256), 0, s, npad, n, P, p, w);
+    KQ_LAUNCHED("chol_step");
+    if (p == P) break;
+    const int q = P - p - 1;
+    hipLaunchKernelGGL(chol_panel, dim3((unsigned)(4 * q + 4 * (p + 1))), dim3(256), lds_tile, s, npad, P, p, w);
+    KQ_LAUNCHED("chol_panel");
+    if (q > 0) {
+      hipLaunchKernelGGL(chol_u1, dim3((unsigned)(4 * q)), dim3(256), lds_tile, s, npad, p, w);
+      KQ_LAUNCHED("chol_u1");
     }
-    // join: the flip reads all of B
-    KQ_HIP(hipStreamWaitEvent(s, ss->u2_done[(P - 1) & 1], 0));
   }
   {
     const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 64);
