@@ -132,11 +132,8 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
  *         order) whose trailing block Hd[k:, k:] is not positive definite
  *         (the factorization runs on the reversed matrix, so this is where its
  *         first non-positive pivot falls).
- * Synchronizes `stream` before returning.  Part of the work runs on a second
- * stream that the library creates on first use for each device (default
- * priority, kept until the process ends), ordered against `stream` with
- * events; `stream` must belong to the current device.  Concurrent calls on one
- * device serialize their enqueueing.
+ * All work runs on `stream`, which is synchronized before returning (the
+ * flag of a failed pivot is read back).
  * ws    : kronq_chol_inv_ws(n) bytes.
  * ------------------------------------------------------------------------- */
 size_t kronq_chol_inv_ws(int64_t n);
