@@ -235,7 +235,6 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-
 // B1 on one wave: factor the stored block Sk (lower triangle read) and
 // overwrite it with M = L^-1 (lower triangular, zeros above).  Columns j and
 // j + 1 are eliminated together: with d0 = S_jj, a = S_j+1,j, e = S_j+1,j+1 d0
@@ -248,35 +247,48 @@ __device__ __forceinline__ void wave_sync_lds() {
 // (finite values of the stored block) only ever update other such entries of
 // the same lane, so they never reach the factor.  Returns the first column
 // whose pivot is not positive (or NaN), else -1; past a failed pivot the
-// sweep continues with harmless values and its results are discarded.  (Kept
-// out of line: inlined into the kernel it spills heavily.)
+// sweep continues with harmless values and its results are discarded.
+// The two columns of a step reach every lane through LDS: col2 holds two
+// buffers of 2 x SB doubles, step j's columns in buffer (j / 2) % 2, so that
+// the S lanes can publish the next step's columns while this step's are still
+// being read.  Each lane reads a column entry just before its update, kPre
+// entries ahead, so the routine holds no copy of the columns.  It stays out
+// of line: inlined into the kernel, the register allocation spills.
+constexpr int kPre = 8;
+
 __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
   const int l = threadIdx.x & 63, r = l & 31;
   const bool isS = l < 32;
-  double v[SB], c0[SB], c1[SB];
+  double v[SB];
 #pragma unroll
   for (int k = 0; k < SB; ++k) v[k] = isS ? Sk[r * LDB + k] : (k == r ? 1.0 : 0.0);
   if (isS) *reinterpret_cast<f64x2_t*>(col2 + 2 * r) = f64x2_t{v[0], v[1]};
   wave_sync_lds();
-#pragma unroll
-  for (int k = 0; k < SB; ++k) {
-    const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
-    c0[k] = t[0];
-    c1[k] = t[1];
-  }
+  // this step's pivot entries (S_jj, S_j+1,j; S_j+1,j+1)
+  f64x2_t pv0 = *reinterpret_cast<const f64x2_t*>(col2);
+  f64x2_t pv1 = *reinterpret_cast<const f64x2_t*>(col2 + 2);
   int bad = -1;
 #pragma unroll
   for (int j = 0; j < SB; j += 2) {
-    double d0 = c0[j];
-    const double a = c0[j + 1];
+    const double* cur = col2 + ((j / 2) & 1) * 2 * SB;
+    double* nxt = col2 + (((j / 2) + 1) & 1) * 2 * SB;
+    double d0 = pv0[0];
+    const double a = pv1[0];
     if (!(d0 > 0.0)) {
       if (bad < 0) bad = j;
       d0 = 1.0;
     }
-    double e = fma(c1[j + 1], d0, -a * a);
+    double e = fma(pv1[1], d0, -a * a);
     if (!(e > 0.0)) {
       if (bad < 0) bad = j + 1;
       e = d0;
+    }
+    // the entries of the next two columns' rows, read while the pivots are
+    // worked out
+    f64x2_t cn[2] = {f64x2_t{0.0, 0.0}, f64x2_t{0.0, 0.0}};
+    if (j + 2 < SB) {
+      cn[0] = *reinterpret_cast<const f64x2_t*>(cur + 2 * (j + 2));
+      cn[1] = *reinterpret_cast<const f64x2_t*>(cur + 2 * (j + 3));
     }
     const double y0 = rsqrt_nr(d0), ye = rsqrt_nr(e);
     const double y0s = y0 * y0;
@@ -284,48 +296,31 @@ __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
     const double y1 = ye * (d0 * y0);
     const double beta = fma(-g, v[j], v[j + 1]) * (y1 * y1);
     const double alpha = fma(v[j], y0s, -g * beta);
-    // The next two columns first, so that their broadcast overlaps the rest
-    // of the update.  From column 18 on both column pairs fit in registers
-    // and the read-back is issued before the remaining FMAs; earlier it
-    // follows them.
-    constexpr int kEarlyRead = 18;
-    double n0[SB], n1[SB];
     if (j + 2 < SB) {
-      v[j + 2] = fma(-alpha, c0[j + 2], fma(-beta, c1[j + 2], v[j + 2]));
-      v[j + 3] = fma(-alpha, c0[j + 3], fma(-beta, c1[j + 3], v[j + 3]));
-      if (isS) *reinterpret_cast<f64x2_t*>(col2 + 2 * r) = f64x2_t{v[j + 2], v[j + 3]};
-      if (j >= kEarlyRead) {
-        wave_sync_lds();
-#pragma unroll
-        for (int k = j + 2; k < SB; ++k) {
-          const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
-          n0[k] = t[0];
-          n1[k] = t[1];
-        }
-      }
+      // the next two columns first; publish them and read the next pivots
+      // while the rest of the update runs
+      v[j + 2] = fma(-alpha, cn[0][0], fma(-beta, cn[0][1], v[j + 2]));
+      v[j + 3] = fma(-alpha, cn[1][0], fma(-beta, cn[1][1], v[j + 3]));
+      if (isS) *reinterpret_cast<f64x2_t*>(nxt + 2 * r) = f64x2_t{v[j + 2], v[j + 3]};
+      wave_sync_lds();
+      pv0 = *reinterpret_cast<const f64x2_t*>(nxt + 2 * (j + 2));
+      pv1 = *reinterpret_cast<const f64x2_t*>(nxt + 2 * (j + 3));
     }
+    // the rest of the update, each column entry read kPre entries ahead
+    f64x2_t cb[kPre];
 #pragma unroll
-    for (int k = j + 4; k < SB; ++k) v[k] = fma(-alpha, c0[k], fma(-beta, c1[k], v[k]));
+    for (int k = j + 4; k < SB && k < j + 4 + kPre; ++k)
+      cb[(k - j - 4) % kPre] = *reinterpret_cast<const f64x2_t*>(cur + 2 * k);
+#pragma unroll
+    for (int k = j + 4; k < SB; ++k) {
+      const f64x2_t t = cb[(k - j - 4) % kPre];
+      if (k + kPre < SB) cb[(k - j - 4) % kPre] = *reinterpret_cast<const f64x2_t*>(cur + 2 * (k + kPre));
+      v[k] = fma(-alpha, t[0], fma(-beta, t[1], v[k]));
+    }
     if (!isS) {
       const double xj = v[j] * y0;
       v[j + 1] = fma(-g, v[j], v[j + 1]) * y1;
       v[j] = xj;
-    }
-    if (j + 2 < SB) {
-      if (j < kEarlyRead) {
-        wave_sync_lds();
-#pragma unroll
-        for (int k = j + 2; k < SB; ++k) {
-          const f64x2_t t = *reinterpret_cast<const f64x2_t*>(col2 + 2 * k);
-          n0[k] = t[0];
-          n1[k] = t[1];
-        }
-      }
-#pragma unroll
-      for (int k = j + 2; k < SB; ++k) {
-        c0[k] = n0[k];
-        c1[k] = n1[k];
-      }
     }
   }
   if (!isS) {
@@ -696,7 +691,7 @@ __device__ __forceinline__ void u2_tile(int64_t npad, int P, int p, int t, const
 // block.  The U2 tiles reuse the diagonal step's LDS for their stages.
 __global__ void __launch_bounds__(256) chol_step(int64_t npad, int64_t n, int P, int p, CholWs w) {
   if (*w.flag) return;
-  __shared__ __align__(16) double lds[kLsD + kBsD + 2 * SB];
+  __shared__ __align__(16) double lds[kLsD + kBsD + 4 * SB];
   __shared__ int s_bad;
   static_assert(sizeof(lds) >= kTileLdsFull, "a U2 tile fits the diagonal step's LDS");
   if (blockIdx.x > 0) {
