@@ -64,6 +64,7 @@ struct GramParams {
   int nitems;        // ntiles * S
   int per_xcd;       // ceil(nitems / 8)
   int64_t nstages;   // ceil(N / stage)
+  bool vec_h;        // H 16-byte aligned and ldh a multiple of 4
 };
 
 // Upper-triangle tile number t -> (ti, tj), tj >= ti, in 4 x 4 super-tile order.
@@ -698,27 +699,70 @@ __global__ void __launch_bounds__(256, 2) gram_f32_kernel(GramParams p) {
   }
 }
 
-// Sum the S partial tiles, apply scale/beta, write both triangles.
-// Grid: (tile * 64) blocks of 256 threads; each thread handles 4 columns of
-// one row of the tile; TS = tile edge.
+// Sum the S partial tiles, apply scale/beta, write both triangles.  A
+// workgroup takes a 64 x 64 sub-block of a tile as 1024 four-float vectors:
+// vector f = threadIdx + 256 q is row f / 16, columns 4 (f % 16) .. + 3, so a
+// wave covers four 256-byte row segments.  The splits are summed in order;
+// for an off-diagonal tile the transposed copy goes through LDS, so that the
+// mirrored writes are row segments too.
+__device__ __forceinline__ void put4(const GramParams& p, int64_t i, int64_t j, f32x4_t v) {
+  if (p.vec_h && i < p.d && j + 4 <= p.d) {
+    f32x4_t* h = reinterpret_cast<f32x4_t*>(p.H + i * p.ldh + j);
+    f32x4_t x;
+    if (p.beta != 0.0f) {
+      const f32x4_t o = *h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fmaf(p.scale, v[e], p.beta * o[e]);
+    } else {
+      x = v * p.scale;
+    }
+    *h = x;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) put(p, i, j + e, v[e], false);
+  }
+}
+
 template <int TS>
 __global__ void __launch_bounds__(256) gram_finalize_kernel(GramParams p) {
-  constexpr int ROWS_PER_BLOCK = 256 * 4 / TS;
-  const int t = blockIdx.x / (TS / ROWS_PER_BLOCK);
-  const int rblk = blockIdx.x % (TS / ROWS_PER_BLOCK);
+  constexpr int SUB = 64, NSUB = TS / SUB;
+  __shared__ float tr[SUB][SUB + 1];
+  const int t = blockIdx.x / (NSUB * NSUB), sb = blockIdx.x % (NSUB * NSUB);
+  const int sr = sb / NSUB, sc = sb % NSUB;
   int ti, tj;
   tile_coords(t, p.T, ti, tj);
   const bool diag = (ti == tj);
-  const int r = rblk * ROWS_PER_BLOCK + threadIdx.x / (TS / 4);
-  const int c = 4 * (threadIdx.x % (TS / 4));
-  f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.S; ++s) {
-    const float* src = p.part + ((int64_t)(s * p.ntiles + t) * TS + r) * TS + c;
-    sum += *reinterpret_cast<const f32x4_t*>(src);
-  }
-  const int64_t i = (int64_t)ti * TS + r;
+  f32x4_t sum[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) put(p, i, (int64_t)tj * TS + c + q, sum[q], !diag);
+  for (int q = 0; q < 4; ++q) sum[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < p.S; ++k) {
+    const float* src = p.part + ((int64_t)(k * p.ntiles + t) * TS + sr * SUB) * TS + sc * SUB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = threadIdx.x + 256 * q, rr = f >> 4, c4 = (f & 15) * 4;
+      sum[q] += *reinterpret_cast<const f32x4_t*>(src + (int64_t)rr * TS + c4);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = threadIdx.x + 256 * q, rr = f >> 4, c4 = (f & 15) * 4;
+    put4(p, (int64_t)ti * TS + sr * SUB + rr, (int64_t)tj * TS + sc * SUB + c4, sum[q]);
+  }
+  if (diag) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = threadIdx.x + 256 * q, rr = f >> 4, c4 = (f & 15) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tr[rr][c4 + e] = sum[q][e];
+  }
+  __syncthreads();
+  // mirrored: row tj * TS + sc * 64 + rr, columns ti * TS + sr * 64 + c4 ..
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = threadIdx.x + 256 * q, rr = f >> 4, c4 = (f & 15) * 4;
+    const f32x4_t v = {tr[c4][rr], tr[c4 + 1][rr], tr[c4 + 2][rr], tr[c4 + 3][rr]};
+    put4(p, (int64_t)tj * TS + sc * SUB + rr, (int64_t)ti * TS + sr * SUB + c4, v);
+  }
 }
 
 int choose_splits(int ntiles, int64_t nstages) {
@@ -792,9 +836,9 @@ kronq_status launch_gram(GramParams p, int kind, hipStream_t s) {
   }
   if (p.S > 1) {
     if (kind == 2)
-      hipLaunchKernelGGL(gram_finalize_kernel<FT>, dim3(p.ntiles * (FT / (1024 / FT))), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(gram_finalize_kernel<FT>, dim3(p.ntiles * (FT / 64) * (FT / 64)), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(gram_finalize_kernel<BT>, dim3(p.ntiles * (BT / (1024 / BT))), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(gram_finalize_kernel<BT>, dim3(p.ntiles * (BT / 64) * (BT / 64)), dim3(256), 0, s, p);
     KQ_LAUNCHED("gram_finalize_kernel");
   }
   return KRONQ_OK;
@@ -813,6 +857,7 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
   p.lda = lda;
   p.ldh = ldh;
   p.H = H;
+  p.vec_h = ldh % 4 == 0 && reinterpret_cast<uintptr_t>(H) % 16 == 0;
   p.part = static_cast<float*>(ws);
   p.scale = scale;
   p.beta = beta;
