@@ -121,6 +121,17 @@ def summarize_traffic(args):
     out["bytes_per_launch"] = total
     out["unit"] = "bytes per kronq_gram call (sum over its kernels, scaled counters)"
     out["gram_source_sha256"] = gram_source_hash()
+    run = "python3 -u bench.py --steps 1 --warmup 0 --no-cpu-baseline"
+    probe = "python3 -u bench.py --copy-probe %d" % args.copy_bytes
+    out["commands"] = {
+        "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o bench -- " + run,
+        "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o bench -- " + run,
+        "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/cfetch -o copy -- " + probe,
+        "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/cwrite -o copy -- " + probe,
+        "summary": "python3 bench.py --summarize-traffic <dir>/fetch/bench_counter_collection.csv "
+                   "<dir>/write/bench_counter_collection.csv <dir>/cfetch/copy_counter_collection.csv "
+                   "<dir>/cwrite/copy_counter_collection.csv --traffic-json <out>",
+    }
     with open(args.traffic_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out), flush=True)
