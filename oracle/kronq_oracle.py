@@ -371,3 +371,78 @@ def quantize_sublayer(W, X, G, in_signs, in_block, out_signs, out_block, alpha, 
     out = gptq(Wp, R, perm, bits, group)
     out.update(HX=HX, HG=HG, Wp=Wp, HXp=HXp, HGp=HGp, sg=s, traces=trs, perm=perm, R=R, H=H)
     return out
+
+
+# --------------------------------------------------------------------------
+# Deploy codec.  [readme] the quantized weights are stored packed int4 / int2
+# and a fused dequant + BiIP matvec unpacks them on the fly for single-token
+# decode; 3-bit weights are not bit-packed.  [review] Theorem 1: W' = U W V^T
+# with U, V orthogonal, and [summary] Method: the output-side rescale S_G is
+# applied before the transforms, so the original-domain weight is
+# S_G^-1 U^T W' V.
+# Readings: codes are packed little-endian within a byte (code j of a row at
+# bit offset bits * (j mod (8 / bits)) of byte j / (8 / bits)), rows padded to
+# whole bytes; a group index follows the processing order as in the column
+# loop (natural column c belongs to group pos(c) / group, pos = perm^-1).
+# --------------------------------------------------------------------------
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """m x n codes (0 .. 2^bits - 1) -> m x ceil(n * bits / 8) bytes."""
+    q = np.asarray(codes, dtype=np.int64)
+    m, n = q.shape
+    per = 8 // bits
+    nb = (n + per - 1) // per
+    out = np.zeros((m, nb), dtype=np.int64)
+    for j in range(n):
+        out[:, j // per] |= (q[:, j] & ((1 << bits) - 1)) << (bits * (j % per))
+    return out.astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.int64)
+    per = 8 // bits
+    q = np.zeros((p.shape[0], n), dtype=np.int64)
+    for j in range(n):
+        q[:, j] = (p[:, j // per] >> (bits * (j % per))) & ((1 << bits) - 1)
+    return q
+
+
+def dequant(codes, scales, zeros, group: int, perm=None) -> np.ndarray:
+    """W'[i][c] = scale[i][g] (q[i][c] - zero[i][g]) with g the group of
+    natural column c (0 per-channel; pos(c) // group otherwise)."""
+    q = np.asarray(codes, dtype=np.float64)
+    m, n = q.shape
+    scales = np.asarray(scales, dtype=np.float64).reshape(m, -1)
+    zeros = np.asarray(zeros, dtype=np.float64).reshape(m, -1)
+    if group <= 0:
+        g = np.zeros(n, dtype=np.int64)
+    else:
+        pos = np.arange(n) if perm is None else np.argsort(np.asarray(perm, dtype=np.int64))
+        g = pos // group
+    return scales[:, g] * (q - zeros[:, g])
+
+
+def unrotate(Wp, in_signs, in_block, out_signs, out_block, sg) -> np.ndarray:
+    """S_G^-1 U^T W' V: the inverse of the weight side of biip()."""
+    Wp = np.asarray(Wp, dtype=np.float64)
+    # U^T M: the transpose of T acts on the row index: undo the Hadamard, then the signs
+    A = fwht(Wp.T.reshape(Wp.shape[1], -1, out_block)).reshape(Wp.shape[1], -1).T / np.sqrt(out_block)
+    A = A * np.asarray(out_signs, dtype=np.float64)[:, None]
+    # M V: V acts on the column index from the right, V = (I (x) H) D / sqrt(k)
+    B = fwht(A.reshape(A.shape[0], -1, in_block)).reshape(A.shape) / np.sqrt(in_block)
+    B = B * np.asarray(in_signs, dtype=np.float64)[None, :]
+    return B / np.asarray(sg, dtype=np.float64)[:, None]
+
+
+def decode_matvec(packed, bits, n, scales, zeros, group, in_signs, in_block, out_signs,
+                  out_block, sg, x, perm=None) -> np.ndarray:
+    """y = S_G^-1 U^T W' V x for the packed quantized W', in the order the
+    deploy path computes it: x' = V x, y' = W' x', y = S_G^-1 U^T y'."""
+    x = np.asarray(x, dtype=np.float64)
+    xp = (fwht((x * np.asarray(in_signs, dtype=np.float64)).reshape(-1, in_block)).reshape(-1)
+          / np.sqrt(in_block))
+    codes = unpack_codes(packed, bits, n) if bits in (2, 4) else np.asarray(packed, dtype=np.int64)
+    yp = dequant(codes, scales, zeros, group, perm) @ xp
+    y = fwht(yp.reshape(-1, out_block)).reshape(-1) / np.sqrt(out_block)
+    return y * np.asarray(out_signs, dtype=np.float64) / np.asarray(sg, dtype=np.float64)

@@ -45,6 +45,16 @@ MUTANTS = [
     ("budget boundary", "while bits[i] < bmax and used + n_params[i] <= budget_bits:",
      "while bits[i] < bmax and used + n_params[i] < budget_bits:"),
     ("wrong un-permutation", "codes=codes[:, inv]", "codes=codes[:, perm]"),
+    ("pack big-endian in a byte", "<< (bits * (j % per))", "<< (bits * (per - 1 - j % per))"),
+    ("dequant group by natural column",
+     "pos = np.arange(n) if perm is None else np.argsort(np.asarray(perm, dtype=np.int64))",
+     "pos = np.arange(n)"),
+    ("dequant zero sign", "return scales[:, g] * (q - zeros[:, g])", "return scales[:, g] * (q + zeros[:, g])"),
+    ("unrotate output signs misaligned", "A = A * np.asarray(out_signs, dtype=np.float64)[:, None]",
+     "A = A * np.asarray(out_signs, dtype=np.float64)[::-1][:, None]"),
+    ("unrotate rescale direction", "return B / np.asarray(sg, dtype=np.float64)[:, None]",
+     "return B * np.asarray(sg, dtype=np.float64)[:, None]"),
+    ("decode input transform normalization", "          / np.sqrt(in_block))", "          / in_block)"),
 ]
 
 

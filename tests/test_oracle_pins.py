@@ -447,3 +447,92 @@ def test_allocation_invariants():
         assert b[top] == min(4, 2 + (budget - 2 * int(n.sum())) // int(n[top]))
     with pytest.raises(ValueError):
         O.allocate_bits([1.0, 2.0], [10, 10], 2, 4, 39)
+
+
+# ---------------------------------------------------------------- deploy codec
+
+
+def test_pack_hand_values():
+    # 2-bit: codes 1, 2, 3, 0 -> 0b00_11_10_01; 4-bit: 0xA, 0x3 -> 0x3A; a
+    # 5-column 2-bit row takes two bytes, the second holding code 4 alone
+    assert O.pack_codes(np.array([[1, 2, 3, 0]]), 2).tolist() == [[0x39]]
+    assert O.pack_codes(np.array([[0xA, 0x3]]), 4).tolist() == [[0x3A]]
+    assert O.pack_codes(np.array([[0, 0, 0, 0, 3]]), 2).tolist() == [[0, 3]]
+    np.testing.assert_array_equal(O.unpack_codes(np.array([[0x39]], dtype=np.uint8), 2, 4), [[1, 2, 3, 0]])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_roundtrip_brute_force(bits):
+    rng = np.random.default_rng(bits)
+    q = rng.integers(0, 2 ** bits, (5, 37))
+    p = O.pack_codes(q, bits)
+    assert p.shape == (5, (37 * bits + 7) // 8)
+    np.testing.assert_array_equal(O.unpack_codes(p, bits, 37), q)
+    # every byte value decodes to the codes whose bits it holds
+    for b in range(256):
+        got = O.unpack_codes(np.array([[b]], dtype=np.uint8), bits, 8 // bits)[0]
+        assert sum(int(c) << (bits * i) for i, c in enumerate(got)) == b
+
+
+@pytest.mark.parametrize("seed,ki,ko", [(3, 4, 8), (4, 2, 2), (5, 1, 1)])
+def test_unrotate_inverts_biip_and_matches_explicit(seed, ki, ko):
+    W, HX, HG, si, _, so, _, a = _biip_case(seed, ki=ki, ko=ko)
+    Wp, _, _, s = O.biip(W, HX, HG, si, ki, so, ko, a)
+    np.testing.assert_allclose(O.unrotate(Wp, si, ki, so, ko, s), W, atol=1e-12)
+    U = O.rotation_matrix(W.shape[0], ko, so)
+    V = O.rotation_matrix(W.shape[1], ki, si)
+    M = np.random.default_rng(seed + 100).standard_normal(W.shape)
+    np.testing.assert_allclose(O.unrotate(M, si, ki, so, ko, s), np.diag(1 / s) @ U.T @ M @ V,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("group,act", [(0, False), (0, True), (4, False), (4, True)])
+def test_dequant_reproduces_column_loop_outputs(group, act):
+    rng = np.random.default_rng(11)
+    m, n = 6, 12
+    W = rng.standard_normal((m, n))
+    H = rand_spd(rng, n, 30.0)
+    perm, Hd = O.prepare_hessian(H, 0.01, act)
+    R, _ = O.chol_inv_upper(Hd)
+    out = O.gptq(W, R, perm, 3, group)
+    Wq = O.dequant(out["codes"], out["scales"], out["zeros"], group, perm)
+    np.testing.assert_array_equal(Wq, out["What"])
+
+
+def test_decode_matvec_equals_dense_product():
+    rng = np.random.default_rng(21)
+    m, n, ki, ko, g = 16, 24, 8, 4, 8
+    q = rng.integers(0, 4, (m, n))
+    scales = rng.uniform(0.5, 2.0, (m, n // g))
+    zeros = rng.integers(0, 4, (m, n // g)).astype(np.float64)
+    si, so = rng.choice([-1.0, 1.0], n), rng.choice([-1.0, 1.0], m)
+    s = rng.uniform(0.5, 2.0, m)
+    x = rng.standard_normal(n)
+    y = O.decode_matvec(O.pack_codes(q, 2), 2, n, scales, zeros, g, si, ki, so, ko, s, x)
+    U = O.rotation_matrix(m, ko, so)
+    V = O.rotation_matrix(n, ki, si)
+    Wd = np.zeros((m, n))
+    for i in range(m):
+        for c in range(n):
+            Wd[i, c] = scales[i, c // g] * (q[i, c] - zeros[i, c // g])
+    np.testing.assert_allclose(y, np.diag(1 / s) @ U.T @ Wd @ V @ x, atol=1e-11)
+    # one code per byte (3-bit weights) takes the codes as they are
+    y8 = O.decode_matvec(q, 8, n, scales, zeros, g, si, ki, so, ko, s, x)
+    np.testing.assert_allclose(y8, y, atol=1e-12)
+
+
+def test_decode_recovers_the_quantized_layer():
+    # end to end: BiIP, the column loop and the decode give back W x up to
+    # the quantization error, and exactly the un-rotated dequantized weight
+    rng = np.random.default_rng(5)
+    m, n, N = 8, 16, 64
+    W = rng.standard_normal((m, n)) * 0.02
+    X, G = rng.standard_normal((N, n)), rng.standard_normal((N, m))
+    si, so = rng.choice([-1.0, 1.0], n), rng.choice([-1.0, 1.0], m)
+    out = O.quantize_sublayer(W, X, G, si, 8, so, 4, 0.25, 0.01, 4, 8, False)
+    x = rng.standard_normal(n)
+    y = O.decode_matvec(O.pack_codes(out["codes"], 4), 4, n, out["scales"], out["zeros"], 8,
+                        si, 8, so, 4, out["sg"], x, out["perm"])
+    Wback = O.unrotate(out["What"], si, 8, so, 4, out["sg"])
+    np.testing.assert_allclose(y, Wback @ x, atol=1e-12)
+    assert np.linalg.norm(Wback - W) < 0.2 * np.linalg.norm(W)
