@@ -115,6 +115,21 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
                                size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Inverse of the weight side of BiIP, back to the original domain (Pith
+ * review, Theorem 1: U and V are orthogonal, so W = U^T W' V; hyper.ai summary,
+ * Method: the S_G rescale was applied first and is divided out last).
+ *   W (m x n) <- diag(sg)^-1 U^T W V      in place, fp32
+ * with U from out_side (dim m) and V from in_side (dim n), the same specs and
+ * sg that kronq_biip_rotate was given (sg NULL: no rescale).  Applied to the
+ * dequantized W'^ it gives the quantized layer in its original basis.
+ * ws : kronq_biip_unrotate_ws(m, n) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_biip_unrotate_ws(int64_t m, int64_t n);
+kronq_status kronq_biip_unrotate(float* W, int64_t m, int64_t n, int64_t ldw,
+                                 const kronq_had* in_side, const kronq_had* out_side,
+                                 const float* sg, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Act-order, damping and inverse Cholesky factor (Pith review, Algorithm 2:
  * the damped H_X is H_X + lambda mean(diag H_X) I and the loop uses its
  * inverse Cholesky factor; GitHub README, flag --act_order).
@@ -172,6 +187,64 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
                                  const kronq_qcfg* q, uint8_t* codes, float* scales,
                                  float* zeros, float* What, float* pre_round, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Deploy codec (GitHub README of the KronQ release: int4 / int2 weights are
+ * stored packed and a fused dequantize + BiIP matvec unpacks them on the fly
+ * for single-token decode).
+ * Packed layout (bits 2 and 4): code j of a row is stored at bit offset
+ * bits * (j mod (8 / bits)) of byte j / (8 / bits) of that row, low bits
+ * first; a row holds kronq_packed_row_bytes(n, bits) = ceil(n * bits / 8)
+ * bytes (the unused high bits of its last byte are zero).  Other widths are
+ * stored one code per byte (kronq_packed_row_bytes = n), as
+ * kronq_gptq_quantize writes them.
+ *
+ * kronq_pack_codes: codes (m x n uint8 device, leading dimension ldc >= n) ->
+ *   packed (m rows of ldp >= row bytes, device); only the low `bits` bits of a
+ *   code are stored; bytes of a row past its row bytes are not written.
+ * kronq_unpack_codes: the inverse (codes < 2^bits).
+ * Both take bits 2 or 4 (KRONQ_EINVAL otherwise); buffers must not overlap.
+ * ------------------------------------------------------------------------- */
+int64_t kronq_packed_row_bytes(int64_t n, int32_t bits);
+kronq_status kronq_pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc,
+                              int32_t bits, uint8_t* packed, int64_t ldp, void* stream);
+kronq_status kronq_unpack_codes(const uint8_t* packed, int64_t m, int64_t n, int64_t ldp,
+                                int32_t bits, uint8_t* codes, int64_t ldc, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Batch-1 decode matvec of a quantized, incoherence-processed layer (GitHub
+ * README: fused dequant + BiIP matvec; Pith review, Theorem 1; hyper.ai summary,
+ * Method).  With W'^[r][c] = scales[r][g] (q[r][c] - zeros[r][g]):
+ *   y = diag(sg)^-1 U^T W'^ V x      computed as  x' = V x,  y' = W'^ x',
+ *                                                 y = diag(sg)^-1 U^T y'
+ * codes  : m rows of ldp bytes (device, 16-byte aligned, ldp a multiple of 16
+ *          and >= kronq_packed_row_bytes(n, q->bits)); packed as above for
+ *          bits 2 and 4, one code per byte otherwise.  The whole m x ldp
+ *          buffer must be readable (the pad bytes of a row may be read, never
+ *          used).
+ * q      : bits 1..8; group <= 0 (one grid per row) or a multiple of 64 that
+ *          divides n (KRONQ_EUNSUPPORTED for other group sizes), groups of
+ *          consecutive natural-order columns.
+ * scales, zeros : m x ngroups fp32 device, leading dimension ngroups, as
+ *          kronq_gptq_quantize writes them.
+ * perm   : the act-order permutation or NULL.  One grid per row does not
+ *          depend on it (it is ignored); grouped codes with a permutation are
+ *          KRONQ_EUNSUPPORTED (their groups are not contiguous columns).
+ * in_side, out_side, sg : the transforms and rescale of kronq_biip_rotate
+ *          (sg device m floats, NULL for no rescale).
+ * x      : n fp32 device;  y : m fp32 device (must not overlap x or ws).
+ * Arithmetic is fp32.  Three kernel launches on `stream`, no host
+ * synchronization and no memset: the call may be captured in a HIP graph
+ * (for blocks above 8192 the first call should be made outside capture, since
+ * it raises a kernel's LDS limit).
+ * ws     : kronq_decode_ws(m, n, bits) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_decode_ws(int64_t m, int64_t n, int32_t bits);
+kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp,
+                                 const kronq_qcfg* q, const float* scales, const float* zeros,
+                                 const int32_t* perm, const kronq_had* in_side,
+                                 const kronq_had* out_side, const float* sg, const float* x,
+                                 float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Sensitivity (hyper.ai summary, Method, Eq. 14: s = tr(H_G) tr(H_X) computed

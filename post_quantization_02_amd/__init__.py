@@ -24,7 +24,9 @@ KRONQ_F32, KRONQ_BF16 = 0, 1
 EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gram_ws",
            "kronq_gram", "kronq_biip_ws", "kronq_biip_rotate", "kronq_chol_inv_ws",
            "kronq_chol_inv", "kronq_gptq_ws", "kronq_gptq_quantize", "kronq_sensitivity",
-           "kronq_allocate_bits")
+           "kronq_allocate_bits", "kronq_biip_unrotate_ws", "kronq_biip_unrotate",
+           "kronq_packed_row_bytes", "kronq_pack_codes", "kronq_unpack_codes", "kronq_decode_ws",
+           "kronq_decode_matvec")
 
 
 class KronqError(RuntimeError):
@@ -80,6 +82,23 @@ def load(path: str = LIB_PATH):
     lib.kronq_sensitivity.restype = i32
     lib.kronq_allocate_bits.argtypes = [i32, vp, vp, i32, i32, i64, vp]
     lib.kronq_allocate_bits.restype = i32
+    lib.kronq_biip_unrotate_ws.argtypes = [i64, i64]
+    lib.kronq_biip_unrotate_ws.restype = sz
+    lib.kronq_biip_unrotate.argtypes = [vp, i64, i64, i64, ctypes.POINTER(Had), ctypes.POINTER(Had),
+                                        vp, vp, sz, vp]
+    lib.kronq_biip_unrotate.restype = i32
+    lib.kronq_packed_row_bytes.argtypes = [i64, i32]
+    lib.kronq_packed_row_bytes.restype = i64
+    lib.kronq_pack_codes.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp]
+    lib.kronq_pack_codes.restype = i32
+    lib.kronq_unpack_codes.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp]
+    lib.kronq_unpack_codes.restype = i32
+    lib.kronq_decode_ws.argtypes = [i64, i64, i32]
+    lib.kronq_decode_ws.restype = sz
+    lib.kronq_decode_matvec.argtypes = [vp, i64, i64, i64, ctypes.POINTER(QCfg), vp, vp, vp,
+                                        ctypes.POINTER(Had), ctypes.POINTER(Had), vp, vp, vp, vp,
+                                        sz, vp]
+    lib.kronq_decode_matvec.restype = i32
     _lib = lib
     return lib
 
@@ -250,3 +269,84 @@ def kronq_allocate_bits(scores, n_params, bmin: int, bmax: int, budget_bits: int
     _check(lib.kronq_allocate_bits(len(sc), sc.ctypes.data, npar.ctypes.data, bmin, bmax,
                                    int(budget_bits), out.ctypes.data), "kronq_allocate_bits")
     return [int(x) for x in out]
+
+
+def kronq_biip_unrotate(W: torch.Tensor, in_signs: torch.Tensor, in_block: int,
+                        out_signs: torch.Tensor, out_block: int, sg: torch.Tensor | None = None,
+                        stream=None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """In place: W <- diag(sg)^-1 U^T W V (the inverse of the weight side of BiIP)."""
+    lib = load()
+    _dev(W, "W", torch.float32)
+    m, n = W.shape
+    for t, nm in ((sg, "sg"), (in_signs, "in_signs"), (out_signs, "out_signs")):
+        if t is not None:
+            _dev(t, nm, torch.float32)
+    hin = Had(n, in_block, _ptr(in_signs))
+    hout = Had(m, out_block, _ptr(out_signs))
+    need = lib.kronq_biip_unrotate_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, W.device)
+    _check(lib.kronq_biip_unrotate(_ptr(W), m, n, _ld(W), ctypes.byref(hin), ctypes.byref(hout),
+                                   _ptr(sg), _ptr(ws), need, _stream(stream)), "kronq_biip_unrotate")
+    return W
+
+
+def kronq_packed_row_bytes(n: int, bits: int) -> int:
+    return int(load().kronq_packed_row_bytes(n, bits))
+
+
+def kronq_pack_codes(codes: torch.Tensor, bits: int, packed: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """m x n uint8 codes -> m x ldp packed bytes (ldp = row bytes unless `packed` is given)."""
+    lib = load()
+    _dev(codes, "codes", torch.uint8)
+    m, n = codes.shape
+    if packed is None:
+        packed = torch.zeros((m, lib.kronq_packed_row_bytes(n, bits)), dtype=torch.uint8,
+                             device=codes.device)
+    _dev(packed, "packed", torch.uint8)
+    _check(lib.kronq_pack_codes(_ptr(codes), m, n, _ld(codes), bits, _ptr(packed), _ld(packed),
+                                _stream(stream)), "kronq_pack_codes")
+    return packed
+
+
+def kronq_unpack_codes(packed: torch.Tensor, bits: int, n: int, codes: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    lib = load()
+    _dev(packed, "packed", torch.uint8)
+    m = packed.shape[0]
+    if codes is None:
+        codes = torch.empty((m, n), dtype=torch.uint8, device=packed.device)
+    _dev(codes, "codes", torch.uint8)
+    _check(lib.kronq_unpack_codes(_ptr(packed), m, n, _ld(packed), bits, _ptr(codes), _ld(codes),
+                                  _stream(stream)), "kronq_unpack_codes")
+    return codes
+
+
+def kronq_decode_matvec(codes: torch.Tensor, n: int, bits: int, group: int, scales: torch.Tensor,
+                        zeros: torch.Tensor, in_signs: torch.Tensor, in_block: int,
+                        out_signs: torch.Tensor, out_block: int, sg: torch.Tensor | None,
+                        x: torch.Tensor, y: torch.Tensor | None = None,
+                        perm: torch.Tensor | None = None, stream=None,
+                        ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y = diag(sg)^-1 U^T W'^ V x for stored codes (m rows of ldp bytes)."""
+    lib = load()
+    _dev(codes, "codes", torch.uint8)
+    for t, nm in ((scales, "scales"), (zeros, "zeros"), (in_signs, "in_signs"),
+                  (out_signs, "out_signs"), (sg, "sg"), (x, "x")):
+        if t is not None:
+            _dev(t, nm, torch.float32)
+    m = codes.shape[0]
+    if y is None:
+        y = torch.empty(m, dtype=torch.float32, device=codes.device)
+    q = QCfg(bits, group)
+    hin = Had(n, in_block, _ptr(in_signs))
+    hout = Had(m, out_block, _ptr(out_signs))
+    need = lib.kronq_decode_ws(m, n, bits)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, codes.device)
+    _check(lib.kronq_decode_matvec(_ptr(codes), m, n, _ld(codes), ctypes.byref(q), _ptr(scales),
+                                   _ptr(zeros), _ptr(perm), ctypes.byref(hin), ctypes.byref(hout),
+                                   _ptr(sg), _ptr(x), _ptr(y), _ptr(ws), need, _stream(stream)),
+           "kronq_decode_matvec")
+    return y

@@ -123,6 +123,26 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
                      (hipStream_t)stream);
 }
 
+size_t kronq_biip_unrotate_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return unrotate_ws_bytes(m);
+}
+
+kronq_status kronq_biip_unrotate(float* W, int64_t m, int64_t n, int64_t ldw,
+                                 const kronq_had* in_side, const kronq_had* out_side,
+                                 const float* sg, void* ws, size_t ws_bytes, void* stream) {
+  if (!W) return fail(KRONQ_EINVAL, "kronq_biip_unrotate: W is NULL");
+  if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "kronq_biip_unrotate: bad W shape");
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  st = check_had(out_side, m, "output-side");
+  if (st) return st;
+  size_t need = unrotate_ws_bytes(m);
+  if (ws_bytes < need || !ws)
+    return fail(KRONQ_EWORKSPACE, "kronq_biip_unrotate: workspace %zu < %zu bytes", ws_bytes, need);
+  return unrotate_launch(W, m, n, ldw, *in_side, *out_side, sg, ws, (hipStream_t)stream);
+}
+
 size_t kronq_chol_inv_ws(int64_t n) {
   if (n < 1) return 0;
   return chol_ws_bytes(n);
@@ -170,6 +190,70 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
     return fail(KRONQ_EWORKSPACE, "kronq_gptq_quantize: workspace %zu < %zu bytes", ws_bytes, need);
   return gptq_launch(W, m, n, ldw, R, ldr, perm, q->bits, q->group > 0 ? q->group : 0, codes,
                      scales, zeros, What, pre_round, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int64_t kronq_packed_row_bytes(int64_t n, int32_t bits) {
+  if (n < 1 || bits < 1 || bits > 8) return 0;
+  return decode_row_bytes(n, bits);
+}
+
+kronq_status kronq_pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc,
+                              int32_t bits, uint8_t* packed, int64_t ldp, void* stream) {
+  if (!codes || !packed) return fail(KRONQ_EINVAL, "kronq_pack_codes: NULL pointer");
+  if (bits != 2 && bits != 4)
+    return fail(KRONQ_EINVAL, "kronq_pack_codes: bits %d (only 2 and 4 are packed)", (int)bits);
+  if (m < 1 || n < 1 || ldc < n || ldp < decode_row_bytes(n, bits))
+    return fail(KRONQ_EINVAL, "kronq_pack_codes: bad shape");
+  return pack_launch(codes, m, n, ldc, bits, packed, ldp, (hipStream_t)stream);
+}
+
+kronq_status kronq_unpack_codes(const uint8_t* packed, int64_t m, int64_t n, int64_t ldp,
+                                int32_t bits, uint8_t* codes, int64_t ldc, void* stream) {
+  if (!codes || !packed) return fail(KRONQ_EINVAL, "kronq_unpack_codes: NULL pointer");
+  if (bits != 2 && bits != 4)
+    return fail(KRONQ_EINVAL, "kronq_unpack_codes: bits %d (only 2 and 4 are packed)", (int)bits);
+  if (m < 1 || n < 1 || ldc < n || ldp < decode_row_bytes(n, bits))
+    return fail(KRONQ_EINVAL, "kronq_unpack_codes: bad shape");
+  return unpack_launch(packed, m, n, ldp, bits, codes, ldc, (hipStream_t)stream);
+}
+
+size_t kronq_decode_ws(int64_t m, int64_t n, int32_t bits) {
+  if (m < 1 || n < 1 || bits < 1 || bits > 8) return 0;
+  return decode_ws_bytes(m, n, bits);
+}
+
+kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp,
+                                 const kronq_qcfg* q, const float* scales, const float* zeros,
+                                 const int32_t* perm, const kronq_had* in_side,
+                                 const kronq_had* out_side, const float* sg, const float* x,
+                                 float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!codes || !q || !scales || !zeros || !x || !y)
+    return fail(KRONQ_EINVAL, "kronq_decode_matvec: NULL pointer");
+  if (q->bits < 1 || q->bits > 8)
+    return fail(KRONQ_EINVAL, "kronq_decode_matvec: bits %d outside 1..8", (int)q->bits);
+  if (m < 1 || n < 1) return fail(KRONQ_EINVAL, "kronq_decode_matvec: bad shape");
+  if (ldp < decode_row_bytes(n, q->bits) || ldp % 16 || !aligned(codes, 16))
+    return fail(KRONQ_EINVAL,
+                "kronq_decode_matvec: codes must be 16-byte aligned with ldp a multiple of 16 "
+                "covering a row (%lld bytes)", (long long)decode_row_bytes(n, q->bits));
+  if (q->group > 0) {
+    if (n % q->group) return fail(KRONQ_EINVAL, "kronq_decode_matvec: group does not divide n");
+    if (q->group % 64)
+      return fail(KRONQ_EUNSUPPORTED, "kronq_decode_matvec: group %d is not a multiple of 64",
+                  (int)q->group);
+    if (perm)
+      return fail(KRONQ_EUNSUPPORTED,
+                  "kronq_decode_matvec: groups in a permuted processing order are not decoded");
+  }
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  st = check_had(out_side, m, "output-side");
+  if (st) return st;
+  size_t need = decode_ws_bytes(m, n, q->bits);
+  if (ws_bytes < need || !ws)
+    return fail(KRONQ_EWORKSPACE, "kronq_decode_matvec: workspace %zu < %zu bytes", ws_bytes, need);
+  return decode_launch(codes, m, n, ldp, q->bits, q->group > 0 ? q->group : 0, scales, zeros,
+                       *in_side, *out_side, sg, x, y, ws, (hipStream_t)stream);
 }
 
 kronq_status kronq_sensitivity(const float* HX, int64_t n, int64_t ldhx, const float* HG,

@@ -6,7 +6,10 @@
 // Every transform here has the form  M <- (I (x) H_kr) Dr M Dc (I (x) H_kc) / sqrt(kr kc)
 // for an R x C matrix M: Dr, Dc diagonal (signs, times the S_G rescale where
 // it applies), H_k Sylvester Hadamard matrices of order k mixing contiguous
-// blocks of rows (kr) and of columns (kc).  Because H_kr = H_{kr/R1} (x) H_R1 in
+// blocks of rows (kr) and of columns (kc).  The inverse used by the deploy path
+// (S_G^-1 U^T W' V) has the factors on the other side,
+// M <- Dr (I (x) H_kr) M (I (x) H_kc) Dc / sqrt(kr kc): the same passes with Dc
+// applied when pass 1 stores and Dr when the last pass stores.  Because H_kr = H_{kr/R1} (x) H_R1 in
 // Sylvester order, the mixing splits into factors that act on separate bits
 // of the (row, column) index and commute, so the whole 2-D transform runs in
 // two read-modify-write passes over HBM:
@@ -26,6 +29,7 @@
 // float4-aligned accesses stay 16-byte aligned and the low-bit rounds are
 // bank-conflict free.
 #include "kronq_internal.h"
+#include "wht_lds.h"
 
 namespace kronq {
 namespace {
@@ -34,52 +38,6 @@ constexpr int LOG_TILE = 14;   // 64 KiB tiles: two workgroups per CU overlap HB
 constexpr int TILE = 1 << LOG_TILE;
 constexpr int NT = 512;
 constexpr int kXcds = 8;
-
-__device__ __forceinline__ int pad(int i) { return i + ((i >> 5) << 2); }
-constexpr int padded(int n) { return n + ((n >> 5) << 2); }
-
-// In-register Walsh-Hadamard over K bits (2^K values, natural order).
-template <int K>
-__device__ __forceinline__ void wht_regs(float (&v)[1 << K]) {
-#pragma unroll
-  for (int h = 1; h < (1 << K); h <<= 1)
-#pragma unroll
-    for (int i = 0; i < (1 << K); ++i)
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-}
-
-template <int K>
-__device__ __forceinline__ void lds_round(float* s, int p, int b) {
-  const int ngroups = 1 << (p - K);
-  const int lowmask = (1 << b) - 1;
-  for (int g = threadIdx.x; g < ngroups; g += NT) {
-    const int base = ((g >> b) << (b + K)) | (g & lowmask);
-    float v[1 << K];
-#pragma unroll
-    for (int c = 0; c < (1 << K); ++c) v[c] = s[pad(base | (c << b))];
-    wht_regs<K>(v);
-#pragma unroll
-    for (int c = 0; c < (1 << K); ++c) s[pad(base | (c << b))] = v[c];
-  }
-}
-
-// Unnormalized WHT over index bits [blo, bhi) of the 2^p-element LDS tile.
-__device__ void lds_wht_bits(float* s, int p, int blo, int bhi) {
-  for (int b = blo; b < bhi; b += 4) {
-    const int k = min(4, bhi - b);
-    switch (k) {
-      case 4: lds_round<4>(s, p, b); break;
-      case 3: lds_round<3>(s, p, b); break;
-      case 2: lds_round<2>(s, p, b); break;
-      default: lds_round<1>(s, p, b); break;
-    }
-    __syncthreads();
-  }
-}
 
 struct Side {
   int64_t block;
@@ -96,6 +54,7 @@ struct TParams {
   int lg_cw;           // pass-2 strip width (log2)
   int64_t strips;      // pass-2 strips per row of blocks
   float norm1, norm2;
+  bool post;           // factors after the transform (inverse) instead of before
   int64_t tiles1, tiles2;
   int per_xcd1, per_xcd2;
 };
@@ -122,8 +81,12 @@ __global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
       const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
       const int64_t r = r0 + rr, c = c0 + cc;
       const float4 x = *reinterpret_cast<const float4*>(p.M + r * p.ld + c);
-      const float4 f = *reinterpret_cast<const float4*>(p.col.fac + c);
-      const float g = p.row.fac[r];
+      float4 f = make_float4(1.f, 1.f, 1.f, 1.f);
+      float g = 1.f;
+      if (!p.post) {
+        f = *reinterpret_cast<const float4*>(p.col.fac + c);
+        g = p.row.fac[r];
+      }
       *reinterpret_cast<float4*>(s + pad(e)) =
           make_float4(x.x * f.x * g, x.y * f.y * g, x.z * f.z * g, x.w * f.w * g);
     }
@@ -131,23 +94,36 @@ __global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
     for (int e = threadIdx.x; e < E; e += NT) {
       const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
       const int64_t r = r0 + rr, c = c0 + cc;
-      s[pad(e)] = p.M[r * p.ld + c] * p.col.fac[c] * p.row.fac[r];
+      const float x = p.M[r * p.ld + c];
+      s[pad(e)] = p.post ? x : x * p.col.fac[c] * p.row.fac[r];
     }
   }
   __syncthreads();
-  lds_wht_bits(s, lg, 0, lg);
+  lds_wht_bits<NT>(s, lg, 0, lg);
   const float nrm = p.norm1;
+  // inverse: Dc always lands here (the column transform is complete); Dr only
+  // when no second pass follows
+  const bool post_c = p.post, post_r = p.post && p.tiles2 == 0;
   if (kVec) {
     for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
       const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
       const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
+      float4 f = make_float4(nrm, nrm, nrm, nrm);
+      if (post_c) {
+        const float4 fc = *reinterpret_cast<const float4*>(p.col.fac + c0 + cc);
+        const float g = post_r ? nrm * p.row.fac[r0 + rr] : nrm;
+        f = make_float4(fc.x * g, fc.y * g, fc.z * g, fc.w * g);
+      }
       *reinterpret_cast<float4*>(p.M + (r0 + rr) * p.ld + c0 + cc) =
-          make_float4(y.x * nrm, y.y * nrm, y.z * nrm, y.w * nrm);
+          make_float4(y.x * f.x, y.y * f.y, y.z * f.z, y.w * f.w);
     }
   } else {
     for (int e = threadIdx.x; e < E; e += NT) {
       const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
-      p.M[(r0 + rr) * p.ld + c0 + cc] = s[pad(e)] * nrm;
+      float f = nrm;
+      if (post_c) f *= p.col.fac[c0 + cc];
+      if (post_r) f *= p.row.fac[r0 + rr];
+      p.M[(r0 + rr) * p.ld + c0 + cc] = s[pad(e)] * f;
     }
   }
 }
@@ -181,21 +157,25 @@ __global__ void __launch_bounds__(NT) biip_pass2(TParams p) {
     }
   }
   __syncthreads();
-  lds_wht_bits(s, lg, p.lg_cw, lg);
+  lds_wht_bits<NT>(s, lg, p.lg_cw, lg);
   const float nrm = p.norm2;
   if (kVec) {
     for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
       const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
       if (c < p.C) {
+        const int64_t r = rbase + j * p.R1;
+        const float f = p.post ? nrm * p.row.fac[r] : nrm;
         const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
-        *reinterpret_cast<float4*>(p.M + (rbase + j * p.R1) * p.ld + c) =
-            make_float4(y.x * nrm, y.y * nrm, y.z * nrm, y.w * nrm);
+        *reinterpret_cast<float4*>(p.M + r * p.ld + c) = make_float4(y.x * f, y.y * f, y.z * f, y.w * f);
       }
     }
   } else {
     for (int e = threadIdx.x; e < E; e += NT) {
       const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
-      if (c < p.C) p.M[(rbase + j * p.R1) * p.ld + c] = s[pad(e)] * nrm;
+      if (c < p.C) {
+        const int64_t r = rbase + j * p.R1;
+        p.M[r * p.ld + c] = s[pad(e)] * (p.post ? nrm * p.row.fac[r] : nrm);
+      }
     }
   }
 }
@@ -217,6 +197,13 @@ __global__ void biip_prep(const float* HG, int64_t ldhg, int64_t m, float alpha,
   if (sg_out) sg_out[i] = g;
 }
 
+// rf[i] = so[i] / sg[i]  (sg NULL: all ones)
+__global__ void unrotate_prep(const float* so, const float* sg, int64_t m, float* rf) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= m) return;
+  rf[i] = sg ? so[i] / sg[i] : so[i];
+}
+
 int ilog2(int64_t x) {
   int l = 0;
   while ((int64_t(1) << l) < x) ++l;
@@ -230,8 +217,9 @@ int64_t pow2_floor(int64_t x) {
 }
 
 kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr, const float* rfac,
-                         int64_t kc, const float* cfac, hipStream_t st) {
+                         int64_t kc, const float* cfac, hipStream_t st, bool post = false) {
   TParams p{};
+  p.post = post;
   p.M = M;
   p.R = R;
   p.C = C;
@@ -302,6 +290,17 @@ kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
     if (st) return st;
   }
   return KRONQ_OK;
+}
+
+size_t unrotate_ws_bytes(int64_t m) { return align_up((size_t)m * sizeof(float), 256); }
+
+kronq_status unrotate_launch(float* W, int64_t m, int64_t n, int64_t ldw, const kronq_had& in,
+                             const kronq_had& out, const float* sg, void* ws, hipStream_t s) {
+  float* rf = static_cast<float*>(ws);
+  hipLaunchKernelGGL(unrotate_prep, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, out.signs,
+                     sg, m, rf);
+  KQ_LAUNCHED("unrotate_prep");
+  return transform2d(W, m, n, ldw, out.block, rf, in.block, in.signs, s, true);
 }
 
 }  // namespace kronq

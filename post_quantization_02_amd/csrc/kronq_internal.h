@@ -43,6 +43,10 @@ kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
                          float* HG, int64_t ldhg, const kronq_had& in, const kronq_had& out,
                          float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s);
 
+size_t unrotate_ws_bytes(int64_t m);
+kronq_status unrotate_launch(float* W, int64_t m, int64_t n, int64_t ldw, const kronq_had& in,
+                             const kronq_had& out, const float* sg, void* ws, hipStream_t s);
+
 // chol.hip
 size_t chol_ws_bytes(int64_t n);
 kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, int act_order,
@@ -59,5 +63,17 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
 // trace.hip
 kronq_status trace_launch(const float* HX, int64_t n, int64_t ldhx, const float* HG, int64_t m,
                           int64_t ldhg, double* out3, hipStream_t s);
+
+// codec.hip
+kronq_status pack_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int bits,
+                         uint8_t* packed, int64_t ldp, hipStream_t s);
+kronq_status unpack_launch(const uint8_t* packed, int64_t m, int64_t n, int64_t ldp, int bits,
+                           uint8_t* codes, int64_t ldc, hipStream_t s);
+int64_t decode_row_bytes(int64_t n, int bits);
+size_t decode_ws_bytes(int64_t m, int64_t n, int bits);
+kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp, int bits,
+                           int64_t group, const float* scales, const float* zeros,
+                           const kronq_had& in, const kronq_had& out, const float* sg,
+                           const float* x, float* y, void* ws, hipStream_t s);
 
 }  // namespace kronq

@@ -141,3 +141,43 @@ def test_workspace_queries(lib):
     assert lib.kronq_gptq_ws(4096, 4096) >= 4096 * 4096 * 8
     assert lib.kronq_chol_inv_ws(200) >= 2 * 256 * 256 * 4
     assert lib.kronq_biip_ws(4096, 4096) >= 3 * 4096 * 4
+
+
+def test_codec_arguments_rejected_before_launch(lib):
+    fake = 1 << 20   # never dereferenced
+    assert lib.kronq_packed_row_bytes(4096, 4) == 2048
+    assert lib.kronq_packed_row_bytes(4095, 4) == 2048
+    assert lib.kronq_packed_row_bytes(4097, 2) == 1025
+    assert lib.kronq_packed_row_bytes(100, 3) == 100
+    # only 2 and 4 bits are bit-packed
+    assert lib.kronq_pack_codes(fake, 4, 8, 8, 3, fake, 8, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_unpack_codes(fake, 4, 8, 8, 8, fake, 8, None) == kq.KRONQ_EINVAL
+    # packed row shorter than ceil(n bits / 8)
+    assert lib.kronq_pack_codes(fake, 4, 9, 9, 4, fake, 4, None) == kq.KRONQ_EINVAL
+    h_in = kq.Had(256, 256, fake)
+    h_out = kq.Had(64, 64, fake)
+    ws = lib.kronq_decode_ws(64, 256, 4)
+    assert ws >= (256 + 64) * 4
+
+    def dec(codes, ldp, bits, group, perm=None, ws_bytes=ws, hin=h_in):
+        q = kq.QCfg(bits, group)
+        return lib.kronq_decode_matvec(codes, 64, 256, ldp, ctypes.byref(q), fake, fake, perm,
+                                       ctypes.byref(hin), ctypes.byref(h_out), None, fake, fake,
+                                       fake, ws_bytes, None)
+
+    # row stride not a multiple of 16 / codes misaligned / row too short
+    assert dec(fake, 136, 4, 0) == kq.KRONQ_EINVAL
+    assert dec(fake + 8, 128, 4, 0) == kq.KRONQ_EINVAL
+    assert dec(fake, 112, 4, 0) == kq.KRONQ_EINVAL
+    # groups: must divide n; a multiple of 64; no permuted order
+    assert dec(fake, 128, 4, 96) == kq.KRONQ_EINVAL
+    assert dec(fake, 128, 4, 32) == kq.KRONQ_EUNSUPPORTED
+    assert dec(fake, 128, 4, 128, perm=fake) == kq.KRONQ_EUNSUPPORTED
+    # Hadamard spec of the wrong dimension; workspace too small
+    assert dec(fake, 128, 4, 0, hin=kq.Had(128, 128, fake)) == kq.KRONQ_EINVAL
+    assert dec(fake, 128, 4, 0, ws_bytes=ws - 1) == kq.KRONQ_EWORKSPACE
+    # unrotate: bad block, small workspace
+    assert lib.kronq_biip_unrotate(fake, 64, 256, 256, ctypes.byref(kq.Had(256, 3, fake)),
+                                   ctypes.byref(h_out), None, fake, 1 << 20, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_biip_unrotate(fake, 64, 256, 256, ctypes.byref(h_in), ctypes.byref(h_out),
+                                   None, fake, 4, None) == kq.KRONQ_EWORKSPACE
