@@ -46,6 +46,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the batch-1 decode measurement of the deploy codec")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode measurement (prints its own JSON line)")
+    ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gram_bf16_llama2_7b_q_proj_traffic.json"))
@@ -190,6 +195,92 @@ def cpu_baseline(w, X, G, W, budget_s):
     }
 
 
+# Batch-1 decode through every linear sublayer of a Llama-2-7B decoder stack
+# (32 layers x q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008) with
+# 4-bit codes in groups of 128: one token = 224 kronq_decode_matvec calls,
+# captured once in a HIP graph and replayed.  Hadamard blocks 4096 on 4096-wide
+# sides, 256 on 11008-wide sides (43 blocks).
+DECODE_SUBLAYERS = (("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096),
+                    ("o_proj", 4096, 4096), ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096),
+                    ("down_proj", 4096, 11008))
+
+
+def decode_leg(steps, warmup, n_layers=32, bits=4, group=128):
+    import torch
+    import post_quantization_02_amd as kq
+    dev = torch.device("cuda:0")
+    lib = kq.load()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+    blk = lambda d: 4096 if d == 4096 else 256
+
+    def signs(d):
+        return (torch.randint(0, 2, (d,), generator=gen, device=dev).float() * 2 - 1)
+
+    dims = sorted({d for _, m, n in DECODE_SUBLAYERS for d in (m, n)})
+    sgn_in = {d: signs(d) for d in dims}
+    sgn_out = {d: signs(d) for d in dims}
+    sg = {d: torch.rand(d, generator=gen, device=dev) + 0.5 for d in dims}
+    xs = {d: torch.randn(d, generator=gen, device=dev) for d in dims}
+    ys = {d: torch.empty(d, device=dev) for d in dims}
+    layers = []
+    alg_bytes = 0
+    for _ in range(n_layers):
+        for name, m, n in DECODE_SUBLAYERS:
+            row = lib.kronq_packed_row_bytes(n, bits)
+            ldp = (row + 15) // 16 * 16
+            codes = torch.randint(0, 256, (m, ldp), dtype=torch.uint8, generator=gen, device=dev)
+            ng = n // group
+            scales = torch.rand((m, ng), generator=gen, device=dev) * 1e-2 + 1e-3
+            zeros = torch.randint(0, 1 << bits, (m, ng), generator=gen, device=dev).float()
+            layers.append((codes, m, n, scales, zeros))
+            # codes, grids, x, y, signs both sides, S_G
+            alg_bytes += m * row + 8 * m * ng + 4 * n + 4 * m + 4 * (n + m) + 4 * m
+    ws = torch.empty(max(lib.kronq_decode_ws(m, n, bits) for _, m, n in DECODE_SUBLAYERS),
+                     dtype=torch.uint8, device=dev)
+
+    def token():
+        for codes, m, n, scales, zeros in layers:
+            kq.kronq_decode_matvec(codes, n, bits, group, scales, zeros, sgn_in[n], blk(n),
+                                   sgn_out[m], blk(m), sg[m], xs[n], y=ys[m], ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        token()                        # eager warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        token()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the same token issued eagerly (one host call per sublayer)
+    t0 = time.perf_counter()
+    for _ in range(3):
+        token()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / 3
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"workload": "llama2_7b_linear_stack_w%dg%d_batch1" % (bits, group),
+            "sublayers": len(layers), "calls_per_token": len(layers),
+            "kernels_per_call": 3, "bits": bits, "group": group,
+            "algorithmic_bytes_per_token": alg_bytes, "ms_per_token_graph": ms,
+            "tokens_per_s": 1e3 / ms, "ms_per_token_eager": eager_ms,
+            "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "steps": steps, "warmup": warmup,
+            "data": "synthetic codes, grids, signs and x (seeded torch generator)"}
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -202,6 +293,10 @@ def main():
         print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.decode_only:
+        log("decode leg only")
+        print(json.dumps({"decode": decode_leg(args.decode_steps, 3)}), flush=True)
+        return
     import torch
     import post_quantization_02_amd as kq
     import synth
@@ -348,6 +443,9 @@ def main():
         "input_gen_s": t_gen,
         "h2d_s": t_h2d,
     }
+    if not args.no_decode:
+        log("decode leg")
+        out["decode"] = decode_leg(args.decode_steps, 3)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(w, X, G, W, args.cpu_budget_s)

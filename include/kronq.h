@@ -233,7 +233,7 @@ kronq_status kronq_unpack_codes(const uint8_t* packed, int64_t m, int64_t n, int
  * in_side, out_side, sg : the transforms and rescale of kronq_biip_rotate
  *          (sg device m floats, NULL for no rescale).
  * x      : n fp32 device;  y : m fp32 device (must not overlap x or ws).
- * Arithmetic is fp32.  Three kernel launches on `stream`, no host
+ * Arithmetic is fp32.  Two kernel launches on `stream`, no host
  * synchronization and no memset: the call may be captured in a HIP graph
  * (for blocks above 8192 the first call should be made outside capture, since
  * it raises a kernel's LDS limit).

@@ -231,7 +231,8 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
     return fail(KRONQ_EINVAL, "kronq_decode_matvec: NULL pointer");
   if (q->bits < 1 || q->bits > 8)
     return fail(KRONQ_EINVAL, "kronq_decode_matvec: bits %d outside 1..8", (int)q->bits);
-  if (m < 1 || n < 1) return fail(KRONQ_EINVAL, "kronq_decode_matvec: bad shape");
+  if (m < 1 || n < 1 || n > INT32_MAX || m > INT32_MAX)
+    return fail(KRONQ_EINVAL, "kronq_decode_matvec: bad shape");
   if (ldp < decode_row_bytes(n, q->bits) || ldp % 16 || !aligned(codes, 16))
     return fail(KRONQ_EINVAL,
                 "kronq_decode_matvec: codes must be 16-byte aligned with ldp a multiple of 16 "

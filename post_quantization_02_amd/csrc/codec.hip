@@ -9,18 +9,22 @@
 // bits * (j mod (8 / bits)) of byte j / (8 / bits); a row is padded to whole
 // bytes.  Other widths keep one code per byte, as the column loop emits them.
 //
-// Decode of y = S_G^-1 U^T W^ V x with W^[r][c] = s[r][g] (q[r][c] - z[r][g]):
-//   decode_xin  x' = V x = (I (x) H_kin) D_in x / sqrt(kin)        LDS butterflies
-//   decode_gemv P[t][r] = sum over column slice t of s (q - z) x'   HBM stream
-//   decode_yout y = S_G^-1 D_out (I (x) H_kout) (sum_t P[t]) / sqrt(kout)
+// Decode of y = S_G^-1 U^T W^ V x with W^[r][c] = s[r][g] (q[r][c] - z[r][g]),
+// two launches:
+//   decode_gemv  x' = V x = (I (x) H_kin) D_in x / sqrt(kin) for the
+//                workgroup's column slice (LDS butterflies), then
+//                P[t][r] = sum over column slice t of s (q - z) x'     HBM stream
+//   decode_yout  y = S_G^-1 D_out (I (x) H_kout) (sum_t P[t]) / sqrt(kout)
 // decode_gemv carries all the weight bytes.  A wave reads 16 bytes of a row per
-// lane (one 1 KiB coalesced load per row and slice) and keeps the x' values
-// of its chunk in registers for every row it visits, so x' costs no LDS or
-// cache traffic per row.  The zero point is folded out of the inner
-// loop: sum s (q - z) x' = s (sum q x' - z sum x') per lane chunk (a chunk
-// never straddles a group: groups are multiples of 64 columns).  The three
-// launches are ordinary stream work (no host synchronization, no memset), so
-// a caller can capture them in a HIP graph.
+// lane (one 1 KiB coalesced load per row and slice).  A workgroup issues its x
+// loads, then every weight load of its rows, and builds x' in LDS while the
+// weights are in flight (a workgroup barrier waits for LDS traffic only).
+// Each lane keeps the x' values of its chunk in registers for all its rows.
+// The zero point is folded out of the inner loop:
+// sum s (q - z) x' = s (sum q x' - z sum x') per lane chunk (a chunk never
+// straddles a group: groups are multiples of 64 columns).  Both launches are
+// ordinary stream work (no host synchronization, no memset), so a caller can
+// capture them in a HIP graph.
 #include <algorithm>
 #include <cmath>
 
@@ -31,7 +35,6 @@ namespace kronq {
 namespace {
 
 constexpr int NT = 256;
-constexpr int kLgTileVec = 13;   // vector transform tile: 8192 floats unless a block is longer
 
 // ---------------------------------------------------------------- pack / unpack
 
@@ -65,52 +68,67 @@ __global__ void unpack_kernel(const uint8_t* __restrict__ packed, int64_t m, int
   }
 }
 
-// ---------------------------------------------------------------- vector transforms
+// ---------------------------------------------------------------- output transform
 
-// x' = WHT_kin(x * signs) * nrm over a tile of 2^lg_tile elements (whole blocks;
-// the tail of the last tile is zero padding and is not stored)
-__global__ void __launch_bounds__(NT) decode_xin(const float* __restrict__ x,
-                                                 const float* __restrict__ sgn, int64_t n,
-                                                 int lg_k, int lg_tile, float nrm,
-                                                 float* __restrict__ xp) {
+// y = (WHT_kout(sum_t part[t]) * nrm) * signs / sg over a tile of 2^lg_tile
+// rows (whole blocks; the tail of the last tile is zero padding, not stored).
+// Thread t owns rows t + NTY * j (coalesced); the factors of its rows and the
+// partial sums are loaded first (clamped addresses, rows past m discarded by a
+// select).  The row bits above 8 (register index j) are transformed in
+// registers, bits 0..7 in LDS.
+constexpr int NTY = 256;
+constexpr int EMAX = 16;   // elements a thread holds: tiles up to 16 * 256 = 4096 in registers
+
+__global__ void __launch_bounds__(NTY) decode_yout(const float* __restrict__ part, int slices,
+                                                   int64_t m, const float* __restrict__ sgn,
+                                                   const float* __restrict__ sg, int lg_k,
+                                                   int lg_tile, float nrm, float* __restrict__ y) {
   extern __shared__ __align__(16) float s[];
   const int T = 1 << lg_tile;
+  const int t = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x << lg_tile;
-  for (int e = threadIdx.x; e < T; e += NT) {
-    const int64_t i = base + e;
-    s[pad(e)] = (i < n) ? x[i] * sgn[i] : 0.f;
+  float v[EMAX], f[EMAX];
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    const int64_t r = base + t + NTY * j;
+    const bool in = (t + NTY * j < T) && r < m;
+    const int64_t rr = in ? r : 0;
+    const float a = sgn[rr], b = sg ? sg[rr] : 1.f;
+    f[j] = nrm * a / b;
+    v[j] = 0.f;
   }
-  __syncthreads();
-  lds_wht_bits<NT>(s, lg_tile, 0, lg_k);
-  for (int e = threadIdx.x; e < T; e += NT) {
-    const int64_t i = base + e;
-    if (i < n) xp[i] = s[pad(e)] * nrm;
-  }
-}
-
-// y = (WHT_kout(sum_t part[t]) * nrm) * signs / sg
-__global__ void __launch_bounds__(NT) decode_yout(const float* __restrict__ part, int slices,
-                                                  int64_t m, const float* __restrict__ sgn,
-                                                  const float* __restrict__ sg, int lg_k,
-                                                  int lg_tile, float nrm, float* __restrict__ y) {
-  extern __shared__ __align__(16) float s[];
-  const int T = 1 << lg_tile;
-  const int64_t base = (int64_t)blockIdx.x << lg_tile;
-  for (int e = threadIdx.x; e < T; e += NT) {
-    const int64_t i = base + e;
-    float v = 0.f;
-    if (i < m)
-      for (int t = 0; t < slices; ++t) v += part[(int64_t)t * m + i];
-    s[pad(e)] = v;
-  }
-  __syncthreads();
-  lds_wht_bits<NT>(s, lg_tile, 0, lg_k);
-  for (int e = threadIdx.x; e < T; e += NT) {
-    const int64_t i = base + e;
-    if (i < m) {
-      const float f = sg ? sgn[i] / sg[i] : sgn[i];
-      y[i] = s[pad(e)] * nrm * f;
+#pragma unroll 2
+  for (int q = 0; q < slices; ++q) {
+    const float* pq = part + (int64_t)q * m;
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j) {
+      const int64_t r = base + t + NTY * j;
+      const bool in = (t + NTY * j < T) && r < m;
+      const float a = pq[in ? r : 0];
+      v[j] += in ? a : 0.f;
     }
+  }
+  const bool regs = T <= EMAX * NTY;
+  wht_regs_masked<EMAX>(v, T / NTY, regs ? (1 << min(4, max(0, lg_k - 8))) - 1 : 0);
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j)
+    if (t + NTY * j < T) s[pad(t + NTY * j)] = v[j];
+  for (int e = t + NTY * EMAX; e < T; e += NTY) {   // tiles above 4096 rows
+    float a = 0.f;
+    for (int q = 0; q < slices; ++q)
+      if (base + e < m) a += part[(int64_t)q * m + base + e];
+    s[pad(e)] = a;
+  }
+  __syncthreads();
+  lds_wht_low_bits<NTY>(s, lg_tile, regs ? min(lg_k, 8) : lg_k);
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    const int64_t r = base + t + NTY * j;
+    if (t + NTY * j < T && r < m) y[r] = s[pad(t + NTY * j)] * f[j];
+  }
+  for (int e = t + NTY * EMAX; e < T; e += NTY) {
+    const int64_t r = base + e;
+    if (r < m) y[r] = s[pad(e)] * (nrm * sgn[r] / (sg ? sg[r] : 1.f));
   }
 }
 
@@ -124,110 +142,179 @@ struct GemvParams {
   const float* zeros;
   int64_t ngroups;
   int64_t group;        // 0: one grid per row
-  const float* xp;
+  const float* x;       // input vector (n)
+  const float* sgn_in;  // D_in (n)
+  int lg_kin;           // log2 of the input block
+  int lg_tile;          // log2 of the x' tile: max(slice width, input block)
+  float nrm_in;         // 1 / sqrt(kin)
   int64_t m, n;
   int slices;
   float* part;          // slices x m partial sums
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+  // lanes the DPP source leaves out (rows outside ROWS) add 0
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                   CTRL, ROWS, 0xF, false));
 }
 
-// sum over the lane's 16 bytes of code * x'  (BITS 2 or 4: 8/BITS codes a byte,
-// low bits first; BITS 8: one code a byte)
+// Sum over the 64 lanes, returned as a wave-uniform value: butterflies within
+// quads and rows of 16 (quad_perm, half-mirror, mirror), then lane 15 of each
+// row into the next row and lane 31 into the upper half (row broadcasts); lane
+// 63 ends with the total.  All VALU data movement, no LDS round trips.
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_add<0xB1>(v);         // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);         // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);        // row_half_mirror
+  v = dpp_add<0x140>(v);        // row_mirror: every lane holds its row's sum
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// sum over the lane's 16 bytes of code * x' (one code a byte for BITS 8; for
+// BITS 2 and 4, 8 / BITS codes a byte, low bits first).  Codes of 2 and 4 bits
+// are spread one a byte and converted two at a time as fp8 e4m3: a byte value
+// c < 16 has exponent field 0 or 1, where the format is linear, so it decodes
+// to exactly c * unit (unit = the value of byte 1, a power of two); the caller
+// multiplies the sum by 1 / unit.
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const uint4& q, const float* xr) {
   constexpr int PER = 8 / BITS;
-  constexpr uint32_t MASK = (BITS == 8) ? 0xFFFFFFFFu
-                                        : ((1u << BITS) - 1u) * 0x01010101u;
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float acc0 = 0.f, acc1 = 0.f;
+  if constexpr (BITS == 8) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const uint32_t b = (w[d] >> (BITS * t)) & MASK;   // byte k holds code 4*PER*d + PER*k + t
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float c = (float)((b >> (8 * k)) & 0xFFu);
-        const float xv = xr[4 * PER * d + PER * k + t];
-        if (k & 1) acc1 = fmaf(c, xv, acc1);
-        else acc0 = fmaf(c, xv, acc0);
+        const float c = (float)((w[d] >> (8 * k)) & 0xFFu);
+        if (k & 1) acc1 = fmaf(c, xr[4 * d + k], acc1);
+        else acc0 = fmaf(c, xr[4 * d + k], acc0);
       }
-    }
+  } else {
+    constexpr uint32_t MASK = ((1u << BITS) - 1u) * 0x01010101u;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const uint32_t b = (w[d] >> (BITS * t)) & MASK;   // byte k holds code 4*PER*d + PER*k + t
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);   // bytes 0, 1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);    // bytes 2, 3
+        const float* xp = xr + 4 * PER * d + t;
+        acc0 = fmaf(lo[0], xp[0], acc0);
+        acc1 = fmaf(lo[1], xp[PER], acc1);
+        acc0 = fmaf(hi[0], xp[2 * PER], acc0);
+        acc1 = fmaf(hi[1], xp[3 * PER], acc1);
+      }
+  }
   return acc0 + acc1;
 }
 
-template <int BITS, int U>
+// One workgroup: column slice sl (SW columns) x 4U rows.  x' of the slice is
+// built here: x * D_in through the input butterflies in LDS over a tile of
+// max(SW, kin) columns (a block wider than the slice is transformed whole and
+// the slice kept).
+template <int BITS, int U, bool GROUPED>
 __global__ void __launch_bounds__(NT) decode_gemv(GemvParams p) {
   constexpr int CPL = (BITS == 8) ? 16 : 128 / BITS;   // codes a lane holds per row (16 bytes)
   constexpr int SW = 64 * CPL;                        // columns per slice
-  __shared__ __align__(16) float xs[SW];
+  extern __shared__ __align__(16) float tile[];
   const int sl = (int)(blockIdx.x % (unsigned)p.slices);
   const int64_t rg = blockIdx.x / (unsigned)p.slices;
   const int64_t c0 = (int64_t)sl * SW;
-  for (int i = threadIdx.x; i < SW; i += NT) xs[i] = (c0 + i < p.n) ? p.xp[c0 + i] : 0.f;
-  __syncthreads();
+  const int T = 1 << p.lg_tile;                       // >= SW >= 1024
+  const int64_t tb = (c0 >> p.lg_tile) << p.lg_tile;  // first column of the tile
+  const int off = (int)(c0 - tb);
+  const int ept = T / NT;                             // tile elements a thread holds (>= 4)
+  const int t = threadIdx.x;
 
+  // Loads below read clamped, always valid addresses and discard what lies
+  // outside the matrix with a select, so they issue back to back.
+  // 1. x and D_in: thread t holds tile elements t + NT * j (coalesced)
+  float xv[EMAX], sv[EMAX];
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    const int64_t c = tb + t + NT * j;
+    const bool in = (j < ept) && (c < p.n);
+    const int64_t cc = in ? c : 0;
+    const float a = p.x[cc], b = p.sgn_in[cc];
+    xv[j] = in ? a : 0.f;
+    sv[j] = in ? b : 0.f;
+  }
+
+  // 2. weight rows and their grids
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  float xr[CPL];
-#pragma unroll
-  for (int k = 0; k < CPL; k += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xs + lane * CPL + k);
-    xr[k] = v.x;
-    xr[k + 1] = v.y;
-    xr[k + 2] = v.z;
-    xr[k + 3] = v.w;
-  }
-  float xsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) xsum += xr[k];
-
   const int64_t lane_b = (int64_t)sl * 1024 + lane * 16;   // first byte of the lane's chunk
   const bool live = lane_b < p.nbytes;                      // then lane_b + 16 <= ldp
-  const bool grouped = p.group > 0;
+  const int64_t lb = live ? lane_b : 0;
   // grouped: the chunk lies in one group (group % 64 == 0, n % group == 0)
-  const int64_t g = (grouped && live) ? (c0 + lane * CPL) / p.group : 0;
-  const float xtot = grouped ? 0.f : wave_sum(xsum);
-
+  const int64_t g = (GROUPED && live) ? (int64_t)((uint32_t)(c0 + lane * CPL) / (uint32_t)p.group) : 0;
   const int64_t r0 = rg * (4 * U) + wave * U;
   uint4 q[U];
   float sc[U], zr[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t r = r0 + u;
-    q[u] = make_uint4(0u, 0u, 0u, 0u);
-    sc[u] = 0.f;
-    zr[u] = 0.f;
-    if (r < p.m) {
-      if (live) q[u] = *reinterpret_cast<const uint4*>(p.codes + r * p.ldp + lane_b);
-      if (grouped) {
-        if (live) {
-          sc[u] = p.scales[r * p.ngroups + g];
-          zr[u] = p.zeros[r * p.ngroups + g];
-        }
-      } else {
-        sc[u] = p.scales[r * p.ngroups];
-        zr[u] = p.zeros[r * p.ngroups];
-      }
-    }
+    const bool rin = r < p.m;
+    const int64_t rr = rin ? r : 0;
+    const uint4 v = *reinterpret_cast<const uint4*>(p.codes + rr * p.ldp + lb);
+    const bool use = rin && live;
+    q[u] = make_uint4(use ? v.x : 0u, use ? v.y : 0u, use ? v.z : 0u, use ? v.w : 0u);
+    const float a = p.scales[rr * p.ngroups + g], b = p.zeros[rr * p.ngroups + g];
+    sc[u] = rin ? a : 0.f;
+    zr[u] = rin ? b : 0.f;
   }
+
+  // 3. x' = WHT(x * D_in): element bits 8.. (register index j) in registers
+  //    when they lie inside an input block, bits below 8 in LDS; tiles above
+  //    EMAX * NT columns load the rest here and run every bit in LDS
+  const bool regs = ept <= EMAX;
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) xv[j] *= sv[j];
+  wht_regs_masked<EMAX>(xv, ept, regs ? (1 << min(4, max(0, p.lg_kin - 8))) - 1 : 0);
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j)
+    if (j < ept) tile[pad(t + NT * j)] = xv[j];
+  for (int j = EMAX; j < ept; ++j) {
+    const int e = t + NT * j;
+    tile[pad(e)] = (tb + e < p.n) ? p.x[tb + e] * p.sgn_in[tb + e] : 0.f;
+  }
+  __syncthreads();
+  lds_wht_low_bits<NT>(tile, p.lg_tile, regs ? min(p.lg_kin, 8) : p.lg_kin);
+  float xr[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; k += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(tile + pad(off + lane * CPL + k));
+    xr[k] = v.x * p.nrm_in;
+    xr[k + 1] = v.y * p.nrm_in;
+    xr[k + 2] = v.z * p.nrm_in;
+    xr[k + 3] = v.w * p.nrm_in;
+  }
+  float xsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) xsum += xr[k];
+  const float xtot = GROUPED ? 0.f : wave_total(xsum);
+
+  // 4. dequantized dot products, zero point folded out of the inner loop;
+  //    lane u stores row u
+  float out = 0.f;
+  const float unit_inv =
+      (BITS == 8) ? 1.f : 1.f / __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t r = r0 + u;
-    const float a = chunk_dot<BITS>(q[u], xr);
+    const float a = chunk_dot<BITS>(q[u], xr) * unit_inv;
     float v;
-    if (grouped) {
-      v = wave_sum(sc[u] * (a - zr[u] * xsum));
+    if (GROUPED) {
+      v = wave_total(live ? sc[u] * (a - zr[u] * xsum) : 0.f);
     } else {
-      v = sc[u] * (wave_sum(a) - zr[u] * xtot);
+      v = sc[u] * (wave_total(a) - zr[u] * xtot);
     }
-    if (lane == 0 && r < p.m) p.part[(int64_t)sl * p.m + r] = v;
+    out = (lane == u) ? v : out;
   }
+  if (lane < U && r0 + lane < p.m) p.part[(int64_t)sl * p.m + r0 + lane] = out;
 }
 
 int ilog2(int64_t x) {
@@ -243,37 +330,40 @@ int64_t slices_of(int64_t n, int bits) {
   return (n + sw - 1) / sw;
 }
 
-template <int BITS>
+kronq_status set_lds(const void* fn, size_t bytes) {
+  if (bytes > 65536)
+    KQ_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
+  return KRONQ_OK;
+}
+
+template <int BITS, bool GROUPED>
 kronq_status gemv_dispatch(const GemvParams& p, hipStream_t st) {
   const int64_t S = p.slices;
-  const int64_t target = 512;   // two workgroups per CU
+  // about one workgroup per CU or more: rows per workgroup 32, 16 or 8
   int U = 2;
-  if (S * ((p.m + 31) / 32) >= target) U = 8;
-  else if (S * ((p.m + 15) / 16) >= target) U = 4;
+  if (S * ((p.m + 31) / 32) >= 256) U = 8;
+  else if (S * ((p.m + 15) / 16) >= 256) U = 4;
   const int64_t rows_per_wg = 4 * U;
   const int64_t grid = S * ((p.m + rows_per_wg - 1) / rows_per_wg);
   if (grid > 0x7fffffff) return fail(KRONQ_EINVAL, "decode_gemv: grid too large");
+  const size_t lds = (size_t)padded(1 << p.lg_tile) * sizeof(float);
+  const void* fn = U == 8 ? (const void*)decode_gemv<BITS, 8, GROUPED>
+                 : U == 4 ? (const void*)decode_gemv<BITS, 4, GROUPED>
+                          : (const void*)decode_gemv<BITS, 2, GROUPED>;
+  kronq_status s = set_lds(fn, lds);
+  if (s) return s;
   switch (U) {
-    case 8: hipLaunchKernelGGL((decode_gemv<BITS, 8>), dim3((unsigned)grid), dim3(NT), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_gemv<BITS, 4>), dim3((unsigned)grid), dim3(NT), 0, st, p); break;
-    default: hipLaunchKernelGGL((decode_gemv<BITS, 2>), dim3((unsigned)grid), dim3(NT), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_gemv<BITS, 8, GROUPED>), dim3((unsigned)grid), dim3(NT), lds, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_gemv<BITS, 4, GROUPED>), dim3((unsigned)grid), dim3(NT), lds, st, p); break;
+    default: hipLaunchKernelGGL((decode_gemv<BITS, 2, GROUPED>), dim3((unsigned)grid), dim3(NT), lds, st, p); break;
   }
   KQ_LAUNCHED("decode_gemv");
   return KRONQ_OK;
 }
 
-// tile of the vector transforms: whole blocks, at least one block, at most
-// max(block, 2^kLgTileVec) elements and no longer than the vector needs
-int vec_tile_lg(int64_t len, int lg_k) {
-  const int lg_len = ilog2(len);
-  int lg = std::min(kLgTileVec, lg_len);
-  return std::max(lg, lg_k);
-}
-
-kronq_status set_lds(const void* fn, size_t bytes) {
-  if (bytes > 65536)
-    KQ_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
-  return KRONQ_OK;
+template <int BITS>
+kronq_status gemv_bits(const GemvParams& p, hipStream_t st) {
+  return p.group > 0 ? gemv_dispatch<BITS, true>(p, st) : gemv_dispatch<BITS, false>(p, st);
 }
 
 }  // namespace
@@ -304,30 +394,14 @@ int64_t decode_row_bytes(int64_t n, int bits) {
 }
 
 size_t decode_ws_bytes(int64_t m, int64_t n, int bits) {
-  return align_up((size_t)n * sizeof(float), 256) +
-         align_up((size_t)slices_of(n, bits) * (size_t)m * sizeof(float), 256);
+  return align_up((size_t)slices_of(n, bits) * (size_t)m * sizeof(float), 256);
 }
 
 kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp, int bits,
                            int64_t group, const float* scales, const float* zeros,
                            const kronq_had& in, const kronq_had& out, const float* sg,
                            const float* x, float* y, void* ws, hipStream_t s) {
-  float* xp = static_cast<float*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                         align_up((size_t)n * sizeof(float), 256));
-  // x' = V x
-  {
-    const int lg_k = ilog2(in.block);
-    const int lg_t = vec_tile_lg(n, lg_k);
-    const int64_t tiles = (n + (int64_t(1) << lg_t) - 1) >> lg_t;
-    const size_t lds = (size_t)padded(1 << lg_t) * sizeof(float);
-    kronq_status st = set_lds((const void*)decode_xin, lds);
-    if (st) return st;
-    hipLaunchKernelGGL(decode_xin, dim3((unsigned)tiles), dim3(NT), lds, s, x, in.signs, n, lg_k,
-                       lg_t, (float)(1.0 / std::sqrt((double)in.block)), xp);
-    KQ_LAUNCHED("decode_xin");
-  }
-  // partial row sums of W^ x'
+  // partial row sums of W^ x', with x' = V x built per workgroup
   GemvParams p{};
   p.codes = codes;
   p.ldp = ldp;
@@ -336,27 +410,29 @@ kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t l
   p.zeros = zeros;
   p.group = group;
   p.ngroups = group > 0 ? n / group : 1;
-  p.xp = xp;
+  p.x = x;
+  p.sgn_in = in.signs;
+  p.lg_kin = ilog2(in.block);
+  p.lg_tile = std::max(ilog2(64 * codes_per_lane(bits)), p.lg_kin);
+  p.nrm_in = (float)(1.0 / std::sqrt((double)in.block));
   p.m = m;
   p.n = n;
   p.slices = (int)slices_of(n, bits);
-  p.part = part;
-  kronq_status st = (bits == 4) ? gemv_dispatch<4>(p, s)
-                   : (bits == 2) ? gemv_dispatch<2>(p, s)
-                                 : gemv_dispatch<8>(p, s);
+  p.part = static_cast<float*>(ws);
+  kronq_status st = (bits == 4) ? gemv_bits<4>(p, s)
+                   : (bits == 2) ? gemv_bits<2>(p, s)
+                                 : gemv_bits<8>(p, s);
   if (st) return st;
-  // y = S_G^-1 U^T y'
-  {
-    const int lg_k = ilog2(out.block);
-    const int lg_t = vec_tile_lg(m, lg_k);
-    const int64_t tiles = (m + (int64_t(1) << lg_t) - 1) >> lg_t;
-    const size_t lds = (size_t)padded(1 << lg_t) * sizeof(float);
-    st = set_lds((const void*)decode_yout, lds);
-    if (st) return st;
-    hipLaunchKernelGGL(decode_yout, dim3((unsigned)tiles), dim3(NT), lds, s, part, p.slices, m,
-                       out.signs, sg, lg_k, lg_t, (float)(1.0 / std::sqrt((double)out.block)), y);
-    KQ_LAUNCHED("decode_yout");
-  }
+  // y = S_G^-1 U^T y'  (tiles of max(kout, min(4096, m)) rows)
+  const int lg_k = ilog2(out.block);
+  const int lg_t = std::max(lg_k, std::min(12, ilog2(m)));
+  const int64_t tiles = (m + (int64_t(1) << lg_t) - 1) >> lg_t;
+  const size_t lds = (size_t)padded(1 << lg_t) * sizeof(float);
+  st = set_lds((const void*)decode_yout, lds);
+  if (st) return st;
+  hipLaunchKernelGGL(decode_yout, dim3((unsigned)tiles), dim3(NTY), lds, s, p.part, p.slices, m,
+                     out.signs, sg, lg_k, lg_t, (float)(1.0 / std::sqrt((double)out.block)), y);
+  KQ_LAUNCHED("decode_yout");
   return KRONQ_OK;
 }
 

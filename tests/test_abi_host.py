@@ -157,7 +157,7 @@ def test_codec_arguments_rejected_before_launch(lib):
     h_in = kq.Had(256, 256, fake)
     h_out = kq.Had(64, 64, fake)
     ws = lib.kronq_decode_ws(64, 256, 4)
-    assert ws >= (256 + 64) * 4
+    assert ws >= 64 * 4   # partial row sums of one column slice
 
     def dec(codes, ldp, bits, group, perm=None, ws_bytes=ws, hin=h_in):
         q = kq.QCfg(bits, group)
