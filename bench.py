@@ -203,21 +203,31 @@ def cpu_baseline(w, X, G, W, budget_s):
 DECODE_SUBLAYERS = (("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096),
                     ("o_proj", 4096, 4096), ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096),
                     ("down_proj", 4096, 11008))
+# The same weights with the sublayers that read one input stacked row-wise
+# (q/k/v: 12288 x 4096; gate/up: 22016 x 4096).  They share V and x'; the
+# output transform of the stack is block-diagonal in the sublayers' own
+# transforms because every output block lies inside one sublayer.
+DECODE_STACKED = (("qkv_proj", 12288, 4096), ("o_proj", 4096, 4096),
+                  ("gate_up_proj", 22016, 4096), ("down_proj", 4096, 11008))
 
 
-def decode_leg(steps, warmup, n_layers=32, bits=4, group=128):
+def decode_leg(steps, warmup, n_layers=32, bits=4, group=128, sublayers=DECODE_SUBLAYERS,
+               name="llama2_7b_linear_stack"):
     import torch
     import post_quantization_02_amd as kq
     dev = torch.device("cuda:0")
     lib = kq.load()
     gen = torch.Generator(device=dev)
     gen.manual_seed(20260)
-    blk = lambda d: 4096 if d == 4096 else 256
+    # Hadamard block of each side: 4096 on 4096-wide sides and on the q/k/v
+    # stack (three 4096 blocks), 256 on 11008-wide sides and the gate/up stack
+    blocks = {4096: 4096, 11008: 256, 12288: 4096, 22016: 256}
+    blk = blocks.__getitem__
 
     def signs(d):
         return (torch.randint(0, 2, (d,), generator=gen, device=dev).float() * 2 - 1)
 
-    dims = sorted({d for _, m, n in DECODE_SUBLAYERS for d in (m, n)})
+    dims = sorted({d for _, m, n in sublayers for d in (m, n)})
     sgn_in = {d: signs(d) for d in dims}
     sgn_out = {d: signs(d) for d in dims}
     sg = {d: torch.rand(d, generator=gen, device=dev) + 0.5 for d in dims}
@@ -226,7 +236,7 @@ def decode_leg(steps, warmup, n_layers=32, bits=4, group=128):
     layers = []
     alg_bytes = 0
     for _ in range(n_layers):
-        for name, m, n in DECODE_SUBLAYERS:
+        for _sub, m, n in sublayers:
             row = lib.kronq_packed_row_bytes(n, bits)
             ldp = (row + 15) // 16 * 16
             codes = torch.randint(0, 256, (m, ldp), dtype=torch.uint8, generator=gen, device=dev)
@@ -236,7 +246,7 @@ def decode_leg(steps, warmup, n_layers=32, bits=4, group=128):
             layers.append((codes, m, n, scales, zeros))
             # codes, grids, x, y, signs both sides, S_G
             alg_bytes += m * row + 8 * m * ng + 4 * n + 4 * m + 4 * (n + m) + 4 * m
-    ws = torch.empty(max(lib.kronq_decode_ws(m, n, bits) for _, m, n in DECODE_SUBLAYERS),
+    ws = torch.empty(max(lib.kronq_decode_ws(m, n, bits) for _, m, n in sublayers),
                      dtype=torch.uint8, device=dev)
 
     def token():
@@ -272,9 +282,9 @@ def decode_leg(steps, warmup, n_layers=32, bits=4, group=128):
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / 3
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    return {"workload": "llama2_7b_linear_stack_w%dg%d_batch1" % (bits, group),
+    return {"workload": "%s_w%dg%d_batch1" % (name, bits, group),
             "sublayers": len(layers), "calls_per_token": len(layers),
-            "kernels_per_call": 3, "bits": bits, "group": group,
+            "kernels_per_call": 2, "bits": bits, "group": group,
             "algorithmic_bytes_per_token": alg_bytes, "ms_per_token_graph": ms,
             "tokens_per_s": 1e3 / ms, "ms_per_token_eager": eager_ms,
             "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "steps": steps, "warmup": warmup,
@@ -295,7 +305,10 @@ def main():
         sys.exit(2)
     if args.decode_only:
         log("decode leg only")
-        print(json.dumps({"decode": decode_leg(args.decode_steps, 3)}), flush=True)
+        print(json.dumps({"decode": decode_leg(args.decode_steps, 3),
+                          "decode_stacked": decode_leg(args.decode_steps, 3, sublayers=DECODE_STACKED,
+                                                       name="llama2_7b_linear_stack_qkv_gateup")}),
+              flush=True)
         return
     import torch
     import post_quantization_02_amd as kq
@@ -446,6 +459,8 @@ def main():
     if not args.no_decode:
         log("decode leg")
         out["decode"] = decode_leg(args.decode_steps, 3)
+        out["decode_stacked"] = decode_leg(args.decode_steps, 3, sublayers=DECODE_STACKED,
+                                           name="llama2_7b_linear_stack_qkv_gateup")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(w, X, G, W, args.cpu_budget_s)

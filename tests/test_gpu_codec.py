@@ -143,6 +143,7 @@ def _check_y(y, want, tag):
     (33, 1000, 2, 0, 1, 8),             # ragged 2-bit rows, block 1 on the output side
     (7, 192, 8, 64, 1, 64),             # one code a byte, groups of 64, odd row count
     (1, 64, 4, 64, 1, 64),              # a single row and group
+    (40000, 1024, 4, 128, 64, 1024),    # tall: a workgroup walks 2-3 row groups
 ])
 def test_decode_matvec(m, n, bits, group, ko, ki):
     say("decode", m, n, bits, group, ko, ki)
@@ -198,7 +199,7 @@ def test_decode_of_an_oracle_quantized_layer():
 
 
 def test_decode_graph_replay():
-    """The three launches captured in a HIP graph: every replay, with new x
+    """The two launches captured in a HIP graph: every replay, with new x
     copied in and eager work in between, equals the eager call."""
     say("decode graph capture and replay")
     m, n, bits, group, ko, ki = 4096, 4096, 4, 128, 4096, 4096
@@ -230,3 +231,23 @@ def test_decode_graph_replay():
         _ = torch.ones(1024, device=DEV).sum()    # unrelated eager work between replays
         if i == 0:
             _check_y(y_static, c["want"], "replay 0")
+
+
+def test_decode_shared_workspace():
+    """Calls of different shapes, one after another on one workspace, each
+    against the oracle (nothing a call leaves in the workspace may leak into
+    the next)."""
+    say("decode: one workspace across shapes")
+    lib = kq.load()
+    shapes = [(4096, 4096, 4, 128, 4096, 4096), (11008, 4096, 4, 128, 256, 4096),
+              (300, 1000, 2, 0, 4, 8), (4096, 11008, 3, 0, 4096, 256)]
+    need = max(lib.kronq_decode_ws(m, n, b) for m, n, b, _, _, _ in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)   # non-zero garbage
+    for i, (m, n, bits, group, ko, ki) in enumerate(shapes):
+        say("  call", i, m, n, bits, group, ko, ki)
+        c = _decode_case(101 + i, m, n, bits, group, ko, ki)
+        y = kq.kronq_decode_matvec(_dev_u8(c["stored"]), n, bits, group, to_dev_f32(c["scales"]),
+                                   to_dev_f32(c["zeros"]), to_dev_f32(c["si"]), ki,
+                                   to_dev_f32(c["so"]), ko, to_dev_f32(c["sg"]),
+                                   to_dev_f32(c["x"]), ws=ws)
+        _check_y(y, c["want"], "call %d" % i)
