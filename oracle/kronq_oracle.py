@@ -24,6 +24,8 @@ hand-worked values (tests/test_oracle_pins.py); none is "parity unpinned".
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 # --------------------------------------------------------------------------
@@ -446,3 +448,78 @@ def decode_matvec(packed, bits, n, scales, zeros, group, in_signs, in_block, out
     yp = dequant(codes, scales, zeros, group, perm) @ xp
     y = fwht(yp.reshape(-1, out_block)).reshape(-1) / np.sqrt(out_block)
     return y * np.asarray(out_signs, dtype=np.float64) / np.asarray(sg, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Allocation variants.  [summary] Method: under the second-order
+# approximation a sublayer's expected loss is proportional to eps^2 tr(H), with
+# tr(H) = tr(H_X) tr(H_G) = s; higher bit-widths go to larger s.  [readme]
+# --inter_layer_mp N: upgrade the top-N sensitive sublayer *types* by +1 bit.
+# Readings:
+#  * pass-wise: visit the sublayers in score order (ties: lower index) and give
+#    each +1 bit when it is below bmax and fits the budget; repeat whole passes
+#    until a pass changes nothing.
+#  * marginal: eps(b) of a uniform grid halves with every bit, so eps^2 ~ 4^-b
+#    and one more bit lowers sublayer i's loss by s_i (4^-b - 4^-(b+1)), at a
+#    cost of n_i bits.  Repeatedly take, among the upgrades that fit, the one
+#    with the largest loss reduction per bit, s_i 4^-b / n_i (the common factor
+#    3/4 dropped; ties: lower index), until none fits.
+#  * types: a type's score is the sum of its sublayers' scores; the N types
+#    with the largest sums (ties: lower type id) get base + 1 bits, the others
+#    base bits.
+# --------------------------------------------------------------------------
+
+
+def _alloc_start(scores, n_params, bmin, bmax, budget_bits):
+    n_params = [int(x) for x in n_params]
+    used = bmin * sum(n_params)
+    if budget_bits < used or bmin > bmax:
+        raise ValueError("budget below the minimum allocation")
+    return n_params, used, [bmin] * len(scores)
+
+
+def allocate_bits_passwise(scores, n_params, bmin: int, bmax: int, budget_bits: int):
+    n_params, used, bits = _alloc_start(scores, n_params, bmin, bmax, budget_bits)
+    order = sorted(range(len(scores)), key=lambda i: (-float(scores[i]), i))
+    changed = True
+    while changed:
+        changed = False
+        for i in order:
+            if bits[i] < bmax and used + n_params[i] <= budget_bits:
+                bits[i] += 1
+                used += n_params[i]
+                changed = True
+    return bits
+
+
+def marginal_gain_per_bit(score: float, b: int, n: int) -> float:
+    """s 4^-b / n: the loss reduction per bit of raising a sublayer from b bits
+    (up to the constant 3/4), formed as ldexp then one division."""
+    return math.ldexp(float(score), -2 * b) / float(n)
+
+
+def allocate_bits_marginal(scores, n_params, bmin: int, bmax: int, budget_bits: int):
+    n_params, used, bits = _alloc_start(scores, n_params, bmin, bmax, budget_bits)
+    while True:
+        best = -1
+        for i in range(len(scores)):
+            if bits[i] >= bmax or used + n_params[i] > budget_bits:
+                continue
+            if best < 0 or (marginal_gain_per_bit(scores[i], bits[i], n_params[i]) >
+                            marginal_gain_per_bit(scores[best], bits[best], n_params[best])):
+                best = i
+        if best < 0:
+            return bits
+        bits[best] += 1
+        used += n_params[best]
+
+
+def allocate_types(scores, type_of, n_types: int, base_bits: int, n_upgrade: int):
+    """Per-sublayer bits: base + 1 for the sublayers of the n_upgrade types
+    with the largest summed scores, base for the rest."""
+    total = [0.0] * n_types
+    for s, t in zip(scores, type_of):
+        total[int(t)] += float(s)
+    ranked = sorted(range(n_types), key=lambda t: (-total[t], t))
+    up = set(ranked[:n_upgrade])
+    return [base_bits + (1 if int(t) in up else 0) for t in type_of]

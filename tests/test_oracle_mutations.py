@@ -55,6 +55,16 @@ MUTANTS = [
     ("unrotate rescale direction", "return B / np.asarray(sg, dtype=np.float64)[:, None]",
      "return B * np.asarray(sg, dtype=np.float64)[:, None]"),
     ("decode input transform normalization", "          / np.sqrt(in_block))", "          / in_block)"),
+    ("pass-wise stops after one pass", "                changed = True\n    return bits",
+     "                changed = False\n    return bits"),
+    ("marginal gain with eps ~ 2^-b/2", "return math.ldexp(float(score), -2 * b) / float(n)",
+     "return math.ldexp(float(score), -b) / float(n)"),
+    ("marginal gain ignores the cost", "return math.ldexp(float(score), -2 * b) / float(n)",
+     "return math.ldexp(float(score), -2 * b)"),
+    ("type score by the largest member", "        total[int(t)] += float(s)",
+     "        total[int(t)] = max(total[int(t)], float(s))"),
+    ("type ties to the higher id", "ranked = sorted(range(n_types), key=lambda t: (-total[t], t))",
+     "ranked = sorted(range(n_types), key=lambda t: (-total[t], -t))"),
 ]
 
 

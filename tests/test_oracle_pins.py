@@ -536,3 +536,84 @@ def test_decode_recovers_the_quantized_layer():
     Wback = O.unrotate(out["What"], si, 8, so, 4, out["sg"])
     np.testing.assert_allclose(y, Wback @ x, atol=1e-12)
     assert np.linalg.norm(Wback - W) < 0.2 * np.linalg.norm(W)
+
+
+# ---------------------------------------------------------------- allocation variants
+
+
+def test_passwise_closed_forms():
+    # equal sizes: after whole passes every sublayer has the same width, whatever the scores
+    sc = [0.3, 5.0, 1.0, 2.0]
+    n = [7, 7, 7, 7]
+    assert O.allocate_bits_passwise(sc, n, 2, 4, 3 * 28) == [3, 3, 3, 3]
+    assert O.allocate_bits_passwise(sc, n, 2, 4, 4 * 28) == [4, 4, 4, 4]   # needs a second pass
+    # one bit short of the second pass: the two most sensitive get their 4th bit... only one fits
+    assert O.allocate_bits_passwise(sc, n, 2, 4, 3 * 28 + 7) == [3, 4, 3, 3]
+
+
+def test_passwise_hand_example():
+    # scores (3, 1, 2), sizes (10, 10, 20), budget 2*40 + 35: pass one raises 0 (90) and 2 (110);
+    # sublayer 1 no longer fits (120), and neither does anything in pass two
+    assert O.allocate_bits_passwise([3, 1, 2], [10, 10, 20], 2, 4, 115) == [3, 2, 3]
+    # the greedy rule raises the top sublayer to the cap first
+    assert O.allocate_bits([3, 1, 2], [10, 10, 20], 2, 4, 115) == [4, 3, 2]
+
+
+def _loss(scores, bits):
+    # expected loss up to a constant: sum_i s_i eps(b_i)^2 with eps(b) = 2^-b
+    return sum(float(s) * 4.0 ** (-b) for s, b in zip(scores, bits))
+
+
+def test_marginal_hand_example_and_ties():
+    # gains per bit at 2 bits: 4/16 vs 1/16 -> sublayer 0; at 3 bits 4/64 = 1/16 ties
+    # with sublayer 1 at 2 bits -> the lower index, sublayer 0, again
+    assert O.allocate_bits_marginal([4, 1], [1, 1], 2, 4, 6) == [4, 2]
+    assert O.allocate_bits_marginal([4, 1], [1, 1], 2, 4, 7) == [4, 3]
+    # cost matters: s 4^-b / n equal for (1, n=1) and (4, n=4) -> lower index first;
+    # then sublayer 1 (4/16/4) beats sublayer 0 at 3 bits (1/64) when it fits ...
+    assert O.allocate_bits_marginal([1, 4], [1, 4], 2, 4, 2 * 5 + 1) == [3, 2]
+    assert O.allocate_bits_marginal([1, 4], [1, 4], 2, 4, 2 * 5 + 5) == [3, 3]
+    # ... and the smaller upgrade is taken when the better one no longer fits
+    assert O.allocate_bits_marginal([1, 4], [1, 4], 2, 4, 2 * 5 + 4) == [4, 2]
+
+
+def test_marginal_is_optimal_by_brute_force():
+    # with equal costs and diminishing returns the greedy choice is optimal:
+    # no allocation within the budget has a lower expected loss
+    import itertools
+    rng = np.random.default_rng(29)
+    for _ in range(40):
+        L = int(rng.integers(1, 5))
+        sc = list(rng.random(L) * 10 ** rng.uniform(-2, 2, L))
+        n = [3] * L
+        budget = int(rng.integers(2 * 3 * L, 4 * 3 * L + 1))
+        got = O.allocate_bits_marginal(sc, n, 2, 4, budget)
+        assert sum(b * 3 for b in got) <= budget
+        best = min(_loss(sc, c) for c in itertools.product(range(2, 5), repeat=L)
+                   if sum(b * 3 for b in c) <= budget)
+        assert _loss(sc, got) <= best * (1 + 1e-12)
+
+
+def test_types_hand_example():
+    # two layers x three types; type sums: t0 = 1 + 1 = 2, t1 = 5 + 0 = 5, t2 = 2 + 2.5 = 4.5.
+    # Ranked by sum: t1, t2, t0 (by the largest single score: t1, t2, t0 too, but
+    # t2 beats t1 by max of its layer-2 score below)
+    sc = [1.0, 5.0, 2.0, 1.0, 0.0, 2.5]
+    ty = [0, 1, 2, 0, 1, 2]
+    assert O.allocate_types(sc, ty, 3, 2, 1) == [2, 3, 2, 2, 3, 2]
+    assert O.allocate_types(sc, ty, 3, 2, 2) == [2, 3, 3, 2, 3, 3]
+    assert O.allocate_types(sc, ty, 3, 2, 0) == [2] * 6
+    assert O.allocate_types(sc, ty, 3, 2, 3) == [3] * 6
+    # summing, not the largest member: t1 = 3 + 3 = 6 beats t0 = 5 + 0 = 5
+    assert O.allocate_types([5.0, 3.0, 0.0, 3.0], [0, 1, 0, 1], 2, 2, 1) == [2, 3, 2, 3]
+    # ties between types go to the lower type id
+    assert O.allocate_types([1.0, 1.0], [1, 0], 2, 3, 1) == [3, 4]
+
+
+def test_types_one_sublayer_per_type_is_score_order():
+    rng = np.random.default_rng(31)
+    sc = list(rng.random(7))
+    for N in range(8):
+        bits = O.allocate_types(sc, list(range(7)), 7, 2, N)
+        top = set(sorted(range(7), key=lambda i: -sc[i])[:N])
+        assert bits == [3 if i in top else 2 for i in range(7)]
