@@ -269,6 +269,42 @@ kronq_status kronq_allocate_bits(int32_t L, const double* scores, const int64_t*
                                  int32_t bmin, int32_t bmax, int64_t budget_bits,
                                  int32_t* bits_out);
 
+/* ---------------------------------------------------------------------------
+ * Allocation variants (hyper.ai summary, Method: a sublayer's expected loss is
+ * proportional to eps^2 tr(H) with tr(H) = tr(H_X) tr(H_G), so higher
+ * bit-widths go to larger scores; GitHub README, --inter_layer_mp N: upgrade
+ * the top-N sensitive sublayer types by +1 bit).  Host only, pure,
+ * deterministic; arguments and errors as kronq_allocate_bits.
+ *
+ * kronq_allocate_bits_passwise: every sublayer starts at bmin; whole passes
+ *   over the sublayers in descending score order (ties: lower index) give each
+ *   +1 bit while it is below bmax and sum(bits * n_params) stays <= budget_bits,
+ *   until a pass changes nothing.
+ * kronq_allocate_bits_marginal: with eps(b) ~ 2^-b (a uniform grid's step
+ *   halves with each bit), one more bit lowers sublayer i's loss in proportion
+ *   to s_i 4^-b_i at a cost of n_params[i] bits.  Repeatedly apply, among the
+ *   upgrades that fit, the one with the largest ldexp(s_i, -2 b_i) / n_params[i]
+ *   (ties: lower index), until none fits.
+ * ------------------------------------------------------------------------- */
+kronq_status kronq_allocate_bits_passwise(int32_t L, const double* scores,
+                                          const int64_t* n_params, int32_t bmin, int32_t bmax,
+                                          int64_t budget_bits, int32_t* bits_out);
+kronq_status kronq_allocate_bits_marginal(int32_t L, const double* scores,
+                                          const int64_t* n_params, int32_t bmin, int32_t bmax,
+                                          int64_t budget_bits, int32_t* bits_out);
+
+/* Type-level allocation (GitHub README, --inter_layer_mp N).  Sublayer i has
+ * type type_of[i] in [0, n_types) (e.g. q, k, v, o, gate, up, down across all
+ * layers); a type's score is the sum of its sublayers' scores (added in
+ * ascending sublayer order).  The n_upgrade types with the largest sums (ties:
+ * lower type id) get base_bits + 1, the others base_bits; bits_out[i] is
+ * sublayer i's width.  KRONQ_EINVAL for L < 1, n_types < 1, a type outside
+ * [0, n_types), base_bits outside 1..63, n_upgrade outside [0, n_types] or a
+ * NaN score.  Host arrays. */
+kronq_status kronq_allocate_types(int32_t L, const double* scores, const int32_t* type_of,
+                                  int32_t n_types, int32_t base_bits, int32_t n_upgrade,
+                                  int32_t* bits_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_chol_inv", "kronq_gptq_ws", "kronq_gptq_quantize", "kronq_sensitivity",
            "kronq_allocate_bits", "kronq_biip_unrotate_ws", "kronq_biip_unrotate",
            "kronq_packed_row_bytes", "kronq_pack_codes", "kronq_unpack_codes", "kronq_decode_ws",
-           "kronq_decode_matvec")
+           "kronq_decode_matvec", "kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal",
+           "kronq_allocate_types")
 
 
 class KronqError(RuntimeError):
@@ -99,6 +100,11 @@ def load(path: str = LIB_PATH):
                                         ctypes.POINTER(Had), ctypes.POINTER(Had), vp, vp, vp, vp,
                                         sz, vp]
     lib.kronq_decode_matvec.restype = i32
+    for nm in ("kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal"):
+        getattr(lib, nm).argtypes = [i32, vp, vp, i32, i32, i64, vp]
+        getattr(lib, nm).restype = i32
+    lib.kronq_allocate_types.argtypes = [i32, vp, vp, i32, i32, i32, vp]
+    lib.kronq_allocate_types.restype = i32
     _lib = lib
     return lib
 
@@ -259,15 +265,38 @@ def kronq_sensitivity(HX: torch.Tensor, HG: torch.Tensor, out: torch.Tensor | No
     return out
 
 
-def kronq_allocate_bits(scores, n_params, bmin: int, bmax: int, budget_bits: int) -> list:
-    """Host-only greedy allocation (see include/kronq.h)."""
+def _allocate(name, scores, n_params, bmin, bmax, budget_bits):
     import numpy as np
     lib = load()
     sc = np.ascontiguousarray(scores, dtype=np.float64)
     npar = np.ascontiguousarray(n_params, dtype=np.int64)
     out = np.zeros(len(sc), dtype=np.int32)
-    _check(lib.kronq_allocate_bits(len(sc), sc.ctypes.data, npar.ctypes.data, bmin, bmax,
-                                   int(budget_bits), out.ctypes.data), "kronq_allocate_bits")
+    _check(getattr(lib, name)(len(sc), sc.ctypes.data, npar.ctypes.data, bmin, bmax,
+                              int(budget_bits), out.ctypes.data), name)
+    return [int(x) for x in out]
+
+
+def kronq_allocate_bits(scores, n_params, bmin: int, bmax: int, budget_bits: int) -> list:
+    """Host-only greedy allocation (see include/kronq.h)."""
+    return _allocate("kronq_allocate_bits", scores, n_params, bmin, bmax, budget_bits)
+
+
+def kronq_allocate_bits_passwise(scores, n_params, bmin: int, bmax: int, budget_bits: int) -> list:
+    return _allocate("kronq_allocate_bits_passwise", scores, n_params, bmin, bmax, budget_bits)
+
+
+def kronq_allocate_bits_marginal(scores, n_params, bmin: int, bmax: int, budget_bits: int) -> list:
+    return _allocate("kronq_allocate_bits_marginal", scores, n_params, bmin, bmax, budget_bits)
+
+
+def kronq_allocate_types(scores, type_of, n_types: int, base_bits: int, n_upgrade: int) -> list:
+    import numpy as np
+    lib = load()
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    ty = np.ascontiguousarray(type_of, dtype=np.int32)
+    out = np.zeros(len(sc), dtype=np.int32)
+    _check(lib.kronq_allocate_types(len(sc), sc.ctypes.data, ty.ctypes.data, n_types, base_bits,
+                                    n_upgrade, out.ctypes.data), "kronq_allocate_types")
     return [int(x) for x in out]
 
 

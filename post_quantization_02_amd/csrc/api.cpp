@@ -265,34 +265,130 @@ kronq_status kronq_sensitivity(const float* HX, int64_t n, int64_t ldhx, const f
   return trace_launch(HX, n, ldhx, HG, m, ldhg, out3, (hipStream_t)stream);
 }
 
-kronq_status kronq_allocate_bits(int32_t L, const double* scores, const int64_t* n_params,
-                                 int32_t bmin, int32_t bmax, int64_t budget_bits,
-                                 int32_t* bits_out) {
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the allocators; on success `total` = sum(n_params).
+kronq_status alloc_check(const char* fn, int32_t L, const double* scores, const int64_t* n_params,
+                         int32_t bmin, int32_t bmax, int64_t budget_bits, int32_t* bits_out,
+                         __int128& total) {
   if (L < 1 || !scores || !n_params || !bits_out)
-    return fail(KRONQ_EINVAL, "kronq_allocate_bits: bad arguments");
+    return fail(KRONQ_EINVAL, "%s: bad arguments", fn);
   if (bmin < 1 || bmax < bmin || bmax > 64)
-    return fail(KRONQ_EINVAL, "kronq_allocate_bits: bad bit range [%d, %d]", (int)bmin, (int)bmax);
-  // exact integer budget arithmetic (__int128 guards the products)
-  __int128 total = 0;
+    return fail(KRONQ_EINVAL, "%s: bad bit range [%d, %d]", fn, (int)bmin, (int)bmax);
+  total = 0;
   for (int32_t i = 0; i < L; ++i) {
-    if (n_params[i] < 1) return fail(KRONQ_EINVAL, "kronq_allocate_bits: n_params[%d] < 1", (int)i);
-    if (std::isnan(scores[i])) return fail(KRONQ_EINVAL, "kronq_allocate_bits: score %d is NaN", (int)i);
+    if (n_params[i] < 1) return fail(KRONQ_EINVAL, "%s: n_params[%d] < 1", fn, (int)i);
+    if (std::isnan(scores[i])) return fail(KRONQ_EINVAL, "%s: score %d is NaN", fn, (int)i);
     total += (__int128)n_params[i];
   }
-  __int128 used = total * bmin;
-  if ((__int128)budget_bits < used)
-    return fail(KRONQ_EINVAL, "kronq_allocate_bits: budget below bmin for every sublayer");
+  if ((__int128)budget_bits < total * bmin)
+    return fail(KRONQ_EINVAL, "%s: budget below bmin for every sublayer", fn);
+  return KRONQ_OK;
+}
+
+// sublayers by descending score, ties to the lower index
+std::vector<int32_t> score_order(int32_t L, const double* scores) {
   std::vector<int32_t> order((size_t)L);
   for (int32_t i = 0; i < L; ++i) order[(size_t)i] = i;
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t a, int32_t b) { return scores[a] > scores[b]; });
+  return order;
+}
+
+}  // namespace
+
+extern "C" {
+
+kronq_status kronq_allocate_bits(int32_t L, const double* scores, const int64_t* n_params,
+                                 int32_t bmin, int32_t bmax, int64_t budget_bits,
+                                 int32_t* bits_out) {
+  __int128 total;
+  kronq_status st = alloc_check("kronq_allocate_bits", L, scores, n_params, bmin, bmax,
+                                budget_bits, bits_out, total);
+  if (st) return st;
+  __int128 used = total * bmin;
   for (int32_t i = 0; i < L; ++i) bits_out[i] = bmin;
-  for (int32_t i : order) {
+  for (int32_t i : score_order(L, scores)) {
     while (bits_out[i] < bmax && used + (__int128)n_params[i] <= (__int128)budget_bits) {
       bits_out[i] += 1;
       used += n_params[i];
     }
   }
+  return KRONQ_OK;
+}
+
+kronq_status kronq_allocate_bits_passwise(int32_t L, const double* scores,
+                                          const int64_t* n_params, int32_t bmin, int32_t bmax,
+                                          int64_t budget_bits, int32_t* bits_out) {
+  __int128 total;
+  kronq_status st = alloc_check("kronq_allocate_bits_passwise", L, scores, n_params, bmin, bmax,
+                                budget_bits, bits_out, total);
+  if (st) return st;
+  __int128 used = total * bmin;
+  for (int32_t i = 0; i < L; ++i) bits_out[i] = bmin;
+  const std::vector<int32_t> order = score_order(L, scores);
+  for (bool changed = true; changed;) {
+    changed = false;
+    for (int32_t i : order)
+      if (bits_out[i] < bmax && used + (__int128)n_params[i] <= (__int128)budget_bits) {
+        bits_out[i] += 1;
+        used += n_params[i];
+        changed = true;
+      }
+  }
+  return KRONQ_OK;
+}
+
+kronq_status kronq_allocate_bits_marginal(int32_t L, const double* scores,
+                                          const int64_t* n_params, int32_t bmin, int32_t bmax,
+                                          int64_t budget_bits, int32_t* bits_out) {
+  __int128 total;
+  kronq_status st = alloc_check("kronq_allocate_bits_marginal", L, scores, n_params, bmin, bmax,
+                                budget_bits, bits_out, total);
+  if (st) return st;
+  __int128 used = total * bmin;
+  for (int32_t i = 0; i < L; ++i) bits_out[i] = bmin;
+  // loss reduction per bit of one more bit: s 4^-b / n (ldexp is exact, one rounding in the divide)
+  auto gain = [&](int32_t i) { return std::ldexp(scores[i], -2 * bits_out[i]) / (double)n_params[i]; };
+  for (;;) {
+    int32_t best = -1;
+    double gbest = 0.0;
+    for (int32_t i = 0; i < L; ++i) {
+      if (bits_out[i] >= bmax || used + (__int128)n_params[i] > (__int128)budget_bits) continue;
+      const double gi = gain(i);
+      if (best < 0 || gi > gbest) {
+        best = i;
+        gbest = gi;
+      }
+    }
+    if (best < 0) return KRONQ_OK;
+    bits_out[best] += 1;
+    used += n_params[best];
+  }
+}
+
+kronq_status kronq_allocate_types(int32_t L, const double* scores, const int32_t* type_of,
+                                  int32_t n_types, int32_t base_bits, int32_t n_upgrade,
+                                  int32_t* bits_out) {
+  if (L < 1 || !scores || !type_of || !bits_out || n_types < 1)
+    return fail(KRONQ_EINVAL, "kronq_allocate_types: bad arguments");
+  if (base_bits < 1 || base_bits > 63 || n_upgrade < 0 || n_upgrade > n_types)
+    return fail(KRONQ_EINVAL, "kronq_allocate_types: base_bits %d / n_upgrade %d out of range",
+                (int)base_bits, (int)n_upgrade);
+  std::vector<double> sum((size_t)n_types, 0.0);
+  for (int32_t i = 0; i < L; ++i) {
+    if (type_of[i] < 0 || type_of[i] >= n_types)
+      return fail(KRONQ_EINVAL, "kronq_allocate_types: type_of[%d] = %d outside [0, %d)", (int)i,
+                  (int)type_of[i], (int)n_types);
+    if (std::isnan(scores[i])) return fail(KRONQ_EINVAL, "kronq_allocate_types: score %d is NaN", (int)i);
+    sum[(size_t)type_of[i]] += scores[i];   // ascending sublayer order
+  }
+  const std::vector<int32_t> ranked = score_order(n_types, sum.data());
+  std::vector<char> up((size_t)n_types, 0);
+  for (int32_t k = 0; k < n_upgrade; ++k) up[(size_t)ranked[(size_t)k]] = 1;
+  for (int32_t i = 0; i < L; ++i) bits_out[i] = base_bits + (up[(size_t)type_of[i]] ? 1 : 0);
   return KRONQ_OK;
 }
 
