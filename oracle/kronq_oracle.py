@@ -523,3 +523,39 @@ def allocate_types(scores, type_of, n_types: int, base_bits: int, n_upgrade: int
     ranked = sorted(range(n_types), key=lambda t: (-total[t], t))
     up = set(ranked[:n_upgrade])
     return [base_bits + (1 if int(t) in up else 0) for t in type_of]
+
+
+# --------------------------------------------------------------------------
+# BiIP variants and diagnostics.  [readme] --incoh_mode {full, no_rescale,
+# su_only, sv_only} (component ablation); [review] Figure 2: CV_in and CV_out
+# are the coefficients of variation of the column and row norms of W, and
+# incoherence on the input side alone leaves CV_out nearly unchanged while
+# BiIP lowers both.
+# Readings: full = S_G, U and V; no_rescale = U and V without S_G (alpha 0);
+# su_only = the output side alone (S_G and U, V = I); sv_only = the input side
+# alone (V, with U = I and no S_G).  An identity side is block 1 with all-one
+# signs.  CV = population standard deviation / mean.
+# --------------------------------------------------------------------------
+
+INCOH_MODES = ("full", "no_rescale", "su_only", "sv_only")
+
+
+def biip_mode(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha, mode: str):
+    m, n = np.asarray(W).shape
+    if mode == "full":
+        return biip(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha)
+    if mode == "no_rescale":
+        return biip(W, HX, HG, in_signs, in_block, out_signs, out_block, 0.0)
+    if mode == "su_only":
+        return biip(W, HX, HG, np.ones(n), 1, out_signs, out_block, alpha)
+    if mode == "sv_only":
+        return biip(W, HX, HG, in_signs, in_block, np.ones(m), 1, 0.0)
+    raise ValueError("unknown incoherence mode %r" % (mode,))
+
+
+def weight_cv(W):
+    """(CV_in, CV_out) of the column norms and the row norms of W."""
+    W = np.asarray(W, dtype=np.float64)
+    col = np.sqrt(np.sum(W * W, axis=0))
+    row = np.sqrt(np.sum(W * W, axis=1))
+    return float(np.std(col) / np.mean(col)), float(np.std(row) / np.mean(row))

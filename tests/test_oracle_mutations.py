@@ -63,6 +63,14 @@ MUTANTS = [
      "return math.ldexp(float(score), -2 * b)"),
     ("type score by the largest member", "        total[int(t)] += float(s)",
      "        total[int(t)] = max(total[int(t)], float(s))"),
+    ("CV with the sample deviation", "return float(np.std(col) / np.mean(col)), float(np.std(row) / np.mean(row))",
+     "return float(np.std(col, ddof=1) / np.mean(col)), float(np.std(row, ddof=1) / np.mean(row))"),
+    ("CV columns and rows swapped", "    col = np.sqrt(np.sum(W * W, axis=0))\n    row = np.sqrt(np.sum(W * W, axis=1))",
+     "    col = np.sqrt(np.sum(W * W, axis=1))\n    row = np.sqrt(np.sum(W * W, axis=0))"),
+    ("su_only keeps the input side", "return biip(W, HX, HG, np.ones(n), 1, out_signs, out_block, alpha)",
+     "return biip(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha)"),
+    ("sv_only keeps the rescale", "return biip(W, HX, HG, in_signs, in_block, np.ones(m), 1, 0.0)",
+     "return biip(W, HX, HG, in_signs, in_block, np.ones(m), 1, alpha)"),
     ("type ties to the higher id", "ranked = sorted(range(n_types), key=lambda t: (-total[t], t))",
      "ranked = sorted(range(n_types), key=lambda t: (-total[t], -t))"),
 ]

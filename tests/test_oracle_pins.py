@@ -11,6 +11,8 @@ import itertools
 import json
 import os
 
+import math
+
 import numpy as np
 import pytest
 
@@ -617,3 +619,71 @@ def test_types_one_sublayer_per_type_is_score_order():
         bits = O.allocate_types(sc, list(range(7)), 7, 2, N)
         top = set(sorted(range(7), key=lambda i: -sc[i])[:N])
         assert bits == [3 if i in top else 2 for i in range(7)]
+
+
+# ---------------------------------------------------------------- BiIP variants and diagnostics
+
+
+def _cv_by_definition(v):
+    k = len(v)
+    mu = sum(v) / k
+    return math.sqrt(sum((x - mu) ** 2 for x in v) / k) / mu
+
+
+def test_weight_cv_by_definition_and_closed_forms():
+    rng = np.random.default_rng(53)
+    W = rng.standard_normal((5, 7)) * rng.uniform(0.1, 3, 7)
+    cols = [math.sqrt(sum(W[i, j] ** 2 for i in range(5))) for j in range(7)]
+    rows = [math.sqrt(sum(W[i, j] ** 2 for j in range(7))) for i in range(5)]
+    cin, cout = O.weight_cv(W)
+    assert abs(cin - _cv_by_definition(cols)) <= 1e-12
+    assert abs(cout - _cv_by_definition(rows)) <= 1e-12
+    # equal column norms -> CV_in = 0; two column norms a, b, half each -> |a - b| / (a + b)
+    H = O.hadamard_matrix(8)
+    assert abs(O.weight_cv(H)[0]) <= 1e-15 and abs(O.weight_cv(H)[1]) <= 1e-15
+    A = np.ones((4, 6))
+    A[:, :3] *= 3.0
+    assert abs(O.weight_cv(A)[0] - (3 - 1) / (3 + 1)) <= 1e-15
+    # scale invariance
+    np.testing.assert_allclose(O.weight_cv(7.5 * W), O.weight_cv(W), rtol=1e-13)
+
+
+def test_weight_cv_rotation_invariances():
+    # an input-side rotation keeps every row norm (CV_out exactly), an
+    # output-side rotation every column norm (CV_in exactly)
+    rng = np.random.default_rng(59)
+    W = rng.standard_normal((16, 32)) * rng.uniform(0.1, 5, 32)[None, :] * rng.uniform(0.1, 5, 16)[:, None]
+    V = O.rotation_matrix(32, 8, rng.choice([-1.0, 1.0], 32))
+    U = O.rotation_matrix(16, 16, rng.choice([-1.0, 1.0], 16))
+    cin, cout = O.weight_cv(W)
+    assert abs(O.weight_cv(W @ V.T)[1] - cout) <= 1e-12
+    assert abs(O.weight_cv(U @ W)[0] - cin) <= 1e-12
+    # and the rotations do change the other one on this matrix
+    assert abs(O.weight_cv(W @ V.T)[0] - cin) > 1e-3
+    assert abs(O.weight_cv(U @ W)[1] - cout) > 1e-3
+
+
+def test_biip_modes_against_explicit_matrices():
+    rng = np.random.default_rng(61)
+    m, n, ko, ki, alpha = 8, 12, 4, 4, 0.25
+    W = rng.standard_normal((m, n))
+    A = rng.standard_normal((3 * n, n))
+    B = rng.standard_normal((3 * m, m)) * rng.uniform(0.1, 4, m)
+    HX, HG = A.T @ A, B.T @ B
+    si, so = rng.choice([-1.0, 1.0], n), rng.choice([-1.0, 1.0], m)
+    U = O.rotation_matrix(m, ko, so)
+    V = O.rotation_matrix(n, ki, si)
+    S = np.diag(np.diag(HG) ** alpha)
+    Si = np.linalg.inv(S)
+    want = {
+        "full": (U @ S @ W @ V.T, V @ HX @ V.T, U @ Si @ HG @ Si @ U.T),
+        "no_rescale": (U @ W @ V.T, V @ HX @ V.T, U @ HG @ U.T),
+        "su_only": (U @ S @ W, HX, U @ Si @ HG @ Si @ U.T),
+        "sv_only": (W @ V.T, V @ HX @ V.T, HG),
+    }
+    for mode in O.INCOH_MODES:
+        Wp, HXp, HGp, s = O.biip_mode(W, HX, HG, si, ki, so, ko, alpha, mode)
+        for got, exp in zip((Wp, HXp, HGp), want[mode]):
+            np.testing.assert_allclose(got, exp, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.biip_mode(W, HX, HG, si, ki, so, ko, alpha, "both")
