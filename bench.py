@@ -456,6 +456,26 @@ def main():
         "input_gen_s": t_gen,
         "h2d_s": t_h2d,
     }
+    # CV_in / CV_out of W before and after BiIP, and the diagnostic's own rate
+    # (one read of W: 4 m n algorithmic bytes per call)
+    cv_out = torch.empty(2, dtype=torch.float64, device=dev)
+    ws_cv = torch.empty(lib.kronq_weight_cv_ws(m, n), dtype=torch.uint8, device=dev)
+    cv_before = [float(v) for v in kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv).cpu()]
+    cv_after = [float(v) for v in kq.kronq_weight_cv(Wk, out=cv_out, ws=ws_cv).cpu()]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv)
+    e0.record(stream)
+    for _ in range(20):
+        kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cv_ms = e0.elapsed_time(e1) / 20
+    out["weight_cv"] = {"cv_in_before": cv_before[0], "cv_out_before": cv_before[1],
+                        "cv_in_after_biip": cv_after[0], "cv_out_after_biip": cv_after[1],
+                        "ms_per_call": cv_ms, "gbs": 4.0 * m * n / (cv_ms * 1e-3) / 1e9,
+                        "frac_hbm_peak": 4.0 * m * n / (cv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if not args.no_decode:
         log("decode leg")
         out["decode"] = decode_leg(args.decode_steps, 3)

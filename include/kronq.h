@@ -54,7 +54,9 @@ typedef int32_t kronq_status;
 /* One side of a randomized (block) Hadamard transform T = (I_b (x) H_block)
  * diag(signs) / sqrt(block) on a dimension dim = b * block; block is a power of
  * two (Sylvester order) between 1 and 32768; signs is a device array of dim
- * floats, each +1.0f or -1.0f (the random draw is the caller's input). */
+ * floats, each +1.0f or -1.0f (the random draw is the caller's input).
+ * block = 1 with signs = NULL is the identity: a side left unprocessed, as in
+ * the incoherence ablations (GitHub README, --incoh_mode su_only / sv_only). */
 typedef struct {
   int64_t dim;
   int64_t block;
@@ -187,6 +189,25 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
                                  const kronq_qcfg* q, uint8_t* codes, float* scales,
                                  float* zeros, float* What, float* pre_round, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Weight diagnostic of incoherence processing (Pith review, Figure 2: CV_in and
+ * CV_out are the coefficients of variation of the column norms and of the row
+ * norms of W).
+ *   out2[0] = CV_in  = std(||W[:, j]||) / mean(||W[:, j]||)   over the n columns
+ *   out2[1] = CV_out = std(||W[i, :]||) / mean(||W[i, :]||)   over the m rows
+ * with the population standard deviation; norms from fp32 squares summed in
+ * fp32 within 16 x 1024 tiles and fp64 across tiles, statistics in fp64.  NaN
+ * when every norm is zero.
+ * W        : m x n fp32 device, leading dimension ldw >= n (read only).
+ * out2     : device, 2 doubles.
+ * col_norms, row_norms : device n and m floats receiving the norms, or NULL.
+ * ws       : kronq_weight_cv_ws(m, n) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_weight_cv_ws(int64_t m, int64_t n);
+kronq_status kronq_weight_cv(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
+                             float* col_norms, float* row_norms, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------
  * Deploy codec (GitHub README of the KronQ release: int4 / int2 weights are

@@ -27,7 +27,7 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_allocate_bits", "kronq_biip_unrotate_ws", "kronq_biip_unrotate",
            "kronq_packed_row_bytes", "kronq_pack_codes", "kronq_unpack_codes", "kronq_decode_ws",
            "kronq_decode_matvec", "kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal",
-           "kronq_allocate_types")
+           "kronq_allocate_types", "kronq_weight_cv_ws", "kronq_weight_cv")
 
 
 class KronqError(RuntimeError):
@@ -105,6 +105,10 @@ def load(path: str = LIB_PATH):
         getattr(lib, nm).restype = i32
     lib.kronq_allocate_types.argtypes = [i32, vp, vp, i32, i32, i32, vp]
     lib.kronq_allocate_types.restype = i32
+    lib.kronq_weight_cv_ws.argtypes = [i64, i64]
+    lib.kronq_weight_cv_ws.restype = sz
+    lib.kronq_weight_cv.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.kronq_weight_cv.restype = i32
     _lib = lib
     return lib
 
@@ -184,7 +188,7 @@ def kronq_biip_rotate(W: torch.Tensor, HX: torch.Tensor | None, HG: torch.Tensor
     for t, nm in ((HX, "HX"), (HG, "HG"), (sg, "sg"), (in_signs, "in_signs"), (out_signs, "out_signs")):
         if t is not None:
             _dev(t, nm, torch.float32)
-    hin = Had(n, in_block, _ptr(in_signs))
+    hin = Had(n, in_block, _ptr(in_signs))     # signs None with block 1: identity side
     hout = Had(m, out_block, _ptr(out_signs))
     need = lib.kronq_biip_ws(m, n)
     if ws is None or ws.numel() < need:
@@ -379,3 +383,39 @@ def kronq_decode_matvec(codes: torch.Tensor, n: int, bits: int, group: int, scal
                                    _ptr(sg), _ptr(x), _ptr(y), _ptr(ws), need, _stream(stream)),
            "kronq_decode_matvec")
     return y
+
+
+INCOH_MODES = ("full", "no_rescale", "su_only", "sv_only")
+
+
+def kronq_biip_rotate_mode(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha, mode="full",
+                           sg=None, stream=None, ws=None):
+    """kronq_biip_rotate for an incoherence mode: full (S_G, U, V), no_rescale
+    (U, V), su_only (S_G and U; V = I), sv_only (V; U = I, no S_G).  An unused
+    side is passed as the identity (block 1, no signs)."""
+    if mode not in INCOH_MODES:
+        raise ValueError("unknown incoherence mode %r" % (mode,))
+    if mode == "no_rescale":
+        alpha = 0.0
+    if mode == "su_only":
+        in_signs, in_block = None, 1
+    if mode == "sv_only":
+        out_signs, out_block, alpha = None, 1, 0.0
+    return kronq_biip_rotate(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha, sg=sg,
+                             stream=stream, ws=ws)
+
+
+def kronq_weight_cv(W: torch.Tensor, col_norms=None, row_norms=None, out=None, stream=None,
+                    ws=None) -> torch.Tensor:
+    """Device tensor of 2 doubles: CV_in (column norms), CV_out (row norms)."""
+    lib = load()
+    _dev(W, "W", torch.float32)
+    m, n = W.shape
+    if out is None:
+        out = torch.empty(2, dtype=torch.float64, device=W.device)
+    need = lib.kronq_weight_cv_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, W.device)
+    _check(lib.kronq_weight_cv(_ptr(W), m, n, _ld(W), _ptr(out), _ptr(col_norms), _ptr(row_norms),
+                               _ptr(ws), need, _stream(stream)), "kronq_weight_cv")
+    return out

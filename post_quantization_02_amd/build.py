@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkronq.so")
 
-SOURCES = ["api.cpp", "gram.hip", "fwht.hip", "chol.hip", "gptq.hip", "trace.hip", "codec.hip"]
+SOURCES = ["api.cpp", "gram.hip", "fwht.hip", "chol.hip", "gptq.hip", "trace.hip", "codec.hip", "diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -45,7 +45,8 @@ static kronq_status check_had(const kronq_had* h, int64_t dim, const char* side)
   if (!pow2(h->block) || h->block > 32768 || dim % h->block)
     return fail(KRONQ_EINVAL, "%s Hadamard block %lld must be a power of two <= 32768 dividing %lld",
                 side, (long long)h->block, (long long)dim);
-  if (!h->signs) return fail(KRONQ_EINVAL, "%s Hadamard signs are NULL", side);
+  if (!h->signs && h->block != 1)
+    return fail(KRONQ_EINVAL, "%s Hadamard signs are NULL (allowed only with block 1: identity)", side);
   return KRONQ_OK;
 }
 
@@ -190,6 +191,22 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
     return fail(KRONQ_EWORKSPACE, "kronq_gptq_quantize: workspace %zu < %zu bytes", ws_bytes, need);
   return gptq_launch(W, m, n, ldw, R, ldr, perm, q->bits, q->group > 0 ? q->group : 0, codes,
                      scales, zeros, What, pre_round, ws, ws_bytes, (hipStream_t)stream);
+}
+
+size_t kronq_weight_cv_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return cv_ws_bytes(m, n);
+}
+
+kronq_status kronq_weight_cv(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
+                             float* col_norms, float* row_norms, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!W || !out2) return fail(KRONQ_EINVAL, "kronq_weight_cv: NULL pointer");
+  if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "kronq_weight_cv: bad shape");
+  size_t need = cv_ws_bytes(m, n);
+  if (ws_bytes < need || !ws)
+    return fail(KRONQ_EWORKSPACE, "kronq_weight_cv: workspace %zu < %zu bytes", ws_bytes, need);
+  return cv_launch(W, m, n, ldw, out2, col_norms, row_norms, ws, (hipStream_t)stream);
 }
 
 int64_t kronq_packed_row_bytes(int64_t n, int32_t bits) {

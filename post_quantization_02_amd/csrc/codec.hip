@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(NTY) decode_yout(const float* __restrict__ par
     const int64_t r = base + t + NTY * j;
     const bool in = (t + NTY * j < T) && r < m;
     const int64_t rr = in ? r : 0;
-    const float a = sgn[rr], b = sg ? sg[rr] : 1.f;
+    const float a = sgn ? sgn[rr] : 1.f, b = sg ? sg[rr] : 1.f;   // NULL signs: identity side
     f[j] = nrm * a / b;
     v[j] = 0.f;
   }
@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(NTY) decode_yout(const float* __restrict__ par
   }
   for (int e = t + NTY * EMAX; e < T; e += NTY) {
     const int64_t r = base + e;
-    if (r < m) y[r] = s[pad(e)] * (nrm * sgn[r] / (sg ? sg[r] : 1.f));
+    if (r < m) y[r] = s[pad(e)] * (nrm * (sgn ? sgn[r] : 1.f) / (sg ? sg[r] : 1.f));
   }
 }
 
@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(NT) decode_gemv(GemvParams p) {
     const int64_t c = tb + t + NT * j;
     const bool in = (j < ept) && (c < p.n);
     const int64_t cc = in ? c : 0;
-    const float a = p.x[cc], b = p.sgn_in[cc];
+    const float a = p.x[cc], b = p.sgn_in ? p.sgn_in[cc] : 1.f;   // NULL signs: identity side
     xv[j] = in ? a : 0.f;
     sv[j] = in ? b : 0.f;
   }
@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(NT) decode_gemv(GemvParams p) {
     if (j < ept) tile[pad(t + NT * j)] = xv[j];
   for (int j = EMAX; j < ept; ++j) {
     const int e = t + NT * j;
-    tile[pad(e)] = (tb + e < p.n) ? p.x[tb + e] * p.sgn_in[tb + e] : 0.f;
+    tile[pad(e)] = (tb + e < p.n) ? p.x[tb + e] * (p.sgn_in ? p.sgn_in[tb + e] : 1.f) : 0.f;
   }
   __syncthreads();
   lds_wht_low_bits<NT>(tile, p.lg_tile, regs ? min(p.lg_kin, 8) : p.lg_kin);

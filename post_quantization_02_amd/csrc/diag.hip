@@ -1,0 +1,203 @@
+// Weight diagnostics of incoherence processing (Pith review, Figure 2: CV_in
+// and CV_out, the coefficients of variation of the column norms and of the
+// row norms of W; incoherence on the input side alone leaves the row norms,
+// and so CV_out, in place, while BiIP lowers both).
+//
+//   cv_partial  one workgroup per tile of 16 rows x 1024 columns: a thread
+//               holds a float4 of each of the 16 rows (16 loads in flight),
+//               squares and sums them down its columns and, through DPP and
+//               LDS, along each row.  Partial column sums per row block and
+//               partial row sums per column block go to the workspace.  This
+//               pass reads W once and carries all of its bytes (HBM-bound).
+//   cv_norms    sums the partials in fp64 and takes square roots: the n column
+//               norms and the m row norms.
+//   cv_final    one workgroup: mean and population standard deviation of each
+//               set of norms in fp64 (two passes over the norms), CV = std /
+//               mean.
+#include <cmath>
+
+#include "kronq_internal.h"
+
+namespace kronq {
+namespace {
+
+constexpr int NT = 256;
+constexpr int RB = 16;     // rows of a tile
+constexpr int CB = 1024;   // columns of a tile (a float4 per thread)
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                   CTRL, ROWS, 0xF, false));
+}
+
+// wave sum in lane 63 (quad and row butterflies, then the row broadcasts)
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  v = dpp_add<0x142, 0xA>(v);
+  v = dpp_add<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Loads read clamped, always valid addresses and discard what lies outside the
+// matrix with a select (VEC: n and ldw multiples of 4, W 16-byte aligned).
+template <bool VEC>
+__global__ void __launch_bounds__(NT) cv_partial(const float* __restrict__ W, int64_t m, int64_t n,
+                                                 int64_t ldw, int64_t nrb, float* __restrict__ colpart,
+                                                 float* __restrict__ rowpart) {
+  __shared__ float red[NT / 64][RB];
+  const int64_t rb = blockIdx.x % nrb, cb = blockIdx.x / nrb;
+  const int64_t r0 = rb * RB;
+  const int64_t c0 = cb * CB + 4 * threadIdx.x;
+  float4 x[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int64_t row = r0 + r;
+    const int64_t rr = row < m ? row : 0;
+    if (VEC) {
+      const int64_t cc = c0 < n ? c0 : 0;
+      const float4 v = *reinterpret_cast<const float4*>(W + rr * ldw + cc);
+      const bool in = row < m && c0 < n;
+      x[r] = in ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + j;
+        const float v = W[rr * ldw + (c < n ? c : 0)];
+        e[j] = (row < m && c < n) ? v : 0.f;
+      }
+      x[r] = make_float4(e[0], e[1], e[2], e[3]);
+    }
+  }
+  float4 col = make_float4(0.f, 0.f, 0.f, 0.f);
+  float rowsq[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const float4 v = x[r];
+    col.x = fmaf(v.x, v.x, col.x);
+    col.y = fmaf(v.y, v.y, col.y);
+    col.z = fmaf(v.z, v.z, col.z);
+    col.w = fmaf(v.w, v.w, col.w);
+    rowsq[r] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
+  }
+  const float cv[4] = {col.x, col.y, col.z, col.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (c0 + j < n) colpart[rb * n + c0 + j] = cv[j];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const float t = wave_total(rowsq[r]);
+    if (lane == 0) red[wave][r] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < RB && r0 + threadIdx.x < m) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) t += red[w][threadIdx.x];
+    rowpart[cb * m + r0 + threadIdx.x] = t;
+  }
+}
+
+// norms[j] = sqrt(sum_b part[b * len + j]) for j < len, summed in fp64
+__global__ void __launch_bounds__(NT) cv_norms(const float* __restrict__ colpart, int64_t nrb,
+                                               int64_t n, const float* __restrict__ rowpart,
+                                               int64_t ncb, int64_t m, float* __restrict__ coln,
+                                               float* __restrict__ rown) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i < n) {
+    double s = 0.0;
+    for (int64_t b = 0; b < nrb; ++b) s += colpart[b * n + i];
+    coln[i] = (float)std::sqrt(s);
+  } else if (i < n + m) {
+    const int64_t r = i - n;
+    double s = 0.0;
+    for (int64_t b = 0; b < ncb; ++b) s += rowpart[b * m + r];
+    rown[r] = (float)std::sqrt(s);
+  }
+}
+
+__device__ double block_sum(double v, double* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;
+}
+
+// out[0] = CV of coln (n values), out[1] = CV of rown (m values)
+__global__ void __launch_bounds__(1024) cv_final(const float* __restrict__ coln, int64_t n,
+                                                 const float* __restrict__ rown, int64_t m,
+                                                 double* __restrict__ out) {
+  __shared__ double red[16];
+  for (int k = 0; k < 2; ++k) {
+    const float* v = k ? rown : coln;
+    const int64_t len = k ? m : n;
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < len; i += blockDim.x) s += v[i];
+    const double mean = block_sum(s, red) / (double)len;
+    double q = 0.0;
+    for (int64_t i = threadIdx.x; i < len; i += blockDim.x) {
+      const double d = (double)v[i] - mean;
+      q += d * d;
+    }
+    const double var = block_sum(q, red) / (double)len;
+    if (threadIdx.x == 0) out[k] = std::sqrt(var) / mean;
+  }
+}
+
+struct CvLayout {
+  int64_t nrb, ncb;
+  size_t colpart, rowpart, coln, rown, total;   // byte offsets and size
+};
+
+CvLayout cv_layout(int64_t m, int64_t n) {
+  CvLayout L{};
+  L.nrb = (m + RB - 1) / RB;
+  L.ncb = (n + CB - 1) / CB;
+  L.colpart = 0;
+  L.rowpart = align_up((size_t)L.nrb * (size_t)n * sizeof(float), 256);
+  L.coln = L.rowpart + align_up((size_t)L.ncb * (size_t)m * sizeof(float), 256);
+  L.rown = L.coln + align_up((size_t)n * sizeof(float), 256);
+  L.total = L.rown + align_up((size_t)m * sizeof(float), 256);
+  return L;
+}
+
+}  // namespace
+
+size_t cv_ws_bytes(int64_t m, int64_t n) { return cv_layout(m, n).total; }
+
+kronq_status cv_launch(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
+                       float* col_norms, float* row_norms, void* ws, hipStream_t s) {
+  const CvLayout L = cv_layout(m, n);
+  char* base = static_cast<char*>(ws);
+  float* colpart = reinterpret_cast<float*>(base + L.colpart);
+  float* rowpart = reinterpret_cast<float*>(base + L.rowpart);
+  float* coln = col_norms ? col_norms : reinterpret_cast<float*>(base + L.coln);
+  float* rown = row_norms ? row_norms : reinterpret_cast<float*>(base + L.rown);
+  const int64_t tiles = L.nrb * L.ncb;
+  if (tiles > 0x7fffffff) return fail(KRONQ_EINVAL, "kronq_weight_cv: matrix too large");
+  const bool vec = n % 4 == 0 && ldw % 4 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(cv_partial<true>, dim3((unsigned)tiles), dim3(NT), 0, s, W, m, n, ldw, L.nrb,
+                       colpart, rowpart);
+  else
+    hipLaunchKernelGGL(cv_partial<false>, dim3((unsigned)tiles), dim3(NT), 0, s, W, m, n, ldw,
+                       L.nrb, colpart, rowpart);
+  KQ_LAUNCHED("cv_partial");
+  hipLaunchKernelGGL(cv_norms, dim3((unsigned)((n + m + NT - 1) / NT)), dim3(NT), 0, s, colpart,
+                     L.nrb, n, rowpart, L.ncb, m, coln, rown);
+  KQ_LAUNCHED("cv_norms");
+  hipLaunchKernelGGL(cv_final, dim3(1), dim3(1024), 0, s, coln, n, rown, m, out2);
+  KQ_LAUNCHED("cv_final");
+  return KRONQ_OK;
+}
+
+}  // namespace kronq

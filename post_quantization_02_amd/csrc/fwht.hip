@@ -13,9 +13,10 @@
 // Sylvester order, the mixing splits into factors that act on separate bits
 // of the (row, column) index and commute, so the whole 2-D transform runs in
 // two read-modify-write passes over HBM:
-//   pass 1: a tile of R1 consecutive rows x one column block (kc columns);
-//           applies Dr, Dc, the full column-side transform and the low R1 part
-//           of the row-side transform (R1 * kc <= tile size);
+//   pass 1: a tile of R1 consecutive rows x C1 columns (C1 = kc, or a few
+//           whole column blocks so that a tile row spans at least 64 bytes when
+//           kc is small); applies Dr, Dc, the full column-side transform and
+//           the low R1 part of the row-side transform (R1 * C1 <= tile size);
 //   pass 2: a tile of kr/R1 rows at stride R1 x a strip of CW columns; applies
 //           the remaining kr/R1 part of the row-side transform (skipped when
 //           R1 == kr).
@@ -50,6 +51,7 @@ struct TParams {
   Side row, col;
   int64_t R1;          // low row-block factor handled by pass 1
   int lg_kc, lg_r1;    // log2 of kc and R1
+  int lg_c1;           // log2 of the pass-1 tile width C1 (a multiple of kc)
   int lg_rows2;        // log2(kr / R1)
   int lg_cw;           // pass-2 strip width (log2)
   int64_t strips;      // pass-2 strips per row of blocks
@@ -65,26 +67,27 @@ __device__ __forceinline__ bool xcd_tile(int64_t ntiles, int per_xcd, int64_t& t
   return (b / kXcds) < per_xcd && t < ntiles;
 }
 
-// pass 1: tile = R1 rows x kc columns, index e = rr * kc + cc
+// pass 1: tile = R1 rows x C1 columns, index e = rr * C1 + cc
 template <bool kVec>
 __global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
   extern __shared__ __align__(16) float s[];
   int64_t t;
   if (!xcd_tile(p.tiles1, p.per_xcd1, t)) return;
-  const int64_t kc = p.col.block;
-  const int64_t nb = p.C / kc;
-  const int64_t r0 = (t / nb) * p.R1, c0 = (t % nb) * kc;
-  const int lg = p.lg_kc + p.lg_r1;
+  const int64_t c1 = int64_t(1) << p.lg_c1;
+  const int64_t nb = p.C / c1;
+  const int64_t r0 = (t / nb) * p.R1, c0 = (t % nb) * c1;
+  const int lg = p.lg_c1 + p.lg_r1;
+  const float* cf = p.col.fac;   // NULL: no column factor (identity side)
   const int E = 1 << lg;
   if (kVec) {
     for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
-      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
       const int64_t r = r0 + rr, c = c0 + cc;
       const float4 x = *reinterpret_cast<const float4*>(p.M + r * p.ld + c);
       float4 f = make_float4(1.f, 1.f, 1.f, 1.f);
       float g = 1.f;
       if (!p.post) {
-        f = *reinterpret_cast<const float4*>(p.col.fac + c);
+        if (cf) f = *reinterpret_cast<const float4*>(cf + c);
         g = p.row.fac[r];
       }
       *reinterpret_cast<float4*>(s + pad(e)) =
@@ -92,25 +95,31 @@ __global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
     }
   } else {
     for (int e = threadIdx.x; e < E; e += NT) {
-      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
       const int64_t r = r0 + rr, c = c0 + cc;
       const float x = p.M[r * p.ld + c];
-      s[pad(e)] = p.post ? x : x * p.col.fac[c] * p.row.fac[r];
+      s[pad(e)] = p.post ? x : x * (cf ? cf[c] : 1.f) * p.row.fac[r];
     }
   }
   __syncthreads();
-  lds_wht_bits<NT>(s, lg, 0, lg);
+  if (p.lg_c1 == p.lg_kc) {
+    lds_wht_bits<NT>(s, lg, 0, lg);
+  } else {   // several column blocks per tile: column bits below kc, then the row bits
+    lds_wht_bits<NT>(s, lg, 0, p.lg_kc);
+    lds_wht_bits<NT>(s, lg, p.lg_c1, lg);
+  }
   const float nrm = p.norm1;
   // inverse: Dc always lands here (the column transform is complete); Dr only
   // when no second pass follows
   const bool post_c = p.post, post_r = p.post && p.tiles2 == 0;
   if (kVec) {
     for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
-      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
       const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
       float4 f = make_float4(nrm, nrm, nrm, nrm);
       if (post_c) {
-        const float4 fc = *reinterpret_cast<const float4*>(p.col.fac + c0 + cc);
+        const float4 fc = cf ? *reinterpret_cast<const float4*>(cf + c0 + cc)
+                             : make_float4(1.f, 1.f, 1.f, 1.f);
         const float g = post_r ? nrm * p.row.fac[r0 + rr] : nrm;
         f = make_float4(fc.x * g, fc.y * g, fc.z * g, fc.w * g);
       }
@@ -119,9 +128,9 @@ __global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
     }
   } else {
     for (int e = threadIdx.x; e < E; e += NT) {
-      const int64_t rr = e >> p.lg_kc, cc = e & (kc - 1);
+      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
       float f = nrm;
-      if (post_c) f *= p.col.fac[c0 + cc];
+      if (post_c && cf) f *= cf[c0 + cc];
       if (post_r) f *= p.row.fac[r0 + rr];
       p.M[(r0 + rr) * p.ld + c0 + cc] = s[pad(e)] * f;
     }
@@ -192,8 +201,9 @@ __global__ void biip_prep(const float* HG, int64_t ldhg, int64_t m, float alpha,
     if (dgi > 0.0f) g = powf(dgi, alpha);
   }
   sg_ws[i] = g;
-  rfW[i] = so[i] * g;
-  rfG[i] = so[i] / g;
+  const float o = so ? so[i] : 1.f;   // NULL: identity output side
+  rfW[i] = o * g;
+  rfG[i] = o / g;
   if (sg_out) sg_out[i] = g;
 }
 
@@ -201,7 +211,8 @@ __global__ void biip_prep(const float* HG, int64_t ldhg, int64_t m, float alpha,
 __global__ void unrotate_prep(const float* so, const float* sg, int64_t m, float* rf) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= m) return;
-  rf[i] = sg ? so[i] / sg[i] : so[i];
+  const float o = so ? so[i] : 1.f;   // NULL: identity output side
+  rf[i] = sg ? o / sg[i] : o;
 }
 
 int ilog2(int64_t x) {
@@ -226,7 +237,12 @@ kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr,
   p.ld = ld;
   p.row = Side{kr, rfac};
   p.col = Side{kc, cfac};
-  p.R1 = std::min<int64_t>(kr, TILE / kc);
+  // pass-1 tile width: whole column blocks, at least 16 columns (64 bytes)
+  // where the width allows, so that a block of 1 does not read single columns
+  int64_t c1 = kc;
+  while (c1 < 16 && (C / kc) % (2 * c1 / kc) == 0) c1 *= 2;
+  p.lg_c1 = ilog2(c1);
+  p.R1 = std::min<int64_t>(kr, TILE / c1);
   p.lg_kc = ilog2(kc);
   p.lg_r1 = ilog2(p.R1);
   const int64_t rows2 = kr / p.R1;
@@ -236,14 +252,14 @@ kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr,
   const int64_t cw = std::min<int64_t>(pow2_floor(C), TILE / rows2);
   p.lg_cw = ilog2(cw);
   p.strips = (C + cw - 1) / cw;
-  p.tiles1 = (R / p.R1) * (C / kc);
+  p.tiles1 = (R / p.R1) * (C / c1);
   p.tiles2 = (rows2 > 1) ? (R / kr) * p.R1 * p.strips : 0;
   p.per_xcd1 = (int)((p.tiles1 + kXcds - 1) / kXcds);
   p.per_xcd2 = (int)((p.tiles2 + kXcds - 1) / kXcds);
-  const bool vec1 = (kc % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0) &&
+  const bool vec1 = (c1 % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0) &&
                     ((uintptr_t)cfac % 16 == 0);
   const bool vec2 = (cw % 4 == 0) && (C % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0);
-  const size_t lds1 = padded(1 << (p.lg_kc + p.lg_r1)) * sizeof(float);
+  const size_t lds1 = padded(1 << (p.lg_c1 + p.lg_r1)) * sizeof(float);
   const size_t lds2 = padded(1 << (p.lg_rows2 + p.lg_cw)) * sizeof(float);
   const size_t ldsmax = padded(TILE) * sizeof(float);
   {
@@ -279,13 +295,19 @@ kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
   hipLaunchKernelGGL(biip_prep, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s,
                      (const float*)HG, ldhg, m, alpha, out.signs, sg_ws, rfW, rfG, sg);
   KQ_LAUNCHED("biip_prep");
-  kronq_status st = transform2d(W, m, n, ldw, out.block, rfW, in.block, in.signs, s);
-  if (st) return st;
-  if (HX) {
+  // an identity side (block 1, no signs) leaves its factor alone: V = I keeps
+  // H_X, U = I without a rescale keeps H_G (and W when both sides are so)
+  const bool v_id = in.block == 1 && !in.signs, u_id = out.block == 1 && !out.signs;
+  kronq_status st = KRONQ_OK;
+  if (!(v_id && u_id && alpha == 0.0f)) {
+    st = transform2d(W, m, n, ldw, out.block, rfW, in.block, in.signs, s);
+    if (st) return st;
+  }
+  if (HX && !v_id) {
     st = transform2d(HX, n, n, ldhx, in.block, in.signs, in.block, in.signs, s);
     if (st) return st;
   }
-  if (HG) {
+  if (HG && !(u_id && alpha == 0.0f)) {
     st = transform2d(HG, m, m, ldhg, out.block, rfG, out.block, rfG, s);
     if (st) return st;
   }

@@ -64,6 +64,11 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
 kronq_status trace_launch(const float* HX, int64_t n, int64_t ldhx, const float* HG, int64_t m,
                           int64_t ldhg, double* out3, hipStream_t s);
 
+// diag.hip
+size_t cv_ws_bytes(int64_t m, int64_t n);
+kronq_status cv_launch(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
+                       float* col_norms, float* row_norms, void* ws, hipStream_t s);
+
 // codec.hip
 kronq_status pack_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int bits,
                          uint8_t* packed, int64_t ldp, hipStream_t s);
