@@ -197,7 +197,7 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
  *   out2[0] = CV_in  = std(||W[:, j]||) / mean(||W[:, j]||)   over the n columns
  *   out2[1] = CV_out = std(||W[i, :]||) / mean(||W[i, :]||)   over the m rows
  * with the population standard deviation; norms from fp32 squares summed in
- * fp32 within 16 x 1024 tiles and fp64 across tiles, statistics in fp64.  NaN
+ * fp32 within 64 x 1024 tiles and fp64 across tiles, statistics in fp64.  NaN
  * when every norm is zero.
  * W        : m x n fp32 device, leading dimension ldw >= n (read only).
  * out2     : device, 2 doubles.
