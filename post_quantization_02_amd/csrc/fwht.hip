@@ -67,9 +67,93 @@ __device__ __forceinline__ bool xcd_tile(int64_t ntiles, int per_xcd, int64_t& t
   return (b / kXcds) < per_xcd && t < ntiles;
 }
 
+// ---------------------------------------------------------------- vector passes
+//
+// 256 threads, each holding 16 float4 chunks of the tile: element
+//   e = 4 * (t + 256 * i) + j    (j < 4 inside a chunk, thread t < 256, chunk i < 16)
+// so index bits 0-1 (j) and 10-13 (i) sit in a thread's registers and bits 2-9
+// (t) across threads.  Loads of the whole tile (data and the factors a load
+// applies) are issued before anything else, from clamped addresses (chunks past
+// the tile read its first element and are dropped).  The butterflies over the
+// register bits run in registers, then bits 2-9 in at most two LDS rounds at
+// compile-time offsets, then the tile goes back to HBM.  Half the VALU work and
+// 40% less LDS traffic than running every bit through LDS.
+constexpr int NTB = 256;
+constexpr int ECH = TILE / (4 * NTB);   // 16 chunks a thread
+
+__device__ __forceinline__ float4 ld4(const float* a) { return *reinterpret_cast<const float4*>(a); }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b, float g) {
+  return make_float4(a.x * b.x * g, a.y * b.y * g, a.z * b.z * g, a.w * b.w * g);
+}
+__device__ __forceinline__ void bfly(float& a, float& b) {
+  const float u = a, v = b;
+  a = u + v;
+  b = u - v;
+}
+
+// butterflies over the register bits: lo bit 0 / 1 (inside a chunk) when set in
+// mask_lo; chunk bit k (element bit 10 + k) when set in mask_i and 2^k < nch
+__device__ __forceinline__ void reg_stages(float4 (&x)[ECH], int nch, int mask_lo, int mask_i) {
+  if (mask_lo & 1) {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) {
+      bfly(x[i].x, x[i].y);
+      bfly(x[i].z, x[i].w);
+    }
+  }
+  if (mask_lo & 2) {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) {
+      bfly(x[i].x, x[i].z);
+      bfly(x[i].y, x[i].w);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int h = 1 << k;
+    if (h < nch && ((mask_i >> k) & 1)) {
+#pragma unroll
+      for (int i = 0; i < ECH; ++i)
+        if ((i & h) == 0) {
+          bfly(x[i].x, x[i + h].x);
+          bfly(x[i].y, x[i + h].y);
+          bfly(x[i].z, x[i + h].z);
+          bfly(x[i].w, x[i + h].w);
+        }
+    }
+  }
+}
+
+// one LDS round over bits [b, b + k) of a 2^p tile, b in 2..9 at compile time
+__device__ __forceinline__ void lds_round_mid(float* s, int p, int b, int k) {
+  switch (b) {
+    case 2: lds_round_k<NTB, 2>(s, p, k); break;
+    case 3: lds_round_k<NTB, 3>(s, p, k); break;
+    case 4: lds_round_k<NTB, 4>(s, p, k); break;
+    case 5: lds_round_k<NTB, 5>(s, p, k); break;
+    case 6: lds_round_k<NTB, 6>(s, p, k); break;
+    case 7: lds_round_k<NTB, 7>(s, p, k); break;
+    case 8: lds_round_k<NTB, 8>(s, p, k); break;
+    default: lds_round_k<NTB, 9>(s, p, k); break;
+  }
+}
+
+// bits [lo, hi) of the tile through LDS (2 <= lo, hi <= 10): at most two rounds
+__device__ __forceinline__ void lds_mid_bits(float* s, int p, int lo, int hi) {
+  for (int b = lo; b < hi; b += 4) {
+    lds_round_mid(s, p, b, min(4, hi - b));
+    __syncthreads();
+  }
+}
+
+// whether element bit b of a pass-1 tile is transformed: inside [0, lg), and
+// not a column-block index bit (bits [lg_kc, lg_c1) when a tile spans blocks)
+__device__ __forceinline__ bool p1_bit(const TParams& p, int lg, int b) {
+  return b < lg && (b < p.lg_kc || b >= p.lg_c1);
+}
+
 // pass 1: tile = R1 rows x C1 columns, index e = rr * C1 + cc
-template <bool kVec>
-__global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
+__global__ void __launch_bounds__(NTB) biip_pass1v(TParams p) {
   extern __shared__ __align__(16) float s[];
   int64_t t;
   if (!xcd_tile(p.tiles1, p.per_xcd1, t)) return;
@@ -78,68 +162,181 @@ __global__ void __launch_bounds__(NT) biip_pass1(TParams p) {
   const int64_t r0 = (t / nb) * p.R1, c0 = (t % nb) * c1;
   const int lg = p.lg_c1 + p.lg_r1;
   const float* cf = p.col.fac;   // NULL: no column factor (identity side)
+  const float* rf = p.row.fac;
   const int E = 1 << lg;
-  if (kVec) {
-    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
-      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
-      const int64_t r = r0 + rr, c = c0 + cc;
-      const float4 x = *reinterpret_cast<const float4*>(p.M + r * p.ld + c);
-      float4 f = make_float4(1.f, 1.f, 1.f, 1.f);
-      float g = 1.f;
-      if (!p.post) {
-        if (cf) f = *reinterpret_cast<const float4*>(cf + c);
-        g = p.row.fac[r];
-      }
-      *reinterpret_cast<float4*>(s + pad(e)) =
-          make_float4(x.x * f.x * g, x.y * f.y * g, x.z * f.z * g, x.w * f.w * g);
+  const int nch = E >= 4 * NTB ? E / (4 * NTB) : 1;
+  const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
+  const float* Mt = p.M + r0 * p.ld + c0;
+  int rowi[ECH], coli[ECH];
+  float4 x[ECH], f[ECH];
+  float g[ECH];
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int e = e0 < E ? e0 : 0;
+    rowi[i] = e >> p.lg_c1;
+    coli[i] = e & (int)(c1 - 1);
+    x[i] = ld4(Mt + (int64_t)rowi[i] * p.ld + coli[i]);
+    f[i] = one4;
+    g[i] = 1.f;
+  }
+  if (!p.post) {
+    if (cf) {
+#pragma unroll
+      for (int i = 0; i < ECH; ++i) f[i] = ld4(cf + c0 + coli[i]);
     }
-  } else {
-    for (int e = threadIdx.x; e < E; e += NT) {
-      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
-      const int64_t r = r0 + rr, c = c0 + cc;
-      const float x = p.M[r * p.ld + c];
-      s[pad(e)] = p.post ? x : x * (cf ? cf[c] : 1.f) * p.row.fac[r];
-    }
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) g[i] = rf[r0 + rowi[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) x[i] = mul4(x[i], f[i], g[i]);
+  int mask_i = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) mask_i |= p1_bit(p, lg, 10 + k) ? (1 << k) : 0;
+  reg_stages(x, nch, (p1_bit(p, lg, 0) ? 1 : 0) | (p1_bit(p, lg, 1) ? 2 : 0), mask_i);
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    if (e0 < E) *reinterpret_cast<float4*>(s + pad(e0)) = x[i];
   }
   __syncthreads();
+  // bits 2-9: the column bits below kc, and the bits from C1 up
+  const int hi = min(lg, 10);
   if (p.lg_c1 == p.lg_kc) {
-    lds_wht_bits<NT>(s, lg, 0, lg);
-  } else {   // several column blocks per tile: column bits below kc, then the row bits
-    lds_wht_bits<NT>(s, lg, 0, p.lg_kc);
-    lds_wht_bits<NT>(s, lg, p.lg_c1, lg);
+    lds_mid_bits(s, lg, 2, hi);
+  } else {
+    lds_mid_bits(s, lg, 2, min(p.lg_kc, hi));
+    lds_mid_bits(s, lg, max(p.lg_c1, 2), hi);
   }
   const float nrm = p.norm1;
   // inverse: Dc always lands here (the column transform is complete); Dr only
   // when no second pass follows
-  const bool post_c = p.post, post_r = p.post && p.tiles2 == 0;
-  if (kVec) {
-    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
-      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
-      const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
-      float4 f = make_float4(nrm, nrm, nrm, nrm);
-      if (post_c) {
-        const float4 fc = cf ? *reinterpret_cast<const float4*>(cf + c0 + cc)
-                             : make_float4(1.f, 1.f, 1.f, 1.f);
-        const float g = post_r ? nrm * p.row.fac[r0 + rr] : nrm;
-        f = make_float4(fc.x * g, fc.y * g, fc.z * g, fc.w * g);
-      }
-      *reinterpret_cast<float4*>(p.M + (r0 + rr) * p.ld + c0 + cc) =
-          make_float4(y.x * f.x, y.y * f.y, y.z * f.z, y.w * f.w);
-    }
-  } else {
-    for (int e = threadIdx.x; e < E; e += NT) {
-      const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
-      float f = nrm;
-      if (post_c && cf) f *= cf[c0 + cc];
-      if (post_r) f *= p.row.fac[r0 + rr];
-      p.M[(r0 + rr) * p.ld + c0 + cc] = s[pad(e)] * f;
+  const bool post_c = p.post && cf, post_r = p.post && p.tiles2 == 0;
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    f[i] = one4;
+    g[i] = nrm;
+  }
+  if (post_c) {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) f[i] = ld4(cf + c0 + coli[i]);
+  }
+  if (post_r) {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) g[i] = nrm * rf[r0 + rowi[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    if (e0 < E) {
+      const float4 y = *reinterpret_cast<const float4*>(s + pad(e0));
+      *reinterpret_cast<float4*>(p.M + (r0 + rowi[i]) * p.ld + c0 + coli[i]) = mul4(y, f[i], g[i]);
     }
   }
 }
 
+// pass 2: tile = (kr / R1) rows at stride R1 x CW columns, index e = j * CW + c;
+// the transformed bits are the row bits [lg_cw, lg)
+__global__ void __launch_bounds__(NTB) biip_pass2v(TParams p) {
+  extern __shared__ __align__(16) float s[];
+  int64_t t;
+  if (!xcd_tile(p.tiles2, p.per_xcd2, t)) return;
+  const int64_t kr = p.row.block;
+  const int64_t strip = t % p.strips;
+  const int64_t rest = t / p.strips;
+  const int64_t res = rest % p.R1, rb = rest / p.R1;
+  const int64_t rbase = rb * kr + res;
+  const int64_t cbase = strip << p.lg_cw;
+  const int lg = p.lg_rows2 + p.lg_cw;
+  const int E = 1 << lg;
+  const int nch = E >= 4 * NTB ? E / (4 * NTB) : 1;
+  const int64_t cmask = (1 << p.lg_cw) - 1;
+  float4 x[ECH];
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int64_t j = e0 >> p.lg_cw, c = cbase + (e0 & cmask);
+    const bool in = e0 < E && c < p.C;
+    const float4 v = ld4(p.M + (in ? (rbase + j * p.R1) * p.ld + c : rbase * p.ld + cbase));
+    x[i] = in ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  int mask_i = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) mask_i |= (10 + k >= p.lg_cw && 10 + k < lg) ? (1 << k) : 0;
+  reg_stages(x, nch, 0, mask_i);   // bits 0-1 are column bits (cw >= 4)
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    if (e0 < E) *reinterpret_cast<float4*>(s + pad(e0)) = x[i];
+  }
+  __syncthreads();
+  lds_mid_bits(s, lg, max(p.lg_cw, 2), min(lg, 10));
+  const float nrm = p.norm2;
+  float g[ECH];
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) g[i] = nrm;
+  if (p.post) {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) {
+      const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+      const int64_t j = e0 < E ? (e0 >> p.lg_cw) : 0;
+      g[i] = nrm * p.row.fac[rbase + j * p.R1];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int64_t j = e0 >> p.lg_cw, c = cbase + (e0 & cmask);
+    if (e0 < E && c < p.C) {
+      const float4 y = *reinterpret_cast<const float4*>(s + pad(e0));
+      const float f = g[i];
+      *reinterpret_cast<float4*>(p.M + (rbase + j * p.R1) * p.ld + c) =
+          make_float4(y.x * f, y.y * f, y.z * f, y.w * f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- scalar passes
+// (widths that are not a multiple of 4): one element a thread at a time
+
+// pass 1: tile = R1 rows x C1 columns, index e = rr * C1 + cc
+__global__ void __launch_bounds__(NT) biip_pass1s(TParams p) {
+  extern __shared__ __align__(16) float s[];
+  int64_t t;
+  if (!xcd_tile(p.tiles1, p.per_xcd1, t)) return;
+  const int64_t c1 = int64_t(1) << p.lg_c1;
+  const int64_t nb = p.C / c1;
+  const int64_t r0 = (t / nb) * p.R1, c0 = (t % nb) * c1;
+  const int lg = p.lg_c1 + p.lg_r1;
+  const float* cf = p.col.fac;
+  const float* rf = p.row.fac;
+  const int E = 1 << lg;
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
+    const int64_t r = r0 + rr, c = c0 + cc;
+    const float x = p.M[r * p.ld + c];
+    s[pad(e)] = p.post ? x : x * (cf ? cf[c] : 1.f) * rf[r];
+  }
+  __syncthreads();
+  if (p.lg_c1 == p.lg_kc) {
+    lds_wht_bits<NT>(s, lg, 0, lg);
+  } else {
+    lds_wht_bits<NT>(s, lg, 0, p.lg_kc);
+    lds_wht_bits<NT>(s, lg, p.lg_c1, lg);
+  }
+  const float nrm = p.norm1;
+  const bool post_c = p.post && cf, post_r = p.post && p.tiles2 == 0;
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int64_t rr = e >> p.lg_c1, cc = e & (c1 - 1);
+    float f = nrm;
+    if (post_c) f *= cf[c0 + cc];
+    if (post_r) f *= rf[r0 + rr];
+    p.M[(r0 + rr) * p.ld + c0 + cc] = s[pad(e)] * f;
+  }
+}
+
 // pass 2: tile = (kr / R1) rows at stride R1 x CW columns, index e = j * CW + c
-template <bool kVec>
-__global__ void __launch_bounds__(NT) biip_pass2(TParams p) {
+__global__ void __launch_bounds__(NT) biip_pass2s(TParams p) {
   extern __shared__ __align__(16) float s[];
   int64_t t;
   if (!xcd_tile(p.tiles2, p.per_xcd2, t)) return;
@@ -152,39 +349,18 @@ __global__ void __launch_bounds__(NT) biip_pass2(TParams p) {
   const int lg = p.lg_rows2 + p.lg_cw;
   const int E = 1 << lg;
   const int64_t cmask = (1 << p.lg_cw) - 1;
-  if (kVec) {
-    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
-      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < p.C) x = *reinterpret_cast<const float4*>(p.M + (rbase + j * p.R1) * p.ld + c);
-      *reinterpret_cast<float4*>(s + pad(e)) = x;
-    }
-  } else {
-    for (int e = threadIdx.x; e < E; e += NT) {
-      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
-      s[pad(e)] = (c < p.C) ? p.M[(rbase + j * p.R1) * p.ld + c] : 0.f;
-    }
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
+    s[pad(e)] = (c < p.C) ? p.M[(rbase + j * p.R1) * p.ld + c] : 0.f;
   }
   __syncthreads();
   lds_wht_bits<NT>(s, lg, p.lg_cw, lg);
   const float nrm = p.norm2;
-  if (kVec) {
-    for (int e = 4 * threadIdx.x; e < E; e += 4 * NT) {
-      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
-      if (c < p.C) {
-        const int64_t r = rbase + j * p.R1;
-        const float f = p.post ? nrm * p.row.fac[r] : nrm;
-        const float4 y = *reinterpret_cast<const float4*>(s + pad(e));
-        *reinterpret_cast<float4*>(p.M + r * p.ld + c) = make_float4(y.x * f, y.y * f, y.z * f, y.w * f);
-      }
-    }
-  } else {
-    for (int e = threadIdx.x; e < E; e += NT) {
-      const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
-      if (c < p.C) {
-        const int64_t r = rbase + j * p.R1;
-        p.M[r * p.ld + c] = s[pad(e)] * (p.post ? nrm * p.row.fac[r] : nrm);
-      }
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int64_t j = e >> p.lg_cw, c = cbase + (e & cmask);
+    if (c < p.C) {
+      const int64_t r = rbase + j * p.R1;
+      p.M[r * p.ld + c] = s[pad(e)] * (p.post ? nrm * p.row.fac[r] : nrm);
     }
   }
 }
@@ -263,15 +439,15 @@ kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr,
   const size_t lds2 = padded(1 << (p.lg_rows2 + p.lg_cw)) * sizeof(float);
   const size_t ldsmax = padded(TILE) * sizeof(float);
   {
-    auto k1 = vec1 ? biip_pass1<true> : biip_pass1<false>;
+    auto k1 = vec1 ? biip_pass1v : biip_pass1s;
     KQ_HIP(hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
-    hipLaunchKernelGGL(k1, dim3(p.per_xcd1 * kXcds), dim3(NT), lds1, st, p);
+    hipLaunchKernelGGL(k1, dim3(p.per_xcd1 * kXcds), dim3(vec1 ? NTB : NT), lds1, st, p);
     KQ_LAUNCHED("biip_pass1");
   }
   if (p.tiles2) {
-    auto k2 = vec2 ? biip_pass2<true> : biip_pass2<false>;
+    auto k2 = vec2 ? biip_pass2v : biip_pass2s;
     KQ_HIP(hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
-    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(NT), lds2, st, p);
+    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(vec2 ? NTB : NT), lds2, st, p);
     KQ_LAUNCHED("biip_pass2");
   }
   return KRONQ_OK;
