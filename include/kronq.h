@@ -181,6 +181,10 @@ kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda
  * What     : m x n fp32 device dequantized weights, natural order, leading
  *            dimension n; may be NULL.  May alias W when ldw == n.
  * pre_round: m x n fp32 device t values (natural order) or NULL.
+ * Group sizes: group > 0 must also be a multiple of 8 that divides 128
+ *            (8, 16, 32, 64, 128): a group's grid comes from the current
+ *            values of one 128-column block of the loop.  Other sizes that
+ *            divide n return KRONQ_EUNSUPPORTED.
  * ws       : kronq_gptq_ws(m, n) bytes.
  * ------------------------------------------------------------------------- */
 size_t kronq_gptq_ws(int64_t m, int64_t n);

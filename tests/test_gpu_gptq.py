@@ -51,6 +51,8 @@ def _compare(W, R32, perm, bits, group, rows=None):
     (33, 256, 4, 64, True),      # groups smaller than a block
     (16, 128, 8, -1, False),     # one block, 8 bits
     (70, 520, 2, 8, False),      # tiny groups
+    (1, 4, 4, -1, False),        # a single row of four weights
+    (5, 96, 1, -1, True),        # 1 bit: two levels
 ])
 def test_gptq_small(m, n, bits, group, act):
     say("gptq", m, n, bits, group, act)
@@ -93,3 +95,29 @@ def test_gptq_full_size_llama2_7b_q_proj_sampled_rows():
     R, _ = O.chol_inv_upper(Hd)
     rows = np.sort(np.random.default_rng(0).choice(m, 64, replace=False))
     _compare(W, R.astype(np.float32), perm, 2, 128, rows=rows)
+
+
+def test_gptq_single_group_equals_per_channel():
+    """A group spanning the whole row takes its grid from the row before any
+    compensation, which is the per-channel grid: identical results."""
+    say("gptq group = n vs per-channel")
+    m, n, bits = 32, 128, 3
+    W, R32, perm = _inputs(m, n, 73, False)
+    Wd, Rd = to_dev_f32(W), to_dev_f32(R32)
+    pd = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    a = kq.kronq_gptq_quantize(Wd, Rd, pd, bits, -1)
+    b = kq.kronq_gptq_quantize(Wd, Rd, pd, bits, n)
+    for k in ("codes", "What"):
+        assert np.array_equal(host(a[k]), host(b[k])), k
+    assert np.array_equal(host(a["scales"]), host(b["scales"]))
+    assert np.array_equal(host(a["zeros"]), host(b["zeros"]))
+
+
+def test_gptq_group_beyond_a_block_is_unsupported():
+    say("gptq group 256: KRONQ_EUNSUPPORTED, nothing launched")
+    W, R32, perm = _inputs(8, 512, 75, False)
+    with pytest.raises(kq.KronqError) as ei:
+        kq.kronq_gptq_quantize(to_dev_f32(W), to_dev_f32(R32),
+                               torch.from_numpy(perm.astype(np.int32)).to(DEV), 3, 256)
+    assert ei.value.status == kq.KRONQ_EUNSUPPORTED
+
