@@ -227,12 +227,16 @@ kronq_status kronq_weight_cv(const float* W, int64_t m, int64_t n, int64_t ldw, 
  * kronq_pack_codes: codes (m x n uint8 device, leading dimension ldc >= n) ->
  *   packed (m rows of ldp >= row bytes, device); only the low `bits` bits of a
  *   code are stored; bytes of a row past its row bytes are not written.
+ *   perm (device int32[n] or NULL): when given, stored column j holds code
+ *   column perm[j], i.e. the codes are stored in the column loop's processing
+ *   order, where its groups are contiguous (act-order layers).
  * kronq_unpack_codes: the inverse (codes < 2^bits).
  * Both take bits 2 or 4 (KRONQ_EINVAL otherwise); buffers must not overlap.
  * ------------------------------------------------------------------------- */
 int64_t kronq_packed_row_bytes(int64_t n, int32_t bits);
 kronq_status kronq_pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc,
-                              int32_t bits, uint8_t* packed, int64_t ldp, void* stream);
+                              int32_t bits, const int32_t* perm, uint8_t* packed, int64_t ldp,
+                              void* stream);
 kronq_status kronq_unpack_codes(const uint8_t* packed, int64_t m, int64_t n, int64_t ldp,
                                 int32_t bits, uint8_t* codes, int64_t ldc, void* stream);
 
@@ -248,13 +252,16 @@ kronq_status kronq_unpack_codes(const uint8_t* packed, int64_t m, int64_t n, int
  *          buffer must be readable (the pad bytes of a row may be read, never
  *          used).
  * q      : bits 1..8; group <= 0 (one grid per row) or a multiple of 64 that
- *          divides n (KRONQ_EUNSUPPORTED for other group sizes), groups of
- *          consecutive natural-order columns.
+ *          divides n (KRONQ_EUNSUPPORTED for other group sizes); group g covers
+ *          stored columns [g * group, (g + 1) * group).
  * scales, zeros : m x ngroups fp32 device, leading dimension ngroups, as
- *          kronq_gptq_quantize writes them.
- * perm   : the act-order permutation or NULL.  One grid per row does not
- *          depend on it (it is ignored); grouped codes with a permutation are
- *          KRONQ_EUNSUPPORTED (their groups are not contiguous columns).
+ *          kronq_gptq_quantize writes them (groups in processing order).
+ * perm   : NULL when the codes are stored in natural column order (a layer
+ *          quantized without act-order, or one grid per row); else the
+ *          act-order permutation, device int32[n], with the codes stored in
+ *          processing order (stored column j = natural column perm[j], as
+ *          kronq_pack_codes writes them when given perm).  Then n <= 32768
+ *          (KRONQ_EUNSUPPORTED above): each workgroup builds the whole x'.
  * in_side, out_side, sg : the transforms and rescale of kronq_biip_rotate
  *          (sg device m floats, NULL for no rescale).
  * x      : n fp32 device;  y : m fp32 device (must not overlap x or ws).

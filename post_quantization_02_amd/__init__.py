@@ -90,7 +90,7 @@ def load(path: str = LIB_PATH):
     lib.kronq_biip_unrotate.restype = i32
     lib.kronq_packed_row_bytes.argtypes = [i64, i32]
     lib.kronq_packed_row_bytes.restype = i64
-    lib.kronq_pack_codes.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp]
+    lib.kronq_pack_codes.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp]
     lib.kronq_pack_codes.restype = i32
     lib.kronq_unpack_codes.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp]
     lib.kronq_unpack_codes.restype = i32
@@ -329,8 +329,9 @@ def kronq_packed_row_bytes(n: int, bits: int) -> int:
 
 
 def kronq_pack_codes(codes: torch.Tensor, bits: int, packed: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
-    """m x n uint8 codes -> m x ldp packed bytes (ldp = row bytes unless `packed` is given)."""
+                     stream=None, perm: torch.Tensor | None = None) -> torch.Tensor:
+    """m x n uint8 codes -> m x ldp packed bytes (ldp = row bytes unless `packed` is given);
+    with `perm`, stored column j holds code column perm[j] (processing order)."""
     lib = load()
     _dev(codes, "codes", torch.uint8)
     m, n = codes.shape
@@ -338,8 +339,8 @@ def kronq_pack_codes(codes: torch.Tensor, bits: int, packed: torch.Tensor | None
         packed = torch.zeros((m, lib.kronq_packed_row_bytes(n, bits)), dtype=torch.uint8,
                              device=codes.device)
     _dev(packed, "packed", torch.uint8)
-    _check(lib.kronq_pack_codes(_ptr(codes), m, n, _ld(codes), bits, _ptr(packed), _ld(packed),
-                                _stream(stream)), "kronq_pack_codes")
+    _check(lib.kronq_pack_codes(_ptr(codes), m, n, _ld(codes), bits, _ptr(perm), _ptr(packed),
+                                _ld(packed), _stream(stream)), "kronq_pack_codes")
     return packed
 
 

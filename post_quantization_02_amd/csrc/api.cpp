@@ -215,13 +215,14 @@ int64_t kronq_packed_row_bytes(int64_t n, int32_t bits) {
 }
 
 kronq_status kronq_pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc,
-                              int32_t bits, uint8_t* packed, int64_t ldp, void* stream) {
+                              int32_t bits, const int32_t* perm, uint8_t* packed, int64_t ldp,
+                              void* stream) {
   if (!codes || !packed) return fail(KRONQ_EINVAL, "kronq_pack_codes: NULL pointer");
   if (bits != 2 && bits != 4)
     return fail(KRONQ_EINVAL, "kronq_pack_codes: bits %d (only 2 and 4 are packed)", (int)bits);
   if (m < 1 || n < 1 || ldc < n || ldp < decode_row_bytes(n, bits))
     return fail(KRONQ_EINVAL, "kronq_pack_codes: bad shape");
-  return pack_launch(codes, m, n, ldc, bits, packed, ldp, (hipStream_t)stream);
+  return pack_launch(codes, m, n, ldc, bits, perm, packed, ldp, (hipStream_t)stream);
 }
 
 kronq_status kronq_unpack_codes(const uint8_t* packed, int64_t m, int64_t n, int64_t ldp,
@@ -259,10 +260,11 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
     if (q->group % 64)
       return fail(KRONQ_EUNSUPPORTED, "kronq_decode_matvec: group %d is not a multiple of 64",
                   (int)q->group);
-    if (perm)
-      return fail(KRONQ_EUNSUPPORTED,
-                  "kronq_decode_matvec: groups in a permuted processing order are not decoded");
   }
+  if (perm && n > 32768)
+    return fail(KRONQ_EUNSUPPORTED,
+                "kronq_decode_matvec: codes in processing order need n <= 32768 (got %lld)",
+                (long long)n);
   kronq_status st = check_had(in_side, n, "input-side");
   if (st) return st;
   st = check_had(out_side, m, "output-side");
@@ -271,7 +273,7 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
   if (ws_bytes < need || !ws)
     return fail(KRONQ_EWORKSPACE, "kronq_decode_matvec: workspace %zu < %zu bytes", ws_bytes, need);
   return decode_launch(codes, m, n, ldp, q->bits, q->group > 0 ? q->group : 0, scales, zeros,
-                       *in_side, *out_side, sg, x, y, ws, (hipStream_t)stream);
+                       perm, *in_side, *out_side, sg, x, y, ws, (hipStream_t)stream);
 }
 
 kronq_status kronq_sensitivity(const float* HX, int64_t n, int64_t ldhx, const float* HG,

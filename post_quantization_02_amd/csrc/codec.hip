@@ -20,6 +20,8 @@
 // loads, then every weight load of its rows, and builds x' in LDS while the
 // weights are in flight (a workgroup barrier waits for LDS traffic only).
 // Each lane keeps the x' values of its chunk in registers for all its rows.
+// Codes stored in processing order (act-order layers) come with the
+// permutation: the workgroup then builds the whole x' and gathers x'[perm[c]].
 // The zero point is folded out of the inner loop:
 // sum s (q - z) x' = s (sum q x' - z sum x') per lane chunk (a chunk never
 // straddles a group: groups are multiples of 64 columns).  Both launches are
@@ -38,8 +40,11 @@ constexpr int NT = 256;
 
 // ---------------------------------------------------------------- pack / unpack
 
+// stored column j holds code column perm[j] (processing order) when perm is
+// given, column j otherwise; an entry of perm outside [0, n) reads column 0
 __global__ void pack_kernel(const uint8_t* __restrict__ codes, int64_t m, int64_t n, int64_t ldc,
-                            int bits, uint8_t* __restrict__ packed, int64_t ldp, int64_t nb) {
+                            int bits, const int32_t* __restrict__ perm, uint8_t* __restrict__ packed,
+                            int64_t ldp, int64_t nb) {
   const int per = 8 / bits;
   const uint32_t mask = (1u << bits) - 1u;
   const int64_t total = m * nb;
@@ -49,7 +54,11 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, int64_t m, int64_
     uint32_t v = 0;
     for (int t = 0; t < per; ++t) {
       const int64_t j = b * per + t;
-      if (j < n) v |= ((uint32_t)codes[r * ldc + j] & mask) << (bits * t);
+      if (j < n) {
+        int64_t c = perm ? (int64_t)perm[j] : j;
+        c = (c >= 0 && c < n) ? c : 0;
+        v |= ((uint32_t)codes[r * ldc + c] & mask) << (bits * t);
+      }
     }
     packed[r * ldp + b] = (uint8_t)v;
   }
@@ -144,6 +153,7 @@ struct GemvParams {
   int64_t group;        // 0: one grid per row
   const float* x;       // input vector (n)
   const float* sgn_in;  // D_in (n)
+  const int32_t* perm;  // stored column j is natural column perm[j] (NULL: natural order)
   int lg_kin;           // log2 of the input block
   int lg_tile;          // log2 of the x' tile: max(slice width, input block)
   float nrm_in;         // 1 / sqrt(kin)
@@ -285,13 +295,27 @@ __global__ void __launch_bounds__(NT) decode_gemv(GemvParams p) {
   __syncthreads();
   lds_wht_low_bits<NT>(tile, p.lg_tile, regs ? min(p.lg_kin, 8) : p.lg_kin);
   float xr[CPL];
+  if (p.perm) {
+    // codes stored in processing order: the tile holds the whole x' and the
+    // lane gathers x'[perm[c]] for its stored columns c (clamped into [0, n))
+    const int64_t cb = c0 + lane * CPL;
+    int pi[CPL];
 #pragma unroll
-  for (int k = 0; k < CPL; k += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(tile + pad(off + lane * CPL + k));
-    xr[k] = v.x * p.nrm_in;
-    xr[k + 1] = v.y * p.nrm_in;
-    xr[k + 2] = v.z * p.nrm_in;
-    xr[k + 3] = v.w * p.nrm_in;
+    for (int k = 0; k < CPL; ++k) pi[k] = p.perm[cb + k < p.n ? cb + k : 0];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = min(max(pi[k], 0), (int)p.n - 1);
+      xr[k] = (cb + k < p.n) ? tile[pad(c)] * p.nrm_in : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPL; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(tile + pad(off + lane * CPL + k));
+      xr[k] = v.x * p.nrm_in;
+      xr[k + 1] = v.y * p.nrm_in;
+      xr[k + 2] = v.z * p.nrm_in;
+      xr[k + 3] = v.w * p.nrm_in;
+    }
   }
   float xsum = 0.f;
 #pragma unroll
@@ -369,12 +393,12 @@ kronq_status gemv_bits(const GemvParams& p, hipStream_t st) {
 }  // namespace
 
 kronq_status pack_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int bits,
-                         uint8_t* packed, int64_t ldp, hipStream_t s) {
+                         const int32_t* perm, uint8_t* packed, int64_t ldp, hipStream_t s) {
   const int64_t nb = (n * bits + 7) / 8;
   const int64_t total = m * nb;
   const int64_t grid = std::min<int64_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, s, codes, m, n, ldc, bits,
-                     packed, ldp, nb);
+                     perm, packed, ldp, nb);
   KQ_LAUNCHED("pack_kernel");
   return KRONQ_OK;
 }
@@ -399,8 +423,8 @@ size_t decode_ws_bytes(int64_t m, int64_t n, int bits) {
 
 kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp, int bits,
                            int64_t group, const float* scales, const float* zeros,
-                           const kronq_had& in, const kronq_had& out, const float* sg,
-                           const float* x, float* y, void* ws, hipStream_t s) {
+                           const int32_t* perm, const kronq_had& in, const kronq_had& out,
+                           const float* sg, const float* x, float* y, void* ws, hipStream_t s) {
   // partial row sums of W^ x', with x' = V x built per workgroup
   GemvParams p{};
   p.codes = codes;
@@ -414,6 +438,8 @@ kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t l
   p.sgn_in = in.signs;
   p.lg_kin = ilog2(in.block);
   p.lg_tile = std::max(ilog2(64 * codes_per_lane(bits)), p.lg_kin);
+  p.perm = perm;
+  if (perm) p.lg_tile = std::max(p.lg_tile, ilog2(n));   // the whole x' in one tile
   p.nrm_in = (float)(1.0 / std::sqrt((double)in.block));
   p.m = m;
   p.n = n;

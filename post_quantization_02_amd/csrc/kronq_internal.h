@@ -71,14 +71,14 @@ kronq_status cv_launch(const float* W, int64_t m, int64_t n, int64_t ldw, double
 
 // codec.hip
 kronq_status pack_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int bits,
-                         uint8_t* packed, int64_t ldp, hipStream_t s);
+                         const int32_t* perm, uint8_t* packed, int64_t ldp, hipStream_t s);
 kronq_status unpack_launch(const uint8_t* packed, int64_t m, int64_t n, int64_t ldp, int bits,
                            uint8_t* codes, int64_t ldc, hipStream_t s);
 int64_t decode_row_bytes(int64_t n, int bits);
 size_t decode_ws_bytes(int64_t m, int64_t n, int bits);
 kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp, int bits,
                            int64_t group, const float* scales, const float* zeros,
-                           const kronq_had& in, const kronq_had& out, const float* sg,
-                           const float* x, float* y, void* ws, hipStream_t s);
+                           const int32_t* perm, const kronq_had& in, const kronq_had& out,
+                           const float* sg, const float* x, float* y, void* ws, hipStream_t s);
 
 }  // namespace kronq

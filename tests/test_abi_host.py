@@ -153,10 +153,10 @@ def test_codec_arguments_rejected_before_launch(lib):
     assert lib.kronq_packed_row_bytes(4097, 2) == 1025
     assert lib.kronq_packed_row_bytes(100, 3) == 100
     # only 2 and 4 bits are bit-packed
-    assert lib.kronq_pack_codes(fake, 4, 8, 8, 3, fake, 8, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_pack_codes(fake, 4, 8, 8, 3, None, fake, 8, None) == kq.KRONQ_EINVAL
     assert lib.kronq_unpack_codes(fake, 4, 8, 8, 8, fake, 8, None) == kq.KRONQ_EINVAL
     # packed row shorter than ceil(n bits / 8)
-    assert lib.kronq_pack_codes(fake, 4, 9, 9, 4, fake, 4, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_pack_codes(fake, 4, 9, 9, 4, None, fake, 4, None) == kq.KRONQ_EINVAL
     h_in = kq.Had(256, 256, fake)
     h_out = kq.Had(64, 64, fake)
     ws = lib.kronq_decode_ws(64, 256, 4)
@@ -175,7 +175,11 @@ def test_codec_arguments_rejected_before_launch(lib):
     # groups: must divide n; a multiple of 64; no permuted order
     assert dec(fake, 128, 4, 96) == kq.KRONQ_EINVAL
     assert dec(fake, 128, 4, 32) == kq.KRONQ_EUNSUPPORTED
-    assert dec(fake, 128, 4, 128, perm=fake) == kq.KRONQ_EUNSUPPORTED
+    # codes in processing order: the whole x' must fit one tile
+    q = kq.QCfg(4, 128)
+    assert lib.kronq_decode_matvec(fake, 64, 65536, 32768, ctypes.byref(q), fake, fake, fake,
+                                   ctypes.byref(kq.Had(65536, 256, fake)), ctypes.byref(h_out), None,
+                                   fake, fake, fake, 1 << 30, None) == kq.KRONQ_EUNSUPPORTED
     # Hadamard spec of the wrong dimension; workspace too small
     assert dec(fake, 128, 4, 0, hin=kq.Had(128, 128, fake)) == kq.KRONQ_EINVAL
     assert dec(fake, 128, 4, 0, ws_bytes=ws - 1) == kq.KRONQ_EWORKSPACE

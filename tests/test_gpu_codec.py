@@ -158,12 +158,77 @@ def test_decode_wide_row_stride():
     _check_y(_run_decode(c, n, bits, 0, 256, 512), c["want"], "ldp=512")
 
 
-def test_decode_per_channel_ignores_permutation():
-    say("decode per-channel with an act-order permutation")
-    m, n, bits = 128, 256, 4
-    c = _decode_case(73, m, n, bits, 0, 128, 256)
-    perm = torch.from_numpy(np.random.default_rng(5).permutation(n).astype(np.int32)).to(DEV)
-    _check_y(_run_decode(c, n, bits, 0, 128, 256, perm=perm), c["want"], "perm")
+def _perm(seed, n):
+    # a seeded permutation (synthetic keys, stable argsort)
+    keys = synth.matrix(synth.NORMAL, seed, 1, n, dtype="f64")[0]
+    return np.argsort(-keys, kind="stable").astype(np.int64)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_in_processing_order(bits):
+    say("pack with a permutation", bits)
+    m, n = 37, 1001
+    codes = _codes(77, m, n, bits)
+    perm = _perm(78, n)
+    got = kq.kronq_pack_codes(_dev_u8(codes), bits,
+                              perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
+    assert np.array_equal(host(got), O.pack_codes(codes[:, perm], bits))
+
+
+@pytest.mark.parametrize("m,n,bits,group,ko,ki", [
+    (4096, 4096, 4, 128, 4096, 4096),   # q_proj shape, act-order, W4 g128
+    (4096, 11008, 4, 128, 4096, 256),   # down_proj shape, act-order g128: x' tile of 16384
+    (256, 2048, 2, 64, 256, 2048),      # 2 bits, groups of 64
+    (128, 256, 4, 0, 128, 256),         # one grid per row, codes in processing order
+    (40, 1000, 4, 0, 8, 8),             # ragged row with a permutation
+])
+def test_decode_processing_order(m, n, bits, group, ko, ki):
+    """Codes of an act-order layer stored in processing order, decoded with
+    the permutation, against the oracle on the natural-order codes."""
+    say("decode processing order", m, n, bits, group, ko, ki)
+    c = _decode_case(67 + bits, m, n, bits, group, ko, ki)
+    perm = _perm(68, n)
+    codes = O.unpack_codes(c["stored"][:, : (n * bits + 7) // 8], bits, n).astype(np.uint8)
+    want = O.decode_matvec(O.pack_codes(codes, bits), bits, n, c["scales"], c["zeros"], group,
+                           c["si"], ki, c["so"], ko, c["sg"], c["x"], perm=perm)
+    permd = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    ldp = c["stored"].shape[1]
+    stored = kq.kronq_pack_codes(_dev_u8(codes), bits, perm=permd,
+                                 packed=torch.zeros((m, ldp), dtype=torch.uint8, device=DEV))
+    y = kq.kronq_decode_matvec(stored, n, bits, group, to_dev_f32(c["scales"]),
+                               to_dev_f32(c["zeros"]), to_dev_f32(c["si"]), ki,
+                               to_dev_f32(c["so"]), ko, to_dev_f32(c["sg"]), to_dev_f32(c["x"]),
+                               perm=permd)
+    _check_y(y, want, "processing order")
+
+
+def test_decode_of_an_act_order_layer():
+    """An act-order, grouped layer quantized by the oracle, packed in
+    processing order and decoded on the device, against the original-domain
+    quantized layer times x."""
+    say("decode of an act-order layer")
+    m, n, bits, group, ko, ki = 64, 256, 4, 64, 64, 256
+    W = synth.matrix(synth.NORMAL, 181, m, n, p1=0.02, dtype="f64")
+    X = synth.matrix(synth.ACT_T4, 182, 4 * n, n, outliers=[3, 70], out_factor=20.0, dtype="f64")
+    G = synth.matrix(synth.GRAD_LOGNORMAL, 183, 4 * m, m, p1=2.0, dtype="f64")
+    si, so = synth.signs(184, n), synth.signs(185, m)
+    Wp, HXp, HGp, sg = O.biip(W, O.gram(X), O.gram(G), si, ki, so, ko, 0.25)
+    perm, Hd = O.prepare_hessian(HXp, 0.01, True)
+    R, _ = O.chol_inv_upper(Hd)
+    res = O.gptq(Wp, R, perm, bits, group)
+    codes = np.asarray(res["codes"], dtype=np.uint8)
+    scales = res["scales"].astype(np.float32).astype(np.float64)
+    zeros = res["zeros"].astype(np.float32).astype(np.float64)
+    sg32 = np.asarray(sg, dtype=np.float32).astype(np.float64)
+    x = synth.matrix(synth.ACT_T4, 186, 1, n, dtype="f32")[0]
+    dense = O.unrotate(O.dequant(codes, scales, zeros, group, perm), si, ki, so, ko, sg32)
+    want = dense @ x.astype(np.float64)
+    permd = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    stored = kq.kronq_pack_codes(_dev_u8(codes), bits, perm=permd)
+    y = kq.kronq_decode_matvec(stored, n, bits, group, to_dev_f32(scales), to_dev_f32(zeros),
+                               to_dev_f32(si), ki, to_dev_f32(so), ko, to_dev_f32(sg32),
+                               to_dev_f32(x), perm=permd)
+    _check_y(y, want, "act-order layer")
 
 
 def test_decode_of_an_oracle_quantized_layer():
