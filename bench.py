@@ -353,7 +353,7 @@ def main():
     ws_c = torch.empty(max(1, lib.kronq_chol_inv_ws(n)), dtype=torch.uint8, device=dev)
     ws_q = torch.empty(max(1, lib.kronq_gptq_ws(m, n)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["gram_x", "gram_g", "biip", "sensitivity", "chol_inv", "gptq", "allocate"]
+    names = ["gram_x", "gram_g", "w_restore", "biip", "sensitivity", "chol_inv", "gptq", "allocate"]
 
     def step(ev=None):
         if ev is not None:
@@ -364,31 +364,34 @@ def main():
         kq.kronq_gram(Gd, HG, ws=ws_g)
         if ev is not None:
             ev[2].record(stream)
-        Wk.copy_(W0)
-        kq.kronq_biip_rotate(Wk, HX, HG, si, s.in_block, so, s.out_block, w.alpha, sg, ws=ws_b)
+        Wk.copy_(W0)   # the rotation works in place: every step starts from the same W
         if ev is not None:
             ev[3].record(stream)
-        kq.kronq_sensitivity(HX, HG, out=tr)
+        kq.kronq_biip_rotate(Wk, HX, HG, si, s.in_block, so, s.out_block, w.alpha, sg, ws=ws_b)
         if ev is not None:
             ev[4].record(stream)
-        kq.kronq_chol_inv(HX, w.lam, s.act_order, perm=perm, R=R, ws=ws_c)
+        kq.kronq_sensitivity(HX, HG, out=tr)
         if ev is not None:
             ev[5].record(stream)
+        kq.kronq_chol_inv(HX, w.lam, s.act_order, perm=perm, R=R, ws=ws_c)
+        if ev is not None:
+            ev[6].record(stream)
         kq.kronq_gptq_quantize(Wk, R, perm, s.bits, s.group, What=What, ws=ws_q, codes=codes,
                                scales=scales, zeros=zeros)
         if ev is not None:
-            ev[6].record(stream)
+            ev[7].record(stream)
         score = float(tr[2].item())
         bits = kq.kronq_allocate_bits([score], [m * n], s.bits, s.bits, s.bits * m * n)
         if ev is not None:
-            ev[7].record(stream)
+            ev[8].record(stream)
         return bits
 
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
     log("timing", args.steps, "steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -296,6 +296,275 @@ __global__ void __launch_bounds__(NTB) biip_pass2v(TParams p) {
   }
 }
 
+// ---------------------------------------------------------------- merged forward passes
+//
+// The forward transform of up to three matrices (W, H_X, H_G) in two launches:
+// pass 1 of every matrix, then pass 2 of every matrix.  The grid is persistent,
+// two workgroups per CU, each walking a run of tiles.  A workgroup issues the
+// next tile's loads (into the registers the current tile has just left) as
+// soon as the current tile sits in LDS, so its HBM reads overlap the LDS
+// butterflies and the stores of the tile before; one tile per workgroup and
+// launch would instead run every workgroup's load, butterfly and store phases
+// in lockstep and leave HBM idle during the butterflies.  Tiles are numbered
+// matrix after matrix and XCD x walks the x-th eighth of that list, so
+// neighbouring pass-2 strips, which share 128-byte lines, meet in one L2.
+// Tiles and butterflies are those of biip_pass1v / biip_pass2v.
+constexpr int kSlots = 512;   // 2 workgroups on each of the 256 CUs
+
+struct MultiParams {
+  TParams p[3];
+  int64_t end1[3], end2[3];   // cumulative pass-1 / pass-2 tile counts
+};
+
+__device__ __forceinline__ int owner(const int64_t (&end)[3], int64_t g) {
+  return (g >= end[0] ? 1 : 0) + (g >= end[1] ? 1 : 0);
+}
+
+// the tiles [lo, hi) of this workgroup's XCD; the workgroup takes every
+// nslot-th of them from lo + slot
+__device__ __forceinline__ void xcd_run(int64_t total, int64_t& lo, int64_t& hi, int& nslot) {
+  const int xcd = blockIdx.x % kXcds;
+  nslot = gridDim.x / kXcds;
+  const int64_t per = (total + kXcds - 1) / kXcds;
+  lo = xcd * per;
+  hi = min(total, lo + per);
+  lo += blockIdx.x / kXcds;
+}
+
+__device__ __forceinline__ void p1_origin(const TParams& p, int64_t t, int64_t& r0, int64_t& c0) {
+  const int64_t nb = p.C >> p.lg_c1;
+  r0 = (t / nb) * p.R1;
+  c0 = (t % nb) << p.lg_c1;
+}
+
+// issue the loads of pass-1 tile t: data, column factors (ones when absent),
+// row factors.  FULL: every tile holds 2^14 elements (no clamping).
+template <bool FULL>
+__device__ __forceinline__ void p1_issue(const TParams& p, int64_t t, float4 (&x)[ECH],
+                                         float4 (&f)[ECH], float (&g)[ECH]) {
+  int64_t r0, c0;
+  p1_origin(p, t, r0, c0);
+  const int E = FULL ? TILE : 1 << (p.lg_c1 + p.lg_r1);
+  const int cm = (1 << p.lg_c1) - 1;
+  const float* Mt = p.M + r0 * p.ld + c0;
+  const float* cf = p.col.fac;
+  const float* rf = p.row.fac + r0;
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int e = e0 < E ? e0 : 0;
+    x[i] = ld4(Mt + (int64_t)(e >> p.lg_c1) * p.ld + (e & cm));
+  }
+  if (cf) {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) {
+      const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+      f[i] = ld4(cf + c0 + ((e0 < E ? e0 : 0) & cm));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ECH; ++i) f[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+  }
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    g[i] = rf[(e0 < E ? e0 : 0) >> p.lg_c1];
+  }
+}
+
+__device__ __forceinline__ const TParams& tile_of(const MultiParams& mp, const int64_t (&end)[3],
+                                                  int64_t g, int64_t& t) {
+  const int k = owner(end, g);
+  t = g - (k ? end[k - 1] : 0);
+  return mp.p[k];
+}
+
+// pass-1 tile, loaded: factors, register butterflies, into LDS
+template <bool FULL>
+__device__ __forceinline__ void p1_stage_in(const TParams& p, float* s, float4 (&x)[ECH],
+                                            const float4 (&f)[ECH], const float (&g)[ECH]) {
+  const int lg = FULL ? LOG_TILE : p.lg_c1 + p.lg_r1;
+  const int E = 1 << lg;
+  const int nch = E >= 4 * NTB ? E / (4 * NTB) : 1;
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) x[i] = mul4(x[i], f[i], g[i]);
+  int mask_i = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) mask_i |= p1_bit(p, lg, 10 + b) ? (1 << b) : 0;
+  reg_stages(x, nch, (p1_bit(p, lg, 0) ? 1 : 0) | (p1_bit(p, lg, 1) ? 2 : 0), mask_i);
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    if (e0 < E) *reinterpret_cast<float4*>(s + pad(e0)) = x[i];
+  }
+  __syncthreads();
+}
+
+// pass-1 tile in LDS: the LDS butterflies, then back to HBM.  The stores of a
+// FULL tile are unconditional, which lets the next tile's waits leave them in
+// flight (a guarded store may not have been issued, so a wait for a load
+// issued before it would have to assume it was not).
+template <bool FULL>
+__device__ __forceinline__ void p1_finish(const TParams& p, int64_t t, float* s) {
+  int64_t r0, c0;
+  p1_origin(p, t, r0, c0);
+  const int lg = FULL ? LOG_TILE : p.lg_c1 + p.lg_r1;
+  const int E = 1 << lg;
+  const int bhi = min(lg, 10);
+  if (p.lg_c1 == p.lg_kc) {
+    lds_mid_bits(s, lg, 2, bhi);
+  } else {
+    lds_mid_bits(s, lg, 2, min(p.lg_kc, bhi));
+    lds_mid_bits(s, lg, max(p.lg_c1, 2), bhi);
+  }
+  const float nrm = p.norm1;
+  const int cm = (1 << p.lg_c1) - 1;
+  float* Mt = p.M + r0 * p.ld + c0;
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    if (e0 < E) {
+      const float4 y = *reinterpret_cast<const float4*>(s + pad(e0));
+      *reinterpret_cast<float4*>(Mt + (int64_t)(e0 >> p.lg_c1) * p.ld + (e0 & cm)) =
+          make_float4(y.x * nrm, y.y * nrm, y.z * nrm, y.w * nrm);
+    }
+  }
+}
+
+// The loop is rotated so that inside it the next tile's loads are always
+// followed by this tile's stores: the waits for those loads then leave the
+// stores in flight.
+template <bool FULL>
+__global__ void __launch_bounds__(NTB) __attribute__((amdgpu_waves_per_eu(2))) biip_pass1m(MultiParams mp) {
+  extern __shared__ __align__(16) float s[];
+  int64_t gt, hi, t;
+  int nslot;
+  xcd_run(mp.end1[2], gt, hi, nslot);
+  if (gt >= hi) return;
+  float4 x[ECH], f[ECH];
+  float g[ECH];
+  {
+    const TParams& p = tile_of(mp, mp.end1, gt, t);
+    p1_issue<FULL>(p, t, x, f, g);
+    p1_stage_in<FULL>(p, s, x, f, g);
+  }
+  for (;;) {
+    const TParams& p = tile_of(mp, mp.end1, gt, t);
+    const int64_t gn = gt + nslot;
+    if (gn >= hi) {
+      p1_finish<FULL>(p, t, s);
+      break;
+    }
+    int64_t tn;
+    const TParams& pn = tile_of(mp, mp.end1, gn, tn);
+    p1_issue<FULL>(pn, tn, x, f, g);
+    p1_finish<FULL>(p, t, s);
+    __syncthreads();   // every thread has read the tile before the next one is written
+    p1_stage_in<FULL>(pn, s, x, f, g);
+    gt = gn;
+  }
+}
+
+struct P2Origin {
+  int64_t rbase, cbase;
+};
+
+__device__ __forceinline__ P2Origin p2_origin(const TParams& p, int64_t t) {
+  const int64_t strip = t % p.strips;
+  const int64_t rest = t / p.strips;
+  return P2Origin{(rest / p.R1) * p.row.block + rest % p.R1, strip << p.lg_cw};
+}
+
+// issue the loads of pass-2 tile t.  Columns past C read a valid element of
+// the tile instead; pass 2 mixes only the row bits, so such a column never
+// meets a valid one and is never stored.  FULL: every tile holds 2^14
+// elements and every strip lies inside the matrix.
+template <bool FULL>
+__device__ __forceinline__ void p2_issue(const TParams& p, int64_t t, float4 (&x)[ECH]) {
+  const P2Origin o = p2_origin(p, t);
+  const int E = FULL ? TILE : 1 << (p.lg_rows2 + p.lg_cw);
+  const int cm = (1 << p.lg_cw) - 1;
+  const float* base = p.M + o.rbase * p.ld + o.cbase;
+  const int64_t rstride = p.R1 * p.ld;
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int e = e0 < E ? e0 : 0;
+    const int c = e & cm;
+    const bool in = FULL || o.cbase + c < p.C;
+    x[i] = ld4(base + (in ? (int64_t)(e >> p.lg_cw) * rstride + c : 0));
+  }
+}
+
+template <bool FULL>
+__device__ __forceinline__ void p2_stage_in(const TParams& p, float* s, float4 (&x)[ECH]) {
+  const int lg = FULL ? LOG_TILE : p.lg_rows2 + p.lg_cw;
+  const int E = 1 << lg;
+  const int nch = E >= 4 * NTB ? E / (4 * NTB) : 1;
+  int mask_i = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) mask_i |= (10 + b >= p.lg_cw && 10 + b < lg) ? (1 << b) : 0;
+  reg_stages(x, nch, 0, mask_i);   // bits 0-1 are column bits (cw >= 4)
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    if (e0 < E) *reinterpret_cast<float4*>(s + pad(e0)) = x[i];
+  }
+  __syncthreads();
+}
+
+template <bool FULL>
+__device__ __forceinline__ void p2_finish(const TParams& p, int64_t t, float* s) {
+  const P2Origin o = p2_origin(p, t);
+  const int lg = FULL ? LOG_TILE : p.lg_rows2 + p.lg_cw;
+  const int E = 1 << lg;
+  lds_mid_bits(s, lg, max(p.lg_cw, 2), min(lg, 10));
+  const float nrm = p.norm2;
+  const int cm = (1 << p.lg_cw) - 1;
+  float* base = p.M + o.rbase * p.ld + o.cbase;
+  const int64_t rstride = p.R1 * p.ld;
+#pragma unroll
+  for (int i = 0; i < ECH; ++i) {
+    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int c = e0 & cm;
+    if (FULL || (e0 < E && o.cbase + c < p.C)) {
+      const float4 y = *reinterpret_cast<const float4*>(s + pad(e0));
+      *reinterpret_cast<float4*>(base + (int64_t)(e0 >> p.lg_cw) * rstride + c) =
+          make_float4(y.x * nrm, y.y * nrm, y.z * nrm, y.w * nrm);
+    }
+  }
+}
+
+template <bool FULL>
+__global__ void __launch_bounds__(NTB) __attribute__((amdgpu_waves_per_eu(2))) biip_pass2m(MultiParams mp) {
+  extern __shared__ __align__(16) float s[];
+  int64_t gt, hi, t;
+  int nslot;
+  xcd_run(mp.end2[2], gt, hi, nslot);
+  if (gt >= hi) return;
+  float4 x[ECH];
+  {
+    const TParams& p = tile_of(mp, mp.end2, gt, t);
+    p2_issue<FULL>(p, t, x);
+    p2_stage_in<FULL>(p, s, x);
+  }
+  for (;;) {
+    const TParams& p = tile_of(mp, mp.end2, gt, t);
+    const int64_t gn = gt + nslot;
+    if (gn >= hi) {
+      p2_finish<FULL>(p, t, s);
+      break;
+    }
+    int64_t tn;
+    const TParams& pn = tile_of(mp, mp.end2, gn, tn);
+    p2_issue<FULL>(pn, tn, x);
+    p2_finish<FULL>(p, t, s);
+    __syncthreads();   // every thread has read the tile before the next one is written
+    p2_stage_in<FULL>(pn, s, x);
+    gt = gn;
+  }
+}
+
 // ---------------------------------------------------------------- scalar passes
 // (widths that are not a multiple of 4): one element a thread at a time
 
@@ -403,9 +672,15 @@ int64_t pow2_floor(int64_t x) {
   return p;
 }
 
-kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr, const float* rfac,
-                         int64_t kc, const float* cfac, hipStream_t st, bool post = false) {
-  TParams p{};
+struct Plan {
+  TParams p;
+  bool vec1, vec2;
+};
+
+Plan plan2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr, const float* rfac, int64_t kc,
+            const float* cfac, bool post) {
+  Plan pl{};
+  TParams& p = pl.p;
   p.post = post;
   p.M = M;
   p.R = R;
@@ -432,23 +707,84 @@ kronq_status transform2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr,
   p.tiles2 = (rows2 > 1) ? (R / kr) * p.R1 * p.strips : 0;
   p.per_xcd1 = (int)((p.tiles1 + kXcds - 1) / kXcds);
   p.per_xcd2 = (int)((p.tiles2 + kXcds - 1) / kXcds);
-  const bool vec1 = (c1 % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0) &&
-                    ((uintptr_t)cfac % 16 == 0);
-  const bool vec2 = (cw % 4 == 0) && (C % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0);
+  pl.vec1 = (c1 % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0) &&
+            ((uintptr_t)cfac % 16 == 0);
+  pl.vec2 = (cw % 4 == 0) && (C % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)M % 16 == 0);
+  return pl;
+}
+
+// one matrix, one workgroup per tile
+kronq_status launch2d(const Plan& pl, hipStream_t st) {
+  const TParams& p = pl.p;
   const size_t lds1 = padded(1 << (p.lg_c1 + p.lg_r1)) * sizeof(float);
   const size_t lds2 = padded(1 << (p.lg_rows2 + p.lg_cw)) * sizeof(float);
   const size_t ldsmax = padded(TILE) * sizeof(float);
   {
-    auto k1 = vec1 ? biip_pass1v : biip_pass1s;
+    auto k1 = pl.vec1 ? biip_pass1v : biip_pass1s;
     KQ_HIP(hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
-    hipLaunchKernelGGL(k1, dim3(p.per_xcd1 * kXcds), dim3(vec1 ? NTB : NT), lds1, st, p);
+    hipLaunchKernelGGL(k1, dim3(p.per_xcd1 * kXcds), dim3(pl.vec1 ? NTB : NT), lds1, st, p);
     KQ_LAUNCHED("biip_pass1");
   }
   if (p.tiles2) {
-    auto k2 = vec2 ? biip_pass2v : biip_pass2s;
+    auto k2 = pl.vec2 ? biip_pass2v : biip_pass2s;
     KQ_HIP(hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
-    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(vec2 ? NTB : NT), lds2, st, p);
+    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(pl.vec2 ? NTB : NT), lds2, st, p);
     KQ_LAUNCHED("biip_pass2");
+  }
+  return KRONQ_OK;
+}
+
+// forward transforms of n <= 3 matrices: the merged persistent passes when
+// every matrix takes the vector path, else one matrix at a time
+kronq_status launch_forward(const Plan* pl, int n, hipStream_t st) {
+  bool merged = n > 0;
+  for (int k = 0; k < n; ++k)
+    merged = merged && !pl[k].p.post && pl[k].p.row.fac && pl[k].vec1 &&
+             (pl[k].vec2 || pl[k].p.tiles2 == 0);
+  if (!merged) {
+    for (int k = 0; k < n; ++k) {
+      const kronq_status s = launch2d(pl[k], st);
+      if (s) return s;
+    }
+    return KRONQ_OK;
+  }
+  MultiParams mp{};
+  int64_t t1 = 0, t2 = 0;
+  for (int k = 0; k < 3; ++k) {
+    if (k < n) {
+      mp.p[k] = pl[k].p;
+      t1 += pl[k].p.tiles1;
+      t2 += pl[k].p.tiles2;
+    }
+    mp.end1[k] = t1;
+    mp.end2[k] = t2;
+  }
+  if (t1 == 0) return KRONQ_OK;
+  // full tiles everywhere (2^14 elements, pass-2 strips inside the matrix):
+  // the variant without bounds checks
+  bool full1 = true, full2 = true;
+  for (int k = 0; k < n; ++k) {
+    const TParams& p = pl[k].p;
+    full1 = full1 && p.lg_c1 + p.lg_r1 == LOG_TILE;
+    if (p.tiles2)
+      full2 = full2 && p.lg_rows2 + p.lg_cw == LOG_TILE && p.C % (int64_t(1) << p.lg_cw) == 0;
+  }
+  const size_t ldsmax = padded(TILE) * sizeof(float);
+  auto grid = [](int64_t tiles) {
+    const int64_t g = std::min<int64_t>((tiles + kXcds - 1) / kXcds * kXcds, kSlots);
+    return dim3((unsigned)g);
+  };
+  {
+    auto k1 = full1 ? biip_pass1m<true> : biip_pass1m<false>;
+    KQ_HIP(hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
+    hipLaunchKernelGGL(k1, grid(t1), dim3(NTB), ldsmax, st, mp);
+    KQ_LAUNCHED("biip_pass1m");
+  }
+  if (t2) {
+    auto k2 = full2 ? biip_pass2m<true> : biip_pass2m<false>;
+    KQ_HIP(hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
+    hipLaunchKernelGGL(k2, grid(t2), dim3(NTB), ldsmax, st, mp);
+    KQ_LAUNCHED("biip_pass2m");
   }
   return KRONQ_OK;
 }
@@ -474,20 +810,14 @@ kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
   // an identity side (block 1, no signs) leaves its factor alone: V = I keeps
   // H_X, U = I without a rescale keeps H_G (and W when both sides are so)
   const bool v_id = in.block == 1 && !in.signs, u_id = out.block == 1 && !out.signs;
-  kronq_status st = KRONQ_OK;
-  if (!(v_id && u_id && alpha == 0.0f)) {
-    st = transform2d(W, m, n, ldw, out.block, rfW, in.block, in.signs, s);
-    if (st) return st;
-  }
-  if (HX && !v_id) {
-    st = transform2d(HX, n, n, ldhx, in.block, in.signs, in.block, in.signs, s);
-    if (st) return st;
-  }
-  if (HG && !(u_id && alpha == 0.0f)) {
-    st = transform2d(HG, m, m, ldhg, out.block, rfG, out.block, rfG, s);
-    if (st) return st;
-  }
-  return KRONQ_OK;
+  Plan pl[3];
+  int n_mat = 0;
+  if (!(v_id && u_id && alpha == 0.0f))
+    pl[n_mat++] = plan2d(W, m, n, ldw, out.block, rfW, in.block, in.signs, false);
+  if (HX && !v_id) pl[n_mat++] = plan2d(HX, n, n, ldhx, in.block, in.signs, in.block, in.signs, false);
+  if (HG && !(u_id && alpha == 0.0f))
+    pl[n_mat++] = plan2d(HG, m, m, ldhg, out.block, rfG, out.block, rfG, false);
+  return launch_forward(pl, n_mat, s);
 }
 
 size_t unrotate_ws_bytes(int64_t m) { return align_up((size_t)m * sizeof(float), 256); }
@@ -498,7 +828,7 @@ kronq_status unrotate_launch(float* W, int64_t m, int64_t n, int64_t ldw, const 
   hipLaunchKernelGGL(unrotate_prep, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, out.signs,
                      sg, m, rf);
   KQ_LAUNCHED("unrotate_prep");
-  return transform2d(W, m, n, ldw, out.block, rf, in.block, in.signs, s, true);
+  return launch2d(plan2d(W, m, n, ldw, out.block, rf, in.block, in.signs, true), s);
 }
 
 }  // namespace kronq
