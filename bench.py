@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode measurement (prints its own JSON line)")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--configs", action="store_true",
+                    help="only time every sublayer of the other workloads (tiny linear, Llama-2-7B "
+                         "down_proj, Llama-3-8B block, Llama-3-70B MLP; prints its own JSON line)")
+    ap.add_argument("--config-steps", type=int, default=2, help="timed steps per sublayer (--configs)")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gram_bf16_llama2_7b_q_proj_traffic.json"))
@@ -291,6 +295,135 @@ def decode_leg(steps, warmup, n_layers=32, bits=4, group=128, sublayers=DECODE_S
             "data": "synthetic codes, grids, signs and x (seeded torch generator)"}
 
 
+CONFIG_LEG_WORKLOADS = ("tiny_linear_256", "llama2_7b_down_proj", "llama3_8b_block", "llama3_70b_mlp")
+
+
+def configs_leg(steps, warmup, names=CONFIG_LEG_WORKLOADS):
+    """Per-sublayer quantize wall time of the other workloads, on inputs generated
+    in device memory; reported apart from the headline value.  A sublayer's path
+    is both Grams, BiIP, sensitivity, the damped inverse Cholesky factor and the
+    column loop.  Where bits are allocated (the Llama-3-8B block) the method needs
+    every sublayer's score first: each sublayer is rotated, scored and factored,
+    the block's bits are allocated, then each column loop runs.  Sublayers that
+    share an input are timed as if each computed its own X Gram (the method
+    computes it once per input)."""
+    import torch
+    import post_quantization_02_amd as kq
+    from synth import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, nev):
+        """warmup + steps repetitions of fn(ev); mean ms between consecutive events"""
+        for _ in range(warmup):
+            fn(None)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        for k in range(steps):
+            fn(evs[k])
+        torch.cuda.synchronize()
+        return [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+                for i in range(nev - 1)]
+
+    out = []
+    for wname in names:
+        w = WL.BY_NAME[wname]
+        log("configs leg:", wname)
+        N = w.N
+        Xd, xname = None, None
+        held = {}
+        rows = []
+        for s in w.sublayers:
+            if s.x != xname:
+                Xd = None
+                torch.cuda.empty_cache()
+                Xd, xname = w.gen_x_dev(s.x), s.x
+            log("  rotate, score, factor:", s.name, s.m, "x", s.n)
+            Gd = w.gen_g_dev(s.name)
+            W0 = torch.from_numpy(w.w_f32(s.name)).to(dev)
+            si = torch.from_numpy(w.in_signs(s.x)).to(dev)
+            so = torch.from_numpy(w.out_signs(s.name)).to(dev)
+            m, n = s.m, s.n
+            HX = torch.empty((n, n), dtype=torch.float32, device=dev)
+            HG = torch.empty((m, m), dtype=torch.float32, device=dev)
+            Wk = torch.empty_like(W0)
+            sg = torch.empty(m, dtype=torch.float32, device=dev)
+            tr = torch.empty(3, dtype=torch.float64, device=dev)
+            R = torch.empty((n, n), dtype=torch.float32, device=dev)
+            perm = torch.empty(n, dtype=torch.int32, device=dev)
+
+            def phase_a(ev):
+                if ev is not None:
+                    ev[0].record(stream)
+                kq.kronq_gram(Xd, HX)
+                if ev is not None:
+                    ev[1].record(stream)
+                kq.kronq_gram(Gd, HG)
+                if ev is not None:
+                    ev[2].record(stream)
+                Wk.copy_(W0)
+                if ev is not None:
+                    ev[3].record(stream)
+                kq.kronq_biip_rotate(Wk, HX, HG, si, s.in_block, so, s.out_block, w.alpha, sg)
+                if ev is not None:
+                    ev[4].record(stream)
+                kq.kronq_sensitivity(HX, HG, out=tr)
+                if ev is not None:
+                    ev[5].record(stream)
+                kq.kronq_chol_inv(HX, w.lam, s.act_order, perm=perm, R=R)
+                if ev is not None:
+                    ev[6].record(stream)
+
+            ta = timed(phase_a, 7)
+            held[s.name] = (Wk, R, perm)
+            rows.append({"sublayer": s.name, "m": m, "n": n, "in_block": s.in_block,
+                         "out_block": s.out_block, "group": s.group, "act_order": s.act_order,
+                         "score": float(tr[2].item()),
+                         "stage_ms": dict(zip(("gram_x", "gram_g", "w_restore", "biip", "sensitivity",
+                                               "chol_inv"), ta)),
+                         "gram_x_tflops": N * n * (n + 1) / (ta[0] * 1e-3) / 1e12,
+                         "gram_g_tflops": N * m * (m + 1) / (ta[1] * 1e-3) / 1e12,
+                         "fwht_gbs": 16.0 * (m * n + n * n + m * m) / (ta[3] * 1e-3) / 1e9})
+            del Gd, HX, HG, sg, tr, W0
+            torch.cuda.empty_cache()
+        Xd = None
+        torch.cuda.empty_cache()
+        nparams = w.n_params()
+        if any(s.bits <= 0 for s in w.sublayers):
+            budget = int(round(w.avg_bits * sum(nparams)))
+            t0 = time.perf_counter()
+            bits = kq.kronq_allocate_bits([r["score"] for r in rows], nparams, 2, 4, budget)
+            alloc_ms = (time.perf_counter() - t0) * 1e3
+        else:
+            bits = [s.bits for s in w.sublayers]
+            alloc_ms = 0.0
+        for s, r, b in zip(w.sublayers, rows, bits):
+            log("  column loop:", s.name, "bits", b)
+            Wk, R, perm = held.pop(s.name)
+            res = kq.kronq_gptq_quantize(Wk, R, perm, b, s.group)
+
+            def phase_b(ev):
+                if ev is not None:
+                    ev[0].record(stream)
+                kq.kronq_gptq_quantize(Wk, R, perm, b, s.group, What=res["What"], codes=res["codes"],
+                                       scales=res["scales"], zeros=res["zeros"])
+                if ev is not None:
+                    ev[1].record(stream)
+
+            r["bits"] = b
+            r["stage_ms"]["gptq"] = timed(phase_b, 2)[0]
+            st = r["stage_ms"]
+            r["ms"] = sum(v for k, v in st.items() if k != "w_restore") + alloc_ms / len(rows)
+            del Wk, R, perm, res
+            torch.cuda.empty_cache()
+        out.append({"workload": w.name, "N": N, "x_dtype": w.dtype, "alpha": w.alpha, "damp": w.lam,
+                    "allocation_ms": alloc_ms, "sublayers": rows,
+                    "total_ms": sum(r["ms"] for r in rows)})
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -303,6 +436,10 @@ def main():
         print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.configs:
+        log("configs leg only")
+        print(json.dumps({"configs": configs_leg(args.config_steps, 1)}), flush=True)
+        return
     if args.decode_only:
         log("decode leg only")
         print(json.dumps({"decode": decode_leg(args.decode_steps, 3),
