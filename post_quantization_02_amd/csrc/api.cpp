@@ -50,6 +50,66 @@ static kronq_status check_had(const kronq_had* h, int64_t dim, const char* side)
   return KRONQ_OK;
 }
 
+// Argument checks of the individual calls (no workspace).
+static kronq_status check_gram(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda,
+                               const float* H, int64_t ldh, float scale, float beta) {
+  if (!A || !H) return fail(KRONQ_EINVAL, "kronq_gram: NULL pointer");
+  if (dtype != KRONQ_F32 && dtype != KRONQ_BF16)
+    return fail(KRONQ_EINVAL, "kronq_gram: dtype %d", (int)dtype);
+  if (N < 1 || d < 1) return fail(KRONQ_EINVAL, "kronq_gram: N=%lld d=%lld", (long long)N, (long long)d);
+  if (lda < d || ldh < d) return fail(KRONQ_EINVAL, "kronq_gram: leading dimension below d");
+  if (!aligned(A, 16) || !aligned(H, 16))
+    return fail(KRONQ_EINVAL, "kronq_gram: A and H must be 16-byte aligned");
+  if ((dtype == KRONQ_BF16 && lda % 8) || (dtype == KRONQ_F32 && lda % 4))
+    return fail(KRONQ_EINVAL, "kronq_gram: lda must be a multiple of 16 bytes");
+  if (!std::isfinite(scale) || !std::isfinite(beta))
+    return fail(KRONQ_EINVAL, "kronq_gram: scale/beta not finite");
+  return KRONQ_OK;
+}
+
+static kronq_status check_biip(const float* W, int64_t m, int64_t n, int64_t ldw, const float* HX,
+                               int64_t ldhx, const float* HG, int64_t ldhg,
+                               const kronq_had* in_side, const kronq_had* out_side, float alpha) {
+  if (!W) return fail(KRONQ_EINVAL, "kronq_biip_rotate: W is NULL");
+  if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "kronq_biip_rotate: bad W shape");
+  if (HX && ldhx < n) return fail(KRONQ_EINVAL, "kronq_biip_rotate: ldhx < n");
+  if (HG && ldhg < m) return fail(KRONQ_EINVAL, "kronq_biip_rotate: ldhg < m");
+  if (!std::isfinite(alpha)) return fail(KRONQ_EINVAL, "kronq_biip_rotate: alpha not finite");
+  if (alpha != 0.0f && !HG)
+    return fail(KRONQ_EINVAL, "kronq_biip_rotate: the output rescale needs HG");
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  return check_had(out_side, m, "output-side");
+}
+
+static kronq_status check_chol(const float* H, int64_t n, int64_t ldh, float lambda,
+                               const int32_t* perm, const float* R, int64_t ldr,
+                               const int64_t* info) {
+  if (!H || !R || !perm || !info) return fail(KRONQ_EINVAL, "kronq_chol_inv: NULL pointer");
+  if (n < 1 || ldh < n || ldr < n) return fail(KRONQ_EINVAL, "kronq_chol_inv: bad shape");
+  if (!(lambda >= 0.0f) || !std::isfinite(lambda))
+    return fail(KRONQ_EINVAL, "kronq_chol_inv: lambda must be finite and >= 0");
+  return KRONQ_OK;
+}
+
+static kronq_status check_gptq(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
+                               int64_t ldr, const kronq_qcfg* q, const uint8_t* codes,
+                               const float* scales, const float* zeros, const float* What) {
+  if (!W || !R || !q || !codes || !scales || !zeros)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: NULL pointer");
+  if (m < 1 || n < 1 || ldw < n || ldr < n)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bad shape");
+  if (!aligned(R, 16) || ldr % 4 != 0)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: R must be 16-byte aligned with ldr a multiple of 4");
+  if (q->bits < 1 || q->bits > 8)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bits %d outside 1..8", (int)q->bits);
+  if (q->group > 0 && n % q->group)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: group %d does not divide n", (int)q->group);
+  if (What == W && ldw != n)
+    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: What may alias W only when ldw == n");
+  return KRONQ_OK;
+}
+
 }  // namespace kronq
 
 using namespace kronq;
@@ -80,17 +140,8 @@ size_t kronq_gram_ws(int64_t N, int64_t d, int32_t dtype) {
 kronq_status kronq_gram(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda, float* H,
                         int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
                         void* stream) {
-  if (!A || !H) return fail(KRONQ_EINVAL, "kronq_gram: NULL pointer");
-  if (dtype != KRONQ_F32 && dtype != KRONQ_BF16)
-    return fail(KRONQ_EINVAL, "kronq_gram: dtype %d", (int)dtype);
-  if (N < 1 || d < 1) return fail(KRONQ_EINVAL, "kronq_gram: N=%lld d=%lld", (long long)N, (long long)d);
-  if (lda < d || ldh < d) return fail(KRONQ_EINVAL, "kronq_gram: leading dimension below d");
-  if (!aligned(A, 16) || !aligned(H, 16))
-    return fail(KRONQ_EINVAL, "kronq_gram: A and H must be 16-byte aligned");
-  if ((dtype == KRONQ_BF16 && lda % 8) || (dtype == KRONQ_F32 && lda % 4))
-    return fail(KRONQ_EINVAL, "kronq_gram: lda must be a multiple of 16 bytes");
-  if (!std::isfinite(scale) || !std::isfinite(beta))
-    return fail(KRONQ_EINVAL, "kronq_gram: scale/beta not finite");
+  kronq_status st = check_gram(A, dtype, N, d, lda, H, ldh, scale, beta);
+  if (st) return st;
   size_t need = gram_ws_bytes(N, d, dtype);
   if (ws_bytes < need || (need && !ws))
     return fail(KRONQ_EWORKSPACE, "kronq_gram: workspace %zu < %zu bytes", ws_bytes, need);
@@ -106,16 +157,7 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
                                int64_t ldhx, float* HG, int64_t ldhg, const kronq_had* in_side,
                                const kronq_had* out_side, float alpha, float* sg, void* ws,
                                size_t ws_bytes, void* stream) {
-  if (!W) return fail(KRONQ_EINVAL, "kronq_biip_rotate: W is NULL");
-  if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "kronq_biip_rotate: bad W shape");
-  if (HX && ldhx < n) return fail(KRONQ_EINVAL, "kronq_biip_rotate: ldhx < n");
-  if (HG && ldhg < m) return fail(KRONQ_EINVAL, "kronq_biip_rotate: ldhg < m");
-  if (!std::isfinite(alpha)) return fail(KRONQ_EINVAL, "kronq_biip_rotate: alpha not finite");
-  if (alpha != 0.0f && !HG)
-    return fail(KRONQ_EINVAL, "kronq_biip_rotate: the output rescale needs HG");
-  kronq_status st = check_had(in_side, n, "input-side");
-  if (st) return st;
-  st = check_had(out_side, m, "output-side");
+  kronq_status st = check_biip(W, m, n, ldw, HX, ldhx, HG, ldhg, in_side, out_side, alpha);
   if (st) return st;
   size_t need = biip_ws_bytes(m, n);
   if (ws_bytes < need || (need && !ws))
@@ -153,10 +195,8 @@ kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda
                             int32_t act_order, int32_t* perm, float* R, int64_t ldr,
                             int64_t* info, void* ws, size_t ws_bytes, void* stream) {
   if (info) *info = -1;
-  if (!H || !R || !perm || !info) return fail(KRONQ_EINVAL, "kronq_chol_inv: NULL pointer");
-  if (n < 1 || ldh < n || ldr < n) return fail(KRONQ_EINVAL, "kronq_chol_inv: bad shape");
-  if (!(lambda >= 0.0f) || !std::isfinite(lambda))
-    return fail(KRONQ_EINVAL, "kronq_chol_inv: lambda must be finite and >= 0");
+  kronq_status st = check_chol(H, n, ldh, lambda, perm, R, ldr, info);
+  if (st) return st;
   size_t need = chol_ws_bytes(n);
   if (ws_bytes < need || (need && !ws))
     return fail(KRONQ_EWORKSPACE, "kronq_chol_inv: workspace %zu < %zu bytes", ws_bytes, need);
@@ -174,18 +214,8 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
                                  const kronq_qcfg* q, uint8_t* codes, float* scales,
                                  float* zeros, float* What, float* pre_round, void* ws,
                                  size_t ws_bytes, void* stream) {
-  if (!W || !R || !q || !codes || !scales || !zeros)
-    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: NULL pointer");
-  if (m < 1 || n < 1 || ldw < n || ldr < n)
-    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bad shape");
-  if (!aligned(R, 16) || ldr % 4 != 0)
-    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: R must be 16-byte aligned with ldr a multiple of 4");
-  if (q->bits < 1 || q->bits > 8)
-    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: bits %d outside 1..8", (int)q->bits);
-  if (q->group > 0 && n % q->group)
-    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: group %d does not divide n", (int)q->group);
-  if (What == W && ldw != n)
-    return fail(KRONQ_EINVAL, "kronq_gptq_quantize: What may alias W only when ldw == n");
+  kronq_status st = check_gptq(W, m, n, ldw, R, ldr, q, codes, scales, zeros, What);
+  if (st) return st;
   size_t need = gptq_ws_bytes(m, n);
   if (ws_bytes < need || (need && !ws))
     return fail(KRONQ_EWORKSPACE, "kronq_gptq_quantize: workspace %zu < %zu bytes", ws_bytes, need);
