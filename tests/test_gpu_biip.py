@@ -30,6 +30,8 @@ def _case(m, n, seed):
     (512, 96, 8, 32, 0.5),          # small blocks
     (128, 1376, 128, 32, 0.25),     # 43 blocks on the input side
     (96, 64, 1, 2, 0.25),           # block 1 (no mixing) on the output side
+    (24, 6, 8, 2, 0.25),            # width not a multiple of 4: every matrix on the scalar kernels
+    (16, 16, 16, 16, 0.25),         # three tiles in all: most persistent workgroups have none
 ])
 def test_biip_small(m, n, ko, ki, alpha):
     say("biip", m, n, ko, ki, alpha)
