@@ -21,14 +21,15 @@
 //           the remaining kr/R1 part of the row-side transform (skipped when
 //           R1 == kr).
 // Each pass stages its tile (up to 2^14 floats = 64 KiB, so that two
-// workgroups share a CU and overlap each other's HBM and LDS phases) in LDS
-// and runs the
-// butterflies radix-16: a thread gathers 16 elements differing in 4 index bits,
-// does 4 butterfly stages in registers and scatters them back.  HBM traffic is
-// float4 and coalesced (rows of a column block are contiguous; pass-2 strips
-// are >= 64 B wide).  LDS rows are padded by 4 floats per 32 so that
-// float4-aligned accesses stay 16-byte aligned and the low-bit rounds are
-// bank-conflict free.
+// workgroups share a CU) in LDS and runs the butterflies radix-16: a thread
+// gathers 16 elements differing in 4 index bits, does 4 butterfly stages in
+// registers and scatters them back.  HBM traffic is float4 and coalesced (rows
+// of a column block are contiguous; pass-2 strips are >= 64 B wide).  LDS rows
+// are padded by 4 floats per 32 so that float4-aligned accesses stay 16-byte
+// aligned and the low-bit rounds are bank-conflict free.  The forward
+// transform of W, H_X and H_G runs as two persistent launches, pass 1 of all
+// three and then pass 2 of all three (biip_pass1m / biip_pass2m); the
+// inverse and widths that are not a multiple of 4 run one matrix at a time.
 #include "kronq_internal.h"
 #include "wht_lds.h"
 
