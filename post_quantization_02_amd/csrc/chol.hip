@@ -161,6 +161,34 @@ __global__ void __launch_bounds__(256) chol_gather(const float* H, int64_t n, in
   }
 }
 
+// The same for the identity permutation with n, ldh multiples of 4 and H
+// 16-byte aligned: four consecutive outputs of a row are one aligned float4
+// of the reversed source row, read backwards.
+__global__ void __launch_bounds__(256) chol_gather_id4(const float* H, int64_t n, int64_t ldh,
+                                                       int64_t npad, CholWs w) {
+  const int64_t a = blockIdx.y;
+  const float damp = (float)*w.damp;
+  for (int64_t b = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); b < npad; b += 4 * (int64_t)gridDim.x * 256) {
+    float v[4], e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[k] = (a == b + k) ? 1.f : 0.f;
+    if (a < n && b < n) {
+      const float4 x = *reinterpret_cast<const float4*>(H + (n - 1 - a) * ldh + (n - 4 - b));
+      v[0] = x.w;
+      v[1] = x.z;
+      v[2] = x.y;
+      v[3] = x.x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = (a == b + k) ? v[k] + damp : v[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = e[k];
+    }
+    *reinterpret_cast<float4*>(w.A + a * npad + b) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(w.B + a * npad + b) = make_float4(e[0], e[1], e[2], e[3]);
+  }
+}
+
 // ------------------------------------------------------- diagonal block
 //
 // Factor the diagonal block S = A_pp = L L^T and invert L (fp64, one
@@ -726,6 +754,24 @@ __global__ void __launch_bounds__(256) chol_flip(int64_t n, int64_t npad, float*
     R[a * ldr + b] = (b >= a) ? w.B[(n - 1 - a) * npad + (n - 1 - b)] : 0.f;
 }
 
+// The same with n, ldr multiples of 4 and R 16-byte aligned: four outputs of a
+// row from one aligned float4 of the reversed source row.
+__global__ void __launch_bounds__(256) chol_flip4(int64_t n, int64_t npad, float* R, int64_t ldr,
+                                                  CholWs w) {
+  if (*w.flag) return;
+  const int64_t a = blockIdx.y;
+  for (int64_t b = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); b < n; b += 4 * (int64_t)gridDim.x * 256) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (b + 3 >= a) {
+      const float4 x = *reinterpret_cast<const float4*>(w.B + (n - 1 - a) * npad + (n - 4 - b));
+      const float y[4] = {x.w, x.z, x.y, x.x};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = (b + k >= a) ? y[k] : 0.f;
+    }
+    *reinterpret_cast<float4*>(R + a * ldr + b) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 }  // namespace
 
 size_t chol_ws_bytes(int64_t n) { return ws_layout(n, nullptr, nullptr); }
@@ -748,9 +794,16 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
     KQ_LAUNCHED("chol_identity_perm");
   }
   {
-    const unsigned gx = (unsigned)std::min<int64_t>((npad + 255) / 256, 64);
-    hipLaunchKernelGGL(chol_gather, dim3(gx, (unsigned)npad), dim3(256), 0, s, H, n, ldh,
-                       (const int32_t*)perm, npad, w);
+    // (A and B sit at 256-byte offsets in the workspace: aligned with it)
+    const bool ws16 = reinterpret_cast<uintptr_t>(w.A) % 16 == 0;
+    if (!act_order && ws16 && n % 4 == 0 && ldh % 4 == 0 && reinterpret_cast<uintptr_t>(H) % 16 == 0) {
+      const unsigned gx = (unsigned)std::min<int64_t>((npad / 4 + 255) / 256, 64);
+      hipLaunchKernelGGL(chol_gather_id4, dim3(gx, (unsigned)npad), dim3(256), 0, s, H, n, ldh, npad, w);
+    } else {
+      const unsigned gx = (unsigned)std::min<int64_t>((npad + 255) / 256, 64);
+      hipLaunchKernelGGL(chol_gather, dim3(gx, (unsigned)npad), dim3(256), 0, s, H, n, ldh,
+                         (const int32_t*)perm, npad, w);
+    }
     KQ_LAUNCHED("chol_gather");
   }
   // one stream: step p (diagonal block p with U2 of step p - 1), the panels
@@ -771,7 +824,13 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
   }
   {
     const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 64);
-    hipLaunchKernelGGL(chol_flip, dim3(gx, (unsigned)n), dim3(256), 0, s, n, npad, R, ldr, w);
+    if (reinterpret_cast<uintptr_t>(w.B) % 16 == 0 && n % 4 == 0 && ldr % 4 == 0 &&
+        reinterpret_cast<uintptr_t>(R) % 16 == 0) {
+      const unsigned gx4 = (unsigned)std::min<int64_t>((n / 4 + 255) / 256, 64);
+      hipLaunchKernelGGL(chol_flip4, dim3(gx4, (unsigned)n), dim3(256), 0, s, n, npad, R, ldr, w);
+    } else {
+      hipLaunchKernelGGL(chol_flip, dim3(gx, (unsigned)n), dim3(256), 0, s, n, npad, R, ldr, w);
+    }
     KQ_LAUNCHED("chol_flip");
   }
   long long h_info = -1;
