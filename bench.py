@@ -433,8 +433,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the whole path on a single MI355X "
+              "and does not shard it across GPUs (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.configs:
         log("configs leg only")

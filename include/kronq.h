@@ -46,7 +46,7 @@ typedef int32_t kronq_status;
 #define KRONQ_ENOTPD 2         /* damped H not positive definite */
 #define KRONQ_EHIP 3           /* HIP runtime error */
 #define KRONQ_EWORKSPACE 4     /* workspace smaller than the *_ws() size */
-#define KRONQ_EUNSUPPORTED 5   /* valid request this build does not implement */
+#define KRONQ_EUNSUPPORTED 5   /* valid request the library does not implement */
 
 #define KRONQ_F32 0            /* element type codes for kronq_gram */
 #define KRONQ_BF16 1
