@@ -20,7 +20,9 @@
  *   - Device pointers are HIP device memory owned by the caller; the library
  *     never allocates, frees or retains caller memory.  Calls that need scratch
  *     memory take a caller-provided device workspace `ws` of at least the size
- *     returned by the matching *_ws() query (KRONQ_EWORKSPACE otherwise).
+ *     returned by the matching *_ws() query (KRONQ_EWORKSPACE otherwise),
+ *     16-byte aligned (KRONQ_EINVAL otherwise; any hipMalloc or torch
+ *     allocation is).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls are
  *     asynchronous on `stream` except kronq_chol_inv, which synchronizes it.
  *   - Arguments are validated on the host before anything is launched; an

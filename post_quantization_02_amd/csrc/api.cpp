@@ -50,6 +50,16 @@ static kronq_status check_had(const kronq_had* h, int64_t dim, const char* side)
   return KRONQ_OK;
 }
 
+// Workspace size and alignment (16 bytes: the kernels read and write their
+// parts of it with 16-byte vector accesses).
+static kronq_status check_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need,
+                             bool always) {
+  if (ws_bytes < need || ((need || always) && !ws))
+    return fail(KRONQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (ws && !aligned(ws, 16)) return fail(KRONQ_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  return KRONQ_OK;
+}
+
 // Argument checks of the individual calls (no workspace).
 static kronq_status check_gram(const void* A, int32_t dtype, int64_t N, int64_t d, int64_t lda,
                                const float* H, int64_t ldh, float scale, float beta) {
@@ -143,8 +153,8 @@ kronq_status kronq_gram(const void* A, int32_t dtype, int64_t N, int64_t d, int6
   kronq_status st = check_gram(A, dtype, N, d, lda, H, ldh, scale, beta);
   if (st) return st;
   size_t need = gram_ws_bytes(N, d, dtype);
-  if (ws_bytes < need || (need && !ws))
-    return fail(KRONQ_EWORKSPACE, "kronq_gram: workspace %zu < %zu bytes", ws_bytes, need);
+  st = check_ws("kronq_gram", ws, ws_bytes, need, false);
+  if (st) return st;
   return gram_launch(A, dtype, N, d, lda, H, ldh, scale, beta, ws, ws_bytes, (hipStream_t)stream);
 }
 
@@ -160,8 +170,8 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
   kronq_status st = check_biip(W, m, n, ldw, HX, ldhx, HG, ldhg, in_side, out_side, alpha);
   if (st) return st;
   size_t need = biip_ws_bytes(m, n);
-  if (ws_bytes < need || (need && !ws))
-    return fail(KRONQ_EWORKSPACE, "kronq_biip_rotate: workspace %zu < %zu bytes", ws_bytes, need);
+  st = check_ws("kronq_biip_rotate", ws, ws_bytes, need, false);
+  if (st) return st;
   return biip_launch(W, m, n, ldw, HX, ldhx, HG, ldhg, *in_side, *out_side, alpha, sg, ws, ws_bytes,
                      (hipStream_t)stream);
 }
@@ -181,8 +191,8 @@ kronq_status kronq_biip_unrotate(float* W, int64_t m, int64_t n, int64_t ldw,
   st = check_had(out_side, m, "output-side");
   if (st) return st;
   size_t need = unrotate_ws_bytes(m);
-  if (ws_bytes < need || !ws)
-    return fail(KRONQ_EWORKSPACE, "kronq_biip_unrotate: workspace %zu < %zu bytes", ws_bytes, need);
+  st = check_ws("kronq_biip_unrotate", ws, ws_bytes, need, true);
+  if (st) return st;
   return unrotate_launch(W, m, n, ldw, *in_side, *out_side, sg, ws, (hipStream_t)stream);
 }
 
@@ -198,8 +208,8 @@ kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda
   kronq_status st = check_chol(H, n, ldh, lambda, perm, R, ldr, info);
   if (st) return st;
   size_t need = chol_ws_bytes(n);
-  if (ws_bytes < need || (need && !ws))
-    return fail(KRONQ_EWORKSPACE, "kronq_chol_inv: workspace %zu < %zu bytes", ws_bytes, need);
+  st = check_ws("kronq_chol_inv", ws, ws_bytes, need, false);
+  if (st) return st;
   return chol_launch(H, n, ldh, lambda, act_order ? 1 : 0, perm, R, ldr, info, ws, ws_bytes,
                      (hipStream_t)stream);
 }
@@ -217,8 +227,8 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
   kronq_status st = check_gptq(W, m, n, ldw, R, ldr, q, codes, scales, zeros, What);
   if (st) return st;
   size_t need = gptq_ws_bytes(m, n);
-  if (ws_bytes < need || (need && !ws))
-    return fail(KRONQ_EWORKSPACE, "kronq_gptq_quantize: workspace %zu < %zu bytes", ws_bytes, need);
+  st = check_ws("kronq_gptq_quantize", ws, ws_bytes, need, false);
+  if (st) return st;
   return gptq_launch(W, m, n, ldw, R, ldr, perm, q->bits, q->group > 0 ? q->group : 0, codes,
                      scales, zeros, What, pre_round, ws, ws_bytes, (hipStream_t)stream);
 }
@@ -234,8 +244,8 @@ kronq_status kronq_weight_cv(const float* W, int64_t m, int64_t n, int64_t ldw, 
   if (!W || !out2) return fail(KRONQ_EINVAL, "kronq_weight_cv: NULL pointer");
   if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "kronq_weight_cv: bad shape");
   size_t need = cv_ws_bytes(m, n);
-  if (ws_bytes < need || !ws)
-    return fail(KRONQ_EWORKSPACE, "kronq_weight_cv: workspace %zu < %zu bytes", ws_bytes, need);
+  const kronq_status st = check_ws("kronq_weight_cv", ws, ws_bytes, need, true);
+  if (st) return st;
   return cv_launch(W, m, n, ldw, out2, col_norms, row_norms, ws, (hipStream_t)stream);
 }
 
@@ -300,8 +310,8 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
   st = check_had(out_side, m, "output-side");
   if (st) return st;
   size_t need = decode_ws_bytes(m, n, q->bits);
-  if (ws_bytes < need || !ws)
-    return fail(KRONQ_EWORKSPACE, "kronq_decode_matvec: workspace %zu < %zu bytes", ws_bytes, need);
+  st = check_ws("kronq_decode_matvec", ws, ws_bytes, need, true);
+  if (st) return st;
   return decode_launch(codes, m, n, ldp, q->bits, q->group > 0 ? q->group : 0, scales, zeros,
                        perm, *in_side, *out_side, sg, x, y, ws, (hipStream_t)stream);
 }

@@ -794,9 +794,7 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
     KQ_LAUNCHED("chol_identity_perm");
   }
   {
-    // (A and B sit at 256-byte offsets in the workspace: aligned with it)
-    const bool ws16 = reinterpret_cast<uintptr_t>(w.A) % 16 == 0;
-    if (!act_order && ws16 && n % 4 == 0 && ldh % 4 == 0 && reinterpret_cast<uintptr_t>(H) % 16 == 0) {
+    if (!act_order && n % 4 == 0 && ldh % 4 == 0 && reinterpret_cast<uintptr_t>(H) % 16 == 0) {
       const unsigned gx = (unsigned)std::min<int64_t>((npad / 4 + 255) / 256, 64);
       hipLaunchKernelGGL(chol_gather_id4, dim3(gx, (unsigned)npad), dim3(256), 0, s, H, n, ldh, npad, w);
     } else {
@@ -824,8 +822,7 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
   }
   {
     const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 64);
-    if (reinterpret_cast<uintptr_t>(w.B) % 16 == 0 && n % 4 == 0 && ldr % 4 == 0 &&
-        reinterpret_cast<uintptr_t>(R) % 16 == 0) {
+    if (n % 4 == 0 && ldr % 4 == 0 && reinterpret_cast<uintptr_t>(R) % 16 == 0) {
       const unsigned gx4 = (unsigned)std::min<int64_t>((n / 4 + 255) / 256, 64);
       hipLaunchKernelGGL(chol_flip4, dim3(gx4, (unsigned)n), dim3(256), 0, s, n, npad, R, ldr, w);
     } else {

@@ -137,6 +137,23 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert lib.kronq_sensitivity(None, 4, 4, fake, 4, 4, fake, None) == kq.KRONQ_EINVAL
 
 
+def test_workspace_must_be_aligned(lib):
+    """Workspaces must be 16-byte aligned (the kernels use 16-byte accesses on
+    them); a misaligned one is rejected before anything runs."""
+    fake = 1 << 20   # never dereferenced
+    info = ctypes.c_int64(0)
+    st = lib.kronq_chol_inv(fake, 8, 8, 0.01, 0, fake, fake, 8, ctypes.byref(info), fake + 4, 1 << 30, None)
+    assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
+    st = lib.kronq_gram(fake, 1, 1 << 18, 4096, 4096, fake, 4096, 1.0, 0.0, fake + 8, 1 << 40, None)
+    assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
+    q = kq.QCfg(4, 128)
+    st = lib.kronq_gptq_quantize(fake, 4, 256, 256, fake, 256, None, ctypes.byref(q), fake, fake, fake,
+                                 None, None, fake + 4, 1 << 30, None)
+    assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
+    st = lib.kronq_weight_cv(fake, 8, 8, 8, fake, None, None, fake + 12, 1 << 30, None)
+    assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
+
+
 def test_workspace_queries(lib):
     # split-K partials only when the tile count cannot fill the CUs
     assert lib.kronq_gram_ws(262144, 28672, 1) == 0

@@ -91,3 +91,20 @@ def test_chol_full_size_llama2_7b_q_proj():
     say("  probe residual %.2e forward %.2e" % (resid, fe))
     assert resid <= 1e-3
     assert fe <= 1e-3
+
+
+def test_chol_layouts_give_the_same_factor():
+    """The final flip into R has a float4 path (n and ldr multiples of 4, R
+    16-byte aligned) and an element path.  The same H through both gives the
+    same R, bit for bit: an R with a leading dimension of n + 3 takes the element
+    path, and the columns past n are left alone."""
+    say("chol float4 and element flip")
+    n = 256
+    H = to_dev_f32(spd_from_gram(67, n).astype(np.float32))
+    R1, p1, _ = kq.kronq_chol_inv(H, 0.01, False)
+    Rw = torch.zeros((n, n + 3), dtype=torch.float32, device=DEV)
+    R2, p2, _ = kq.kronq_chol_inv(H, 0.01, False, R=Rw[:, :n])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(R2), host(R1))
+    np.testing.assert_array_equal(host(p2), host(p1))
+    assert torch.all(Rw[:, n:] == 0)
