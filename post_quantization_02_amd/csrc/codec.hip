@@ -96,13 +96,18 @@ __global__ void __launch_bounds__(NTY) decode_yout(const float* __restrict__ par
   const int T = 1 << lg_tile;
   const int t = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x << lg_tile;
+  // NULL signs or S_G: the loads read the partial sums (at least m floats)
+  // in their place and a select takes 1, so that no load sits behind a branch
+  const float* sga = sgn ? sgn : part;
+  const float* sgb = sg ? sg : part;
   float v[EMAX], f[EMAX];
 #pragma unroll
   for (int j = 0; j < EMAX; ++j) {
     const int64_t r = base + t + NTY * j;
     const bool in = (t + NTY * j < T) && r < m;
     const int64_t rr = in ? r : 0;
-    const float a = sgn ? sgn[rr] : 1.f, b = sg ? sg[rr] : 1.f;   // NULL signs: identity side
+    const float a0 = sga[rr], b0 = sgb[rr];
+    const float a = sgn ? a0 : 1.f, b = sg ? b0 : 1.f;   // NULL signs: identity side
     f[j] = nrm * a / b;
     v[j] = 0.f;
   }
@@ -243,13 +248,17 @@ __global__ void __launch_bounds__(NT) decode_gemv(GemvParams p) {
   // Loads below read clamped, always valid addresses and discard what lies
   // outside the matrix with a select, so they issue back to back.
   // 1. x and D_in: thread t holds tile elements t + NT * j (coalesced)
+  // NULL signs (identity side): the loads read x in their place and a select
+  // takes 1, so that no load sits behind a branch
+  const float* sgi = p.sgn_in ? p.sgn_in : p.x;
   float xv[EMAX], sv[EMAX];
 #pragma unroll
   for (int j = 0; j < EMAX; ++j) {
     const int64_t c = tb + t + NT * j;
     const bool in = (j < ept) && (c < p.n);
     const int64_t cc = in ? c : 0;
-    const float a = p.x[cc], b = p.sgn_in ? p.sgn_in[cc] : 1.f;   // NULL signs: identity side
+    const float a = p.x[cc], b0 = sgi[cc];
+    const float b = p.sgn_in ? b0 : 1.f;
     xv[j] = in ? a : 0.f;
     sv[j] = in ? b : 0.f;
   }
