@@ -299,7 +299,9 @@ __global__ void __launch_bounds__(NT) decode_gemv(GemvParams p) {
     if (j < ept) tile[pad(t + NT * j)] = xv[j];
   for (int j = EMAX; j < ept; ++j) {
     const int e = t + NT * j;
-    tile[pad(e)] = (tb + e < p.n) ? p.x[tb + e] * (p.sgn_in ? p.sgn_in[tb + e] : 1.f) : 0.f;
+    const int64_t ce = (tb + e < p.n) ? tb + e : 0;
+    const float a = p.x[ce], b0 = sgi[ce];
+    tile[pad(e)] = (tb + e < p.n) ? a * (p.sgn_in ? b0 : 1.f) : 0.f;
   }
   __syncthreads();
   lds_wht_low_bits<NT>(tile, p.lg_tile, regs ? min(p.lg_kin, 8) : p.lg_kin);
