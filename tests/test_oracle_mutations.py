@@ -71,6 +71,10 @@ MUTANTS = [
      "return biip(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha)"),
     ("sv_only keeps the rescale", "return biip(W, HX, HG, in_signs, in_block, np.ones(m), 1, 0.0)",
      "return biip(W, HX, HG, in_signs, in_block, np.ones(m), 1, alpha)"),
+    ("act-order reordering transposed", "Hp = np.asarray(HXp, dtype=np.float64)[np.ix_(perm, perm)]",
+     "Hp = np.asarray(HXp, dtype=np.float64)[np.ix_(np.argsort(perm), np.argsort(perm))]"),
+    ("zero pre-round snapped to a half-integer", "    return -xmin / ((xmax - xmin) / maxq)",
+     "    return np.floor(-xmin / ((xmax - xmin) / maxq)) + 0.5"),
     ("type ties to the higher id", "ranked = sorted(range(n_types), key=lambda t: (-total[t], t))",
      "ranked = sorted(range(n_types), key=lambda t: (-total[t], -t))"),
 ]

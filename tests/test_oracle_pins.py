@@ -194,6 +194,34 @@ def test_act_order_ties_stable():
     np.testing.assert_array_equal(O.act_order_perm(H), [1, 2, 3, 0])
 
 
+def test_prepare_hessian_explicit_permutation_matrix():
+    # Algorithm 2's damping (H + lambda mean(diag H) I) and the act-order
+    # reordering, checked against an explicit permutation matrix P with
+    # P[j, perm[j]] = 1 (row j of Hd is original column perm[j]):
+    # Hd = P (H + lambda mean(diag) I) P^T.  The diagonal 1, 4, 2, 3 gives
+    # perm = [1, 3, 2, 0], which is not its own inverse ([3, 0, 2, 1]), so a
+    # transposed reordering is caught.
+    rng = np.random.default_rng(21)
+    n = 4
+    A = rng.standard_normal((n, n)) * 0.1
+    H = A @ A.T + np.diag([1.0, 4.0, 2.0, 3.0])
+    perm, Hd = O.prepare_hessian(H, 0.05, True)
+    np.testing.assert_array_equal(perm, [1, 3, 2, 0])
+    P = np.zeros((n, n))
+    P[np.arange(n), perm] = 1.0
+    lam_mu = 0.05 * np.trace(H) / n
+    np.testing.assert_allclose(Hd, P @ (H + lam_mu * np.eye(n)) @ P.T, rtol=0, atol=1e-15)
+    # processing-order diagonal is descending; the damped matrix factors
+    assert np.all(np.diff(np.diag(Hd)) <= 0)
+    R, info = O.chol_inv_upper(Hd)
+    assert info == -1
+    np.testing.assert_allclose(R.T @ R @ Hd, np.eye(n), atol=1e-12)
+    # without act-order the reordering is the identity
+    perm0, Hd0 = O.prepare_hessian(H, 0.05, False)
+    np.testing.assert_array_equal(perm0, np.arange(n))
+    np.testing.assert_allclose(Hd0, H + lam_mu * np.eye(n), rtol=0, atol=1e-15)
+
+
 def test_damping_hand_value():
     H = np.array([[2.0, 1.0], [1.0, 4.0]])
     np.testing.assert_array_equal(O.damp(H, 0.5), [[3.5, 1.0], [1.0, 5.5]])
@@ -253,6 +281,34 @@ def test_quant_params_hand_values():
     # clamp to [0, 2^b - 1]
     q, _, _ = O.rtn(np.array([[-3.0, 9.0]]), np.array([1.0]), np.array([0.0]), 2)
     np.testing.assert_array_equal(q, [[0, 3]])
+
+
+def test_zero_pre_round_hand_values():
+    # -xmin / scale before rounding, the value whose distance to a half-integer
+    # decides whether two zero points may differ by a rounding tie
+    cases = [
+        (np.array([[-1.0, 0.0, 2.0]]), 2, 1.0),          # scale 1, -min 1
+        (np.array([[-0.3, 1.0]]), 2, 0.3 / (1.3 / 3)),    # 0.6923..., not a half-integer
+        (np.array([[-0.5, 0.5]]), 1, 0.5),                # an exact tie
+        (np.array([[1.0, 2.0, 3.0]]), 2, 0.0),            # range widened to 0
+        (np.array([[0.0, 0.0]]), 2, 1.5),                 # degenerate -> [-1, 1], scale 2/3
+        (np.array([[-2.0, -1.0]]), 3, 7.0),               # all negative: max widened to 0
+    ]
+    for V, bits, want in cases:
+        assert O.zero_pre_round(V, bits)[0] == pytest.approx(want, rel=1e-15, abs=1e-15)
+
+
+def test_zero_pre_round_is_zero_before_rint():
+    # equals -min(0, min v) / scale with quant_params' scale, and rounds
+    # half-to-even to quant_params' zero point
+    rng = np.random.default_rng(22)
+    for bits in (1, 2, 3, 4, 8):
+        V = rng.standard_normal((50, 7)) + rng.uniform(-1, 1, (50, 1))
+        zt = O.zero_pre_round(V, bits)
+        scale, zero = O.quant_params(V, bits)
+        np.testing.assert_allclose(zt, -np.minimum(V.min(axis=1), 0.0) / scale, rtol=1e-15)
+        np.testing.assert_array_equal(np.rint(zt), zero)
+        assert np.all((zt >= 0) & (zt <= (2 ** bits - 1) * (1 + 1e-12)))
 
 
 # --------------------------------------------------------- GPTQ loop
