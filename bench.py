@@ -1,21 +1,27 @@
 """Benchmark of the KronQ per-sublayer quantization path on one MI355X.
 
-One step = the whole hot path for one sublayer, inputs resident in HBM:
+One step = the whole hot path for every sublayer of the workload, inputs
+resident in HBM; per sublayer:
   H_X = X^T X / N, H_G = G^T G / N            (kronq_gram x 2, bf16 matrix cores)
   BiIP: S_G rescale + Hadamard both sides      (kronq_biip_rotate)
   sensitivity tr(H_X') tr(H_G')                (kronq_sensitivity)
   damping + inverse Cholesky factor            (kronq_chol_inv, synchronizes)
   column-wise OBS quantize-and-compensate      (kronq_gptq_quantize)
-  bit allocation                               (kronq_allocate_bits, host)
-Workload: Llama-2-7B q_proj shape -- W 4096 x 4096, X and G 262144 x 4096 bf16
-(128 sequences x 2048 tokens), 2-bit asymmetric groups of 128, Hadamard 4096 on
-both sides, alpha 0.25, damping 1% of the mean diagonal.  Synthetic inputs
-(heavy-tailed activations with outlier channels, log-normal gradient channel
-scales) stand in for the calibration set.
+Workload: the Llama-3-70B MLP -- gate_proj W 28672 x 8192 (X 262144 x 8192,
+G 262144 x 28672) and down_proj W 8192 x 28672 (X 262144 x 28672, G 262144 x
+8192), bf16 calibration rows (128 sequences x 2048 tokens), 2-bit asymmetric
+groups of 128, block-Hadamard 7 x 4096 on the 28672-wide sides and 8192 on the
+others, alpha 0.25, damping 1% of the mean diagonal, fp32 Cholesky of the
+28672 x 28672 H_X.  Synthetic inputs (heavy-tailed activations with outlier
+channels, log-normal gradient channel scales) generated in device memory stand
+in for the calibration set.  The Llama-2-7B q_proj workload (4096 x 4096) is
+timed the same way as a secondary object of the line.
 
-Prints one JSON line.  `value` is the wall time of one sublayer quantization
-(seconds, lower is better).  Per-stage times come from HIP events recorded on
-the stream the kernels run on; `roofline` is for the Gram kernel call.
+Prints one JSON line.  `value` is the mean wall time of one sublayer
+quantization (seconds, lower is better): the wall time of a step divided by the
+number of sublayers.  Per-stage times come from HIP events recorded on the
+stream the kernels run on; `roofline` is for the Gram kernel launch at
+d = 28672 (the dominant kernel).
 """
 from __future__ import annotations
 
@@ -43,9 +49,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the Llama-2-7B q_proj secondary object (and the weight CV figures)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the batch-1 decode measurement of the deploy codec")
     ap.add_argument("--decode-only", action="store_true",
@@ -57,7 +65,7 @@ def parse():
     ap.add_argument("--config-steps", type=int, default=2, help="timed steps per sublayer (--configs)")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle baseline sample")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gram_bf16_llama2_7b_q_proj_traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gram_bf16_llama3_70b_mlp_traffic.json"))
     ap.add_argument("--copy-probe", type=int, metavar="BYTES", default=0,
                     help="only run a plain device copy of BYTES five times (calibrates the HBM byte "
                          "counters) and exit")
@@ -72,7 +80,7 @@ def parse():
 
 
 GRAM_SRC = os.path.join(ROOT, "post_quantization_02_amd", "csrc", "gram.hip")
-GRAM_KERNELS = ("gram_bf16_lds_kernel", "gram_finalize_kernel", "gram_bf16_kernel")
+GRAM_MAIN = "gram_bf16_lds_kernel"
 
 
 def gram_source_hash():
@@ -92,22 +100,33 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 5}), flush=True)
 
 
-def _pmc_mean(path, kernel_pred, counter):
+def _pmc_groups(path, kernel_pred, counter):
+    """{grid size: [per-dispatch counter sums]} for the matching kernels."""
     import csv
     per_dispatch = {}
+    grid = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter and kernel_pred(r["Kernel_Name"]):
                 key = r["Dispatch_Id"]
                 per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
-    vals = list(per_dispatch.values())
+                grid[key] = int(r.get("Grid_Size", 0) or 0)
+    out = {}
+    for k, v in per_dispatch.items():
+        out.setdefault(grid[k], []).append(v)
+    return out
+
+
+def _pmc_mean(path, kernel_pred, counter):
+    vals = [v for vs in _pmc_groups(path, kernel_pred, counter).values() for v in vs]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
 def summarize_traffic(args):
-    """HBM bytes per kronq_gram call (the Gram kernel and its split-K finalize)
-    from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled so that the
-    same counter over a plain copy of known size reads that size."""
+    """HBM bytes per launch of the roofline kernel (the Gram at d = 28672 of the
+    Llama-3-70B MLP step: the launches with the largest grid) from FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled so that the same counter over a
+    plain copy of known size reads that size."""
     f_csv, w_csv, cf_csv, cw_csv = args.summarize_traffic
     copy = lambda k: "copyBuffer" in k
     cf, _ = _pmc_mean(cf_csv, copy, "FETCH_SIZE")
@@ -116,21 +135,21 @@ def summarize_traffic(args):
     f_scale, w_scale = kib / cf, kib / cw
     out = {"counters": {}, "copy_probe": {"bytes": args.copy_bytes, "fetch_kib": cf, "write_kib": cw,
                                           "fetch_scale": f_scale, "write_scale": w_scale}}
-    total = 0.0
-    for k in GRAM_KERNELS:
-        pred = lambda name, k=k: k in name
-        fk, nf = _pmc_mean(f_csv, pred, "FETCH_SIZE")
-        wk, nw = _pmc_mean(w_csv, pred, "WRITE_SIZE")
-        if fk is None or wk is None:
-            continue
-        b = (fk * f_scale + wk * w_scale) * 1024.0
-        out["counters"][k] = {"fetch_kib": fk, "write_kib": wk, "dispatches": nf,
-                              "hbm_bytes_per_dispatch": b}
-        total += b
-    out["bytes_per_launch"] = total
-    out["unit"] = "bytes per kronq_gram call (sum over its kernels, scaled counters)"
+    pred = lambda name: GRAM_MAIN in name
+    fg = _pmc_groups(f_csv, pred, "FETCH_SIZE")
+    wg = _pmc_groups(w_csv, pred, "WRITE_SIZE")
+    for grid in sorted(set(fg) & set(wg)):
+        fk = sum(fg[grid]) / len(fg[grid])
+        wk = sum(wg[grid]) / len(wg[grid])
+        out["counters"]["%s grid %d" % (GRAM_MAIN, grid)] = {
+            "fetch_kib": fk, "write_kib": wk, "dispatches": len(fg[grid]),
+            "hbm_bytes_per_dispatch": (fk * f_scale + wk * w_scale) * 1024.0}
+    big = max(set(fg) & set(wg))          # d = 28672: the largest grid of the step
+    out["roofline_grid"] = big
+    out["bytes_per_launch"] = out["counters"]["%s grid %d" % (GRAM_MAIN, big)]["hbm_bytes_per_dispatch"]
+    out["unit"] = "bytes per launch of %s at d = 28672 (scaled counters)" % GRAM_MAIN
     out["gram_source_sha256"] = gram_source_hash()
-    run = "python3 -u bench.py --steps 1 --warmup 0 --no-cpu-baseline"
+    run = "python3 -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-secondary"
     probe = "python3 -u bench.py --copy-probe %d" % args.copy_bytes
     out["commands"] = {
         "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o bench -- " + run,
@@ -146,12 +165,27 @@ def summarize_traffic(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, X, G, W, budget_s):
-    """The oracle (numpy float64, as it stands) on a bounded sample of the same
-    workload, extrapolated to one sublayer:
-      Gram: a token prefix of X and of G (the Gram is linear in N),
-      BiIP: full W, H_X, H_G rotations (sample-free),
-      damping + inverse Cholesky: full,
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (numpy float64, as it stands) on a bounded sample of every
+    sublayer of workload `w`, extrapolated to the whole step and reported per
+    sublayer (the mean, like `value`):
+      Gram: a token prefix of X and of G on their first 4096 columns (the Gram
+            is linear in N and quadratic in d),
+      BiIP: the two-sided rotation of a row slice of W (rows are independent on
+            the input side; the output side is timed on a column slice), scaled
+            by element count, then by (mn + n^2 + m^2) / (mn) for H_X and H_G,
+      damping + inverse Cholesky: at n_s = min(n, 2048), scaled by (n / n_s)^3,
       column loop: a row sample (rows are independent), all columns."""
     import synth
     from oracle import kronq_oracle as O
@@ -160,42 +194,65 @@ def cpu_baseline(w, X, G, W, budget_s):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    s = w.sub("q_proj")
     N = w.N
     t0 = time.perf_counter()
-    Np = 4096
-    xs = synth.bf16_to_f64(X[:Np])
-    gs = synth.bf16_to_f64(G[:Np])
-    t_g0 = time.perf_counter()
-    HXs = O.gram(xs)
-    HGs = O.gram(gs)
-    t_gram = (time.perf_counter() - t_g0) * (N / Np)
-    # BiIP: the three 4096 x 4096 rotations cost the same; W's is timed, x3
-    t_b0 = time.perf_counter()
-    Wp, _, _, sg = O.biip(synth.bf16_to_f64(W), None, HGs, w.in_signs("x"), s.in_block,
-                          w.out_signs("q_proj"), s.out_block, w.alpha)
-    t_biip = 3.0 * (time.perf_counter() - t_b0)
-    t_s0 = time.perf_counter()
-    O.sensitivity(HXs, HGs)
-    t_sens = time.perf_counter() - t_s0
-    t_c0 = time.perf_counter()
-    perm, H = O.prepare_hessian(HXs, w.lam, s.act_order)
-    R, _ = O.chol_inv_upper(H)
-    t_chol = time.perf_counter() - t_c0
-    rows = 16
-    t_q0 = time.perf_counter()
-    O.gptq(Wp[:rows], R, perm, s.bits, s.group)
-    t_gptq = (time.perf_counter() - t_q0) * (s.m / rows)
-    total = t_gram + t_biip + t_sens + t_chol + t_gptq
+    Np = 128
+    stages = {"gram_x_g": 0.0, "biip": 0.0, "sensitivity": 0.0, "chol_inv": 0.0, "gptq": 0.0}
+    notes = []
+    for s in w.sublayers:
+        m, n = s.m, s.n
+        # Gram: Np tokens and the first ds columns (cost N d^2)
+        dx, dg = min(n, 4096), min(m, 4096)
+        xs = synth.bf16_to_f64(w.gen_x(s.x, r0=0, nr=Np, c0=0, nc=dx))
+        gs = synth.bf16_to_f64(w.gen_g(s.name, r0=0, nr=Np, c0=0, nc=dg))
+        t_g0 = time.perf_counter()
+        HXs = O.gram(xs)
+        t_x = (time.perf_counter() - t_g0) * (N / Np) * (n / dx) ** 2
+        t_g0 = time.perf_counter()
+        HGs = O.gram(gs)
+        t_gg = (time.perf_counter() - t_g0) * (N / Np) * (m / dg) ** 2
+        stages["gram_x_g"] += t_x + t_gg
+        # BiIP: input side on a slice of rows, output side on a slice of columns
+        rs = min(m, 512)
+        cs = min(n, 512)
+        Wr = synth.bf16_to_f64(w.gen_w(s.name, r0=0, nr=rs))
+        Wc = synth.bf16_to_f64(w.gen_w(s.name, c0=0, nc=cs))
+        t_b0 = time.perf_counter()
+        O.rotate_rows(Wr, s.in_block, w.in_signs(s.x))
+        t_in = (time.perf_counter() - t_b0) * (m / rs)
+        t_b0 = time.perf_counter()
+        O.rotate_cols(Wc, s.out_block, w.out_signs(s.name))
+        t_out = (time.perf_counter() - t_b0) * (n / cs)
+        stages["biip"] += (t_in + t_out) * (m * n + n * n + m * m) / (m * n)
+        t_s0 = time.perf_counter()
+        O.sensitivity(HXs, HGs)
+        stages["sensitivity"] += time.perf_counter() - t_s0
+        ns = min(dx, 2048)
+        Hs = HXs[:ns, :ns] + np.eye(ns)
+        t_c0 = time.perf_counter()
+        perm, H = O.prepare_hessian(Hs, w.lam, s.act_order)
+        Rs, _ = O.chol_inv_upper(H)
+        stages["chol_inv"] += (time.perf_counter() - t_c0) * (n / ns) ** 3
+        # column loop: two rows against an n x n upper factor
+        rows = 2
+        R = np.triu(np.full((n, n), 0.5 / np.sqrt(n))) + np.eye(n)
+        t_q0 = time.perf_counter()
+        O.gptq(Wr[:rows], R, np.arange(n), s.bits, s.group)
+        stages["gptq"] += (time.perf_counter() - t_q0) * (m / rows)
+        notes.append("%s %dx%d: Gram on the first %d of %d tokens and the first %d / %d columns "
+                     "(x N/%d x (d/d_s)^2), W rotated on %d rows and %d columns, inverse Cholesky at "
+                     "n=%d (x(n/%d)^3), column loop on %d rows (x%d)"
+                     % (s.name, m, n, Np, N, dx, dg, Np, rs, cs, ns, ns, rows, m // rows))
+        del Wr, Wc, R
+    total = sum(stages.values())
     wall = time.perf_counter() - t0
+    L = len(w.sublayers)
     return {
-        "value": total, "unit": "s", "cores": int(cores), "kind": "oracle",
-        "sample": ("Gram on the first %d of %d tokens of X and G, scaled x%d; BiIP rotation of W "
-                   "timed and scaled x3 (H_X, H_G cost the same); sensitivity and damped inverse "
-                   "Cholesky in full; column loop on %d of %d rows, scaled x%d; float64 numpy; "
-                   "%.1f s of host time") % (Np, N, N // Np, rows, s.m, s.m // rows, wall),
-        "stages_s": {"gram_x_g": t_gram, "biip": t_biip, "sensitivity": t_sens, "chol_inv": t_chol,
-                     "gptq": t_gptq},
+        "value": total / L, "unit": "s", "cores": int(cores), "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "sample": "%s, per sublayer (mean of %d): %s; float64 numpy, extrapolated; %.1f s of host time"
+                  % (w.name, L, "; ".join(notes), wall),
+        "stages_s_per_step": stages,
     }
 
 
@@ -424,6 +481,128 @@ def configs_leg(steps, warmup, names=CONFIG_LEG_WORKLOADS):
     return out
 
 
+class SublayerPath:
+    """Device buffers and one pass of the path for one sublayer (inputs resident)."""
+
+    NAMES = ("gram_x", "gram_g", "biip", "sensitivity", "chol_inv", "gptq")
+
+    def __init__(self, w, s, Xd, Gd, W0, dev):
+        import torch
+        import post_quantization_02_amd as kq
+        self.kq, self.w, self.s = kq, w, s
+        m, n, N = s.m, s.n, w.N
+        self.Xd, self.Gd, self.W0 = Xd, Gd, W0
+        self.si = torch.from_numpy(w.in_signs(s.x)).to(dev)
+        self.so = torch.from_numpy(w.out_signs(s.name)).to(dev)
+        f32 = torch.float32
+        self.HX = torch.empty((n, n), dtype=f32, device=dev)
+        self.HG = torch.empty((m, m), dtype=f32, device=dev)
+        self.sg = torch.empty(m, dtype=f32, device=dev)
+        self.tr = torch.empty(3, dtype=torch.float64, device=dev)
+        self.R = torch.empty((n, n), dtype=f32, device=dev)
+        self.perm = torch.empty(n, dtype=torch.int32, device=dev)
+        self.What = torch.empty((m, n), dtype=f32, device=dev)
+        self.codes = torch.empty((m, n), dtype=torch.uint8, device=dev)
+        ng = 1 if s.group <= 0 else n // s.group
+        self.scales = torch.empty((m, ng), dtype=f32, device=dev)
+        self.zeros = torch.empty((m, ng), dtype=f32, device=dev)
+        lib = kq.load()
+        u8 = torch.uint8
+        self.ws_gx = torch.empty(max(1, lib.kronq_gram_ws(N, n, kq.KRONQ_BF16)), dtype=u8, device=dev)
+        self.ws_gg = torch.empty(max(1, lib.kronq_gram_ws(N, m, kq.KRONQ_BF16)), dtype=u8, device=dev)
+        self.ws_b = torch.empty(max(1, lib.kronq_biip_ws(m, n)), dtype=u8, device=dev)
+        self.ws_c = torch.empty(max(1, lib.kronq_chol_inv_ws(n)), dtype=u8, device=dev)
+        self.ws_q = torch.empty(max(1, lib.kronq_gptq_ws(m, n)), dtype=u8, device=dev)
+
+    def step(self, Wk, stream, ev=None):
+        """One pass; Wk (rotated in place) holds the step's own copy of W.
+        ev: 7 events, recorded between the stages."""
+        kq, w, s = self.kq, self.w, self.s
+
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+
+        mark(0)
+        kq.kronq_gram(self.Xd, self.HX, ws=self.ws_gx)
+        mark(1)
+        kq.kronq_gram(self.Gd, self.HG, ws=self.ws_gg)
+        mark(2)
+        kq.kronq_biip_rotate(Wk, self.HX, self.HG, self.si, s.in_block, self.so, s.out_block, w.alpha,
+                             self.sg, ws=self.ws_b)
+        mark(3)
+        kq.kronq_sensitivity(self.HX, self.HG, out=self.tr)
+        mark(4)
+        kq.kronq_chol_inv(self.HX, w.lam, s.act_order, perm=self.perm, R=self.R, ws=self.ws_c)
+        mark(5)
+        kq.kronq_gptq_quantize(Wk, self.R, self.perm, s.bits, s.group, What=self.What, ws=self.ws_q,
+                               codes=self.codes, scales=self.scales, zeros=self.zeros)
+        mark(6)
+
+
+def run_workload(w, steps, warmup, dev):
+    """Time `steps` passes of the path over every sublayer of `w` (after
+    `warmup` untimed passes).  Returns (per-step wall ms, per-sublayer event
+    times, input generation seconds, the SublayerPath objects)."""
+    import torch
+    import synth
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    paths = []
+    xs = {}
+    for s in w.sublayers:
+        log("  inputs", w.name, s.name, s.m, "x", s.n)
+        if s.x not in xs:
+            xs[s.x] = w.gen_x_dev(s.x)
+        Gd = w.gen_g_dev(s.name)
+        W0 = torch.from_numpy(w.w_f32(s.name)).to(dev)
+        paths.append(SublayerPath(w, s, xs[s.x], Gd, W0, dev))
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t0
+    log("  warmup", warmup)
+    for _ in range(warmup):
+        for p in paths:
+            Wk = p.W0.clone()
+            p.step(Wk, stream)
+            del Wk
+    # the rotation works in place: every timed step gets its own copy of each W,
+    # resident before the timed region like X and G
+    Wts = [[p.W0.clone() for p in paths] for _ in range(steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in paths] for _ in range(steps)]
+    torch.cuda.synchronize()
+    log("  timing", steps, "steps")
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for j, p in enumerate(paths):
+            p.step(Wts[k][j], stream, evs[k][j])
+        log("    step", k + 1, "done")
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per_sub = []
+    for j, p in enumerate(paths):
+        st = {nm: float(np.mean([evs[k][j][i].elapsed_time(evs[k][j][i + 1]) for k in range(steps)]))
+              for i, nm in enumerate(SublayerPath.NAMES)}
+        per_sub.append(st)
+    for j, p in enumerate(paths):
+        p.Wk_last = Wts[-1][j]
+    return wall_ms, per_sub, t_gen, paths
+
+
+def sublayer_record(w, s, st):
+    m, n, N = s.m, s.n, w.N
+    return {
+        "sublayer": s.name, "m": m, "n": n, "bits": s.bits, "group": s.group,
+        "hadamard_in": s.in_block, "hadamard_out": s.out_block, "act_order": s.act_order,
+        "ms": sum(st.values()), "stage_ms": st,
+        "gram_x_tflops": N * n * (n + 1) / (st["gram_x"] * 1e-3) / 1e12,
+        "gram_g_tflops": N * m * (m + 1) / (st["gram_g"] * 1e-3) / 1e12,
+        "fwht_gbs": 16.0 * (m * n + n * n + m * m) / (st["biip"] * 1e-3) / 1e9,
+        "chol_tflops_fp32": 2.0 * n ** 3 / 3 / (st["chol_inv"] * 1e-3) / 1e12,
+        "gptq_tflops_fp64": float(m) * n * n / (st["gptq"] * 1e-3) / 1e12,
+        "gptq_min_bytes_gbs": (9.0 * m * n + 2.0 * n * n) / (st["gptq"] * 1e-3) / 1e9,
+    }
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -449,113 +628,28 @@ def main():
         return
     import torch
     import post_quantization_02_amd as kq
-    import synth
     from synth import workloads as WL
 
-    w = WL.C2
-    s = w.sub("q_proj")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log("generating inputs", w.name)
-    t0 = time.perf_counter()
-    X = w.gen_x("x")
-    G = w.gen_g("q_proj")
-    W = w.gen_w("q_proj")
-    t_gen = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
-    Gd = torch.from_numpy(G.view(np.int16)).view(torch.bfloat16).to(dev)
-    W0 = torch.from_numpy(synth.bf16_to_f32(W)).to(dev)
-    si = torch.from_numpy(w.in_signs("x")).to(dev)
-    so = torch.from_numpy(w.out_signs("q_proj")).to(dev)
-    torch.cuda.synchronize()
-    t_h2d = time.perf_counter() - t0
-    m, n, N = s.m, s.n, w.N
-
-    HX = torch.empty((n, n), dtype=torch.float32, device=dev)
-    HG = torch.empty((m, m), dtype=torch.float32, device=dev)
-    Wk = torch.empty_like(W0)
-    sg = torch.empty(m, dtype=torch.float32, device=dev)
-    tr = torch.empty(3, dtype=torch.float64, device=dev)
-    R = torch.empty((n, n), dtype=torch.float32, device=dev)
-    perm = torch.empty(n, dtype=torch.int32, device=dev)
-    What = torch.empty((m, n), dtype=torch.float32, device=dev)
-    codes = torch.empty((m, n), dtype=torch.uint8, device=dev)
-    ng = n // s.group
-    scales = torch.empty((m, ng), dtype=torch.float32, device=dev)
-    zeros = torch.empty((m, ng), dtype=torch.float32, device=dev)
-    lib = kq.load()
-    ws_g = torch.empty(max(1, lib.kronq_gram_ws(N, n, kq.KRONQ_BF16)), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(1, lib.kronq_biip_ws(m, n)), dtype=torch.uint8, device=dev)
-    ws_c = torch.empty(max(1, lib.kronq_chol_inv_ws(n)), dtype=torch.uint8, device=dev)
-    ws_q = torch.empty(max(1, lib.kronq_gptq_ws(m, n)), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    names = ["gram_x", "gram_g", "biip", "sensitivity", "chol_inv", "gptq", "allocate"]
-
-    def step(Wk, ev=None):
-        """One pass of the path; Wk (rotated in place) holds the step's own copy of W."""
-        if ev is not None:
-            ev[0].record(stream)
-        kq.kronq_gram(Xd, HX, ws=ws_g)
-        if ev is not None:
-            ev[1].record(stream)
-        kq.kronq_gram(Gd, HG, ws=ws_g)
-        if ev is not None:
-            ev[2].record(stream)
-        kq.kronq_biip_rotate(Wk, HX, HG, si, s.in_block, so, s.out_block, w.alpha, sg, ws=ws_b)
-        if ev is not None:
-            ev[3].record(stream)
-        kq.kronq_sensitivity(HX, HG, out=tr)
-        if ev is not None:
-            ev[4].record(stream)
-        kq.kronq_chol_inv(HX, w.lam, s.act_order, perm=perm, R=R, ws=ws_c)
-        if ev is not None:
-            ev[5].record(stream)
-        kq.kronq_gptq_quantize(Wk, R, perm, s.bits, s.group, What=What, ws=ws_q, codes=codes,
-                               scales=scales, zeros=zeros)
-        if ev is not None:
-            ev[6].record(stream)
-        score = float(tr[2].item())
-        bits = kq.kronq_allocate_bits([score], [m * n], s.bits, s.bits, s.bits * m * n)
-        if ev is not None:
-            ev[7].record(stream)
-        return bits
-
-    log("warmup", args.warmup)
-    for _ in range(args.warmup):
-        Wk.copy_(W0)
-        step(Wk)
-    # the rotation works in place: every timed step gets its own copy of W,
-    # resident before the timed region like X and G
-    Wts = [W0.clone() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
-    log("timing", args.steps, "steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(Wts[k], evs[k])
-        log("  step", k + 1, "done")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stage_ms = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-                for i, nm in enumerate(names)}
-    ms_step = wall * 1e3 / args.steps
-    Wk = Wts[-1]
-    del Wts[:-1]
-
-    gram_flops = float(N) * n * (n + 1)        # one factor, unique triangle
-    gram_ms = 0.5 * (stage_ms["gram_x"] + stage_ms["gram_g"])
+    kq.load()
+    w = WL.C5
+    log("headline workload", w.name)
+    wall_ms, per_sub, t_gen, paths = run_workload(w, args.steps, args.warmup, dev)
+    L = len(w.sublayers)
+    subs = [sublayer_record(w, s, st) for s, st in zip(w.sublayers, per_sub)]
+    N = w.N
+    # roofline: the Gram launches at d = 28672 (G of gate_proj, X of down_proj)
+    big = []
+    for s, st in zip(w.sublayers, per_sub):
+        if s.m == 28672:
+            big.append(st["gram_g"])
+        if s.n == 28672:
+            big.append(st["gram_x"])
+    d = 28672
+    gram_ms = float(np.mean(big))
+    gram_flops = float(N) * d * (d + 1)
     gram_tflops = gram_flops / (gram_ms * 1e-3) / 1e12
-    fwht_bytes = 16.0 * (m * n + n * n + m * m)   # two one-sided passes, 8 B per element each
-    fwht_gbs = fwht_bytes / (stage_ms["biip"] * 1e-3) / 1e9
-    chol_flops = 2.0 * n ** 3 / 3
-    gptq_flops = float(m) * n * n
-    gptq_bytes = 9.0 * m * n + 2.0 * n * n
-
-    # HBM traffic per Gram call from the committed counter summary, null when the
-    # Gram source has changed since the counters were taken
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
@@ -565,61 +659,89 @@ def main():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
-
+    fwht_bytes = sum(16.0 * (s.m * s.n + s.n * s.n + s.m * s.m) for s in w.sublayers)
+    fwht_ms = sum(st["biip"] for st in per_sub)
     out = {
         "metric": "sublayer quantize wall time (s) + Gram TFLOP/s & FWHT GB/s vs MI355X peak",
-        "value": ms_step / 1e3,
+        "value": wall_ms / 1e3 / L,
         "unit": "s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": wall_ms,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "N": N, "m": m, "n": n, "x_dtype": "bf16", "bits": s.bits,
-                   "group": s.group, "hadamard_in": s.in_block, "hadamard_out": s.out_block,
-                   "alpha": w.alpha, "damp": w.lam, "act_order": s.act_order},
-        "stage_ms": stage_ms,
+        "config": {"workload": w.name, "N": N, "sublayers": ["%s %dx%d" % (s.name, s.m, s.n)
+                                                             for s in w.sublayers],
+                   "x_dtype": "bf16", "bits": 2, "group": 128, "hadamard": "7x4096 on 28672, 8192 full",
+                   "alpha": w.alpha, "damp": w.lam, "act_order": False,
+                   "value_is": "step wall time / %d sublayers" % L},
+        "sublayers": subs,
         "stage_dtypes": {"gram": "bf16 products, fp32 accumulate", "biip": "fp32",
                          "chol_inv": "fp32 (diagonal blocks fp64)", "gptq": "fp64",
                          "sensitivity": "fp64 sums"},
         "gram_tflops": gram_tflops,
         "gram_frac_bf16_peak": gram_tflops / PEAK_BF16_TFLOPS,
-        "fwht_gbs": fwht_gbs,
-        "fwht_frac_hbm_peak": fwht_gbs / PEAK_HBM_GBS,
-        "chol_tflops_fp32": chol_flops / (stage_ms["chol_inv"] * 1e-3) / 1e12,
-        "gptq_tflops_fp64": gptq_flops / (stage_ms["gptq"] * 1e-3) / 1e12,
-        "gptq_min_bytes_gbs": gptq_bytes / (stage_ms["gptq"] * 1e-3) / 1e9,
-        "roofline": {"kernel": "kronq_gram call (gram_bf16_kernel + gram_finalize_kernel)",
+        "fwht_gbs": fwht_bytes / (fwht_ms * 1e-3) / 1e9,
+        "fwht_frac_hbm_peak": fwht_bytes / (fwht_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {"kernel": "%s, kronq_gram at d = 28672 (one launch, no split-K)" % GRAM_MAIN,
                      "bound": "mfma", "achieved": gram_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": gram_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "algorithmic_flops_per_launch": gram_flops,
+                     "algorithmic_bytes_per_launch": 2.0 * N * d + 4.0 * d * d},
         "input_gen_s": t_gen,
-        "h2d_s": t_h2d,
     }
-    # CV_in / CV_out of W before and after BiIP, and the diagnostic's own rate
-    # (one read of W: 4 m n algorithmic bytes per call)
-    cv_out = torch.empty(2, dtype=torch.float64, device=dev)
-    ws_cv = torch.empty(lib.kronq_weight_cv_ws(m, n), dtype=torch.uint8, device=dev)
-    cv_before = [float(v) for v in kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv).cpu()]
-    cv_after = [float(v) for v in kq.kronq_weight_cv(Wk, out=cv_out, ws=ws_cv).cpu()]
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    for _ in range(3):
-        kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv)
-    e0.record(stream)
-    for _ in range(20):
-        kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    cv_ms = e0.elapsed_time(e1) / 20
-    out["weight_cv"] = {"cv_in_before": cv_before[0], "cv_out_before": cv_before[1],
-                        "cv_in_after_biip": cv_after[0], "cv_out_after_biip": cv_after[1],
-                        "ms_per_call": cv_ms, "gbs": 4.0 * m * n / (cv_ms * 1e-3) / 1e9,
-                        "frac_hbm_peak": 4.0 * m * n / (cv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del paths
+    torch.cuda.empty_cache()
+    # host-only allocation on the Llama-3-8B block's seven scores (3.0-bit budget)
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "allocation_llama3_8b_block.json")))
+    t0 = time.perf_counter()
+    for _ in range(1000):
+        kq.kronq_allocate_bits(g["scores"], g["n_params"], g["bmin"], g["bmax"], g["budget_bits"])
+    out["allocation"] = {"workload": "llama3_8b_block scores, 7 sublayers, {2,3,4} bits, 3.0 average",
+                         "us_per_call": (time.perf_counter() - t0) * 1e3}
+    if not args.no_secondary:
+        w2 = WL.C2
+        log("secondary workload", w2.name)
+        wall2, per2, _, p2 = run_workload(w2, max(args.steps, 5), args.warmup, dev)
+        s2 = w2.sublayers[0]
+        r2 = sublayer_record(w2, s2, per2[0])
+        gms = 0.5 * (per2[0]["gram_x"] + per2[0]["gram_g"])
+        gt = w2.N * s2.n * (s2.n + 1) / (gms * 1e-3) / 1e12
+        r2.update({"workload": w2.name, "ms_per_step": wall2, "gram_frac_bf16_peak": gt / PEAK_BF16_TFLOPS,
+                   "fwht_frac_hbm_peak": r2["fwht_gbs"] / PEAK_HBM_GBS})
+        out["secondary"] = r2
+        # CV_in / CV_out of W before and after BiIP, and the diagnostic's own rate
+        # (one read of W: 4 m n algorithmic bytes per call)
+        m, n = s2.m, s2.n
+        lib = kq.load()
+        W0, Wk = p2[0].W0, p2[0].Wk_last
+        cv_out = torch.empty(2, dtype=torch.float64, device=dev)
+        ws_cv = torch.empty(lib.kronq_weight_cv_ws(m, n), dtype=torch.uint8, device=dev)
+        cv_before = [float(v) for v in kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv).cpu()]
+        cv_after = [float(v) for v in kq.kronq_weight_cv(Wk, out=cv_out, ws=ws_cv).cpu()]
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv)
+        e0.record(stream)
+        for _ in range(20):
+            kq.kronq_weight_cv(W0, out=cv_out, ws=ws_cv)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cv_ms = e0.elapsed_time(e1) / 20
+        out["weight_cv"] = {"workload": w2.name, "cv_in_before": cv_before[0],
+                            "cv_out_before": cv_before[1], "cv_in_after_biip": cv_after[0],
+                            "cv_out_after_biip": cv_after[1], "ms_per_call": cv_ms,
+                            "gbs": 4.0 * m * n / (cv_ms * 1e-3) / 1e9,
+                            "frac_hbm_peak": 4.0 * m * n / (cv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del p2
+        torch.cuda.empty_cache()
     if not args.no_decode:
         log("decode leg")
         out["decode"] = decode_leg(args.decode_steps, 3)
@@ -627,7 +749,7 @@ def main():
                                            name="llama2_7b_linear_stack_qkv_gateup")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
-        out["cpu_baseline"] = cpu_baseline(w, X, G, W, args.cpu_budget_s)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
 
 

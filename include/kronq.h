@@ -49,6 +49,8 @@ typedef int32_t kronq_status;
 #define KRONQ_EHIP 3           /* HIP runtime error */
 #define KRONQ_EWORKSPACE 4     /* workspace smaller than the *_ws() size */
 #define KRONQ_EUNSUPPORTED 5   /* valid request the library does not implement */
+#define KRONQ_ENUMERIC 6       /* input holds a NaN or an infinity (found on the device) */
+#define KRONQ_ENOMEM 7         /* request larger than a fixed device buffer of the library */
 
 #define KRONQ_F32 0            /* element type codes for kronq_gram */
 #define KRONQ_BF16 1
@@ -77,6 +79,38 @@ typedef struct {
 const char* kronq_status_string(kronq_status s);
 const char* kronq_last_error(void);
 int32_t kronq_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Random signs of the randomized Hadamard transforms (hyper.ai summary, Method:
+ * U and V are randomized Hadamard transforms; GitHub README: the incoherence
+ * machinery follows QuIP#, whose randomized Hadamard transform multiplies by
+ * random signs before the transform).  The pages fix no generator; this is
+ * the library's documented draw, so that a caller can reproduce a rotation
+ * from its seed alone.  With the public splitmix64 finalizer
+ *   mix(z): z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9;
+ *           z = (z ^ (z >> 27)) * 0x94D049BB133111EB; return z ^ (z >> 31)
+ * (Steele, Lea and Flood, OOPSLA 2014) and its increment g = 0x9E3779B97F4A7C15:
+ *   key   = mix(mix(seed) ^ (6 * g))
+ *   out[i] = top bit of mix(key + (i + 1) * g) ? -1.0f : +1.0f,  i = 0..n-1
+ * (all products modulo 2^64).  out_host: host array of n floats.  KRONQ_EINVAL
+ * for n < 0 or out_host NULL with n > 0.  Host only; thread safe.
+ * ------------------------------------------------------------------------- */
+kronq_status kronq_signs(uint64_t seed, int64_t n, float* out_host);
+
+/* ---------------------------------------------------------------------------
+ * Finiteness check of a device matrix (the library's guard against NaN and
+ * infinite values: kronq_chol_inv applies it to its input and returns
+ * KRONQ_ENUMERIC; the asynchronous calls cannot report a device-side finding
+ * as a status, so a caller checks their inputs or outputs with this call).
+ *   flag_dev (device int32) <- 1 if some A[i][j], i < rows, j < cols, is NaN or
+ *                              infinite, else 0
+ * A : rows x cols fp32 device, leading dimension ld >= cols (read only).
+ * Two launches on `stream` (clear, then scan), no host synchronization and no
+ * memset; the caller reads flag_dev after synchronizing.  rows or cols 0
+ * writes 0.
+ * ------------------------------------------------------------------------- */
+kronq_status kronq_check_finite(const float* A, int64_t rows, int64_t cols, int64_t ld,
+                                int32_t* flag_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Kronecker factor (hyper.ai summary, Method: H_X = E[x x^T], H_G = E[g g^T]
@@ -150,7 +184,9 @@ kronq_status kronq_biip_unrotate(float* W, int64_t m, int64_t n, int64_t ldw,
  *         KRONQ_ENOTPD is returned and info is the largest k (processing
  *         order) whose trailing block Hd[k:, k:] is not positive definite
  *         (the factorization runs on the reversed matrix, so this is where its
- *         first non-positive pivot falls).
+ *         first non-positive pivot falls).  When H holds a NaN or an
+ *         infinity (or its damping term is not finite), KRONQ_ENUMERIC is
+ *         returned instead, info stays -1 and R is not written.
  * All work runs on `stream`, which is synchronized before returning (the
  * flag of a failed pivot is read back).
  * ws    : kronq_chol_inv_ws(n) bytes.
@@ -183,6 +219,12 @@ kronq_status kronq_chol_inv(const float* H, int64_t n, int64_t ldh, float lambda
  * What     : m x n fp32 device dequantized weights, natural order, leading
  *            dimension n; may be NULL.  May alias W when ldw == n.
  * pre_round: m x n fp32 device t values (natural order) or NULL.
+ * row_loss : m fp64 device values or NULL: row_loss[r] = sum_j e_j^2 over the
+ *            row's scaled errors e_j (processing order), summed in fp64.
+ *            Since the weight change of the row is e R (R's rows in
+ *            processing order), this is the row's proxy loss
+ *            (W - What)[r] Hd (W - What)[r]^T with H_G = I (the LDL form of the
+ *            GPTQ bound, Pith review, Table 9).
  * Group sizes: group > 0 must also be a multiple of 8 that divides 128
  *            (8, 16, 32, 64, 128): a group's grid comes from the current
  *            values of one 128-column block of the loop.  Other sizes that
@@ -193,8 +235,8 @@ size_t kronq_gptq_ws(int64_t m, int64_t n);
 kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t ldw,
                                  const float* R, int64_t ldr, const int32_t* perm,
                                  const kronq_qcfg* q, uint8_t* codes, float* scales,
-                                 float* zeros, float* What, float* pre_round, void* ws,
-                                 size_t ws_bytes, void* stream);
+                                 float* zeros, float* What, float* pre_round, double* row_loss,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Weight diagnostic of incoherence processing (Pith review, Figure 2: CV_in and

@@ -17,7 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkronq.so")
 
-KRONQ_OK, KRONQ_EINVAL, KRONQ_ENOTPD, KRONQ_EHIP, KRONQ_EWORKSPACE, KRONQ_EUNSUPPORTED = range(6)
+(KRONQ_OK, KRONQ_EINVAL, KRONQ_ENOTPD, KRONQ_EHIP, KRONQ_EWORKSPACE, KRONQ_EUNSUPPORTED,
+ KRONQ_ENUMERIC, KRONQ_ENOMEM) = range(8)
 KRONQ_F32, KRONQ_BF16 = 0, 1
 
 # every entry point declared in include/kronq.h
@@ -27,7 +28,8 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_allocate_bits", "kronq_biip_unrotate_ws", "kronq_biip_unrotate",
            "kronq_packed_row_bytes", "kronq_pack_codes", "kronq_unpack_codes", "kronq_decode_ws",
            "kronq_decode_matvec", "kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal",
-           "kronq_allocate_types", "kronq_weight_cv_ws", "kronq_weight_cv")
+           "kronq_allocate_types", "kronq_weight_cv_ws", "kronq_weight_cv", "kronq_signs",
+           "kronq_check_finite")
 
 
 class KronqError(RuntimeError):
@@ -77,7 +79,7 @@ def load(path: str = LIB_PATH):
     lib.kronq_gptq_ws.argtypes = [i64, i64]
     lib.kronq_gptq_ws.restype = sz
     lib.kronq_gptq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.POINTER(QCfg), vp, vp,
-                                        vp, vp, vp, vp, sz, vp]
+                                        vp, vp, vp, vp, vp, sz, vp]
     lib.kronq_gptq_quantize.restype = i32
     lib.kronq_sensitivity.argtypes = [vp, i64, i64, vp, i64, i64, vp, vp]
     lib.kronq_sensitivity.restype = i32
@@ -109,6 +111,10 @@ def load(path: str = LIB_PATH):
     lib.kronq_weight_cv_ws.restype = sz
     lib.kronq_weight_cv.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.kronq_weight_cv.restype = i32
+    lib.kronq_signs.argtypes = [ctypes.c_uint64, i64, vp]
+    lib.kronq_signs.restype = i32
+    lib.kronq_check_finite.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.kronq_check_finite.restype = i32
     _lib = lib
     return lib
 
@@ -228,8 +234,9 @@ def kronq_chol_inv(H: torch.Tensor, lam: float, act_order: bool = False,
 def kronq_gptq_quantize(W: torch.Tensor, R: torch.Tensor, perm: torch.Tensor | None, bits: int,
                         group: int, What: torch.Tensor | None = None, want_pre: bool = False,
                         stream=None, ws: torch.Tensor | None = None, codes=None, scales=None,
-                        zeros=None):
-    """Column-wise OBS loop.  Returns dict(codes, scales, zeros, What, pre)."""
+                        zeros=None, want_row_loss: bool = False, row_loss=None):
+    """Column-wise OBS loop.  Returns dict(codes, scales, zeros, What, pre,
+    row_loss); pre and row_loss are None unless asked for."""
     lib = load()
     _dev(W, "W", torch.float32)
     _dev(R, "R", torch.float32)
@@ -245,15 +252,18 @@ def kronq_gptq_quantize(W: torch.Tensor, R: torch.Tensor, perm: torch.Tensor | N
     if What is None:
         What = torch.empty((m, n), dtype=torch.float32, device=dev)
     pre = torch.empty((m, n), dtype=torch.float32, device=dev) if want_pre else None
+    if row_loss is None and want_row_loss:
+        row_loss = torch.empty(m, dtype=torch.float64, device=dev)
     q = QCfg(bits, group)
     need = lib.kronq_gptq_ws(m, n)
     if ws is None or ws.numel() < need:
         ws = _ws(need, dev)
     _check(lib.kronq_gptq_quantize(_ptr(W), m, n, _ld(W), _ptr(R), _ld(R), _ptr(perm),
                                    ctypes.byref(q), _ptr(codes), _ptr(scales), _ptr(zeros),
-                                   _ptr(What), _ptr(pre), _ptr(ws), need, _stream(stream)),
+                                   _ptr(What), _ptr(pre), _ptr(row_loss), _ptr(ws), need,
+                                   _stream(stream)),
            "kronq_gptq_quantize")
-    return dict(codes=codes, scales=scales, zeros=zeros, What=What, pre=pre)
+    return dict(codes=codes, scales=scales, zeros=zeros, What=What, pre=pre, row_loss=row_loss)
 
 
 def kronq_sensitivity(HX: torch.Tensor, HG: torch.Tensor, out: torch.Tensor | None = None,
@@ -420,3 +430,23 @@ def kronq_weight_cv(W: torch.Tensor, col_norms=None, row_norms=None, out=None, s
     _check(lib.kronq_weight_cv(_ptr(W), m, n, _ld(W), _ptr(out), _ptr(col_norms), _ptr(row_norms),
                                _ptr(ws), need, _stream(stream)), "kronq_weight_cv")
     return out
+
+
+def kronq_signs(seed: int, n: int) -> torch.Tensor:
+    """The library's documented sign draw: n floats of +-1 (host tensor)."""
+    lib = load()
+    out = torch.empty(max(n, 1), dtype=torch.float32)
+    _check(lib.kronq_signs(ctypes.c_uint64(seed & (2 ** 64 - 1)), n, out.data_ptr()), "kronq_signs")
+    return out[:n].clone()
+
+
+def kronq_check_finite(A: torch.Tensor, flag: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Device int32 flag: 1 if A (fp32, 2-D row-major) holds a NaN or an infinity."""
+    lib = load()
+    _dev(A, "A", torch.float32)
+    rows, cols = (A.shape if A.dim() == 2 else (1, A.numel()))
+    if flag is None:
+        flag = torch.empty(1, dtype=torch.int32, device=A.device)
+    _check(lib.kronq_check_finite(_ptr(A), rows, cols, _ld(A) if A.dim() == 2 else cols, _ptr(flag),
+                                  _stream(stream)), "kronq_check_finite")
+    return flag

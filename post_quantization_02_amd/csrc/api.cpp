@@ -134,6 +134,8 @@ const char* kronq_status_string(kronq_status s) {
     case KRONQ_EHIP: return "HIP runtime error";
     case KRONQ_EWORKSPACE: return "workspace too small";
     case KRONQ_EUNSUPPORTED: return "unsupported";
+    case KRONQ_ENUMERIC: return "non-finite value";
+    case KRONQ_ENOMEM: return "request exceeds a fixed device buffer";
     default: return "unknown status";
   }
 }
@@ -141,6 +143,33 @@ const char* kronq_status_string(kronq_status s) {
 const char* kronq_last_error(void) { return g_err; }
 
 int32_t kronq_version(void) { return 1; }
+
+// The sign draw: splitmix64's finalizer over a counter with the golden-ratio
+// increment, keyed by the seed (stream 5 of the seed's key sequence).
+static uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+kronq_status kronq_signs(uint64_t seed, int64_t n, float* out_host) {
+  if (n < 0 || (n > 0 && !out_host)) return fail(KRONQ_EINVAL, "kronq_signs: n=%lld out=%p",
+                                                 (long long)n, (void*)out_host);
+  const uint64_t g = 0x9E3779B97F4A7C15ULL;
+  const uint64_t key = sm64_mix(sm64_mix(seed) ^ (6ULL * g));
+  for (int64_t i = 0; i < n; ++i)
+    out_host[i] = (sm64_mix(key + (uint64_t)(i + 1) * g) >> 63) ? -1.0f : 1.0f;
+  return KRONQ_OK;
+}
+
+kronq_status kronq_check_finite(const float* A, int64_t rows, int64_t cols, int64_t ld,
+                                int32_t* flag_dev, void* stream) {
+  if (!flag_dev) return fail(KRONQ_EINVAL, "kronq_check_finite: flag is NULL");
+  if (rows < 0 || cols < 0) return fail(KRONQ_EINVAL, "kronq_check_finite: negative shape");
+  if (rows > 0 && cols > 0 && (!A || ld < cols))
+    return fail(KRONQ_EINVAL, "kronq_check_finite: NULL matrix or ld < cols");
+  return finite_launch(A, rows, cols, ld, flag_dev, (hipStream_t)stream);
+}
 
 size_t kronq_gram_ws(int64_t N, int64_t d, int32_t dtype) {
   if (N < 1 || d < 1 || (dtype != KRONQ_F32 && dtype != KRONQ_BF16)) return 0;
@@ -222,15 +251,15 @@ size_t kronq_gptq_ws(int64_t m, int64_t n) {
 kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t ldw,
                                  const float* R, int64_t ldr, const int32_t* perm,
                                  const kronq_qcfg* q, uint8_t* codes, float* scales,
-                                 float* zeros, float* What, float* pre_round, void* ws,
-                                 size_t ws_bytes, void* stream) {
+                                 float* zeros, float* What, float* pre_round, double* row_loss,
+                                 void* ws, size_t ws_bytes, void* stream) {
   kronq_status st = check_gptq(W, m, n, ldw, R, ldr, q, codes, scales, zeros, What);
   if (st) return st;
   size_t need = gptq_ws_bytes(m, n);
   st = check_ws("kronq_gptq_quantize", ws, ws_bytes, need, false);
   if (st) return st;
   return gptq_launch(W, m, n, ldw, R, ldr, perm, q->bits, q->group > 0 ? q->group : 0, codes,
-                     scales, zeros, What, pre_round, ws, ws_bytes, (hipStream_t)stream);
+                     scales, zeros, What, pre_round, row_loss, ws, ws_bytes, (hipStream_t)stream);
 }
 
 size_t kronq_weight_cv_ws(int64_t m, int64_t n) {

@@ -54,7 +54,8 @@ struct CholWs {
   float* Yp;      // NB x npad   (row block Y_p of step p; two buffers)
   float* Linv;    // NB x NB     (inverse of diagonal block p; two buffers)
   double* damp;   // lambda * mean(diag H)
-  int* flag;      // nonzero after a failed pivot
+  int* flag;      // nonzero after a failed pivot or a non-finite input
+  int* nonfinite; // nonzero when H (or the damping term) holds a NaN or infinity
   long long* info;
   int64_t sP;     // floats between the two Lp (and the two Yp) buffers
 };
@@ -87,6 +88,8 @@ size_t ws_layout(int64_t n, CholWs* w, void* base) {
   off += 256;
   if (w) w->info = reinterpret_cast<long long*>(b + off);
   off += 256;
+  if (w) w->nonfinite = reinterpret_cast<int*>(b + off);
+  off += 256;
   return off;
 }
 
@@ -105,8 +108,21 @@ __global__ void __launch_bounds__(256) chol_prep(const float* H, int64_t n, int6
     const double tr = red[0] + red[1] + red[2] + red[3];
     *w.damp = (double)lambda * (tr / (double)n);
     *w.flag = 0;
+    *w.nonfinite = 0;
     *w.info = -1;
   }
+}
+
+// an fp32 value is NaN or infinite exactly when its exponent field is all ones
+__device__ __forceinline__ bool nonfinite_bits(float v) {
+  return (__float_as_uint(v) & 0x7f800000u) == 0x7f800000u;
+}
+
+// a non-finite entry of the damped matrix stops the factorization: every
+// later kernel sees the flag and returns
+__device__ __forceinline__ void mark_nonfinite(const CholWs& w) {
+  *w.nonfinite = 1;
+  *w.flag = 1;
 }
 
 // perm = stable descending order of diag(H): rank(i) = #{j : d_j > d_i} +
@@ -153,6 +169,7 @@ __global__ void __launch_bounds__(256) chol_gather(const float* H, int64_t n, in
       const int64_t c = min<int64_t>(max<int32_t>(perm[n - 1 - b], 0), n - 1);
       v = H[r * ldh + c];
       if (a == b) v += damp;
+      if (nonfinite_bits(v)) mark_nonfinite(w);
     } else {
       v = (a == b) ? 1.f : 0.f;
     }
@@ -180,6 +197,8 @@ __global__ void __launch_bounds__(256) chol_gather_id4(const float* H, int64_t n
       v[3] = x.x;
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[k] = (a == b + k) ? v[k] + damp : v[k];
+      if (nonfinite_bits(v[0]) | nonfinite_bits(v[1]) | nonfinite_bits(v[2]) | nonfinite_bits(v[3]))
+        mark_nonfinite(w);
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[k] = e[k];
@@ -831,10 +850,16 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
     KQ_LAUNCHED("chol_flip");
   }
   long long h_info = -1;
-  int h_flag = 0;
+  int h_flag = 0, h_nonfinite = 0;
   KQ_HIP(hipMemcpyAsync(&h_info, w.info, sizeof(h_info), hipMemcpyDeviceToHost, s));
   KQ_HIP(hipMemcpyAsync(&h_flag, w.flag, sizeof(h_flag), hipMemcpyDeviceToHost, s));
+  KQ_HIP(hipMemcpyAsync(&h_nonfinite, w.nonfinite, sizeof(h_nonfinite), hipMemcpyDeviceToHost, s));
   KQ_HIP(hipStreamSynchronize(s));
+  if (h_nonfinite) {
+    *info = -1;
+    return fail(KRONQ_ENUMERIC, "kronq_chol_inv: H holds a NaN or an infinity (or its damping term "
+                "is not finite)");
+  }
   if (h_flag) {
     *info = h_info;
     return fail(KRONQ_ENOTPD, "kronq_chol_inv: trailing block at processing index %lld is not "

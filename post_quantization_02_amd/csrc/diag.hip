@@ -18,6 +18,7 @@
 //               norms as E[x] and E[x^2] - E[x]^2 in fp64 (the cancellation
 //               costs 2^-52 / CV^2 relative, below 1e-8 for CV >= 1e-4),
 //               CV = std / mean.
+#include <algorithm>
 #include <cmath>
 
 #include "kronq_internal.h"
@@ -200,7 +201,41 @@ CvLayout cv_layout(int64_t m, int64_t n) {
   return L;
 }
 
+// ---------------------------------------------------------------- finiteness
+
+// an fp32 value is NaN or infinite exactly when its exponent field is all ones
+__device__ __forceinline__ bool nonfinite_bits(float v) {
+  return (__float_as_uint(v) & 0x7f800000u) == 0x7f800000u;
+}
+
+__global__ void finite_clear(int32_t* flag) { *flag = 0; }
+
+// grid-stride scan; any thread that meets a non-finite value stores 1 (all
+// such stores write the same value, so their order does not matter)
+__global__ void __launch_bounds__(256) finite_scan(const float* __restrict__ A, int64_t rows,
+                                                   int64_t cols, int64_t ld, int32_t* flag) {
+  bool bad = false;
+  const int64_t total = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols, c = i - r * cols;
+    bad |= nonfinite_bits(A[r * ld + c]);
+  }
+  if (bad) *flag = 1;
+}
+
 }  // namespace
+
+kronq_status finite_launch(const float* A, int64_t rows, int64_t cols, int64_t ld, int32_t* flag,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(finite_clear, dim3(1), dim3(1), 0, s, flag);
+  KQ_LAUNCHED("finite_clear");
+  if (rows == 0 || cols == 0) return KRONQ_OK;
+  const int64_t total = rows * cols;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(finite_scan, dim3(grid), dim3(256), 0, s, A, rows, cols, ld, flag);
+  KQ_LAUNCHED("finite_scan");
+  return KRONQ_OK;
+}
 
 size_t cv_ws_bytes(int64_t m, int64_t n) { return cv_layout(m, n).total; }
 

@@ -569,6 +569,21 @@ __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
 
 int64_t lde(int64_t n) { return (n + 15) / 16 * 16; }
 
+// row_loss[r] = sum_j E[r][j]^2 over the row's n scaled errors, fp64: one wave
+// per row, lanes striding the row, butterfly reduction across the wave.
+__global__ void __launch_bounds__(256) gptq_row_loss(const double* E, int64_t ldE, int64_t m,
+                                                      int64_t n, double* out) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= m) return;
+  const double* e = E + r * ldE;
+  double acc = 0.0;
+  for (int64_t j = lane; j < n; j += 64) acc = fma(e[j], e[j], acc);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) out[r] = acc;
+}
+
 bool aligned(const void* q, size_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; }
 
 }  // namespace
@@ -582,8 +597,8 @@ size_t gptq_ws_bytes(int64_t m, int64_t n) {
 
 kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
                          int64_t ldr, const int32_t* perm, int bits, int group, uint8_t* codes,
-                         float* scales, float* zeros, float* What, float* pre_round, void* ws,
-                         size_t ws_bytes, hipStream_t s) {
+                         float* scales, float* zeros, float* What, float* pre_round,
+                         double* row_loss, void* ws, size_t ws_bytes, hipStream_t s) {
   (void)ws_bytes;
   if (group > 0 && (BLK % group != 0 || group % 8 != 0))
     return fail(KRONQ_EUNSUPPORTED, "kronq_gptq_quantize: group %d must be a multiple of 8 dividing %d",
@@ -625,6 +640,11 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
                              (int)lds));
   hipLaunchKernelGGL(gptq_kernel, dim3((unsigned)((m + RT - 1) / RT)), dim3(GT), lds, s, p);
   KQ_LAUNCHED("gptq_kernel");
+  if (row_loss) {
+    hipLaunchKernelGGL(gptq_row_loss, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, s,
+                       (const double*)p.E, p.ldE, m, n, row_loss);
+    KQ_LAUNCHED("gptq_row_loss");
+  }
   return KRONQ_OK;
 }
 

@@ -57,8 +57,8 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
 size_t gptq_ws_bytes(int64_t m, int64_t n);
 kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
                          int64_t ldr, const int32_t* perm, int bits, int group, uint8_t* codes,
-                         float* scales, float* zeros, float* What, float* pre_round, void* ws,
-                         size_t ws_bytes, hipStream_t s);
+                         float* scales, float* zeros, float* What, float* pre_round,
+                         double* row_loss, void* ws, size_t ws_bytes, hipStream_t s);
 
 // trace.hip
 kronq_status trace_launch(const float* HX, int64_t n, int64_t ldhx, const float* HG, int64_t m,
@@ -66,6 +66,8 @@ kronq_status trace_launch(const float* HX, int64_t n, int64_t ldhx, const float*
 
 // diag.hip
 size_t cv_ws_bytes(int64_t m, int64_t n);
+kronq_status finite_launch(const float* A, int64_t rows, int64_t cols, int64_t ld, int32_t* flag,
+                           hipStream_t s);
 kronq_status cv_launch(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
                        float* col_norms, float* row_norms, void* ws, hipStream_t s);
 

@@ -103,10 +103,10 @@ class Workload:
         return synth.matrix_dev(synth.GRAD_LOGNORMAL, self.g_seed(sname), self.N, s.m,
                                 p1=self.grad_sigma, dtype=self.dtype, device=device)
 
-    def gen_w(self, sname, dtype=None):
+    def gen_w(self, sname, dtype=None, r0=0, nr=None, c0=0, nc=None):
         s = self.sub(sname)
-        return synth.matrix(synth.NORMAL, self.w_seed(sname), s.m, s.n, p1=self.w_std,
-                            dtype=dtype or self.dtype)
+        return synth.matrix(synth.NORMAL, self.w_seed(sname), s.m, s.n, r0=r0, nr=nr, c0=c0, nc=nc,
+                            p1=self.w_std, dtype=dtype or self.dtype)
 
     def w_f32(self, sname) -> np.ndarray:
         """W as float32 (bf16 storage widened exactly)."""

@@ -115,20 +115,21 @@ def test_invalid_arguments_rejected_before_launch(lib):
     # bits out of range, group not dividing n
     q = kq.QCfg(9, -1)
     st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake, 8, None, ctypes.byref(q), fake, fake, fake,
-                                 None, None, fake, 1 << 30, None)
+                                 None, None, None, fake, 1 << 30, None)
     assert st == kq.KRONQ_EINVAL
     q = kq.QCfg(2, 3)
     st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake, 8, None, ctypes.byref(q), fake, fake, fake,
-                                 None, None, fake, 1 << 30, None)
+                                 None, None, None, fake, 1 << 30, None)
     assert st == kq.KRONQ_EINVAL
     # R not 16-byte aligned, ldr not a multiple of 4 (the product reads R rows
     # with 16-byte loads)
     q = kq.QCfg(2, 4)
     st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake + 4, 8, None,
-                                 ctypes.byref(q), fake, fake, fake, None, None, fake, 1 << 30, None)
+                                 ctypes.byref(q), fake, fake, fake, None, None, None, fake, 1 << 30,
+                                 None)
     assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
     st = lib.kronq_gptq_quantize(fake, 4, 8, 8, fake, 10, None, ctypes.byref(q), fake, fake, fake,
-                                 None, None, fake, 1 << 30, None)
+                                 None, None, None, fake, 1 << 30, None)
     assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
     # negative damping
     info = i64(0)
@@ -148,7 +149,7 @@ def test_workspace_must_be_aligned(lib):
     assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
     q = kq.QCfg(4, 128)
     st = lib.kronq_gptq_quantize(fake, 4, 256, 256, fake, 256, None, ctypes.byref(q), fake, fake, fake,
-                                 None, None, fake + 4, 1 << 30, None)
+                                 None, None, None, fake + 4, 1 << 30, None)
     assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
     st = lib.kronq_weight_cv(fake, 8, 8, 8, fake, None, None, fake + 12, 1 << 30, None)
     assert st == kq.KRONQ_EINVAL and b"aligned" in lib.kronq_last_error()
@@ -244,3 +245,47 @@ def test_allocate_types_bit_exact_vs_oracle():
         kq.kronq_allocate_types([1.0], [2], 2, 2, 1)      # type outside [0, n_types)
     with pytest.raises(kq.KronqError):
         kq.kronq_allocate_types([1.0], [0], 1, 2, 2)      # more upgrades than types
+
+
+def test_signs_match_the_generator_bit_for_bit(lib):
+    # kronq_signs (the library's draw) and synth_signs (the input generator)
+    # are separate implementations of the same documented splitmix64 draw
+    import synth
+    for seed in (0, 1, 5305, 2 ** 63 + 7, 2 ** 64 - 1):
+        for n in (0, 1, 7, 4096, 28672):
+            got = kq.kronq_signs(seed, n).numpy()
+            assert got.shape == (n,)
+            if n:
+                np.testing.assert_array_equal(got, synth.signs(seed, n))
+                assert set(np.unique(got)) <= {-1.0, 1.0}
+    # a balanced draw: about half of each sign
+    s = kq.kronq_signs(123, 1 << 16).numpy()
+    assert abs(float(np.mean(s))) < 0.02
+    assert lib.kronq_signs(1, -1, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_signs(1, 4, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_signs(1, 0, None) == kq.KRONQ_OK
+
+
+def test_signs_hand_value(lib):
+    # first draw of seed 0, worked out from the definition in include/kronq.h
+    M = 2 ** 64 - 1
+    g = 0x9E3779B97F4A7C15
+
+    def mix(z):
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+        return z ^ (z >> 31)
+
+    key = mix(mix(0) ^ ((6 * g) & M))
+    want = [-1.0 if mix((key + (i + 1) * g) & M) >> 63 else 1.0 for i in range(64)]
+    np.testing.assert_array_equal(kq.kronq_signs(0, 64).numpy(), want)
+
+
+def test_new_status_strings_and_check_finite_args(lib):
+    assert lib.kronq_status_string(kq.KRONQ_ENUMERIC) == b"non-finite value"
+    assert lib.kronq_status_string(kq.KRONQ_ENOMEM) == b"request exceeds a fixed device buffer"
+    fake = 1 << 20
+    assert lib.kronq_check_finite(fake, 4, 4, 4, None, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_check_finite(fake, 4, 4, 3, fake, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_check_finite(None, 4, 4, 4, fake, None) == kq.KRONQ_EINVAL
+    assert lib.kronq_check_finite(fake, -1, 4, 4, fake, None) == kq.KRONQ_EINVAL

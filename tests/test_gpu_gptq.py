@@ -22,12 +22,21 @@ def _inputs(m, n, seed, act):
     return W, R.astype(np.float32), perm
 
 
-def _compare(W, R32, perm, bits, group, rows=None):
+def _compare(W, R32, perm, bits, group, rows=None, natural=False):
+    """natural=True passes perm=NULL (identity order: the kernel's vectorised
+    output path when n is a multiple of 8) and requires the same outputs, bit
+    for bit, as the call with the identity permutation as a tensor."""
     m, n = W.shape
     out = kq.kronq_gptq_quantize(to_dev_f32(W), to_dev_f32(R32),
                                  torch.from_numpy(perm.astype(np.int32)).to(DEV), bits, group,
-                                 want_pre=True)
+                                 want_pre=True, want_row_loss=True)
     g = {k: host(v) for k, v in out.items()}
+    if natural:
+        assert np.array_equal(perm, np.arange(n))
+        nat = kq.kronq_gptq_quantize(to_dev_f32(W), to_dev_f32(R32), None, bits, group, want_pre=True,
+                                     want_row_loss=True)
+        for k, v in nat.items():
+            np.testing.assert_array_equal(host(v), g[k], err_msg=k)
     rows = np.arange(m) if rows is None else rows
     tf = TeacherForcing(g["codes"][rows], g["scales"][rows], g["zeros"][rows], perm)
     o = O.gptq(W[rows].astype(np.float64), R32.astype(np.float64), perm, bits, group,
@@ -42,6 +51,11 @@ def _compare(W, R32, perm, bits, group, rows=None):
     assert e <= 1e-4
     assert np.max(np.abs(g["pre"][rows] - o["pre"])) <= 1e-4
     assert g["codes"].max() <= 2 ** bits - 1
+    # row loss: sum of the squared scaled errors (LDL form of the proxy loss)
+    ol = np.sum(o["E"] ** 2, axis=1)
+    el = float(np.max(np.abs(g["row_loss"][rows] - ol) / np.maximum(ol, 1e-300)))
+    say("  row loss rel err %.2e" % el)
+    assert el <= 1e-6
     return g, o
 
 
@@ -58,6 +72,37 @@ def test_gptq_small(m, n, bits, group, act):
     say("gptq", m, n, bits, group, act)
     W, R32, perm = _inputs(m, n, 71, act)
     _compare(W, R32, perm, bits, group)
+
+
+@pytest.mark.parametrize("m,n,bits,group", [(48, 384, 2, 128), (33, 256, 4, -1), (9, 520, 3, 8)])
+def test_gptq_natural_order_vector_outputs(m, n, bits, group):
+    """perm = NULL takes the vectorised output path (n % 8 == 0); its codes,
+    grids, What, pre-round values and row losses match the permuted path
+    bit for bit and the oracle by teacher forcing."""
+    say("gptq natural order", m, n, bits, group)
+    W, R32, perm = _inputs(m, n, 76, False)
+    _compare(W, R32, perm, bits, group, natural=True)
+
+
+def test_gptq_row_loss_is_the_proxy_loss():
+    """With H_G = I the row's proxy loss (W - What) Hd (W - What)^T equals the
+    row loss the kernel reports (the LDL identity), for every row."""
+    say("gptq row loss = proxy loss")
+    m, n = 24, 256
+    W = synth.matrix(synth.NORMAL, 77, m, n, p1=0.02, dtype="f32")
+    H = spd_from_gram(78, n)
+    perm, Hd = O.prepare_hessian(H, 0.01, True)
+    R, _ = O.chol_inv_upper(Hd)
+    out = kq.kronq_gptq_quantize(to_dev_f32(W), to_dev_f32(R.astype(np.float32)),
+                                 torch.from_numpy(perm.astype(np.int32)).to(DEV), 3, 64,
+                                 want_row_loss=True)
+    dW = (W.astype(np.float64) - host(out["What"]).astype(np.float64))[:, perm]
+    Hd32 = np.linalg.inv(R.astype(np.float32).astype(np.float64).T @ R.astype(np.float32).astype(np.float64))
+    want = np.einsum("ij,jk,ik->i", dW, Hd32, dW)
+    got = host(out["row_loss"])
+    e = float(np.max(np.abs(got - want) / want))
+    say("  rel err %.2e" % e)
+    assert e <= 1e-4
 
 
 def test_gptq_identity_factor_is_rtn():
@@ -94,7 +139,7 @@ def test_gptq_full_size_llama2_7b_q_proj_sampled_rows():
     perm, Hd = O.prepare_hessian(H, 0.01, False)
     R, _ = O.chol_inv_upper(Hd)
     rows = np.sort(np.random.default_rng(0).choice(m, 64, replace=False))
-    _compare(W, R.astype(np.float32), perm, 2, 128, rows=rows)
+    _compare(W, R.astype(np.float32), perm, 2, 128, rows=rows, natural=True)
 
 
 def test_gptq_single_group_equals_per_channel():
