@@ -150,7 +150,7 @@ def test_check_finite():
             assert int(host(kq.kronq_check_finite(view))[0]) == 1, (val, i, j)
             full[i, j] = 1.0
     # the largest finite value and denormals are finite
-    full[3, 4] = np.finfo(np.float32).max
+    full[3, 4] = float(np.finfo(np.float32).max)
     full[3, 5] = 1e-45
     assert int(host(kq.kronq_check_finite(view))[0]) == 0
     flag = torch.ones(1, dtype=torch.int32, device=DEV)
