@@ -323,6 +323,29 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
                                  float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The same decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, layouts, results and errors are those of kronq_decode_matvec,
+ * without the workspace: the per-slice partial sums go to a fixed device
+ * buffer inside the library of kronq_decode_noalloc_max_bytes() bytes (4 MiB)
+ * per GPU, which each GPU the library runs on holds until the process ends.
+ * A request whose partial sums, kronq_decode_ws(m, n, bits), exceed it returns
+ * KRONQ_ENOMEM and launches nothing.  The call runs on the calling thread's
+ * current device (`stream` must belong to it); its first call on a device
+ * looks up the buffer's address once (no allocation).  No hipMalloc, hipFree
+ * or allocating library routine is called.  Every call on one GPU shares that
+ * GPU's buffer: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialized by the caller; calls on one stream are
+ * ordered and safe.
+ * ------------------------------------------------------------------------- */
+size_t kronq_decode_noalloc_max_bytes(void);
+kronq_status kronq_decode_matvec_noalloc(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp,
+                                         const kronq_qcfg* q, const float* scales,
+                                         const float* zeros, const int32_t* perm,
+                                         const kronq_had* in_side, const kronq_had* out_side,
+                                         const float* sg, const float* x, float* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sensitivity (hyper.ai summary, Method, Eq. 14: s = tr(H_G) tr(H_X) computed
  * after BiIP).  out3 (device, 3 doubles) = { tr(HX), tr(HG), tr(HX) * tr(HG) },
  * diagonals summed in fp64.  HX is n x n, HG is m x m (fp32 device).

@@ -29,7 +29,7 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_packed_row_bytes", "kronq_pack_codes", "kronq_unpack_codes", "kronq_decode_ws",
            "kronq_decode_matvec", "kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal",
            "kronq_allocate_types", "kronq_weight_cv_ws", "kronq_weight_cv", "kronq_signs",
-           "kronq_check_finite")
+           "kronq_check_finite", "kronq_decode_matvec_noalloc", "kronq_decode_noalloc_max_bytes")
 
 
 class KronqError(RuntimeError):
@@ -115,6 +115,12 @@ def load(path: str = LIB_PATH):
     lib.kronq_signs.restype = i32
     lib.kronq_check_finite.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.kronq_check_finite.restype = i32
+    lib.kronq_decode_matvec_noalloc.argtypes = [vp, i64, i64, i64, ctypes.POINTER(QCfg), vp, vp, vp,
+                                                ctypes.POINTER(Had), ctypes.POINTER(Had), vp, vp, vp,
+                                                vp]
+    lib.kronq_decode_matvec_noalloc.restype = i32
+    lib.kronq_decode_noalloc_max_bytes.argtypes = []
+    lib.kronq_decode_noalloc_max_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -393,6 +399,26 @@ def kronq_decode_matvec(codes: torch.Tensor, n: int, bits: int, group: int, scal
                                    _ptr(zeros), _ptr(perm), ctypes.byref(hin), ctypes.byref(hout),
                                    _ptr(sg), _ptr(x), _ptr(y), _ptr(ws), need, _stream(stream)),
            "kronq_decode_matvec")
+    return y
+
+
+def kronq_decode_matvec_noalloc(codes: torch.Tensor, n: int, bits: int, group: int,
+                                scales: torch.Tensor, zeros: torch.Tensor, in_signs: torch.Tensor,
+                                in_block: int, out_signs: torch.Tensor, out_block: int,
+                                sg: torch.Tensor | None, x: torch.Tensor, y: torch.Tensor,
+                                perm: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kronq_decode_matvec without a workspace (the library's fixed per-GPU
+    buffer); y must be given, so the call allocates nothing."""
+    lib = load()
+    m = codes.shape[0]
+    q = QCfg(bits, group)
+    hin = Had(n, in_block, _ptr(in_signs))
+    hout = Had(m, out_block, _ptr(out_signs))
+    _check(lib.kronq_decode_matvec_noalloc(_ptr(codes), m, n, _ld(codes), ctypes.byref(q),
+                                           _ptr(scales), _ptr(zeros), _ptr(perm), ctypes.byref(hin),
+                                           ctypes.byref(hout), _ptr(sg), _ptr(x), _ptr(y),
+                                           _stream(stream)),
+           "kronq_decode_matvec_noalloc")
     return y
 
 

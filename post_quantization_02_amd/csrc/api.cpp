@@ -120,6 +120,32 @@ static kronq_status check_gptq(const float* W, int64_t m, int64_t n, int64_t ldw
   return KRONQ_OK;
 }
 
+// Argument checks shared by the two decode entry points (no workspace).
+static kronq_status check_decode(const char* fn, const uint8_t* codes, int64_t m, int64_t n,
+                                 int64_t ldp, const kronq_qcfg* q, const float* scales,
+                                 const float* zeros, const int32_t* perm, const kronq_had* in_side,
+                                 const kronq_had* out_side, const float* x, const float* y) {
+  if (!codes || !q || !scales || !zeros || !x || !y) return fail(KRONQ_EINVAL, "%s: NULL pointer", fn);
+  if (q->bits < 1 || q->bits > 8)
+    return fail(KRONQ_EINVAL, "%s: bits %d outside 1..8", fn, (int)q->bits);
+  if (m < 1 || n < 1 || n > INT32_MAX || m > INT32_MAX) return fail(KRONQ_EINVAL, "%s: bad shape", fn);
+  if (ldp < decode_row_bytes(n, q->bits) || ldp % 16 || !aligned(codes, 16))
+    return fail(KRONQ_EINVAL,
+                "%s: codes must be 16-byte aligned with ldp a multiple of 16 covering a row (%lld "
+                "bytes)", fn, (long long)decode_row_bytes(n, q->bits));
+  if (q->group > 0) {
+    if (n % q->group) return fail(KRONQ_EINVAL, "%s: group does not divide n", fn);
+    if (q->group % 64)
+      return fail(KRONQ_EUNSUPPORTED, "%s: group %d is not a multiple of 64", fn, (int)q->group);
+  }
+  if (perm && n > 32768)
+    return fail(KRONQ_EUNSUPPORTED, "%s: codes in processing order need n <= 32768 (got %lld)", fn,
+                (long long)n);
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  return check_had(out_side, m, "output-side");
+}
+
 }  // namespace kronq
 
 using namespace kronq;
@@ -314,29 +340,8 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
                                  const int32_t* perm, const kronq_had* in_side,
                                  const kronq_had* out_side, const float* sg, const float* x,
                                  float* y, void* ws, size_t ws_bytes, void* stream) {
-  if (!codes || !q || !scales || !zeros || !x || !y)
-    return fail(KRONQ_EINVAL, "kronq_decode_matvec: NULL pointer");
-  if (q->bits < 1 || q->bits > 8)
-    return fail(KRONQ_EINVAL, "kronq_decode_matvec: bits %d outside 1..8", (int)q->bits);
-  if (m < 1 || n < 1 || n > INT32_MAX || m > INT32_MAX)
-    return fail(KRONQ_EINVAL, "kronq_decode_matvec: bad shape");
-  if (ldp < decode_row_bytes(n, q->bits) || ldp % 16 || !aligned(codes, 16))
-    return fail(KRONQ_EINVAL,
-                "kronq_decode_matvec: codes must be 16-byte aligned with ldp a multiple of 16 "
-                "covering a row (%lld bytes)", (long long)decode_row_bytes(n, q->bits));
-  if (q->group > 0) {
-    if (n % q->group) return fail(KRONQ_EINVAL, "kronq_decode_matvec: group does not divide n");
-    if (q->group % 64)
-      return fail(KRONQ_EUNSUPPORTED, "kronq_decode_matvec: group %d is not a multiple of 64",
-                  (int)q->group);
-  }
-  if (perm && n > 32768)
-    return fail(KRONQ_EUNSUPPORTED,
-                "kronq_decode_matvec: codes in processing order need n <= 32768 (got %lld)",
-                (long long)n);
-  kronq_status st = check_had(in_side, n, "input-side");
-  if (st) return st;
-  st = check_had(out_side, m, "output-side");
+  kronq_status st = check_decode("kronq_decode_matvec", codes, m, n, ldp, q, scales, zeros, perm,
+                                 in_side, out_side, x, y);
   if (st) return st;
   size_t need = decode_ws_bytes(m, n, q->bits);
   st = check_ws("kronq_decode_matvec", ws, ws_bytes, need, true);
@@ -344,6 +349,20 @@ kronq_status kronq_decode_matvec(const uint8_t* codes, int64_t m, int64_t n, int
   return decode_launch(codes, m, n, ldp, q->bits, q->group > 0 ? q->group : 0, scales, zeros,
                        perm, *in_side, *out_side, sg, x, y, ws, (hipStream_t)stream);
 }
+
+kronq_status kronq_decode_matvec_noalloc(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp,
+                                         const kronq_qcfg* q, const float* scales,
+                                         const float* zeros, const int32_t* perm,
+                                         const kronq_had* in_side, const kronq_had* out_side,
+                                         const float* sg, const float* x, float* y, void* stream) {
+  kronq_status st = check_decode("kronq_decode_matvec_noalloc", codes, m, n, ldp, q, scales, zeros,
+                                 perm, in_side, out_side, x, y);
+  if (st) return st;
+  return decode_launch_noalloc(codes, m, n, ldp, q->bits, q->group > 0 ? q->group : 0, scales, zeros,
+                               perm, *in_side, *out_side, sg, x, y, (hipStream_t)stream);
+}
+
+size_t kronq_decode_noalloc_max_bytes(void) { return decode_scratch_bytes(); }
 
 kronq_status kronq_sensitivity(const float* HX, int64_t n, int64_t ldhx, const float* HG,
                                int64_t m, int64_t ldhg, double* out3, void* stream) {

@@ -29,6 +29,7 @@
 // capture them in a HIP graph.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "kronq_internal.h"
 #include "wht_lds.h"
@@ -471,6 +472,63 @@ kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t l
                      out.signs, sg, lg_k, lg_t, (float)(1.0 / std::sqrt((double)out.block)), y);
   KQ_LAUNCHED("decode_yout");
   return KRONQ_OK;
+}
+
+// ------------------------------------------------- decode without allocation
+//
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the slice partial sums live in a
+// fixed device array of this module, one copy per GPU, held until the process
+// ends.  On the host the array's name is only a stand-in for the symbol; its
+// device address is looked up once per device (with that device current) and
+// only that address is handed to kernels.  Every call on a GPU shares the
+// GPU's copy: calls that overlap on one GPU race on it.  The partial sums are
+// written in full before they are read, so nothing needs clearing.
+
+constexpr size_t kDecodeScratchBytes = size_t(4) << 20;   // 4 MiB: 2^20 partial sums
+
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the calling thread's current device
+kronq_status scratch_address(void** out) {
+  int dev = -1;
+  KQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KRONQ_EUNSUPPORTED, "decode scratch: device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(decode scratch)");
+    if (!p) return fail(KRONQ_EHIP, "hipGetSymbolAddress(decode scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KRONQ_OK;
+}
+
+}  // namespace
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+kronq_status decode_launch_noalloc(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp, int bits,
+                                   int64_t group, const float* scales, const float* zeros,
+                                   const int32_t* perm, const kronq_had& in, const kronq_had& out,
+                                   const float* sg, const float* x, float* y, hipStream_t s) {
+  const size_t need = decode_ws_bytes(m, n, bits);
+  if (need > kDecodeScratchBytes)
+    return fail(KRONQ_ENOMEM, "kronq_decode_matvec_noalloc: %zu bytes of partial sums exceed the "
+                "fixed %zu-byte buffer", need, kDecodeScratchBytes);
+  void* ws = nullptr;
+  const kronq_status st = scratch_address(&ws);
+  if (st) return st;
+  return decode_launch(codes, m, n, ldp, bits, group, scales, zeros, perm, in, out, sg, x, y, ws, s);
 }
 
 }  // namespace kronq

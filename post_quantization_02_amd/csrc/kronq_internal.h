@@ -82,5 +82,10 @@ kronq_status decode_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t l
                            int64_t group, const float* scales, const float* zeros,
                            const int32_t* perm, const kronq_had& in, const kronq_had& out,
                            const float* sg, const float* x, float* y, void* ws, hipStream_t s);
+size_t decode_scratch_bytes();
+kronq_status decode_launch_noalloc(const uint8_t* codes, int64_t m, int64_t n, int64_t ldp, int bits,
+                                   int64_t group, const float* scales, const float* zeros,
+                                   const int32_t* perm, const kronq_had& in, const kronq_had& out,
+                                   const float* sg, const float* x, float* y, hipStream_t s);
 
 }  // namespace kronq
