@@ -474,9 +474,46 @@ __device__ inline bool my_item_group(const GramParams& p, int& item) {
   return true;
 }
 
-__global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p) {
-  int item;
-  if (!my_item_group(p, item)) return;
+// Lockstep of the 32 workgroups of an XCD (one split, S = 1).  With a single
+// split an item streams all N tokens (thousands of stages), and workgroups
+// that started together drift apart by more than the few stages of their
+// shared panels that fit the XCD's L2, so the panels came from the fabric
+// again for nearly every tile.  The persistent variant therefore meets at a
+// barrier of its XCD group every kSyncStages stages: an agent-scope counter per
+// XCD that each workgroup increments and then polls until every workgroup of
+// the group has arrived.  The barrier only orders timing (no data passes
+// through it), and the poll is bounded: after kSyncSpins polls a workgroup
+// goes on, so a group member that is not resident can delay the others but
+// never stop them.
+constexpr int kSyncStages = 128;
+constexpr int kSyncSpins = 4096;
+constexpr int kSyncStride = 64;   // counters 256 bytes apart
+
+struct GramSync {
+  unsigned* ctr;       // this XCD's counter (NULL: no lockstep)
+  unsigned target;     // counter value once the group has reached this barrier
+  unsigned act;        // workgroups in the current group
+};
+
+__device__ __forceinline__ void xcd_barrier(GramSync& sy) {
+  sy.target += sy.act;
+  __builtin_amdgcn_s_barrier();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(sy.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < kSyncSpins; ++k) {
+      if (__hip_atomic_load(sy.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= sy.target) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ void gram_sync_clear(unsigned* ctr) {
+  if (threadIdx.x < kXcds) ctr[threadIdx.x * kSyncStride] = 0u;
+}
+
+template <bool SYNC>
+__device__ __forceinline__ void gram_lds_item(const GramParams& p, int item, GramSync& sy) {
   const int s = item / p.ntiles;
   const int t = item % p.ntiles;
   int ti, tj;
@@ -550,6 +587,9 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p
     v2_step<2>(c, it + 2, st0, st_last, H0, H1, acc);
     v2_step<3>(c, it + 3, st0, st_last, H0, H1, acc);
     if constexpr (V2D > 4) v2_step<V2D - 1>(c, it + V2D - 1, st0, st_last, H0, H1, acc);
+    if constexpr (SYNC) {
+      if ((it + V2D) % kSyncStages == 0 && it + V2D < nstages) xcd_barrier(sy);
+    }
   }
   // the refills past the end are still landing in LDS: drain them before the
   // workgroup can exit
@@ -585,6 +625,30 @@ __global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p
         for (int v = 0; v < 16; ++v)
           __builtin_nontemporal_store(acc[a][b][v],
                                       out + (32 * a + 8 * (v >> 2) + (v & 3)) * BT + 32 * b);
+  }
+}
+
+__global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_kernel(GramParams p) {
+  int item;
+  if (!my_item_group(p, item)) return;
+  GramSync sy{nullptr, 0u, 0u};
+  gram_lds_item<false>(p, item, sy);
+}
+
+// Persistent variant for one split: a grid of kCUs workgroups, workgroup b on
+// XCD x = b % 8 in slot b / 8 of its group; round r runs item 32 (8 r + x) +
+// slot (the item numbering of my_item_group), with the XCD group in lockstep.
+__global__ void __launch_bounds__(BTHREADS, 1) gram_bf16_lds_sync_kernel(GramParams p, unsigned* ctr) {
+  const int b = blockIdx.x;
+  const int x = b % kXcds, slot = b / kXcds;
+  GramSync sy{ctr + x * kSyncStride, 0u, 0u};
+  for (int r = 0;; ++r) {
+    const int g = kXcds * r + x;
+    if (32 * g >= p.nitems) break;
+    const int act = min(32, p.nitems - 32 * g);
+    if (slot >= act) break;   // only the last group can be partial
+    sy.act = (unsigned)act;
+    gram_lds_item<true>(p, 32 * g + slot, sy);
   }
 }
 
@@ -783,6 +847,12 @@ int choose_splits(int ntiles, int64_t nstages) {
   return best;
 }
 
+// the one-split launch of the direct-to-LDS pipeline runs persistent, its
+// XCD groups in lockstep (needs the counters in the workspace)
+bool sync_launch(int64_t N, int64_t d, int32_t dtype) {
+  return dtype == KRONQ_BF16 && d % BT == 0 && N >= (int64_t)V2D * V2K;
+}
+
 void plan(int64_t N, int64_t d, int32_t dtype, int& T, int& ntiles, int& S, int64_t& nstages) {
   const int ts = (dtype == KRONQ_BF16) ? BT : FT;
   const int kst = (dtype == KRONQ_BF16) ? BK : FK;
@@ -795,12 +865,15 @@ void plan(int64_t N, int64_t d, int32_t dtype, int& T, int& ntiles, int& S, int6
 }  // namespace
 
 // workspace: the split-K partial tiles (S > 1)
+// workspace: the split-K partial tiles (S > 1), or the lockstep counters of
+// the persistent one-split launch
 size_t gram_ws_bytes(int64_t N, int64_t d, int32_t dtype) {
   int T, ntiles, S;
   int64_t nstages;
   plan(N, d, dtype, T, ntiles, S, nstages);
   const int ts = (dtype == KRONQ_BF16) ? BT : FT;
-  return (S == 1) ? 0 : (size_t)ntiles * (size_t)S * (size_t)ts * (size_t)ts * sizeof(float);
+  if (S == 1) return sync_launch(N, d, dtype) ? (size_t)kXcds * kSyncStride * sizeof(unsigned) : 0;
+  return (size_t)ntiles * (size_t)S * (size_t)ts * (size_t)ts * sizeof(float);
 }
 
 namespace {
@@ -812,7 +885,13 @@ kronq_status launch_gram(GramParams p, int kind, hipStream_t s) {
   p.nitems = p.ntiles * p.S;
   p.per_xcd = (p.nitems + kXcds - 1) / kXcds;
   const int grid = p.per_xcd * kXcds;
-  if (kind == 0) {
+  if (kind == 0 && p.S == 1) {
+    unsigned* ctr = static_cast<unsigned*>(static_cast<void*>(p.part));
+    hipLaunchKernelGGL(gram_sync_clear, dim3(1), dim3(64), 0, s, ctr);
+    KQ_LAUNCHED("gram_sync_clear");
+    hipLaunchKernelGGL(gram_bf16_lds_sync_kernel, dim3(kCUs), dim3(BTHREADS), 0, s, p, ctr);
+    KQ_LAUNCHED("gram_bf16_lds_sync_kernel");
+  } else if (kind == 0) {
     const int ngroups = (p.nitems + 31) / 32;
     const int rgrid = 32 * kXcds * ((ngroups + kXcds - 1) / kXcds);
     hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(rgrid), dim3(BTHREADS), 0, s, p);
