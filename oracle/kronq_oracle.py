@@ -321,6 +321,100 @@ def gptq(W: np.ndarray, R: np.ndarray, perm, bits: int, group: int, decide_codes
 
 
 # --------------------------------------------------------------------------
+# GPTAQ asymmetric correction.  [summary] Method: building on GPTAQ, the
+# objective also corrects for input drift (asymmetric calibration): the
+# quantized layer sees the inputs X of the partly quantized model while its
+# target is the full-precision layer on the full-precision inputs X_fp;
+# [review] Algorithm 2 takes dXX^T with the Hessian factor, forms
+# P = alpha (dXX^T L) (.) M_U L^T after the inverse Cholesky step (M_U an
+# upper-triangular mask) and uses P in the column loop, whose update is cut
+# off on the pages; [review] proof of Theorem 1: (dXX^T)' = V dXX^T V^T.
+# Readings (derived, pinned by brute force in the tests):
+#  * objective, per output row w (H_G cancels as in Proposition 1):
+#      || X w^ - X_fp w ||^2 / N = d^T H_X d + 2 d^T C^T w + const,
+#    with d = w - w^, dX = X_fp - X and C = dX^T X / N (row form of the
+#    pages' dXX^T, normalized like H_X = X^T X / N); alpha scales the drift
+#    term (alpha = 1 is the full asymmetric objective, 0 is GPTQ);
+#  * the loop is the sequential OBS where column j's drift term is committed
+#    once column j is quantized: each column is rounded at the optimum of the
+#    objective given the quantized earlier columns and the drift of the
+#    earlier columns.  In the coordinates e = R^-T d that objective separates,
+#    and the value at which column k is rounded works out to
+#      w~_k = w_k - sum_{i<k} eps_i R_ik + sum_{j<k} w_j P_jk,
+#    eps_i = (w~_i - q_i) / R_ii (the scaled quantization error), with
+#      P = alpha ((C R^T) (.) M) R,  M_ji = 1 for j < i (strictly upper),
+#    i.e. L = R^T is the pages' lower inverse Cholesky factor (L L^T = H^-1);
+#    after column j is quantized every later column k moves by
+#    -eps_j R_jk + w_j P_jk, with w_j the full-precision weight;
+#  * C, like H_X, is rotated by the input side of BiIP and reordered by the
+#    act-order permutation; P is formed in processing order.
+# --------------------------------------------------------------------------
+
+
+def drift_cross(X, Xfp) -> np.ndarray:
+    """C = (X_fp - X)^T X / N for the N token rows of X (inputs of the partly
+    quantized model) and X_fp (inputs of the full-precision model)."""
+    X = np.asarray(X, dtype=np.float64)
+    dX = np.asarray(Xfp, dtype=np.float64) - X
+    return (dX.T @ X) / X.shape[0]
+
+
+def gptaq_correction(C, R, alpha: float) -> np.ndarray:
+    """P = alpha ((C R^T) (.) M) R with M strictly upper triangular; C and R
+    in processing order (R^T R = Hd^-1)."""
+    C = np.asarray(C, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    K = C @ R.T
+    return alpha * (np.triu(K, 1) @ R)
+
+
+def gptaq(W, R, perm, bits: int, group: int, P, decide_codes=None, decide_params=None):
+    """The column loop with the asymmetric correction: as gptq(), and after
+    column j is quantized every later column k (processing order) also moves
+    by + w_j P[j, k], w_j the full-precision weights of column j.  P = 0 is
+    gptq().  Returns gptq()'s dict."""
+    W = np.asarray(W, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    m, n = W.shape
+    perm = np.asarray(perm, dtype=np.int64)
+    maxq = 2 ** bits - 1
+    W0 = W[:, perm]
+    Wt = W0.copy()
+    ng = 1 if group <= 0 else (n + group - 1) // group
+    scales = np.zeros((m, ng))
+    zeros = np.zeros((m, ng))
+    codes = np.zeros((m, n))
+    What = np.zeros((m, n))
+    pre = np.zeros((m, n))
+    E = np.zeros((m, n))
+    if group <= 0:
+        scale, zero = quant_params(W0, bits)
+        if decide_params is not None:
+            scale, zero = decide_params(0, scale, zero, zero_pre_round(W0, bits))
+        scales[:, 0], zeros[:, 0] = scale, zero
+    for j in range(n):
+        if group > 0 and j % group == 0:
+            scale, zero = quant_params(Wt[:, j:j + group], bits)
+            if decide_params is not None:
+                scale, zero = decide_params(j // group, scale, zero,
+                                            zero_pre_round(Wt[:, j:j + group], bits))
+            scales[:, j // group], zeros[:, j // group] = scale, zero
+        t = Wt[:, j] / scale + zero
+        q = np.clip(np.rint(t), 0, maxq)
+        if decide_codes is not None:
+            q = decide_codes(j, t, q)
+        wq = scale * (q - zero)
+        e = (Wt[:, j] - wq) / R[j, j]
+        Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) - np.outer(W0[:, j], P[j, j + 1:])
+        codes[:, j], What[:, j], pre[:, j], E[:, j] = q, wq, t, e
+    inv = np.empty(n, dtype=np.int64)
+    inv[perm] = np.arange(n)
+    return dict(codes=codes[:, inv], scales=scales, zeros=zeros, What=What[:, inv],
+                pre=pre[:, inv], E=E)
+
+
+# --------------------------------------------------------------------------
 # Step 5: sensitivity and bit allocation.  [summary] Method: the expected loss
 # of a sublayer scales with eps^2 tr(H); with H ~ H_X (x) H_G the score is
 # s = tr(H_G) tr(H_X), computed after BiIP; higher bit-widths go to larger s.

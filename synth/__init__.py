@@ -18,7 +18,7 @@ _SRC = os.path.join(_HERE, "synth.c")
 _SO_DEV = os.path.join(_HERE, "libsynth_gpu.so")
 _SRC_DEV = os.path.join(_HERE, "synth_gpu.hip")
 
-NORMAL, ACT_NORMAL, ACT_T4, GRAD_LOGNORMAL, INT = 0, 1, 2, 3, 4
+NORMAL, ACT_NORMAL, ACT_T4, GRAD_LOGNORMAL, INT, ACT_T4_DRIFT = 0, 1, 2, 3, 4, 5
 _DT = {"f64": (0, np.float64), "f32": (1, np.float32), "bf16": (2, np.uint16)}
 
 _lib = None

@@ -19,7 +19,8 @@
  *                   -ln(u_a u_b) / 2; variance 2)
  * Element (r, c) of a logical rows x cols matrix uses counter e = r * cols + c.
  * Streams: 0 weights, 1 activations, 2 outlier-channel choice, 3 gradient
- * noise, 4 gradient channel scales, 5 Hadamard signs, 6 chi-square part of t4.
+ * noise, 4 gradient channel scales, 5 Hadamard signs, 6 chi-square part of t4,
+ * 7 input drift.
  * Values are produced in double and rounded to the output type: f32 by
  * round-to-nearest-even; bf16 by f64 -> f32 -> bf16, each step nearest-even.
  */
@@ -30,7 +31,8 @@
 
 #define GAMMA 0x9E3779B97F4A7C15ULL
 
-enum { SYN_NORMAL = 0, SYN_ACT_NORMAL = 1, SYN_ACT_T4 = 2, SYN_GRAD_LOGNORMAL = 3, SYN_INT = 4 };
+enum { SYN_NORMAL = 0, SYN_ACT_NORMAL = 1, SYN_ACT_T4 = 2, SYN_GRAD_LOGNORMAL = 3, SYN_INT = 4,
+       SYN_ACT_T4_DRIFT = 5 };
 enum { OUT_F64 = 0, OUT_F32 = 1, OUT_BF16 = 2 };
 
 static inline uint64_t mix64(uint64_t z) {
@@ -98,7 +100,7 @@ int synth_col_factors(int kind, uint64_t seed, int64_t c0, int64_t nc, double p1
                       const int64_t* outliers, int64_t n_out, double out_factor, double* colf) {
   if (c0 < 0 || nc < 0 || (nc > 0 && !colf)) return 1;
   for (int64_t c = 0; c < nc; ++c) colf[c] = 1.0;
-  if (kind == SYN_ACT_NORMAL || kind == SYN_ACT_T4) {
+  if (kind == SYN_ACT_NORMAL || kind == SYN_ACT_T4 || kind == SYN_ACT_T4_DRIFT) {
     for (int64_t o = 0; o < n_out; ++o) {
       int64_t ch = outliers[o];
       if (ch >= c0 && ch < c0 + nc) colf[ch - c0] = out_factor;
@@ -117,6 +119,11 @@ int synth_col_factors(int kind, uint64_t seed, int64_t c0, int64_t nc, double p1
  *   kind SYN_ACT_T4         : t4(stream 1, stream 6) * channel factor
  *   kind SYN_GRAD_LOGNORMAL : normal(stream 3) * exp(p1 * normal(stream 4, column))
  *   kind SYN_INT            : integer uniform in [-p1, p1] (stream 1)
+ *   kind SYN_ACT_T4_DRIFT   : (t4(stream 1, stream 6) + p1 * normal(stream 7)) *
+ *                             channel factor: the SYN_ACT_T4 matrix of the same
+ *                             seed before rounding, plus a drift of relative
+ *                             size p1 (the full-precision model's inputs next to
+ *                             the inputs of a partly quantized model)
  * The channel factor is out_factor for the columns listed in outliers[0..n_out),
  * 1 elsewhere.  out is row-major with leading dimension ld (elements).
  */
@@ -126,12 +133,12 @@ int synth_matrix(int kind, uint64_t seed, int64_t rows, int64_t cols, int64_t r0
   if (rows < 0 || cols < 0 || r0 < 0 || c0 < 0 || nr < 0 || nc < 0) return 1;
   if (r0 + nr > rows || c0 + nc > cols || ld < nc || (nr > 0 && nc > 0 && !out)) return 1;
   if (out_dtype < OUT_F64 || out_dtype > OUT_BF16) return 1;
-  if (kind < SYN_NORMAL || kind > SYN_INT) return 1;
+  if (kind < SYN_NORMAL || kind > SYN_ACT_T4_DRIFT) return 1;
   double* colf = (double*)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
   if (!colf) return 2;
   synth_col_factors(kind, seed, c0, nc, p1, outliers, n_out, out_factor, colf);
   uint64_t k0 = stream_key(seed, 0), k1 = stream_key(seed, 1), k3 = stream_key(seed, 3),
-           k6 = stream_key(seed, 6);
+           k6 = stream_key(seed, 6), k7 = stream_key(seed, 7);
   int64_t ip1 = (int64_t)p1;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < nr; ++r) {
@@ -148,6 +155,12 @@ int synth_matrix(int kind, uint64_t seed, int64_t rows, int64_t cols, int64_t r0
           break;
         }
         case SYN_GRAD_LOGNORMAL: v = normal_at(k3, e) * colf[c]; break;
+        case SYN_ACT_T4_DRIFT: {
+          double z = normal_at(k1, e);
+          double ua = unif_at(k6, 2 * e), ub = unif_at(k6, 2 * e + 1);
+          v = (z * sqrt(2.0 / -log(ua * ub)) + p1 * normal_at(k7, e)) * colf[c];
+          break;
+        }
         default: v = (double)((int64_t)(u64_at(k1, e) % (uint64_t)(2 * ip1 + 1)) - ip1); break;
       }
       int64_t o = r * ld + c;

@@ -18,7 +18,8 @@
 
 namespace {
 
-enum { SYN_NORMAL = 0, SYN_ACT_NORMAL = 1, SYN_ACT_T4 = 2, SYN_GRAD_LOGNORMAL = 3, SYN_INT = 4 };
+enum { SYN_NORMAL = 0, SYN_ACT_NORMAL = 1, SYN_ACT_T4 = 2, SYN_GRAD_LOGNORMAL = 3, SYN_INT = 4,
+       SYN_ACT_T4_DRIFT = 5 };
 enum { OUT_F64 = 0, OUT_F32 = 1, OUT_BF16 = 2 };
 
 __host__ __device__ inline uint64_t mix64(uint64_t z) {
@@ -50,7 +51,7 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 }
 
 struct Keys {
-  uint64_t k0, k1, k3, k6;
+  uint64_t k0, k1, k3, k6, k7;
 };
 
 __global__ void __launch_bounds__(256) synth_fill(int kind, Keys k, int64_t rows, int64_t cols, double p1,
@@ -73,6 +74,12 @@ __global__ void __launch_bounds__(256) synth_fill(int kind, Keys k, int64_t rows
         break;
       }
       case SYN_GRAD_LOGNORMAL: v = normal_at(k.k3, e) * colf[c]; break;
+      case SYN_ACT_T4_DRIFT: {
+        const double z = normal_at(k.k1, e);
+        const double ua = unif_at(k.k6, 2 * e), ub = unif_at(k.k6, 2 * e + 1);
+        v = (z * sqrt(2.0 / -log(ua * ub)) + p1 * normal_at(k.k7, e)) * colf[c];
+        break;
+      }
       default: v = (double)((int64_t)(u64_at(k.k1, e) % (uint64_t)(2 * ip1 + 1)) - ip1); break;
     }
     const int64_t o = r * ld + c;
@@ -90,9 +97,10 @@ __global__ void __launch_bounds__(256) synth_fill(int kind, Keys k, int64_t rows
 extern "C" int synth_matrix_dev(int kind, uint64_t seed, int64_t rows, int64_t cols, double p1,
                                 const double* colf, int out_dtype, void* out, int64_t ld, void* stream) {
   if (rows < 0 || cols < 0 || ld < cols || (rows > 0 && cols > 0 && (!out || !colf))) return 1;
-  if (out_dtype < OUT_F64 || out_dtype > OUT_BF16 || kind < SYN_NORMAL || kind > SYN_INT) return 1;
+  if (out_dtype < OUT_F64 || out_dtype > OUT_BF16 || kind < SYN_NORMAL || kind > SYN_ACT_T4_DRIFT) return 1;
   if (rows == 0 || cols == 0) return 0;
-  Keys k{stream_key(seed, 0), stream_key(seed, 1), stream_key(seed, 3), stream_key(seed, 6)};
+  Keys k{stream_key(seed, 0), stream_key(seed, 1), stream_key(seed, 3), stream_key(seed, 6),
+         stream_key(seed, 7)};
   const int64_t total = rows * cols;
   const unsigned grid = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   hipLaunchKernelGGL(synth_fill, dim3(grid), dim3(256), 0, (hipStream_t)stream, kind, k, rows, cols, p1,

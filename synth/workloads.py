@@ -54,6 +54,7 @@ class Workload:
     avg_bits: float | None = None        # budget of the bit allocation, if any
     grad_sigma: float = 2.0
     w_std: float = 0.02
+    drift: float = 0.05                  # relative size of the full-precision inputs' drift
     description: str = ""
 
     # ---- seeds: one per tensor, derived from the workload seed ----
@@ -91,10 +92,25 @@ class Workload:
         return synth.matrix(synth.GRAD_LOGNORMAL, self.g_seed(sname), self.N, s.m, r0=r0, nr=nr,
                             c0=c0, nc=nc, p1=self.grad_sigma, dtype=dtype or self.dtype, out=out)
 
+    def gen_xfp(self, xname, r0=0, nr=None, c0=0, nc=None, dtype=None, out=None):
+        """Inputs of the full-precision model next to gen_x's (the inputs of a
+        partly quantized model): the same activations plus a drift of relative
+        size `drift` per channel, each rounded on its own."""
+        spec = self.input(xname)
+        return synth.matrix(synth.ACT_T4_DRIFT, self.x_seed(xname), self.N, spec.n, r0=r0, nr=nr,
+                            c0=c0, nc=nc, p1=self.drift, outliers=self.outliers(xname),
+                            out_factor=spec.factor, dtype=dtype or self.dtype, out=out)
+
     # ---- generation in device memory (large inputs; torch tensors) ----
     def gen_x_dev(self, xname, device="cuda:0"):
         spec = self.input(xname)
         return synth.matrix_dev(spec.kind, self.x_seed(xname), self.N, spec.n,
+                                outliers=self.outliers(xname), out_factor=spec.factor,
+                                dtype=self.dtype, device=device)
+
+    def gen_xfp_dev(self, xname, device="cuda:0"):
+        spec = self.input(xname)
+        return synth.matrix_dev(synth.ACT_T4_DRIFT, self.x_seed(xname), self.N, spec.n, p1=self.drift,
                                 outliers=self.outliers(xname), out_factor=spec.factor,
                                 dtype=self.dtype, device=device)
 
@@ -183,4 +199,4 @@ def scaled(w: Workload, *, N: int, div: int, name: str | None = None) -> Workloa
                           max(16, s.out_block // div), s.bits, s.group, s.act_order)
                  for s in w.sublayers)
     return Workload(name or (w.name + "_div%d" % div), w.seed, N, w.dtype, ins, subs, w.alpha,
-                    w.lam, w.block, w.avg_bits, w.grad_sigma, w.w_std, w.description)
+                    w.lam, w.block, w.avg_bits, w.grad_sigma, w.w_std, w.drift, w.description)

@@ -75,6 +75,15 @@ MUTANTS = [
      "Hp = np.asarray(HXp, dtype=np.float64)[np.ix_(np.argsort(perm), np.argsort(perm))]"),
     ("zero pre-round snapped to a half-integer", "    return -xmin / ((xmax - xmin) / maxq)",
      "    return np.floor(-xmin / ((xmax - xmin) / maxq)) + 0.5"),
+    ("GPTAQ mask with the diagonal", "return alpha * (np.triu(K, 1) @ R)", "return alpha * (np.triu(K, 0) @ R)"),
+    ("GPTAQ factor not transposed", "K = C @ R.T\n    return alpha", "K = C @ R\n    return alpha"),
+    ("GPTAQ drift term sign",
+     "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) - np.outer(W0[:, j], P[j, j + 1:])",
+     "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) + np.outer(W0[:, j], P[j, j + 1:])"),
+    ("GPTAQ drift term on compensated weights",
+     "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) - np.outer(W0[:, j], P[j, j + 1:])",
+     "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) - np.outer(Wt[:, j], P[j, j + 1:])"),
+    ("drift cross product transposed", "    return (dX.T @ X) / X.shape[0]", "    return (X.T @ dX) / X.shape[0]"),
     ("type ties to the higher id", "ranked = sorted(range(n_types), key=lambda t: (-total[t], t))",
      "ranked = sorted(range(n_types), key=lambda t: (-total[t], -t))"),
 ]

@@ -743,3 +743,145 @@ def test_biip_modes_against_explicit_matrices():
             np.testing.assert_allclose(got, exp, rtol=1e-12, atol=1e-12)
     with pytest.raises(ValueError):
         O.biip_mode(W, HX, HG, si, ki, so, ko, alpha, "both")
+
+
+# ------------------------------------------------ GPTAQ asymmetric correction
+
+
+def test_drift_cross_brute_force_and_closed_forms():
+    rng = np.random.default_rng(31)
+    N, n = 40, 6
+    X = rng.integers(-3, 4, (N, n)).astype(float)
+    Xfp = X + rng.integers(-1, 2, (N, n)).astype(float)
+    C = O.drift_cross(X, Xfp)
+    ref = np.zeros((n, n))
+    for i in range(n):
+        for k in range(n):
+            ref[i, k] = sum((Xfp[t, i] - X[t, i]) * X[t, k] for t in range(N)) / N
+    np.testing.assert_allclose(C, ref, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(O.drift_cross(X, X), np.zeros((n, n)))
+    np.testing.assert_allclose(O.drift_cross(X, 2 * X), O.gram(X), rtol=1e-15, atol=1e-15)
+
+
+def test_gptaq_correction_structure():
+    # P = alpha ((C R^T) (.) M) R, M strictly upper: P_jk = alpha sum_{j<i<=k}
+    # (C R^T)_ji R_ik, zero on and below the diagonal
+    rng = np.random.default_rng(32)
+    n = 6
+    C = rng.standard_normal((n, n))
+    R, _ = O.chol_inv_upper(rand_spd(rng, n, 30.0))
+    P = O.gptaq_correction(C, R, 0.7)
+    K = C @ R.T
+    ref = np.zeros((n, n))
+    for j in range(n):
+        for k in range(n):
+            ref[j, k] = 0.7 * sum(K[j, i] * R[i, k] for i in range(j + 1, k + 1))
+    np.testing.assert_allclose(P, ref, rtol=1e-13, atol=1e-14)
+    assert not np.any(np.tril(P))
+
+
+def _asym_sequential_obs(W, Hd, HG, C, alpha, bits, group):
+    """Sequential OBS on the explicit Kronecker asymmetric objective
+    vec(dW)^T (Hd (x) HG) vec(dW) + 2 alpha <dW, HG W_<k C>, where W_<k keeps
+    the full-precision columns before k (the drift committed so far): at each
+    column k (and at each group start, for the group's grid) the free columns
+    take the optimum of that objective given the quantized earlier columns;
+    column k is then rounded on its grid.  Returns codes and the pre-round
+    values (m x n, natural order = processing order here)."""
+    m, n = W.shape
+    A = np.kron(Hd, HG)                      # vec index = column * m + row
+    maxq = 2 ** bits - 1
+    Q = np.zeros((m, n))
+    codes = np.zeros((m, n))
+    pre = np.zeros((m, n))
+    if group <= 0:
+        scale, zero = O.quant_params(W, bits)
+
+    def cond_opt(k):
+        # optimum of the free columns >= k given columns < k fixed at Q
+        dW = np.zeros((m, n))
+        dW[:, :k] = W[:, :k] - Q[:, :k]
+        Wk = np.zeros((m, n))
+        Wk[:, :k] = W[:, :k]
+        g = alpha * (HG @ Wk @ C)
+        S = [c * m + r for c in range(k) for r in range(m)]
+        F = [c * m + r for c in range(k, n) for r in range(m)]
+        x = dW.reshape(-1, order="F")
+        gv = g.reshape(-1, order="F")
+        rhs = -(A[np.ix_(F, S)] @ x[S] if S else 0) - gv[F]
+        x[F] = np.linalg.solve(A[np.ix_(F, F)], rhs)
+        return W - x.reshape((m, n), order="F")
+
+    for k in range(n):
+        Wc = cond_opt(k)
+        if group > 0 and k % group == 0:
+            scale, zero = O.quant_params(Wc[:, k:k + group], bits)
+        t = Wc[:, k] / scale + zero
+        q = np.clip(np.rint(t), 0, maxq)
+        Q[:, k] = scale * (q - zero)
+        codes[:, k], pre[:, k] = q, t
+    return codes, pre
+
+
+@pytest.mark.parametrize("seed,group,act", [(33, -1, False), (34, -1, True), (35, 2, False),
+                                            (36, 3, True)])
+def test_gptaq_loop_is_sequential_obs_of_the_asymmetric_objective(seed, group, act):
+    # the reading of the cut-off column update, pinned by brute force: the loop
+    # with P equals the sequential optimum of the explicit Kronecker objective
+    # with the drift term (H_G still cancels); groups take their grid from
+    # those optima at the group's first column
+    rng = np.random.default_rng(seed)
+    m, N, n, bits, alpha = 3, 64, 6, 2, 0.6
+    X = rng.standard_normal((N, n)) * rng.uniform(0.3, 2.0, n)
+    Xfp = X + 0.3 * rng.standard_normal((N, n))
+    W = rng.standard_normal((m, n))
+    HG = rand_spd(rng, m, 1e3)
+    perm, Hd = O.prepare_hessian(O.gram(X), 0.01, act)
+    C = O.drift_cross(X, Xfp)[np.ix_(perm, perm)]
+    R, _ = O.chol_inv_upper(Hd)
+    out = O.gptaq(W, R, perm, bits, group, O.gptaq_correction(C, R, alpha))
+    codes_b, pre_b = _asym_sequential_obs(W[:, perm], Hd, HG, C, alpha, bits, group)
+    np.testing.assert_array_equal(out["codes"][:, perm], codes_b)
+    np.testing.assert_allclose(out["pre"][:, perm], pre_b, rtol=1e-9, atol=1e-9)
+    # the drift term matters here: the plain loop decides differently
+    plain = O.gptq(W, R, perm, bits, group)
+    assert np.max(np.abs(plain["pre"] - out["pre"])) > 1e-3
+
+
+def test_gptaq_without_drift_is_gptq():
+    rng = np.random.default_rng(37)
+    m, n = 5, 12
+    W = rng.standard_normal((m, n))
+    X = rng.standard_normal((50, n))
+    perm, Hd = O.prepare_hessian(O.gram(X), 0.01, True)
+    R, _ = O.chol_inv_upper(Hd)
+    for P in (O.gptaq_correction(O.drift_cross(X, X)[np.ix_(perm, perm)], R, 0.5),
+              O.gptaq_correction(rng.standard_normal((n, n)), R, 0.0)):
+        a = O.gptaq(W, R, perm, 3, 4, P)
+        b = O.gptq(W, R, perm, 3, 4)
+        for k in ("codes", "What", "pre", "E", "scales", "zeros"):
+            np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_drift_term_rotation_invariance():
+    # Theorem 1's transformed drift matrix (dXX^T)' = V dXX^T V^T keeps the
+    # objective's drift term tr(H_G dW C^T W^T) under W' = U S W V^T,
+    # H_G' = U S^-1 H_G S^-1 U^T (and dW' = U S dW V^T)
+    rng = np.random.default_rng(38)
+    m, n, N = 8, 16, 40
+    W = rng.standard_normal((m, n))
+    dW = 0.1 * rng.standard_normal((m, n))
+    X = rng.standard_normal((N, n))
+    C = O.drift_cross(X, X + 0.2 * rng.standard_normal((N, n)))
+    HG = O.gram(rng.standard_normal((N, m)) * rng.uniform(0.2, 3.0, m))
+    si, so = np.sign(rng.standard_normal(n)), np.sign(rng.standard_normal(m))
+    V = O.rotation_matrix(n, 8, si)
+    U = O.rotation_matrix(m, 4, so)
+    s = O.output_rescale(HG, 0.25)
+    S = np.diag(s)
+    Wp, dWp = U @ S @ W @ V.T, U @ S @ dW @ V.T
+    HGp = U @ np.linalg.inv(S) @ HG @ np.linalg.inv(S) @ U.T
+    Cp = V @ C @ V.T
+    lhs = np.trace(HGp @ dWp @ Cp.T @ Wp.T)
+    rhs = np.trace(HG @ dW @ C.T @ W.T)
+    assert lhs == pytest.approx(rhs, rel=1e-10)
