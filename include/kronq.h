@@ -239,6 +239,58 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
                                  void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * GPTAQ asymmetric correction (hyper.ai summary, Method: building on GPTAQ the
+ * objective corrects for input drift by asymmetric calibration -- the
+ * quantized layer sees the inputs X of the partly quantized model while its
+ * target is the full-precision layer on the full-precision inputs X_fp;
+ * Pith review, Algorithm 2: P = alpha (dXX^T L) (.) M_U L^T after the inverse
+ * Cholesky step, used by the column loop; proof of Theorem 1:
+ * (dXX^T)' = V dXX^T V^T).  The column update that uses P is cut off on the
+ * pages; the library's reading is the sequential OBS in which column j's drift
+ * is committed once it is quantized: every later column k then also moves by
+ * + w_j P[j][k], w_j the full-precision weight of column j, with L = R^T and
+ * M_U the strictly upper mask.
+ *
+ * kronq_gram_cross: C = scale A^T B - sub, A and B N x d bf16 (same leading
+ *   dimension ld, a multiple of 8; 16-byte aligned), C d x d fp32 (ldc), sub
+ *   d x d fp32 (ldsub) or NULL.  The drift term is C = X_fp^T X / N - H_X:
+ *   A = X_fp, B = X, scale = 1/N, sub = H_X = X^T X / N (kronq_gram of X).
+ *   bf16 products are exact in fp32 and accumulate in fp32 on the matrix
+ *   cores.  d must be a multiple of 256 and N of 128 (KRONQ_EUNSUPPORTED
+ *   otherwise).  ws: kronq_gram_cross_ws(N, d) bytes.  The input side of BiIP
+ *   applies to C as to H_X: C' = V C V^T is kronq_biip_rotate with W = C,
+ *   both sides the input side's spec, no factors and alpha 0.
+ * kronq_gptaq_correction: P = alpha ((C_p R^T) (.) M) R with
+ *   C_p[a][b] = C[perm[a]][perm[b]] (perm NULL: identity), R the n x n upper
+ *   factor of kronq_chol_inv (processing order, lower triangle zero) and M the
+ *   strictly upper mask; P is n x n fp32 (ldp), strictly upper triangular
+ *   (zeros written on and below the diagonal).  fp32 on the matrix cores.
+ *   ws: kronq_gptaq_correction_ws(n) bytes.
+ * kronq_gptaq_quantize: kronq_gptq_quantize with the drift term: as there,
+ *   and after column j (processing order) is quantized every later column k
+ *   also moves by + W[r][perm[j]] P[j][k] (P n x n fp32, processing order,
+ *   strictly upper, ldp).  The drift shifts are formed up front on the fp32
+ *   matrix cores; a group's grid includes the drift of every earlier column;
+ *   the loop runs in fp64.  row_loss reports the sum of the squared scaled
+ *   errors (w~_j - wq_j) / R_jj.  Groups as kronq_gptq_quantize.  What may
+ *   alias W when ldw == n.  ws: kronq_gptaq_ws(m, n) bytes.
+ * ------------------------------------------------------------------------- */
+size_t kronq_gram_cross_ws(int64_t N, int64_t d);
+kronq_status kronq_gram_cross(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
+                              int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,
+                              size_t ws_bytes, void* stream);
+size_t kronq_gptaq_correction_ws(int64_t n);
+kronq_status kronq_gptaq_correction(const float* C, int64_t n, int64_t ldc, const float* R, int64_t ldr,
+                                    const int32_t* perm, float alpha, float* P, int64_t ldp, void* ws,
+                                    size_t ws_bytes, void* stream);
+size_t kronq_gptaq_ws(int64_t m, int64_t n);
+kronq_status kronq_gptaq_quantize(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
+                                  int64_t ldr, const int32_t* perm, const kronq_qcfg* q, const float* P,
+                                  int64_t ldp, uint8_t* codes, float* scales, float* zeros, float* What,
+                                  float* pre_round, double* row_loss, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* ---------------------------------------------------------------------------
  * Weight diagnostic of incoherence processing (Pith review, Figure 2: CV_in and
  * CV_out are the coefficients of variation of the column norms and of the row
  * norms of W).

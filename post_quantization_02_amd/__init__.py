@@ -29,7 +29,9 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_packed_row_bytes", "kronq_pack_codes", "kronq_unpack_codes", "kronq_decode_ws",
            "kronq_decode_matvec", "kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal",
            "kronq_allocate_types", "kronq_weight_cv_ws", "kronq_weight_cv", "kronq_signs",
-           "kronq_check_finite", "kronq_decode_matvec_noalloc", "kronq_decode_noalloc_max_bytes")
+           "kronq_check_finite", "kronq_decode_matvec_noalloc", "kronq_decode_noalloc_max_bytes",
+           "kronq_gram_cross_ws", "kronq_gram_cross", "kronq_gptaq_correction_ws",
+           "kronq_gptaq_correction", "kronq_gptaq_ws", "kronq_gptaq_quantize")
 
 
 class KronqError(RuntimeError):
@@ -121,6 +123,19 @@ def load(path: str = LIB_PATH):
     lib.kronq_decode_matvec_noalloc.restype = i32
     lib.kronq_decode_noalloc_max_bytes.argtypes = []
     lib.kronq_decode_noalloc_max_bytes.restype = sz
+    lib.kronq_gram_cross_ws.argtypes = [i64, i64]
+    lib.kronq_gram_cross_ws.restype = sz
+    lib.kronq_gram_cross.argtypes = [vp, vp, i64, i64, i64, vp, i64, f32, vp, i64, vp, sz, vp]
+    lib.kronq_gram_cross.restype = i32
+    lib.kronq_gptaq_correction_ws.argtypes = [i64]
+    lib.kronq_gptaq_correction_ws.restype = sz
+    lib.kronq_gptaq_correction.argtypes = [vp, i64, i64, vp, i64, vp, f32, vp, i64, vp, sz, vp]
+    lib.kronq_gptaq_correction.restype = i32
+    lib.kronq_gptaq_ws.argtypes = [i64, i64]
+    lib.kronq_gptaq_ws.restype = sz
+    lib.kronq_gptaq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.POINTER(QCfg), vp, i64,
+                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kronq_gptaq_quantize.restype = i32
     _lib = lib
     return lib
 
@@ -476,3 +491,76 @@ def kronq_check_finite(A: torch.Tensor, flag: torch.Tensor | None = None, stream
     _check(lib.kronq_check_finite(_ptr(A), rows, cols, _ld(A) if A.dim() == 2 else cols, _ptr(flag),
                                   _stream(stream)), "kronq_check_finite")
     return flag
+
+
+def kronq_gram_cross(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
+                     scale: float | None = None, sub: torch.Tensor | None = None, stream=None,
+                     ws: torch.Tensor | None = None) -> torch.Tensor:
+    """C = scale A^T B - sub (A, B: N x d bf16 with one layout; C, sub: d x d fp32).
+    The drift term of the asymmetric objective: A = X_fp, B = X, sub = H_X."""
+    lib = load()
+    _dev(A, "A", torch.bfloat16)
+    _dev(B, "B", torch.bfloat16)
+    N, d = A.shape
+    if tuple(B.shape) != (N, d) or _ld(A) != _ld(B):
+        raise ValueError("A and B must have the same shape and leading dimension")
+    if C is None:
+        C = torch.empty((d, d), dtype=torch.float32, device=A.device)
+    if sub is not None:
+        _dev(sub, "sub", torch.float32)
+    scale = 1.0 / N if scale is None else scale
+    need = lib.kronq_gram_cross_ws(N, d)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, A.device)
+    _check(lib.kronq_gram_cross(_ptr(A), _ptr(B), N, d, _ld(A), _ptr(C), _ld(C), scale, _ptr(sub),
+                                _ld(sub) if sub is not None else d, _ptr(ws), need, _stream(stream)),
+           "kronq_gram_cross")
+    return C
+
+
+def kronq_gptaq_correction(C: torch.Tensor, R: torch.Tensor, perm: torch.Tensor | None, alpha: float,
+                           P: torch.Tensor | None = None, stream=None,
+                           ws: torch.Tensor | None = None) -> torch.Tensor:
+    """P = alpha ((C_p R^T) (.) M) R, M strictly upper, C_p = C[perm][:, perm]."""
+    lib = load()
+    _dev(C, "C", torch.float32)
+    _dev(R, "R", torch.float32)
+    n = C.shape[0]
+    if P is None:
+        P = torch.empty((n, n), dtype=torch.float32, device=C.device)
+    need = lib.kronq_gptaq_correction_ws(n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, C.device)
+    _check(lib.kronq_gptaq_correction(_ptr(C), n, _ld(C), _ptr(R), _ld(R), _ptr(perm), alpha, _ptr(P),
+                                      _ld(P), _ptr(ws), need, _stream(stream)), "kronq_gptaq_correction")
+    return P
+
+
+def kronq_gptaq_quantize(W: torch.Tensor, R: torch.Tensor, perm: torch.Tensor | None, bits: int,
+                         group: int, P: torch.Tensor, What: torch.Tensor | None = None,
+                         want_pre: bool = False, want_row_loss: bool = False, stream=None,
+                         ws: torch.Tensor | None = None, codes=None, scales=None, zeros=None):
+    """The column loop with the asymmetric correction.  Returns the dict of
+    kronq_gptq_quantize."""
+    lib = load()
+    _dev(W, "W", torch.float32)
+    _dev(R, "R", torch.float32)
+    _dev(P, "P", torch.float32)
+    m, n = W.shape
+    ng = 1 if group <= 0 else n // group
+    dev = W.device
+    codes = torch.empty((m, n), dtype=torch.uint8, device=dev) if codes is None else codes
+    scales = torch.empty((m, ng), dtype=torch.float32, device=dev) if scales is None else scales
+    zeros = torch.empty((m, ng), dtype=torch.float32, device=dev) if zeros is None else zeros
+    What = torch.empty((m, n), dtype=torch.float32, device=dev) if What is None else What
+    pre = torch.empty((m, n), dtype=torch.float32, device=dev) if want_pre else None
+    row_loss = torch.empty(m, dtype=torch.float64, device=dev) if want_row_loss else None
+    q = QCfg(bits, group)
+    need = lib.kronq_gptaq_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(lib.kronq_gptaq_quantize(_ptr(W), m, n, _ld(W), _ptr(R), _ld(R), _ptr(perm), ctypes.byref(q),
+                                    _ptr(P), _ld(P), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(What),
+                                    _ptr(pre), _ptr(row_loss), _ptr(ws), need, _stream(stream)),
+           "kronq_gptaq_quantize")
+    return dict(codes=codes, scales=scales, zeros=zeros, What=What, pre=pre, row_loss=row_loss)

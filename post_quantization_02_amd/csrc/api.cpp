@@ -288,6 +288,75 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
                      scales, zeros, What, pre_round, row_loss, ws, ws_bytes, (hipStream_t)stream);
 }
 
+size_t kronq_gram_cross_ws(int64_t N, int64_t d) {
+  if (N < 1 || d < 1) return 0;
+  return gram_cross_ws_bytes(N, d);
+}
+
+kronq_status kronq_gram_cross(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
+                              int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!A || !B || !C) return fail(KRONQ_EINVAL, "kronq_gram_cross: NULL pointer");
+  if (N < 1 || d < 1 || ld < d || ldc < d || (sub && ldsub < d))
+    return fail(KRONQ_EINVAL, "kronq_gram_cross: bad shape");
+  if (!aligned(A, 16) || !aligned(B, 16) || ld % 8 || !aligned(C, 16))
+    return fail(KRONQ_EINVAL, "kronq_gram_cross: A, B and C must be 16-byte aligned, ld a multiple of 8");
+  if (!std::isfinite(scale)) return fail(KRONQ_EINVAL, "kronq_gram_cross: scale not finite");
+  if (d % 256 || N % 128)
+    return fail(KRONQ_EUNSUPPORTED, "kronq_gram_cross: d (%lld) must be a multiple of 256 and N (%lld) "
+                "of 128", (long long)d, (long long)N);
+  const size_t need = gram_cross_ws_bytes(N, d);
+  kronq_status st = check_ws("kronq_gram_cross", ws, ws_bytes, need, true);
+  if (st) return st;
+  return gram_cross_launch(A, B, N, d, ld, C, ldc, scale, sub, ldsub, ws, (hipStream_t)stream);
+}
+
+size_t kronq_gptaq_correction_ws(int64_t n) {
+  if (n < 1) return 0;
+  return gptaq_correction_ws_bytes(n);
+}
+
+kronq_status kronq_gptaq_correction(const float* C, int64_t n, int64_t ldc, const float* R, int64_t ldr,
+                                    const int32_t* perm, float alpha, float* P, int64_t ldp, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!C || !R || !P) return fail(KRONQ_EINVAL, "kronq_gptaq_correction: NULL pointer");
+  if (n < 1 || ldc < n || ldr < n || ldp < n) return fail(KRONQ_EINVAL, "kronq_gptaq_correction: bad shape");
+  if (!std::isfinite(alpha)) return fail(KRONQ_EINVAL, "kronq_gptaq_correction: alpha not finite");
+  kronq_status st = check_ws("kronq_gptaq_correction", ws, ws_bytes, gptaq_correction_ws_bytes(n), true);
+  if (st) return st;
+  return gptaq_correction_launch(C, n, ldc, R, ldr, perm, alpha, P, ldp, ws, (hipStream_t)stream);
+}
+
+size_t kronq_gptaq_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return align_up(gptq_ws_bytes(m, n), 256) + gptaq_shift_ws_bytes(m, n);
+}
+
+kronq_status kronq_gptaq_quantize(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
+                                  int64_t ldr, const int32_t* perm, const kronq_qcfg* q, const float* P,
+                                  int64_t ldp, uint8_t* codes, float* scales, float* zeros, float* What,
+                                  float* pre_round, double* row_loss, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  kronq_status st = check_gptq(W, m, n, ldw, R, ldr, q, codes, scales, zeros, What);
+  if (st) return st;
+  if (!P || ldp < n) return fail(KRONQ_EINVAL, "kronq_gptaq_quantize: P is NULL or ldp < n");
+  if (q->group > 0 && (128 % q->group != 0 || q->group % 8 != 0))
+    return fail(KRONQ_EUNSUPPORTED, "kronq_gptaq_quantize: group %d must be a multiple of 8 dividing 128",
+                (int)q->group);
+  const size_t need = kronq_gptaq_ws(m, n);
+  st = check_ws("kronq_gptaq_quantize", ws, ws_bytes, need, true);
+  if (st) return st;
+  const size_t off = align_up(gptq_ws_bytes(m, n), 256);
+  float* W1 = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+  float* X2 = reinterpret_cast<float*>(static_cast<char*>(ws) + off +
+                                       align_up((size_t)m * (size_t)n * sizeof(float), 256));
+  const int unit = q->group > 0 ? q->group : 128;
+  st = gptaq_shift_launch(W, m, n, ldw, perm, P, ldp, unit, W1, X2, (hipStream_t)stream);
+  if (st) return st;
+  return gptq_launch(W, m, n, ldw, R, ldr, perm, q->bits, q->group > 0 ? q->group : 0, codes, scales,
+                     zeros, What, pre_round, row_loss, ws, off, (hipStream_t)stream, W1, X2);
+}
+
 size_t kronq_weight_cv_ws(int64_t m, int64_t n) {
   if (m < 1 || n < 1) return 0;
   return cv_ws_bytes(m, n);

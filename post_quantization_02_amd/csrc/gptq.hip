@@ -34,8 +34,13 @@ constexpr int CT = 256;        // chain threads (waves 0..3)
 constexpr int GT = 512;        // threads: chain waves, then four product waves
 
 struct GptqParams {
-  const float* W;
-  int64_t m, n, ldw;
+  const float* W;          // the weights (per-channel grids)
+  const float* Wp;         // what the start values begin from: W, or W plus the
+                           // drift shift of earlier units (asymmetric correction)
+  const float* X2;         // drift shift from earlier columns of a unit (m x n,
+                           // processing order), added after the unit's grid; or NULL
+  int unit;                // columns of a unit: the group, or 128 per-channel
+  int64_t m, n, ldw, ldwp;
   const float* R;
   int64_t ldr;
   const int32_t* perm;     // may be NULL
@@ -167,6 +172,7 @@ __device__ __forceinline__ Quant quant(double v, double scale, double zero, doub
 
 struct Chain {
   double v[8];               // this lane's 8 columns of its row
+  float x2[8];               // drift shift of those columns from earlier columns of their unit
   f64x2_t rc[4];             // staged R row of the current column (this lane's 8 entries)
   double idc;                // 1 / R_cc of the current column
   double scale, zero, inv_scale;     // grid of the current group
@@ -176,7 +182,7 @@ struct Chain {
 __device__ __forceinline__ double rc_at(const Chain& st, int q) { return st.rc[q >> 1][q & 1]; }
 
 // Columns 8 O .. 8 O + 7 of the block (owned by lane O of each 16-lane row).
-template <int O>
+template <bool DRIFT, int O>
 __device__ __forceinline__ void chain_octet(Chain& st, const GptqParams& p, const double* Rsq,
                                             int part_id, bool row_ok, int64_t grow, int64_t jb,
                                             int ncols, double maxq) {
@@ -207,6 +213,15 @@ __device__ __forceinline__ void chain_octet(Chain& st, const GptqParams& p, cons
     st.oscale = mine ? st.scale : st.oscale;
     st.ozero = mine ? st.zero : st.ozero;
     st.oinv = mine ? st.inv_scale : st.oinv;
+  }
+  if (DRIFT && ((8 * O) % p.unit) == 0) {
+    // the unit starting at column 8 O has its grid: add the drift shift of
+    // its own earlier columns to its values (it does not depend on rounding)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int cc = 8 * part_id + q;
+      if (cc >= 8 * O && cc < 8 * O + p.unit) st.v[q] += (double)st.x2[q];
+    }
   }
   // this lane's entries of row 8 O, and the reciprocal diagonal from column
   // 8 O on: one address per octet (kept out of the block loop by the empty
@@ -248,11 +263,11 @@ __device__ __forceinline__ void chain_octet(Chain& st, const GptqParams& p, cons
   }
 }
 
-template <int... O>
+template <bool DRIFT, int... O>
 __device__ __forceinline__ void chain_octets(Chain& st, const GptqParams& p, const double* Rsq,
                                              int part_id, bool row_ok, int64_t grow, int64_t jb,
                                              int ncols, double maxq, std::integer_sequence<int, O...>) {
-  (chain_octet<O>(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq), ...);
+  (chain_octet<DRIFT, O>(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq), ...);
 }
 
 // Stage diagonal block b (its fp64 image, made once per call) into Rsq.
@@ -270,6 +285,7 @@ __device__ __forceinline__ void stage_rsq(const GptqParams& p, double* Rsq, int 
   }
 }
 
+template <bool DRIFT>
 __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int tid) {
   double* Rsq = gl;
   const double* P0 = gl + SQ;
@@ -313,13 +329,20 @@ __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int 
         st.rc[q] = *reinterpret_cast<const f64x2_t*>(Rsq + 8 * part_id + 2 * q);
       }
       st.idc = Rsq[(BLK - 1) * BLK];
+      if constexpr (DRIFT) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int64_t col = jb + 8 * part_id + q;
+          st.x2[q] = (row_ok && col < p.n) ? p.X2[grow * p.n + col] : 0.f;
+        }
+      }
     }
     // Every column of the block is walked (past ncols the values, staged rows
     // and reciprocals are zero and nothing is stored), so the loop has no exit
     // inside and the reads of the staged rows do not wait on the chain.  The 16
     // octets of columns are a compile-time sequence, so the owner lane of a
     // column (broadcast by DPP) and the register holding it are constants.
-    chain_octets(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq,
+    chain_octets<DRIFT>(st, p, Rsq, part_id, row_ok, grow, jb, ncols, maxq,
                  std::make_integer_sequence<int, 16>{});
     // ---- outputs of this lane's columns ----
     // A column's value is final once its own step is done (later steps
@@ -455,6 +478,7 @@ __global__ void __launch_bounds__(256) gptq_r64(GptqParams p) {
   for (int64_t j = n4 + threadIdx.x; j < p.n; j += 256) dst[j] = (double)src[j];
 }
 
+template <bool DRIFT>
 __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, int tid) {
   double* P0 = gl + SQ;
   double* P1 = P0 + RT * BLK;
@@ -480,7 +504,7 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
       for (int t = 0; t < 4; ++t) {
         const int64_t wr = min<int64_t>(row0 + 4 * v + g, p.m - 1);
         const int64_t wc = colmap(p, min<int64_t>(jn + 64 * ch + 4 * r + t, p.n - 1));
-        w[v][t] = p.W[wr * p.ldw + wc];
+        w[v][t] = DRIFT ? p.Wp[wr * p.ldwp + wc] : p.W[wr * p.ldw + wc];
       }
   };
   // start values of the block at column jn: W - acc (first half), acc (second)
@@ -556,15 +580,19 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
   }
 }
 
+// DRIFT: the asymmetric correction's drift shifts (start values from Wp, X2
+// added at unit starts); a separate instantiation so that the plain loop keeps
+// its registers
+template <bool DRIFT>
 __global__ void __launch_bounds__(GT, 1) gptq_kernel(GptqParams p) {
   extern __shared__ __align__(16) double gl[];
   const int tid = threadIdx.x;
   // the role is uniform per wave: a scalar branch; both roles pass the same
   // sequence of barriers
   if (__builtin_amdgcn_readfirstlane(tid >> 6) < CT / 64)
-    chain_role(p, gl, tid);
+    chain_role<DRIFT>(p, gl, tid);
   else
-    product_role(p, gl, tid);
+    product_role<DRIFT>(p, gl, tid);
 }
 
 int64_t lde(int64_t n) { return (n + 15) / 16 * 16; }
@@ -598,16 +626,21 @@ size_t gptq_ws_bytes(int64_t m, int64_t n) {
 kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
                          int64_t ldr, const int32_t* perm, int bits, int group, uint8_t* codes,
                          float* scales, float* zeros, float* What, float* pre_round,
-                         double* row_loss, void* ws, size_t ws_bytes, hipStream_t s) {
+                         double* row_loss, void* ws, size_t ws_bytes, hipStream_t s,
+                         const float* Wp, const float* X2) {
   (void)ws_bytes;
   if (group > 0 && (BLK % group != 0 || group % 8 != 0))
     return fail(KRONQ_EUNSUPPORTED, "kronq_gptq_quantize: group %d must be a multiple of 8 dividing %d",
                 group, BLK);
   GptqParams p{};
   p.W = W;
+  p.Wp = Wp ? Wp : W;
+  p.X2 = X2;
+  p.unit = group > 0 ? group : BLK;
   p.m = m;
   p.n = n;
   p.ldw = ldw;
+  p.ldwp = Wp ? n : ldw;
   p.R = R;
   p.ldr = ldr;
   p.perm = perm;
@@ -636,9 +669,15 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
   hipLaunchKernelGGL(gptq_r64, dim3((unsigned)((n + BLK - 1) / BLK * BLK)), dim3(256), 0, s, p);
   KQ_LAUNCHED("gptq_r64");
   const size_t lds = kGptqLds;
-  KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)lds));
-  hipLaunchKernelGGL(gptq_kernel, dim3((unsigned)((m + RT - 1) / RT)), dim3(GT), lds, s, p);
+  if (X2) {
+    KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(gptq_kernel<true>, dim3((unsigned)((m + RT - 1) / RT)), dim3(GT), lds, s, p);
+  } else {
+    KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(gptq_kernel<false>, dim3((unsigned)((m + RT - 1) / RT)), dim3(GT), lds, s, p);
+  }
   KQ_LAUNCHED("gptq_kernel");
   if (row_loss) {
     hipLaunchKernelGGL(gptq_row_loss, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, s,

@@ -54,8 +54,12 @@ constexpr int FPANEL = FK * FLD;
 
 struct GramParams {
   const void* A;
+  const void* B;     // J panels: A for the Gram; the second operand of a cross product
   int64_t N, d, lda, ldh;
   float* H;
+  const float* sub;  // cross product: subtracted after scaling (may be NULL)
+  int64_t ldsub;
+  bool cross;        // H = scale A^T B - sub over all tiles, no mirroring
   float* part;       // S > 1: partial tiles [item][tile][tile]
   float scale, beta;
   int T;             // tiles per side
@@ -94,6 +98,31 @@ __device__ inline void tile_coords(int t, int T, int& ti, int& tj) {
   ti = tj = 0;
 }
 
+// All-tiles number t -> (ti, tj) of a cross product, in 4 x 4 super-tile order.
+__device__ inline void tile_coords_full(int t, int T, int& ti, int& tj) {
+  const int SB = 4;
+  const int R = (T + SB - 1) / SB;
+  for (int sr = 0; sr < R; ++sr) {
+    const int r0 = sr * SB, nr = min(SB, T - r0);
+    const int cnt = nr * T;
+    if (t < cnt) {
+      const int sc = (t / nr) / SB;                    // column super-tile
+      const int c0 = sc * SB, nc = min(SB, T - c0);
+      const int u = t - nr * c0;                        // index inside the super-tile
+      ti = r0 + u / nc;
+      tj = c0 + u % nc;
+      return;
+    }
+    t -= cnt;
+  }
+  ti = tj = 0;
+}
+
+__device__ inline void tile_of(const GramParams& p, int t, int& ti, int& tj) {
+  if (p.cross) tile_coords_full(t, p.T, ti, tj);
+  else tile_coords(t, p.T, ti, tj);
+}
+
 // XCD-aware item of this workgroup; false when the slot is past the end.
 __device__ inline bool my_item(const GramParams& p, int& item) {
   const int b = blockIdx.x;
@@ -110,7 +139,9 @@ __device__ inline void split_range(const GramParams& p, int s, int64_t& st0, int
 __device__ inline void put(const GramParams& p, int64_t i, int64_t j, float v, bool mirror) {
   if (i >= p.d || j >= p.d) return;
   float* h = p.H + i * p.ldh + j;
-  *h = (p.beta != 0.0f) ? fmaf(p.scale, v, p.beta * *h) : p.scale * v;
+  float x = (p.beta != 0.0f) ? fmaf(p.scale, v, p.beta * *h) : p.scale * v;
+  if (p.sub) x -= p.sub[i * p.ldsub + j];
+  *h = x;
   if (mirror) {
     float* g = p.H + j * p.ldh + i;
     *g = (p.beta != 0.0f) ? fmaf(p.scale, v, p.beta * *g) : p.scale * v;
@@ -517,7 +548,7 @@ __device__ __forceinline__ void gram_lds_item(const GramParams& p, int item, Gra
   const int s = item / p.ntiles;
   const int t = item % p.ntiles;
   int ti, tj;
-  tile_coords(t, p.T, ti, tj);
+  tile_of(p, t, ti, tj);
   const int64_t I0 = (int64_t)ti * BT, J0 = (int64_t)tj * BT;
   const bool diag = ti == tj;
   const int tid = threadIdx.x;
@@ -532,7 +563,7 @@ __device__ __forceinline__ void gram_lds_item(const GramParams& p, int item, Gra
   c.lane = lane;
   c.row_bytes = p.lda * 2;
   c.gI = static_cast<const unsigned char*>(p.A) + I0 * 2;
-  c.gJ = static_cast<const unsigned char*>(p.A) + J0 * 2;
+  c.gJ = static_cast<const unsigned char*>(p.B) + J0 * 2;
   {
     // operand reads: group g = lane / 16, j = lane % 16 addresses token
     // 8 (g / 2) + j / 4 (+ 4 for the second read) and features
@@ -599,6 +630,7 @@ __device__ __forceinline__ void gram_lds_item(const GramParams& p, int item, Gra
   if (p.S == 1) {
     const int64_t ib = I0 + wm * 128 + 4 * lk, jb = J0 + wn * 128 + lr;
     const bool beta0 = (p.beta == 0.0f);
+    const bool mirror = !diag && !p.cross;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -609,8 +641,9 @@ __device__ __forceinline__ void gram_lds_item(const GramParams& p, int item, Gra
           const int64_t jj = jb + 32 * b;
           const float x = p.scale * acc[a][b][v];
           float* h = p.H + i * p.ldh + jj;
-          *h = beta0 ? x : fmaf(p.beta, *h, x);
-          if (!diag) {
+          if (p.sub) *h = (beta0 ? x : fmaf(p.beta, *h, x)) - p.sub[i * p.ldsub + jj];
+          else *h = beta0 ? x : fmaf(p.beta, *h, x);
+          if (mirror) {
             float* gg = p.H + jj * p.ldh + i;
             *gg = beta0 ? x : fmaf(p.beta, *gg, x);
           }
@@ -770,7 +803,7 @@ __global__ void __launch_bounds__(256, 2) gram_f32_kernel(GramParams p) {
 // for an off-diagonal tile the transposed copy goes through LDS, so that the
 // mirrored writes are row segments too.
 __device__ __forceinline__ void put4(const GramParams& p, int64_t i, int64_t j, f32x4_t v) {
-  if (p.vec_h && i < p.d && j + 4 <= p.d) {
+  if (p.vec_h && i < p.d && j + 4 <= p.d) {   // vec_h: H (and sub) 16-byte rows
     f32x4_t* h = reinterpret_cast<f32x4_t*>(p.H + i * p.ldh + j);
     f32x4_t x;
     if (p.beta != 0.0f) {
@@ -779,6 +812,10 @@ __device__ __forceinline__ void put4(const GramParams& p, int64_t i, int64_t j, 
       for (int e = 0; e < 4; ++e) x[e] = fmaf(p.scale, v[e], p.beta * o[e]);
     } else {
       x = v * p.scale;
+    }
+    if (p.sub) {
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(p.sub + i * p.ldsub + j);
+      x -= s4;
     }
     *h = x;
   } else {
@@ -794,7 +831,7 @@ __global__ void __launch_bounds__(256) gram_finalize_kernel(GramParams p) {
   const int t = blockIdx.x / (NSUB * NSUB), sb = blockIdx.x % (NSUB * NSUB);
   const int sr = sb / NSUB, sc = sb % NSUB;
   int ti, tj;
-  tile_coords(t, p.T, ti, tj);
+  tile_of(p, t, ti, tj);
   const bool diag = (ti == tj);
   f32x4_t sum[4];
 #pragma unroll
@@ -812,7 +849,7 @@ __global__ void __launch_bounds__(256) gram_finalize_kernel(GramParams p) {
     const int f = threadIdx.x + 256 * q, rr = f >> 4, c4 = (f & 15) * 4;
     put4(p, (int64_t)ti * TS + sr * SUB + rr, (int64_t)tj * TS + sc * SUB + c4, sum[q]);
   }
-  if (diag) return;
+  if (diag || p.cross) return;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int f = threadIdx.x + 256 * q, rr = f >> 4, c4 = (f & 15) * 4;
@@ -864,7 +901,6 @@ void plan(int64_t N, int64_t d, int32_t dtype, int& T, int& ntiles, int& S, int6
 
 }  // namespace
 
-// workspace: the split-K partial tiles (S > 1)
 // workspace: the split-K partial tiles (S > 1), or the lockstep counters of
 // the persistent one-split launch
 size_t gram_ws_bytes(int64_t N, int64_t d, int32_t dtype) {
@@ -931,6 +967,7 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
   (void)ws_bytes;
   GramParams p{};
   p.A = A;
+  p.B = A;
   p.N = N;
   p.d = d;
   p.lda = lda;
@@ -965,6 +1002,58 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
     return launch_gram(q, 1, s);
   }
   return KRONQ_OK;
+}
+
+// ------------------------------------------------------------- cross product
+//
+// C = scale A^T B - sub for two N x d bf16 matrices with the same layout: the
+// same pipelined tiles over all T x T tiles (no symmetry, no mirroring).  The
+// drift term of the asymmetric objective is C = X_fp^T X / N - H_X (A = X_fp,
+// B = X, sub = H_X = X^T X / N).
+
+namespace {
+
+void plan_cross(int64_t N, int64_t d, int& T, int& ntiles, int& S, int64_t& nstages) {
+  T = (int)(d / BT);
+  ntiles = T * T;
+  nstages = N / BK;
+  S = choose_splits(ntiles, nstages);
+}
+
+}  // namespace
+
+size_t gram_cross_ws_bytes(int64_t N, int64_t d) {
+  int T, ntiles, S;
+  int64_t nstages;
+  plan_cross(N, d, T, ntiles, S, nstages);
+  const int64_t units = N / ((int64_t)V2D * V2K);
+  S = (int)std::max<int64_t>(1, std::min<int64_t>(S, units));
+  if (S == 1) return (size_t)kXcds * kSyncStride * sizeof(unsigned);
+  return (size_t)ntiles * (size_t)S * (size_t)BT * (size_t)BT * sizeof(float);
+}
+
+kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
+                               int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,
+                               hipStream_t s) {
+  GramParams p{};
+  p.A = A;
+  p.B = B;
+  p.N = N;
+  p.d = d;
+  p.lda = ld;
+  p.ldh = ldc;
+  p.H = C;
+  p.sub = sub;
+  p.ldsub = ldsub;
+  p.cross = true;
+  p.vec_h = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
+            (!sub || (ldsub % 4 == 0 && reinterpret_cast<uintptr_t>(sub) % 16 == 0));
+  p.part = static_cast<float*>(ws);
+  p.scale = scale;
+  p.beta = 0.0f;
+  plan_cross(N, d, p.T, p.ntiles, p.S, p.nstages);
+  p.S = (int)std::max<int64_t>(1, std::min<int64_t>(p.S, N / ((int64_t)V2D * V2K)));
+  return launch_gram(p, 0, s);
 }
 
 }  // namespace kronq

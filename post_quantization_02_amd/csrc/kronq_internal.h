@@ -37,6 +37,11 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
                          int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
                          hipStream_t s);
 
+size_t gram_cross_ws_bytes(int64_t N, int64_t d);
+kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
+                               int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,
+                               hipStream_t s);
+
 // fwht.hip
 size_t biip_ws_bytes(int64_t m, int64_t n);
 kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX, int64_t ldhx,
@@ -58,7 +63,18 @@ size_t gptq_ws_bytes(int64_t m, int64_t n);
 kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const float* R,
                          int64_t ldr, const int32_t* perm, int bits, int group, uint8_t* codes,
                          float* scales, float* zeros, float* What, float* pre_round,
-                         double* row_loss, void* ws, size_t ws_bytes, hipStream_t s);
+                         double* row_loss, void* ws, size_t ws_bytes, hipStream_t s,
+                         const float* Wp = nullptr, const float* X2 = nullptr);
+
+// gptaq.hip
+size_t gptaq_correction_ws_bytes(int64_t n);
+kronq_status gptaq_correction_launch(const float* C, int64_t n, int64_t ldc, const float* R, int64_t ldr,
+                                     const int32_t* perm, float alpha, float* P, int64_t ldp, void* ws,
+                                     hipStream_t s);
+size_t gptaq_shift_ws_bytes(int64_t m, int64_t n);
+kronq_status gptaq_shift_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const int32_t* perm,
+                                const float* P, int64_t ldp, int unit, float* W1, float* X2,
+                                hipStream_t s);
 
 // trace.hip
 kronq_status trace_launch(const float* HX, int64_t n, int64_t ldhx, const float* HG, int64_t m,

@@ -1,0 +1,205 @@
+"""Parity of the GPTAQ asymmetric correction with the oracle: the drift cross
+term C = X_fp^T X / N - H_X (kronq_gram_cross), its input-side rotation
+(kronq_biip_rotate on C), P = alpha ((C_p R^T) (.) M) R
+(kronq_gptaq_correction) and the column loop with the drift term
+(kronq_gptaq_quantize), each stage on the same inputs as the oracle stage.
+
+Tolerances: the cross term is a bf16 contraction accumulated in fp32 (like the
+Gram): bit-exact on integer inputs, <= 1e-4 relative Frobenius on the drifted
+activations (the 1e-3 Gram bar, tightened), where the subtraction of H_X
+cancels about 1 / drift^2 of the magnitude.  P is two fp32 products of
+length <= n: <= 1e-5 relative Frobenius, zeros on and below the diagonal
+exact.  The column loop is teacher-forced as kronq_gptq_quantize's parity."""
+import numpy as np
+import pytest
+import torch
+
+import post_quantization_02_amd as kq
+import synth
+from synth import workloads as WL
+from oracle import kronq_oracle as O
+from gpu_helpers import DEV, TeacherForcing, host, rel_fro, say, spd_from_gram, to_dev_bf16, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,d,with_sub", [(2048, 512, False), (2048, 512, True), (8192, 4096, True)])
+def test_gram_cross_integer_inputs_bit_exact(N, d, with_sub):
+    # integers in {-2..2}: every partial sum is an integer below 2^24; (2048,
+    # 512) takes the split-token path with the finalize kernel, (8192, 4096)
+    # the persistent one-split launch with XCD-group barriers
+    say("gram cross integer exact", N, d, with_sub)
+    a = synth.matrix(synth.INT, 21, N, d, p1=2, dtype="bf16")
+    b = synth.matrix(synth.INT, 22, N, d, p1=2, dtype="bf16")
+    A64, B64 = synth.bf16_to_f64(a), synth.bf16_to_f64(b)
+    sub = None
+    ref = A64.T @ B64
+    if with_sub:
+        s = synth.matrix(synth.INT, 23, d, d, p1=100, dtype="f32")
+        sub = to_dev_f32(s)
+        ref = ref - s
+    C = kq.kronq_gram_cross(to_dev_bf16(a), to_dev_bf16(b), scale=1.0, sub=sub)
+    np.testing.assert_array_equal(host(C), ref.astype(np.float32))
+
+
+def _drift_inputs(div, N):
+    w = WL.scaled(WL.C2, N=N, div=div)
+    return w, w.gen_x("x"), w.gen_xfp("x")
+
+
+def test_drift_cross_term_parity():
+    say("drift cross term vs oracle")
+    w, X, Xfp = _drift_inputs(8, 8192)          # 8192 x 512 bf16
+    Xd, Xfd = to_dev_bf16(X), to_dev_bf16(Xfp)
+    HX = kq.kronq_gram(Xd)
+    C = host(kq.kronq_gram_cross(Xfd, Xd, sub=HX))
+    ref = O.drift_cross(synth.bf16_to_f64(X), synth.bf16_to_f64(Xfp))
+    e = rel_fro(C, ref)
+    say("  rel fro %.2e (|C| / |H_X| = %.3f)" % (e, np.linalg.norm(ref) / np.linalg.norm(host(HX))))
+    assert e <= 1e-4
+
+
+def test_drift_cross_term_rotation():
+    # (dXX^T)' = V dXX^T V^T through kronq_biip_rotate with both sides the
+    # input side's spec, no rescale
+    say("drift cross term rotation")
+    n, k = 512, 256
+    C = synth.matrix(synth.NORMAL, 24, n, n, p1=0.1, dtype="f32")
+    si = synth.signs(25, n)
+    Cd = to_dev_f32(C)
+    sd = to_dev_f32(si)
+    kq.kronq_biip_rotate(Cd, None, None, sd, k, sd, k, 0.0)
+    V = O.rotation_matrix(n, k, si)
+    e = rel_fro(host(Cd), V @ C.astype(np.float64) @ V.T)
+    say("  rel fro %.2e" % e)
+    assert e <= 1e-5
+
+
+def _correction_inputs(n, seed, act):
+    H = spd_from_gram(seed, n)
+    perm, Hd = O.prepare_hessian(H, 0.01, act)
+    R, _ = O.chol_inv_upper(Hd)
+    X = synth.matrix(synth.ACT_T4, seed + 1, 4 * n, n, dtype="f64")
+    C = O.drift_cross(X, X + 0.05 * synth.matrix(synth.NORMAL, seed + 2, 4 * n, n, dtype="f64"))
+    return C.astype(np.float32), R.astype(np.float32), perm
+
+
+@pytest.mark.parametrize("n,act,alpha", [(300, True, 0.25), (512, False, 1.0), (1024, True, 0.5),
+                                         (129, False, 0.25)])
+def test_gptaq_correction_parity(n, act, alpha):
+    say("gptaq correction", n, act, alpha)
+    C32, R32, perm = _correction_inputs(n, 31 + n, act)
+    pd = torch.from_numpy(perm.astype(np.int32)).to(DEV) if act else None
+    P = host(kq.kronq_gptaq_correction(to_dev_f32(C32), to_dev_f32(R32), pd, alpha))
+    Cp = C32.astype(np.float64)[np.ix_(perm, perm)]
+    ref = O.gptaq_correction(Cp, R32.astype(np.float64), alpha)
+    e = rel_fro(P, ref)
+    say("  rel fro %.2e" % e)
+    assert e <= 1e-5
+    assert not np.any(np.tril(P))
+
+
+def _loop_compare(W, R32, perm, P32, bits, group, rows=None):
+    m, n = W.shape
+    pd = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    out = kq.kronq_gptaq_quantize(to_dev_f32(W), to_dev_f32(R32), pd, bits, group, to_dev_f32(P32),
+                                  want_pre=True, want_row_loss=True)
+    g = {k: host(v) for k, v in out.items()}
+    rows = np.arange(m) if rows is None else rows
+    tf = TeacherForcing(g["codes"][rows], g["scales"][rows], g["zeros"][rows], perm)
+    o = O.gptaq(W[rows].astype(np.float64), R32.astype(np.float64), perm, bits, group,
+                P32.astype(np.float64), decide_codes=tf.codes_hook, decide_params=tf.params_hook)
+    say("  hard %d ties %d scale err %.2e" % (tf.hard, tf.ties, tf.scale_err), tf.hard_where)
+    assert tf.hard == 0
+    assert tf.ties <= 1e-4 * len(rows) * n + 0.5
+    assert tf.scale_err <= 1e-6
+    np.testing.assert_array_equal(g["zeros"][rows], o["zeros"].astype(np.float32))
+    e = rel_fro(g["What"][rows], o["What"])
+    say("  What rel fro %.2e" % e)
+    assert e <= 1e-4
+    assert np.max(np.abs(g["pre"][rows] - o["pre"])) <= 1e-4
+    ol = np.sum(o["E"] ** 2, axis=1)
+    assert np.max(np.abs(g["row_loss"][rows] - ol) / ol) <= 1e-6
+    return g, o
+
+
+@pytest.mark.parametrize("m,n,bits,group,act", [
+    (40, 300, 3, -1, True),      # ragged, per-channel, act-order
+    (48, 384, 2, 128, False),    # groups of 128
+    (33, 256, 4, 64, True),      # two groups a block: the second group's grid sees the first's drift
+    (70, 520, 2, 8, False),      # tiny groups
+])
+def test_gptaq_loop_parity(m, n, bits, group, act):
+    say("gptaq loop", m, n, bits, group, act)
+    W = synth.matrix(synth.NORMAL, 41 + n, m, n, p1=0.02, dtype="f32")
+    C32, R32, perm = _correction_inputs(n, 42 + n, act)
+    P = O.gptaq_correction(C32.astype(np.float64)[np.ix_(perm, perm)], R32.astype(np.float64), 0.5)
+    g, o = _loop_compare(W, R32, perm, P.astype(np.float32), bits, group)
+    # the drift term moves the loop: the plain loop's values differ
+    plain = O.gptq(W.astype(np.float64), R32.astype(np.float64), perm, bits, group)
+    assert np.max(np.abs(plain["pre"] - o["pre"])) > 1e-3
+
+
+def test_gptaq_without_drift_equals_gptq():
+    say("gptaq with P = 0 is the plain loop")
+    m, n = 32, 384
+    W = synth.matrix(synth.NORMAL, 51, m, n, p1=0.02, dtype="f32")
+    _, R32, perm = _correction_inputs(n, 52, True)
+    pd = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    Wd, Rd = to_dev_f32(W), to_dev_f32(R32)
+    Z = torch.zeros((n, n), dtype=torch.float32, device=DEV)
+    for group in (-1, 128):
+        a = kq.kronq_gptaq_quantize(Wd, Rd, pd, 3, group, Z, want_pre=True)
+        b = kq.kronq_gptq_quantize(Wd, Rd, pd, 3, group, want_pre=True)
+        for k in ("codes", "What", "pre", "scales", "zeros"):
+            np.testing.assert_array_equal(host(a[k]), host(b[k]), err_msg=k)
+
+
+def test_gptaq_whole_chain_stage_by_stage():
+    """Gram, cross term, BiIP (W, H_X, H_G and C), factor, P and the loop on a
+    Llama-2-7B q_proj recipe scaled to 512 x 512 with 8192 tokens, each stage
+    fed the device's previous outputs and compared with the oracle stage."""
+    say("gptaq whole chain")
+    w, X, Xfp = _drift_inputs(8, 8192)
+    s = w.sublayers[0]
+    G = w.gen_g(s.name)
+    W = w.w_f32(s.name)
+    si, so = w.in_signs("x"), w.out_signs(s.name)
+    Xd, Xfd = to_dev_bf16(X), to_dev_bf16(Xfp)
+    HX = kq.kronq_gram(Xd)
+    HG = kq.kronq_gram(to_dev_bf16(G))
+    C = kq.kronq_gram_cross(Xfd, Xd, sub=HX)
+    C_in = host(C).astype(np.float64)
+    HX_in, HG_in = host(HX).astype(np.float64), host(HG).astype(np.float64)
+    Wd = to_dev_f32(W)
+    sid, sod = to_dev_f32(si), to_dev_f32(so)
+    kq.kronq_biip_rotate(Wd, HX, HG, sid, s.in_block, sod, s.out_block, w.alpha)
+    kq.kronq_biip_rotate(C, None, None, sid, s.in_block, sid, s.in_block, 0.0)
+    Wp, HXp, _, _ = O.biip(W.astype(np.float64), HX_in, HG_in, si, s.in_block, so, s.out_block, w.alpha)
+    V = O.rotation_matrix(s.n, s.in_block, si)
+    assert rel_fro(host(C), V @ C_in @ V.T) <= 1e-5
+    assert rel_fro(host(Wd), Wp) <= 1e-5 and rel_fro(host(HX), HXp) <= 1e-5
+    R, perm, info = kq.kronq_chol_inv(HX, w.lam, True)
+    assert info == -1
+    R32, perm_h = host(R), host(perm)
+    P = kq.kronq_gptaq_correction(C, R, perm, 0.25)
+    Cp = host(C).astype(np.float64)[np.ix_(perm_h, perm_h)]
+    Po = O.gptaq_correction(Cp, R32.astype(np.float64), 0.25)
+    assert rel_fro(host(P), Po) <= 1e-5
+    _loop_compare(host(Wd), R32, perm_h, host(P), s.bits, s.group)
+
+
+def test_gptaq_full_size_llama2_7b_q_proj_sampled_rows():
+    # 4096 x 4096, W2 g128: P from the oracle's factor and a drift term, the
+    # loop on every row, 48 sampled rows replayed
+    say("gptaq full size q_proj")
+    m = n = 4096
+    W = WL.C2.w_f32("q_proj")
+    C32, R32, perm = _correction_inputs(n, 61, False)
+    P = host(kq.kronq_gptaq_correction(to_dev_f32(C32), to_dev_f32(R32), None, 0.25))
+    Po = O.gptaq_correction(C32.astype(np.float64), R32.astype(np.float64), 0.25)
+    e = rel_fro(P, Po)
+    say("  P rel fro %.2e" % e)
+    assert e <= 1e-5
+    rows = np.sort(np.random.default_rng(1).choice(m, 48, replace=False))
+    _loop_compare(W, R32, perm, P, 2, 128, rows=rows)
