@@ -251,15 +251,20 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
  * + w_j P[j][k], w_j the full-precision weight of column j, with L = R^T and
  * M_U the strictly upper mask.
  *
- * kronq_gram_cross: C = scale A^T B - sub, A and B N x d bf16 (same leading
- *   dimension ld, a multiple of 8; 16-byte aligned), C d x d fp32 (ldc), sub
- *   d x d fp32 (ldsub) or NULL.  The drift term is C = X_fp^T X / N - H_X:
- *   A = X_fp, B = X, scale = 1/N, sub = H_X = X^T X / N (kronq_gram of X).
- *   bf16 products are exact in fp32 and accumulate in fp32 on the matrix
- *   cores.  d must be a multiple of 256 and N of 128 (KRONQ_EUNSUPPORTED
- *   otherwise).  ws: kronq_gram_cross_ws(N, d) bytes.  The input side of BiIP
- *   applies to C as to H_X: C' = V C V^T is kronq_biip_rotate with W = C,
- *   both sides the input side's spec, no factors and alpha 0.
+ * kronq_drift_cross: the drift term C = (X_fp - X)^T X / N (the pages' dXX^T
+ *   in the normalization of H_X), X_fp and X N x n bf16 (same leading
+ *   dimension ld, a multiple of 8; 16-byte aligned), C n x n fp32 (ldc).
+ *   dX = X_fp - X is formed exactly in fp32 and split into two bf16 parts (hi
+ *   + lo, 16 significant bits: exact unless X_fp and X differ by more than a
+ *   factor 2^8), then hi^T X + lo^T X accumulates in fp32 on the bf16 matrix
+ *   cores, in chunks of 32768 tokens.  n must be a multiple of 256 and N of
+ *   128 (KRONQ_EUNSUPPORTED otherwise).  ws: kronq_drift_cross_ws(N, n)
+ *   bytes.  The input side of BiIP applies to C as to H_X: C' = V C V^T is
+ *   kronq_biip_rotate with W = C, both sides the input side's spec, HX and HG
+ *   NULL and alpha 0.
+ * kronq_gram_cross: the general cross product C = scale A^T B - sub (A and B
+ *   N x d bf16 with one layout as above, sub d x d fp32 or NULL), on the same
+ *   tiles.  ws: kronq_gram_cross_ws(N, d) bytes.
  * kronq_gptaq_correction: P = alpha ((C_p R^T) (.) M) R with
  *   C_p[a][b] = C[perm[a]][perm[b]] (perm NULL: identity), R the n x n upper
  *   factor of kronq_chol_inv (processing order, lower triangle zero) and M the
@@ -275,6 +280,9 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
  *   errors (w~_j - wq_j) / R_jj.  Groups as kronq_gptq_quantize.  What may
  *   alias W when ldw == n.  ws: kronq_gptaq_ws(m, n) bytes.
  * ------------------------------------------------------------------------- */
+size_t kronq_drift_cross_ws(int64_t N, int64_t n);
+kronq_status kronq_drift_cross(const void* Xfp, const void* X, int64_t N, int64_t n, int64_t ld, float* C,
+                               int64_t ldc, void* ws, size_t ws_bytes, void* stream);
 size_t kronq_gram_cross_ws(int64_t N, int64_t d);
 kronq_status kronq_gram_cross(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
                               int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,

@@ -30,7 +30,8 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_decode_matvec", "kronq_allocate_bits_passwise", "kronq_allocate_bits_marginal",
            "kronq_allocate_types", "kronq_weight_cv_ws", "kronq_weight_cv", "kronq_signs",
            "kronq_check_finite", "kronq_decode_matvec_noalloc", "kronq_decode_noalloc_max_bytes",
-           "kronq_gram_cross_ws", "kronq_gram_cross", "kronq_gptaq_correction_ws",
+           "kronq_gram_cross_ws", "kronq_gram_cross", "kronq_drift_cross_ws", "kronq_drift_cross",
+           "kronq_gptaq_correction_ws",
            "kronq_gptaq_correction", "kronq_gptaq_ws", "kronq_gptaq_quantize")
 
 
@@ -127,6 +128,10 @@ def load(path: str = LIB_PATH):
     lib.kronq_gram_cross_ws.restype = sz
     lib.kronq_gram_cross.argtypes = [vp, vp, i64, i64, i64, vp, i64, f32, vp, i64, vp, sz, vp]
     lib.kronq_gram_cross.restype = i32
+    lib.kronq_drift_cross_ws.argtypes = [i64, i64]
+    lib.kronq_drift_cross_ws.restype = sz
+    lib.kronq_drift_cross.argtypes = [vp, vp, i64, i64, i64, vp, i64, vp, sz, vp]
+    lib.kronq_drift_cross.restype = i32
     lib.kronq_gptaq_correction_ws.argtypes = [i64]
     lib.kronq_gptaq_correction_ws.restype = sz
     lib.kronq_gptaq_correction.argtypes = [vp, i64, i64, vp, i64, vp, f32, vp, i64, vp, sz, vp]
@@ -515,6 +520,25 @@ def kronq_gram_cross(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = 
     _check(lib.kronq_gram_cross(_ptr(A), _ptr(B), N, d, _ld(A), _ptr(C), _ld(C), scale, _ptr(sub),
                                 _ld(sub) if sub is not None else d, _ptr(ws), need, _stream(stream)),
            "kronq_gram_cross")
+    return C
+
+
+def kronq_drift_cross(Xfp: torch.Tensor, X: torch.Tensor, C: torch.Tensor | None = None, stream=None,
+                      ws: torch.Tensor | None = None) -> torch.Tensor:
+    """C = (X_fp - X)^T X / N (X_fp, X: N x n bf16 with one layout; C n x n fp32)."""
+    lib = load()
+    _dev(Xfp, "Xfp", torch.bfloat16)
+    _dev(X, "X", torch.bfloat16)
+    N, n = X.shape
+    if tuple(Xfp.shape) != (N, n) or _ld(Xfp) != _ld(X):
+        raise ValueError("X_fp and X must have the same shape and leading dimension")
+    if C is None:
+        C = torch.empty((n, n), dtype=torch.float32, device=X.device)
+    need = lib.kronq_drift_cross_ws(N, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, X.device)
+    _check(lib.kronq_drift_cross(_ptr(Xfp), _ptr(X), N, n, _ld(X), _ptr(C), _ld(C), _ptr(ws), need,
+                                 _stream(stream)), "kronq_drift_cross")
     return C
 
 

@@ -308,7 +308,26 @@ kronq_status kronq_gram_cross(const void* A, const void* B, int64_t N, int64_t d
   const size_t need = gram_cross_ws_bytes(N, d);
   kronq_status st = check_ws("kronq_gram_cross", ws, ws_bytes, need, true);
   if (st) return st;
-  return gram_cross_launch(A, B, N, d, ld, C, ldc, scale, sub, ldsub, ws, (hipStream_t)stream);
+  return gram_cross_launch(A, B, N, d, ld, C, ldc, scale, 0.0f, sub, ldsub, ws, (hipStream_t)stream);
+}
+
+size_t kronq_drift_cross_ws(int64_t N, int64_t n) {
+  if (N < 1 || n < 1) return 0;
+  return drift_cross_ws_bytes(N, n);
+}
+
+kronq_status kronq_drift_cross(const void* Xfp, const void* X, int64_t N, int64_t n, int64_t ld, float* C,
+                               int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+  if (!Xfp || !X || !C) return fail(KRONQ_EINVAL, "kronq_drift_cross: NULL pointer");
+  if (N < 1 || n < 1 || ld < n || ldc < n) return fail(KRONQ_EINVAL, "kronq_drift_cross: bad shape");
+  if (!aligned(Xfp, 16) || !aligned(X, 16) || ld % 8 || !aligned(C, 16))
+    return fail(KRONQ_EINVAL, "kronq_drift_cross: X, X_fp and C must be 16-byte aligned, ld a multiple of 8");
+  if (n % 256 || N % 128)
+    return fail(KRONQ_EUNSUPPORTED, "kronq_drift_cross: n (%lld) must be a multiple of 256 and N (%lld) "
+                "of 128", (long long)n, (long long)N);
+  kronq_status st = check_ws("kronq_drift_cross", ws, ws_bytes, drift_cross_ws_bytes(N, n), true);
+  if (st) return st;
+  return drift_cross_launch(Xfp, X, N, n, ld, C, ldc, ws, (hipStream_t)stream);
 }
 
 size_t kronq_gptaq_correction_ws(int64_t n) {

@@ -7,7 +7,8 @@
 //
 // With R the upper factor (R^T R = Hd^-1, processing order) the pages' lower
 // factor is L = R^T, so
-//   K = C_p R^T            C_p = C[perm][:, perm], C = X_fp^T X / N - H_X
+//   K = C_p R^T            C_p = C[perm][:, perm], C = (X_fp - X)^T X / N
+//                          (the drift term, rotated by the input side of BiIP)
 //   P = alpha triu1(K) R   triu1: the strictly upper part
 // and in the column loop every later column k moves by + w_j P[j][k] once
 // column j is quantized, w_j the full-precision weight of column j.  That
@@ -180,7 +181,69 @@ kronq_status run_gemm(GemmArgs g, hipStream_t s, const char* name) {
   return KRONQ_OK;
 }
 
+// dX = X_fp - X (exact in fp32: both are bf16) as hi + lo, each bf16: hi =
+// bf16(dX), lo = bf16(dX - hi); the pair carries 16 significant bits, which is
+// dX exactly unless X_fp and X differ by more than a factor 2^8.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__global__ void __launch_bounds__(256) drift_split(const uint16_t* __restrict__ Xfp,
+                                                   const uint16_t* __restrict__ X, int64_t rows, int64_t n,
+                                                   int64_t ld, uint16_t* __restrict__ hi,
+                                                   uint16_t* __restrict__ lo) {
+  const int64_t total = rows * n;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / n, c = i - r * n;
+    const float a = __uint_as_float((uint32_t)Xfp[r * ld + c] << 16);
+    const float b = __uint_as_float((uint32_t)X[r * ld + c] << 16);
+    const float d = a - b;
+    const uint16_t h = bf16_rne(d);
+    const float hf = __uint_as_float((uint32_t)h << 16);
+    hi[i] = h;
+    lo[i] = bf16_rne(d - hf);
+  }
+}
+
+constexpr int64_t kDriftChunk = 32768;   // tokens per chunk of the drift term
+
 }  // namespace
+
+// C = (X_fp - X)^T X / N in token chunks: each chunk's dX is split into two
+// bf16 matrices, and C accumulates hi^T X + lo^T X on the bf16 matrix cores
+// (the cross-product tiles with beta = 1 after the first call).  Forming dX
+// first keeps the fp32 accumulation on the drift's own scale; X_fp^T X - H_X
+// would cancel most of the fp32 sums.
+size_t drift_cross_ws_bytes(int64_t N, int64_t n) {
+  const int64_t ch = std::min<int64_t>(N, kDriftChunk);
+  return 2 * align_up((size_t)ch * (size_t)n * sizeof(uint16_t), 256) + gram_cross_ws_bytes(ch, n);
+}
+
+kronq_status drift_cross_launch(const void* Xfp, const void* X, int64_t N, int64_t n, int64_t ld, float* C,
+                                int64_t ldc, void* ws, hipStream_t s) {
+  const int64_t ch = std::min<int64_t>(N, kDriftChunk);
+  const size_t half = align_up((size_t)ch * (size_t)n * sizeof(uint16_t), 256);
+  uint16_t* hi = static_cast<uint16_t*>(ws);
+  uint16_t* lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
+  void* cws = static_cast<char*>(ws) + 2 * half;
+  const float scale = (float)(1.0 / (double)N);
+  for (int64_t t0 = 0; t0 < N; t0 += ch) {
+    const int64_t rows = std::min<int64_t>(ch, N - t0);
+    const uint16_t* a = static_cast<const uint16_t*>(Xfp) + t0 * ld;
+    const uint16_t* b = static_cast<const uint16_t*>(X) + t0 * ld;
+    const unsigned grid = (unsigned)std::min<int64_t>((rows * n + 255) / 256, 16384);
+    hipLaunchKernelGGL(drift_split, dim3(grid), dim3(256), 0, s, a, b, rows, n, ld, hi, lo);
+    KQ_LAUNCHED("drift_split");
+    kronq_status st = gram_cross_launch(hi, b, rows, n, n, C, ldc, scale, t0 == 0 ? 0.0f : 1.0f, nullptr, 0,
+                                        cws, s);
+    if (st) return st;
+    st = gram_cross_launch(lo, b, rows, n, n, C, ldc, scale, 1.0f, nullptr, 0, cws, s);
+    if (st) return st;
+  }
+  return KRONQ_OK;
+}
 
 size_t gptaq_correction_ws_bytes(int64_t n) { return align_up((size_t)n * (size_t)n * sizeof(float), 256); }
 

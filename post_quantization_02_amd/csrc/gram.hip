@@ -1006,10 +1006,9 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
 
 // ------------------------------------------------------------- cross product
 //
-// C = scale A^T B - sub for two N x d bf16 matrices with the same layout: the
-// same pipelined tiles over all T x T tiles (no symmetry, no mirroring).  The
-// drift term of the asymmetric objective is C = X_fp^T X / N - H_X (A = X_fp,
-// B = X, sub = H_X = X^T X / N).
+// C = scale A^T B + beta C - sub for two N x d bf16 matrices with the same
+// layout: the same pipelined tiles over all T x T tiles (no symmetry, no
+// mirroring).
 
 namespace {
 
@@ -1033,8 +1032,8 @@ size_t gram_cross_ws_bytes(int64_t N, int64_t d) {
 }
 
 kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
-                               int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,
-                               hipStream_t s) {
+                               int64_t ldc, float scale, float beta, const float* sub, int64_t ldsub,
+                               void* ws, hipStream_t s) {
   GramParams p{};
   p.A = A;
   p.B = B;
@@ -1050,7 +1049,7 @@ kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t 
             (!sub || (ldsub % 4 == 0 && reinterpret_cast<uintptr_t>(sub) % 16 == 0));
   p.part = static_cast<float*>(ws);
   p.scale = scale;
-  p.beta = 0.0f;
+  p.beta = beta;
   plan_cross(N, d, p.T, p.ntiles, p.S, p.nstages);
   p.S = (int)std::max<int64_t>(1, std::min<int64_t>(p.S, N / ((int64_t)V2D * V2K)));
   return launch_gram(p, 0, s);

@@ -39,8 +39,8 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
 
 size_t gram_cross_ws_bytes(int64_t N, int64_t d);
 kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
-                               int64_t ldc, float scale, const float* sub, int64_t ldsub, void* ws,
-                               hipStream_t s);
+                               int64_t ldc, float scale, float beta, const float* sub, int64_t ldsub,
+                               void* ws, hipStream_t s);
 
 // fwht.hip
 size_t biip_ws_bytes(int64_t m, int64_t n);
@@ -71,6 +71,9 @@ size_t gptaq_correction_ws_bytes(int64_t n);
 kronq_status gptaq_correction_launch(const float* C, int64_t n, int64_t ldc, const float* R, int64_t ldr,
                                      const int32_t* perm, float alpha, float* P, int64_t ldp, void* ws,
                                      hipStream_t s);
+size_t drift_cross_ws_bytes(int64_t N, int64_t n);
+kronq_status drift_cross_launch(const void* Xfp, const void* X, int64_t N, int64_t n, int64_t ld, float* C,
+                                int64_t ldc, void* ws, hipStream_t s);
 size_t gptaq_shift_ws_bytes(int64_t m, int64_t n);
 kronq_status gptaq_shift_launch(const float* W, int64_t m, int64_t n, int64_t ldw, const int32_t* perm,
                                 const float* P, int64_t ldp, int unit, float* W1, float* X2,
