@@ -588,6 +588,59 @@ def run_workload(w, steps, warmup, dev):
     return wall_ms, per_sub, t_gen, paths
 
 
+def gptaq_leg(w, path, dev, steps=5):
+    """The asymmetric correction on the Llama-2-7B q_proj shape: the drift term
+    (X_fp - X)^T X / N from a drifted input stream, its input-side rotation, P,
+    and the column loop with the drift term; event-timed, inputs resident."""
+    import torch
+    import post_quantization_02_amd as kq
+    s = w.sublayers[0]
+    m, n, N = s.m, s.n, w.N
+    lib = kq.load()
+    stream = torch.cuda.current_stream()
+    Xd = path.Xd
+    Xfd = w.gen_xfp_dev(s.x)
+    C = torch.empty((n, n), dtype=torch.float32, device=dev)
+    P = torch.empty((n, n), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(lib.kronq_drift_cross_ws(N, n), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(lib.kronq_gptaq_correction_ws(n), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(lib.kronq_gptaq_ws(m, n), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, lib.kronq_biip_ws(n, n)), dtype=torch.uint8, device=dev)
+    Wk = path.Wk_last
+    names = ("drift_cross", "rotate_c", "correction_p", "gptaq_loop")
+
+    def one(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        kq.kronq_drift_cross(Xfd, Xd, C, ws=ws_d)
+        mark(1)
+        kq.kronq_biip_rotate(C, None, None, path.si, s.in_block, path.si, s.in_block, 0.0, ws=ws_b)
+        mark(2)
+        kq.kronq_gptaq_correction(C, path.R, path.perm, 0.25, P, ws=ws_p)
+        mark(3)
+        kq.kronq_gptaq_quantize(Wk, path.R, path.perm, s.bits, s.group, P, What=path.What, ws=ws_q,
+                                codes=path.codes, scales=path.scales, zeros=path.zeros)
+        mark(4)
+
+    one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for k in range(steps):
+        one(evs[k])
+    torch.cuda.synchronize()
+    st = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+          for i, nm in enumerate(names)}
+    cross_flops = 4.0 * N * n * n            # hi^T X and lo^T X, all n^2 entries
+    p_flops = 2.0 * n ** 3 / 2 + 2.0 * n ** 3 / 6   # triangular K = C_p R^T, P = triu1(K) R
+    return {"workload": w.name + " with a drifted input stream (drift %.2f)" % w.drift,
+            "alpha": 0.25, "stage_ms": st,
+            "drift_cross_tflops": cross_flops / (st["drift_cross"] * 1e-3) / 1e12,
+            "correction_tflops_fp32": p_flops / (st["correction_p"] * 1e-3) / 1e12,
+            "loop_ms": st["gptaq_loop"]}
+
+
 def sublayer_record(w, s, st):
     m, n, N = s.m, s.n, w.N
     return {
@@ -715,6 +768,7 @@ def main():
         r2.update({"workload": w2.name, "ms_per_step": wall2, "gram_frac_bf16_peak": gt / PEAK_BF16_TFLOPS,
                    "fwht_frac_hbm_peak": r2["fwht_gbs"] / PEAK_HBM_GBS})
         out["secondary"] = r2
+        out["gptaq"] = gptaq_leg(w2, p2[0], dev)
         # CV_in / CV_out of W before and after BiIP, and the diagnostic's own rate
         # (one read of W: 4 m n algorithmic bytes per call)
         m, n = s2.m, s2.n

@@ -46,6 +46,8 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int NB = 128;
 constexpr int KS = 32;        // K rows per LDS stage
+constexpr int NBO = 4;        // panels of an outer block (two-level sweep)
+constexpr int kTwoLevelMinPanels = 48;   // two-level from n > 6016 on
 
 struct CholWs {
   float* A;       // npad x npad (reversed, permuted, damped)
@@ -57,7 +59,7 @@ struct CholWs {
   int* flag;      // nonzero after a failed pivot or a non-finite input
   int* nonfinite; // nonzero when H (or the damping term) holds a NaN or infinity
   long long* info;
-  int64_t sP;     // floats between the two Lp (and the two Yp) buffers
+  int64_t sP;     // floats between consecutive Lp (and Yp) buffers (NBO of each)
 };
 
 // buffer of parity `par` of a double-buffered array
@@ -76,9 +78,9 @@ size_t ws_layout(int64_t n, CholWs* w, void* base) {
   if (w) w->B = reinterpret_cast<float*>(b + off);
   off += sA;
   if (w) w->Lp = reinterpret_cast<float*>(b + off);
-  off += 2 * sP;
+  off += NBO * sP;
   if (w) w->Yp = reinterpret_cast<float*>(b + off);
-  off += 2 * sP;
+  off += NBO * sP;
   if (w) w->Linv = reinterpret_cast<float*>(b + off);
   off += 2 * align_up((size_t)NB * NB * sizeof(float), 256);
   if (w) w->sP = (int64_t)(sP / sizeof(float));
@@ -679,39 +681,46 @@ __global__ void __launch_bounds__(256) chol_panel(int64_t npad, int P, int p, Ch
     const float* Aip = w.A + (int64_t)i * NB * npad + (int64_t)p * NB;
     // B(j, k) = Linv[32 quarter + j][k]
     mm.run<XK, XK>(Aip, npad, Linv + (int64_t)32 * quarter * NB, NB, sm);
-    mm.store<0>(lp_buf(w, p & 1) + (int64_t)i * NB * NB + 32 * quarter, NB);
+    mm.store<0>(lp_buf(w, p % NBO) + (int64_t)i * NB * NB + 32 * quarter, NB);
   } else {
     const int c = t;
     // A(i, k) = Linv[i][k]; B(j, k) = B[p NB + k][c NB + 32 quarter + j]
     const float* Bpc = w.B + (int64_t)p * NB * npad + (int64_t)c * NB + 32 * quarter;
     mm.run<XK, KX>(Linv, NB, Bpc, npad, sm);
-    mm.store<0>(yp_buf(w, p & 1) + (int64_t)c * NB + 32 * quarter, npad);
+    mm.store<0>(yp_buf(w, p % NBO) + (int64_t)c * NB + 32 * quarter, npad);
   }
 }
 
-// Number of U2 tiles of step p (see u2_tile).
-__host__ __device__ inline int u2_tiles(int P, int p) {
-  const int q = P - p - 1, q2 = q - 1;
-  return (q2 > 0 ? q2 * (q2 + 1) / 2 : 0) + q * (p + 1) + (p + 1);
+// U2 of step p with the step's panel p's outer block ending at panel `bend`
+// (the last panel, P - 1, when the sweep is one-level): the SYRK tiles
+// A_ij -= Lp_i Lp_j^T for p + 2 <= j <= bend, i >= j, then the forward-
+// substitution tiles B_ic -= Lp_i Yp_c for p < i <= bend, c <= p, then the copy
+// of Y_p into row block p of B.  The columns and rows past `bend` get panel p's
+// share from the outer update of its block.
+__host__ __device__ inline int u2_syrk_tiles(int P, int p, int bend) {
+  int cnt = 0;
+  for (int j = p + 2; j <= bend; ++j) cnt += P - j;
+  return cnt;
 }
 
-// U2 of step p, tile t: the SYRK tiles A_ij -= Lp_i Lp_j^T (i >= j > p + 1),
-// then the forward-substitution tiles B_ic -= Lp_i Yp_c (i > p, c <= p), then
-// the copy of Y_p into row block p of B.  `sm` holds kTileLdsFull bytes.
-__device__ __forceinline__ void u2_tile(int64_t npad, int P, int p, int t, const CholWs& w, float* sm) {
-  const float* Lp = lp_buf(w, p & 1);
-  const float* Yp = yp_buf(w, p & 1);
-  const int q = P - p - 1;
-  const int q2 = q - 1;   // trailing columns after p + 1
-  const int nsyrk = q2 > 0 ? q2 * (q2 + 1) / 2 : 0;
-  const int nfwd = q * (p + 1);
+__host__ __device__ inline int u2_tiles(int P, int p, int bend) {
+  return u2_syrk_tiles(P, p, bend) + (bend - p) * (p + 1) + (p + 1);
+}
+
+// `sm` holds kTileLdsFull bytes.
+__device__ __forceinline__ void u2_tile(int64_t npad, int P, int p, int bend, int t, const CholWs& w,
+                                        float* sm) {
+  const float* Lp = lp_buf(w, p % NBO);
+  const float* Yp = yp_buf(w, p % NBO);
+  const int nsyrk = u2_syrk_tiles(P, p, bend);
+  const int nfwd = (bend - p) * (p + 1);
   if (t < nsyrk + nfwd) {
     TileMma<2, 2, 2, 2> mm;
     mm.zero();
     if (t < nsyrk) {
-      int a = 0;
-      while (t >= a + 1) { t -= a + 1; ++a; }
-      const int i = p + 2 + a, j = p + 2 + t;   // j <= i
+      int j = p + 2;
+      while (t >= P - j) { t -= P - j; ++j; }
+      const int i = j + t;   // j <= i
       mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB, NB, sm);
       mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB, npad);
     } else {
@@ -736,13 +745,14 @@ __device__ __forceinline__ void u2_tile(int64_t npad, int P, int p, int t, const
 // block p (if p < P); the others run U2 of step p - 1, which writes only
 // columns past p and row blocks past p - 1 of B, so it overlaps the diagonal
 // block.  The U2 tiles reuse the diagonal step's LDS for their stages.
-__global__ void __launch_bounds__(256) chol_step(int64_t npad, int64_t n, int P, int p, CholWs w) {
+__global__ void __launch_bounds__(256) chol_step(int64_t npad, int64_t n, int P, int p, int bend_prev,
+                                                 CholWs w) {
   if (*w.flag) return;
   __shared__ __align__(16) double lds[kLsD + kBsD + 4 * SB];
   __shared__ int s_bad;
   static_assert(sizeof(lds) >= kTileLdsFull, "a U2 tile fits the diagonal step's LDS");
   if (blockIdx.x > 0) {
-    u2_tile(npad, P, p - 1, (int)blockIdx.x - 1, w, reinterpret_cast<float*>(lds));
+    u2_tile(npad, P, p - 1, bend_prev, (int)blockIdx.x - 1, w, reinterpret_cast<float*>(lds));
     return;
   }
   if (p < P) diag_step(npad, n, p, w, lds, lds + kLsD, lds + kLsD + kBsD, s_bad);
@@ -754,7 +764,7 @@ __global__ void __launch_bounds__(256) chol_step(int64_t npad, int64_t n, int P,
 __global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
   if (*w.flag) return;
   extern __shared__ __align__(16) float sm[];
-  const float* Lp = lp_buf(w, p & 1);
+  const float* Lp = lp_buf(w, p % NBO);
   const int t = blockIdx.x;
   TileMma<4, 1, 1, 1> mm;
   mm.zero();
@@ -762,6 +772,131 @@ __global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
   const int i = p + 1 + (t >> 2), j = p + 1;
   mm.run<XK, XK>(Lp + (int64_t)i * NB * NB, NB, Lp + (int64_t)j * NB * NB + 32 * quarter * NB, NB, sm);
   mm.store<1>(w.A + (int64_t)i * NB * npad + (int64_t)j * NB + 32 * quarter, npad);
+}
+
+// Outer update of the outer block of panels b0 .. b0 + NBO - 1 (two-level
+// sweep), once its last panel's L and Y are out: every column and row block
+// past the block gets the block's share at once, with K = NBO * NB:
+//   SYRK  A_ij -= sum_q L_i,b0+q L_j,b0+q^T            (j >= b1 = b0 + NBO, i >= j)
+//   fwd   B_ic -= sum_{q: b0+q >= c} L_i,b0+q Y_b0+q,c  (i >= b1, c < b1)
+// One 128 x 128 output tile per workgroup (four waves as 2 x 2, each 64 x 64
+// as 2 x 2 accumulators of v_mfma_f32_32x32x2f32), K staged 16 at a time
+// through LDS with the next stage's global loads in registers.  A right-
+// looking sweep reads and writes the whole trailing matrix once per panel;
+// with rank-512 updates it does so once per outer block, and each tile's
+// read-modify-write is amortized over four times the products.
+constexpr int OK16 = 16;            // K per stage
+constexpr int OLD = NB + 4;         // padded LDS row (floats)
+
+__global__ void __launch_bounds__(256) chol_outer(int64_t npad, int P, int b0, CholWs w) {
+  if (*w.flag) return;
+  __shared__ float As[OK16][OLD];
+  __shared__ float Bs[OK16][OLD];
+  const int b1 = b0 + NBO;
+  int t = blockIdx.x;
+  const int q2 = P - b1;
+  const int nsyrk = q2 * (q2 + 1) / 2;
+  bool fwd = t >= nsyrk;
+  int i, j, qlo = 0;
+  if (!fwd) {
+    j = b1;
+    while (t >= P - j) { t -= P - j; ++j; }
+    i = j + t;
+  } else {
+    t -= nsyrk;
+    i = b1 + t / b1;
+    j = t % b1;                       // the column block c of B
+    qlo = j > b0 ? j - b0 : 0;        // panels b0 + q >= c
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+  const int k_lo = qlo * NB, k_hi = NBO * NB;
+  float ra[8], rb[8];
+  // stage at k0: A element (r, k) = L_i,b0+q[r][kk]; B element (col, k) =
+  // L_j,b0+q[col][kk] (SYRK) or (k, col) = Y_b0+q[kk][c NB + col] (fwd), with
+  // q = k / NB, kk = k % NB; panel q sits in slot q of the buffers (b0 is a
+  // multiple of NBO)
+  auto load = [&](int k0) {
+    const int q = k0 / NB, kk0 = k0 % NB;
+    const float* La = lp_buf(w, q) + (int64_t)i * NB * NB;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 4, k = e & 15;
+      ra[u] = La[(int64_t)r * NB + kk0 + k];
+      if (!fwd) {
+        rb[u] = lp_buf(w, q)[((int64_t)j * NB + r) * NB + kk0 + k];
+      } else {
+        const int kr = e >> 7, col = e & 127;
+        rb[u] = yp_buf(w, q)[(int64_t)(kk0 + kr) * npad + (int64_t)j * NB + col];
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      As[e & 15][e >> 4] = ra[u];
+      if (!fwd) Bs[e & 15][e >> 4] = rb[u];
+      else Bs[e >> 7][e & 127] = rb[u];
+    }
+  };
+  load(k_lo);
+  store();
+  __syncthreads();
+  for (int k0 = k_lo; k0 < k_hi; k0 += OK16) {
+    const bool more = k0 + OK16 < k_hi;
+    if (more) load(k0 + OK16);
+#pragma unroll
+    for (int kk = 0; kk < OK16; kk += 2) {
+      float af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) af[a] = As[kk + lk][wm * 64 + 32 * a + lr];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bf[b] = Bs[kk + lk][wn * 64 + 32 * b + lr];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) {
+      store();
+      __syncthreads();
+    }
+  }
+  // C -= acc, every old value loaded before the first store
+  float* C = (fwd ? w.B : w.A) + (int64_t)i * NB * npad + (int64_t)j * NB;
+  float old[2][2][16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + 32 * a + 8 * (v >> 2) + 4 * lk + (v & 3);
+        const int c = wn * 64 + 32 * b + lr;
+        old[a][b][v] = C[(int64_t)r * npad + c];
+      }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + 32 * a + 8 * (v >> 2) + 4 * lk + (v & 3);
+        const int c = wn * 64 + 32 * b + lr;
+        C[(int64_t)r * npad + c] = old[a][b][v] - acc[a][b][v];
+      }
 }
 
 // R[a][b] = Y[n-1-a][n-1-b] for b >= a, 0 below the diagonal.
@@ -824,19 +959,33 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
     KQ_LAUNCHED("chol_gather");
   }
   // one stream: step p (diagonal block p with U2 of step p - 1), the panels
-  // of step p, U1 of step p; a last step launch runs U2 of step P - 1
+  // of step p, then U1 of step p or, after the last panel of an outer block,
+  // the block's outer update; a last step launch runs U2 of step P - 1.  The
+  // sweep is two-level (outer blocks of NBO panels) from two_level_min_panels
+  // panels on; below that every U2 covers the whole trailing matrix and the
+  // look-ahead keeps it beside the next diagonal block.
+  const bool two = P >= kTwoLevelMinPanels;
+  auto bend_of = [&](int q) { return two ? std::min(P - 1, (q / NBO) * NBO + NBO - 1) : P - 1; };
   const size_t lds_tile = kTileLdsQuarter;
   for (int p = 0; p <= P; ++p) {
-    const int nu2 = p > 0 ? u2_tiles(P, p - 1) : 0;
-    hipLaunchKernelGGL(chol_step, dim3((unsigned)(1 + nu2)), dim3(256), 0, s, npad, n, P, p, w);
+    const int bend_prev = p > 0 ? bend_of(p - 1) : 0;
+    const int nu2 = p > 0 ? u2_tiles(P, p - 1, bend_prev) : 0;
+    hipLaunchKernelGGL(chol_step, dim3((unsigned)(1 + nu2)), dim3(256), 0, s, npad, n, P, p, bend_prev, w);
     KQ_LAUNCHED("chol_step");
     if (p == P) break;
     const int q = P - p - 1;
     hipLaunchKernelGGL(chol_panel, dim3((unsigned)(4 * q + 4 * (p + 1))), dim3(256), lds_tile, s, npad, P, p, w);
     KQ_LAUNCHED("chol_panel");
-    if (q > 0) {
+    const int bend = bend_of(p);
+    if (p < bend) {
       hipLaunchKernelGGL(chol_u1, dim3((unsigned)(4 * q)), dim3(256), lds_tile, s, npad, p, w);
       KQ_LAUNCHED("chol_u1");
+    } else if (p < P - 1) {
+      // p ends its outer block b0 .. p (two-level only)
+      const int b0 = p - NBO + 1, b1 = p + 1, q2 = P - b1;
+      const int tiles = q2 * (q2 + 1) / 2 + q2 * b1;
+      hipLaunchKernelGGL(chol_outer, dim3((unsigned)tiles), dim3(256), 0, s, npad, P, b0, w);
+      KQ_LAUNCHED("chol_outer");
     }
   }
   {

@@ -95,6 +95,29 @@ def test_chol_full_size_llama2_7b_q_proj():
     assert fe <= 1e-3
 
 
+@pytest.mark.parametrize("n,act", [(6200, False), (8192, True)])
+def test_chol_two_level_sweep(n, act):
+    """From 48 panels of 128 on, the sweep is two-level: outer blocks of four
+    panels whose rank-512 update covers the trailing matrix at once.  6200 ends
+    in a partial outer block of one panel (no outer update after it); 8192 with
+    act-order runs sixteen full blocks."""
+    say("chol two-level", n, act)
+    H = spd_from_gram(69 + n, n, N=2 * n).astype(np.float32)
+    R, perm, info = kq.kronq_chol_inv(to_dev_f32(H), 0.01, act)
+    R, perm = host(R), host(perm)
+    assert info == -1
+    operm, Hd = O.prepare_hessian(H.astype(np.float64), 0.01, act)
+    np.testing.assert_array_equal(perm, operm)
+    assert np.all(np.tril(R, -1) == 0) and np.all(np.diag(R) > 0)
+    be = _backward_error(R, Hd)
+    V = np.random.default_rng(2).standard_normal((n, 4))
+    Rd = R.astype(np.float64)
+    resid = np.linalg.norm(Hd @ (Rd.T @ (Rd @ V)) - V) / np.linalg.norm(V)
+    say("  backward %.2e probe residual %.2e" % (be, resid))
+    assert be <= 1e-5
+    assert resid <= 1e-4
+
+
 def test_chol_layouts_give_the_same_factor():
     """The final flip into R has a float4 path (n and ldr multiples of 4, R
     16-byte aligned) and an element path.  The same H through both gives the
