@@ -47,7 +47,7 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 constexpr int NB = 128;
 constexpr int KS = 32;        // K rows per LDS stage
 constexpr int NBO = 4;        // panels of an outer block (two-level sweep)
-constexpr int kTwoLevelMinPanels = 48;   // two-level from n > 6016 on
+constexpr int kTwoLevelMinPanels = 72;   // two-level from n > 9088 on (measured crossover)
 
 struct CholWs {
   float* A;       // npad x npad (reversed, permuted, damped)
@@ -785,18 +785,18 @@ __global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
 // looking sweep reads and writes the whole trailing matrix once per panel;
 // with rank-512 updates it does so once per outer block, and each tile's
 // read-modify-write is amortized over four times the products.
-constexpr int OK16 = 16;            // K per stage
+constexpr int OKS = 32;             // K per stage
 constexpr int OLD = NB + 4;         // padded LDS row (floats)
 
-__global__ void __launch_bounds__(256) chol_outer(int64_t npad, int P, int b0, CholWs w) {
+__global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0, CholWs w) {
   if (*w.flag) return;
-  __shared__ float As[OK16][OLD];
-  __shared__ float Bs[OK16][OLD];
+  __shared__ __align__(16) float As[OKS][OLD];
+  __shared__ __align__(16) float Bs[OKS][OLD];
   const int b1 = b0 + NBO;
   int t = blockIdx.x;
   const int q2 = P - b1;
   const int nsyrk = q2 * (q2 + 1) / 2;
-  bool fwd = t >= nsyrk;
+  const bool fwd = t >= nsyrk;
   int i, j, qlo = 0;
   if (!fwd) {
     j = b1;
@@ -819,44 +819,54 @@ __global__ void __launch_bounds__(256) chol_outer(int64_t npad, int P, int b0, C
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
   const int k_lo = qlo * NB, k_hi = NBO * NB;
-  float ra[8], rb[8];
-  // stage at k0: A element (r, k) = L_i,b0+q[r][kk]; B element (col, k) =
-  // L_j,b0+q[col][kk] (SYRK) or (k, col) = Y_b0+q[kk][c NB + col] (fwd), with
-  // q = k / NB, kk = k % NB; panel q sits in slot q of the buffers (b0 is a
-  // multiple of NBO)
+  float4 ra[4], rb[4];
+  // stage at k0 (32 values of k): A element (r, k) = L_i,b0+q[r][kk]; B
+  // element (col, k) = L_j,b0+q[col][kk] (SYRK) or (k, col) =
+  // Y_b0+q[kk][c NB + col] (fwd), with q = k / NB, kk = k % NB; panel q sits
+  // in slot q of the buffers (b0 is a multiple of NBO).  Float4 u of a thread
+  // is row (tid + 256 u) / 8, k quad (tid + 256 u) % 8 (A, SYRK B), or k row
+  // (tid + 256 u) / 32, column quad (tid + 256 u) % 32 (fwd B).
   auto load = [&](int k0) {
     const int q = k0 / NB, kk0 = k0 % NB;
-    const float* La = lp_buf(w, q) + (int64_t)i * NB * NB;
+    const float* La = lp_buf(w, q) + (int64_t)i * NB * NB + kk0;
+    const float* Lb = lp_buf(w, q) + (int64_t)j * NB * NB + kk0;
+    const float* Yb = yp_buf(w, q) + (int64_t)kk0 * npad + (int64_t)j * NB;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int e = tid + 256 * u;
-      const int r = e >> 4, k = e & 15;
-      ra[u] = La[(int64_t)r * NB + kk0 + k];
-      if (!fwd) {
-        rb[u] = lp_buf(w, q)[((int64_t)j * NB + r) * NB + kk0 + k];
-      } else {
-        const int kr = e >> 7, col = e & 127;
-        rb[u] = yp_buf(w, q)[(int64_t)(kk0 + kr) * npad + (int64_t)j * NB + col];
-      }
+      const int r = e >> 3, k4 = (e & 7) * 4;
+      ra[u] = *reinterpret_cast<const float4*>(La + (int64_t)r * NB + k4);
+      if (!fwd) rb[u] = *reinterpret_cast<const float4*>(Lb + (int64_t)r * NB + k4);
+      else rb[u] = *reinterpret_cast<const float4*>(Yb + (int64_t)(e >> 5) * npad + (e & 31) * 4);
     }
   };
   auto store = [&]() {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int e = tid + 256 * u;
-      As[e & 15][e >> 4] = ra[u];
-      if (!fwd) Bs[e & 15][e >> 4] = rb[u];
-      else Bs[e >> 7][e & 127] = rb[u];
+      const int r = e >> 3, k4 = (e & 7) * 4;
+      As[k4][r] = ra[u].x;
+      As[k4 + 1][r] = ra[u].y;
+      As[k4 + 2][r] = ra[u].z;
+      As[k4 + 3][r] = ra[u].w;
+      if (!fwd) {
+        Bs[k4][r] = rb[u].x;
+        Bs[k4 + 1][r] = rb[u].y;
+        Bs[k4 + 2][r] = rb[u].z;
+        Bs[k4 + 3][r] = rb[u].w;
+      } else {
+        *reinterpret_cast<float4*>(&Bs[e >> 5][(e & 31) * 4]) = rb[u];
+      }
     }
   };
   load(k_lo);
   store();
   __syncthreads();
-  for (int k0 = k_lo; k0 < k_hi; k0 += OK16) {
-    const bool more = k0 + OK16 < k_hi;
-    if (more) load(k0 + OK16);
+  for (int k0 = k_lo; k0 < k_hi; k0 += OKS) {
+    const bool more = k0 + OKS < k_hi;
+    if (more) load(k0 + OKS);
 #pragma unroll
-    for (int kk = 0; kk < OK16; kk += 2) {
+    for (int kk = 0; kk < OKS; kk += 2) {
       float af[2], bf[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a) af[a] = As[kk + lk][wm * 64 + 32 * a + lr];
@@ -874,29 +884,24 @@ __global__ void __launch_bounds__(256) chol_outer(int64_t npad, int P, int b0, C
       __syncthreads();
     }
   }
-  // C -= acc, every old value loaded before the first store
+  // C -= acc, every old value of an accumulator tile loaded before its stores
   float* C = (fwd ? w.B : w.A) + (int64_t)i * NB * npad + (int64_t)j * NB;
-  float old[2][2][16];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+      float old[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 64 + 32 * a + 8 * (v >> 2) + 4 * lk + (v & 3);
-        const int c = wn * 64 + 32 * b + lr;
-        old[a][b][v] = C[(int64_t)r * npad + c];
+        old[v] = C[(int64_t)r * npad + wn * 64 + 32 * b + lr];
       }
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 64 + 32 * a + 8 * (v >> 2) + 4 * lk + (v & 3);
-        const int c = wn * 64 + 32 * b + lr;
-        C[(int64_t)r * npad + c] = old[a][b][v] - acc[a][b][v];
+        C[(int64_t)r * npad + wn * 64 + 32 * b + lr] = old[v] - acc[a][b][v];
       }
+    }
 }
 
 // R[a][b] = Y[n-1-a][n-1-b] for b >= a, 0 below the diagonal.
@@ -961,7 +966,7 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
   // one stream: step p (diagonal block p with U2 of step p - 1), the panels
   // of step p, then U1 of step p or, after the last panel of an outer block,
   // the block's outer update; a last step launch runs U2 of step P - 1.  The
-  // sweep is two-level (outer blocks of NBO panels) from two_level_min_panels
+  // sweep is two-level (outer blocks of NBO panels) from kTwoLevelMinPanels
   // panels on; below that every U2 covers the whole trailing matrix and the
   // look-ahead keeps it beside the next diagonal block.
   const bool two = P >= kTwoLevelMinPanels;
