@@ -80,7 +80,7 @@ def parse():
 
 
 GRAM_SRC = os.path.join(ROOT, "post_quantization_02_amd", "csrc", "gram.hip")
-GRAM_MAIN = "gram_bf16_lds_kernel"
+GRAM_MAIN = "gram_bf16_lds"          # gram_bf16_lds_kernel and its persistent one-split variant
 
 
 def gram_source_hash():
@@ -101,19 +101,20 @@ def copy_probe(nbytes):
 
 
 def _pmc_groups(path, kernel_pred, counter):
-    """{grid size: [per-dispatch counter sums]} for the matching kernels."""
+    """{(kernel, grid size): [per-dispatch counter sums]} for the matching kernels."""
     import csv
     per_dispatch = {}
-    grid = {}
+    key_of = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter and kernel_pred(r["Kernel_Name"]):
                 key = r["Dispatch_Id"]
                 per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
-                grid[key] = int(r.get("Grid_Size", 0) or 0)
+                name = r["Kernel_Name"].replace("(anonymous namespace)", "anon").split("(")[0].split("::")[-1]
+                key_of[key] = (name, int(r.get("Grid_Size", 0) or 0))
     out = {}
     for k, v in per_dispatch.items():
-        out.setdefault(grid[k], []).append(v)
+        out.setdefault(key_of[k], []).append(v)
     return out
 
 
@@ -138,16 +139,17 @@ def summarize_traffic(args):
     pred = lambda name: GRAM_MAIN in name
     fg = _pmc_groups(f_csv, pred, "FETCH_SIZE")
     wg = _pmc_groups(w_csv, pred, "WRITE_SIZE")
-    for grid in sorted(set(fg) & set(wg)):
-        fk = sum(fg[grid]) / len(fg[grid])
-        wk = sum(wg[grid]) / len(wg[grid])
-        out["counters"]["%s grid %d" % (GRAM_MAIN, grid)] = {
-            "fetch_kib": fk, "write_kib": wk, "dispatches": len(fg[grid]),
+    for key in sorted(set(fg) & set(wg)):
+        fk = sum(fg[key]) / len(fg[key])
+        wk = sum(wg[key]) / len(wg[key])
+        out["counters"]["%s grid %d" % key] = {
+            "fetch_kib": fk, "write_kib": wk, "dispatches": len(fg[key]),
             "hbm_bytes_per_dispatch": (fk * f_scale + wk * w_scale) * 1024.0}
-    big = max(set(fg) & set(wg))          # d = 28672: the largest grid of the step
-    out["roofline_grid"] = big
-    out["bytes_per_launch"] = out["counters"]["%s grid %d" % (GRAM_MAIN, big)]["hbm_bytes_per_dispatch"]
-    out["unit"] = "bytes per launch of %s at d = 28672 (scaled counters)" % GRAM_MAIN
+    # d = 28672: the launches that read the 14 GiB inputs fetch the most
+    big = max(set(fg) & set(wg), key=lambda k: sum(fg[k]) / len(fg[k]))
+    out["roofline_launch"] = "%s grid %d" % big
+    out["bytes_per_launch"] = out["counters"]["%s grid %d" % big]["hbm_bytes_per_dispatch"]
+    out["unit"] = "bytes per launch of the Gram at d = 28672 (scaled counters)"
     out["gram_source_sha256"] = gram_source_hash()
     run = "python3 -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-secondary"
     probe = "python3 -u bench.py --copy-probe %d" % args.copy_bytes
@@ -740,7 +742,7 @@ def main():
         "gram_frac_bf16_peak": gram_tflops / PEAK_BF16_TFLOPS,
         "fwht_gbs": fwht_bytes / (fwht_ms * 1e-3) / 1e9,
         "fwht_frac_hbm_peak": fwht_bytes / (fwht_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "roofline": {"kernel": "%s, kronq_gram at d = 28672 (one launch, no split-K)" % GRAM_MAIN,
+        "roofline": {"kernel": "gram_bf16_lds_sync_kernel, kronq_gram at d = 28672 (one launch, no split-K)",
                      "bound": "mfma", "achieved": gram_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": gram_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
