@@ -653,3 +653,66 @@ def weight_cv(W):
     col = np.sqrt(np.sum(W * W, axis=0))
     row = np.sqrt(np.sum(W * W, axis=1))
     return float(np.std(col) / np.mean(col)), float(np.std(row) / np.mean(row))
+
+
+# --------------------------------------------------------------------------
+# Input-side rescale S_X.  [summary] Method: BiIP extends the input-side
+# diagonal rescaling to both directions (the output-side S_G being the new
+# part) before the orthogonal transforms; [review] Algorithm 1 returns S_X
+# beside S_G, U and V; [review] proof of Theorem 1: the proxy loss
+# tr(H_G dW H_X dW^T) is unchanged by the transforms.
+# Reading: S_X has the form of S_G on the other side, s_x = diag(H_X)^alpha_x
+# (a non-positive diagonal entry gives 1), taken from H_X before any
+# transform; W is scaled column-wise by s_x and H_X by s_x^-1 on both sides,
+# which leaves the proxy loss of a correspondingly transformed dW unchanged:
+#   W'   = U S_G W S_X V^T
+#   H_X' = V S_X^-1 H_X S_X^-1 V^T
+#   H_G' = U S_G^-1 H_G S_G^-1 U^T
+# --------------------------------------------------------------------------
+
+def input_rescale(HX: np.ndarray, alpha_x: float) -> np.ndarray:
+    """s_x = diag(H_X)^alpha_x; a non-positive diagonal entry gives 1."""
+    d = np.diag(np.asarray(HX, dtype=np.float64)).copy()
+    s = np.ones_like(d)
+    pos = d > 0
+    s[pos] = d[pos] ** alpha_x
+    return s
+
+
+def biip_sx(W, HX, HG, in_signs, in_block, out_signs, out_block, alpha, alpha_x, sx=None):
+    """Returns (W', H_X', H_G', s_g, s_x) as above.  s_x is input_rescale(HX,
+    alpha_x) unless given (then HX may be None, or any n x n matrix that is to
+    be transformed the way H_X is, such as the drift cross product)."""
+    W = np.asarray(W, dtype=np.float64)
+    if sx is None:
+        sx = input_rescale(HX, alpha_x)
+    sx = np.asarray(sx, dtype=np.float64)
+    Wp, _, HGp, sg = biip(W * sx[None, :], None, HG, in_signs, in_block, out_signs, out_block, alpha)
+    HXp = None
+    if HX is not None:
+        HXs = np.asarray(HX, dtype=np.float64) / sx[:, None] / sx[None, :]
+        HXp = rotate_cols(rotate_rows(HXs, in_block, in_signs), in_block, in_signs)
+    return Wp, HXp, HGp, sg, sx
+
+
+def unrotate_sx(Wp, in_signs, in_block, out_signs, out_block, sg, sx) -> np.ndarray:
+    """S_G^-1 U^T W' V S_X^-1: the inverse of the weight side of biip_sx()."""
+    return unrotate(Wp, in_signs, in_block, out_signs, out_block, sg) / np.asarray(sx, dtype=np.float64)[None, :]
+
+
+# --------------------------------------------------------------------------
+# mu-incoherence.  [summary] Method and [review] Figure 2(a): the incoherence
+# of a proxy Hessian is reported as mu(H)/sqrt(d); it is near 1 when an
+# eigenvector lies along a coordinate axis and small once the transforms have
+# spread every eigenvector over all coordinates.
+# Reading: the textbook definition of a mu-incoherent symmetric matrix
+# H = Q Lambda Q^T (Q orthogonal) is max_ij |Q_ij| <= mu / sqrt(d), so
+# mu(H)/sqrt(d) = max_ij |Q_ij| over the eigenvector matrix.  Where eigenvalues
+# repeat, Q (and so the value) is not unique; the checks then compare the
+# eigen-decomposition's validity instead.
+# --------------------------------------------------------------------------
+
+def mu_incoherence(H: np.ndarray) -> float:
+    """max_ij |Q_ij| for the eigenvectors Q of the symmetric H (numpy eigh)."""
+    _, Q = np.linalg.eigh(np.asarray(H, dtype=np.float64))
+    return float(np.max(np.abs(Q)))

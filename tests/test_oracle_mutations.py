@@ -84,6 +84,18 @@ MUTANTS = [
      "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) - np.outer(W0[:, j], P[j, j + 1:])",
      "Wt[:, j + 1:] -= np.outer(e, R[j, j + 1:]) - np.outer(Wt[:, j], P[j, j + 1:])"),
     ("drift cross product transposed", "    return (dX.T @ X) / X.shape[0]", "    return (X.T @ dX) / X.shape[0]"),
+    ("S_X on H_X multiplies", "HXs = np.asarray(HX, dtype=np.float64) / sx[:, None] / sx[None, :]",
+     "HXs = np.asarray(HX, dtype=np.float64) * sx[:, None] * sx[None, :]"),
+    ("S_X on W divides", "biip(W * sx[None, :], None", "biip(W / sx[None, :], None"),
+    ("S_X exponent sign", "s[pos] = d[pos] ** alpha_x", "s[pos] = d[pos] ** (-alpha_x)"),
+    ("S_X from the rotated H_X", "        sx = input_rescale(HX, alpha_x)",
+     "        sx = input_rescale(rotate_cols(rotate_rows(HX, in_block, in_signs), in_block, in_signs), alpha_x)"),
+    ("unrotate S_X direction", "/ np.asarray(sx, dtype=np.float64)[None, :]",
+     "* np.asarray(sx, dtype=np.float64)[None, :]"),
+    ("mu without the 1/sqrt(d)", "    return float(np.max(np.abs(Q)))",
+     "    return float(np.max(np.abs(Q)) * math.sqrt(Q.shape[0]))"),
+    ("mu of the least coherent eigenvector", "    return float(np.max(np.abs(Q)))",
+     "    return float(np.min(np.max(np.abs(Q), axis=0)))"),
     ("type ties to the higher id", "ranked = sorted(range(n_types), key=lambda t: (-total[t], t))",
      "ranked = sorted(range(n_types), key=lambda t: (-total[t], -t))"),
 ]

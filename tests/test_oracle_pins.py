@@ -885,3 +885,143 @@ def test_drift_term_rotation_invariance():
     lhs = np.trace(HGp @ dWp @ Cp.T @ Wp.T)
     rhs = np.trace(HG @ dW @ C.T @ W.T)
     assert lhs == pytest.approx(rhs, rel=1e-10)
+
+
+# ------------------------------------------------ input-side rescale S_X
+
+
+def _sx_case(seed, m=8, n=16, ki=8, ko=4):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((m, n))
+    d = np.exp(rng.standard_normal(n))          # input channels of very different scales
+    HX = rand_spd(rng, n, 20.0) * d[:, None] * d[None, :]
+    HG = rand_spd(rng, m, 1e3)
+    si, so = rng.choice([-1.0, 1.0], n), rng.choice([-1.0, 1.0], m)
+    return W, HX, HG, si, ki, so, ko
+
+
+def test_input_rescale_hand_values():
+    HX = np.diag([4.0, 0.0, 9.0, -1.0])
+    np.testing.assert_allclose(O.input_rescale(HX, 0.5), [2.0, 1.0, 3.0, 1.0])
+    np.testing.assert_allclose(O.input_rescale(np.diag([16.0, 81.0]), 0.25), [2.0, 3.0])
+    np.testing.assert_array_equal(O.input_rescale(np.diag([16.0, 81.0]), 0.0), [1.0, 1.0])
+
+
+def test_biip_sx_explicit_matrices():
+    W, HX, HG, si, ki, so, ko = _sx_case(40)
+    Wp, HXp, HGp, sg, sx = O.biip_sx(W, HX, HG, si, ki, so, ko, 0.25, 0.25)
+    U = O.rotation_matrix(W.shape[0], ko, so)
+    V = O.rotation_matrix(W.shape[1], ki, si)
+    SG = np.diag(np.diag(HG) ** 0.25)
+    SX = np.diag(np.diag(HX) ** 0.25)
+    np.testing.assert_allclose(Wp, U @ SG @ W @ SX @ V.T, atol=1e-12)
+    np.testing.assert_allclose(HXp, V @ np.linalg.inv(SX) @ HX @ np.linalg.inv(SX) @ V.T, atol=1e-10)
+    np.testing.assert_allclose(HGp, U @ np.linalg.inv(SG) @ HG @ np.linalg.inv(SG) @ U.T, atol=1e-10)
+    np.testing.assert_allclose(sx, np.diag(SX), rtol=1e-15)
+
+
+@pytest.mark.parametrize("ax", [0.25, 0.5, -0.3])
+def test_biip_sx_objective_invariance(ax):
+    # Theorem 1's invariance of tr(H_G dW H_X dW^T), with both rescales
+    W, HX, HG, si, ki, so, ko = _sx_case(41)
+    dW = np.random.default_rng(42).standard_normal(W.shape)
+    _, HXp, HGp, sg, sx = O.biip_sx(W, HX, HG, si, ki, so, ko, 0.25, ax)
+    dWp, _, _, _, _ = O.biip_sx(dW, None, HG, si, ki, so, ko, 0.25, ax, sx=sx)
+    assert O.proxy_loss(dWp, HXp, HGp) == pytest.approx(O.proxy_loss(dW, HX, HG), rel=1e-11)
+
+
+def test_biip_sx_trace_closed_forms():
+    W, HX, HG, si, ki, so, ko = _sx_case(43)
+    for ax in (0.25, 0.5):
+        _, HXp, _, _, _ = O.biip_sx(W, HX, HG, si, ki, so, ko, 0.25, ax)
+        assert np.trace(HXp) == pytest.approx(np.sum(np.diag(HX) ** (1 - 2 * ax)), rel=1e-13)
+    # alpha_x = 1/2 and no rotation: H_X' is the correlation matrix (unit diagonal)
+    n = W.shape[1]
+    _, HXc, _, _, sx = O.biip_sx(W, HX, HG, np.ones(n), 1, so, ko, 0.25, 0.5)
+    np.testing.assert_allclose(np.diag(HXc), np.ones(n), rtol=1e-14)
+    np.testing.assert_allclose(HXc, HX / np.sqrt(np.outer(np.diag(HX), np.diag(HX))), rtol=1e-13)
+    # the rescale comes from H_X before its rotation: W's columns grow by diag(H_X)^1/2
+    Wc, _, _, _, _ = O.biip_sx(W, HX, None, np.ones(n), 1, np.ones(W.shape[0]), 1, 0.0, 0.5)
+    np.testing.assert_allclose(Wc, W * np.sqrt(np.diag(HX))[None, :], rtol=1e-14)
+
+
+def test_biip_sx_alpha_zero_is_biip():
+    W, HX, HG, si, ki, so, ko = _sx_case(44)
+    a = O.biip(W, HX, HG, si, ki, so, ko, 0.25)
+    b = O.biip_sx(W, HX, HG, si, ki, so, ko, 0.25, 0.0)
+    for x, y in zip(a, b[:4]):
+        np.testing.assert_allclose(x, y, rtol=0, atol=0)
+    np.testing.assert_array_equal(b[4], np.ones(W.shape[1]))
+
+
+@pytest.mark.parametrize("seed,ki,ko", [(45, 8, 4), (46, 1, 1), (47, 16, 8)])
+def test_unrotate_sx_inverts_biip_sx(seed, ki, ko):
+    W, HX, HG, si, _, so, _ = _sx_case(seed, ki=ki, ko=ko)
+    Wp, _, _, sg, sx = O.biip_sx(W, HX, HG, si, ki, so, ko, 0.25, 0.25)
+    np.testing.assert_allclose(O.unrotate_sx(Wp, si, ki, so, ko, sg, sx), W, atol=1e-12)
+    U = O.rotation_matrix(W.shape[0], ko, so)
+    V = O.rotation_matrix(W.shape[1], ki, si)
+    M = np.random.default_rng(seed).standard_normal(W.shape)
+    np.testing.assert_allclose(O.unrotate_sx(M, si, ki, so, ko, sg, sx),
+                               np.diag(1 / sg) @ U.T @ M @ V @ np.diag(1 / sx), atol=1e-12)
+
+
+def test_biip_sx_drift_matrix_keeps_the_drift_term():
+    # the drift cross product transforms as H_X does (C' = V S_X^-1 C S_X^-1 V^T),
+    # which keeps the asymmetric objective's drift term tr(H_G dW C^T W^T)
+    rng = np.random.default_rng(48)
+    W, HX, HG, si, ki, so, ko = _sx_case(48)
+    m, n = W.shape
+    X = rng.standard_normal((40, n))
+    C = O.drift_cross(X, X + 0.2 * rng.standard_normal((40, n)))
+    dW = 0.1 * rng.standard_normal((m, n))
+    Wp, _, HGp, sg, sx = O.biip_sx(W, HX, HG, si, ki, so, ko, 0.25, 0.25)
+    dWp = O.biip_sx(dW, None, HG, si, ki, so, ko, 0.25, 0.0, sx=sx)[0]
+    Cp = O.biip_sx(np.zeros((n, n)), C, None, si, ki, si, ki, 0.0, 0.0, sx=sx)[1]
+    lhs = np.trace(HGp @ dWp @ Cp.T @ Wp.T)
+    rhs = np.trace(HG @ dW @ C.T @ W.T)
+    assert lhs == pytest.approx(rhs, rel=1e-10)
+
+
+# ------------------------------------------------------ mu-incoherence
+
+
+def test_mu_closed_forms():
+    # eigenvectors along the axes: mu / sqrt(d) = 1
+    assert O.mu_incoherence(np.diag([3.0, 1.0, 2.0, 5.0])) == pytest.approx(1.0, abs=1e-15)
+    # a distinct spectrum rotated by a block Hadamard of order b: every
+    # eigenvector is a column of T^T, whose entries are +-1/sqrt(b)
+    rng = np.random.default_rng(50)
+    for d, b in ((16, 16), (32, 8), (64, 64)):
+        T = O.rotation_matrix(d, b, rng.choice([-1.0, 1.0], d))
+        H = T @ np.diag(np.linspace(1.0, 2.0, d)) @ T.T
+        assert O.mu_incoherence(H) == pytest.approx(1 / math.sqrt(b), rel=1e-12)
+    # 2 x 2: the eigenvectors make the angle theta = atan2(2c, a - b) / 2
+    for a, b, c in ((2.0, 1.0, 0.3), (1.0, 4.0, -2.0), (1.0, 1.0 + 1e-3, 5.0)):
+        th = 0.5 * math.atan2(2 * c, a - b)
+        want = max(abs(math.cos(th)), abs(math.sin(th)))
+        assert O.mu_incoherence(np.array([[a, c], [c, b]])) == pytest.approx(want, rel=1e-13)
+    # block diagonal: the value is the largest over all eigenvectors -- one
+    # coordinate left alone (1) beside a Hadamard-rotated block of 4 (1/2)
+    T = O.rotation_matrix(4, 4, np.array([1.0, -1.0, 1.0, 1.0]))
+    H = np.zeros((5, 5))
+    H[:4, :4] = T @ np.diag([1.0, 2.0, 3.0, 4.0]) @ T.T
+    H[4, 4] = 2.5
+    assert O.mu_incoherence(H) == pytest.approx(1.0, rel=1e-13)
+    assert O.mu_incoherence(H[:4, :4]) == pytest.approx(0.5, rel=1e-13)
+
+
+def test_mu_invariances():
+    rng = np.random.default_rng(51)
+    d = 24
+    H = rand_spd(rng, d, 100.0)
+    H[:, 3] *= 5.0
+    H[3, :] *= 5.0
+    mu = O.mu_incoherence(H)
+    p = rng.permutation(d)
+    s = rng.choice([-1.0, 1.0], d)
+    assert O.mu_incoherence(H[np.ix_(p, p)]) == pytest.approx(mu, rel=1e-10)
+    assert O.mu_incoherence(H * s[:, None] * s[None, :]) == pytest.approx(mu, rel=1e-10)
+    assert O.mu_incoherence(7.5 * H) == pytest.approx(mu, rel=1e-10)
+    assert O.mu_incoherence(H + 3.0 * np.eye(d)) == pytest.approx(mu, rel=1e-9)
+    assert 1 / math.sqrt(d) <= mu <= 1.0
