@@ -168,6 +168,49 @@ kronq_status kronq_biip_unrotate(float* W, int64_t m, int64_t n, int64_t ldw,
                                  const float* sg, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * BiIP with the input-side rescale S_X as well (hyper.ai summary, Method: the
+ * input-side diagonal rescaling is extended to both directions, S_G being the
+ * output-side part; Pith review, Algorithm 1 returns S_X beside S_G, U, V).
+ * The input side takes the form of the output side:
+ *   sx[j] = HX[j][j]^alpha_x  (1 where HX[j][j] <= 0; all 1 when alpha_x == 0),
+ *           read from H_X before it is transformed
+ *   W  (m x n) <- U diag(sg) W diag(sx) V^T
+ *   HX (n x n) <- V diag(sx)^-1 HX diag(sx)^-1 V^T
+ *   HG (m x m) <- as kronq_biip_rotate
+ * which keeps the proxy loss tr(H_G dW H_X dW^T) of a perturbation dW that is
+ * transformed as W is.  Arguments as kronq_biip_rotate, plus:
+ *   alpha_x  : exponent of the input rescale.
+ *   sx       : device, n floats.  sx_given = 0: the computed rescale is written
+ *              there (sx may be NULL); HX is required unless alpha_x == 0.
+ *              sx_given = 1: sx is read (nonzero finite values, e.g. from an
+ *              earlier call on the same input) and alpha_x is ignored; HX may
+ *              then be NULL (a shared H_X already transformed) or any n x n
+ *              matrix that transforms as H_X does -- the drift cross product
+ *              of kronq_drift_cross, with W and HG NULL.
+ *   W may be NULL (only HX and HG are transformed); not all of W, HX, HG NULL.
+ * The deploy decode of a layer rescaled this way takes x' = V diag(sx)^-1 x:
+ * kronq_decode_matvec multiplies by its input-side signs array, so a caller
+ * passes the product D_in[j] / sx[j] there.
+ * ws : kronq_biip_sx_ws(m, n) bytes (required).
+ * ------------------------------------------------------------------------- */
+size_t kronq_biip_sx_ws(int64_t m, int64_t n);
+kronq_status kronq_biip_rotate_sx(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
+                                  int64_t ldhx, float* HG, int64_t ldhg, const kronq_had* in_side,
+                                  const kronq_had* out_side, float alpha, float alpha_x, float* sg,
+                                  float* sx, int32_t sx_given, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Inverse of the weight side of kronq_biip_rotate_sx:
+ *   W (m x n) <- diag(sg)^-1 U^T W V diag(sx)^-1      in place, fp32
+ * sx (device, n floats) as returned by kronq_biip_rotate_sx; sg as in
+ * kronq_biip_unrotate.  ws : kronq_biip_unrotate_sx_ws(m, n) bytes. */
+size_t kronq_biip_unrotate_sx_ws(int64_t m, int64_t n);
+kronq_status kronq_biip_unrotate_sx(float* W, int64_t m, int64_t n, int64_t ldw,
+                                    const kronq_had* in_side, const kronq_had* out_side,
+                                    const float* sg, const float* sx, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------
  * Act-order, damping and inverse Cholesky factor (Pith review, Algorithm 2:
  * the damped H_X is H_X + lambda mean(diag H_X) I and the loop uses its
  * inverse Cholesky factor; GitHub README, flag --act_order).
@@ -316,6 +359,34 @@ size_t kronq_weight_cv_ws(int64_t m, int64_t n);
 kronq_status kronq_weight_cv(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
                              float* col_norms, float* row_norms, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mu-incoherence of a symmetric matrix (hyper.ai summary, Method, and Pith
+ * review, Figure 2(a): mu(H)/sqrt(d) near 1 when an eigenvector lies along a
+ * coordinate axis, small once the transforms have spread them out).  With
+ * H = Q Lambda Q^T (Q orthogonal):
+ *   mu (host double) <- max_ij |Q_ij|       (= mu(H) / sqrt(n))
+ * H     : n x n fp32 device, leading dimension ldh >= n; only the lower
+ *         triangle is read (the matrix is taken as symmetric).
+ * evals : device double[n] or NULL: the eigenvalues, in the order of Q's
+ *         columns (not sorted).
+ * Q     : device double n x n (leading dimension ldq >= n) or NULL: the
+ *         eigenvectors as columns.
+ * sweeps: host int32 or NULL: the Jacobi sweeps taken.
+ * Computed in fp64 by two-sided block Jacobi (sweeps over all pairs of
+ * 16-index blocks, each 32 x 32 pair subproblem diagonalized in full) until the
+ * off-diagonal Frobenius norm is at most tol times the Frobenius norm
+ * (tol in [1e-15, 1e-2]; 1e-13 is typical and reaches the eigenvectors to
+ * about 1e-13 * ||H|| / gap); KRONQ_ENUMERIC when that takes more than
+ * max_sweeps sweeps (1..100) or H holds a NaN or an infinity.  Where
+ * eigenvalues repeat, Q and so mu are not unique.  Synchronous on `stream`
+ * (the host reads the norm after each sweep).  n <= 32768.
+ * ws : kronq_incoherence_ws(n) bytes (about 16 n^2).
+ * ------------------------------------------------------------------------- */
+size_t kronq_incoherence_ws(int64_t n);
+kronq_status kronq_incoherence(const float* H, int64_t n, int64_t ldh, double tol, int32_t max_sweeps,
+                               double* mu, double* evals, double* Q, int64_t ldq, int32_t* sweeps,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Deploy codec (GitHub README of the KronQ release: int4 / int2 weights are

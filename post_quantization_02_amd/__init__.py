@@ -32,7 +32,9 @@ EXPORTS = ("kronq_status_string", "kronq_last_error", "kronq_version", "kronq_gr
            "kronq_check_finite", "kronq_decode_matvec_noalloc", "kronq_decode_noalloc_max_bytes",
            "kronq_gram_cross_ws", "kronq_gram_cross", "kronq_drift_cross_ws", "kronq_drift_cross",
            "kronq_gptaq_correction_ws",
-           "kronq_gptaq_correction", "kronq_gptaq_ws", "kronq_gptaq_quantize")
+           "kronq_gptaq_correction", "kronq_gptaq_ws", "kronq_gptaq_quantize", "kronq_biip_sx_ws",
+           "kronq_biip_rotate_sx", "kronq_biip_unrotate_sx_ws", "kronq_biip_unrotate_sx",
+           "kronq_incoherence_ws", "kronq_incoherence")
 
 
 class KronqError(RuntimeError):
@@ -141,6 +143,21 @@ def load(path: str = LIB_PATH):
     lib.kronq_gptaq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.POINTER(QCfg), vp, i64,
                                          vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kronq_gptaq_quantize.restype = i32
+    lib.kronq_biip_sx_ws.argtypes = [i64, i64]
+    lib.kronq_biip_sx_ws.restype = sz
+    lib.kronq_biip_rotate_sx.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, ctypes.POINTER(Had),
+                                         ctypes.POINTER(Had), f32, f32, vp, vp, i32, vp, sz, vp]
+    lib.kronq_biip_rotate_sx.restype = i32
+    lib.kronq_biip_unrotate_sx_ws.argtypes = [i64, i64]
+    lib.kronq_biip_unrotate_sx_ws.restype = sz
+    lib.kronq_biip_unrotate_sx.argtypes = [vp, i64, i64, i64, ctypes.POINTER(Had), ctypes.POINTER(Had),
+                                           vp, vp, vp, sz, vp]
+    lib.kronq_biip_unrotate_sx.restype = i32
+    lib.kronq_incoherence_ws.argtypes = [i64]
+    lib.kronq_incoherence_ws.restype = sz
+    lib.kronq_incoherence.argtypes = [vp, i64, i64, ctypes.c_double, i32, ctypes.POINTER(ctypes.c_double),
+                                      vp, vp, i64, ctypes.POINTER(i32), vp, sz, vp]
+    lib.kronq_incoherence.restype = i32
     _lib = lib
     return lib
 
@@ -230,6 +247,45 @@ def kronq_biip_rotate(W: torch.Tensor, HX: torch.Tensor | None, HG: torch.Tensor
                                  ctypes.byref(hout), alpha, _ptr(sg), _ptr(ws), need,
                                  _stream(stream)), "kronq_biip_rotate")
     return sg
+
+
+def kronq_biip_rotate_sx(W: torch.Tensor | None, HX: torch.Tensor | None, HG: torch.Tensor | None,
+                         in_signs: torch.Tensor | None, in_block: int, out_signs: torch.Tensor | None,
+                         out_block: int, alpha: float, alpha_x: float, sg: torch.Tensor | None = None,
+                         sx: torch.Tensor | None = None, sx_given: bool = False, m: int | None = None,
+                         n: int | None = None, stream=None, ws: torch.Tensor | None = None):
+    """In place, with the input rescale: W <- U S_G W S_X V^T,
+    HX <- V S_X^-1 HX S_X^-1 V^T, HG <- U S_G^-1 HG S_G^-1 U^T.  Returns (sg, sx);
+    sx is computed as diag(HX)^alpha_x unless sx_given (then it is read).  With
+    W None, m and n come from HG / HX or the arguments."""
+    lib = load()
+    if W is not None:
+        _dev(W, "W", torch.float32)
+        m, n = W.shape
+    else:
+        m = m if m is not None else (HG.shape[0] if HG is not None else 1)
+        n = n if n is not None else HX.shape[0]
+    dev = next(t.device for t in (W, HX, HG, sx) if t is not None)
+    if sg is None:
+        sg = torch.empty(m, dtype=torch.float32, device=dev)
+    if sx is None and not sx_given:
+        sx = torch.empty(n, dtype=torch.float32, device=dev)
+    for t, nm in ((HX, "HX"), (HG, "HG"), (sg, "sg"), (sx, "sx"), (in_signs, "in_signs"),
+                  (out_signs, "out_signs")):
+        if t is not None:
+            _dev(t, nm, torch.float32)
+    hin = Had(n, in_block, _ptr(in_signs))
+    hout = Had(m, out_block, _ptr(out_signs))
+    need = lib.kronq_biip_sx_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check(lib.kronq_biip_rotate_sx(_ptr(W), m, n, _ld(W) if W is not None else n, _ptr(HX),
+                                    _ld(HX) if HX is not None else n, _ptr(HG),
+                                    _ld(HG) if HG is not None else m, ctypes.byref(hin),
+                                    ctypes.byref(hout), alpha, alpha_x, _ptr(sg), _ptr(sx),
+                                    1 if sx_given else 0, _ptr(ws), need, _stream(stream)),
+           "kronq_biip_rotate_sx")
+    return sg, sx
 
 
 def kronq_chol_inv(H: torch.Tensor, lam: float, act_order: bool = False,
@@ -358,6 +414,53 @@ def kronq_biip_unrotate(W: torch.Tensor, in_signs: torch.Tensor, in_block: int,
     _check(lib.kronq_biip_unrotate(_ptr(W), m, n, _ld(W), ctypes.byref(hin), ctypes.byref(hout),
                                    _ptr(sg), _ptr(ws), need, _stream(stream)), "kronq_biip_unrotate")
     return W
+
+
+def kronq_biip_unrotate_sx(W: torch.Tensor, in_signs: torch.Tensor | None, in_block: int,
+                           out_signs: torch.Tensor | None, out_block: int, sg: torch.Tensor | None,
+                           sx: torch.Tensor, stream=None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """In place: W <- diag(sg)^-1 U^T W V diag(sx)^-1."""
+    lib = load()
+    _dev(W, "W", torch.float32)
+    m, n = W.shape
+    for t, nm in ((sg, "sg"), (sx, "sx"), (in_signs, "in_signs"), (out_signs, "out_signs")):
+        if t is not None:
+            _dev(t, nm, torch.float32)
+    hin = Had(n, in_block, _ptr(in_signs))
+    hout = Had(m, out_block, _ptr(out_signs))
+    need = lib.kronq_biip_unrotate_sx_ws(m, n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, W.device)
+    _check(lib.kronq_biip_unrotate_sx(_ptr(W), m, n, _ld(W), ctypes.byref(hin), ctypes.byref(hout),
+                                      _ptr(sg), _ptr(sx), _ptr(ws), need, _stream(stream)),
+           "kronq_biip_unrotate_sx")
+    return W
+
+
+def kronq_incoherence(H: torch.Tensor, tol: float = 1e-13, max_sweeps: int = 40,
+                      want_evals: bool = False, want_q: bool = False, stream=None,
+                      ws: torch.Tensor | None = None) -> dict:
+    """mu(H)/sqrt(n) = max_ij |Q_ij| of H = Q Lambda Q^T (fp64 block Jacobi).
+    Returns {"mu", "sweeps"} and, when asked, "evals" (n doubles) and "Q"."""
+    lib = load()
+    _dev(H, "H", torch.float32)
+    n = H.shape[0]
+    evals = torch.empty(n, dtype=torch.float64, device=H.device) if want_evals else None
+    Q = torch.empty((n, n), dtype=torch.float64, device=H.device) if want_q else None
+    need = lib.kronq_incoherence_ws(n)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, H.device)
+    mu = ctypes.c_double(0.0)
+    sw = ctypes.c_int32(0)
+    _check(lib.kronq_incoherence(_ptr(H), n, _ld(H), tol, max_sweeps, ctypes.byref(mu), _ptr(evals),
+                                 _ptr(Q), n, ctypes.byref(sw), _ptr(ws), need, _stream(stream)),
+           "kronq_incoherence")
+    out = {"mu": mu.value, "sweeps": sw.value}
+    if want_evals:
+        out["evals"] = evals
+    if want_q:
+        out["Q"] = Q
+    return out
 
 
 def kronq_packed_row_bytes(n: int, bits: int) -> int:

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkronq.so")
 
 SOURCES = ["api.cpp", "gram.hip", "fwht.hip", "chol.hip", "gptq.hip", "gptaq.hip", "trace.hip", "codec.hip",
-           "diag.hip"]
+           "diag.hip", "eig.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -231,6 +231,79 @@ kronq_status kronq_biip_rotate(float* W, int64_t m, int64_t n, int64_t ldw, floa
                      (hipStream_t)stream);
 }
 
+size_t kronq_incoherence_ws(int64_t n) {
+  if (n < 1 || n > 32768) return 0;
+  return eig_ws_bytes(n);
+}
+
+kronq_status kronq_incoherence(const float* H, int64_t n, int64_t ldh, double tol, int32_t max_sweeps,
+                               double* mu, double* evals, double* Q, int64_t ldq, int32_t* sweeps,
+                               void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "kronq_incoherence";
+  if (!H || !mu) return fail(KRONQ_EINVAL, "%s: H or mu is NULL", fn);
+  if (n < 1 || n > 32768 || ldh < n) return fail(KRONQ_EINVAL, "%s: bad H shape", fn);
+  if (Q && ldq < n) return fail(KRONQ_EINVAL, "%s: ldq < n", fn);
+  if (!(tol >= 1e-15 && tol <= 1e-2)) return fail(KRONQ_EINVAL, "%s: tol outside [1e-15, 1e-2]", fn);
+  if (max_sweeps < 1 || max_sweeps > 100) return fail(KRONQ_EINVAL, "%s: max_sweeps outside 1..100", fn);
+  kronq_status st = check_ws(fn, ws, ws_bytes, eig_ws_bytes(n), true);
+  if (st) return st;
+  return eig_launch(H, n, ldh, tol, max_sweeps, mu, evals, Q, ldq, sweeps, ws, (hipStream_t)stream);
+}
+
+size_t kronq_biip_sx_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return biip_sx_ws_bytes(m, n);
+}
+
+kronq_status kronq_biip_rotate_sx(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
+                                  int64_t ldhx, float* HG, int64_t ldhg, const kronq_had* in_side,
+                                  const kronq_had* out_side, float alpha, float alpha_x, float* sg,
+                                  float* sx, int32_t sx_given, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const char* fn = "kronq_biip_rotate_sx";
+  if (!W && !HX && !HG) return fail(KRONQ_EINVAL, "%s: W, HX and HG are all NULL", fn);
+  if (m < 1 || n < 1 || (W && ldw < n)) return fail(KRONQ_EINVAL, "%s: bad W shape", fn);
+  if (HX && ldhx < n) return fail(KRONQ_EINVAL, "%s: ldhx < n", fn);
+  if (HG && ldhg < m) return fail(KRONQ_EINVAL, "%s: ldhg < m", fn);
+  if (!std::isfinite(alpha) || !std::isfinite(alpha_x))
+    return fail(KRONQ_EINVAL, "%s: alpha or alpha_x not finite", fn);
+  if (alpha != 0.0f && !HG) return fail(KRONQ_EINVAL, "%s: the output rescale needs HG", fn);
+  if (sx_given != 0 && sx_given != 1) return fail(KRONQ_EINVAL, "%s: sx_given must be 0 or 1", fn);
+  if (sx_given && !sx) return fail(KRONQ_EINVAL, "%s: sx_given but sx is NULL", fn);
+  if (!sx_given && alpha_x != 0.0f && !HX)
+    return fail(KRONQ_EINVAL, "%s: the input rescale needs HX (or a given sx)", fn);
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  st = check_had(out_side, m, "output-side");
+  if (st) return st;
+  st = check_ws(fn, ws, ws_bytes, biip_sx_ws_bytes(m, n), true);
+  if (st) return st;
+  return biip_launch(W, m, n, ldw, HX, ldhx, HG, ldhg, *in_side, *out_side, alpha, sg, ws, ws_bytes,
+                     (hipStream_t)stream, true, alpha_x, sx_given ? sx : nullptr,
+                     sx_given ? nullptr : sx);
+}
+
+size_t kronq_biip_unrotate_sx_ws(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return unrotate_sx_ws_bytes(m, n);
+}
+
+kronq_status kronq_biip_unrotate_sx(float* W, int64_t m, int64_t n, int64_t ldw,
+                                    const kronq_had* in_side, const kronq_had* out_side,
+                                    const float* sg, const float* sx, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  const char* fn = "kronq_biip_unrotate_sx";
+  if (!W || !sx) return fail(KRONQ_EINVAL, "%s: W or sx is NULL", fn);
+  if (m < 1 || n < 1 || ldw < n) return fail(KRONQ_EINVAL, "%s: bad W shape", fn);
+  kronq_status st = check_had(in_side, n, "input-side");
+  if (st) return st;
+  st = check_had(out_side, m, "output-side");
+  if (st) return st;
+  st = check_ws(fn, ws, ws_bytes, unrotate_sx_ws_bytes(m, n), true);
+  if (st) return st;
+  return unrotate_sx_launch(W, m, n, ldw, *in_side, *out_side, sg, sx, ws, (hipStream_t)stream);
+}
+
 size_t kronq_biip_unrotate_ws(int64_t m, int64_t n) {
   if (m < 1 || n < 1) return 0;
   return unrotate_ws_bytes(m);

@@ -653,6 +653,34 @@ __global__ void biip_prep(const float* HG, int64_t ldhg, int64_t m, float alpha,
   if (sg_out) sg_out[i] = g;
 }
 
+// input-side rescale: sx[j] = sx_in[j] when given, else HX[j][j]^alpha_x
+// (1 when not positive or alpha_x == 0), read before any transform;
+// cfW[j] = si[j] * sx[j] (W's columns), cfX[j] = si[j] / sx[j] (both sides of H_X)
+__global__ void biip_prep_in(const float* HX, int64_t ldhx, int64_t n, float alpha_x,
+                             const float* sx_in, const float* si, float* cfW, float* cfX,
+                             float* sx_out) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  float x = 1.0f;
+  if (sx_in) {
+    x = sx_in[j];
+  } else if (alpha_x != 0.0f) {
+    const float dxj = HX[j * ldhx + j];
+    if (dxj > 0.0f) x = powf(dxj, alpha_x);
+  }
+  const float o = si ? si[j] : 1.f;   // NULL: identity input side
+  cfW[j] = o * x;
+  cfX[j] = o / x;
+  if (sx_out && !sx_in) sx_out[j] = x;
+}
+
+// cf[j] = si[j] / sx[j]: the column factor of the inverse with an input rescale
+__global__ void unrotate_prep_in(const float* si, const float* sx, int64_t n, float* cf) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  cf[j] = (si ? si[j] : 1.f) / sx[j];
+}
+
 // rf[i] = so[i] / sg[i]  (sg NULL: all ones)
 __global__ void unrotate_prep(const float* so, const float* sg, int64_t m, float* rf) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -797,9 +825,14 @@ size_t biip_ws_bytes(int64_t m, int64_t n) {
   return 3 * align_up((size_t)m * sizeof(float), 256);
 }
 
+size_t biip_sx_ws_bytes(int64_t m, int64_t n) {
+  return biip_ws_bytes(m, n) + 2 * align_up((size_t)n * sizeof(float), 256);
+}
+
 kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX, int64_t ldhx,
                          float* HG, int64_t ldhg, const kronq_had& in, const kronq_had& out,
-                         float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s) {
+                         float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s,
+                         bool rescale_in, float alpha_x, const float* sx_in, float* sx_out) {
   (void)ws_bytes;
   const size_t seg = align_up((size_t)m * sizeof(float), 256);
   float* sg_ws = static_cast<float*>(ws);
@@ -811,11 +844,24 @@ kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX,
   // an identity side (block 1, no signs) leaves its factor alone: V = I keeps
   // H_X, U = I without a rescale keeps H_G (and W when both sides are so)
   const bool v_id = in.block == 1 && !in.signs, u_id = out.block == 1 && !out.signs;
+  // input rescale: W's columns take si * sx, H_X's rows and columns si / sx
+  const float* cfW = in.signs;
+  const float* cfX = in.signs;
+  if (rescale_in) {
+    float* cw = reinterpret_cast<float*>(static_cast<char*>(ws) + 3 * seg);
+    float* cx = cw + align_up((size_t)n * sizeof(float), 256) / sizeof(float);
+    hipLaunchKernelGGL(biip_prep_in, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const float*)HX, ldhx, n, alpha_x, sx_in, in.signs, cw, cx, sx_out);
+    KQ_LAUNCHED("biip_prep_in");
+    cfW = cw;
+    cfX = cx;
+  }
   Plan pl[3];
   int n_mat = 0;
-  if (!(v_id && u_id && alpha == 0.0f))
-    pl[n_mat++] = plan2d(W, m, n, ldw, out.block, rfW, in.block, in.signs, false);
-  if (HX && !v_id) pl[n_mat++] = plan2d(HX, n, n, ldhx, in.block, in.signs, in.block, in.signs, false);
+  if (W && !(v_id && u_id && alpha == 0.0f && !rescale_in))
+    pl[n_mat++] = plan2d(W, m, n, ldw, out.block, rfW, in.block, cfW, false);
+  if (HX && !(v_id && !rescale_in))
+    pl[n_mat++] = plan2d(HX, n, n, ldhx, in.block, cfX, in.block, cfX, false);
   if (HG && !(u_id && alpha == 0.0f))
     pl[n_mat++] = plan2d(HG, m, m, ldhg, out.block, rfG, out.block, rfG, false);
   return launch_forward(pl, n_mat, s);
@@ -830,6 +876,24 @@ kronq_status unrotate_launch(float* W, int64_t m, int64_t n, int64_t ldw, const 
                      sg, m, rf);
   KQ_LAUNCHED("unrotate_prep");
   return launch2d(plan2d(W, m, n, ldw, out.block, rf, in.block, in.signs, true), s);
+}
+
+size_t unrotate_sx_ws_bytes(int64_t m, int64_t n) {
+  return unrotate_ws_bytes(m) + align_up((size_t)n * sizeof(float), 256);
+}
+
+kronq_status unrotate_sx_launch(float* W, int64_t m, int64_t n, int64_t ldw, const kronq_had& in,
+                                const kronq_had& out, const float* sg, const float* sx, void* ws,
+                                hipStream_t s) {
+  float* rf = static_cast<float*>(ws);
+  float* cf = reinterpret_cast<float*>(static_cast<char*>(ws) + unrotate_ws_bytes(m));
+  hipLaunchKernelGGL(unrotate_prep, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, out.signs,
+                     sg, m, rf);
+  KQ_LAUNCHED("unrotate_prep");
+  hipLaunchKernelGGL(unrotate_prep_in, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in.signs,
+                     sx, n, cf);
+  KQ_LAUNCHED("unrotate_prep_in");
+  return launch2d(plan2d(W, m, n, ldw, out.block, rf, in.block, cf, true), s);
 }
 
 }  // namespace kronq

@@ -44,13 +44,22 @@ kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t 
 
 // fwht.hip
 size_t biip_ws_bytes(int64_t m, int64_t n);
+// rescale_in: also the input-side rescale (sx_in when given, else diag(HX)^alpha_x;
+// written to sx_out when computed); W may then be NULL.  Workspace biip_sx_ws_bytes.
 kronq_status biip_launch(float* W, int64_t m, int64_t n, int64_t ldw, float* HX, int64_t ldhx,
                          float* HG, int64_t ldhg, const kronq_had& in, const kronq_had& out,
-                         float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s);
+                         float alpha, float* sg, void* ws, size_t ws_bytes, hipStream_t s,
+                         bool rescale_in = false, float alpha_x = 0.0f,
+                         const float* sx_in = nullptr, float* sx_out = nullptr);
+size_t biip_sx_ws_bytes(int64_t m, int64_t n);
 
 size_t unrotate_ws_bytes(int64_t m);
 kronq_status unrotate_launch(float* W, int64_t m, int64_t n, int64_t ldw, const kronq_had& in,
                              const kronq_had& out, const float* sg, void* ws, hipStream_t s);
+size_t unrotate_sx_ws_bytes(int64_t m, int64_t n);
+kronq_status unrotate_sx_launch(float* W, int64_t m, int64_t n, int64_t ldw, const kronq_had& in,
+                                const kronq_had& out, const float* sg, const float* sx, void* ws,
+                                hipStream_t s);
 
 // chol.hip
 size_t chol_ws_bytes(int64_t n);
@@ -89,6 +98,12 @@ kronq_status finite_launch(const float* A, int64_t rows, int64_t cols, int64_t l
                            hipStream_t s);
 kronq_status cv_launch(const float* W, int64_t m, int64_t n, int64_t ldw, double* out2,
                        float* col_norms, float* row_norms, void* ws, hipStream_t s);
+
+// eig.hip
+size_t eig_ws_bytes(int64_t n);
+kronq_status eig_launch(const float* H, int64_t n, int64_t ldh, double tol, int max_sweeps,
+                        double* mu, double* evals, double* Q, int64_t ldq, int32_t* sweeps, void* ws,
+                        hipStream_t s);
 
 // codec.hip
 kronq_status pack_launch(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int bits,

@@ -289,3 +289,26 @@ def test_new_status_strings_and_check_finite_args(lib):
     assert lib.kronq_check_finite(fake, 4, 4, 3, fake, None) == kq.KRONQ_EINVAL
     assert lib.kronq_check_finite(None, 4, 4, 4, fake, None) == kq.KRONQ_EINVAL
     assert lib.kronq_check_finite(fake, -1, 4, 4, fake, None) == kq.KRONQ_EINVAL
+
+
+def test_input_rescale_arguments_rejected_before_launch(lib):
+    fake = 1 << 20   # never dereferenced
+    h_in, h_out = kq.Had(16, 16, fake), kq.Had(8, 8, fake)
+    need = lib.kronq_biip_sx_ws(8, 16)
+    assert need >= lib.kronq_biip_ws(8, 16) + 2 * 16 * 4
+    assert lib.kronq_biip_unrotate_sx_ws(8, 16) >= lib.kronq_biip_unrotate_ws(8, 16) + 16 * 4
+
+    def rot(W, HX, HG, alpha, alpha_x, sx, given, ws=fake, wsb=need):
+        return lib.kronq_biip_rotate_sx(W, 8, 16, 16, HX, 16, HG, 8, ctypes.byref(h_in),
+                                        ctypes.byref(h_out), alpha, alpha_x, None, sx, given, ws,
+                                        wsb, None)
+    assert rot(None, None, None, 0.0, 0.0, None, 0) == kq.KRONQ_EINVAL          # nothing to do
+    assert rot(fake, None, fake, 0.25, 0.25, None, 0) == kq.KRONQ_EINVAL        # S_X needs HX
+    assert rot(fake, fake, fake, 0.25, 0.25, None, 1) == kq.KRONQ_EINVAL        # given but NULL
+    assert rot(fake, fake, fake, 0.25, 0.25, fake, 2) == kq.KRONQ_EINVAL        # bad flag
+    assert rot(fake, fake, fake, 0.25, float("nan"), fake, 0) == kq.KRONQ_EINVAL
+    assert rot(fake, fake, None, 0.25, 0.25, fake, 0) == kq.KRONQ_EINVAL        # S_G needs HG
+    assert rot(fake, fake, fake, 0.25, 0.25, fake, 0, wsb=need - 1) == kq.KRONQ_EWORKSPACE
+    assert rot(fake, fake, fake, 0.25, 0.25, fake, 0, ws=None, wsb=need) == kq.KRONQ_EWORKSPACE
+    assert lib.kronq_biip_unrotate_sx(fake, 8, 16, 16, ctypes.byref(h_in), ctypes.byref(h_out),
+                                      fake, None, fake, 1 << 20, None) == kq.KRONQ_EINVAL
