@@ -54,8 +54,6 @@ struct GptqParams {
   double* E;               // m x ldE, processing order
   int64_t ldE;             // n rounded up to 16 (128-byte rows)
   const double* pc;        // per-channel (scale, zero) pairs, m x 2
-  double* R64;             // fp64 copy of R right of the diagonal blocks, n x ldr64
-  int64_t ldr64;
   double* D64;             // staged images of the diagonal blocks, nblocks x 128 x 128
   bool vec_out;            // natural order, n % 8 == 0, outputs 16-byte aligned
 };
@@ -417,24 +415,22 @@ __device__ __forceinline__ void chain_role(const GptqParams& p, double* gl, int 
 // 4 r + t]: each lane loads 8 contiguous doubles of E and 8 rows of 4
 // contiguous doubles of R per batch (16-byte loads).  Tile t's lane column r
 // is block column 64 ch + 4 r + t; accumulator register v holds row 4 v + g.
-// R is read from its fp64 copy: a conversion in this loop would take issue
-// cycles from the fp64 matrix operations.
+// R is read as stored (fp32, exact in fp64) and widened in registers: half the
+// bytes of an fp64 copy on the loop's largest stream (down_proj's loop at
+// n = 28672 took 168 ms reading an fp64 copy, 126 ms this way).
 struct PBatch {
   f64x2_t e[4];      // E[arow][kb + 8 g .. + 7]
-  f64x2_t r[8][2];   // R[kb + 8 g + s][64 ch + 4 r .. + 3]
+  f32x4_t r[8];      // R[kb + 8 g + s][64 ch + 4 r .. + 3]
 };
 
-__device__ __forceinline__ void pb_load(PBatch& B, const double* Eg, const double* Rg, int64_t ldr,
+__device__ __forceinline__ void pb_load(PBatch& B, const double* Eg, const float* Rg, int64_t ldr,
                                         int64_t kb) {
   const double* e = Eg + kb;
 #pragma unroll
   for (int q = 0; q < 4; ++q) B.e[q] = *reinterpret_cast<const f64x2_t*>(e + 2 * q);
-  const double* r = Rg + kb * ldr;
+  const float* r = Rg + kb * ldr;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    B.r[s][0] = *reinterpret_cast<const f64x2_t*>(r + s * ldr);
-    B.r[s][1] = *reinterpret_cast<const f64x2_t*>(r + s * ldr + 2);
-  }
+  for (int s = 0; s < 8; ++s) B.r[s] = *reinterpret_cast<const f32x4_t*>(r + s * ldr);
 }
 
 __device__ __forceinline__ void pb_mma(const PBatch& B, f64x4_t (&acc)[4]) {
@@ -443,16 +439,15 @@ __device__ __forceinline__ void pb_mma(const PBatch& B, f64x4_t (&acc)[4]) {
     const double a = B.e[s >> 1][s & 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, B.r[s][t >> 1][t & 1], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t], acc[t], 0, 0, 0);
   }
 }
 
-// fp64 images of R, made once per call.  Row k of R64: the blocks right of
-// k's diagonal block (the only part the product reads).  D64: each diagonal
-// block as staged for the column loop, its strictly upper part with zeros on
-// and below the diagonal and past n, and in row 127 the reciprocal diagonal.
-// One workgroup per row of the padded block grid.
-__global__ void __launch_bounds__(256) gptq_r64(GptqParams p) {
+// fp64 images of R's diagonal blocks, made once per call: each block as staged
+// for the column loop, its strictly upper part with zeros on and below the
+// diagonal and past n, and in row 127 the reciprocal diagonal.  One workgroup
+// per row of the padded block grid.
+__global__ void __launch_bounds__(256) gptq_diag64(GptqParams p) {
   const int64_t k = blockIdx.x;
   const int i = (int)(k % BLK);
   const int64_t jb = k - i;
@@ -465,17 +460,6 @@ __global__ void __launch_bounds__(256) gptq_r64(GptqParams p) {
     for (int j = threadIdx.x; j < BLK; j += 256)
       drow[j] = (j > i && j < ncols) ? (double)p.R[k * p.ldr + jb + j] : 0.0;
   }
-  if (k >= p.n) return;
-  const int64_t j0 = jb + BLK;
-  const float* src = p.R + k * p.ldr;
-  double* dst = p.R64 + k * p.ldr64;
-  const int64_t n4 = j0 + max<int64_t>(p.n - j0, 0) / 4 * 4;
-  for (int64_t j = j0 + 4 * threadIdx.x; j < n4; j += 4 * 256) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + j);
-    *reinterpret_cast<f64x2_t*>(dst + j) = f64x2_t{(double)v[0], (double)v[1]};
-    *reinterpret_cast<f64x2_t*>(dst + j + 2) = f64x2_t{(double)v[2], (double)v[3]};
-  }
-  for (int64_t j = n4 + threadIdx.x; j < p.n; j += 256) dst[j] = (double)src[j];
 }
 
 template <bool DRIFT>
@@ -540,7 +524,8 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
   for (int b = 0; b < nblocks; ++b) {
     const int64_t jb = (int64_t)b * BLK, jn = jb + BLK;
     const bool more = b + 1 < nblocks;
-    const double* Rg = p.R64 + (int64_t)(8 * g) * p.ldr64 + jn + 64 * ch + 4 * r;
+    const float* Rg = p.R + (int64_t)(8 * g) * p.ldr + jn + 64 * ch + 4 * r;
+    const int64_t ldrr = p.ldr;
     f64x4_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
@@ -554,13 +539,13 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
       // is consumed; the scheduling barriers keep the compiler from sinking
       // the loads next to their use
       PBatch A, B;
-      pb_load(A, Eg, Rg, p.ldr64, k0);
+      pb_load(A, Eg, Rg, ldrr, k0);
       for (int i = 0; i < nbat; i += 2) {
-        pb_load(B, Eg, Rg, p.ldr64, k0 + (int64_t)KB * (i + 1));
+        pb_load(B, Eg, Rg, ldrr, k0 + (int64_t)KB * (i + 1));
         __builtin_amdgcn_sched_barrier(0);
         pb_mma(A, acc);
         __builtin_amdgcn_sched_barrier(0);
-        pb_load(A, Eg, Rg, p.ldr64, k0 + (int64_t)KB * min(i + 2, nbat - 1));
+        pb_load(A, Eg, Rg, ldrr, k0 + (int64_t)KB * min(i + 2, nbat - 1));
         __builtin_amdgcn_sched_barrier(0);
         pb_mma(B, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -570,8 +555,8 @@ __device__ __forceinline__ void product_role(const GptqParams& p, double* gl, in
     if (more) {
       // block b's errors: this half of [jb, jb + 128)
       PBatch A, B;
-      pb_load(A, Eg, Rg, p.ldr64, jb + BLK / 2 * kh);
-      pb_load(B, Eg, Rg, p.ldr64, jb + BLK / 2 * kh + KB);
+      pb_load(A, Eg, Rg, ldrr, jb + BLK / 2 * kh);
+      pb_load(B, Eg, Rg, ldrr, jb + BLK / 2 * kh + KB);
       pb_mma(A, acc);
       pb_mma(B, acc);
       store(jn, acc, w);
@@ -619,7 +604,7 @@ bool aligned(const void* q, size_t a) { return (reinterpret_cast<uintptr_t>(q) %
 size_t gptq_ws_bytes(int64_t m, int64_t n) {
   return align_up((size_t)m * lde(n) * sizeof(double), 256) +
          align_up((size_t)m * 2 * sizeof(double), 256) +
-         align_up((size_t)n * lde(n) * sizeof(double), 256) +
+
          (size_t)((n + BLK - 1) / BLK) * SQ * sizeof(double);
 }
 
@@ -657,17 +642,15 @@ kronq_status gptq_launch(const float* W, int64_t m, int64_t n, int64_t ldw, cons
   double* pc = reinterpret_cast<double*>(static_cast<char*>(ws) +
                                          align_up((size_t)m * p.ldE * sizeof(double), 256));
   p.pc = pc;
-  p.ldr64 = lde(n);
-  p.R64 = reinterpret_cast<double*>(reinterpret_cast<char*>(pc) + align_up((size_t)m * 2 * sizeof(double), 256));
+  p.D64 = reinterpret_cast<double*>(reinterpret_cast<char*>(pc) + align_up((size_t)m * 2 * sizeof(double), 256));
   p.vec_out = perm == nullptr && n % 8 == 0 && aligned(codes, 8) && (What == nullptr || aligned(What, 16)) &&
               (pre_round == nullptr || aligned(pre_round, 16));
   if (group == 0) {
     hipLaunchKernelGGL(gptq_row_params, dim3((unsigned)m), dim3(256), 0, s, p, pc);
     KQ_LAUNCHED("gptq_row_params");
   }
-  p.D64 = p.R64 + align_up((size_t)n * lde(n) * sizeof(double), 256) / sizeof(double);
-  hipLaunchKernelGGL(gptq_r64, dim3((unsigned)((n + BLK - 1) / BLK * BLK)), dim3(256), 0, s, p);
-  KQ_LAUNCHED("gptq_r64");
+  hipLaunchKernelGGL(gptq_diag64, dim3((unsigned)((n + BLK - 1) / BLK * BLK)), dim3(256), 0, s, p);
+  KQ_LAUNCHED("gptq_diag64");
   const size_t lds = kGptqLds;
   if (X2) {
     KQ_HIP(hipFuncSetAttribute((const void*)gptq_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
