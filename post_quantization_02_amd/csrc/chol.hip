@@ -779,19 +779,61 @@ __global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
 // past the block gets the block's share at once, with K = NBO * NB:
 //   SYRK  A_ij -= sum_q L_i,b0+q L_j,b0+q^T            (j >= b1 = b0 + NBO, i >= j)
 //   fwd   B_ic -= sum_{q: b0+q >= c} L_i,b0+q Y_b0+q,c  (i >= b1, c < b1)
+// A right-looking sweep reads and writes the whole trailing matrix once per
+// panel; with rank-512 updates it does so once per outer block, and each
+// tile's read-modify-write is amortized over four times the products.
+//
+// The products run on the bf16 matrix cores at fp32 accuracy: every fp32
+// operand is split exactly into three bf16 parts, x = x1 + x2 + x3 (8 + 8 + 8
+// significant bits), and a b = sum of the six products a_i b_j with i + j <= 4
+// (the three dropped ones are below 2^-24 |a b|).  bf16 products are exact in
+// fp32; a1 b1 accumulates in one fp32 accumulator and the five smaller terms
+// in another, so the accumulation rounds as often as an fp32 product would.
+// Six v_mfma_f32_32x32x16_bf16 (32 cycles each) replace eight
+// v_mfma_f32_32x32x2f32 (64 cycles each) per 32 x 32 x 16 step.
+//
 // One 128 x 128 output tile per workgroup (four waves as 2 x 2, each 64 x 64
-// as 2 x 2 accumulators of v_mfma_f32_32x32x2f32), K staged 16 at a time
-// through LDS with the next stage's global loads in registers.  A right-
-// looking sweep reads and writes the whole trailing matrix once per panel;
-// with rank-512 updates it does so once per outer block, and each tile's
-// read-modify-write is amortized over four times the products.
+// as 2 x 2 accumulator pairs), K staged 32 at a time: the fp32 values of the
+// next stage are loaded into registers while the current one is multiplied,
+// then split and stored to LDS as bf16 rows [part][row or column][k] (80-byte
+// rows: the 16-byte operand reads of 16 consecutive rows hit distinct banks).
 constexpr int OKS = 32;             // K per stage
-constexpr int OLD = NB + 4;         // padded LDS row (floats)
+constexpr int OLD = OKS + 8;        // padded LDS row (bf16 elements)
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+
+// round-to-nearest-even bf16 bits of a finite fp32 value
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x = x1 + x2 + x3 exactly (each remainder is exact in fp32)
+__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = bf16_bits(x);
+  const float r1 = x - __uint_as_float(h << 16);
+  m = bf16_bits(r1);
+  const float r2 = r1 - __uint_as_float(m << 16);
+  l = bf16_bits(r2);
+}
+
+// four consecutive-k values of one row or column -> its three bf16 parts,
+// 8 bytes each, at dst[part * 128 * OLD]
+__device__ __forceinline__ void put_split4(unsigned short* dst, float x0, float x1, float x2, float x3) {
+  uint32_t h[4], m[4], l[4];
+  split3(x0, h[0], m[0], l[0]);
+  split3(x1, h[1], m[1], l[1]);
+  split3(x2, h[2], m[2], l[2]);
+  split3(x3, h[3], m[3], l[3]);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2*>(dst + NB * OLD) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
+  *reinterpret_cast<uint2*>(dst + 2 * NB * OLD) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
 
 __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0, CholWs w) {
   if (*w.flag) return;
-  __shared__ __align__(16) float As[OKS][OLD];
-  __shared__ __align__(16) float Bs[OKS][OLD];
+  __shared__ __align__(16) unsigned short As[3 * NB * OLD];
+  __shared__ __align__(16) unsigned short Bs[3 * NB * OLD];
   const int b1 = b0 + NBO;
   int t = blockIdx.x;
   const int q2 = P - b1;
@@ -811,21 +853,25 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lk = lane >> 5;
-  f32x16_t acc[2][2];
+  f32x16_t hi[2][2], lo[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+      for (int v = 0; v < 16; ++v) {
+        hi[a][b][v] = 0.f;
+        lo[a][b][v] = 0.f;
+      }
   const int k_lo = qlo * NB, k_hi = NBO * NB;
   float4 ra[4], rb[4];
   // stage at k0 (32 values of k): A element (r, k) = L_i,b0+q[r][kk]; B
   // element (col, k) = L_j,b0+q[col][kk] (SYRK) or (k, col) =
   // Y_b0+q[kk][c NB + col] (fwd), with q = k / NB, kk = k % NB; panel q sits
   // in slot q of the buffers (b0 is a multiple of NBO).  Float4 u of a thread
-  // is row (tid + 256 u) / 8, k quad (tid + 256 u) % 8 (A, SYRK B), or k row
-  // (tid + 256 u) / 32, column quad (tid + 256 u) % 32 (fwd B).
+  // is row (tid + 256 u) / 8, k quad (tid + 256 u) % 8 (A, SYRK B), or, for
+  // the fwd B, k row 4 (tid / 32) + u of column quad tid % 32 (a 4 x 4 block
+  // that the store transposes).
   auto load = [&](int k0) {
     const int q = k0 / NB, kk0 = k0 % NB;
     const float* La = lp_buf(w, q) + (int64_t)i * NB * NB + kk0;
@@ -837,7 +883,7 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
       const int r = e >> 3, k4 = (e & 7) * 4;
       ra[u] = *reinterpret_cast<const float4*>(La + (int64_t)r * NB + k4);
       if (!fwd) rb[u] = *reinterpret_cast<const float4*>(Lb + (int64_t)r * NB + k4);
-      else rb[u] = *reinterpret_cast<const float4*>(Yb + (int64_t)(e >> 5) * npad + (e & 31) * 4);
+      else rb[u] = *reinterpret_cast<const float4*>(Yb + (int64_t)(4 * (tid >> 5) + u) * npad + (tid & 31) * 4);
     }
   };
   auto store = [&]() {
@@ -845,18 +891,15 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
     for (int u = 0; u < 4; ++u) {
       const int e = tid + 256 * u;
       const int r = e >> 3, k4 = (e & 7) * 4;
-      As[k4][r] = ra[u].x;
-      As[k4 + 1][r] = ra[u].y;
-      As[k4 + 2][r] = ra[u].z;
-      As[k4 + 3][r] = ra[u].w;
-      if (!fwd) {
-        Bs[k4][r] = rb[u].x;
-        Bs[k4 + 1][r] = rb[u].y;
-        Bs[k4 + 2][r] = rb[u].z;
-        Bs[k4 + 3][r] = rb[u].w;
-      } else {
-        *reinterpret_cast<float4*>(&Bs[e >> 5][(e & 31) * 4]) = rb[u];
-      }
+      put_split4(As + r * OLD + k4, ra[u].x, ra[u].y, ra[u].z, ra[u].w);
+      if (!fwd) put_split4(Bs + r * OLD + k4, rb[u].x, rb[u].y, rb[u].z, rb[u].w);
+    }
+    if (fwd) {
+      const int c0 = (tid & 31) * 4, kq = 4 * (tid >> 5);
+      put_split4(Bs + (c0 + 0) * OLD + kq, rb[0].x, rb[1].x, rb[2].x, rb[3].x);
+      put_split4(Bs + (c0 + 1) * OLD + kq, rb[0].y, rb[1].y, rb[2].y, rb[3].y);
+      put_split4(Bs + (c0 + 2) * OLD + kq, rb[0].z, rb[1].z, rb[2].z, rb[3].z);
+      put_split4(Bs + (c0 + 3) * OLD + kq, rb[0].w, rb[1].w, rb[2].w, rb[3].w);
     }
   };
   load(k_lo);
@@ -866,17 +909,37 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
     const bool more = k0 + OKS < k_hi;
     if (more) load(k0 + OKS);
 #pragma unroll
-    for (int kk = 0; kk < OKS; kk += 2) {
-      float af[2], bf[2];
+    for (int ks = 0; ks < OKS; ks += 16) {
+      bf16x8_t af[2][3], bf[2][3];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = As[kk + lk][wm * 64 + 32 * a + lr];
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bf[b] = Bs[kk + lk][wn * 64 + 32 * b + lr];
+        for (int pt = 0; pt < 3; ++pt)
+          af[a][pt] = *reinterpret_cast<const bf16x8_t*>(As + pt * NB * OLD + (wm * 64 + 32 * a + lr) * OLD +
+                                                          ks + 8 * lk);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt)
+          bf[b][pt] = *reinterpret_cast<const bf16x8_t*>(Bs + pt * NB * OLD + (wn * 64 + 32 * b + lr) * OLD +
+                                                          ks + 8 * lk);
+      // term order: each group of four MFMAs updates four different
+      // accumulators
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
+          hi[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][0], bf[b][0], hi[a][b], 0, 0, 0);
+#pragma unroll
+      for (int term = 0; term < 5; ++term) {
+        const int pa = term == 0 ? 0 : term == 1 ? 1 : term == 2 ? 0 : term == 3 ? 1 : 2;
+        const int pb = term == 0 ? 1 : term == 1 ? 0 : term == 2 ? 2 : term == 3 ? 1 : 0;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            lo[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][pa], bf[b][pb], lo[a][b], 0, 0, 0);
+      }
     }
     __syncthreads();
     if (more) {
@@ -884,7 +947,7 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
       __syncthreads();
     }
   }
-  // C -= acc, every old value of an accumulator tile loaded before its stores
+  // C -= hi + lo, every old value of an accumulator tile loaded before its stores
   float* C = (fwd ? w.B : w.A) + (int64_t)i * NB * npad + (int64_t)j * NB;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -899,7 +962,7 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 64 + 32 * a + 8 * (v >> 2) + 4 * lk + (v & 3);
-        C[(int64_t)r * npad + wn * 64 + 32 * b + lr] = old[v] - acc[a][b][v];
+        C[(int64_t)r * npad + wn * 64 + 32 * b + lr] = old[v] - (hi[a][b][v] + lo[a][b][v]);
       }
     }
 }
