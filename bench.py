@@ -590,6 +590,28 @@ def run_workload(w, steps, warmup, dev):
     return wall_ms, per_sub, t_gen, paths
 
 
+def incoherence_leg(w, path, dev):
+    """mu(H)/sqrt(d) of H_G and H_X before and after BiIP (the incoherence
+    diagnostic), with the time of one call at d = 4096."""
+    kq = path.kq
+    s = w.sublayers[0]
+    HG0 = kq.kronq_gram(path.Gd)
+    HX0 = kq.kronq_gram(path.Xd)
+    W = path.W0.clone()
+    HG1, HX1 = HG0.clone(), HX0.clone()
+    kq.kronq_biip_rotate(W, HX1, HG1, path.si, s.in_block, path.so, s.out_block, w.alpha)
+    lib = kq.load()
+    ws = torch.empty(lib.kronq_incoherence_ws(max(s.m, s.n)), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, H in (("hg_before", HG0), ("hg_after_biip", HG1), ("hx_before", HX0), ("hx_after_biip", HX1)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = kq.kronq_incoherence(H, ws=ws)
+        res[name] = {"mu_over_sqrt_d": r["mu"], "sweeps": r["sweeps"],
+                     "ms": (time.perf_counter() - t0) * 1e3}
+    return {"workload": w.name, "d": [s.m, s.n], "tol": 1e-13, **res}
+
+
 def gptaq_leg(w, path, dev, steps=5):
     """The asymmetric correction on the Llama-2-7B q_proj shape: the drift term
     (X_fp - X)^T X / N from a drifted input stream, its input-side rotation, P,
@@ -796,6 +818,7 @@ def main():
                             "cv_out_after_biip": cv_after[1], "ms_per_call": cv_ms,
                             "gbs": 4.0 * m * n / (cv_ms * 1e-3) / 1e9,
                             "frac_hbm_peak": 4.0 * m * n / (cv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        out["incoherence"] = incoherence_leg(w2, p2[0], dev)
         del p2
         torch.cuda.empty_cache()
     if not args.no_decode:
