@@ -593,6 +593,7 @@ def run_workload(w, steps, warmup, dev):
 def incoherence_leg(w, path, dev):
     """mu(H)/sqrt(d) of H_G and H_X before and after BiIP (the incoherence
     diagnostic), with the time of one call at d = 4096."""
+    import torch
     kq = path.kq
     s = w.sublayers[0]
     HG0 = kq.kronq_gram(path.Gd)
