@@ -607,7 +607,11 @@ def incoherence_leg(w, path, dev):
     for name, H in (("hg_before", HG0), ("hg_after_biip", HG1), ("hx_before", HX0), ("hx_after_biip", HX1)):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        r = kq.kronq_incoherence(H, ws=ws)
+        try:
+            r = kq.kronq_incoherence(H, ws=ws)
+        except kq.KronqError as e:   # reported, not fatal: a diagnostic leg
+            res[name] = {"error": str(e)}
+            continue
         res[name] = {"mu_over_sqrt_d": r["mu"], "sweeps": r["sweeps"],
                      "ms": (time.perf_counter() - t0) * 1e3}
     return {"workload": w.name, "d": [s.m, s.n], "tol": 1e-13, **res}
