@@ -29,7 +29,8 @@
 // aligned and the low-bit rounds are bank-conflict free.  The forward
 // transform of W, H_X and H_G runs as two persistent launches, pass 1 of all
 // three and then pass 2 of all three (biip_pass1m / biip_pass2m); the
-// inverse and widths that are not a multiple of 4 run one matrix at a time.
+// inverse, widths that are not a multiple of 4 and large problems (more than
+// kMergeMaxTiles pass-1 tiles) run one matrix at a time.
 #include "kronq_internal.h"
 #include "wht_lds.h"
 
@@ -765,11 +766,22 @@ kronq_status launch2d(const Plan& pl, hipStream_t st) {
 
 // forward transforms of n <= 3 matrices: the merged persistent passes when
 // every matrix takes the vector path, else one matrix at a time
+// Up to this many pass-1 tiles in all, the merged persistent passes are
+// faster; above it a launch per matrix and pass is (measured, W + H_X + H_G:
+// 4096^2 0.162 ms merged against 0.200 per matrix, 1024 x 4096 0.085 against
+// 0.121; 4096 x 11008 (11172 tiles) 0.723 against 0.617, 14336 x 4096 1.034
+// against 0.895, 28672 x 8192 and 8192 x 28672 6.12 against 4.01-4.07).
+constexpr int64_t kMergeMaxTiles = 4096;
+
 kronq_status launch_forward(const Plan* pl, int n, hipStream_t st) {
   bool merged = n > 0;
-  for (int k = 0; k < n; ++k)
+  int64_t all1 = 0;
+  for (int k = 0; k < n; ++k) {
     merged = merged && !pl[k].p.post && pl[k].p.row.fac && pl[k].vec1 &&
              (pl[k].vec2 || pl[k].p.tiles2 == 0);
+    all1 += pl[k].p.tiles1;
+  }
+  merged = merged && all1 <= kMergeMaxTiles;
   if (!merged) {
     for (int k = 0; k < n; ++k) {
       const kronq_status s = launch2d(pl[k], st);
