@@ -805,32 +805,39 @@ constexpr int OLD = OKS + 8;        // padded LDS row (bf16 elements)
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 
-// round-to-nearest-even bf16 bits of a finite fp32 value
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 values -> two bf16 rounded to nearest (one v_cvt_pk_bf16_f32),
+// packed low then high
+__device__ __forceinline__ uint32_t pack_bf16(f32x2_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// the two bf16 of a packed word, widened (exactly) to fp32
+__device__ __forceinline__ f32x2_t unpack_bf16(uint32_t u) {
+  return f32x2_t{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
 }
 
-// x = x1 + x2 + x3 exactly (each remainder is exact in fp32)
-__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
-  h = bf16_bits(x);
-  const float r1 = x - __uint_as_float(h << 16);
-  m = bf16_bits(r1);
-  const float r2 = r1 - __uint_as_float(m << 16);
-  l = bf16_bits(r2);
+// a pair x = x1 + x2 + x3 exactly, each part packed for the pair (each
+// remainder is exact in fp32): 11 VALU operations for two values, where the
+// rounding done in integer arithmetic took about 40
+__device__ __forceinline__ void split3_pair(f32x2_t x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = pack_bf16(x);
+  const f32x2_t r1 = x - unpack_bf16(h);
+  m = pack_bf16(r1);
+  const f32x2_t r2 = r1 - unpack_bf16(m);
+  l = pack_bf16(r2);
 }
 
 // four consecutive-k values of one row or column -> its three bf16 parts,
 // 8 bytes each, at dst[part * 128 * OLD]
 __device__ __forceinline__ void put_split4(unsigned short* dst, float x0, float x1, float x2, float x3) {
-  uint32_t h[4], m[4], l[4];
-  split3(x0, h[0], m[0], l[0]);
-  split3(x1, h[1], m[1], l[1]);
-  split3(x2, h[2], m[2], l[2]);
-  split3(x3, h[3], m[3], l[3]);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  *reinterpret_cast<uint2*>(dst + NB * OLD) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
-  *reinterpret_cast<uint2*>(dst + 2 * NB * OLD) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  uint32_t h0, m0, l0, h1, m1, l1;
+  split3_pair(f32x2_t{x0, x1}, h0, m0, l0);
+  split3_pair(f32x2_t{x2, x3}, h1, m1, l1);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2*>(dst + NB * OLD) = make_uint2(m0, m1);
+  *reinterpret_cast<uint2*>(dst + 2 * NB * OLD) = make_uint2(l0, l1);
 }
 
 __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0, CholWs w) {
