@@ -60,6 +60,9 @@ struct CholWs {
   int* nonfinite; // nonzero when H (or the damping term) holds a NaN or infinity
   long long* info;
   int64_t sP;     // floats between consecutive Lp (and Yp) buffers (NBO of each)
+  unsigned short* Ls;  // two-level sweep: the bf16 parts of the outer block's L
+                       // panels, k-major: [slot][k / 32][part][k % 32][row]
+  unsigned short* Ys;  // and of its Y panels: [slot][k / 32][part][k % 32][column]
 };
 
 // buffer of parity `par` of a double-buffered array
@@ -92,6 +95,13 @@ size_t ws_layout(int64_t n, CholWs* w, void* base) {
   off += 256;
   if (w) w->nonfinite = reinterpret_cast<int*>(b + off);
   off += 256;
+  if (npad / NB >= kTwoLevelMinPanels) {
+    const size_t sS = align_up((size_t)NBO * 3 * npad * NB * sizeof(unsigned short), 256);
+    if (w) w->Ls = reinterpret_cast<unsigned short*>(b + off);
+    off += sS;
+    if (w) w->Ys = reinterpret_cast<unsigned short*>(b + off);
+    off += sS;
+  }
   return off;
 }
 
@@ -792,14 +802,14 @@ __global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
 // Six v_mfma_f32_32x32x16_bf16 (32 cycles each) replace eight
 // v_mfma_f32_32x32x2f32 (64 cycles each) per 32 x 32 x 16 step.
 //
-// One 128 x 128 output tile per workgroup (four waves as 2 x 2, each 64 x 64
-// as 2 x 2 accumulator pairs), K staged 32 at a time: the fp32 values of the
-// next stage are loaded into registers while the current one is multiplied,
-// then split and stored to LDS as bf16 rows [part][row or column][k] (80-byte
-// rows: the 16-byte operand reads of 16 consecutive rows hit distinct banks;
-// two 8-byte reads over 72-byte rows measured 3% slower).  The loop waits on
-// its operand loads: at n = 28672 waves spend 43% of their cycles waiting,
-// the matrix cores are busy 38% of the time and L2 hits 59% of requests.
+// The split is made once per outer block (chol_presplit: every panel feeds
+// all the tiles of its row or column block, which split it again each when
+// the tiles split their own operands).  One 128 x 128 output tile per
+// workgroup (four waves as 2 x 2, each 64 x 64 as 2 x 2 accumulator pairs),
+// K staged 32 at a time: the bf16 parts of the next stage are loaded into
+// registers while the current one is multiplied, then copied to LDS as rows
+// [part][row or column][k] (80-byte rows: the 16-byte operand reads of 16
+// consecutive rows hit distinct banks).
 constexpr int OKS = 32;             // K per stage
 constexpr int OLD = OKS + 8;        // padded LDS row (bf16 elements)
 
@@ -829,35 +839,118 @@ __device__ __forceinline__ void split3_pair(f32x2_t x, uint32_t& h, uint32_t& m,
   l = pack_bf16(r2);
 }
 
-// four consecutive-k values of one row or column -> its three bf16 parts,
-// 8 bytes each, at dst[part * 128 * OLD]
-__device__ __forceinline__ void put_split4(unsigned short* dst, float x0, float x1, float x2, float x3) {
+// The bf16 parts of an outer block's panels, made once for all of its outer
+// update's tiles (each panel feeds every tile of its row or column block),
+// k-major like Y: [slot][k / 32][part][k % 32][row or column], so that a
+// tile's stage holds, per part and k, 256 contiguous bytes of its 128 rows.
+// L slot q rows r0 .. npad - 1 (transposed through LDS, 32 rows a
+// workgroup: workgroups [0, nL)); Y slot q columns 0 .. c1 - 1 (already
+// k-major: 1024 columns of one k a workgroup).
+__device__ __forceinline__ int64_t kmaj_at(int64_t npad, int q, int part, int k, int64_t row) {
+  return ((int64_t)((q * (NB / 32) + k / 32) * 3 + part) * 32 + (k % 32)) * npad + row;
+}
+
+__global__ void __launch_bounds__(256) chol_presplit(int64_t npad, int64_t r0, int64_t c1, int nL,
+                                                     CholWs w) {
+  if (*w.flag) return;
+  __shared__ float tile[32][NB + 1];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < nL) {
+    const int64_t ntiles = (npad - r0) / 32;   // npad - r0 is a multiple of NB
+    const int q = (int)(blockIdx.x / ntiles);
+    const int64_t row0 = r0 + (blockIdx.x % ntiles) * 32;
+    const float* src = lp_buf(w, q) + row0 * NB;
+    // 32 rows x 128 k: float4 u of a thread is row tid / 8, k (tid % 8) * 16 + 4 u
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = tid >> 3, k = (tid & 7) * 16 + 4 * u;
+      const float4 x = *reinterpret_cast<const float4*>(src + r * NB + k);
+      tile[r][k] = x.x;
+      tile[r][k + 1] = x.y;
+      tile[r][k + 2] = x.z;
+      tile[r][k + 3] = x.w;
+    }
+    __syncthreads();
+    // k = tid % 128, rows (tid / 128) * 16 .. + 15: eight pairs of rows
+    const int k = tid & (NB - 1), rb = (tid >> 7) * 16;
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      split3_pair(f32x2_t{tile[rb + 2 * v][k], tile[rb + 2 * v + 1][k]}, h[v], m[v], l[v]);
+    const uint32_t* pp[3] = {h, m, l};
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      unsigned short* dst = w.Ls + kmaj_at(npad, q, part, k, row0 + rb);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pp[part][0], pp[part][1], pp[part][2], pp[part][3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pp[part][4], pp[part][5], pp[part][6], pp[part][7]);
+    }
+    return;
+  }
+  // Y: 1024 consecutive columns of one k of slot q, four a thread
+  const int64_t b = blockIdx.x - nL;
+  const int64_t nch = (c1 + 1023) / 1024;
+  const int q = (int)(b / (NB * nch));
+  const int k = (int)((b / nch) % NB);
+  const int64_t col = (b % nch) * 1024 + 4 * tid;
+  if (col >= c1) return;
+  const float4 x = *reinterpret_cast<const float4*>(yp_buf(w, q) + (int64_t)k * npad + col);
   uint32_t h0, m0, l0, h1, m1, l1;
-  split3_pair(f32x2_t{x0, x1}, h0, m0, l0);
-  split3_pair(f32x2_t{x2, x3}, h1, m1, l1);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(h0, h1);
-  *reinterpret_cast<uint2*>(dst + NB * OLD) = make_uint2(m0, m1);
-  *reinterpret_cast<uint2*>(dst + 2 * NB * OLD) = make_uint2(l0, l1);
+  split3_pair(f32x2_t{x.x, x.y}, h0, m0, l0);
+  split3_pair(f32x2_t{x.z, x.w}, h1, m1, l1);
+  *reinterpret_cast<uint2*>(w.Ys + kmaj_at(npad, q, 0, k, col)) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2*>(w.Ys + kmaj_at(npad, q, 1, k, col)) = make_uint2(m0, m1);
+  *reinterpret_cast<uint2*>(w.Ys + kmaj_at(npad, q, 2, k, col)) = make_uint2(l0, l1);
+}
+
+// chunk swizzle {0, 6, 12, 10}[k % 4] of the 16-byte chunks of an LDS k-row:
+// the transposing operand reads of 16 lanes (4 values of k x 16 rows) then
+// fall on distinct banks
+__device__ __forceinline__ int ko_swz(int k) { return (0xAC60 >> (4 * (k & 3))) & 15; }
+
+typedef short ko_i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) ko_i16x4_t ko_lds_i16x4_t;
+
+// 4 values of k of one row, transposed out of the k-major stage
+__device__ __forceinline__ ko_i16x4_t ko_ld(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((ko_lds_i16x4_t*)p);
 }
 
 __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0, CholWs w) {
   if (*w.flag) return;
-  __shared__ __align__(16) unsigned short As[3 * NB * OLD];
-  __shared__ __align__(16) unsigned short Bs[3 * NB * OLD];
+  // a stage of one operand: [part][k][128 rows] bf16, 24 KB
+  __shared__ __align__(16) unsigned short As[3 * OKS * NB];
+  __shared__ __align__(16) unsigned short Bs[3 * OKS * NB];
   const int b1 = b0 + NBO;
-  int t = blockIdx.x;
+  // Tiles in 8 x 8 super-tiles, one super-tile per XCD at a time: workgroup
+  // b runs on XCD b % 8, so its slot b / 8 on that XCD takes tile b / 8 % 64
+  // of super-tile 8 (b / 512) + b % 8.  The 64 workgroups an XCD holds then
+  // share 8 row blocks and 8 column blocks of operands in its L2 (in launch
+  // order they were 64 row blocks of one column block).  Super-tiles: the
+  // SYRK triangle (i >= j >= b1) by super-rows, then the fwd rectangle
+  // (i >= b1, c < b1); tiles outside them (past the edges, above the
+  // diagonal, and the padding of the super-tile count to a multiple of 8)
+  // exit at once.
   const int q2 = P - b1;
-  const int nsyrk = q2 * (q2 + 1) / 2;
-  const bool fwd = t >= nsyrk;
+  const int T = (q2 + 7) / 8, Cs = (b1 + 7) / 8;
+  const int nsS = T * (T + 1) / 2;
+  const int slot = blockIdx.x / 8;
+  const int st = 8 * (slot / 64) + blockIdx.x % 8;
+  const int di = (slot % 64) / 8, dj = slot % 8;
+  const bool fwd = st >= nsS;
   int i, j, qlo = 0;
   if (!fwd) {
-    j = b1;
-    while (t >= P - j) { t -= P - j; ++j; }
-    i = j + t;
+    int si = 0;
+    while ((si + 1) * (si + 2) / 2 <= st) ++si;
+    const int sj = st - si * (si + 1) / 2;
+    i = b1 + 8 * si + di;
+    j = b1 + 8 * sj + dj;
+    if (i >= P || j > i) return;
   } else {
-    t -= nsyrk;
-    i = b1 + t / b1;
-    j = t % b1;                       // the column block c of B
+    const int sp = st - nsS;
+    if (sp >= T * Cs) return;
+    i = b1 + 8 * (sp / Cs) + di;
+    j = 8 * (sp % Cs) + dj;           // the column block c of B
+    if (i >= P || j >= b1) return;
     qlo = j > b0 ? j - b0 : 0;        // panels b0 + q >= c
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -874,67 +967,92 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
         lo[a][b][v] = 0.f;
       }
   const int k_lo = qlo * NB, k_hi = NBO * NB;
-  float4 ra[4], rb[4];
-  // stage at k0 (32 values of k): A element (r, k) = L_i,b0+q[r][kk]; B
-  // element (col, k) = L_j,b0+q[col][kk] (SYRK) or (k, col) =
-  // Y_b0+q[kk][c NB + col] (fwd), with q = k / NB, kk = k % NB; panel q sits
-  // in slot q of the buffers (b0 is a multiple of NBO).  Float4 u of a thread
-  // is row (tid + 256 u) / 8, k quad (tid + 256 u) % 8 (A, SYRK B), or, for
-  // the fwd B, k row 4 (tid % 8) + u of column quad tid / 8 (a 4 x 4 block
-  // that the store transposes: eight lanes write 64 contiguous bytes of one
-  // column and the next eight lanes the column four further on, 320 bytes =
-  // 64 bytes mod 256 away, so 32 lanes cover every bank once).
-  auto load = [&](int k0) {
-    const int q = k0 / NB, kk0 = k0 % NB;
-    const float* La = lp_buf(w, q) + (int64_t)i * NB * NB + kk0;
-    const float* Lb = lp_buf(w, q) + (int64_t)j * NB * NB + kk0;
-    const float* Yb = yp_buf(w, q) + (int64_t)kk0 * npad + (int64_t)j * NB;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e >> 3, k4 = (e & 7) * 4;
-      ra[u] = *reinterpret_cast<const float4*>(La + (int64_t)r * NB + k4);
-      if (!fwd) rb[u] = *reinterpret_cast<const float4*>(Lb + (int64_t)r * NB + k4);
-      else rb[u] = *reinterpret_cast<const float4*>(Yb + (int64_t)(4 * (tid & 7) + u) * npad + (tid >> 3) * 4);
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e >> 3, k4 = (e & 7) * 4;
-      put_split4(As + r * OLD + k4, ra[u].x, ra[u].y, ra[u].z, ra[u].w);
-      if (!fwd) put_split4(Bs + r * OLD + k4, rb[u].x, rb[u].y, rb[u].z, rb[u].w);
-    }
-    if (fwd) {
-      const int c0 = (tid >> 3) * 4, kq = 4 * (tid & 7);
-      put_split4(Bs + (c0 + 0) * OLD + kq, rb[0].x, rb[1].x, rb[2].x, rb[3].x);
-      put_split4(Bs + (c0 + 1) * OLD + kq, rb[0].y, rb[1].y, rb[2].y, rb[3].y);
-      put_split4(Bs + (c0 + 2) * OLD + kq, rb[0].z, rb[1].z, rb[2].z, rb[3].z);
-      put_split4(Bs + (c0 + 3) * OLD + kq, rb[0].w, rb[1].w, rb[2].w, rb[3].w);
-    }
-  };
-  load(k_lo);
-  store();
+  // stage at k0 (32 values of k) from the split panels: A rows i NB .. + 127
+  // of L_b0+q, B rows j NB .. + 127 of L_b0+q (SYRK) or columns j NB .. +
+  // 127 of Y_b0+q (fwd), with q = k0 / NB (panel q in slot q: b0 is a
+  // multiple of NBO).  A thread's six 16-byte chunks (8 rows at one k of one
+  // part) are rows 8 (tid % 16) .. + 7 at k tid / 16 and tid / 16 + 16 of
+  // each part; 16 lanes store one k-row of 256 bytes, chunks swizzled.
+  // (plain code over named registers: as arrays captured by a helper lambda
+  // the staging registers went to scratch memory)
+  const unsigned short* Lbase = w.Ls;
+  const unsigned short* Bbase = fwd ? w.Ys : w.Ls;
+  const int64_t ri = (int64_t)i * NB + 8 * (tid & 15), rj = (int64_t)j * NB + 8 * (tid & 15);
+  const int kt = tid >> 4;
+  const int64_t gk = (int64_t)16 * npad;   // 16 k-rows on
+  const int64_t gp = (int64_t)32 * npad;   // the next part
+  const int o0 = kt * NB * 1 + ((((tid & 15)) ^ ko_swz(kt)) << 3);   // bf16 units, k = kt
+  const int o1 = o0 + 16 * NB;                                          // k = kt + 16 (same swizzle)
+  uint4 a0, a1, a2, a3, a4, a5, c0, c1, c2, c3, c4, c5;
+#define KQ_OUTER_LOAD(k0)                                                          \
+  {                                                                                \
+    const unsigned short* La = Lbase + kmaj_at(npad, (k0) / NB, 0, (k0) % NB + kt, ri); \
+    const unsigned short* Lb = Bbase + kmaj_at(npad, (k0) / NB, 0, (k0) % NB + kt, rj); \
+    a0 = *reinterpret_cast<const uint4*>(La);                                      \
+    a1 = *reinterpret_cast<const uint4*>(La + gk);                                 \
+    a2 = *reinterpret_cast<const uint4*>(La + gp);                                 \
+    a3 = *reinterpret_cast<const uint4*>(La + gp + gk);                            \
+    a4 = *reinterpret_cast<const uint4*>(La + 2 * gp);                             \
+    a5 = *reinterpret_cast<const uint4*>(La + 2 * gp + gk);                        \
+    c0 = *reinterpret_cast<const uint4*>(Lb);                                      \
+    c1 = *reinterpret_cast<const uint4*>(Lb + gk);                                 \
+    c2 = *reinterpret_cast<const uint4*>(Lb + gp);                                 \
+    c3 = *reinterpret_cast<const uint4*>(Lb + gp + gk);                            \
+    c4 = *reinterpret_cast<const uint4*>(Lb + 2 * gp);                             \
+    c5 = *reinterpret_cast<const uint4*>(Lb + 2 * gp + gk);                        \
+  }
+#define KQ_OUTER_STORE()                                                           \
+  {                                                                                \
+    *reinterpret_cast<uint4*>(As + o0) = a0;                                       \
+    *reinterpret_cast<uint4*>(As + o1) = a1;                                       \
+    *reinterpret_cast<uint4*>(As + OKS * NB + o0) = a2;                            \
+    *reinterpret_cast<uint4*>(As + OKS * NB + o1) = a3;                            \
+    *reinterpret_cast<uint4*>(As + 2 * OKS * NB + o0) = a4;                        \
+    *reinterpret_cast<uint4*>(As + 2 * OKS * NB + o1) = a5;                        \
+    *reinterpret_cast<uint4*>(Bs + o0) = c0;                                       \
+    *reinterpret_cast<uint4*>(Bs + o1) = c1;                                       \
+    *reinterpret_cast<uint4*>(Bs + OKS * NB + o0) = c2;                            \
+    *reinterpret_cast<uint4*>(Bs + OKS * NB + o1) = c3;                            \
+    *reinterpret_cast<uint4*>(Bs + 2 * OKS * NB + o0) = c4;                        \
+    *reinterpret_cast<uint4*>(Bs + 2 * OKS * NB + o1) = c5;                        \
+  }
+  // operand reads (the layout of v_mfma_f32_32x32x16_bf16: lane l takes row
+  // l % 32 of the operand tile, k 8 (l / 32) .. + 7): within each 16 lanes,
+  // lane jj addresses k kr = 8 (g / 2) + jj / 4 (+ 4 for the second read) and
+  // rows fo = 16 (g % 2) + 4 (jj % 4) .. + 3 of the 32-row tile, g = lane / 16;
+  // lane jj then receives 4 values of k of row 16 (g % 2) + jj.  The swizzle
+  // of kr is that of kr + 4 and of kr + 16.
+  const int rg = lane >> 4, rjj = lane & 15;
+  const int kr = 8 * (rg >> 1) + (rjj >> 2);
+  const int fo = 16 * (rg & 1) + 4 * (rjj & 3);
+  auto rd_off = [&](int row) { return kr * NB + (((row >> 3) ^ ko_swz(kr)) << 3) + (row & 7); };
+  const int rdA0 = rd_off(wm * 64 + fo), rdA1 = rd_off(wm * 64 + 32 + fo);
+  const int rdB0 = rd_off(wn * 64 + fo), rdB1 = rd_off(wn * 64 + 32 + fo);
+  KQ_OUTER_LOAD(k_lo)
+  KQ_OUTER_STORE()
   __syncthreads();
   for (int k0 = k_lo; k0 < k_hi; k0 += OKS) {
     const bool more = k0 + OKS < k_hi;
-    if (more) load(k0 + OKS);
+    if (more) KQ_OUTER_LOAD(k0 + OKS)
 #pragma unroll
     for (int ks = 0; ks < OKS; ks += 16) {
       bf16x8_t af[2][3], bf[2][3];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int pt = 0; pt < 3; ++pt)
-          af[a][pt] = *reinterpret_cast<const bf16x8_t*>(As + pt * NB * OLD + (wm * 64 + 32 * a + lr) * OLD +
-                                                          ks + 8 * lk);
+        for (int pt = 0; pt < 3; ++pt) {
+          const unsigned short* q = As + pt * OKS * NB + ks * NB + (a ? rdA1 : rdA0);
+          af[a][pt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ko_ld(q), ko_ld(q + 4 * NB), 0, 1, 2,
+                                                                           3, 4, 5, 6, 7));
+        }
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int pt = 0; pt < 3; ++pt)
-          bf[b][pt] = *reinterpret_cast<const bf16x8_t*>(Bs + pt * NB * OLD + (wn * 64 + 32 * b + lr) * OLD +
-                                                          ks + 8 * lk);
+        for (int pt = 0; pt < 3; ++pt) {
+          const unsigned short* q = Bs + pt * OKS * NB + ks * NB + (b ? rdB1 : rdB0);
+          bf[b][pt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ko_ld(q), ko_ld(q + 4 * NB), 0, 1, 2,
+                                                                           3, 4, 5, 6, 7));
+        }
       // term order: each group of four MFMAs updates four different
       // accumulators
 #pragma unroll
@@ -955,10 +1073,12 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
     }
     __syncthreads();
     if (more) {
-      store();
+      KQ_OUTER_STORE()
       __syncthreads();
     }
   }
+#undef KQ_OUTER_LOAD
+#undef KQ_OUTER_STORE
   // C -= hi + lo, every old value of an accumulator tile loaded before its stores
   float* C = (fwd ? w.B : w.A) + (int64_t)i * NB * npad + (int64_t)j * NB;
 #pragma unroll
@@ -1063,8 +1183,15 @@ kronq_status chol_launch(const float* H, int64_t n, int64_t ldh, float lambda, i
     } else if (p < P - 1) {
       // p ends its outer block b0 .. p (two-level only)
       const int b0 = p - NBO + 1, b1 = p + 1, q2 = P - b1;
-      const int tiles = q2 * (q2 + 1) / 2 + q2 * b1;
-      hipLaunchKernelGGL(chol_outer, dim3((unsigned)tiles), dim3(256), 0, s, npad, P, b0, w);
+      const int64_t r0 = (int64_t)b1 * NB, c1 = (int64_t)b1 * NB;
+      const int nL = (int)(NBO * ((npad - r0) / 32));
+      const int nY = (int)(NBO * NB * ((c1 + 1023) / 1024));
+      hipLaunchKernelGGL(chol_presplit, dim3((unsigned)(nL + nY)), dim3(256), 0, s, npad, r0, c1, nL, w);
+      KQ_LAUNCHED("chol_presplit");
+      // whole 8 x 8 super-tiles, their count padded to a multiple of 8 (see chol_outer)
+      const int T = (q2 + 7) / 8, Cs = (b1 + 7) / 8;
+      const int nsup = (T * (T + 1) / 2 + T * Cs + 7) / 8 * 8;
+      hipLaunchKernelGGL(chol_outer, dim3((unsigned)(nsup * 64)), dim3(256), 0, s, npad, P, b0, w);
       KQ_LAUNCHED("chol_outer");
     }
   }
