@@ -47,7 +47,7 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 constexpr int NB = 128;
 constexpr int KS = 32;        // K rows per LDS stage
 constexpr int NBO = 4;        // panels of an outer block (two-level sweep)
-constexpr int kTwoLevelMinPanels = 72;   // two-level from n > 9088 on (measured crossover)
+constexpr int kTwoLevelMinPanels = 64;   // two-level from n > 8064 on (measured crossover)
 
 struct CholWs {
   float* A;       // npad x npad (reversed, permuted, damped)

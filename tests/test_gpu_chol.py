@@ -95,12 +95,13 @@ def test_chol_full_size_llama2_7b_q_proj():
     assert fe <= 1e-3
 
 
-@pytest.mark.parametrize("n,act", [(9300, False), (10240, True)])
+@pytest.mark.parametrize("n,act", [(8192, False), (9300, False), (10240, True)])
 def test_chol_two_level_sweep(n, act):
-    """From 72 panels of 128 on, the sweep is two-level: outer blocks of four
-    panels whose rank-512 update covers the trailing matrix at once.  9300 ends
-    in a partial outer block of one panel (no outer update after it); 10240
-    with act-order runs twenty full blocks."""
+    """From 64 panels of 128 on, the sweep is two-level: outer blocks of four
+    panels whose rank-512 update covers the trailing matrix at once.  8192 is
+    the smallest such size (sixteen full blocks); 9300 ends in a partial outer
+    block of one panel (no outer update after it); 10240 with act-order runs
+    twenty full blocks."""
     say("chol two-level", n, act)
     H = spd_from_gram(69 + n, n, N=2 * n).astype(np.float32)
     R, perm, info = kq.kronq_chol_inv(to_dev_f32(H), 0.01, act)
