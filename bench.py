@@ -74,6 +74,9 @@ def parse():
                     help="only turn four rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and "
                          "WRITE_SIZE of this benchmark, then of --copy-probe) into the traffic file "
                          "(--traffic-json) and exit")
+    ap.add_argument("--library-gram", metavar="D[,D...]", default="",
+                    help="only time kronq_gram against the vendor GEMM (torch.mm, hipBLASLt) on the "
+                         "same bf16 262144 x D operand, for each D, and exit")
     ap.add_argument("--copy-bytes", type=int, default=256 * 1024 * 1024,
                     help="BYTES the copy-probe runs used (for --summarize-traffic)")
     return ap.parse_args()
@@ -98,6 +101,52 @@ def copy_probe(nbytes):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 5}), flush=True)
+
+
+def library_gram(dims, reps=3):
+    """kronq_gram beside the vendor GEMM on one bf16 operand A (262144 x d):
+    kronq_gram forms the unique triangle of A^T A (N d (d + 1) flops), torch.mm
+    the full product of a transposed copy with A (2 N d^2 flops).  Both rates
+    are useful flops per second, so equal rates mean equal efficiency."""
+    import torch
+    import post_quantization_02_amd as kq
+    dev = torch.device("cuda:0")
+    kq.load()
+    N = 262144
+    rows = []
+    for d in dims:
+        log("library gram d", d)
+        g = torch.Generator(device=dev)
+        g.manual_seed(d)
+        A = torch.randn((N, d), device=dev, dtype=torch.bfloat16, generator=g)
+        At = A.t().contiguous()
+        H = torch.empty((d, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(kq.load().kronq_gram_ws(N, d, kq.KRONQ_BF16), dtype=torch.uint8, device=dev)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms_k = timed(lambda: kq.kronq_gram(A, H, ws=ws))
+        ms_l = timed(lambda: torch.mm(At, A))
+        fk, fl = float(N) * d * (d + 1), 2.0 * N * d * d
+        rows.append({"d": d, "N": N, "kronq_gram_ms": ms_k, "kronq_gram_tflops": fk / ms_k / 1e9,
+                     "kronq_gram_frac": fk / ms_k / 1e9 / PEAK_BF16_TFLOPS, "torch_mm_ms": ms_l,
+                     "torch_mm_tflops": fl / ms_l / 1e9,
+                     "torch_mm_frac": fl / ms_l / 1e9 / PEAK_BF16_TFLOPS})
+        log("  kronq_gram %.2f ms (%.0f TF/s)  torch.mm %.2f ms (%.0f TF/s)" %
+            (ms_k, rows[-1]["kronq_gram_tflops"], ms_l, rows[-1]["torch_mm_tflops"]))
+        del A, At, H, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"library_gram": rows, "reps": reps, "dtype": "bf16",
+                      "data": "synthetic N(0,1) (seeded torch generator)"}), flush=True)
 
 
 def _pmc_groups(path, kernel_pred, counter):
@@ -692,6 +741,9 @@ def main():
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.library_gram:
+        library_gram([int(x) for x in args.library_gram.split(",")])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library runs the whole path on a single MI355X "

@@ -433,13 +433,25 @@ __device__ __forceinline__ void pb_load(PBatch& B, const double* Eg, const float
   for (int s = 0; s < 8; ++s) B.r[s] = *reinterpret_cast<const f32x4_t*>(r + s * ldr);
 }
 
+// The batch's 32 R values are widened first, into registers of their own, and
+// only then fed to the matrix cores.  Widened one at a time beside its MFMA,
+// each value went to the one register that the MFMA issued just before was
+// still reading, and every widening waited for that MFMA: about 28 cycles lost
+// per 64-cycle MFMA (down_proj's loop at n = 28672: 129 ms this way against
+// 117 ms widened first, codes identical).
 __device__ __forceinline__ void pb_mma(const PBatch& B, f64x4_t (&acc)[4]) {
+  double cv[8][4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cv[s][t] = (double)B.r[s][t];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const double a = B.e[s >> 1][s & 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)B.r[s][t], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, cv[s][t], acc[t], 0, 0, 0);
   }
 }
 
