@@ -385,13 +385,20 @@ __device__ __forceinline__ int v2_opaque(int x) {
 // Stages here are always whole (the host hands a token tail shorter than a
 // stage to the generic kernel), so a load is a uniform base plus the lane's
 // fixed 32-bit offset.
+// The lane offset is added as an unsigned 32-bit value (it is below 2^32: a
+// row within the stage times the row pitch), so each load takes the form with a
+// scalar 64-bit base and a 32-bit vector offset.  Added as a signed value it
+// was sign-extended into a 64-bit vector address, three VALU instructions per
+// load between the MFMAs whose results landed in registers that the MFMAs just
+// issued were still reading (the d = 28672 call: 190 ms that way, 182 ms this
+// way, results identical).
 template <int SLOT, int PN>
 __device__ __forceinline__ void v2_issue_panel(const V2Ctx& c, int64_t tok0) {
   unsigned char* lbase = v2_panel<SLOT, PN>() + c.wave * 4 * 2 * V2ROW;
   const unsigned char* gbase = (PN ? c.gJ : c.gI) + tok0 * c.row_bytes;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_global_load_lds((const void*)(gbase + v2_opaque(c.ldoff[q])),
+    __builtin_amdgcn_global_load_lds((const void*)(gbase + (uint32_t)v2_opaque(c.ldoff[q])),
                                      (lds_void_t*)(lbase + q * 2 * V2ROW), 16, 0, 0);
 }
 
