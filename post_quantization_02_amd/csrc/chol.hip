@@ -310,27 +310,46 @@ __device__ __forceinline__ void wave_sync_lds() {
 // The two columns of a step reach every lane through LDS: col2 holds two
 // buffers of 2 x SB doubles, step j's columns in buffer (j / 2) % 2, so that
 // the S lanes can publish the next step's columns while this step's are still
-// being read.  Each lane reads a column entry just before its update, kPre
-// entries ahead, so the routine holds no copy of the columns.  It stays out
-// of line: inlined into the kernel, the register allocation spills.
+// being read, and behind them two buffers that only the M lanes write to (no
+// lane reads them), so that the publishing store needs no branch.  Each lane
+// reads a column entry just before its update, kPre entries ahead, so the
+// routine holds no copy of the columns.  All LDS accesses go through LDS-typed
+// pointers off one base register (the buffers lie past the 64 KiB an
+// immediate offset reaches from address zero; addressed one by one they cost
+// a register move per read).  The routine stays out of line: inlined into the
+// kernel, the register allocation spills.
 constexpr int kPre = 8;
 
-__device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
+typedef __attribute__((address_space(3))) double lds_f64;
+typedef __attribute__((address_space(3))) f64x2_t lds_f64x2;
+
+__device__ __noinline__ int diag_factor32(double* Sk_, double* col2_) {
   const int l = threadIdx.x & 63, r = l & 31;
   const bool isS = l < 32;
+  lds_f64* Sk = (lds_f64*)Sk_;
+  // one base register for every column access (the buffers sit past the
+  // 64 KiB reach of a read's immediate offset from address zero)
+  unsigned cb = (unsigned)(size_t)(lds_f64*)col2_;
+  asm volatile("" : "+v"(cb));
+  lds_f64* col2 = (lds_f64*)(size_t)cb;
+  // the M half publishes into two further, unread buffers (col2 + 4 SB ..
+  // col2 + 8 SB), so the stores need no branch
+  lds_f64* pub = col2 + (isS ? 0 : 4 * SB) + 2 * r;
   double v[SB];
 #pragma unroll
-  for (int k = 0; k < SB; ++k) v[k] = isS ? Sk[r * LDB + k] : (k == r ? 1.0 : 0.0);
-  if (isS) *reinterpret_cast<f64x2_t*>(col2 + 2 * r) = f64x2_t{v[0], v[1]};
+  for (int k = 0; k < SB; ++k) v[k] = Sk[r * LDB + k];
+#pragma unroll
+  for (int k = 0; k < SB; ++k) v[k] = isS ? v[k] : (k == r ? 1.0 : 0.0);
+  *(lds_f64x2*)pub = f64x2_t{v[0], v[1]};
   wave_sync_lds();
   // this step's pivot entries (S_jj, S_j+1,j; S_j+1,j+1)
-  f64x2_t pv0 = *reinterpret_cast<const f64x2_t*>(col2);
-  f64x2_t pv1 = *reinterpret_cast<const f64x2_t*>(col2 + 2);
+  f64x2_t pv0 = *(const lds_f64x2*)(col2);
+  f64x2_t pv1 = *(const lds_f64x2*)(col2 + 2);
   int bad = -1;
 #pragma unroll
   for (int j = 0; j < SB; j += 2) {
-    const double* cur = col2 + ((j / 2) & 1) * 2 * SB;
-    double* nxt = col2 + (((j / 2) + 1) & 1) * 2 * SB;
+    const lds_f64* cur = col2 + ((j / 2) & 1) * 2 * SB;
+    const int nxo = (((j / 2) + 1) & 1) * 2 * SB;
     double d0 = pv0[0];
     const double a = pv1[0];
     if (!(d0 > 0.0)) {
@@ -342,12 +361,10 @@ __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
       if (bad < 0) bad = j + 1;
       e = d0;
     }
-    // the entries of the next two columns' rows, read while the pivots are
-    // worked out
     f64x2_t cn[2] = {f64x2_t{0.0, 0.0}, f64x2_t{0.0, 0.0}};
     if (j + 2 < SB) {
-      cn[0] = *reinterpret_cast<const f64x2_t*>(cur + 2 * (j + 2));
-      cn[1] = *reinterpret_cast<const f64x2_t*>(cur + 2 * (j + 3));
+      cn[0] = *(const lds_f64x2*)(cur + 2 * (j + 2));
+      cn[1] = *(const lds_f64x2*)(cur + 2 * (j + 3));
     }
     const double y0 = rsqrt_nr(d0), ye = rsqrt_nr(e);
     const double y0s = y0 * y0;
@@ -356,31 +373,27 @@ __device__ __noinline__ int diag_factor32(double* Sk, double* col2) {
     const double beta = fma(-g, v[j], v[j + 1]) * (y1 * y1);
     const double alpha = fma(v[j], y0s, -g * beta);
     if (j + 2 < SB) {
-      // the next two columns first; publish them and read the next pivots
-      // while the rest of the update runs
       v[j + 2] = fma(-alpha, cn[0][0], fma(-beta, cn[0][1], v[j + 2]));
       v[j + 3] = fma(-alpha, cn[1][0], fma(-beta, cn[1][1], v[j + 3]));
-      if (isS) *reinterpret_cast<f64x2_t*>(nxt + 2 * r) = f64x2_t{v[j + 2], v[j + 3]};
+      *(lds_f64x2*)(pub + nxo) = f64x2_t{v[j + 2], v[j + 3]};
       wave_sync_lds();
-      pv0 = *reinterpret_cast<const f64x2_t*>(nxt + 2 * (j + 2));
-      pv1 = *reinterpret_cast<const f64x2_t*>(nxt + 2 * (j + 3));
+      pv0 = *(const lds_f64x2*)(col2 + nxo + 2 * (j + 2));
+      pv1 = *(const lds_f64x2*)(col2 + nxo + 2 * (j + 3));
     }
-    // the rest of the update, each column entry read kPre entries ahead
-    f64x2_t cb[kPre];
+    f64x2_t cbuf[kPre];
 #pragma unroll
     for (int k = j + 4; k < SB && k < j + 4 + kPre; ++k)
-      cb[(k - j - 4) % kPre] = *reinterpret_cast<const f64x2_t*>(cur + 2 * k);
+      cbuf[(k - j - 4) % kPre] = *(const lds_f64x2*)(cur + 2 * k);
 #pragma unroll
     for (int k = j + 4; k < SB; ++k) {
-      const f64x2_t t = cb[(k - j - 4) % kPre];
-      if (k + kPre < SB) cb[(k - j - 4) % kPre] = *reinterpret_cast<const f64x2_t*>(cur + 2 * (k + kPre));
+      const f64x2_t t = cbuf[(k - j - 4) % kPre];
+      if (k + kPre < SB) cbuf[(k - j - 4) % kPre] = *(const lds_f64x2*)(cur + 2 * (k + kPre));
       v[k] = fma(-alpha, t[0], fma(-beta, t[1], v[k]));
     }
-    if (!isS) {
-      const double xj = v[j] * y0;
-      v[j + 1] = fma(-g, v[j], v[j + 1]) * y1;
-      v[j] = xj;
-    }
+    // the M half's columns j, j + 1 (the S half never reads them again)
+    const double xj = v[j] * y0;
+    v[j + 1] = fma(-g, v[j], v[j + 1]) * y1;
+    v[j] = xj;
   }
   if (!isS) {
 #pragma unroll
@@ -758,7 +771,7 @@ __device__ __forceinline__ void u2_tile(int64_t npad, int P, int p, int bend, in
 __global__ void __launch_bounds__(256) chol_step(int64_t npad, int64_t n, int P, int p, int bend_prev,
                                                  CholWs w) {
   if (*w.flag) return;
-  __shared__ __align__(16) double lds[kLsD + kBsD + 4 * SB];
+  __shared__ __align__(16) double lds[kLsD + kBsD + 8 * SB];
   __shared__ int s_bad;
   static_assert(sizeof(lds) >= kTileLdsFull, "a U2 tile fits the diagonal step's LDS");
   if (blockIdx.x > 0) {
