@@ -413,8 +413,9 @@ def configs_leg(steps, warmup, names=CONFIG_LEG_WORKLOADS):
     column loop.  Where bits are allocated (the Llama-3-8B block) the method needs
     every sublayer's score first: each sublayer is rotated, scored and factored,
     the block's bits are allocated, then each column loop runs.  Sublayers that
-    share an input are timed as if each computed its own X Gram (the method
-    computes it once per input)."""
+    share an input (q/k/v, gate/up) share its X Gram, the rotation of H_X and the
+    damped inverse factor, computed once per input; a sublayer's time carries an
+    equal share of them."""
     import torch
     import post_quantization_02_amd as kq
     from synth import workloads as WL
@@ -440,64 +441,94 @@ def configs_leg(steps, warmup, names=CONFIG_LEG_WORKLOADS):
         w = WL.BY_NAME[wname]
         log("configs leg:", wname)
         N = w.N
-        Xd, xname = None, None
         held = {}
         rows = []
+        # consecutive sublayers that read the same input form a group
+        groups = []
         for s in w.sublayers:
-            if s.x != xname:
-                Xd = None
-                torch.cuda.empty_cache()
-                Xd, xname = w.gen_x_dev(s.x), s.x
-            log("  rotate, score, factor:", s.name, s.m, "x", s.n)
-            Gd = w.gen_g_dev(s.name)
-            W0 = torch.from_numpy(w.w_f32(s.name)).to(dev)
-            si = torch.from_numpy(w.in_signs(s.x)).to(dev)
-            so = torch.from_numpy(w.out_signs(s.name)).to(dev)
-            m, n = s.m, s.n
+            if groups and groups[-1][0].x == s.x:
+                groups[-1].append(s)
+            else:
+                groups.append([s])
+        for grp in groups:
+            s0 = grp[0]
+            k = len(grp)
+            n = s0.n
+            log("  shared input %s: Gram, input-side rotation, factor (%d sublayers)" % (s0.x, k))
+            Xd = w.gen_x_dev(s0.x)
+            si = torch.from_numpy(w.in_signs(s0.x)).to(dev)
             HX = torch.empty((n, n), dtype=torch.float32, device=dev)
-            HG = torch.empty((m, m), dtype=torch.float32, device=dev)
-            Wk = torch.empty_like(W0)
-            sg = torch.empty(m, dtype=torch.float32, device=dev)
-            tr = torch.empty(3, dtype=torch.float64, device=dev)
+            HXs = torch.empty_like(HX)
             R = torch.empty((n, n), dtype=torch.float32, device=dev)
             perm = torch.empty(n, dtype=torch.int32, device=dev)
 
-            def phase_a(ev):
+            def phase_x(ev):
+                # the input's H_X, its rotation V H_X V^T (shared input-side
+                # signs, no rescale on this side) and the damped inverse factor;
+                # the copy kept for the sublayers' traces is not timed
                 if ev is not None:
                     ev[0].record(stream)
                 kq.kronq_gram(Xd, HX)
                 if ev is not None:
                     ev[1].record(stream)
-                kq.kronq_gram(Gd, HG)
+                kq.kronq_biip_rotate_sx(None, HX, None, si, s0.in_block, None, 1, 0.0, 0.0, m=1)
                 if ev is not None:
                     ev[2].record(stream)
-                Wk.copy_(W0)
+                HXs.copy_(HX)
                 if ev is not None:
                     ev[3].record(stream)
-                kq.kronq_biip_rotate(Wk, HX, HG, si, s.in_block, so, s.out_block, w.alpha, sg)
+                kq.kronq_chol_inv(HX, w.lam, s0.act_order, perm=perm, R=R)
                 if ev is not None:
                     ev[4].record(stream)
-                kq.kronq_sensitivity(HX, HG, out=tr)
-                if ev is not None:
-                    ev[5].record(stream)
-                kq.kronq_chol_inv(HX, w.lam, s.act_order, perm=perm, R=R)
-                if ev is not None:
-                    ev[6].record(stream)
 
-            ta = timed(phase_a, 7)
-            held[s.name] = (Wk, R, perm)
-            rows.append({"sublayer": s.name, "m": m, "n": n, "in_block": s.in_block,
-                         "out_block": s.out_block, "group": s.group, "act_order": s.act_order,
-                         "score": float(tr[2].item()),
-                         "stage_ms": dict(zip(("gram_x", "gram_g", "w_restore", "biip", "sensitivity",
-                                               "chol_inv"), ta)),
-                         "gram_x_tflops": N * n * (n + 1) / (ta[0] * 1e-3) / 1e12,
-                         "gram_g_tflops": N * m * (m + 1) / (ta[1] * 1e-3) / 1e12,
-                         "fwht_gbs": 16.0 * (m * n + n * n + m * m) / (ta[3] * 1e-3) / 1e9})
-            del Gd, HX, HG, sg, tr, W0
+            tx = timed(phase_x, 5)
+            shared = {"gram_x": tx[0], "rot_hx": tx[1], "chol_inv": tx[3]}
+            del Xd, HX
             torch.cuda.empty_cache()
-        Xd = None
-        torch.cuda.empty_cache()
+            for s in grp:
+                log("  rotate, score:", s.name, s.m, "x", s.n)
+                Gd = w.gen_g_dev(s.name)
+                W0 = torch.from_numpy(w.w_f32(s.name)).to(dev)
+                so = torch.from_numpy(w.out_signs(s.name)).to(dev)
+                m = s.m
+                HG = torch.empty((m, m), dtype=torch.float32, device=dev)
+                Wk = torch.empty_like(W0)
+                sg = torch.empty(m, dtype=torch.float32, device=dev)
+                tr = torch.empty(3, dtype=torch.float64, device=dev)
+
+                def phase_a(ev):
+                    if ev is not None:
+                        ev[0].record(stream)
+                    kq.kronq_gram(Gd, HG)
+                    if ev is not None:
+                        ev[1].record(stream)
+                    Wk.copy_(W0)
+                    if ev is not None:
+                        ev[2].record(stream)
+                    kq.kronq_biip_rotate(Wk, None, HG, si, s.in_block, so, s.out_block, w.alpha, sg)
+                    if ev is not None:
+                        ev[3].record(stream)
+                    kq.kronq_sensitivity(HXs, HG, out=tr)
+                    if ev is not None:
+                        ev[4].record(stream)
+
+                ta = timed(phase_a, 5)
+                held[s.name] = (Wk, R, perm)
+                biip_ms = ta[2] + shared["rot_hx"] / k
+                rows.append({"sublayer": s.name, "m": m, "n": n, "in_block": s.in_block,
+                             "out_block": s.out_block, "group": s.group, "act_order": s.act_order,
+                             "score": float(tr[2].item()), "input_shared_by": k,
+                             "stage_ms": {"gram_x": shared["gram_x"] / k, "gram_g": ta[0], "w_restore": ta[1],
+                                          "biip": biip_ms, "sensitivity": ta[3],
+                                          "chol_inv": shared["chol_inv"] / k},
+                             "shared_input_ms": shared,
+                             "gram_x_tflops": N * n * (n + 1) / (shared["gram_x"] * 1e-3) / 1e12,
+                             "gram_g_tflops": N * m * (m + 1) / (ta[0] * 1e-3) / 1e12,
+                             "fwht_gbs": 16.0 * (m * n + m * m) / (ta[2] * 1e-3) / 1e9})
+                del Gd, HG, sg, tr, W0
+                torch.cuda.empty_cache()
+            del HXs
+            torch.cuda.empty_cache()
         nparams = w.n_params()
         if any(s.bits <= 0 for s in w.sublayers):
             budget = int(round(w.avg_bits * sum(nparams)))
