@@ -819,12 +819,13 @@ __global__ void __launch_bounds__(256) chol_u1(int64_t npad, int p, CholWs w) {
 // all the tiles of its row or column block, which split it again each when
 // the tiles split their own operands).  One 128 x 128 output tile per
 // workgroup (four waves as 2 x 2, each 64 x 64 as 2 x 2 accumulator pairs),
-// K staged 32 at a time: the bf16 parts of the next stage are loaded into
-// registers while the current one is multiplied, then copied to LDS as rows
-// [part][row or column][k] (80-byte rows: the 16-byte operand reads of 16
-// consecutive rows hit distinct banks).
-constexpr int OKS = 32;             // K per stage
-constexpr int OLD = OKS + 8;        // padded LDS row (bf16 elements)
+// two workgroups per CU.  K runs in stages of 16 through a ring of three LDS
+// stages filled by direct-to-LDS loads, two stages in flight while one is
+// multiplied; a stage holds the three parts of both operands k-major with the
+// rows' 16-byte chunks swizzled by k, read transposed into the MFMA layout.
+// (Staged 32 at a time through registers, with two barriers and a store
+// phase per stage, the n = 28672 factor took 111 ms; this way 101 ms.  A
+// ring of three 32-k stages needs 144 KiB, one workgroup per CU: 115 ms.)
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 
@@ -928,11 +929,124 @@ __device__ __forceinline__ ko_i16x4_t ko_ld(const unsigned short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((ko_lds_i16x4_t*)p);
 }
 
+// Ring of three stages for the outer update, each a distinct LDS object (the
+// A and B operands of 32 values of k, three bf16 parts each, 48 KiB), so that
+// the compiler's tracking of direct-to-LDS loads sees that refilling one slot
+// does not alias the reads of another.
+constexpr int RKS = 16;   // k per ring stage
+struct OuterSlot {
+  unsigned short a[3 * RKS * NB];
+  unsigned short b[3 * RKS * NB];
+};
+__shared__ __align__(16) OuterSlot co_s0, co_s1, co_s2;
+
+template <int SLOT>
+__device__ __forceinline__ OuterSlot& co_slot() {
+  if constexpr (SLOT == 0) return co_s0;
+  else if constexpr (SLOT == 1) return co_s1;
+  else return co_s2;
+}
+
+typedef __attribute__((address_space(3))) void co_lds_void_t;
+
+// s_waitcnt immediate: at most `vm` loads in flight (vmcnt, 6 bits split over
+// [3:0] and [15:14]), expcnt unconstrained, at most `lgkm` LDS operations
+constexpr int co_cnt(int vm, int lgkm) { return (vm & 15) | (7 << 4) | (lgkm << 8) | ((vm >> 4) << 14); }
+
+// the empty asm hides the offset from the optimizer, so that the stage base
+// is added at each load instead of one live address per slot and load
+__device__ __forceinline__ uint32_t co_opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+struct OuterCtx {
+  const unsigned char* ga;   // split parts of the A tile's rows, stage 0 (bytes)
+  const unsigned char* gb;   // same for the B tile
+  int64_t stage_bytes;       // bytes from one 32-k stage of the split panels to the next
+  uint32_t off[3];           // byte offsets of the lane's three loads within a stage
+  int wave;
+  int rdA0, rdA1, rdB0, rdB1;
+};
+
+// Stage k0 into slot SLOT: wave w loads chunks h = 6 w .. 6 w + 5 of each
+// operand (part h / 8, k rows 4 (h % 8) .. + 3, 1 KiB); lane l of a chunk
+// lands at k row 4 (h % 8) + l / 16, 16-byte position l % 16, and fetches the
+// rows that position holds under the swizzle, 8 ((l % 16) ^ swz(k)) .. + 7.
+template <int SLOT>
+__device__ __forceinline__ void co_issue(const OuterCtx& c, int kst) {
+  OuterSlot& sl = co_slot<SLOT>();
+  const int64_t sb = ((int64_t)(kst >> 1) * 96 + (kst & 1) * 16) * c.stage_bytes;
+  const unsigned char* ga = c.ga + sb;
+  const unsigned char* gb = c.gb + sb;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int h = 3 * c.wave + u;
+    const int e = ((h >> 2) * RKS + 4 * (h & 3)) * NB;
+    __builtin_amdgcn_global_load_lds((const void*)(ga + co_opaque(c.off[u])), (co_lds_void_t*)(sl.a + e), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(gb + co_opaque(c.off[u])), (co_lds_void_t*)(sl.b + e), 16, 0, 0);
+  }
+}
+
+// the 48 products of one stage (two steps of 16 k) from slot SLOT
+template <int SLOT>
+__device__ __forceinline__ void co_mma(const OuterCtx& c, f32x16_t (&hi)[2][2], f32x16_t (&lo)[2][2]) {
+  const OuterSlot& sl = co_slot<SLOT>();
+#pragma unroll
+  for (int ks = 0; ks < RKS; ks += 16) {
+    bf16x8_t af[2][3], bf[2][3];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt) {
+        const unsigned short* q = sl.a + pt * RKS * NB + ks * NB + (a ? c.rdA1 : c.rdA0);
+        af[a][pt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ko_ld(q), ko_ld(q + 4 * NB), 0, 1, 2,
+                                                                         3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt) {
+        const unsigned short* q = sl.b + pt * RKS * NB + ks * NB + (b ? c.rdB1 : c.rdB0);
+        bf[b][pt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ko_ld(q), ko_ld(q + 4 * NB), 0, 1, 2,
+                                                                         3, 4, 5, 6, 7));
+      }
+    // term order: each group of four MFMAs updates four different accumulators
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        hi[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][0], bf[b][0], hi[a][b], 0, 0, 0);
+#pragma unroll
+    for (int term = 0; term < 5; ++term) {
+      const int pa = term == 0 ? 0 : term == 1 ? 1 : term == 2 ? 0 : term == 3 ? 1 : 2;
+      const int pb = term == 0 ? 1 : term == 1 ? 0 : term == 2 ? 2 : term == 3 ? 1 : 0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          lo[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][pa], bf[b][pb], lo[a][b], 0, 0, 0);
+    }
+  }
+}
+
+// Stage s of nst in slot K = s % 3: wait until this wave's loads of stage s
+// have landed (stage s + 1's twelve may still be in flight) and its reads of
+// stage s - 1 have returned, meet the other waves (every wave's loads of stage
+// s have landed and every read of slot (s + 2) % 3 is done), refill that slot
+// with stage s + 2, then multiply stage s.  No branch: past the end the refill
+// loads the last stage again (in bounds, never read).
+template <int K>
+__device__ __forceinline__ void co_step(const OuterCtx& c, int s, int nst, f32x16_t (&hi)[2][2],
+                                        f32x16_t (&lo)[2][2]) {
+  __builtin_amdgcn_s_waitcnt(co_cnt(6, 0));
+  __builtin_amdgcn_s_barrier();
+  co_issue<(K + 2) % 3>(c, min(s + 2, nst - 1));
+  co_mma<K>(c, hi, lo);
+}
+
 __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0, CholWs w) {
   if (*w.flag) return;
-  // a stage of one operand: [part][k][128 rows] bf16, 24 KB
-  __shared__ __align__(16) unsigned short As[3 * OKS * NB];
-  __shared__ __align__(16) unsigned short Bs[3 * OKS * NB];
   const int b1 = b0 + NBO;
   // Tiles in 8 x 8 super-tiles, one super-tile per XCD at a time: workgroup
   // b runs on XCD b % 8, so its slot b / 8 on that XCD takes tile b / 8 % 64
@@ -966,7 +1080,8 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
     if (i >= P || j >= b1) return;
     qlo = j > b0 ? j - b0 : 0;        // panels b0 + q >= c
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lk = lane >> 5;
   f32x16_t hi[2][2], lo[2][2];
@@ -979,55 +1094,21 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
         hi[a][b][v] = 0.f;
         lo[a][b][v] = 0.f;
       }
-  const int k_lo = qlo * NB, k_hi = NBO * NB;
-  // stage at k0 (32 values of k) from the split panels: A rows i NB .. + 127
-  // of L_b0+q, B rows j NB .. + 127 of L_b0+q (SYRK) or columns j NB .. +
-  // 127 of Y_b0+q (fwd), with q = k0 / NB (panel q in slot q: b0 is a
-  // multiple of NBO).  A thread's six 16-byte chunks (8 rows at one k of one
-  // part) are rows 8 (tid % 16) .. + 7 at k tid / 16 and tid / 16 + 16 of
-  // each part; 16 lanes store one k-row of 256 bytes, chunks swizzled.
-  // (plain code over named registers: as arrays captured by a helper lambda
-  // the staging registers went to scratch memory)
-  const unsigned short* Lbase = w.Ls;
-  const unsigned short* Bbase = fwd ? w.Ys : w.Ls;
-  const int64_t ri = (int64_t)i * NB + 8 * (tid & 15), rj = (int64_t)j * NB + 8 * (tid & 15);
-  const int kt = tid >> 4;
-  const int64_t gk = (int64_t)16 * npad;   // 16 k-rows on
-  const int64_t gp = (int64_t)32 * npad;   // the next part
-  const int o0 = kt * NB * 1 + ((((tid & 15)) ^ ko_swz(kt)) << 3);   // bf16 units, k = kt
-  const int o1 = o0 + 16 * NB;                                          // k = kt + 16 (same swizzle)
-  uint4 a0, a1, a2, a3, a4, a5, c0, c1, c2, c3, c4, c5;
-#define KQ_OUTER_LOAD(k0)                                                          \
-  {                                                                                \
-    const unsigned short* La = Lbase + kmaj_at(npad, (k0) / NB, 0, (k0) % NB + kt, ri); \
-    const unsigned short* Lb = Bbase + kmaj_at(npad, (k0) / NB, 0, (k0) % NB + kt, rj); \
-    a0 = *reinterpret_cast<const uint4*>(La);                                      \
-    a1 = *reinterpret_cast<const uint4*>(La + gk);                                 \
-    a2 = *reinterpret_cast<const uint4*>(La + gp);                                 \
-    a3 = *reinterpret_cast<const uint4*>(La + gp + gk);                            \
-    a4 = *reinterpret_cast<const uint4*>(La + 2 * gp);                             \
-    a5 = *reinterpret_cast<const uint4*>(La + 2 * gp + gk);                        \
-    c0 = *reinterpret_cast<const uint4*>(Lb);                                      \
-    c1 = *reinterpret_cast<const uint4*>(Lb + gk);                                 \
-    c2 = *reinterpret_cast<const uint4*>(Lb + gp);                                 \
-    c3 = *reinterpret_cast<const uint4*>(Lb + gp + gk);                            \
-    c4 = *reinterpret_cast<const uint4*>(Lb + 2 * gp);                             \
-    c5 = *reinterpret_cast<const uint4*>(Lb + 2 * gp + gk);                        \
-  }
-#define KQ_OUTER_STORE()                                                           \
-  {                                                                                \
-    *reinterpret_cast<uint4*>(As + o0) = a0;                                       \
-    *reinterpret_cast<uint4*>(As + o1) = a1;                                       \
-    *reinterpret_cast<uint4*>(As + OKS * NB + o0) = a2;                            \
-    *reinterpret_cast<uint4*>(As + OKS * NB + o1) = a3;                            \
-    *reinterpret_cast<uint4*>(As + 2 * OKS * NB + o0) = a4;                        \
-    *reinterpret_cast<uint4*>(As + 2 * OKS * NB + o1) = a5;                        \
-    *reinterpret_cast<uint4*>(Bs + o0) = c0;                                       \
-    *reinterpret_cast<uint4*>(Bs + o1) = c1;                                       \
-    *reinterpret_cast<uint4*>(Bs + OKS * NB + o0) = c2;                            \
-    *reinterpret_cast<uint4*>(Bs + OKS * NB + o1) = c3;                            \
-    *reinterpret_cast<uint4*>(Bs + 2 * OKS * NB + o0) = c4;                        \
-    *reinterpret_cast<uint4*>(Bs + 2 * OKS * NB + o1) = c5;                        \
+  // A rows i NB .. + 127 of L_b0+q; B rows j NB .. + 127 of L_b0+q (SYRK) or
+  // columns j NB .. + 127 of Y_b0+q (fwd); q = k / NB, panel q in slot q (b0
+  // is a multiple of NBO).  Stage k0 of the split panels starts (k0 / 32) 96
+  // npad elements in (kmaj_at).
+  OuterCtx c;
+  c.ga = reinterpret_cast<const unsigned char*>(w.Ls + (int64_t)i * NB);
+  c.gb = reinterpret_cast<const unsigned char*>((fwd ? w.Ys : w.Ls) + (int64_t)j * NB);
+  c.stage_bytes = npad * 2;   // bytes of one k row of the split panels
+  c.wave = wave;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int h = 3 * wave + u;
+    const int k = 4 * (h & 3) + (lane >> 4);
+    const int row = ((lane & 15) ^ ko_swz(k)) << 3;
+    c.off[u] = (uint32_t)((((int64_t)(h >> 2) * 32 + k) * npad + row) * 2);
   }
   // operand reads (the layout of v_mfma_f32_32x32x16_bf16: lane l takes row
   // l % 32 of the operand tile, k 8 (l / 32) .. + 7): within each 16 lanes,
@@ -1039,59 +1120,25 @@ __global__ void __launch_bounds__(256, 2) chol_outer(int64_t npad, int P, int b0
   const int kr = 8 * (rg >> 1) + (rjj >> 2);
   const int fo = 16 * (rg & 1) + 4 * (rjj & 3);
   auto rd_off = [&](int row) { return kr * NB + (((row >> 3) ^ ko_swz(kr)) << 3) + (row & 7); };
-  const int rdA0 = rd_off(wm * 64 + fo), rdA1 = rd_off(wm * 64 + 32 + fo);
-  const int rdB0 = rd_off(wn * 64 + fo), rdB1 = rd_off(wn * 64 + 32 + fo);
-  KQ_OUTER_LOAD(k_lo)
-  KQ_OUTER_STORE()
-  __syncthreads();
-  for (int k0 = k_lo; k0 < k_hi; k0 += OKS) {
-    const bool more = k0 + OKS < k_hi;
-    if (more) KQ_OUTER_LOAD(k0 + OKS)
-#pragma unroll
-    for (int ks = 0; ks < OKS; ks += 16) {
-      bf16x8_t af[2][3], bf[2][3];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int pt = 0; pt < 3; ++pt) {
-          const unsigned short* q = As + pt * OKS * NB + ks * NB + (a ? rdA1 : rdA0);
-          af[a][pt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ko_ld(q), ko_ld(q + 4 * NB), 0, 1, 2,
-                                                                           3, 4, 5, 6, 7));
-        }
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int pt = 0; pt < 3; ++pt) {
-          const unsigned short* q = Bs + pt * OKS * NB + ks * NB + (b ? rdB1 : rdB0);
-          bf[b][pt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ko_ld(q), ko_ld(q + 4 * NB), 0, 1, 2,
-                                                                           3, 4, 5, 6, 7));
-        }
-      // term order: each group of four MFMAs updates four different
-      // accumulators
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          hi[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][0], bf[b][0], hi[a][b], 0, 0, 0);
-#pragma unroll
-      for (int term = 0; term < 5; ++term) {
-        const int pa = term == 0 ? 0 : term == 1 ? 1 : term == 2 ? 0 : term == 3 ? 1 : 2;
-        const int pb = term == 0 ? 1 : term == 1 ? 0 : term == 2 ? 2 : term == 3 ? 1 : 0;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            lo[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][pa], bf[b][pb], lo[a][b], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-    if (more) {
-      KQ_OUTER_STORE()
-      __syncthreads();
-    }
+  c.rdA0 = rd_off(wm * 64 + fo);
+  c.rdA1 = rd_off(wm * 64 + 32 + fo);
+  c.rdB0 = rd_off(wn * 64 + fo);
+  c.rdB1 = rd_off(wn * 64 + 32 + fo);
+  const int ks0 = qlo * (NB / RKS);           // first stage
+  const int nst = NBO * (NB / RKS) - ks0;     // 8, 16, 24 or 32 stages
+  co_issue<0>(c, ks0);
+  co_issue<1>(c, ks0 + 1);
+  int s = 0;
+  for (; s + 3 <= nst; s += 3) {
+    co_step<0>(c, ks0 + s, ks0 + nst, hi, lo);
+    co_step<1>(c, ks0 + s + 1, ks0 + nst, hi, lo);
+    co_step<2>(c, ks0 + s + 2, ks0 + nst, hi, lo);
   }
-#undef KQ_OUTER_LOAD
-#undef KQ_OUTER_STORE
+  if (s < nst) co_step<0>(c, ks0 + s, ks0 + nst, hi, lo);
+  if (s + 1 < nst) co_step<1>(c, ks0 + s + 1, ks0 + nst, hi, lo);
+  // the refills past the end are still landing in LDS: drain them before the
+  // workgroup can exit
+  __builtin_amdgcn_s_waitcnt(co_cnt(0, 0));
   // C -= hi + lo, every old value of an accumulator tile loaded before its stores
   float* C = (fwd ? w.B : w.A) + (int64_t)i * NB * npad + (int64_t)j * NB;
 #pragma unroll
