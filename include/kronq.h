@@ -300,14 +300,16 @@ kronq_status kronq_gptq_quantize(const float* W, int64_t m, int64_t n, int64_t l
  *   dX = X_fp - X is formed exactly in fp32 and split into two bf16 parts (hi
  *   + lo, 16 significant bits: exact unless X_fp and X differ by more than a
  *   factor 2^8), then hi^T X + lo^T X accumulates in fp32 on the bf16 matrix
- *   cores, in chunks of 32768 tokens.  n must be a multiple of 256 and N of
- *   128 (KRONQ_EUNSUPPORTED otherwise).  ws: kronq_drift_cross_ws(N, n)
+ *   cores, in chunks of 32768 tokens.  n must be a multiple of 256, N of 128
+ *   and ld at most 67108848 (KRONQ_EUNSUPPORTED otherwise: the pipeline
+ *   addresses a stage with 32-bit offsets).  ws: kronq_drift_cross_ws(N, n)
  *   bytes.  The input side of BiIP applies to C as to H_X: C' = V C V^T is
  *   kronq_biip_rotate with W = C, both sides the input side's spec, HX and HG
  *   NULL and alpha 0.
  * kronq_gram_cross: the general cross product C = scale A^T B - sub (A and B
  *   N x d bf16 with one layout as above, sub d x d fp32 or NULL), on the same
- *   tiles.  ws: kronq_gram_cross_ws(N, d) bytes.
+ *   tiles, with the same limits on d, N and ld.  ws: kronq_gram_cross_ws(N, d)
+ *   bytes.
  * kronq_gptaq_correction: P = alpha ((C_p R^T) (.) M) R with
  *   C_p[a][b] = C[perm[a]][perm[b]] (perm NULL: identity), R the n x n upper
  *   factor of kronq_chol_inv (processing order, lower triangle zero) and M the

@@ -378,6 +378,8 @@ kronq_status kronq_gram_cross(const void* A, const void* B, int64_t N, int64_t d
   if (d % 256 || N % 128)
     return fail(KRONQ_EUNSUPPORTED, "kronq_gram_cross: d (%lld) must be a multiple of 256 and N (%lld) "
                 "of 128", (long long)d, (long long)N);
+  if (!gram_pipeline_ld_ok(ld))
+    return fail(KRONQ_EUNSUPPORTED, "kronq_gram_cross: ld (%lld) above 67108848", (long long)ld);
   const size_t need = gram_cross_ws_bytes(N, d);
   kronq_status st = check_ws("kronq_gram_cross", ws, ws_bytes, need, true);
   if (st) return st;
@@ -398,6 +400,8 @@ kronq_status kronq_drift_cross(const void* Xfp, const void* X, int64_t N, int64_
   if (n % 256 || N % 128)
     return fail(KRONQ_EUNSUPPORTED, "kronq_drift_cross: n (%lld) must be a multiple of 256 and N (%lld) "
                 "of 128", (long long)n, (long long)N);
+  if (!gram_pipeline_ld_ok(ld))
+    return fail(KRONQ_EUNSUPPORTED, "kronq_drift_cross: ld (%lld) above 67108848", (long long)ld);
   kronq_status st = check_ws("kronq_drift_cross", ws, ws_bytes, drift_cross_ws_bytes(N, n), true);
   if (st) return st;
   return drift_cross_launch(Xfp, X, N, n, ld, C, ldc, ws, (hipStream_t)stream);

@@ -921,6 +921,10 @@ size_t gram_ws_bytes(int64_t N, int64_t d, int32_t dtype) {
 
 namespace {
 
+// The direct-to-LDS pipeline addresses a lane's load within a stage with an
+// unsigned 32-bit byte offset (up to V2K - 1 rows of the operand's pitch)
+bool lds_offsets_fit(int64_t lda) { return lda * 2 * V2K + 1024 <= (int64_t(1) << 32); }
+
 // One launch of the split-K scheme for rows [0, p.N) of p.A with the split
 // count already planned; `kind` 0 = direct-to-LDS bf16 pipeline (N a multiple
 // of V2K, d a multiple of 256), 1 = generic bf16, 2 = fp32.
@@ -986,7 +990,7 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
   p.beta = beta;
   plan(N, d, dtype, p.T, p.ntiles, p.S, p.nstages);
   if (dtype != KRONQ_BF16) return launch_gram(p, 2, s);
-  if (d % BT != 0) return launch_gram(p, 1, s);
+  if (d % BT != 0 || !lds_offsets_fit(lda)) return launch_gram(p, 1, s);
   // whole units of V2D stages (128 tokens) through the direct-to-LDS
   // pipeline, then the remaining < 128 tokens accumulated by the generic
   // kernel (beta = 1)
@@ -1028,6 +1032,8 @@ void plan_cross(int64_t N, int64_t d, int& T, int& ntiles, int& S, int64_t& nsta
 
 }  // namespace
 
+bool gram_pipeline_ld_ok(int64_t ld) { return lds_offsets_fit(ld); }
+
 size_t gram_cross_ws_bytes(int64_t N, int64_t d) {
   int T, ntiles, S;
   int64_t nstages;
@@ -1057,6 +1063,10 @@ kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t 
   p.part = static_cast<float*>(ws);
   p.scale = scale;
   p.beta = beta;
+  if (!lds_offsets_fit(ld))
+    return fail(KRONQ_EUNSUPPORTED, "cross product: leading dimension %lld too large for 32-bit "
+                "stage offsets (at most %lld)", (long long)ld,
+                (long long)(((int64_t(1) << 32) - 1024) / (2 * V2K)));
   plan_cross(N, d, p.T, p.ntiles, p.S, p.nstages);
   p.S = (int)std::max<int64_t>(1, std::min<int64_t>(p.S, N / ((int64_t)V2D * V2K)));
   return launch_gram(p, 0, s);

@@ -37,6 +37,9 @@ kronq_status gram_launch(const void* A, int32_t dtype, int64_t N, int64_t d, int
                          int64_t ldh, float scale, float beta, void* ws, size_t ws_bytes,
                          hipStream_t s);
 
+// whether the direct-to-LDS Gram pipeline can address an operand with this
+// leading dimension (32-bit offsets within a stage)
+bool gram_pipeline_ld_ok(int64_t ld);
 size_t gram_cross_ws_bytes(int64_t N, int64_t d);
 kronq_status gram_cross_launch(const void* A, const void* B, int64_t N, int64_t d, int64_t ld, float* C,
                                int64_t ldc, float scale, float beta, const float* sub, int64_t ldsub,

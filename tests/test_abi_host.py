@@ -312,3 +312,19 @@ def test_input_rescale_arguments_rejected_before_launch(lib):
     assert rot(fake, fake, fake, 0.25, 0.25, fake, 0, ws=None, wsb=need) == kq.KRONQ_EWORKSPACE
     assert lib.kronq_biip_unrotate_sx(fake, 8, 16, 16, ctypes.byref(h_in), ctypes.byref(h_out),
                                       fake, None, fake, 1 << 20, None) == kq.KRONQ_EINVAL
+
+
+def test_cross_products_reject_leading_dimensions_past_32bit_offsets(lib):
+    """The direct-to-LDS pipeline addresses a stage with 32-bit byte offsets
+    (31 rows of the operand's pitch): the cross products refuse larger leading
+    dimensions before any launch, and accept the largest one that fits."""
+    fake = 1 << 20   # 16-byte aligned, never dereferenced
+    ws = lib.kronq_gram_cross_ws(128, 256)
+    big, top = 67108856, 67108848    # multiples of 8; the first is past the limit
+    assert lib.kronq_gram_cross(fake, fake, 128, 256, big, fake, 256, 1.0, None, 0, fake, ws,
+                                None) == kq.KRONQ_EUNSUPPORTED
+    assert lib.kronq_drift_cross(fake, fake, 128, 256, big, fake, 256, fake,
+                                 lib.kronq_drift_cross_ws(128, 256), None) == kq.KRONQ_EUNSUPPORTED
+    # the largest accepted pitch passes the checks up to the workspace test
+    assert lib.kronq_gram_cross(fake, fake, 128, 256, top, fake, 256, 1.0, None, 0, fake, ws - 1,
+                                None) == kq.KRONQ_EWORKSPACE
