@@ -324,7 +324,9 @@ DECODE_STACKED = (("qkv_proj", 12288, 4096), ("o_proj", 4096, 4096),
 
 
 def decode_leg(steps, warmup, n_layers=32, bits=4, group=128, sublayers=DECODE_SUBLAYERS,
-               name="llama2_7b_linear_stack"):
+               name="llama2_7b_linear_stack", noalloc=False):
+    """noalloc: each call through kronq_decode_matvec_noalloc (the library's own
+    partial-sum buffer) instead of kronq_decode_matvec with a caller workspace."""
     import torch
     import post_quantization_02_amd as kq
     dev = torch.device("cuda:0")
@@ -363,8 +365,12 @@ def decode_leg(steps, warmup, n_layers=32, bits=4, group=128, sublayers=DECODE_S
 
     def token():
         for codes, m, n, scales, zeros in layers:
-            kq.kronq_decode_matvec(codes, n, bits, group, scales, zeros, sgn_in[n], blk(n),
-                                   sgn_out[m], blk(m), sg[m], xs[n], y=ys[m], ws=ws)
+            if noalloc:
+                kq.kronq_decode_matvec_noalloc(codes, n, bits, group, scales, zeros, sgn_in[n], blk(n),
+                                               sgn_out[m], blk(m), sg[m], xs[n], ys[m])
+            else:
+                kq.kronq_decode_matvec(codes, n, bits, group, scales, zeros, sgn_in[n], blk(n),
+                                       sgn_out[m], blk(m), sg[m], xs[n], y=ys[m], ws=ws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -396,6 +402,7 @@ def decode_leg(steps, warmup, n_layers=32, bits=4, group=128, sublayers=DECODE_S
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     return {"workload": "%s_w%dg%d_batch1" % (name, bits, group),
             "sublayers": len(layers), "calls_per_token": len(layers),
+            "entry_point": "kronq_decode_matvec_noalloc" if noalloc else "kronq_decode_matvec",
             "kernels_per_call": 2, "bits": bits, "group": group,
             "algorithmic_bytes_per_token": alg_bytes, "ms_per_token_graph": ms,
             "tokens_per_s": 1e3 / ms, "ms_per_token_eager": eager_ms,
@@ -788,7 +795,8 @@ def main():
         log("decode leg only")
         print(json.dumps({"decode": decode_leg(args.decode_steps, 3),
                           "decode_stacked": decode_leg(args.decode_steps, 3, sublayers=DECODE_STACKED,
-                                                       name="llama2_7b_linear_stack_qkv_gateup")}),
+                                                       name="llama2_7b_linear_stack_qkv_gateup"),
+                          "decode_noalloc": decode_leg(args.decode_steps, 3, noalloc=True)}),
               flush=True)
         return
     import torch
@@ -914,6 +922,7 @@ def main():
         out["decode"] = decode_leg(args.decode_steps, 3)
         out["decode_stacked"] = decode_leg(args.decode_steps, 3, sublayers=DECODE_STACKED,
                                            name="llama2_7b_linear_stack_qkv_gateup")
+        out["decode_noalloc"] = decode_leg(args.decode_steps, 3, noalloc=True)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)

@@ -64,6 +64,59 @@ def test_noalloc_matches_the_workspace_entry_point_twice():
         assert np.max(np.abs(y_na - want)) <= 1e-4 * np.max(np.abs(want))
 
 
+def _stored(seed, m, n, bits, group, perm=False):
+    """Random stored codes (any byte is a valid pack of 2- or 4-bit codes; one
+    code a byte below 2^bits otherwise), grids, signs, S_G, x and an optional
+    column permutation, on the device."""
+    row = kq.kronq_packed_row_bytes(n, bits)
+    ldp = (row + 15) // 16 * 16
+    top = 256 if bits in (2, 4) else 1 << bits
+    raw = np.mod(synth.matrix(synth.INT, seed, m, ldp, p1=1024.0, dtype="f64"), top).astype(np.uint8)
+    raw[:, row:] = 0
+    ng = 1 if group <= 0 else n // group
+    d = dict(codes=torch.from_numpy(raw).to(DEV),
+             scales=to_dev_f32(np.abs(synth.matrix(synth.NORMAL, seed + 1, m, ng, p1=1e-2, dtype="f32")) + 1e-3),
+             zeros=to_dev_f32(np.mod(synth.matrix(synth.INT, seed + 2, m, ng, p1=64.0, dtype="f64"),
+                                     1 << bits).astype(np.float32)),
+             si=to_dev_f32(synth.signs(seed + 3, n)), so=to_dev_f32(synth.signs(seed + 4, m)),
+             sg=to_dev_f32(np.exp(synth.matrix(synth.NORMAL, seed + 5, 1, m, p1=0.3, dtype="f64")[0])
+                           .astype(np.float32)),
+             x=to_dev_f32(synth.matrix(synth.ACT_T4, seed + 6, 1, n, dtype="f32")[0]), perm=None)
+    if perm:
+        keys = synth.matrix(synth.NORMAL, seed + 7, 1, n, dtype="f64")[0]
+        d["perm"] = torch.from_numpy(np.argsort(-keys, kind="stable").astype(np.int32)).to(DEV)
+    return d
+
+
+@pytest.mark.parametrize("m,n,bits,group,ko,ki,extra", [
+    (4096, 4096, 4, 0, 4096, 4096, ""),       # one grid per row, 32 rows a workgroup
+    (4096, 11008, 3, 0, 4096, 256, ""),       # one code a byte, 43 input blocks
+    (14336, 4096, 4, 128, 2048, 4096, ""),    # last output tile half full
+    (11008, 4096, 2, 64, 256, 4096, ""),      # last output tile 2816 rows
+    (8192, 1024, 4, 128, 8192, 1024, ""),     # output tile of 8192 rows (past the registers)
+    (40000, 1024, 4, 128, 64, 1024, ""),      # ten output tiles
+    (100, 200, 4, 0, 4, 8, ""),               # 8 rows a workgroup, ragged rows
+    (33, 1000, 2, 0, 1, 8, "no_out_signs"),   # block 1 and no signs on the output side
+    (7, 192, 8, 64, 1, 64, "no_sg"),          # one output tile of 8 rows, no S_G
+    (1, 64, 4, 64, 1, 64, ""),                # tile of one row: output stage launched apart
+    (4096, 11008, 4, 128, 4096, 256, "perm"), # codes in processing order
+])
+def test_noalloc_matches_the_workspace_entry_point_across_shapes(m, n, bits, group, ko, ki, extra):
+    """Bit for bit the workspace entry point's result over the decode's shape
+    cases: grid sizes, ragged last tiles, tiles wider than the registers hold,
+    NULL output signs or S_G, and the case whose output stage is not fused."""
+    say("noalloc decode", m, n, bits, group, ko, ki, extra)
+    d = _stored(950 + m % 97 + bits, m, n, bits, group, perm=extra == "perm")
+    so = None if extra == "no_out_signs" else d["so"]
+    sg = None if extra == "no_sg" else d["sg"]
+    args = (d["codes"], n, bits, group, d["scales"], d["zeros"], d["si"], ki, so, ko, sg, d["x"])
+    y_ws = kq.kronq_decode_matvec(*args, perm=d["perm"])
+    for rep in range(2):
+        y_na = torch.full((m,), float("nan"), dtype=torch.float32, device=DEV)
+        kq.kronq_decode_matvec_noalloc(*args, y_na, perm=d["perm"])
+        np.testing.assert_array_equal(host(y_na), host(y_ws))
+
+
 def test_noalloc_too_large_is_enomem():
     # 8-bit codes keep 1024 columns a slice: 8 slices x 140000 rows of partial
     # sums exceed the 4 MiB buffer; rejected before anything is launched
