@@ -126,24 +126,28 @@ __device__ __forceinline__ void reg_stages(float4 (&x)[ECH], int nch, int mask_l
   }
 }
 
-// one LDS round over bits [b, b + k) of a 2^p tile, b in 2..9 at compile time
+// one LDS round over bits [b, b + k) of a 2^p tile, b in 2..10 at compile time
+template <int NTH = NTB>
 __device__ __forceinline__ void lds_round_mid(float* s, int p, int b, int k) {
   switch (b) {
-    case 2: lds_round_k<NTB, 2>(s, p, k); break;
-    case 3: lds_round_k<NTB, 3>(s, p, k); break;
-    case 4: lds_round_k<NTB, 4>(s, p, k); break;
-    case 5: lds_round_k<NTB, 5>(s, p, k); break;
-    case 6: lds_round_k<NTB, 6>(s, p, k); break;
-    case 7: lds_round_k<NTB, 7>(s, p, k); break;
-    case 8: lds_round_k<NTB, 8>(s, p, k); break;
-    default: lds_round_k<NTB, 9>(s, p, k); break;
+    case 2: lds_round_k<NTH, 2>(s, p, k); break;
+    case 3: lds_round_k<NTH, 3>(s, p, k); break;
+    case 4: lds_round_k<NTH, 4>(s, p, k); break;
+    case 5: lds_round_k<NTH, 5>(s, p, k); break;
+    case 6: lds_round_k<NTH, 6>(s, p, k); break;
+    case 7: lds_round_k<NTH, 7>(s, p, k); break;
+    case 8: lds_round_k<NTH, 8>(s, p, k); break;
+    case 9: lds_round_k<NTH, 9>(s, p, k); break;
+    default: lds_round_k<NTH, 10>(s, p, k); break;
   }
 }
 
-// bits [lo, hi) of the tile through LDS (2 <= lo, hi <= 10): at most two rounds
+// bits [lo, hi) of the tile through LDS (2 <= lo, hi <= 2 + log2 NTH): the
+// thread-index bits, at most two rounds for 256 threads, three for 512
+template <int NTH = NTB>
 __device__ __forceinline__ void lds_mid_bits(float* s, int p, int lo, int hi) {
   for (int b = lo; b < hi; b += 4) {
-    lds_round_mid(s, p, b, min(4, hi - b));
+    lds_round_mid<NTH>(s, p, b, min(4, hi - b));
     __syncthreads();
   }
 }
@@ -238,8 +242,14 @@ __global__ void __launch_bounds__(NTB) biip_pass1v(TParams p) {
 }
 
 // pass 2: tile = (kr / R1) rows at stride R1 x CW columns, index e = j * CW + c;
-// the transformed bits are the row bits [lg_cw, lg)
-__global__ void __launch_bounds__(NTB) biip_pass2v(TParams p) {
+// the transformed bits are the row bits [lg_cw, lg).  NTH threads of 16 float4
+// chunks: tiles of up to 2^14 elements with 256 threads, 2^15 with 512 (the
+// wide form: twice the strip width, 144 KiB of LDS, one workgroup per CU).
+// Element e = 4 * (t + NTH * i) + j, so chunk bit k is element bit CB + k.
+template <int NTH>
+__global__ void __launch_bounds__(NTH) biip_pass2v(TParams p) {
+  constexpr int CB = NTH == 512 ? 11 : 10;
+  static_assert(NTH == 256 || NTH == 512, "pass 2 runs 256 or 512 threads");
   extern __shared__ __align__(16) float s[];
   int64_t t;
   if (!xcd_tile(p.tiles2, p.per_xcd2, t)) return;
@@ -251,12 +261,12 @@ __global__ void __launch_bounds__(NTB) biip_pass2v(TParams p) {
   const int64_t cbase = strip << p.lg_cw;
   const int lg = p.lg_rows2 + p.lg_cw;
   const int E = 1 << lg;
-  const int nch = E >= 4 * NTB ? E / (4 * NTB) : 1;
+  const int nch = E >= 4 * NTH ? E / (4 * NTH) : 1;
   const int64_t cmask = (1 << p.lg_cw) - 1;
   float4 x[ECH];
 #pragma unroll
   for (int i = 0; i < ECH; ++i) {
-    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int e0 = 4 * ((int)threadIdx.x + NTH * i);
     const int64_t j = e0 >> p.lg_cw, c = cbase + (e0 & cmask);
     const bool in = e0 < E && c < p.C;
     const float4 v = ld4(p.M + (in ? (rbase + j * p.R1) * p.ld + c : rbase * p.ld + cbase));
@@ -264,15 +274,15 @@ __global__ void __launch_bounds__(NTB) biip_pass2v(TParams p) {
   }
   int mask_i = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) mask_i |= (10 + k >= p.lg_cw && 10 + k < lg) ? (1 << k) : 0;
+  for (int k = 0; k < 4; ++k) mask_i |= (CB + k >= p.lg_cw && CB + k < lg) ? (1 << k) : 0;
   reg_stages(x, nch, 0, mask_i);   // bits 0-1 are column bits (cw >= 4)
 #pragma unroll
   for (int i = 0; i < ECH; ++i) {
-    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int e0 = 4 * ((int)threadIdx.x + NTH * i);
     if (e0 < E) *reinterpret_cast<float4*>(s + pad(e0)) = x[i];
   }
   __syncthreads();
-  lds_mid_bits(s, lg, max(p.lg_cw, 2), min(lg, 10));
+  lds_mid_bits<NTH>(s, lg, max(p.lg_cw, 2), min(lg, CB));
   const float nrm = p.norm2;
   float g[ECH];
 #pragma unroll
@@ -280,14 +290,14 @@ __global__ void __launch_bounds__(NTB) biip_pass2v(TParams p) {
   if (p.post) {
 #pragma unroll
     for (int i = 0; i < ECH; ++i) {
-      const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+      const int e0 = 4 * ((int)threadIdx.x + NTH * i);
       const int64_t j = e0 < E ? (e0 >> p.lg_cw) : 0;
       g[i] = nrm * p.row.fac[rbase + j * p.R1];
     }
   }
 #pragma unroll
   for (int i = 0; i < ECH; ++i) {
-    const int e0 = 4 * ((int)threadIdx.x + NTB * i);
+    const int e0 = 4 * ((int)threadIdx.x + NTH * i);
     const int64_t j = e0 >> p.lg_cw, c = cbase + (e0 & cmask);
     if (e0 < E && c < p.C) {
       const float4 y = *reinterpret_cast<const float4*>(s + pad(e0));
@@ -743,11 +753,25 @@ Plan plan2d(float* M, int64_t R, int64_t C, int64_t ld, int64_t kr, const float*
   return pl;
 }
 
+// Pass-2 strips narrower than 128 bytes (cw < 32) are doubled where the
+// matrix is wide enough, with tiles of 2^15 elements (the 512-thread pass 2).
+// Measured on a 28672^2 matrix (column block 4096, pass 1 unchanged), pass 2
+// took 1.46-1.50 ms with 64-byte strips, 1.31 ms with 128-byte and 1.28 ms
+// with 256-byte strips.
+bool widen_pass2(TParams& p) {
+  const int64_t cw = int64_t(1) << p.lg_cw;
+  if (cw >= 32 || pow2_floor(p.C) < 2 * cw || p.lg_rows2 + p.lg_cw != LOG_TILE) return false;
+  p.lg_cw += 1;
+  p.strips = (p.C + 2 * cw - 1) / (2 * cw);
+  p.tiles2 = (p.R / p.row.block) * p.R1 * p.strips;
+  p.per_xcd2 = (int)((p.tiles2 + kXcds - 1) / kXcds);
+  return true;
+}
+
 // one matrix, one workgroup per tile
 kronq_status launch2d(const Plan& pl, hipStream_t st) {
-  const TParams& p = pl.p;
+  TParams p = pl.p;
   const size_t lds1 = padded(1 << (p.lg_c1 + p.lg_r1)) * sizeof(float);
-  const size_t lds2 = padded(1 << (p.lg_rows2 + p.lg_cw)) * sizeof(float);
   const size_t ldsmax = padded(TILE) * sizeof(float);
   {
     auto k1 = pl.vec1 ? biip_pass1v : biip_pass1s;
@@ -756,9 +780,12 @@ kronq_status launch2d(const Plan& pl, hipStream_t st) {
     KQ_LAUNCHED("biip_pass1");
   }
   if (p.tiles2) {
-    auto k2 = pl.vec2 ? biip_pass2v : biip_pass2s;
-    KQ_HIP(hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax));
-    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(pl.vec2 ? NTB : NT), lds2, st, p);
+    const bool wide = pl.vec2 && widen_pass2(p);
+    const size_t lds2 = padded(1 << (p.lg_rows2 + p.lg_cw)) * sizeof(float);
+    auto k2 = wide ? biip_pass2v<512> : pl.vec2 ? biip_pass2v<NTB> : biip_pass2s;
+    const size_t lmax = wide ? padded(2 * TILE) * sizeof(float) : ldsmax;
+    KQ_HIP(hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lmax));
+    hipLaunchKernelGGL(k2, dim3(p.per_xcd2 * kXcds), dim3(wide ? 512 : pl.vec2 ? NTB : NT), lds2, st, p);
     KQ_LAUNCHED("biip_pass2");
   }
   return KRONQ_OK;

@@ -86,3 +86,21 @@ def test_biip_full_size_llama2_7b_q_proj():
     e = (rel_fro(host(Wd), Wp), rel_fro(host(HXd), HXp), rel_fro(host(HGd), HGp))
     say("  rel fro W %.2e HX %.2e HG %.2e" % e)
     assert max(e) <= 1e-5
+
+
+def test_biip_per_matrix_passes_wide_strips():
+    """Above the merged passes' tile limit every matrix runs its own two
+    launches, and pass 2 takes 2^15-element tiles where a 2^14 tile would leave
+    strips under 128 bytes: here W (8192 x 4096, row block 8192: strips of 32
+    bytes become 64), H_X (4096^2: 64 -> 128 bytes) and H_G (8192^2: 16 -> 32
+    bytes).  Element by element against the oracle."""
+    m, n = 8192, 4096
+    say("biip per-matrix passes, wide pass-2 strips", m, n)
+    W, HX, HG, si, so = _case(m, n, 61)
+    Wd, HXd, HGd = to_dev_f32(W), to_dev_f32(HX), to_dev_f32(HG)
+    kq.kronq_biip_rotate(Wd, HXd, HGd, to_dev_f32(si), 4096, to_dev_f32(so), 8192, 0.25)
+    Wp, HXp, HGp, _ = O.biip(W.astype(np.float64), HX.astype(np.float64), HG.astype(np.float64),
+                             si, 4096, so, 8192, 0.25)
+    e = (rel_fro(host(Wd), Wp), rel_fro(host(HXd), HXp), rel_fro(host(HGd), HGp))
+    say("  rel fro W %.2e HX %.2e HG %.2e" % e)
+    assert max(e) <= 1e-5

@@ -61,6 +61,7 @@ def test_pack_unpack_bit_exact(bits, m, n, pad):
     (4096, 64, 4096, 64, True),     # wide output block (two passes on the column side)
     (128, 1376, 128, 32, True),     # 43 input blocks
     (96, 64, 1, 2, True),           # block 1 (no mixing) on the output side
+    (4096, 4096, 4096, 4096, True), # one launch per pass, pass 2 on 2^15-element tiles
 ])
 def test_unrotate(m, n, ko, ki, with_sg):
     say("unrotate", m, n, ko, ki, with_sg)
