@@ -21,10 +21,11 @@
 //           the remaining kr/R1 part of the row-side transform (skipped when
 //           R1 == kr).
 // Each pass stages its tile (up to 2^14 floats = 64 KiB, so that two
-// workgroups share a CU) in LDS and runs the butterflies radix-16: a thread
-// gathers 16 elements differing in 4 index bits, does 4 butterfly stages in
-// registers and scatters them back.  HBM traffic is float4 and coalesced (rows
-// of a column block are contiguous; pass-2 strips are >= 64 B wide).  LDS rows
+// workgroups share a CU; 2^15 for a pass 2 whose strips would otherwise be
+// under 128 bytes) in LDS and runs the butterflies radix-16: a thread gathers
+// 16 elements differing in 4 index bits, does 4 butterfly stages in registers
+// and scatters them back.  HBM traffic is float4 and coalesced (rows of a
+// column block are contiguous; pass-2 strips are whole 16-byte chunks).  LDS rows
 // are padded by 4 floats per 32 so that float4-aligned accesses stay 16-byte
 // aligned and the low-bit rounds are bank-conflict free.  The forward
 // transform of W, H_X and H_G runs as two persistent launches, pass 1 of all
