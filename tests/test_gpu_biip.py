@@ -104,3 +104,13 @@ def test_biip_per_matrix_passes_wide_strips():
     e = (rel_fro(host(Wd), Wp), rel_fro(host(HXd), HXp), rel_fro(host(HGd), HGp))
     say("  rel fro W %.2e HX %.2e HG %.2e" % e)
     assert max(e) <= 1e-5
+    # the same call with W in a buffer of a padded leading dimension (still
+    # the per-matrix passes): the padding is left untouched and every result
+    # equals the dense call's bit for bit
+    buf = torch.full((m, n + 64), 7.0, dtype=torch.float32, device=DEV)
+    Wv = buf[:, :n]
+    Wv.copy_(to_dev_f32(W))
+    HXv, HGv = to_dev_f32(HX), to_dev_f32(HG)
+    kq.kronq_biip_rotate(Wv, HXv, HGv, to_dev_f32(si), 4096, to_dev_f32(so), 8192, 0.25)
+    assert torch.equal(Wv, Wd) and torch.equal(HXv, HXd) and torch.equal(HGv, HGd)
+    assert bool((buf[:, n:] == 7.0).all())
